@@ -1,0 +1,228 @@
+/*
+ * pero.c -- CPU oracle for the prioritized-replay sum tree.
+ *
+ * TEST INFRASTRUCTURE ONLY (see pero.h).  Plain C, one element at a time,
+ * built with -O2 -ffp-contract=off and no fast-math so that every f32 add,
+ * subtract and min is a single IEEE round-to-nearest operation.
+ */
+#include "pero.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+struct pero {
+    int64_t n;          /* capacity = number of leaves, a power of two */
+    int32_t D;          /* state_dim; 0 = no transition storage */
+    double alpha, eps;
+    float* sum;         /* [2n], index 0 unused, leaves at [n, 2n) */
+    float* mn;          /* [2n], same layout, min in place of sum */
+    float* states;      /* [n*D] */
+    float* next_states; /* [n*D] */
+    uint32_t* actions;  /* [n] */
+    float* rewards;     /* [n] */
+    uint8_t* dones;     /* [n] */
+    int64_t size, cursor;
+    float maxp;         /* running max priority */
+};
+
+/* Recompute every ancestor of tree node i, from its parent up to the root.
+ * "The Tree Under Every Prioritized Replay": an internal node holds the sum of
+ * its children (and, in the twin tree, their min); a point update touches one
+ * leaf-to-root path. */
+static void walk_to_root(pero_t* t, int64_t i) {
+    for (i >>= 1; i >= 1; i >>= 1) {
+        float l = t->sum[2 * i], r = t->sum[2 * i + 1];
+        t->sum[i] = l + r;
+        float a = t->mn[2 * i], b = t->mn[2 * i + 1];
+        t->mn[i] = (b < a) ? b : a;
+    }
+}
+
+static void set_leaf(pero_t* t, int64_t slot, float p) {
+    int64_t i = t->n + slot;
+    t->sum[i] = p;
+    t->mn[i] = p;
+    walk_to_root(t, i);
+}
+
+pero_t* pero_create(int64_t capacity, int32_t state_dim, double alpha, double eps) {
+    if (capacity < 2 || capacity > ((int64_t)1 << 30)) return NULL;
+    if ((capacity & (capacity - 1)) != 0) return NULL;
+    if (state_dim < 0) return NULL;
+    pero_t* t = (pero_t*)calloc(1, sizeof(pero_t));
+    if (!t) return NULL;
+    t->n = capacity;
+    t->D = state_dim;
+    t->alpha = alpha;
+    t->eps = eps;
+    t->sum = (float*)malloc(sizeof(float) * 2 * capacity);
+    t->mn = (float*)malloc(sizeof(float) * 2 * capacity);
+    if (!t->sum || !t->mn) { pero_destroy(t); return NULL; }
+    /* Empty slots are the neutral elements: 0 for sum, +inf for min. */
+    for (int64_t i = 0; i < 2 * capacity; ++i) {
+        t->sum[i] = 0.0f;
+        t->mn[i] = INFINITY;
+    }
+    if (state_dim > 0) {
+        t->states = (float*)calloc((size_t)capacity * state_dim, sizeof(float));
+        t->next_states = (float*)calloc((size_t)capacity * state_dim, sizeof(float));
+        t->actions = (uint32_t*)calloc((size_t)capacity, sizeof(uint32_t));
+        t->rewards = (float*)calloc((size_t)capacity, sizeof(float));
+        t->dones = (uint8_t*)calloc((size_t)capacity, sizeof(uint8_t));
+        if (!t->states || !t->next_states || !t->actions || !t->rewards || !t->dones) {
+            pero_destroy(t);
+            return NULL;
+        }
+    }
+    t->size = 0;
+    t->cursor = 0;
+    t->maxp = 1.0f;
+    return t;
+}
+
+void pero_destroy(pero_t* t) {
+    if (!t) return;
+    free(t->sum);
+    free(t->mn);
+    free(t->states);
+    free(t->next_states);
+    free(t->actions);
+    free(t->rewards);
+    free(t->dones);
+    free(t);
+}
+
+/* "GPU-Resident Prioritized Experience Replay", section "Experience
+ * Insertion": new experiences take the current max priority and the write
+ * cursor wraps modulo capacity; section "Error Handling & Fallback": ring
+ * overflow overwrites the oldest items.  Given priorities replace the max
+ * priority and raise it; -0.0 is read as +0.0. */
+int pero_add(pero_t* t, int64_t count, const float* states, const float* next_states,
+             const uint32_t* actions, const float* rewards, const uint8_t* dones,
+             const float* prio) {
+    if (count < 0 || count > t->n) return -1;
+    const int64_t D = t->D;
+    for (int64_t j = 0; j < count; ++j) {
+        int64_t slot = (t->cursor + j) % t->n;
+        if (D > 0) {
+            memcpy(t->states + slot * D, states + j * D, sizeof(float) * D);
+            memcpy(t->next_states + slot * D, next_states + j * D, sizeof(float) * D);
+            t->actions[slot] = actions[j];
+            t->rewards[slot] = rewards[j];
+            t->dones[slot] = dones[j];
+        }
+        float p;
+        if (prio) {
+            p = prio[j] + 0.0f;
+            if (p > t->maxp) t->maxp = p;
+        } else {
+            p = t->maxp;
+        }
+        set_leaf(t, slot, p);
+    }
+    t->cursor = (t->cursor + count) % t->n;
+    t->size = (t->size + count < t->n) ? t->size + count : t->n;
+    return 0;
+}
+
+/* Priority of one TD error.  "GPU-Resident Prioritized Experience Replay",
+ * section "Priority update" (|td| to the power alpha, plus epsilon; read here
+ * as (|td| + eps)^alpha, evaluated in f64 and rounded once to f32) and
+ * section "Error Handling & Fallback" (NaN/Inf are clamped: NaN to the td = 0
+ * value, the lowest priority; Inf to the running max at batch start). */
+static float priority_of(const pero_t* t, float td, float max_at_start) {
+    float x = fabsf(td);
+    if (isnan(x)) return (float)pow(t->eps, t->alpha);
+    if (isinf(x)) return max_at_start;
+    return (float)pow((double)x + t->eps, t->alpha);
+}
+
+/* Batch update, element by element in batch order so that a later position
+ * of a repeated index wins; each element walks its leaf-to-root path
+ * ("Putting prioritized replay's segment tree on a GPU", section "Second
+ * Port: Make the Update GPU-Shaped", the per-element propagation it starts
+ * from). */
+int pero_update(pero_t* t, int64_t B, const int64_t* idx, const float* td) {
+    if (B < 0) return -1;
+    const float max_at_start = t->maxp;
+    for (int64_t b = 0; b < B; ++b) {
+        int64_t slot = idx[b];
+        if (slot < 0 || slot >= t->size) continue;
+        float p = priority_of(t, td[b], max_at_start);
+        if (p > t->maxp) t->maxp = p;
+        set_leaf(t, slot, p);
+    }
+    return 0;
+}
+
+/* One descent for mass m in [0, total).  "Putting prioritized replay's
+ * segment tree on a GPU", section "Sampling Is a Descent": if the left
+ * child's sum exceeds the remaining mass go left, otherwise subtract it and
+ * go right.  Reading: the mass is carried in f32 and a zero right child
+ * also sends the walk left. */
+static int64_t descend(const pero_t* t, float m) {
+    int64_t i = 1;
+    while (i < t->n) {
+        float l = t->sum[2 * i];
+        float r = t->sum[2 * i + 1];
+        if (l > m || r == 0.0f) {
+            i = 2 * i;
+        } else {
+            m = m - l;
+            i = 2 * i + 1;
+        }
+    }
+    return i - t->n;
+}
+
+/* "GPU-Resident Prioritized Experience Replay", section "Sampling Kernels":
+ * masses in [0, total), one search per sample, gather of the sampled rows,
+ * then IS weights.  The weight is (N*P(i))^-beta normalised by its largest
+ * value, which belongs to the minimum priority (the min tree serves this
+ * normalisation: "The Tree Under Every Prioritized Replay"). */
+int pero_sample(const pero_t* t, int64_t B, const float* u, double beta, int64_t* idx_out,
+                float* w_out, float* states_out, float* next_states_out,
+                uint32_t* actions_out, float* rewards_out, uint8_t* dones_out) {
+    if (B < 0) return -1;
+    if (B == 0) return 0;
+    if (t->size == 0) return -3;
+    const float total = t->sum[1];
+    const float pmin = t->mn[1];
+    const double N = (double)t->size;
+    const int64_t D = t->D;
+    for (int64_t b = 0; b < B; ++b) {
+        float m = u[b] * total;
+        if (!(m < total)) m = nextafterf(total, 0.0f);
+        int64_t slot = descend(t, m);
+        idx_out[b] = slot;
+        if (w_out) {
+            float p = t->sum[t->n + slot];
+            if (pmin > 0.0f) {
+                double P_i = (double)p / (double)total;
+                double P_min = (double)pmin / (double)total;
+                w_out[b] = (float)(pow(N * P_i, -beta) / pow(N * P_min, -beta));
+            } else {
+                w_out[b] = 0.0f;
+            }
+        }
+        if (D > 0 && states_out) {
+            memcpy(states_out + b * D, t->states + slot * D, sizeof(float) * D);
+            memcpy(next_states_out + b * D, t->next_states + slot * D, sizeof(float) * D);
+            actions_out[b] = t->actions[slot];
+            rewards_out[b] = t->rewards[slot];
+            dones_out[b] = t->dones[slot];
+        }
+    }
+    return 0;
+}
+
+float pero_total(const pero_t* t) { return t->sum[1]; }
+float pero_min(const pero_t* t) { return t->mn[1]; }
+float pero_max_priority(const pero_t* t) { return t->maxp; }
+int64_t pero_size(const pero_t* t) { return t->size; }
+int64_t pero_cursor(const pero_t* t) { return t->cursor; }
+int64_t pero_capacity(const pero_t* t) { return t->n; }
+int32_t pero_state_dim(const pero_t* t) { return t->D; }
+const float* pero_sum_tree(const pero_t* t) { return t->sum; }
+const float* pero_min_tree(const pero_t* t) { return t->mn; }
