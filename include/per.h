@@ -1,0 +1,175 @@
+/*
+ * per.h -- C ABI of the MI355X (gfx950) prioritized-replay sum tree.
+ *
+ * A flat implicit sum tree and a twin min tree over 2n f32 nodes ("Putting
+ * prioritized replay's segment tree on a GPU", section "The Tree Under Every
+ * Prioritized Replay": leaves at [n, 2n), node i has children 2i and 2i+1,
+ * internal nodes hold the sum -- or, in the twin tree, the min -- of their
+ * children, the root at index 1), plus ring storage of transitions
+ * ("GPU-Resident Prioritized Experience Replay", section "Architecture").
+ *
+ * Conventions shared by every entry point
+ *  - Pointers prefixed d_ are device pointers (HBM of the device the handle
+ *    was created on).  Every device buffer is owned by the caller; the
+ *    library never allocates or frees device memory.
+ *  - Work is enqueued on the caller's stream and is ordered by it; no entry
+ *    point synchronises the host with the device.  Inputs must stay alive and
+ *    unchanged, and outputs untouched, until the stream has passed the call.
+ *  - Host-side checks happen before anything is enqueued: on an error return
+ *    nothing was enqueued and the handle is unchanged.
+ *  - A handle may be used from one host thread at a time, and calls on one
+ *    handle must go to streams that are ordered with respect to each other.
+ *  - Return codes: PER_OK, or a negative PER_E* code; per_last_error() then
+ *    describes the failure (text is per host thread).
+ *  - Numerics: every f32 tree node is recomputed as the round-to-nearest f32
+ *    sum (min) of its two children, never by adding a delta, so the trees are
+ *    a pure function of the leaves; no flush-to-zero, no fused multiply-add.
+ */
+#ifndef PER_H
+#define PER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PER_OK 0
+#define PER_EINVAL (-1) /* an argument is out of range or a required pointer is NULL */
+#define PER_ENOSPC (-2) /* the workspace is smaller than per_workspace_bytes() */
+#define PER_EEMPTY (-3) /* sampling from a buffer that holds no transition */
+#define PER_EHIP (-4)   /* the HIP runtime reported an error (see per_last_error) */
+
+#define PER_MAX_CAPACITY (1LL << 30)
+#define PER_MAX_BATCH (1LL << 24)
+
+typedef struct per_s per_t;
+
+/*
+ * Bytes of device workspace a handle needs: both trees (2 x 2n f32), a small
+ * control block (running max priority, completion counters) and the scratch
+ * the batched update uses for batches of up to max_batch entries.
+ * capacity: number of leaves, a power of two in [2, PER_MAX_CAPACITY].
+ * max_batch: largest B later passed to per_update / per_sample, in
+ * [1, PER_MAX_BATCH].  Writes *out and returns PER_OK, or PER_EINVAL.
+ */
+int per_workspace_bytes(int64_t capacity, int64_t max_batch, size_t* out);
+
+/*
+ * Creates a handle over caller-owned memory and enqueues the initialisation
+ * of the trees on `stream`: every sum node 0, every min node +inf (the
+ * neutral elements, so empty slots never count), running max priority 1.0;
+ * size = cursor = 0.
+ *  d_ws / ws_bytes: device workspace, 256-byte aligned, at least
+ *    per_workspace_bytes(capacity, max_batch) bytes (else PER_ENOSPC).
+ *  alpha, eps: priority exponent and offset, p = (|td| + eps)^alpha
+ *    ("GPU-Resident Prioritized Experience Replay", section "Priority
+ *    update"); alpha > 0, eps >= 0, both finite.
+ *  state_dim: floats per state row, >= 0.  With state_dim > 0 the five
+ *    storage arrays (section "Architecture" of the same page) must all be
+ *    given: d_states and d_next_states [capacity x state_dim] f32 row-major,
+ *    16-byte aligned; d_actions [capacity] u32; d_rewards [capacity] f32;
+ *    d_dones [capacity] u8.  With state_dim == 0 they must all be NULL and the
+ *    handle keeps priorities only.  The storage must outlive the handle.
+ * On success *out receives the handle (free with per_destroy).
+ */
+int per_create(per_t** out, int64_t capacity, int32_t state_dim, int64_t max_batch,
+               double alpha, double eps, void* d_ws, size_t ws_bytes, float* d_states,
+               float* d_next_states, uint32_t* d_actions, float* d_rewards,
+               uint8_t* d_dones, hipStream_t stream);
+
+/* Frees the host-side handle only (no device work, no synchronisation). */
+int per_destroy(per_t* h);
+
+/*
+ * Ring intake ("GPU-Resident Prioritized Experience Replay", section
+ * "Experience Insertion"; overflow overwrites the oldest slots, section
+ * "Error Handling & Fallback").  Transition j of the call goes to slot
+ * (cursor + j) mod capacity; afterwards cursor = (cursor + count) mod
+ * capacity and size = min(size + count, capacity).
+ *  count in [0, capacity] (0 enqueues nothing).
+ *  Rows: d_states / d_next_states [count x state_dim] f32 (16-byte aligned),
+ *    d_actions / d_rewards / d_dones [count]; required when the handle has
+ *    storage, ignored otherwise.
+ *  d_prio: [count] f32 priorities, finite and >= 0 (-0.0 is stored as +0.0;
+ *    not checked on the device).  NULL gives every new slot the running max
+ *    priority (the new items' priority at the time the stream runs the call).
+ *    Given priorities raise the running max to their maximum.
+ */
+int per_add(per_t* h, int64_t count, const float* d_states, const float* d_next_states,
+            const uint32_t* d_actions, const float* d_rewards, const uint8_t* d_dones,
+            const float* d_prio, hipStream_t stream);
+
+/*
+ * Batched priority update ("GPU-Resident Prioritized Experience Replay",
+ * sections "Priority update" and "Error Handling & Fallback"; the batch
+ * update of "Putting prioritized replay's segment tree on a GPU", section
+ * "Second Port: Make the Update GPU-Shaped", with the level-synchronous
+ * dependency rule of section "The Race Condition Worth Writing Down").
+ *  B in [0, max_batch]; d_idx [B] i64 slot indices; d_td [B] f32 TD errors.
+ * The result equals applying the entries one by one in batch order: for a
+ * slot repeated in the batch the last position wins.  Entry b sets slot
+ * d_idx[b] to p = f32(pow_f64(|td| + eps, alpha)); NaN td gives the td = 0
+ * value and +/-Inf td the running max priority as of the start of the call.
+ * Indices outside [0, size) are skipped (defined, not an error).  The
+ * running max priority becomes the max of itself and every p of the call.
+ */
+int per_update(per_t* h, int64_t B, const int64_t* d_idx, const float* d_td,
+               hipStream_t stream);
+
+/*
+ * Batched proportional sample ("Putting prioritized replay's segment tree on a
+ * GPU", section "Sampling Is a Descent"; importance weights and gather,
+ * "GPU-Resident Prioritized Experience Replay", section "Sampling Kernels";
+ * writing straight into caller buffers, "True Single-Graph Implementation
+ * Plan", Task 3).
+ *  B in [0, max_batch]; PER_EEMPTY if size == 0 (checked on the host).
+ *  d_u [B] f32 uniforms in [0, 1) (unchecked).  Sample b uses the mass
+ *    m = f32(u_b * total), clamped below total, and walks from the root: if
+ *    the left child's sum exceeds m, or the right child's sum is 0, go left;
+ *    otherwise m = f32(m - left) and go right.
+ *  d_idx_out [B] i64: sampled slots (required).
+ *  d_w_out [B] f32 or NULL: w_b = f32((N*P_b)^-beta / (N*P_min)^-beta) in
+ *    f64, N = size, P_b = p_b / total, P_min = min-tree root / total; 0 when
+ *    the min priority is 0.
+ *  Row outputs (all NULL, or all given when the handle has storage):
+ *    d_states_out / d_next_states_out [B x state_dim] f32 (16-byte aligned),
+ *    d_actions_out [B] u32, d_rewards_out [B] f32, d_dones_out [B] u8: byte
+ *    copies of the sampled slots.
+ * Preconditions (unchecked): total finite and > 0.
+ */
+int per_sample(per_t* h, int64_t B, const float* d_u, double beta, int64_t* d_idx_out,
+               float* d_w_out, float* d_states_out, float* d_next_states_out,
+               uint32_t* d_actions_out, float* d_rewards_out, uint8_t* d_dones_out,
+               hipStream_t stream);
+
+/*
+ * Enqueue a 4-byte device copy of the sum-tree root (total priority), the
+ * min-tree root (min priority over written slots; +inf when empty) or the
+ * running max priority into d_out.  The caller synchronises to read it.
+ */
+int per_total(per_t* h, float* d_out, hipStream_t stream);
+int per_min(per_t* h, float* d_out, hipStream_t stream);
+int per_max_priority(per_t* h, float* d_out, hipStream_t stream);
+
+/* Host-side state: number of written slots, next slot to write, capacity,
+ * floats per state row.  -1 for a NULL handle. */
+int64_t per_size(const per_t* h);
+int64_t per_cursor(const per_t* h);
+int64_t per_capacity(const per_t* h);
+int32_t per_state_dim(const per_t* h);
+
+/* Read-only device pointers to the two [2 x capacity] f32 trees (index 0
+ * unused), for inspection after the stream has passed the writing calls. */
+int per_tree_ptrs(const per_t* h, const float** d_sum, const float** d_min);
+
+/* Text of the last error on this host thread ("" if none). */
+const char* per_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PER_H */

@@ -1,0 +1,298 @@
+// per_api.hip -- the C ABI declared in include/per.h: argument checks,
+// workspace layout, handle state and kernel launches.  Nothing here
+// allocates device memory or waits for the device.
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <cstdlib>
+#include <new>
+#include <string>
+
+#include "../../include/per.h"
+#include "per_internal.h"
+
+struct per_s {
+  per::Geom g;
+  int64_t max_batch;
+  double alpha, eps;
+  per::TreePtrs t;
+  per::Buckets bk;
+  per::Storage st;
+  int64_t size, cursor;
+  int device;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return PER_OK;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(PER_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+int log2i(int64_t v) {
+  int l = 0;
+  while ((int64_t(1) << l) < v) ++l;
+  return l;
+}
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+int check_capacity(int64_t capacity) {
+  if (!pow2(capacity) || capacity < 2 || capacity > PER_MAX_CAPACITY)
+    return fail(PER_EINVAL, "capacity %lld is not a power of two in [2, 2^30]",
+                (long long)capacity);
+  return PER_OK;
+}
+
+int check_batch_limit(int64_t max_batch) {
+  if (max_batch < 1 || max_batch > PER_MAX_BATCH)
+    return fail(PER_EINVAL, "max_batch %lld outside [1, 2^24]", (long long)max_batch);
+  return PER_OK;
+}
+
+per::Geom make_geom(int64_t capacity) {
+  per::Geom g;
+  g.n = (uint32_t)capacity;
+  g.L = log2i(capacity);
+  g.S = g.L < per::kMaxSpanBits ? g.L : per::kMaxSpanBits;
+  g.P = g.L - g.S;
+  return g;
+}
+
+}  // namespace
+
+namespace per {
+
+Layout workspace_layout(int64_t n, int64_t max_batch) {
+  const Geom g = make_geom(n);
+  const size_t np = size_t(1) << g.P;
+  Layout l;
+  size_t o = 0;
+  l.sum = o;
+  o = align256(o + sizeof(float) * 2 * (size_t)n);
+  l.mn = o;
+  o = align256(o + sizeof(float) * 2 * (size_t)n);
+  l.ctrl = o;
+  o = align256(o + sizeof(Ctrl));
+  l.counts = o;
+  o = align256(o + sizeof(uint32_t) * np);
+  l.fill = o;
+  o = align256(o + sizeof(uint32_t) * np);
+  l.offs = o;
+  o = align256(o + sizeof(uint32_t) * (np + 1));
+  l.slot = o;
+  o = align256(o + sizeof(uint32_t) * (size_t)max_batch);
+  l.pos = o;
+  o = align256(o + sizeof(uint32_t) * (size_t)max_batch);
+  l.td = o;
+  o = align256(o + sizeof(float) * (size_t)max_batch);
+  l.total = o;
+  return l;
+}
+
+}  // namespace per
+
+extern "C" {
+
+int per_workspace_bytes(int64_t capacity, int64_t max_batch, size_t* out) {
+  if (!out) return fail(PER_EINVAL, "out is NULL");
+  int rc = check_capacity(capacity);
+  if (rc) return rc;
+  rc = check_batch_limit(max_batch);
+  if (rc) return rc;
+  *out = per::workspace_layout(capacity, max_batch).total;
+  return ok();
+}
+
+int per_create(per_t** out, int64_t capacity, int32_t state_dim, int64_t max_batch,
+               double alpha, double eps, void* d_ws, size_t ws_bytes, float* d_states,
+               float* d_next_states, uint32_t* d_actions, float* d_rewards,
+               uint8_t* d_dones, hipStream_t stream) {
+  if (!out) return fail(PER_EINVAL, "out is NULL");
+  *out = nullptr;
+  int rc = check_capacity(capacity);
+  if (rc) return rc;
+  rc = check_batch_limit(max_batch);
+  if (rc) return rc;
+  if (state_dim < 0) return fail(PER_EINVAL, "state_dim %d < 0", (int)state_dim);
+  if (!(alpha > 0.0) || !(alpha < 1e300) || !(eps >= 0.0) || !(eps < 1e300))
+    return fail(PER_EINVAL, "alpha must be finite and > 0, eps finite and >= 0");
+  if (!d_ws) return fail(PER_EINVAL, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(d_ws) & 255u)
+    return fail(PER_EINVAL, "workspace is not 256-byte aligned");
+  const per::Layout lay = per::workspace_layout(capacity, max_batch);
+  if (ws_bytes < lay.total)
+    return fail(PER_ENOSPC, "workspace of %zu bytes, %zu needed", ws_bytes, lay.total);
+  const bool any_storage = d_states || d_next_states || d_actions || d_rewards || d_dones;
+  const bool all_storage = d_states && d_next_states && d_actions && d_rewards && d_dones;
+  if (state_dim > 0 && !all_storage)
+    return fail(PER_EINVAL, "state_dim > 0 needs all five storage arrays");
+  if (state_dim == 0 && any_storage)
+    return fail(PER_EINVAL, "state_dim == 0 takes no storage arrays");
+  if (state_dim > 0 && ((reinterpret_cast<uintptr_t>(d_states) |
+                         reinterpret_cast<uintptr_t>(d_next_states)) & 15u))
+    return fail(PER_EINVAL, "state arrays must be 16-byte aligned");
+
+  per_s* h = new (std::nothrow) per_s();
+  if (!h) return fail(PER_EINVAL, "out of host memory");
+  h->g = make_geom(capacity);
+  h->max_batch = max_batch;
+  h->alpha = alpha;
+  h->eps = eps;
+  char* base = static_cast<char*>(d_ws);
+  h->t.sum = reinterpret_cast<float*>(base + lay.sum);
+  h->t.mn = reinterpret_cast<float*>(base + lay.mn);
+  h->t.ctrl = reinterpret_cast<per::Ctrl*>(base + lay.ctrl);
+  h->bk.counts = reinterpret_cast<uint32_t*>(base + lay.counts);
+  h->bk.fill = reinterpret_cast<uint32_t*>(base + lay.fill);
+  h->bk.offs = reinterpret_cast<uint32_t*>(base + lay.offs);
+  h->bk.slot = reinterpret_cast<uint32_t*>(base + lay.slot);
+  h->bk.pos = reinterpret_cast<uint32_t*>(base + lay.pos);
+  h->bk.td = reinterpret_cast<float*>(base + lay.td);
+  h->st.states = d_states;
+  h->st.next_states = d_next_states;
+  h->st.actions = d_actions;
+  h->st.rewards = d_rewards;
+  h->st.dones = d_dones;
+  h->st.D = state_dim;
+  h->size = 0;
+  h->cursor = 0;
+  if (hipGetDevice(&h->device) != hipSuccess) h->device = -1;
+  hipError_t e = per::launch_init(h->t, h->bk, h->g, stream);
+  if (e != hipSuccess) {
+    delete h;
+    return hip_fail(e, "per_create: init launch");
+  }
+  *out = h;
+  return ok();
+}
+
+int per_destroy(per_t* h) {
+  if (!h) return fail(PER_EINVAL, "handle is NULL");
+  delete h;
+  return ok();
+}
+
+int per_add(per_t* h, int64_t count, const float* d_states, const float* d_next_states,
+            const uint32_t* d_actions, const float* d_rewards, const uint8_t* d_dones,
+            const float* d_prio, hipStream_t stream) {
+  if (!h) return fail(PER_EINVAL, "handle is NULL");
+  if (count < 0 || count > (int64_t)h->g.n)
+    return fail(PER_EINVAL, "count %lld outside [0, capacity]", (long long)count);
+  if (count == 0) return ok();
+  if (h->st.D > 0) {
+    if (!(d_states && d_next_states && d_actions && d_rewards && d_dones))
+      return fail(PER_EINVAL, "the handle has storage: all five row arrays are required");
+    if ((reinterpret_cast<uintptr_t>(d_states) | reinterpret_cast<uintptr_t>(d_next_states)) &
+        15u)
+      return fail(PER_EINVAL, "state rows must be 16-byte aligned");
+  }
+  hipError_t e = per::launch_add(h->t, h->g, h->st, (uint32_t)h->cursor, (uint32_t)count,
+                                 d_states, d_next_states, d_actions, d_rewards, d_dones,
+                                 d_prio, stream);
+  if (e != hipSuccess) return hip_fail(e, "per_add");
+  h->cursor = (h->cursor + count) % (int64_t)h->g.n;
+  h->size = (h->size + count < (int64_t)h->g.n) ? h->size + count : (int64_t)h->g.n;
+  return ok();
+}
+
+int per_update(per_t* h, int64_t B, const int64_t* d_idx, const float* d_td,
+               hipStream_t stream) {
+  if (!h) return fail(PER_EINVAL, "handle is NULL");
+  if (B < 0 || B > h->max_batch)
+    return fail(PER_EINVAL, "B %lld outside [0, max_batch=%lld]", (long long)B,
+                (long long)h->max_batch);
+  if (B == 0) return ok();
+  if (!d_idx || !d_td) return fail(PER_EINVAL, "idx and td are required");
+  hipError_t e = per::launch_update(h->t, h->bk, h->g, (uint32_t)h->size, B, d_idx, d_td,
+                                    h->alpha, h->eps, stream);
+  if (e != hipSuccess) return hip_fail(e, "per_update");
+  return ok();
+}
+
+int per_sample(per_t* h, int64_t B, const float* d_u, double beta, int64_t* d_idx_out,
+               float* d_w_out, float* d_states_out, float* d_next_states_out,
+               uint32_t* d_actions_out, float* d_rewards_out, uint8_t* d_dones_out,
+               hipStream_t stream) {
+  if (!h) return fail(PER_EINVAL, "handle is NULL");
+  if (B < 0 || B > h->max_batch)
+    return fail(PER_EINVAL, "B %lld outside [0, max_batch=%lld]", (long long)B,
+                (long long)h->max_batch);
+  if (B == 0) return ok();
+  if (!d_u || !d_idx_out) return fail(PER_EINVAL, "u and idx_out are required");
+  if (!(beta >= 0.0) || !(beta < 1e300)) return fail(PER_EINVAL, "beta must be finite, >= 0");
+  const bool any_rows = d_states_out || d_next_states_out || d_actions_out || d_rewards_out ||
+                        d_dones_out;
+  const bool all_rows = d_states_out && d_next_states_out && d_actions_out && d_rewards_out &&
+                        d_dones_out;
+  if (any_rows && !all_rows) return fail(PER_EINVAL, "row outputs go all together");
+  if (any_rows && h->st.D == 0) return fail(PER_EINVAL, "the handle keeps no rows");
+  if (any_rows && ((reinterpret_cast<uintptr_t>(d_states_out) |
+                    reinterpret_cast<uintptr_t>(d_next_states_out)) & 15u))
+    return fail(PER_EINVAL, "state outputs must be 16-byte aligned");
+  if (h->size == 0) return fail(PER_EEMPTY, "sample from an empty buffer");
+  const per::SamplePlan plan = per::make_sample_plan(h->g, B);
+  hipError_t e = per::launch_sample(h->t, h->g, h->st, plan, (uint32_t)h->size, B, d_u, beta,
+                                    d_idx_out, d_w_out, any_rows ? d_states_out : nullptr,
+                                    d_next_states_out, d_actions_out, d_rewards_out,
+                                    d_dones_out, stream);
+  if (e != hipSuccess) return hip_fail(e, "per_sample");
+  return ok();
+}
+
+static int copy_scalar(per_t* h, const void* src, float* d_out, hipStream_t stream,
+                       const char* what) {
+  if (!h) return fail(PER_EINVAL, "handle is NULL");
+  if (!d_out) return fail(PER_EINVAL, "out is NULL");
+  hipError_t e = hipMemcpyAsync(d_out, src, sizeof(float), hipMemcpyDeviceToDevice, stream);
+  if (e != hipSuccess) return hip_fail(e, what);
+  return ok();
+}
+
+int per_total(per_t* h, float* d_out, hipStream_t stream) {
+  return copy_scalar(h, h ? h->t.sum + 1 : nullptr, d_out, stream, "per_total");
+}
+
+int per_min(per_t* h, float* d_out, hipStream_t stream) {
+  return copy_scalar(h, h ? h->t.mn + 1 : nullptr, d_out, stream, "per_min");
+}
+
+int per_max_priority(per_t* h, float* d_out, hipStream_t stream) {
+  return copy_scalar(h, h ? &h->t.ctrl->maxp : nullptr, d_out, stream, "per_max_priority");
+}
+
+int64_t per_size(const per_t* h) { return h ? h->size : -1; }
+int64_t per_cursor(const per_t* h) { return h ? h->cursor : -1; }
+int64_t per_capacity(const per_t* h) { return h ? (int64_t)h->g.n : -1; }
+int32_t per_state_dim(const per_t* h) { return h ? h->st.D : -1; }
+
+int per_tree_ptrs(const per_t* h, const float** d_sum, const float** d_min) {
+  if (!h || !d_sum || !d_min) return fail(PER_EINVAL, "NULL argument");
+  *d_sum = h->t.sum;
+  *d_min = h->t.mn;
+  return ok();
+}
+
+const char* per_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

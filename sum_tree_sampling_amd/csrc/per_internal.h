@@ -1,0 +1,101 @@
+// per_internal.h -- shared definitions of the HIP sum-tree library (not
+// installed; the public ABI is include/per.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace per {
+
+// Leaves per partition = 2^kMaxSpanBits.  The batched update and the intake
+// work one workgroup per partition (an aligned subtree) and finish the few
+// levels above the partitions in the last workgroup to complete.
+constexpr int kMaxSpanBits = 12;
+constexpr int kMaxSpan = 1 << kMaxSpanBits;
+// Partitions holding at most this many updated leaves are repaired by one
+// wave walking the leaf-to-partition-root chains; denser ones are rebuilt
+// in LDS.
+constexpr int kSparseMax = 64;
+// Top levels (above the partitions) that fit in the workgroup's LDS.
+constexpr int kMaxTopBits = 12;
+constexpr int kTreeThreads = 256;
+
+// Device control block at the start of the workspace's control area.
+struct Ctrl {
+  float maxp;              // running max priority
+  uint32_t ticket;         // completion counter of the partition kernels
+  uint32_t batch_max;      // max priority written by the running call, f32 bits + 1 (0 = none)
+  uint32_t pad0;
+};
+
+// Geometry shared by host and kernels.
+struct Geom {
+  uint32_t n;      // capacity (leaves)
+  int L;           // log2(n)
+  int S;           // leaves per partition = 2^S, S = min(L, kMaxSpanBits)
+  int P;           // partitions = 2^P, P = L - S
+};
+
+struct TreePtrs {
+  float* sum;      // [2n]
+  float* mn;       // [2n]
+  Ctrl* ctrl;
+};
+
+// Scratch of the bucketed (large-batch) update.
+struct Buckets {
+  uint32_t* counts;   // [2^P] entries per partition
+  uint32_t* fill;     // [2^P] fill cursors
+  uint32_t* offs;     // [2^P + 1] exclusive prefix of counts
+  uint32_t* slot;     // [max_batch] leaf slot of each bucketed entry
+  uint32_t* pos;      // [max_batch] its batch position
+  float* td;          // [max_batch] its TD error
+};
+
+struct Storage {
+  float* states;
+  float* next_states;
+  uint32_t* actions;
+  float* rewards;
+  uint8_t* dones;
+  int D;
+};
+
+// Workspace layout (byte offsets from the 256-byte aligned base).
+struct Layout {
+  size_t sum, mn, ctrl, counts, fill, offs, slot, pos, td, total;
+};
+Layout workspace_layout(int64_t n, int64_t max_batch);
+
+// Descent plan of the sampler.
+constexpr int kMaxRounds = 12;
+struct SamplePlan {
+  int mode;                 // kernel variant (group size, values per lane)
+  int top_levels;           // levels walked in the LDS copy of the tree top
+  int nrounds;              // global rounds after the LDS top
+  int rounds[kMaxRounds];   // levels per round
+};
+
+// ----------------------------------------------------------------- launchers
+hipError_t launch_init(const TreePtrs& t, const Buckets& bk, const Geom& g, hipStream_t s);
+
+// Batched update; B > 0.
+hipError_t launch_update(const TreePtrs& t, const Buckets& bk, const Geom& g, uint32_t size,
+                         int64_t B, const int64_t* idx, const float* td, double alpha,
+                         double eps, hipStream_t s);
+
+// Ring intake of count > 0 items at cursor.
+hipError_t launch_add(const TreePtrs& t, const Geom& g, const Storage& st, uint32_t cursor,
+                      uint32_t count, const float* states, const float* next_states,
+                      const uint32_t* actions, const float* rewards, const uint8_t* dones,
+                      const float* prio, hipStream_t s);
+
+hipError_t launch_sample(const TreePtrs& t, const Geom& g, const Storage& st,
+                         const SamplePlan& plan, uint32_t size, int64_t B, const float* u,
+                         double beta, int64_t* idx_out, float* w_out, float* states_out,
+                         float* next_out, uint32_t* actions_out, float* rewards_out,
+                         uint8_t* dones_out, hipStream_t s);
+
+SamplePlan make_sample_plan(const Geom& g, int64_t B);
+
+}  // namespace per

@@ -1,0 +1,330 @@
+// sample_kernels.hip -- batched proportional sampling on gfx950: root-to-leaf
+// descent, importance-sampling weights and the gather of the sampled rows,
+// fused in one kernel.
+//
+// Descent rule ("Putting prioritized replay's segment tree on a GPU",
+// section "Sampling Is a Descent"): at each node, if the left child's sum
+// exceeds the remaining mass m (or the right child's sum is 0) go left,
+// otherwise m = f32(m - left) and go right.
+//
+// Layout of the work: a group of G lanes (G = 64: one wave per sample; G = 1:
+// one lane per sample) carries one sample.  The top K levels are walked in an
+// LDS copy of the tree top (nodes [1, 2^(K+1))), staged once per block.  The
+// rest is covered in rounds: a round of R levels below node c loads the 2^R
+// contiguous descendants of c at depth +R (G lanes x V values, 16-byte
+// vector loads), rebuilds the R-1 intermediate levels by pairwise adds --
+// bit-identical to the stored nodes, since every stored node is exactly the
+// f32 sum of its children -- and takes all R decisions from registers.  A
+// round is one dependent trip to memory instead of R.
+//
+// Weights ("GPU-Resident Prioritized Experience Replay", section "Sampling
+// Kernels"): w = (N*P(i))^-beta normalised by the weight of the min-tree root
+// priority, in f64.  Rows are copied by the whole wave, 16 bytes per lane per
+// access, straight into the caller's buffers ("True Single-Graph
+// Implementation Plan", Task 3).
+
+#include <cstdlib>
+
+#include "per_internal.h"
+
+namespace per {
+namespace {
+
+constexpr int kSampleThreads = 256;
+constexpr int kMaxTopLevels = 12;
+
+struct SampleArgs {
+  const float* sum;
+  const float* mn;
+  uint32_t n;
+  uint32_t size;
+  uint32_t B;
+  const float* u;
+  double beta;
+  int64_t* idx_out;
+  float* w_out;
+  float* states_out;
+  float* next_out;
+  uint32_t* actions_out;
+  float* rewards_out;
+  uint8_t* dones_out;
+  Storage st;
+  int top;
+  int nrounds;
+  int rounds[kMaxRounds];
+};
+
+// Pairwise (heap-order) sum of LEN register values: the value of their
+// common ancestor node.
+template <int LEN>
+__device__ __forceinline__ float pair_sum(const float* x) {
+  if constexpr (LEN == 1) {
+    return x[0];
+  } else {
+    return pair_sum<LEN / 2>(x) + pair_sum<LEN / 2>(x + LEN / 2);
+  }
+}
+
+// Descent through the V values one lane holds (the bottom log2(V) levels of
+// a round).  Returns the chosen offset; leaf receives its value.
+template <int V>
+__device__ __forceinline__ int lane_descent(const float* x, float& m, float& leaf) {
+  if constexpr (V == 1) {
+    leaf = x[0];
+    return 0;
+  } else {
+    constexpr int H = V / 2;
+    const float ls = pair_sum<H>(x), rs = pair_sum<H>(x + H);
+    const bool right = !(ls > m || rs == 0.0f);
+    if (right) m = m - ls;
+    float y[H];
+#pragma unroll
+    for (int i = 0; i < H; ++i) y[i] = right ? x[H + i] : x[i];
+    return (right ? H : 0) + lane_descent<H>(y, m, leaf);
+  }
+}
+
+template <int V>
+__device__ __forceinline__ void load_values(const float* p, float* x) {
+  if constexpr (V == 1) {
+    x[0] = p[0];
+  } else if constexpr (V == 2) {
+    const float2 q = *reinterpret_cast<const float2*>(p);
+    x[0] = q.x;
+    x[1] = q.y;
+  } else {
+#pragma unroll
+    for (int i = 0; i < V; i += 4) {
+      const float4 q = *reinterpret_cast<const float4*>(p + i);
+      x[i] = q.x;
+      x[i + 1] = q.y;
+      x[i + 2] = q.z;
+      x[i + 3] = q.w;
+    }
+  }
+}
+
+constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v / 2); }
+
+template <int G, int V>
+__global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleArgs a) {
+  extern __shared__ float top[];  // nodes [0, 2^(K+1)) of the sum tree
+  constexpr int LOGG = ilog2(G);
+  constexpr int LOGV = ilog2(V);
+  constexpr int SPW = 64 / G;  // samples per wave
+
+  const int lane = threadIdx.x & 63;
+  const int j = lane & (G - 1);
+  const int gbase = lane & ~(G - 1);
+  const uint32_t wave = blockIdx.x * (kSampleThreads / 64) + (threadIdx.x >> 6);
+  const uint32_t b = wave * SPW + (uint32_t)(lane / G);
+  const bool active = b < a.B;
+
+  if (a.top > 0) {
+    const uint32_t cnt = 1u << (a.top + 1);  // multiple of 4 (top >= 1)
+    for (uint32_t i = threadIdx.x * 4; i < cnt; i += kSampleThreads * 4)
+      *reinterpret_cast<float4*>(top + i) = *reinterpret_cast<const float4*>(a.sum + i);
+    __syncthreads();
+  }
+
+  const float T = a.sum[1];
+  float m = active ? a.u[b] * T : 0.0f;
+  if (!(m < T)) m = __uint_as_float(__float_as_uint(T) - 1u);  // largest f32 below T
+
+  uint32_t node = 1;
+  for (int l = 0; l < a.top; ++l) {
+    const float2 c = reinterpret_cast<const float2*>(top)[node];  // children 2node, 2node+1
+    const bool right = !(c.x > m || c.y == 0.0f);
+    if (right) m = m - c.x;
+    node = 2 * node + (right ? 1u : 0u);
+  }
+  float leaf = 0.0f;
+  if (a.nrounds == 0) leaf = top[node];
+
+  for (int r = 0; r < a.nrounds; ++r) {
+    const int R = a.rounds[r];
+    const int lg = R - LOGV;  // log2 of the lanes used this round (<= LOGG)
+    const uint32_t base = node << R;
+    const bool used = j < (1 << lg);
+    float x[V];
+    if (used) {
+      load_values<V>(a.sum + base + (uint32_t)j * V, x);
+    } else {
+#pragma unroll
+      for (int i = 0; i < V; ++i) x[i] = 0.0f;
+    }
+    float v = pair_sum<V>(x);
+    float lrec[LOGG + 1], rrec[LOGG + 1];
+#pragma unroll
+    for (int s = 1; s <= LOGG; ++s) {
+      lrec[s] = rrec[s] = 0.0f;
+      if (s <= lg) {
+        const float pv = __shfl_xor(v, 1 << (s - 1));
+        const bool hi = (j >> (s - 1)) & 1;
+        lrec[s] = hi ? pv : v;
+        rrec[s] = hi ? v : pv;
+        v = lrec[s] + rrec[s];
+      }
+    }
+    bool on = used;
+#pragma unroll
+    for (int s = LOGG; s >= 1; --s) {
+      if (s <= lg) {
+        const bool right = !(lrec[s] > m || rrec[s] == 0.0f);
+        if (right) m = m - lrec[s];
+        on = on && (((j >> (s - 1)) & 1) == (right ? 1 : 0));
+      }
+    }
+    float lv;
+    const int e = lane_descent<V>(x, m, lv);
+    uint32_t pos = (uint32_t)j * V + (uint32_t)e;
+    if constexpr (G > 1) {
+      const uint64_t mask = __ballot(on);
+      const uint64_t gm = (G == 64) ? mask : ((mask >> gbase) & ((1ull << G) - 1ull));
+      const int src = gbase + (gm ? (__ffsll((unsigned long long)gm) - 1) : 0);
+      m = __shfl(m, src);
+      pos = (uint32_t)__shfl((int)pos, src);
+      lv = __shfl(lv, src);
+    }
+    node = base + pos;
+    leaf = lv;
+  }
+
+  const uint32_t slot = node - a.n;
+  if (active && j == 0) {
+    a.idx_out[b] = (int64_t)slot;
+    if (a.w_out) {
+      const float pmin = a.mn[1];
+      float w = 0.0f;
+      if (pmin > 0.0f) {
+        const double N = (double)a.size;
+        const double P_i = (double)leaf / (double)T;
+        const double P_min = (double)pmin / (double)T;
+        w = (float)(pow(N * P_i, -a.beta) / pow(N * P_min, -a.beta));
+      }
+      a.w_out[b] = w;
+    }
+    if (a.states_out) {
+      a.actions_out[b] = a.st.actions[slot];
+      a.rewards_out[b] = a.st.rewards[slot];
+      a.dones_out[b] = a.st.dones[slot];
+    }
+  }
+
+  if (a.states_out) {
+    // Wave-cooperative row copy of the wave's SPW samples.
+    const uint32_t D = (uint32_t)a.st.D;
+    const bool vec = (D & 3u) == 0u;
+    const uint32_t per_row = vec ? D / 4 : D;  // accesses per row
+    const uint32_t total = SPW * 2u * per_row;
+    const uint32_t wave_b0 = wave * SPW;
+    for (uint32_t t0 = 0; t0 < total; t0 += 64) {
+      const uint32_t t = t0 + lane;
+      uint32_t s = t / (2u * per_row);
+      if (s >= SPW) s = SPW - 1;
+      const uint32_t slot_s = (uint32_t)__shfl((int)slot, (int)s * G);
+      const uint32_t bs = wave_b0 + s;
+      if (t < total && bs < a.B) {
+        const uint32_t rem = t - s * 2u * per_row;
+        const bool nxt = rem >= per_row;
+        const uint32_t c = nxt ? rem - per_row : rem;
+        const float* src = (nxt ? a.st.next_states : a.st.states) + (uint64_t)slot_s * D;
+        float* dst = (nxt ? a.next_out : a.states_out) + (uint64_t)bs * D;
+        if (vec) {
+          *reinterpret_cast<float4*>(dst + 4u * c) = *reinterpret_cast<const float4*>(src + 4u * c);
+        } else {
+          dst[c] = src[c];
+        }
+      }
+    }
+  }
+}
+
+template <int G, int V>
+hipError_t launch_variant(const SampleArgs& a, hipStream_t s) {
+  constexpr int SPW = 64 / G;
+  const uint64_t waves = (a.B + SPW - 1) / SPW;
+  const unsigned grid = (unsigned)((waves + 3) / 4);
+  const size_t lds = a.top > 0 ? (sizeof(float) << (a.top + 1)) : 0;
+  hipLaunchKernelGGL((sample_kernel<G, V>), dim3(grid), dim3(kSampleThreads), lds, s, a);
+  return hipGetLastError();
+}
+
+// Split `levels` into rounds of lo..hi levels, larger rounds first.
+void split_rounds(int levels, int hi, SamplePlan& p) {
+  p.nrounds = 0;
+  if (levels <= 0) return;
+  const int k = (levels + hi - 1) / hi;
+  const int base = levels / k, extra = levels % k;
+  for (int r = 0; r < k; ++r) p.rounds[p.nrounds++] = base + (r < extra ? 1 : 0);
+}
+
+}  // namespace
+
+// Modes: 1 = one wave per sample (G=64, V=4, rounds up to 8 levels);
+// 2 = 16 lanes per sample (G=16, V=4, up to 6 levels);
+// 3 = one lane per sample (G=1, V=32, rounds of exactly 5 levels).
+SamplePlan make_sample_plan(const Geom& g, int64_t B) {
+  SamplePlan p{};
+  p.mode = (B <= 16384) ? 1 : 3;
+  const char* env = getenv("PER_SAMPLE_MODE");
+  if (env && atoi(env) >= 1 && atoi(env) <= 3) p.mode = atoi(env);
+  if (g.L <= 10) {  // the whole tree fits the LDS copy
+    p.top_levels = g.L;
+    p.nrounds = 0;
+    return p;
+  }
+  int top = 0;
+  if (p.mode == 3) {
+    for (int k = (g.L < kMaxTopLevels ? g.L : kMaxTopLevels); k >= 0; --k)
+      if ((g.L - k) % 5 == 0) {
+        top = k;
+        break;
+      }
+  }
+  const char* envt = getenv("PER_SAMPLE_TOP");
+  if (envt && p.mode != 3) {
+    const int k = atoi(envt);
+    if (k >= 0 && k <= kMaxTopLevels && k <= g.L - 6) top = k;
+  }
+  p.top_levels = top;
+  const int hi = (p.mode == 1) ? 8 : (p.mode == 2 ? 6 : 5);
+  split_rounds(g.L - top, hi, p);
+  return p;
+}
+
+hipError_t launch_sample(const TreePtrs& t, const Geom& g, const Storage& st,
+                         const SamplePlan& plan, uint32_t size, int64_t B, const float* u,
+                         double beta, int64_t* idx_out, float* w_out, float* states_out,
+                         float* next_out, uint32_t* actions_out, float* rewards_out,
+                         uint8_t* dones_out, hipStream_t s) {
+  SampleArgs a{};
+  a.sum = t.sum;
+  a.mn = t.mn;
+  a.n = g.n;
+  a.size = size;
+  a.B = (uint32_t)B;
+  a.u = u;
+  a.beta = beta;
+  a.idx_out = idx_out;
+  a.w_out = w_out;
+  a.states_out = states_out;
+  a.next_out = next_out;
+  a.actions_out = actions_out;
+  a.rewards_out = rewards_out;
+  a.dones_out = dones_out;
+  a.st = st;
+  a.top = plan.top_levels;
+  a.nrounds = plan.nrounds;
+  for (int r = 0; r < kMaxRounds; ++r) a.rounds[r] = plan.rounds[r];
+  switch (plan.mode) {
+    case 2:
+      return launch_variant<16, 4>(a, s);
+    case 3:
+      return launch_variant<1, 32>(a, s);
+    default:
+      return launch_variant<64, 4>(a, s);
+  }
+}
+
+}  // namespace per

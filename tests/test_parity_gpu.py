@@ -1,0 +1,275 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.  Trees, indices, rows and the running max are compared
+bit for bit; IS weights within 1e-6 relative."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import Oracle
+from parity_util import (compare_sample, compare_trees, compare_weights, dev, fill, host, say,
+                         assert_bits_equal)
+
+pytestmark = pytest.mark.gpu
+
+
+def _buf(n, D=0, max_batch=4096, **kw):
+    from sum_tree_sampling_amd import PerBuffer
+    return PerBuffer(n, D, max_batch=max_batch, **kw)
+
+
+# ------------------------------------------------------------ the five workloads
+
+STEPS = {"tiny_1k": 30, "apex_shard_2m": 5, "dqn_1m": 3, "collision_stress_2m": 3}
+
+
+@pytest.mark.parametrize("name", list(STEPS))
+def test_workload_parity(name):
+    s = workloads.spec(name)
+    n, B, D = s["capacity"], s["batch"], s["state_dim"]
+    say("workload", name, "n", n, "B", B, "D", D)
+    o = Oracle(n, D)
+    g = _buf(n, D, max_batch=max(B, 4096))
+    fill(name, o, g)
+    compare_trees(o, g, name + " after fill")
+    inp = workloads.StepInputs(name)
+    rows = D > 0
+    for step in range(STEPS[name]):
+        u = inp.u()
+        ro = o.sample(u, beta=s["beta"], weights=True, rows=rows)
+        rg = g.sample(dev(u), beta=s["beta"], weights=True, rows=rows)
+        compare_sample(rg, ro, "%s step %d sample" % (name, step), rows=rows)
+        idx = inp.update_idx() if "unique" in s else ro["idx"]
+        td = inp.td()
+        o.update(idx, td)
+        g.update(dev(idx), dev(td))
+        compare_trees(o, g, "%s step %d update" % (name, step))
+        if s["intake"]:
+            o.add(s["intake"])
+            g.add(s["intake"])
+            compare_trees(o, g, "%s step %d intake" % (name, step))
+    say("workload", name, "ok")
+
+
+@pytest.mark.parametrize("mode", ["1", "2", "3"])
+def test_sampler_modes_agree(mode, monkeypatch):
+    """Each descent variant (one wave, 16 lanes, one lane per sample) returns
+    the oracle's indices, weights and rows."""
+    monkeypatch.setenv("PER_SAMPLE_MODE", mode)
+    n, D = 1 << 20, 64
+    say("sampler mode", mode)
+    o = Oracle(n, D)
+    g = _buf(n, D, max_batch=20000)
+    fill("dqn_1m", o, g)
+    # non-uniform priorities so that every level matters
+    inp = workloads.StepInputs("dqn_1m", batch=3000)
+    idx = np.arange(0, n, 7, dtype=np.int64)
+    td = np.random.default_rng(5).standard_normal(idx.size).astype(np.float32) * 3
+    o.update(idx, td)
+    for lo in range(0, idx.size, 20000):
+        g.update(dev(idx[lo:lo + 20000]), dev(td[lo:lo + 20000]))
+    compare_trees(o, g, "mode %s prep" % mode)
+    for top in (None, "0", "4", "9"):
+        if top is not None:
+            monkeypatch.setenv("PER_SAMPLE_TOP", top)
+        u = inp.u()
+        u[:3] = [0.0, np.nextafter(np.float32(1), np.float32(0)), 0.5]
+        ro = o.sample(u, beta=0.4, rows=True)
+        rg = g.sample(dev(u), beta=0.4, rows=True)
+        compare_sample(rg, ro, "mode %s top %s" % (mode, top), rows=True)
+
+
+def test_zero_priorities_never_sampled():
+    name = "collision_stress_2m"
+    n = 1 << 21
+    say("zeros", name)
+    o = Oracle(n)
+    g = _buf(n)
+    pr = fill(name, o, g)
+    rng = np.random.default_rng(3)
+    for mode in ("1", "2", "3"):
+        os.environ["PER_SAMPLE_MODE"] = mode
+        try:
+            u = rng.random(4096, dtype=np.float32)
+            u[:64] = np.float32(1) - np.float32(2.0 ** -24) * np.arange(1, 65, dtype=np.float32)
+            ro = o.sample(u, weights=False)
+            rg = g.sample(dev(u), weights=True)
+            compare_sample(rg, ro, "zeros mode " + mode, weights=False)
+            got = host(rg["idx"])
+            assert np.all(pr[got] > 0)
+            assert np.all(host(rg["w"]) == 0.0)  # min priority is 0
+        finally:
+            del os.environ["PER_SAMPLE_MODE"]
+
+
+# ------------------------------------------------------------ update paths
+
+@pytest.mark.parametrize("n,B,dense", [
+    (1 << 14, 40, False),          # sparse chains, 4 partitions
+    (1 << 14, 3000, True),         # dense partitions
+    (1 << 20, 1 << 15, False),     # bucketed large-batch path
+    (1 << 12, 4096, True),         # single partition, every slot
+])
+def test_update_paths(n, B, dense):
+    say("update paths", n, B, dense)
+    rng = np.random.default_rng(n + B)
+    o = Oracle(n)
+    g = _buf(n, max_batch=B)
+    p0 = (rng.random(n) * 2).astype(np.float32)
+    o.add(n, prio=p0)
+    g.add(n, prio=dev(p0))
+    for step in range(4):
+        if dense:
+            lo = int(rng.integers(0, n - min(n, 4096) + 1))
+            idx = lo + rng.integers(0, min(n, 4096), B)
+        else:
+            idx = rng.integers(0, n, B)
+        idx[: B // 5] = idx[B // 5: 2 * (B // 5)]          # duplicates, last wins
+        idx[::97] = rng.integers(n, n + 5, idx[::97].size)  # skipped
+        idx[1::89] = -1
+        td = rng.standard_normal(B).astype(np.float32)
+        td[::53] = np.nan
+        td[3::71] = np.inf
+        td[5::71] = -np.inf
+        o.update(idx.astype(np.int64), td)
+        g.update(dev(idx, np.int64), dev(td))
+        compare_trees(o, g, "update n=%d B=%d step %d" % (n, B, step))
+
+
+def test_update_all_entries_one_slot():
+    n, B = 1 << 16, 5000
+    o = Oracle(n)
+    g = _buf(n, max_batch=B)
+    o.add(n)
+    g.add(n)
+    idx = np.full(B, 12345, np.int64)
+    td = np.linspace(-3, 3, B).astype(np.float32)
+    o.update(idx, td)
+    g.update(dev(idx), dev(td))
+    compare_trees(o, g, "one slot")
+
+
+# ------------------------------------------------------------ intake and ring
+
+@pytest.mark.parametrize("n", [2, 4, 64, 1 << 12, 1 << 13, 1 << 16])
+def test_ring_intake_and_random_ops(n):
+    say("ring", n)
+    rng = np.random.default_rng(n)
+    D = 5  # not a multiple of 4: scalar row copies
+    o = Oracle(n, D)
+    g = _buf(n, D, max_batch=256)
+    for step in range(25):
+        c = int(rng.integers(1, n + 1)) if step % 5 == 0 else int(rng.integers(1, max(2, n // 3)))
+        c = min(c, n)
+        st = rng.standard_normal((c, D)).astype(np.float32)
+        nx = rng.standard_normal((c, D)).astype(np.float32)
+        ac = rng.integers(0, 3, c).astype(np.uint32)
+        rw = rng.standard_normal(c).astype(np.float32)
+        dn = (rng.random(c) < 0.5).astype(np.uint8)
+        prio = None if step % 2 else (rng.random(c) * 4).astype(np.float32)
+        if prio is not None and step % 4 == 0:
+            prio[0] = -0.0
+        o.add(c, st, nx, ac, rw, dn, prio=prio)
+        g.add(c, dev(st), dev(nx), dev(ac), dev(rw), dev(dn),
+              prio=None if prio is None else dev(prio))
+        compare_trees(o, g, "ring n=%d step %d add %d" % (n, step, c))
+        B = int(rng.integers(1, 200))
+        if o.total > 0:
+            u = rng.random(B, dtype=np.float32)
+            ro = o.sample(u, beta=0.6, rows=True)
+            rg = g.sample(dev(u), beta=0.6, rows=True)
+            compare_sample(rg, ro, "ring n=%d step %d sample" % (n, step), rows=True)
+        idx = rng.integers(-2, n + 2, B).astype(np.int64)
+        td = (rng.standard_normal(B) * 2).astype(np.float32)
+        o.update(idx, td)
+        g.update(dev(idx), dev(td))
+        compare_trees(o, g, "ring n=%d step %d update" % (n, step))
+
+
+def test_partial_fill_and_empty():
+    from sum_tree_sampling_amd import PerError
+    n = 1 << 15
+    g = _buf(n)
+    o = Oracle(n)
+    u = dev(np.array([0.5], np.float32))
+    with pytest.raises(PerError) as e:
+        g.sample(u)
+    assert e.value.code == -3
+    # empty batches are no-ops
+    g.update(dev(np.zeros(0, np.int64)), dev(np.zeros(0, np.float32)))
+    g.add(0)
+    compare_trees(o, g, "empty")
+    o.add(777)
+    g.add(777)
+    compare_trees(o, g, "partial")
+    assert float(host(g.scalar("min"))[0]) == 1.0
+    rng = np.random.default_rng(9)
+    uu = rng.random(1000, dtype=np.float32)
+    compare_sample(g.sample(dev(uu)), o.sample(uu), "partial sample")
+    idx = np.arange(700, 900, dtype=np.int64)  # the tail is past size and skipped
+    td = np.ones(200, np.float32)
+    o.update(idx, td)
+    g.update(dev(idx), dev(td))
+    compare_trees(o, g, "partial update")
+
+
+def test_scalars_and_errors():
+    from sum_tree_sampling_amd import PerError
+    n = 1 << 10
+    g = _buf(n, max_batch=16)
+    with pytest.raises(PerError):
+        g.sample(dev(np.zeros(17, np.float32)))
+    with pytest.raises(PerError):
+        g.add(n + 1)
+    g.add(n, prio=dev(np.full(n, 0.25, np.float32)))
+    assert float(host(g.scalar("total"))[0]) == 256.0
+    assert float(host(g.scalar("min"))[0]) == 0.25
+    assert float(host(g.scalar("max_priority"))[0]) == 1.0
+
+
+# ------------------------------------------------------------ full-size large buffer
+
+def test_large_16m_full_size():
+    """2^24 leaves, 2 x [2^24 x 128] f32 rows, B = 65536 with the sampler's
+    default plan: the whole trees and all indices against the oracle; rows of
+    sampled slots against the generator for four row chunks and against a
+    PyTorch index_select of the device storage for all of them."""
+    name = "large_16m"
+    s = workloads.spec(name)
+    n, B, D = s["capacity"], s["batch"], s["state_dim"]
+    say("large: filling", n, D)
+    o = Oracle(n)  # trees only: rows are checked against the generator
+    g = _buf(n, D, max_batch=B)
+    fill(name, o, g)
+    compare_trees(o, g, "large after fill")
+    keep = [0, 7, 100, 255]
+    kept = {k: workloads.row_chunk(name, k) for k in keep}
+    for k, r in kept.items():
+        lo = k * workloads.ROW_CHUNK
+        assert_bits_equal(host(g.storage["states"][lo:lo + workloads.ROW_CHUNK]), r["states"],
+                          "storage chunk %d" % k)
+    inp = workloads.StepInputs(name)
+    for step in range(2):
+        say("large step", step)
+        u = inp.u()
+        ro = o.sample(u, beta=s["beta"])
+        rg = g.sample(dev(u), beta=s["beta"], rows=True)
+        compare_sample(rg, ro, "large step %d" % step)
+        idx_t = rg["idx"]
+        for key in ("states", "next_states", "actions", "rewards", "dones"):
+            ref = torch.index_select(g.storage[key], 0, idx_t)
+            assert torch.equal(rg[key], ref), key
+        idx = ro["idx"]
+        ch = idx // workloads.ROW_CHUNK
+        for k, r in kept.items():
+            sel = np.nonzero(ch == k)[0]
+            off = idx[sel] - k * workloads.ROW_CHUNK
+            assert_bits_equal(host(rg["states"])[sel], r["states"][off], "rows chunk %d" % k)
+            assert_bits_equal(host(rg["next_states"])[sel], r["next_states"][off],
+                              "next rows chunk %d" % k)
+        td = inp.td()
+        o.update(idx, td)
+        g.update(dev(idx), dev(td))
+        compare_trees(o, g, "large step %d update" % step)
