@@ -147,6 +147,16 @@ int per_sample(per_t* h, int64_t B, const float* d_u, double beta, int64_t* d_id
                hipStream_t stream);
 
 /*
+ * The nodes above the update partitions (the top levels of both trees) are
+ * rebuilt lazily: per_add and per_update leave them to the next per_sample,
+ * which needs them anyway and writes them back.  per_flush enqueues that
+ * rebuild now if it is pending (one small kernel; a no-op otherwise), so that
+ * the arrays of per_tree_ptrs hold every node.  per_total and per_min call
+ * it themselves.
+ */
+int per_flush(per_t* h, hipStream_t stream);
+
+/*
  * Enqueue a 4-byte device copy of the sum-tree root (total priority), the
  * min-tree root (min priority over written slots; +inf when empty) or the
  * running max priority into d_out.  The caller synchronises to read it.
@@ -163,7 +173,7 @@ int64_t per_capacity(const per_t* h);
 int32_t per_state_dim(const per_t* h);
 
 /* Read-only device pointers to the two [2 x capacity] f32 trees (index 0
- * unused), for inspection after the stream has passed the writing calls. */
+ * unused), for inspection after the stream has passed per_flush. */
 int per_tree_ptrs(const per_t* h, const float** d_sum, const float** d_min);
 
 /* Text of the last error on this host thread ("" if none). */

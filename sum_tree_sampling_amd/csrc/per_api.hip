@@ -21,6 +21,8 @@ struct per_s {
   per::Buckets bk;
   per::Storage st;
   int64_t size, cursor;
+  int epoch;       // committed running-max slot
+  bool top_stale;  // nodes above the partitions not yet rebuilt
   int device;
 };
 
@@ -177,6 +179,8 @@ int per_create(per_t** out, int64_t capacity, int32_t state_dim, int64_t max_bat
   h->st.D = state_dim;
   h->size = 0;
   h->cursor = 0;
+  h->epoch = 0;
+  h->top_stale = false;
   if (hipGetDevice(&h->device) != hipSuccess) h->device = -1;
   hipError_t e = per::launch_init(h->t, h->bk, h->g, stream);
   if (e != hipSuccess) {
@@ -207,10 +211,13 @@ int per_add(per_t* h, int64_t count, const float* d_states, const float* d_next_
         15u)
       return fail(PER_EINVAL, "state rows must be 16-byte aligned");
   }
+  const int src = h->epoch, dst = d_prio ? (h->epoch ^ 1) : h->epoch;
   hipError_t e = per::launch_add(h->t, h->g, h->st, (uint32_t)h->cursor, (uint32_t)count,
                                  d_states, d_next_states, d_actions, d_rewards, d_dones,
-                                 d_prio, stream);
+                                 d_prio, src, dst, stream);
   if (e != hipSuccess) return hip_fail(e, "per_add");
+  h->epoch = dst;
+  h->top_stale = h->g.P > 0;
   h->cursor = (h->cursor + count) % (int64_t)h->g.n;
   h->size = (h->size + count < (int64_t)h->g.n) ? h->size + count : (int64_t)h->g.n;
   return ok();
@@ -225,8 +232,10 @@ int per_update(per_t* h, int64_t B, const int64_t* d_idx, const float* d_td,
   if (B == 0) return ok();
   if (!d_idx || !d_td) return fail(PER_EINVAL, "idx and td are required");
   hipError_t e = per::launch_update(h->t, h->bk, h->g, (uint32_t)h->size, B, d_idx, d_td,
-                                    h->alpha, h->eps, stream);
+                                    h->alpha, h->eps, h->epoch, h->epoch ^ 1, stream);
   if (e != hipSuccess) return hip_fail(e, "per_update");
+  h->epoch ^= 1;
+  h->top_stale = h->g.P > 0;
   return ok();
 }
 
@@ -252,11 +261,17 @@ int per_sample(per_t* h, int64_t B, const float* d_u, double beta, int64_t* d_id
     return fail(PER_EINVAL, "state outputs must be 16-byte aligned");
   if (h->size == 0) return fail(PER_EEMPTY, "sample from an empty buffer");
   const per::SamplePlan plan = per::make_sample_plan(h->g, B);
+  if (h->top_stale && plan.top_mode != per::kTopRebuild) {  // the sampler will not rebuild the top itself
+    hipError_t e = per::launch_top(h->t, h->g, stream);
+    if (e != hipSuccess) return hip_fail(e, "per_sample: top rebuild");
+    h->top_stale = false;
+  }
   hipError_t e = per::launch_sample(h->t, h->g, h->st, plan, (uint32_t)h->size, B, d_u, beta,
                                     d_idx_out, d_w_out, any_rows ? d_states_out : nullptr,
                                     d_next_states_out, d_actions_out, d_rewards_out,
-                                    d_dones_out, stream);
+                                    d_dones_out, h->top_stale, stream);
   if (e != hipSuccess) return hip_fail(e, "per_sample");
+  h->top_stale = false;
   return ok();
 }
 
@@ -269,16 +284,33 @@ static int copy_scalar(per_t* h, const void* src, float* d_out, hipStream_t stre
   return ok();
 }
 
+int per_flush(per_t* h, hipStream_t stream) {
+  if (!h) return fail(PER_EINVAL, "handle is NULL");
+  if (h->top_stale) {
+    hipError_t e = per::launch_top(h->t, h->g, stream);
+    if (e != hipSuccess) return hip_fail(e, "per_flush");
+    h->top_stale = false;
+  }
+  return ok();
+}
+
 int per_total(per_t* h, float* d_out, hipStream_t stream) {
-  return copy_scalar(h, h ? h->t.sum + 1 : nullptr, d_out, stream, "per_total");
+  if (!h || !d_out) return fail(PER_EINVAL, "NULL argument");
+  int rc = per_flush(h, stream);
+  if (rc) return rc;
+  return copy_scalar(h, h->t.sum + 1, d_out, stream, "per_total");
 }
 
 int per_min(per_t* h, float* d_out, hipStream_t stream) {
-  return copy_scalar(h, h ? h->t.mn + 1 : nullptr, d_out, stream, "per_min");
+  if (!h || !d_out) return fail(PER_EINVAL, "NULL argument");
+  int rc = per_flush(h, stream);
+  if (rc) return rc;
+  return copy_scalar(h, h->t.mn + 1, d_out, stream, "per_min");
 }
 
 int per_max_priority(per_t* h, float* d_out, hipStream_t stream) {
-  return copy_scalar(h, h ? &h->t.ctrl->maxp : nullptr, d_out, stream, "per_max_priority");
+  if (!h || !d_out) return fail(PER_EINVAL, "NULL argument");
+  return copy_scalar(h, &h->t.ctrl->maxp_bits[h->epoch], d_out, stream, "per_max_priority");
 }
 
 int64_t per_size(const per_t* h) { return h ? h->size : -1; }

@@ -21,11 +21,12 @@ constexpr int kMaxTopBits = 12;
 constexpr int kTreeThreads = 256;
 
 // Device control block at the start of the workspace's control area.
+// The running max priority is kept in two slots (f32 bit patterns, raised
+// with atomicMax): a call that may raise it reads the committed slot and
+// raises the other, and the host then commits the other slot.
 struct Ctrl {
-  float maxp;              // running max priority
-  uint32_t ticket;         // completion counter of the partition kernels
-  uint32_t batch_max;      // max priority written by the running call, f32 bits + 1 (0 = none)
-  uint32_t pad0;
+  uint32_t maxp_bits[2];
+  uint32_t pad[2];
 };
 
 // Geometry shared by host and kernels.
@@ -67,10 +68,14 @@ struct Layout {
 };
 Layout workspace_layout(int64_t n, int64_t max_batch);
 
-// Descent plan of the sampler.
+// Descent plan of the sampler.  The top of the tree reaches LDS either by a
+// rebuild from the partition roots (kTopRebuild, 0 < P <= kMaxTopBits), by
+// staging a whole small tree (kTopWhole, n <= 2^10), or not at all.
 constexpr int kMaxRounds = 12;
+constexpr int kTopNone = 0, kTopRebuild = 1, kTopWhole = 2;
 struct SamplePlan {
   int mode;                 // kernel variant (group size, values per lane)
+  int top_mode;             // how the top of the tree reaches LDS
   int top_levels;           // levels walked in the LDS copy of the tree top
   int nrounds;              // global rounds after the LDS top
   int rounds[kMaxRounds];   // levels per round
@@ -79,22 +84,25 @@ struct SamplePlan {
 // ----------------------------------------------------------------- launchers
 hipError_t launch_init(const TreePtrs& t, const Buckets& bk, const Geom& g, hipStream_t s);
 
-// Batched update; B > 0.
+// Batched update; B > 0.  src / dst: running-max slots to read / raise.
 hipError_t launch_update(const TreePtrs& t, const Buckets& bk, const Geom& g, uint32_t size,
                          int64_t B, const int64_t* idx, const float* td, double alpha,
-                         double eps, hipStream_t s);
+                         double eps, int src, int dst, hipStream_t s);
+
+// Rebuild of the nodes above the partitions (one block).
+hipError_t launch_top(const TreePtrs& t, const Geom& g, hipStream_t s);
 
 // Ring intake of count > 0 items at cursor.
 hipError_t launch_add(const TreePtrs& t, const Geom& g, const Storage& st, uint32_t cursor,
                       uint32_t count, const float* states, const float* next_states,
                       const uint32_t* actions, const float* rewards, const uint8_t* dones,
-                      const float* prio, hipStream_t s);
+                      const float* prio, int src, int dst, hipStream_t s);
 
 hipError_t launch_sample(const TreePtrs& t, const Geom& g, const Storage& st,
                          const SamplePlan& plan, uint32_t size, int64_t B, const float* u,
                          double beta, int64_t* idx_out, float* w_out, float* states_out,
                          float* next_out, uint32_t* actions_out, float* rewards_out,
-                         uint8_t* dones_out, hipStream_t s);
+                         uint8_t* dones_out, bool write_top, hipStream_t s);
 
 SamplePlan make_sample_plan(const Geom& g, int64_t B);
 

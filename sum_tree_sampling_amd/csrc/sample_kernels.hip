@@ -7,15 +7,19 @@
 // exceeds the remaining mass m (or the right child's sum is 0) go left,
 // otherwise m = f32(m - left) and go right.
 //
-// Layout of the work: a group of G lanes (G = 64: one wave per sample; G = 1:
-// one lane per sample) carries one sample.  The top K levels are walked in an
-// LDS copy of the tree top (nodes [1, 2^(K+1))), staged once per block.  The
-// rest is covered in rounds: a round of R levels below node c loads the 2^R
-// contiguous descendants of c at depth +R (G lanes x V values, 16-byte
-// vector loads), rebuilds the R-1 intermediate levels by pairwise adds --
-// bit-identical to the stored nodes, since every stored node is exactly the
-// f32 sum of its children -- and takes all R decisions from registers.  A
-// round is one dependent trip to memory instead of R.
+// Layout of the work: a group of G lanes (G = 16: four samples per wave;
+// G = 1: one lane per sample; G = 64: one wave per sample) carries one
+// sample.  The top of the tree is walked in LDS: each block first rebuilds the
+// 2^P - 1 nodes above the update partitions from the 2^P partition roots (one
+// coalesced load), which also gives it the total and the min priority; block
+// 0 writes those nodes back when the writers left them stale.  (Trees of at
+// most 2^10 leaves are staged whole.)  The remaining levels are covered in
+// rounds: a round of R levels below node c loads the 2^R contiguous
+// descendants of c at depth +R (G lanes x V values, 16-byte vector loads),
+// rebuilds the R-1 intermediate levels by pairwise adds -- bit-identical to
+// the stored nodes, since every stored node is exactly the f32 sum of its
+// children -- and takes all R decisions from registers.  A round is one
+// dependent trip to memory instead of R.
 //
 // Weights ("GPU-Resident Prioritized Experience Replay", section "Sampling
 // Kernels"): w = (N*P(i))^-beta normalised by the weight of the min-tree root
@@ -31,11 +35,10 @@ namespace per {
 namespace {
 
 constexpr int kSampleThreads = 256;
-constexpr int kMaxTopLevels = 12;
 
 struct SampleArgs {
-  const float* sum;
-  const float* mn;
+  float* sum;
+  float* mn;
   uint32_t n;
   uint32_t size;
   uint32_t B;
@@ -49,7 +52,10 @@ struct SampleArgs {
   float* rewards_out;
   uint8_t* dones_out;
   Storage st;
-  int top;
+  int P;          // partitions = 2^P; the top P levels are rebuilt in LDS
+  int top_mode;   // kTopNone / kTopRebuild / kTopWhole
+  int write_top;  // block 0 stores the rebuilt top nodes
+  int top;        // levels walked in LDS
   int nrounds;
   int rounds[kMaxRounds];
 };
@@ -120,14 +126,59 @@ __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleArgs a) {
   const uint32_t b = wave * SPW + (uint32_t)(lane / G);
   const bool active = b < a.B;
 
-  if (a.top > 0) {
-    const uint32_t cnt = 1u << (a.top + 1);  // multiple of 4 (top >= 1)
-    for (uint32_t i = threadIdx.x * 4; i < cnt; i += kSampleThreads * 4)
-      *reinterpret_cast<float4*>(top + i) = *reinterpret_cast<const float4*>(a.sum + i);
+  float T, pmin;
+  if (a.top_mode == kTopRebuild) {
+    // Nodes [1, 2^P) from the partition roots at depth P: sums in top[],
+    // mins in mtop[].
+    const uint32_t np = 1u << a.P;
+    float* mtop = top + 2 * np;
+    // All of a thread's loads go out before the first one is stored to LDS.
+    constexpr int kPer = (1 << kMaxTopBits) / kSampleThreads;
+    float ls[kPer], lm[kPer];
+#pragma unroll
+    for (int c = 0; c < kPer; ++c) {
+      const uint32_t k = threadIdx.x + c * kSampleThreads;
+      if (k < np) {
+        ls[c] = a.sum[np + k];
+        lm[c] = a.mn[np + k];
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < kPer; ++c) {
+      const uint32_t k = threadIdx.x + c * kSampleThreads;
+      if (k < np) {
+        top[np + k] = ls[c];
+        mtop[np + k] = lm[c];
+      }
+    }
     __syncthreads();
+    for (uint32_t width = np >> 1; width >= 1; width >>= 1) {
+      for (uint32_t h = width + threadIdx.x; h < 2 * width; h += kSampleThreads) {
+        top[h] = top[2 * h] + top[2 * h + 1];
+        const float l = mtop[2 * h], r = mtop[2 * h + 1];
+        mtop[h] = (r < l) ? r : l;
+      }
+      __syncthreads();
+    }
+    if (a.write_top && blockIdx.x == 0) {
+      for (uint32_t h = 1 + threadIdx.x; h < np; h += kSampleThreads) {
+        a.sum[h] = top[h];
+        a.mn[h] = mtop[h];
+      }
+    }
+    T = top[1];
+    pmin = mtop[1];
+  } else {
+    if (a.top_mode == kTopWhole) {
+      const uint32_t cnt = 1u << (a.top + 1);  // whole tree, >= 4 floats
+      for (uint32_t i = threadIdx.x * 4; i < cnt; i += kSampleThreads * 4)
+        *reinterpret_cast<float4*>(top + i) = *reinterpret_cast<const float4*>(a.sum + i);
+      __syncthreads();
+    }
+    T = a.sum[1];
+    pmin = a.mn[1];
   }
 
-  const float T = a.sum[1];
   float m = active ? a.u[b] * T : 0.0f;
   if (!(m < T)) m = __uint_as_float(__float_as_uint(T) - 1u);  // largest f32 below T
 
@@ -194,7 +245,6 @@ __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleArgs a) {
   if (active && j == 0) {
     a.idx_out[b] = (int64_t)slot;
     if (a.w_out) {
-      const float pmin = a.mn[1];
       float w = 0.0f;
       if (pmin > 0.0f) {
         const double N = (double)a.size;
@@ -245,7 +295,9 @@ hipError_t launch_variant(const SampleArgs& a, hipStream_t s) {
   constexpr int SPW = 64 / G;
   const uint64_t waves = (a.B + SPW - 1) / SPW;
   const unsigned grid = (unsigned)((waves + 3) / 4);
-  const size_t lds = a.top > 0 ? (sizeof(float) << (a.top + 1)) : 0;
+  size_t lds = 0;
+  if (a.top_mode == kTopRebuild) lds = 2 * (sizeof(float) << (a.P + 1));
+  if (a.top_mode == kTopWhole) lds = sizeof(float) << (a.top + 1);
   hipLaunchKernelGGL((sample_kernel<G, V>), dim3(grid), dim3(kSampleThreads), lds, s, a);
   return hipGetLastError();
 }
@@ -261,35 +313,29 @@ void split_rounds(int levels, int hi, SamplePlan& p) {
 
 }  // namespace
 
-// Modes: 1 = one wave per sample (G=64, V=4, rounds up to 8 levels);
+// Modes: 1 = one wave per sample (G=64, V=4, rounds of up to 8 levels);
 // 2 = 16 lanes per sample (G=16, V=4, up to 6 levels);
-// 3 = one lane per sample (G=1, V=32, rounds of exactly 5 levels).
+// 3 = one lane per sample (G=1, V=16, rounds of exactly 4 levels).
 SamplePlan make_sample_plan(const Geom& g, int64_t B) {
   SamplePlan p{};
-  p.mode = (B <= 16384) ? 1 : 3;
+  p.mode = (B <= 16384) ? 2 : 3;
   const char* env = getenv("PER_SAMPLE_MODE");
   if (env && atoi(env) >= 1 && atoi(env) <= 3) p.mode = atoi(env);
-  if (g.L <= 10) {  // the whole tree fits the LDS copy
+  if (g.P > 0 && g.P <= kMaxTopBits) {
+    p.top_mode = kTopRebuild;
+    p.top_levels = g.P;
+  } else if (g.P == 0 && g.L <= 10) {
+    p.top_mode = kTopWhole;
     p.top_levels = g.L;
-    p.nrounds = 0;
-    return p;
+  } else {
+    p.top_mode = kTopNone;
+    p.top_levels = 0;
   }
-  int top = 0;
-  if (p.mode == 3) {
-    for (int k = (g.L < kMaxTopLevels ? g.L : kMaxTopLevels); k >= 0; --k)
-      if ((g.L - k) % 5 == 0) {
-        top = k;
-        break;
-      }
-  }
-  const char* envt = getenv("PER_SAMPLE_TOP");
-  if (envt && p.mode != 3) {
-    const int k = atoi(envt);
-    if (k >= 0 && k <= kMaxTopLevels && k <= g.L - 6) top = k;
-  }
-  p.top_levels = top;
-  const int hi = (p.mode == 1) ? 8 : (p.mode == 2 ? 6 : 5);
-  split_rounds(g.L - top, hi, p);
+  const int levels = g.L - p.top_levels;
+  if (p.mode == 3 && levels % 4 != 0) p.mode = 2;
+  if (p.mode == 2 && levels > 0 && levels < 2) p.mode = 1;
+  const int hi = (p.mode == 1) ? 8 : (p.mode == 2 ? 6 : 4);
+  split_rounds(levels, hi, p);
   return p;
 }
 
@@ -297,7 +343,7 @@ hipError_t launch_sample(const TreePtrs& t, const Geom& g, const Storage& st,
                          const SamplePlan& plan, uint32_t size, int64_t B, const float* u,
                          double beta, int64_t* idx_out, float* w_out, float* states_out,
                          float* next_out, uint32_t* actions_out, float* rewards_out,
-                         uint8_t* dones_out, hipStream_t s) {
+                         uint8_t* dones_out, bool write_top, hipStream_t s) {
   SampleArgs a{};
   a.sum = t.sum;
   a.mn = t.mn;
@@ -314,6 +360,9 @@ hipError_t launch_sample(const TreePtrs& t, const Geom& g, const Storage& st,
   a.rewards_out = rewards_out;
   a.dones_out = dones_out;
   a.st = st;
+  a.P = g.P;
+  a.top_mode = plan.top_mode;
+  a.write_top = write_top ? 1 : 0;
   a.top = plan.top_levels;
   a.nrounds = plan.nrounds;
   for (int r = 0; r < kMaxRounds; ++r) a.rounds[r] = plan.rounds[r];
@@ -321,7 +370,7 @@ hipError_t launch_sample(const TreePtrs& t, const Geom& g, const Storage& st,
     case 2:
       return launch_variant<16, 4>(a, s);
     case 3:
-      return launch_variant<1, 32>(a, s);
+      return launch_variant<1, 16>(a, s);
     default:
       return launch_variant<64, 4>(a, s);
   }

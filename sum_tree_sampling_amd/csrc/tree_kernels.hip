@@ -1,5 +1,5 @@
-// tree_kernels.hip -- initialisation, batched priority update and ring intake
-// of the sum + min tree on gfx950.
+// tree_kernels.hip -- initialisation, batched priority update, ring intake and
+// top-level rebuild of the sum + min tree on gfx950.
 //
 // Tree layout ("Putting prioritized replay's segment tree on a GPU", section
 // "The Tree Under Every Prioritized Replay"): node i has children 2i and
@@ -7,27 +7,38 @@
 //
 // Both writers (update and intake) follow the same plan:
 //  1. The leaves are cut into 2^P aligned partitions of 2^S leaves (S <= 12);
-//     one 256-thread workgroup owns one partition, i.e. one subtree.
+//     one 256-thread workgroup owns one partition, i.e. one subtree, so no
+//     two workgroups ever write the same node.
 //  2. The workgroup collects the leaves it must set (for the update: the last
 //     batch position per slot wins; for the intake: the ring range), writes
 //     them, and repairs every dirty node of its subtree up to the partition
-//     root.  Sparse partitions (<= 64 new leaves) are repaired by one wave:
-//     each leaf's lane walks up its own chain until it meets the chain of its
-//     right neighbour; siblings along the chains are fetched in one round of
-//     independent loads and values meet through lane shuffles, so the levels
-//     stay ordered without a barrier.  Dense partitions are rebuilt level by
-//     level in LDS with a barrier between levels.
-//  3. The last workgroup to finish (a device-scope completion counter)
-//     rebuilds the 2^P - 1 nodes above the partitions and updates the running
-//     max priority.
+//     root.  Sparse partitions (<= 64 new leaves, the common case) are
+//     repaired by one wave: each leaf's lane walks up its own chain until it
+//     meets the chain of its right neighbour; siblings along the chains are
+//     fetched in one round of independent loads and values meet through lane
+//     shuffles, so the levels stay ordered without a barrier.  Dense
+//     partitions are rebuilt level by level in LDS, a barrier between levels.
+//  3. The 2^P - 1 nodes above the partitions are not touched by the writers.
+//     They are a pure function of the partition roots, and the sampler
+//     rebuilds them in LDS anyway to walk the top of the tree; its first
+//     block writes them back.  top_kernel rebuilds them for readers of the
+//     stored tree (total, min, inspection).
 // Every node is recomputed from its two children, never updated by adding a
 // delta, and no level is read before the level below it is complete (the
 // dependency rule of section "The Race Condition Worth Writing Down").
+//
+// The running max priority lives in two slots of the control block.  A call
+// that may raise it reads the committed slot (its value at the start of the
+// call) and raises the other slot with atomicMax on the f32 bit patterns
+// (all priorities are >= 0, so the bit patterns order like the values); the
+// host flips the committed slot after enqueueing the call.
 
 #include "per_internal.h"
 
 namespace per {
 namespace {
+
+constexpr int kListCap = 1024;  // entries a partition block keeps in LDS
 
 __device__ __forceinline__ float min_f32(float a, float b) { return (b < a) ? b : a; }
 
@@ -43,22 +54,36 @@ __device__ __forceinline__ float priority_of(float td, float max_at_start, doubl
   return (float)pow((double)x + eps, alpha);
 }
 
+struct Entry {
+  uint32_t off;  // slot offset inside the partition
+  uint32_t pos;  // batch position
+  float p;       // its priority
+};
+
 struct PartSmem {
-  float val[kMaxSpan];                 // new leaf value by offset in the partition
+  float val[kMaxSpan];  // new leaf value by offset in the partition
   union {
-    int owner[kMaxSpan];               // last batch position per offset (update dedupe)
+    struct {
+      int owner[kMaxSpan];     // last batch position per offset
+      Entry ent[kListCap];     // this partition's entries
+    } d;
     struct {
       float s[kMaxSpan];
       float m[kMaxSpan];
-    } heap;                            // local heap [1, 2^S) / top nodes [1, 2^P)
+    } heap;                    // local heap [1, 2^S) / top nodes [1, 2^P)
   } u;
-  uint32_t bits[kMaxSpan / 32];        // offsets that receive a new leaf
-  uint8_t dirty[kMaxSpan];             // dense repair: node has a new leaf below it
-  uint16_t list[kSparseMax];           // sparse repair: sorted offsets
+  uint32_t bits[kMaxSpan / 32];  // offsets that receive a new leaf
+  uint8_t dirty[kMaxSpan];       // dense repair: node has a new leaf below it
+  uint16_t list[kSparseMax];     // sorted offsets of a sparse partition
+  float sib_s[kSparseMax][kMaxSpanBits];  // prefetched siblings along each
+  float sib_m[kSparseMax][kMaxSpanBits];  // of the first 64 entries' chains
+  uint64_t key[kSparseMax];      // (offset << 32 | batch position) of those entries
+  float pval[kSparseMax];        // and their priorities
+  uint8_t order[kSparseMax];     // sparse wave: entry at each sorted position
+  uint32_t bmax;                 // max priority bits of the block's entries
   int wsum[kTreeThreads / 64];
   uint32_t wmax[kTreeThreads / 64];
-  int total;
-  uint32_t last;
+  int count;
 };
 
 // Exclusive scan of one int per thread over the 256-thread block.
@@ -83,11 +108,16 @@ __device__ int block_excl_scan(int v, PartSmem& sm, int* total) {
   return off + x - v;
 }
 
-// Block max of non-negative f32 values held as bits + 1 (0 = none).
-__device__ uint32_t block_max_tagged(uint32_t v, PartSmem& sm) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
+  return v;
+}
+
+// Block max of f32 bit patterns of non-negative values (0 if none).
+__device__ uint32_t block_max_bits(uint32_t v, PartSmem& sm) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  v = wave_max_u32(v);
   if (lane == 0) sm.wmax[w] = v;
   __syncthreads();
   uint32_t r = 0;
@@ -101,42 +131,43 @@ __device__ __forceinline__ bool has_bit(const PartSmem& sm, uint32_t off) {
   return (sm.bits[off >> 5] >> (off & 31)) & 1u;
 }
 
-// Sparse repair by wave 0: U <= 64 sorted new leaves, lane i owns leaf i.
-// d_i is the depth of the lowest common ancestor of leaves i and i+1 (P-1
-// for the last leaf, whose chain ends at the partition root).  Lane i
+// Position of the r-th (0-based) set bit of mask; mask has more than r bits.
+__device__ __forceinline__ int nth_set_bit(uint64_t mask, int r) {
+  int pos = 0;
+#pragma unroll
+  for (int w = 32; w >= 1; w >>= 1) {
+    const uint64_t below = (1ull << (pos + w)) - 1ull;
+    if (__popcll(mask & below) <= r) pos += w;
+  }
+  return pos;
+}
+
+// Sparse repair by one wave.  Lanes [0, m) hold the new leaves of the
+// partition sorted by offset (offset off, value p); `valid` marks one lane
+// per distinct offset (the others are ignored) and ps / pm hold the stored
+// values of the siblings of the lane's ancestors (index k: the ancestor k
+// levels above the leaf's parent level, 0 = the leaf's sibling).  d_i is the
+// depth of the lowest common ancestor of the leaves of lanes i and i+1 (P-1
+// for the last lane, whose chain ends at the partition root).  Lane i
 // computes the nodes of its chain at depths L-1 .. d_i+1: it is the last
 // (rightmost) new leaf under each of them.  When lane i's path enters a node
 // X from the right child, X's left child holds new leaves iff the nearest
-// lane j < i with d_j <= depth(X) has d_j == depth(X); that lane's chain ends
-// exactly at the left child, whose value it holds, frozen.  Otherwise the
-// other child is unchanged and its value was prefetched.
-__device__ void sparse_repair(const PartSmem& sm, const TreePtrs& t, const Geom& g,
-                              uint32_t part, int U) {
-  const int lane = threadIdx.x;
-  const bool valid = lane < U;
-  const uint32_t off = valid ? sm.list[lane] : 0u;
+// valid lane j < i with d_j <= depth(X) has d_j == depth(X); that lane's
+// chain ends exactly at the left child, whose value it holds, frozen.
+// Otherwise the other child is unchanged and its stored value is the
+// sibling's.  Must be called by all 64 lanes of the wave.
+__device__ void sparse_chain(const TreePtrs& t, const Geom& g, uint32_t part, int m, bool valid,
+                             uint32_t off, float p, const float* ps, const float* pm) {
+  const int lane = threadIdx.x & 63;
   const uint32_t leaf = (part << g.S) + off;
   const uint32_t node = g.n + leaf;
-  const float p = sm.val[off];
   if (valid) {
     t.sum[node] = p;
     t.mn[node] = p;
   }
   const uint32_t next_leaf = __shfl_down(leaf, 1);
   int d = g.P - 1;
-  if (lane < U - 1) d = g.L - 1 - (31 - __clz(leaf ^ next_leaf));
-
-  float ps[kMaxSpanBits], pm[kMaxSpanBits];
-#pragma unroll
-  for (int k = 0; k < kMaxSpanBits; ++k) {
-    ps[k] = 0.0f;
-    pm[k] = 0.0f;
-    if (k < g.S && valid && (g.L - 1 - k) > d) {
-      const uint32_t sib = (node >> k) ^ 1u;
-      ps[k] = t.sum[sib];
-      pm[k] = t.mn[sib];
-    }
-  }
+  if (lane < m - 1) d = g.L - 1 - (31 - __clz(leaf ^ next_leaf));
 
   float vs = p, vm = p;
   const uint64_t lanes_below = (1ull << lane) - 1ull;
@@ -144,20 +175,26 @@ __device__ void sparse_repair(const PartSmem& sm, const TreePtrs& t, const Geom&
   for (int k = 0; k < kMaxSpanBits; ++k) {
     if (k >= g.S) continue;     // uniform across the wave
     const int l = g.L - 1 - k;  // depth of the node computed at this step
-    const uint64_t le = __ballot(valid && d <= l);
-    const uint64_t below = le & lanes_below;
-    const int src = below ? 63 - __clzll(below) : lane;
-    const int d_src = __shfl(d, src);
-    const float s_src = __shfl(vs, src);
-    const float m_src = __shfl(vm, src);
-    if (valid && d < l) {
-      const uint32_t child = node >> k;
-      const bool right = child & 1u;
-      float os = ps[k], om = pm[k];
-      if (right && below != 0ull && d_src == l) {
+    const bool active = valid && d < l;
+    const uint32_t child = node >> k;
+    const bool right = child & 1u;
+    float os = ps[k], om = pm[k];
+    // Chains ending here (d == l) deliver their value to the right; most
+    // levels have none, so the lookup runs only when one does (uniform test).
+    const uint64_t eq = __ballot(valid && d == l);
+    if (eq != 0ull) {
+      const uint64_t le = __ballot(valid && d <= l);
+      const uint64_t below = le & lanes_below;
+      const int src = below ? 63 - __clzll(below) : lane;
+      const bool take = active && right && below != 0ull && ((eq >> src) & 1ull);
+      const float s_src = __shfl(vs, src);
+      const float m_src = __shfl(vm, src);
+      if (take) {
         os = s_src;
         om = m_src;
       }
+    }
+    if (active) {
       if (right) {
         vs = os + vs;
         vm = min_f32(om, vm);
@@ -173,43 +210,54 @@ __device__ void sparse_repair(const PartSmem& sm, const TreePtrs& t, const Geom&
 }
 
 // Dense repair by the whole block: rebuild the partition's subtree in LDS and
-// write back the nodes with a new leaf below them.
+// write back the nodes with a new leaf below them.  All old leaves are loaded
+// before anything is stored, so the loads go out in one round.
 __device__ void dense_repair(PartSmem& sm, const TreePtrs& t, const Geom& g, uint32_t part) {
+  constexpr int kPairs = kMaxSpan / 2 / kTreeThreads;  // leaf pairs per thread
   const uint32_t span = 1u << g.S, half = span >> 1;
   const uint32_t root = (1u << g.P) + part;
   const uint32_t leaf0 = g.n + (part << g.S);
-  for (uint32_t k = threadIdx.x; k < span; k += kTreeThreads) {
-    if (has_bit(sm, k)) {
-      t.sum[leaf0 + k] = sm.val[k];
-      t.mn[leaf0 + k] = sm.val[k];
+  float2 os[kPairs], om[kPairs];
+#pragma unroll
+  for (int r = 0; r < kPairs; ++r) {
+    os[r] = om[r] = make_float2(0.0f, 0.0f);
+    const uint32_t h = half + threadIdx.x + r * kTreeThreads;
+    if (h < span) {
+      const uint32_t a = 2 * h - span;
+      if (!(has_bit(sm, a) && has_bit(sm, a + 1))) {
+        os[r] = *reinterpret_cast<const float2*>(t.sum + leaf0 + a);
+        om[r] = *reinterpret_cast<const float2*>(t.mn + leaf0 + a);
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < kPairs; ++r) {
+    const uint32_t h = half + threadIdx.x + r * kTreeThreads;
+    if (h < span) {
+      const uint32_t a = 2 * h - span;
+      const bool ba = has_bit(sm, a), bb = has_bit(sm, a + 1);
+      const float ls = ba ? sm.val[a] : os[r].x, lm = ba ? sm.val[a] : om[r].x;
+      const float rs = bb ? sm.val[a + 1] : os[r].y, rm = bb ? sm.val[a + 1] : om[r].y;
+      if (ba) {
+        t.sum[leaf0 + a] = ls;
+        t.mn[leaf0 + a] = lm;
+      }
+      if (bb) {
+        t.sum[leaf0 + a + 1] = rs;
+        t.mn[leaf0 + a + 1] = rm;
+      }
+      const float s = ls + rs, m = min_f32(lm, rm);
+      sm.u.heap.s[h] = s;
+      sm.u.heap.m[h] = m;
+      sm.dirty[h] = ba | bb;
+      if (ba | bb) {
+        const uint32_t gnode = ((root - 1u) << (g.S - 1)) + h;
+        t.sum[gnode] = s;
+        t.mn[gnode] = m;
+      }
     }
   }
   // local heap index h in [1, span) <-> global node ((root - 1) << depth(h)) + h
-  for (uint32_t h = half + threadIdx.x; h < span; h += kTreeThreads) {
-    const uint32_t a = 2 * h - span;
-    const bool ba = has_bit(sm, a), bb = has_bit(sm, a + 1);
-    float ls, lm, rs, rm;
-    if (ba && bb) {
-      ls = lm = sm.val[a];
-      rs = rm = sm.val[a + 1];
-    } else {
-      const float2 os = *reinterpret_cast<const float2*>(t.sum + leaf0 + a);
-      const float2 om = *reinterpret_cast<const float2*>(t.mn + leaf0 + a);
-      ls = ba ? sm.val[a] : os.x;
-      lm = ba ? sm.val[a] : om.x;
-      rs = bb ? sm.val[a + 1] : os.y;
-      rm = bb ? sm.val[a + 1] : om.y;
-    }
-    const float s = ls + rs, m = min_f32(lm, rm);
-    sm.u.heap.s[h] = s;
-    sm.u.heap.m[h] = m;
-    sm.dirty[h] = ba | bb;
-    if (ba | bb) {
-      const uint32_t gnode = ((root - 1u) << (g.S - 1)) + h;
-      t.sum[gnode] = s;
-      t.mn[gnode] = m;
-    }
-  }
   for (uint32_t width = half >> 1, dl = g.S - 2; width >= 1; width >>= 1, --dl) {
     __syncthreads();
     for (uint32_t h = width + threadIdx.x; h < 2 * width; h += kTreeThreads) {
@@ -228,7 +276,7 @@ __device__ void dense_repair(PartSmem& sm, const TreePtrs& t, const Geom& g, uin
   }
 }
 
-// Repair the partition after sm.val / sm.bits hold its new leaves.
+// Repair the partition once sm.val / sm.bits hold its new leaves (whole block).
 __device__ void repair_partition(PartSmem& sm, const TreePtrs& t, const Geom& g,
                                  uint32_t part) {
   const uint32_t nwords = ((1u << g.S) + 31) >> 5;
@@ -245,104 +293,193 @@ __device__ void repair_partition(PartSmem& sm, const TreePtrs& t, const Geom& g,
       x &= x - 1;
     }
     __syncthreads();
-    if (threadIdx.x < 64) sparse_repair(sm, t, g, part, U);
+    if (threadIdx.x < 64) {
+      const bool valid = threadIdx.x < (unsigned)U;
+      const uint32_t off = valid ? sm.list[threadIdx.x] : 0u;
+      const uint32_t node = g.n + (part << g.S) + off;
+      float ps[kMaxSpanBits], pm[kMaxSpanBits];
+#pragma unroll
+      for (int k = 0; k < kMaxSpanBits; ++k) {
+        ps[k] = pm[k] = 0.0f;
+        if (k < g.S && valid) {
+          const uint32_t sib = (node >> k) ^ 1u;
+          ps[k] = t.sum[sib];
+          pm[k] = t.mn[sib];
+        }
+      }
+      sparse_chain(t, g, part, U, valid, off, sm.val[off], ps, pm);
+    }
   } else {
     dense_repair(sm, t, g, part);
   }
 }
 
-// Nodes [1, 2^P) above the partitions, recomputed from depth P upwards.
-__device__ void top_rebuild(PartSmem& sm, const TreePtrs& t, const Geom& g) {
-  const uint32_t np = 1u << g.P;
-  if (g.P <= kMaxTopBits) {
-    const uint32_t half = np >> 1;
-    for (uint32_t h = half + threadIdx.x; h < np; h += kTreeThreads) {
-      const float2 cs = *reinterpret_cast<const float2*>(t.sum + 2 * h);
-      const float2 cm = *reinterpret_cast<const float2*>(t.mn + 2 * h);
-      const float s = cs.x + cs.y, m = min_f32(cm.x, cm.y);
-      sm.u.heap.s[h] = s;
-      sm.u.heap.m[h] = m;
-      t.sum[h] = s;
-      t.mn[h] = m;
-    }
-    for (uint32_t width = half >> 1; width >= 1; width >>= 1) {
-      __syncthreads();
-      for (uint32_t h = width + threadIdx.x; h < 2 * width; h += kTreeThreads) {
-        const float s = sm.u.heap.s[2 * h] + sm.u.heap.s[2 * h + 1];
-        const float m = min_f32(sm.u.heap.m[2 * h], sm.u.heap.m[2 * h + 1]);
-        sm.u.heap.s[h] = s;
-        sm.u.heap.m[h] = m;
-        t.sum[h] = s;
-        t.mn[h] = m;
+// Collect one entry of this block's partition into the LDS list (any
+// thread): the entry with its priority and, for the first 64 entries, the
+// stored siblings along its leaf's whole path to the partition root, loaded
+// before the priority's pow so that both latencies overlap.
+__device__ __forceinline__ void collect(PartSmem& sm, const TreePtrs& t, const Geom& g,
+                                        uint32_t part, uint32_t off, uint32_t pos, float td,
+                                        float m0, double alpha, double eps, float p_nan) {
+  const int k = atomicAdd(&sm.count, 1);
+  float ps[kMaxSpanBits], pm[kMaxSpanBits];
+  const uint32_t node = g.n + (part << g.S) + off;
+  if (k < kSparseMax) {
+#pragma unroll
+    for (int q = 0; q < kMaxSpanBits; ++q) {
+      if (q < g.S) {
+        const uint32_t sib = (node >> q) ^ 1u;
+        ps[q] = t.sum[sib];
+        pm[q] = t.mn[sib];
       }
     }
-  } else {
-    // More top nodes than LDS holds: level by level through global memory.
-    for (int l = g.P - 1; l >= 0; --l) {
-      const uint32_t lo = 1u << l;
-      for (uint32_t h = lo + threadIdx.x; h < 2 * lo; h += kTreeThreads) {
-        const float2 cs = *reinterpret_cast<const float2*>(t.sum + 2 * h);
-        const float2 cm = *reinterpret_cast<const float2*>(t.mn + 2 * h);
-        t.sum[h] = cs.x + cs.y;
-        t.mn[h] = min_f32(cm.x, cm.y);
+  }
+  const float p = priority_of(td, m0, alpha, eps, p_nan);
+  atomicMax(&sm.bmax, __float_as_uint(p));
+  if (k < kListCap) sm.u.d.ent[k] = Entry{off, pos, p};
+  if (k < kSparseMax) {
+    sm.key[k] = ((uint64_t)off << 32) | pos;
+    sm.pval[k] = p;
+#pragma unroll
+    for (int q = 0; q < kMaxSpanBits; ++q) {
+      if (q < g.S) {
+        sm.sib_s[k][q] = ps[q];
+        sm.sib_m[k][q] = pm[q];
       }
-      __threadfence();
-      __syncthreads();
     }
   }
 }
 
-// Completion: the last block to finish rebuilds the top levels and folds the
-// call's max priority into the running max.
-__device__ void finish(PartSmem& sm, const TreePtrs& t, const Geom& g, float max_at_start,
-                       uint32_t nblocks, uint32_t* reset_a, uint32_t* reset_b) {
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) sm.last = (atomicAdd(&t.ctrl->ticket, 1u) == nblocks - 1u) ? 1u : 0u;
-  __syncthreads();
-  if (!sm.last) return;
-  __threadfence();
-  if (g.P > 0) top_rebuild(sm, t, g);
-  if (threadIdx.x == 0) {
-    const uint32_t bm = atomicExch(&t.ctrl->batch_max, 0u);
-    if (bm != 0u) {
-      const float pm = __uint_as_float(bm - 1u);
-      if (pm > max_at_start) t.ctrl->maxp = pm;
-    }
-    atomicExch(&t.ctrl->ticket, 0u);
-  }
-  if (reset_a) {
-    const uint32_t np = 1u << g.P;
-    for (uint32_t k = threadIdx.x; k < np; k += kTreeThreads) {
-      reset_a[k] = 0u;
-      reset_b[k] = 0u;
-    }
-  }
+// Publish the block's max priority into the raised running-max slot (one
+// thread; part 0 also carries the value at the start of the call over).
+__device__ __forceinline__ void publish_max(const PartSmem& sm, uint32_t part, float m0,
+                                            uint32_t* max_dst) {
+  uint32_t mb = sm.bmax;
+  if (part == 0) mb = max(mb, __float_as_uint(m0));
+  if (mb) atomicMax(max_dst, mb);
 }
 
-__device__ void clear_partition_tables(PartSmem& sm, const Geom& g, bool with_owner) {
-  const uint32_t span = 1u << g.S;
-  if (with_owner)
-    for (uint32_t k = threadIdx.x; k < span; k += kTreeThreads) sm.u.owner[k] = -1;
-  const uint32_t nwords = (span + 31) >> 5;
+// One wave updates a partition holding m <= 64 collected entries: sort them
+// by (offset, batch position) -- the rank of each key among the m keys,
+// counted from LDS (m is small) -- so that the last batch position of each
+// offset is the last of its run, and repair the chains of those winners with
+// the prefetched siblings.
+__device__ void wave_update(PartSmem& sm, const TreePtrs& t, const Geom& g, uint32_t part,
+                            int m) {
+  const int lane = threadIdx.x & 63;
+  const bool in = lane < m;
+  const uint64_t mine = in ? sm.key[lane] : ~0ull;
+  int rank = 0;
+#pragma unroll 4
+  for (int j = 0; j < m; ++j) rank += (sm.key[j] < mine) ? 1 : 0;
+  if (in) sm.order[rank] = (uint8_t)lane;
+  __builtin_amdgcn_wave_barrier();
+  const int src = in ? sm.order[lane] : 0;
+  const uint64_t key = sm.key[src];
+  const uint32_t off = (uint32_t)(key >> 32);
+  const float p = sm.pval[src];
+  const uint32_t next_off = __shfl_down(off, 1);
+  const bool win = in && (lane == m - 1 || next_off != off);
+  float ps[kMaxSpanBits], pm[kMaxSpanBits];
+#pragma unroll
+  for (int k = 0; k < kMaxSpanBits; ++k) {
+    ps[k] = sm.sib_s[src][k];
+    pm[k] = sm.sib_m[src][k];
+  }
+  sparse_chain(t, g, part, m, win, in ? off : 0u, p, ps, pm);
+}
+
+__device__ void clear_bits(PartSmem& sm, const Geom& g) {
+  const uint32_t nwords = ((1u << g.S) + 31) >> 5;
   for (uint32_t k = threadIdx.x; k < nwords; k += kTreeThreads) sm.bits[k] = 0u;
 }
 
-// Record entry (slot offset, batch position) as a candidate; the last batch
-// position per slot wins.
-__device__ __forceinline__ void note_position(PartSmem& sm, uint32_t off, int pos) {
-  atomicMax(&sm.u.owner[off], pos);
+// Block-wide update of a crowded partition.  each(f) calls f(off, pos, p)
+// for every entry of the partition, spread over the block's threads.
+template <typename Each>
+__device__ void block_update(PartSmem& sm, const TreePtrs& t, const Geom& g, uint32_t part,
+                             uint32_t* max_dst, Each each) {
+  const uint32_t span = 1u << g.S;
+  clear_bits(sm, g);
+  for (uint32_t k = threadIdx.x; k < span; k += kTreeThreads) sm.u.d.owner[k] = -1;
+  __syncthreads();
+  each([&](uint32_t off, uint32_t pos, float) { atomicMax(&sm.u.d.owner[off], (int)pos); });
+  __syncthreads();
+  uint32_t mb = 0;
+  each([&](uint32_t off, uint32_t pos, float p) {
+    mb = max(mb, __float_as_uint(p));
+    if (sm.u.d.owner[off] == (int)pos) {
+      sm.val[off] = p;
+      atomicOr(&sm.bits[off >> 5], 1u << (off & 31));
+    }
+  });
+  mb = block_max_bits(mb, sm);
+  if (threadIdx.x == 0) atomicMax(max_dst, mb);
+  __syncthreads();
+  repair_partition(sm, t, g, part);
 }
 
-__device__ __forceinline__ void set_winner(PartSmem& sm, uint32_t off, float p) {
-  sm.val[off] = p;
-  atomicOr(&sm.bits[off >> 5], 1u << (off & 31));
+
+// Repair after a contiguous run of new leaves, offsets [lo, hi) of the
+// partition, whose values are in sm.val (whole block).  At every level the
+// dirty nodes form a contiguous range and only its two end nodes can have an
+// unchanged child: the sibling left of the range's first node when that node
+// is a right child, and the sibling right of its last node when that node is
+// a left child.  Those (at most 2 per level) are loaded up front with the
+// caller's other loads; the range itself is rebuilt level by level in LDS.
+// Fills the boundary values into sm.sib_s / sib_m rows 0 (left) and 1 (right)
+// in prefetch_range_boundaries(), to be called before the values are known.
+__device__ __forceinline__ void prefetch_range_boundaries(PartSmem& sm, const TreePtrs& t,
+                                                          const Geom& g, uint32_t part,
+                                                          uint32_t lo, uint32_t hi) {
+  const uint32_t a = g.n + (part << g.S) + lo, b = g.n + (part << g.S) + hi - 1;
+  const int q = threadIdx.x & 31;
+  if (threadIdx.x < 64 && q < g.S) {
+    const bool left = threadIdx.x < 32;
+    const uint32_t x = (left ? a : b) >> q;
+    const bool need = left ? (x & 1u) : !(x & 1u);
+    if (need) {
+      const uint32_t sib = left ? x - 1 : x + 1;
+      sm.sib_s[left ? 0 : 1][q] = t.sum[sib];
+      sm.sib_m[left ? 0 : 1][q] = t.mn[sib];
+    }
+  }
 }
 
-__device__ void publish_batch_max(PartSmem& sm, const TreePtrs& t, float pmax_local, bool any) {
-  const uint32_t tag = any ? __float_as_uint(pmax_local) + 1u : 0u;
-  const uint32_t m = block_max_tagged(tag, sm);
-  if (threadIdx.x == 0 && m != 0u) atomicMax(&t.ctrl->batch_max, m);
+__device__ void range_repair(PartSmem& sm, const TreePtrs& t, const Geom& g, uint32_t part,
+                             uint32_t lo, uint32_t hi) {
+  const uint32_t leaf0 = g.n + (part << g.S);
+  for (uint32_t off = lo + threadIdx.x; off < hi; off += kTreeThreads) {
+    t.sum[leaf0 + off] = sm.val[off];
+    t.mn[leaf0 + off] = sm.val[off];
+  }
+  float* bs[2] = {sm.u.heap.s, sm.u.heap.s + kMaxSpan / 2};
+  float* bm[2] = {sm.u.heap.m, sm.u.heap.m + kMaxSpan / 2};
+  uint32_t A = leaf0 + lo, Bn = leaf0 + hi - 1;  // children range (node indices)
+  const float* cs = sm.val + lo;                  // children values, index x - A
+  const float* cm = sm.val + lo;
+  for (int k = 0; k < g.S; ++k) {
+    const uint32_t pa = A >> 1, pb = Bn >> 1;
+    float* ns = bs[k & 1];
+    float* nm = bm[k & 1];
+    for (uint32_t x = pa + threadIdx.x; x <= pb; x += kTreeThreads) {
+      const uint32_t l = 2 * x, r = 2 * x + 1;
+      const float ls = (l >= A) ? cs[l - A] : sm.sib_s[0][k];
+      const float lm = (l >= A) ? cm[l - A] : sm.sib_m[0][k];
+      const float rs = (r <= Bn) ? cs[r - A] : sm.sib_s[1][k];
+      const float rm = (r <= Bn) ? cm[r - A] : sm.sib_m[1][k];
+      const float s = ls + rs, m = min_f32(lm, rm);
+      ns[x - pa] = s;
+      nm[x - pa] = m;
+      t.sum[x] = s;
+      t.mn[x] = m;
+    }
+    __syncthreads();
+    cs = ns;
+    cm = nm;
+    A = pa;
+    Bn = pb;
+  }
 }
 
 // ------------------------------------------------------------------ kernels
@@ -360,9 +497,8 @@ __global__ void __launch_bounds__(256) init_kernel(TreePtrs t, Buckets bk, Geom 
     bk.fill[i] = 0u;
   }
   if (blockIdx.x == 0 && threadIdx.x == 0) {
-    t.ctrl->maxp = 1.0f;
-    t.ctrl->ticket = 0u;
-    t.ctrl->batch_max = 0u;
+    t.ctrl->maxp_bits[0] = __float_as_uint(1.0f);
+    t.ctrl->maxp_bits[1] = __float_as_uint(1.0f);
   }
 }
 
@@ -373,6 +509,7 @@ struct UpdateArgs {
   uint32_t size;
   double alpha, eps;
   float p_nan;
+  int src, dst;  // running-max slots: read / raise
 };
 
 // Small batches: every partition's block scans the whole batch for its slots.
@@ -380,31 +517,65 @@ __global__ void __launch_bounds__(256) update_scan_kernel(TreePtrs t, Geom g, Up
   __shared__ PartSmem sm;
   const uint32_t part = blockIdx.x;
   const uint32_t base = part << g.S;
-  const float m0 = t.ctrl->maxp;
-  clear_partition_tables(sm, g, true);
-  __syncthreads();
-  for (uint32_t b = threadIdx.x; b < a.B; b += kTreeThreads) {
-    const int64_t i = a.idx[b];
-    if (i >= 0 && i < (int64_t)a.size && ((uint64_t)i >> g.S) == part)
-      note_position(sm, (uint32_t)i - base, (int)b);
+  const float m0 = __uint_as_float(t.ctrl->maxp_bits[a.src]);
+  uint32_t* max_dst = &t.ctrl->maxp_bits[a.dst];
+  if (threadIdx.x == 0) {
+    sm.count = 0;
+    sm.bmax = 0u;
   }
   __syncthreads();
-  float pmax = 0.0f;
-  bool any = false;
-  for (uint32_t b = threadIdx.x; b < a.B; b += kTreeThreads) {
-    const int64_t i = a.idx[b];
-    if (i >= 0 && i < (int64_t)a.size && ((uint64_t)i >> g.S) == part) {
-      const float p = priority_of(a.td[b], m0, a.alpha, a.eps, a.p_nan);
-      pmax = any ? fmaxf(pmax, p) : p;
-      any = true;
-      const uint32_t off = (uint32_t)i - base;
-      if (sm.u.owner[off] == (int)b) set_winner(sm, off, p);
+  // Each thread loads its share of the batch in chunks of kChunk entries, all
+  // loads of a chunk issued before any of them is looked at.
+  constexpr int kChunk = 8;
+  for (uint32_t b0 = 0; b0 < a.B; b0 += kTreeThreads * kChunk) {
+    int64_t ix[kChunk];
+    float tx[kChunk];
+#pragma unroll
+    for (int c = 0; c < kChunk; ++c) {
+      const uint32_t b = b0 + c * kTreeThreads + threadIdx.x;
+      ix[c] = -1;
+      tx[c] = 0.0f;
+      if (b < a.B) {
+        ix[c] = a.idx[b];
+        tx[c] = a.td[b];
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < kChunk; ++c) asm volatile("" ::"v"(tx[c]), "v"(ix[c]));
+#pragma unroll
+    for (int c = 0; c < kChunk; ++c) {
+      const uint32_t b = b0 + c * kTreeThreads + threadIdx.x;
+      const int64_t i = ix[c];
+      if (i >= 0 && i < (int64_t)a.size && ((uint64_t)i >> g.S) == part)
+        collect(sm, t, g, part, (uint32_t)i - base, b, tx[c], m0, a.alpha, a.eps, a.p_nan);
     }
   }
-  publish_batch_max(sm, t, pmax, any);
   __syncthreads();
-  repair_partition(sm, t, g, part);
-  finish(sm, t, g, m0, gridDim.x, nullptr, nullptr);
+  const int m = sm.count;
+  if (threadIdx.x == 64) publish_max(sm, part, m0, max_dst);
+  if (m == 0) return;
+  if (m <= kSparseMax) {
+    if (threadIdx.x < 64) wave_update(sm, t, g, part, m);
+    return;
+  }
+  // A crowded partition: the block reads its entries back from the LDS list,
+  // or -- past the list capacity -- straight from the batch again.
+  if (m <= kListCap) {
+    block_update(sm, t, g, part, max_dst, [&](auto f) {
+      for (int k = threadIdx.x; k < m; k += kTreeThreads) {
+        const Entry e = sm.u.d.ent[k];
+        f(e.off, e.pos, e.p);
+      }
+    });
+  } else {
+    block_update(sm, t, g, part, max_dst, [&](auto f) {
+      for (uint32_t b = threadIdx.x; b < a.B; b += kTreeThreads) {
+        const int64_t i = a.idx[b];
+        if (i >= 0 && i < (int64_t)a.size && ((uint64_t)i >> g.S) == part)
+          f((uint32_t)i - base, b, priority_of(a.td[b], m0, a.alpha, a.eps, a.p_nan));
+      }
+    });
+  }
 }
 
 // Large batches, step 1: entries per partition.
@@ -450,33 +621,43 @@ __global__ void __launch_bounds__(256) update_bucket_kernel(TreePtrs t, Buckets 
   __shared__ PartSmem sm;
   const uint32_t part = blockIdx.x;
   const uint32_t base = part << g.S;
-  const float m0 = t.ctrl->maxp;
+  const float m0 = __uint_as_float(t.ctrl->maxp_bits[a.src]);
+  uint32_t* max_dst = &t.ctrl->maxp_bits[a.dst];
   const uint32_t lo = bk.offs[part], hi = bk.offs[part + 1];
-  clear_partition_tables(sm, g, true);
-  __syncthreads();
-  for (uint32_t e = lo + threadIdx.x; e < hi; e += kTreeThreads)
-    note_position(sm, bk.slot[e] - base, (int)bk.pos[e]);
-  __syncthreads();
-  float pmax = 0.0f;
-  bool any = false;
-  for (uint32_t e = lo + threadIdx.x; e < hi; e += kTreeThreads) {
-    const float p = priority_of(bk.td[e], m0, a.alpha, a.eps, a.p_nan);
-    pmax = any ? fmaxf(pmax, p) : p;
-    any = true;
-    const uint32_t off = bk.slot[e] - base;
-    if (sm.u.owner[off] == (int)bk.pos[e]) set_winner(sm, off, p);
+  const int m = (int)(hi - lo);
+  if (threadIdx.x == 0) {  // ready for the next call's counting pass
+    bk.counts[part] = 0u;
+    bk.fill[part] = 0u;
+    sm.count = 0;
+    sm.bmax = 0u;
   }
-  publish_batch_max(sm, t, pmax, any);
+  if (m == 0) {
+    if (part == 0 && threadIdx.x == 0) atomicMax(max_dst, __float_as_uint(m0));
+    return;
+  }
   __syncthreads();
-  repair_partition(sm, t, g, part);
-  finish(sm, t, g, m0, gridDim.x, bk.counts, bk.fill);
+  if (m <= kSparseMax) {
+    for (int k = threadIdx.x; k < m; k += kTreeThreads)
+      collect(sm, t, g, part, bk.slot[lo + k] - base, bk.pos[lo + k], bk.td[lo + k], m0,
+              a.alpha, a.eps, a.p_nan);
+    __syncthreads();
+    if (threadIdx.x == 64) publish_max(sm, part, m0, max_dst);
+    if (threadIdx.x < 64) wave_update(sm, t, g, part, m);
+    return;
+  }
+  if (part == 0 && threadIdx.x == 0) atomicMax(max_dst, __float_as_uint(m0));
+  block_update(sm, t, g, part, max_dst, [&](auto f) {
+    for (uint32_t e = lo + threadIdx.x; e < hi; e += kTreeThreads)
+      f(bk.slot[e] - base, bk.pos[e], priority_of(bk.td[e], m0, a.alpha, a.eps, a.p_nan));
+  });
 }
 
 struct AddArgs {
   uint32_t cursor, count;
   const float* prio;
-  uint32_t run_first[2], run_len[2];   // touched partitions: two disjoint runs
-  uint32_t ntree;                      // blocks doing tree work (the rest copy rows)
+  uint32_t run_first[2], run_len[2];  // touched partitions: two disjoint runs
+  uint32_t ntree;                     // blocks doing tree work (the rest copy rows)
+  int src, dst;                       // running-max slots: read / raise
   const float* states;
   const float* next_states;
   const uint32_t* actions;
@@ -528,36 +709,103 @@ __global__ void __launch_bounds__(256) add_kernel(TreePtrs t, Geom g, Storage st
     return;
   }
   const uint32_t w = blockIdx.x;
-  const uint32_t part = (w < a.run_len[0]) ? a.run_first[0] + w : a.run_first[1] + (w - a.run_len[0]);
+  const uint32_t part =
+      (w < a.run_len[0]) ? a.run_first[0] + w : a.run_first[1] + (w - a.run_len[0]);
   const uint32_t span = 1u << g.S;
   const uint32_t base = part << g.S;
-  const float m0 = t.ctrl->maxp;
-  clear_partition_tables(sm, g, false);
-  __syncthreads();
-  // The ring range [cursor, cursor + count) split at the wrap.
+  // The ring range [cursor, cursor + count) split at the wrap, clipped to
+  // this partition: one or two runs of offsets.
   const uint64_t end = (uint64_t)a.cursor + a.count;
   const uint32_t r_lo[2] = {a.cursor, 0u};
   const uint32_t r_hi[2] = {(uint32_t)(end < g.n ? end : g.n),
                             (uint32_t)(end > g.n ? end - g.n : 0u)};
-  float pmax = 0.0f;
-  bool any = false;
+  uint32_t lo[2], hi[2];
+  int runs = 0;
   for (int r = 0; r < 2; ++r) {
-    const uint32_t lo = max(r_lo[r], base), hi = min(r_hi[r], base + span);
-    for (uint32_t slot = lo + threadIdx.x; slot < hi; slot += kTreeThreads) {
+    const uint32_t l = max(r_lo[r], base), h = min(r_hi[r], base + span);
+    if (l < h) {
+      lo[runs] = l - base;
+      hi[runs] = h - base;
+      ++runs;
+    }
+  }
+  // One run (the usual case): its boundary siblings go out with the other loads.
+  if (runs == 1) prefetch_range_boundaries(sm, t, g, part, lo[0], hi[0]);
+  const float m0 = __uint_as_float(t.ctrl->maxp_bits[a.src]);
+  if (runs == 2) clear_bits(sm, g);
+  uint32_t mb = 0;
+  for (int r = 0; r < runs; ++r) {
+    for (uint32_t off = lo[r] + threadIdx.x; off < hi[r]; off += kTreeThreads) {
+      const uint32_t slot = base + off;
       const uint32_t j = (slot >= a.cursor) ? slot - a.cursor : slot + (g.n - a.cursor);
       float p = m0;
       if (a.prio) {
         p = a.prio[j] + 0.0f;
-        pmax = any ? fmaxf(pmax, p) : p;
-        any = true;
+        mb = max(mb, __float_as_uint(p));
       }
-      set_winner(sm, slot - base, p);
+      sm.val[off] = p;
     }
   }
-  if (a.prio) publish_batch_max(sm, t, pmax, any);
+  if (a.prio) {
+    mb = block_max_bits(mb, sm);
+    if (threadIdx.x == 0) {
+      if (w == 0) mb = max(mb, __float_as_uint(m0));
+      atomicMax(&t.ctrl->maxp_bits[a.dst], mb);
+    }
+  }
+  __syncthreads();
+  if (runs == 1) {
+    range_repair(sm, t, g, part, lo[0], hi[0]);
+    return;
+  }
+  // Two runs in one partition (the ring wrapped inside it): general repair.
+  for (int r = 0; r < runs; ++r)
+    for (uint32_t off = lo[r] + threadIdx.x; off < hi[r]; off += kTreeThreads)
+      atomicOr(&sm.bits[off >> 5], 1u << (off & 31));
   __syncthreads();
   repair_partition(sm, t, g, part);
-  finish(sm, t, g, m0, a.ntree, nullptr, nullptr);
+}
+
+// Nodes [1, 2^P) above the partitions, recomputed from depth P upwards.
+__global__ void __launch_bounds__(256) top_kernel(TreePtrs t, Geom g) {
+  __shared__ PartSmem sm;
+  const uint32_t np = 1u << g.P;
+  if (g.P <= kMaxTopBits) {
+    const uint32_t half = np >> 1;
+    for (uint32_t h = half + threadIdx.x; h < np; h += kTreeThreads) {
+      const float2 cs = *reinterpret_cast<const float2*>(t.sum + 2 * h);
+      const float2 cm = *reinterpret_cast<const float2*>(t.mn + 2 * h);
+      const float s = cs.x + cs.y, m = min_f32(cm.x, cm.y);
+      sm.u.heap.s[h] = s;
+      sm.u.heap.m[h] = m;
+      t.sum[h] = s;
+      t.mn[h] = m;
+    }
+    for (uint32_t width = half >> 1; width >= 1; width >>= 1) {
+      __syncthreads();
+      for (uint32_t h = width + threadIdx.x; h < 2 * width; h += kTreeThreads) {
+        const float s = sm.u.heap.s[2 * h] + sm.u.heap.s[2 * h + 1];
+        const float m = min_f32(sm.u.heap.m[2 * h], sm.u.heap.m[2 * h + 1]);
+        sm.u.heap.s[h] = s;
+        sm.u.heap.m[h] = m;
+        t.sum[h] = s;
+        t.mn[h] = m;
+      }
+    }
+  } else {
+    // More top nodes than LDS holds: level by level through global memory.
+    for (int l = g.P - 1; l >= 0; --l) {
+      const uint32_t lo = 1u << l;
+      for (uint32_t h = lo + threadIdx.x; h < 2 * lo; h += kTreeThreads) {
+        const float2 cs = *reinterpret_cast<const float2*>(t.sum + 2 * h);
+        const float2 cm = *reinterpret_cast<const float2*>(t.mn + 2 * h);
+        t.sum[h] = cs.x + cs.y;
+        t.mn[h] = min_f32(cm.x, cm.y);
+      }
+      __threadfence_block();
+      __syncthreads();
+    }
+  }
 }
 
 inline unsigned grid_for(uint64_t work, unsigned per_block, unsigned cap) {
@@ -575,9 +823,14 @@ hipError_t launch_init(const TreePtrs& t, const Buckets& bk, const Geom& g, hipS
   return hipGetLastError();
 }
 
+hipError_t launch_top(const TreePtrs& t, const Geom& g, hipStream_t s) {
+  hipLaunchKernelGGL(top_kernel, dim3(1), dim3(kTreeThreads), 0, s, t, g);
+  return hipGetLastError();
+}
+
 hipError_t launch_update(const TreePtrs& t, const Buckets& bk, const Geom& g, uint32_t size,
                          int64_t B, const int64_t* idx, const float* td, double alpha,
-                         double eps, hipStream_t s) {
+                         double eps, int src, int dst, hipStream_t s) {
   UpdateArgs a;
   a.idx = idx;
   a.td = td;
@@ -586,9 +839,12 @@ hipError_t launch_update(const TreePtrs& t, const Buckets& bk, const Geom& g, ui
   a.alpha = alpha;
   a.eps = eps;
   a.p_nan = (float)pow(eps, alpha);
+  a.src = src;
+  a.dst = dst;
   const uint64_t np = 1ull << g.P;
-  // Scanning costs np * B loads; past ~4M use the bucketed path.
-  if (np * (uint64_t)B <= (1ull << 22)) {
+  // Every partition block scans the batch: np * B loads in all.  Past ~4M
+  // loads, or for batches the LDS list could not hold, bucket first.
+  if (np * (uint64_t)B <= (1ull << 22) && B <= 8192) {
     hipLaunchKernelGGL(update_scan_kernel, dim3((unsigned)np), dim3(kTreeThreads), 0, s, t, g,
                        a);
     return hipGetLastError();
@@ -605,11 +861,13 @@ hipError_t launch_update(const TreePtrs& t, const Buckets& bk, const Geom& g, ui
 hipError_t launch_add(const TreePtrs& t, const Geom& g, const Storage& st, uint32_t cursor,
                       uint32_t count, const float* states, const float* next_states,
                       const uint32_t* actions, const float* rewards, const uint8_t* dones,
-                      const float* prio, hipStream_t s) {
+                      const float* prio, int src, int dst, hipStream_t s) {
   AddArgs a;
   a.cursor = cursor;
   a.count = count;
   a.prio = prio;
+  a.src = src;
+  a.dst = dst;
   a.states = states;
   a.next_states = next_states;
   a.actions = actions;
@@ -623,13 +881,9 @@ hipError_t launch_add(const TreePtrs& t, const Geom& g, const Storage& st, uint3
   bool second = end > g.n;
   if (second) {
     l1 = (uint32_t)(end - g.n - 1) >> g.S;
-    f1 = 0;
-    if (l1 >= f0) {  // the runs meet: one run covers everything touched
+    if (l1 + 1 >= f0) {  // the two runs meet or overlap: one run over every partition
       f0 = 0;
       l0 = (1u << g.P) - 1;
-      second = false;
-    } else if (l1 + 1 == f0) {
-      f0 = 0;
       second = false;
     }
   }
@@ -639,7 +893,8 @@ hipError_t launch_add(const TreePtrs& t, const Geom& g, const Storage& st, uint3
   a.run_len[1] = second ? (l1 - f1 + 1) : 0;
   a.ntree = a.run_len[0] + a.run_len[1];
   unsigned ncopy = 0;
-  if (st.D > 0) ncopy = grid_for((uint64_t)count * (uint64_t)st.D / 4 + count, kTreeThreads * 4, 2048);
+  if (st.D > 0)
+    ncopy = grid_for((uint64_t)count * (uint64_t)st.D / 4 + count, kTreeThreads * 4, 2048);
   hipLaunchKernelGGL(add_kernel, dim3(a.ntree + ncopy), dim3(kTreeThreads), 0, s, t, g, st, a);
   return hipGetLastError();
 }

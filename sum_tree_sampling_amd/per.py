@@ -45,6 +45,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
         "per_add": (c_int, [vp, i64, vp, vp, vp, vp, vp, vp, vp]),
         "per_update": (c_int, [vp, i64, vp, vp, vp]),
         "per_sample": (c_int, [vp, i64, vp, f64, vp, vp, vp, vp, vp, vp, vp, vp]),
+        "per_flush": (c_int, [vp, vp]),
         "per_total": (c_int, [vp, vp, vp]),
         "per_min": (c_int, [vp, vp, vp]),
         "per_max_priority": (c_int, [vp, vp, vp]),
@@ -125,6 +126,10 @@ def per_sample(h, B, u, beta, idx_out, w_out=None, states_out=None, next_states_
     _check(load().per_sample(h, int(B), _p(u), float(beta), _p(idx_out), _p(w_out),
                              _p(states_out), _p(next_states_out), _p(actions_out),
                              _p(rewards_out), _p(dones_out), _stream(stream)))
+
+
+def per_flush(h, stream=None) -> None:
+    _check(load().per_flush(h, _stream(stream)))
 
 
 def per_total(h, out, stream=None) -> None:
@@ -216,11 +221,13 @@ class PerBuffer:
     def cursor(self) -> int:
         return per_cursor(self.h)
 
-    def sum_tree(self) -> torch.Tensor:
-        """Device view of the [2n] sum tree (index 0 unused)."""
+    def sum_tree(self, stream=None) -> torch.Tensor:
+        """Device view of the [2n] sum tree (index 0 unused), flushed first."""
+        per_flush(self.h, stream)
         return self._sum
 
-    def min_tree(self) -> torch.Tensor:
+    def min_tree(self, stream=None) -> torch.Tensor:
+        per_flush(self.h, stream)
         return self._min
 
     def add(self, count, states=None, next_states=None, actions=None, rewards=None, dones=None,

@@ -41,6 +41,8 @@ def test_workload_parity(name):
         ro = o.sample(u, beta=s["beta"], weights=True, rows=rows)
         rg = g.sample(dev(u), beta=s["beta"], weights=True, rows=rows)
         compare_sample(rg, ro, "%s step %d sample" % (name, step), rows=rows)
+        # the sampler rebuilt the top levels in LDS and wrote them back
+        compare_trees(o, g, "%s step %d after sample" % (name, step))
         idx = inp.update_idx() if "unique" in s else ro["idx"]
         td = inp.td()
         o.update(idx, td)
@@ -71,14 +73,13 @@ def test_sampler_modes_agree(mode, monkeypatch):
     for lo in range(0, idx.size, 20000):
         g.update(dev(idx[lo:lo + 20000]), dev(td[lo:lo + 20000]))
     compare_trees(o, g, "mode %s prep" % mode)
-    for top in (None, "0", "4", "9"):
-        if top is not None:
-            monkeypatch.setenv("PER_SAMPLE_TOP", top)
+    for rep in range(3):
         u = inp.u()
         u[:3] = [0.0, np.nextafter(np.float32(1), np.float32(0)), 0.5]
         ro = o.sample(u, beta=0.4, rows=True)
         rg = g.sample(dev(u), beta=0.4, rows=True)
-        compare_sample(rg, ro, "mode %s top %s" % (mode, top), rows=True)
+        compare_sample(rg, ro, "mode %s batch %d" % (mode, rep), rows=True)
+        compare_trees(o, g, "mode %s batch %d tree" % (mode, rep))
 
 
 def test_zero_priorities_never_sampled():
@@ -227,6 +228,35 @@ def test_scalars_and_errors():
     assert float(host(g.scalar("total"))[0]) == 256.0
     assert float(host(g.scalar("min"))[0]) == 0.25
     assert float(host(g.scalar("max_priority"))[0]) == 1.0
+
+
+def test_top_deeper_than_lds():
+    """2^25 leaves: 2^13 partitions, so the levels above them are rebuilt by
+    the one-block top kernel through global memory before sampling."""
+    n = 1 << 25
+    say("deep top", n)
+    rng = np.random.default_rng(25)
+    o = Oracle(n)
+    g = _buf(n, max_batch=2048)
+    p0 = rng.random(n).astype(np.float32)
+    o.add(n, prio=p0)
+    g.add(n, prio=dev(p0))
+    compare_trees(o, g, "2^25 fill")
+    for step in range(2):
+        u = rng.random(2048, dtype=np.float32)
+        for mode in ("1", "2", "3"):
+            os.environ["PER_SAMPLE_MODE"] = mode
+            try:
+                compare_sample(g.sample(dev(u)), o.sample(u), "2^25 mode " + mode)
+            finally:
+                del os.environ["PER_SAMPLE_MODE"]
+        idx = rng.integers(0, n, 2048).astype(np.int64)
+        td = rng.standard_normal(2048).astype(np.float32)
+        o.update(idx, td)
+        g.update(dev(idx), dev(td))
+        u = rng.random(100, dtype=np.float32)
+        compare_sample(g.sample(dev(u)), o.sample(u), "2^25 after update %d" % step)
+        compare_trees(o, g, "2^25 step %d" % step)
 
 
 # ------------------------------------------------------------ full-size large buffer
