@@ -76,16 +76,21 @@ def _p(t) -> int | None:
         return None
     if isinstance(t, int):
         return t
-    if not t.is_cuda:
-        raise ValueError("expected a device tensor")
-    if not t.is_contiguous():
-        raise ValueError("expected a contiguous tensor")
+    if not (t.is_cuda and t.is_contiguous()):
+        raise ValueError("expected a contiguous device tensor")
     return t.data_ptr()
 
 
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(stream=None) -> int:
-    s = stream if stream is not None else torch.cuda.current_stream()
-    return s.cuda_stream if hasattr(s, "cuda_stream") else int(s)
+    """hipStream_t of `stream`, or of torch's current stream on the current device."""
+    if stream is None:
+        if _raw_stream is not None:
+            return _raw_stream(torch.cuda.current_device())
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
 # ---------------------------------------------------------------- C names
