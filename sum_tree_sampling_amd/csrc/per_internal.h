@@ -8,8 +8,8 @@
 namespace per {
 
 // Leaves per partition = 2^kMaxSpanBits.  The batched update and the intake
-// work one workgroup per partition (an aligned subtree) and finish the few
-// levels above the partitions in the last workgroup to complete.
+// work one workgroup per partition (an aligned subtree); the few levels above
+// the partitions are rebuilt lazily (by the sampler, or by top_kernel).
 constexpr int kMaxSpanBits = 12;
 constexpr int kMaxSpan = 1 << kMaxSpanBits;
 // Partitions holding at most this many updated leaves are repaired by one

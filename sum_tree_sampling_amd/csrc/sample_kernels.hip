@@ -262,28 +262,50 @@ __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleArgs a) {
   }
 
   if (a.states_out) {
-    // Wave-cooperative row copy of the wave's SPW samples.
+    // Wave-cooperative row copy of the wave's SPW samples, in batches of
+    // kBatch accesses per lane: every load of a batch is issued before the
+    // first store, so each lane keeps kBatch 16-byte reads in flight.
+    constexpr int kBatch = 8;
     const uint32_t D = (uint32_t)a.st.D;
     const bool vec = (D & 3u) == 0u;
     const uint32_t per_row = vec ? D / 4 : D;  // accesses per row
     const uint32_t total = SPW * 2u * per_row;
     const uint32_t wave_b0 = wave * SPW;
-    for (uint32_t t0 = 0; t0 < total; t0 += 64) {
-      const uint32_t t = t0 + lane;
-      uint32_t s = t / (2u * per_row);
-      if (s >= SPW) s = SPW - 1;
-      const uint32_t slot_s = (uint32_t)__shfl((int)slot, (int)s * G);
-      const uint32_t bs = wave_b0 + s;
-      if (t < total && bs < a.B) {
+    for (uint32_t t0 = 0; t0 < total; t0 += 64 * kBatch) {
+      float4 buf[kBatch];
+      float* dst[kBatch];
+      bool ok[kBatch];
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q) {
+        const uint32_t t = t0 + q * 64 + lane;
+        uint32_t s = t / (2u * per_row);
+        if (s >= SPW) s = SPW - 1;
+        const uint32_t slot_s = (uint32_t)__shfl((int)slot, (int)s * G);
+        const uint32_t bs = wave_b0 + s;
+        ok[q] = t < total && bs < a.B;
         const uint32_t rem = t - s * 2u * per_row;
         const bool nxt = rem >= per_row;
         const uint32_t c = nxt ? rem - per_row : rem;
         const float* src = (nxt ? a.st.next_states : a.st.states) + (uint64_t)slot_s * D;
-        float* dst = (nxt ? a.next_out : a.states_out) + (uint64_t)bs * D;
-        if (vec) {
-          *reinterpret_cast<float4*>(dst + 4u * c) = *reinterpret_cast<const float4*>(src + 4u * c);
-        } else {
-          dst[c] = src[c];
+        dst[q] = (nxt ? a.next_out : a.states_out) + (uint64_t)bs * D;
+        buf[q] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if (ok[q]) {
+          if (vec) {
+            buf[q] = *reinterpret_cast<const float4*>(src + 4u * c);
+            dst[q] += 4u * c;
+          } else {
+            buf[q].x = src[c];
+            dst[q] += c;
+          }
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q) {
+        if (ok[q]) {
+          if (vec)
+            *reinterpret_cast<float4*>(dst[q]) = buf[q];
+          else
+            *dst[q] = buf[q].x;
         }
       }
     }
