@@ -22,6 +22,7 @@ struct per_s {
   per::Storage st;
   int64_t size, cursor;
   int epoch;       // committed running-max slot
+  int ovf;         // overflow counter for the next bucketed update
   bool top_stale;  // nodes above the partitions not yet rebuilt
   int device;
 };
@@ -88,26 +89,25 @@ namespace per {
 Layout workspace_layout(int64_t n, int64_t max_batch) {
   const Geom g = make_geom(n);
   const size_t np = size_t(1) << g.P;
+  const size_t nb = np * kBucketCap;
   Layout l;
   size_t o = 0;
-  l.sum = o;
-  o = align256(o + sizeof(float) * 2 * (size_t)n);
-  l.mn = o;
-  o = align256(o + sizeof(float) * 2 * (size_t)n);
-  l.ctrl = o;
-  o = align256(o + sizeof(Ctrl));
-  l.counts = o;
-  o = align256(o + sizeof(uint32_t) * np);
-  l.fill = o;
-  o = align256(o + sizeof(uint32_t) * np);
-  l.offs = o;
-  o = align256(o + sizeof(uint32_t) * (np + 1));
-  l.slot = o;
-  o = align256(o + sizeof(uint32_t) * (size_t)max_batch);
-  l.pos = o;
-  o = align256(o + sizeof(uint32_t) * (size_t)max_batch);
-  l.td = o;
-  o = align256(o + sizeof(float) * (size_t)max_batch);
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align256(o + bytes);
+    return at;
+  };
+  l.sum = take(sizeof(float) * 2 * (size_t)n);
+  l.mn = take(sizeof(float) * 2 * (size_t)n);
+  l.ctrl = take(sizeof(Ctrl));
+  l.counts = take(sizeof(uint32_t) * np);
+  l.ovf_n = take(sizeof(uint32_t) * 2);
+  l.slot = take(sizeof(uint32_t) * nb);
+  l.pos = take(sizeof(uint32_t) * nb);
+  l.td = take(sizeof(float) * nb);
+  l.oslot = take(sizeof(uint32_t) * (size_t)max_batch);
+  l.opos = take(sizeof(uint32_t) * (size_t)max_batch);
+  l.otd = take(sizeof(float) * (size_t)max_batch);
   l.total = o;
   return l;
 }
@@ -166,11 +166,13 @@ int per_create(per_t** out, int64_t capacity, int32_t state_dim, int64_t max_bat
   h->t.mn = reinterpret_cast<float*>(base + lay.mn);
   h->t.ctrl = reinterpret_cast<per::Ctrl*>(base + lay.ctrl);
   h->bk.counts = reinterpret_cast<uint32_t*>(base + lay.counts);
-  h->bk.fill = reinterpret_cast<uint32_t*>(base + lay.fill);
-  h->bk.offs = reinterpret_cast<uint32_t*>(base + lay.offs);
+  h->bk.ovf_n = reinterpret_cast<uint32_t*>(base + lay.ovf_n);
   h->bk.slot = reinterpret_cast<uint32_t*>(base + lay.slot);
   h->bk.pos = reinterpret_cast<uint32_t*>(base + lay.pos);
   h->bk.td = reinterpret_cast<float*>(base + lay.td);
+  h->bk.oslot = reinterpret_cast<uint32_t*>(base + lay.oslot);
+  h->bk.opos = reinterpret_cast<uint32_t*>(base + lay.opos);
+  h->bk.otd = reinterpret_cast<float*>(base + lay.otd);
   h->st.states = d_states;
   h->st.next_states = d_next_states;
   h->st.actions = d_actions;
@@ -180,6 +182,7 @@ int per_create(per_t** out, int64_t capacity, int32_t state_dim, int64_t max_bat
   h->size = 0;
   h->cursor = 0;
   h->epoch = 0;
+  h->ovf = 0;
   h->top_stale = false;
   if (hipGetDevice(&h->device) != hipSuccess) h->device = -1;
   hipError_t e = per::launch_init(h->t, h->bk, h->g, stream);
@@ -232,9 +235,10 @@ int per_update(per_t* h, int64_t B, const int64_t* d_idx, const float* d_td,
   if (B == 0) return ok();
   if (!d_idx || !d_td) return fail(PER_EINVAL, "idx and td are required");
   hipError_t e = per::launch_update(h->t, h->bk, h->g, (uint32_t)h->size, B, d_idx, d_td,
-                                    h->alpha, h->eps, h->epoch, h->epoch ^ 1, stream);
+                                    h->alpha, h->eps, h->epoch, h->epoch ^ 1, h->ovf, stream);
   if (e != hipSuccess) return hip_fail(e, "per_update");
   h->epoch ^= 1;
+  if (per::update_uses_buckets(h->g, B)) h->ovf ^= 1;
   h->top_stale = h->g.P > 0;
   return ok();
 }

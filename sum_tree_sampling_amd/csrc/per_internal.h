@@ -38,19 +38,23 @@ struct Geom {
 };
 
 struct TreePtrs {
-  float* sum;      // [2n]
-  float* mn;       // [2n]
+  float* sum;      // [2n] sum tree; index 0 unused
+  float* mn;       // [2n] min tree
   Ctrl* ctrl;
 };
 
-// Scratch of the bucketed (large-batch) update.
+// Scratch of the bucketed (large-batch) update: a bucket of kBucketCap
+// entries per partition and an overflow list for the rest.
+constexpr int kBucketCap = kSparseMax;
 struct Buckets {
-  uint32_t* counts;   // [2^P] entries per partition
-  uint32_t* fill;     // [2^P] fill cursors
-  uint32_t* offs;     // [2^P + 1] exclusive prefix of counts
-  uint32_t* slot;     // [max_batch] leaf slot of each bucketed entry
-  uint32_t* pos;      // [max_batch] its batch position
-  float* td;          // [max_batch] its TD error
+  uint32_t* counts;   // [2^P] entries per partition (reset by the update)
+  uint32_t* ovf_n;    // [2] overflow counters, used by alternate calls
+  uint32_t* slot;     // [2^P * kBucketCap] leaf slot of each bucketed entry
+  uint32_t* pos;      // its batch position
+  float* td;          // its TD error
+  uint32_t* oslot;    // [max_batch] overflow entries
+  uint32_t* opos;
+  float* otd;
 };
 
 struct Storage {
@@ -64,7 +68,7 @@ struct Storage {
 
 // Workspace layout (byte offsets from the 256-byte aligned base).
 struct Layout {
-  size_t sum, mn, ctrl, counts, fill, offs, slot, pos, td, total;
+  size_t sum, mn, ctrl, counts, ovf_n, slot, pos, td, oslot, opos, otd, total;
 };
 Layout workspace_layout(int64_t n, int64_t max_batch);
 
@@ -85,9 +89,12 @@ struct SamplePlan {
 hipError_t launch_init(const TreePtrs& t, const Buckets& bk, const Geom& g, hipStream_t s);
 
 // Batched update; B > 0.  src / dst: running-max slots to read / raise.
+// ovf: overflow counter of this call when the batch is bucketed (see
+// update_uses_buckets); alternate calls must alternate it.
 hipError_t launch_update(const TreePtrs& t, const Buckets& bk, const Geom& g, uint32_t size,
                          int64_t B, const int64_t* idx, const float* td, double alpha,
-                         double eps, int src, int dst, hipStream_t s);
+                         double eps, int src, int dst, int ovf, hipStream_t s);
+bool update_uses_buckets(const Geom& g, int64_t B);
 
 // Rebuild of the nodes above the partitions (one block).
 hipError_t launch_top(const TreePtrs& t, const Geom& g, hipStream_t s);

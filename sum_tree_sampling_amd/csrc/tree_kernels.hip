@@ -3,7 +3,8 @@
 //
 // Tree layout ("Putting prioritized replay's segment tree on a GPU", section
 // "The Tree Under Every Prioritized Replay"): node i has children 2i and
-// 2i+1, leaves at [n, 2n), sum tree and twin min tree in two [2n] f32 arrays.
+// 2i+1, leaves at [n, 2n).  The sum tree and its twin min tree are two
+// separate arrays of 2n f32 with the same indexing.
 //
 // Both writers (update and intake) follow the same plan:
 //  1. The leaves are cut into 2^P aligned partitions of 2^S leaves (S <= 12);
@@ -16,8 +17,10 @@
 //     repaired by one wave: each leaf's lane walks up its own chain until it
 //     meets the chain of its right neighbour; siblings along the chains are
 //     fetched in one round of independent loads and values meet through lane
-//     shuffles, so the levels stay ordered without a barrier.  Dense
-//     partitions are rebuilt level by level in LDS, a barrier between levels.
+//     shuffles, so the levels stay ordered without a barrier.  Crowded
+//     partitions are rebuilt level by level in LDS, one 1024-leaf
+//     sub-partition at a time, a barrier between levels.  A contiguous intake
+//     run is rebuilt from its range and the two boundary paths.
 //  3. The 2^P - 1 nodes above the partitions are not touched by the writers.
 //     They are a pure function of the partition roots, and the sampler
 //     rebuilds them in LDS anyway to walk the top of the tree; its first
@@ -38,7 +41,9 @@
 namespace per {
 namespace {
 
-constexpr int kListCap = 1024;  // entries a partition block keeps in LDS
+constexpr int kSubBits = 10;  // crowded partitions are rebuilt in 2^10-leaf pieces
+constexpr int kUpdThreads = 256;  // threads of an update block
+constexpr int kSub = 1 << kSubBits;
 
 __device__ __forceinline__ float min_f32(float a, float b) { return (b < a) ? b : a; }
 
@@ -54,40 +59,15 @@ __device__ __forceinline__ float priority_of(float td, float max_at_start, doubl
   return (float)pow((double)x + eps, alpha);
 }
 
-struct Entry {
-  uint32_t off;  // slot offset inside the partition
-  uint32_t pos;  // batch position
-  float p;       // its priority
-};
+// ------------------------------------------------------------ block helpers
 
-struct PartSmem {
-  float val[kMaxSpan];  // new leaf value by offset in the partition
-  union {
-    struct {
-      int owner[kMaxSpan];     // last batch position per offset
-      Entry ent[kListCap];     // this partition's entries
-    } d;
-    struct {
-      float s[kMaxSpan];
-      float m[kMaxSpan];
-    } heap;                    // local heap [1, 2^S) / top nodes [1, 2^P)
-  } u;
-  uint32_t bits[kMaxSpan / 32];  // offsets that receive a new leaf
-  uint8_t dirty[kMaxSpan];       // dense repair: node has a new leaf below it
-  uint16_t list[kSparseMax];     // sorted offsets of a sparse partition
-  float sib_s[kSparseMax][kMaxSpanBits];  // prefetched siblings along each
-  float sib_m[kSparseMax][kMaxSpanBits];  // of the first 64 entries' chains
-  uint64_t key[kSparseMax];      // (offset << 32 | batch position) of those entries
-  float pval[kSparseMax];        // and their priorities
-  uint8_t order[kSparseMax];     // sparse wave: entry at each sorted position
-  uint32_t bmax;                 // max priority bits of the block's entries
+struct BlockScratch {
   int wsum[kTreeThreads / 64];
   uint32_t wmax[kTreeThreads / 64];
-  int count;
 };
 
 // Exclusive scan of one int per thread over the 256-thread block.
-__device__ int block_excl_scan(int v, PartSmem& sm, int* total) {
+__device__ int block_excl_scan(int v, BlockScratch& sx, int* total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   int x = v;
 #pragma unroll
@@ -95,13 +75,13 @@ __device__ int block_excl_scan(int v, PartSmem& sm, int* total) {
     int y = __shfl_up(x, o);
     if (lane >= o) x += y;
   }
-  if (lane == 63) sm.wsum[w] = x;
+  if (lane == 63) sx.wsum[w] = x;
   __syncthreads();
   int off = 0, tot = 0;
 #pragma unroll
   for (int k = 0; k < kTreeThreads / 64; ++k) {
-    off += (k < w) ? sm.wsum[k] : 0;
-    tot += sm.wsum[k];
+    off += (k < w) ? sx.wsum[k] : 0;
+    tot += sx.wsum[k];
   }
   __syncthreads();
   *total = tot;
@@ -114,41 +94,31 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return v;
 }
 
-// Block max of f32 bit patterns of non-negative values (0 if none).
-__device__ uint32_t block_max_bits(uint32_t v, PartSmem& sm) {
+// Block max of f32 bit patterns of non-negative values (0 if none); NT
+// threads per block.
+template <int NT = kTreeThreads>
+__device__ uint32_t block_max_bits(uint32_t v, BlockScratch& sx) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   v = wave_max_u32(v);
-  if (lane == 0) sm.wmax[w] = v;
+  if (NT == 64) return v;
+  if (lane == 0) sx.wmax[w] = v;
   __syncthreads();
   uint32_t r = 0;
 #pragma unroll
-  for (int k = 0; k < kTreeThreads / 64; ++k) r = max(r, sm.wmax[k]);
+  for (int k = 0; k < NT / 64; ++k) r = max(r, sx.wmax[k]);
   __syncthreads();
   return r;
 }
 
-__device__ __forceinline__ bool has_bit(const PartSmem& sm, uint32_t off) {
-  return (sm.bits[off >> 5] >> (off & 31)) & 1u;
-}
-
-// Position of the r-th (0-based) set bit of mask; mask has more than r bits.
-__device__ __forceinline__ int nth_set_bit(uint64_t mask, int r) {
-  int pos = 0;
-#pragma unroll
-  for (int w = 32; w >= 1; w >>= 1) {
-    const uint64_t below = (1ull << (pos + w)) - 1ull;
-    if (__popcll(mask & below) <= r) pos += w;
-  }
-  return pos;
-}
+// ------------------------------------------------------------ sparse chains
 
 // Sparse repair by one wave.  Lanes [0, m) hold the new leaves of the
 // partition sorted by offset (offset off, value p); `valid` marks one lane
 // per distinct offset (the others are ignored) and ps / pm hold the stored
-// values of the siblings of the lane's ancestors (index k: the ancestor k
-// levels above the leaf's parent level, 0 = the leaf's sibling).  d_i is the
-// depth of the lowest common ancestor of the leaves of lanes i and i+1 (P-1
-// for the last lane, whose chain ends at the partition root).  Lane i
+// values of the siblings of the lane's ancestors (index k: the sibling of
+// the ancestor k levels above the leaf, 0 = the leaf's own sibling).  d_i is
+// the depth of the lowest common ancestor of the leaves of lanes i and i+1
+// (P-1 for the last lane, whose chain ends at the partition root).  Lane i
 // computes the nodes of its chain at depths L-1 .. d_i+1: it is the last
 // (rightmost) new leaf under each of them.  When lane i's path enters a node
 // X from the right child, X's left child holds new leaves iff the nearest
@@ -202,123 +172,47 @@ __device__ void sparse_chain(const TreePtrs& t, const Geom& g, uint32_t part, in
         vs = vs + os;
         vm = min_f32(vm, om);
       }
-      const uint32_t parent = child >> 1;
-      t.sum[parent] = vs;
-      t.mn[parent] = vm;
+      t.sum[child >> 1] = vs;
+      t.mn[child >> 1] = vm;
     }
   }
 }
 
-// Dense repair by the whole block: rebuild the partition's subtree in LDS and
-// write back the nodes with a new leaf below them.  All old leaves are loaded
-// before anything is stored, so the loads go out in one round.
-__device__ void dense_repair(PartSmem& sm, const TreePtrs& t, const Geom& g, uint32_t part) {
-  constexpr int kPairs = kMaxSpan / 2 / kTreeThreads;  // leaf pairs per thread
-  const uint32_t span = 1u << g.S, half = span >> 1;
-  const uint32_t root = (1u << g.P) + part;
-  const uint32_t leaf0 = g.n + (part << g.S);
-  float2 os[kPairs], om[kPairs];
-#pragma unroll
-  for (int r = 0; r < kPairs; ++r) {
-    os[r] = om[r] = make_float2(0.0f, 0.0f);
-    const uint32_t h = half + threadIdx.x + r * kTreeThreads;
-    if (h < span) {
-      const uint32_t a = 2 * h - span;
-      if (!(has_bit(sm, a) && has_bit(sm, a + 1))) {
-        os[r] = *reinterpret_cast<const float2*>(t.sum + leaf0 + a);
-        om[r] = *reinterpret_cast<const float2*>(t.mn + leaf0 + a);
-      }
-    }
-  }
-#pragma unroll
-  for (int r = 0; r < kPairs; ++r) {
-    const uint32_t h = half + threadIdx.x + r * kTreeThreads;
-    if (h < span) {
-      const uint32_t a = 2 * h - span;
-      const bool ba = has_bit(sm, a), bb = has_bit(sm, a + 1);
-      const float ls = ba ? sm.val[a] : os[r].x, lm = ba ? sm.val[a] : om[r].x;
-      const float rs = bb ? sm.val[a + 1] : os[r].y, rm = bb ? sm.val[a + 1] : om[r].y;
-      if (ba) {
-        t.sum[leaf0 + a] = ls;
-        t.mn[leaf0 + a] = lm;
-      }
-      if (bb) {
-        t.sum[leaf0 + a + 1] = rs;
-        t.mn[leaf0 + a + 1] = rm;
-      }
-      const float s = ls + rs, m = min_f32(lm, rm);
-      sm.u.heap.s[h] = s;
-      sm.u.heap.m[h] = m;
-      sm.dirty[h] = ba | bb;
-      if (ba | bb) {
-        const uint32_t gnode = ((root - 1u) << (g.S - 1)) + h;
-        t.sum[gnode] = s;
-        t.mn[gnode] = m;
-      }
-    }
-  }
-  // local heap index h in [1, span) <-> global node ((root - 1) << depth(h)) + h
-  for (uint32_t width = half >> 1, dl = g.S - 2; width >= 1; width >>= 1, --dl) {
-    __syncthreads();
-    for (uint32_t h = width + threadIdx.x; h < 2 * width; h += kTreeThreads) {
-      const float s = sm.u.heap.s[2 * h] + sm.u.heap.s[2 * h + 1];
-      const float m = min_f32(sm.u.heap.m[2 * h], sm.u.heap.m[2 * h + 1]);
-      const uint8_t dv = sm.dirty[2 * h] | sm.dirty[2 * h + 1];
-      sm.u.heap.s[h] = s;
-      sm.u.heap.m[h] = m;
-      sm.dirty[h] = dv;
-      if (dv) {
-        const uint32_t gnode = ((root - 1u) << dl) + h;
-        t.sum[gnode] = s;
-        t.mn[gnode] = m;
-      }
-    }
-  }
-}
+// ------------------------------------------------------------ update LDS
 
-// Repair the partition once sm.val / sm.bits hold its new leaves (whole block).
-__device__ void repair_partition(PartSmem& sm, const TreePtrs& t, const Geom& g,
-                                 uint32_t part) {
-  const uint32_t nwords = ((1u << g.S) + 31) >> 5;
-  const uint32_t w = (threadIdx.x < nwords) ? sm.bits[threadIdx.x] : 0u;
-  int U;
-  const int before = block_excl_scan(__popc(w), sm, &U);
-  if (U == 0) return;
-  if (U <= kSparseMax) {
-    uint32_t x = w;
-    int r = before;
-    while (x) {
-      const int b = __ffs(x) - 1;
-      sm.list[r++] = (uint16_t)(threadIdx.x * 32 + b);
-      x &= x - 1;
-    }
-    __syncthreads();
-    if (threadIdx.x < 64) {
-      const bool valid = threadIdx.x < (unsigned)U;
-      const uint32_t off = valid ? sm.list[threadIdx.x] : 0u;
-      const uint32_t node = g.n + (part << g.S) + off;
-      float ps[kMaxSpanBits], pm[kMaxSpanBits];
-#pragma unroll
-      for (int k = 0; k < kMaxSpanBits; ++k) {
-        ps[k] = pm[k] = 0.0f;
-        if (k < g.S && valid) {
-          const uint32_t sib = (node >> k) ^ 1u;
-          ps[k] = t.sum[sib];
-          pm[k] = t.mn[sib];
-        }
-      }
-      sparse_chain(t, g, part, U, valid, off, sm.val[off], ps, pm);
-    }
-  } else {
-    dense_repair(sm, t, g, part);
-  }
-}
+struct SparseSmem {
+  float sib_s[kSparseMax][kMaxSpanBits];  // stored siblings along each of the
+  float sib_m[kSparseMax][kMaxSpanBits];  // first 64 entries' leaf paths
+  uint64_t key[kSparseMax];               // (offset << 32 | batch position)
+  float pval[kSparseMax];                 // priorities
+  uint8_t order[kSparseMax];              // entry at each sorted position
+};
 
-// Collect one entry of this block's partition into the LDS list (any
-// thread): the entry with its priority and, for the first 64 entries, the
-// stored siblings along its leaf's whole path to the partition root, loaded
-// before the priority's pow so that both latencies overlap.
-__device__ __forceinline__ void collect(PartSmem& sm, const TreePtrs& t, const Geom& g,
+struct DenseSmem {
+  int owner[kSub];         // last batch position per offset of the sub-partition
+  float val[kSub];         // its new leaf values
+  float hs[kSub], hm[kSub];  // local heap [1, 2^sb) of the sub-partition
+  uint8_t dirty[kSub];     // node has a new leaf below it
+  uint32_t bits[kSub / 32];  // offsets that receive a new leaf
+};
+
+struct UpdSmem {
+  union {
+    SparseSmem sp;
+    DenseSmem dn;
+  } u;
+  BlockScratch sx;
+  int count;      // entries collected
+  uint32_t bmax;  // max priority bits of the block's entries
+  uint32_t mtot;  // entries of the partition (bucketed path)
+  int flag;
+};
+
+// Collect one entry of this block's partition (any thread): its priority
+// and, for the first 64 entries, the stored siblings along its leaf's whole
+// path to the partition root, loaded before the priority's pow so that both
+// latencies overlap.
+__device__ __forceinline__ void collect(UpdSmem& sm, const TreePtrs& t, const Geom& g,
                                         uint32_t part, uint32_t off, uint32_t pos, float td,
                                         float m0, double alpha, double eps, float p_nan) {
   const int k = atomicAdd(&sm.count, 1);
@@ -336,25 +230,24 @@ __device__ __forceinline__ void collect(PartSmem& sm, const TreePtrs& t, const G
   }
   const float p = priority_of(td, m0, alpha, eps, p_nan);
   atomicMax(&sm.bmax, __float_as_uint(p));
-  if (k < kListCap) sm.u.d.ent[k] = Entry{off, pos, p};
   if (k < kSparseMax) {
-    sm.key[k] = ((uint64_t)off << 32) | pos;
-    sm.pval[k] = p;
+    sm.u.sp.key[k] = ((uint64_t)off << 32) | pos;
+    sm.u.sp.pval[k] = p;
 #pragma unroll
     for (int q = 0; q < kMaxSpanBits; ++q) {
       if (q < g.S) {
-        sm.sib_s[k][q] = ps[q];
-        sm.sib_m[k][q] = pm[q];
+        sm.u.sp.sib_s[k][q] = ps[q];
+        sm.u.sp.sib_m[k][q] = pm[q];
       }
     }
   }
 }
 
-// Publish the block's max priority into the raised running-max slot (one
-// thread; part 0 also carries the value at the start of the call over).
-__device__ __forceinline__ void publish_max(const PartSmem& sm, uint32_t part, float m0,
+// Raise the running-max slot by the block's max priority (one thread; part 0
+// also carries the value at the start of the call over).
+__device__ __forceinline__ void publish_max(uint32_t bmax, uint32_t part, float m0,
                                             uint32_t* max_dst) {
-  uint32_t mb = sm.bmax;
+  uint32_t mb = bmax;
   if (part == 0) mb = max(mb, __float_as_uint(m0));
   if (mb) atomicMax(max_dst, mb);
 }
@@ -364,72 +257,182 @@ __device__ __forceinline__ void publish_max(const PartSmem& sm, uint32_t part, f
 // counted from LDS (m is small) -- so that the last batch position of each
 // offset is the last of its run, and repair the chains of those winners with
 // the prefetched siblings.
-__device__ void wave_update(PartSmem& sm, const TreePtrs& t, const Geom& g, uint32_t part,
+__device__ void wave_update(SparseSmem& sp, const TreePtrs& t, const Geom& g, uint32_t part,
                             int m) {
   const int lane = threadIdx.x & 63;
   const bool in = lane < m;
-  const uint64_t mine = in ? sm.key[lane] : ~0ull;
+  const uint64_t mine = in ? sp.key[lane] : ~0ull;
   int rank = 0;
 #pragma unroll 4
-  for (int j = 0; j < m; ++j) rank += (sm.key[j] < mine) ? 1 : 0;
-  if (in) sm.order[rank] = (uint8_t)lane;
+  for (int j = 0; j < m; ++j) rank += (sp.key[j] < mine) ? 1 : 0;
+  if (in) sp.order[rank] = (uint8_t)lane;
   __builtin_amdgcn_wave_barrier();
-  const int src = in ? sm.order[lane] : 0;
-  const uint64_t key = sm.key[src];
+  const int src = in ? sp.order[lane] : 0;
+  const uint64_t key = sp.key[src];
   const uint32_t off = (uint32_t)(key >> 32);
-  const float p = sm.pval[src];
+  const float p = sp.pval[src];
   const uint32_t next_off = __shfl_down(off, 1);
   const bool win = in && (lane == m - 1 || next_off != off);
   float ps[kMaxSpanBits], pm[kMaxSpanBits];
 #pragma unroll
   for (int k = 0; k < kMaxSpanBits; ++k) {
-    ps[k] = sm.sib_s[src][k];
-    pm[k] = sm.sib_m[src][k];
+    ps[k] = sp.sib_s[src][k];
+    pm[k] = sp.sib_m[src][k];
   }
   sparse_chain(t, g, part, m, win, in ? off : 0u, p, ps, pm);
 }
 
-__device__ void clear_bits(PartSmem& sm, const Geom& g) {
-  const uint32_t nwords = ((1u << g.S) + 31) >> 5;
-  for (uint32_t k = threadIdx.x; k < nwords; k += kTreeThreads) sm.bits[k] = 0u;
+// ------------------------------------------------------------ crowded partitions
+
+__device__ __forceinline__ bool has_bit(const DenseSmem& dn, uint32_t off) {
+  return (dn.bits[off >> 5] >> (off & 31)) & 1u;
+}
+
+// Rebuild one sub-partition of 2^sb leaves (sb <= kSubBits) in LDS from its
+// new leaves (dn.val / dn.bits) and its stored old ones, and write back the
+// new leaves and every node with a new leaf below it.  subroot: node index
+// of the sub-partition's root; leaf0: node index of its first leaf.  All old
+// leaves are loaded before anything is stored.
+template <int NT>
+__device__ void dense_sub_rebuild(DenseSmem& dn, const TreePtrs& t, uint32_t subroot,
+                                  uint32_t leaf0, int sb) {
+  constexpr int kPairs = kSub / 2 / NT;
+  const uint32_t span = 1u << sb, half = span >> 1;
+  float2 os[kPairs], om[kPairs];
+#pragma unroll
+  for (int r = 0; r < kPairs; ++r) {
+    os[r] = om[r] = make_float2(0.0f, 0.0f);
+    const uint32_t h = half + threadIdx.x + r * NT;
+    if (h < span) {
+      const uint32_t a = 2 * h - span;
+      if (!(has_bit(dn, a) && has_bit(dn, a + 1))) {
+        os[r] = *reinterpret_cast<const float2*>(t.sum + leaf0 + a);
+        om[r] = *reinterpret_cast<const float2*>(t.mn + leaf0 + a);
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < kPairs; ++r) {
+    const uint32_t h = half + threadIdx.x + r * NT;
+    if (h < span) {
+      const uint32_t a = 2 * h - span;
+      const bool ba = has_bit(dn, a), bb = has_bit(dn, a + 1);
+      const float ls = ba ? dn.val[a] : os[r].x, lm = ba ? dn.val[a] : om[r].x;
+      const float rs = bb ? dn.val[a + 1] : os[r].y, rm = bb ? dn.val[a + 1] : om[r].y;
+      if (ba) {
+        t.sum[leaf0 + a] = ls;
+        t.mn[leaf0 + a] = lm;
+      }
+      if (bb) {
+        t.sum[leaf0 + a + 1] = rs;
+        t.mn[leaf0 + a + 1] = rm;
+      }
+      const float s = ls + rs, m = min_f32(lm, rm);
+      dn.hs[h] = s;
+      dn.hm[h] = m;
+      dn.dirty[h] = ba | bb;
+      if (ba | bb) {
+        const uint32_t x = ((subroot - 1u) << (sb - 1)) + h;
+        t.sum[x] = s;
+        t.mn[x] = m;
+      }
+    }
+  }
+  // local heap index h in [1, span) <-> global node ((subroot - 1) << depth(h)) + h
+  for (uint32_t width = half >> 1, dl = sb - 2; width >= 1; width >>= 1, --dl) {
+    __syncthreads();
+    for (uint32_t h = width + threadIdx.x; h < 2 * width; h += NT) {
+      const float s = dn.hs[2 * h] + dn.hs[2 * h + 1];
+      const float m = min_f32(dn.hm[2 * h], dn.hm[2 * h + 1]);
+      const uint8_t dv = dn.dirty[2 * h] | dn.dirty[2 * h + 1];
+      dn.hs[h] = s;
+      dn.hm[h] = m;
+      dn.dirty[h] = dv;
+      if (dv) {
+        const uint32_t x = ((subroot - 1u) << dl) + h;
+        t.sum[x] = s;
+        t.mn[x] = m;
+      }
+    }
+  }
 }
 
 // Block-wide update of a crowded partition.  each(f) calls f(off, pos, p)
-// for every entry of the partition, spread over the block's threads.
-template <typename Each>
-__device__ void block_update(PartSmem& sm, const TreePtrs& t, const Geom& g, uint32_t part,
-                             uint32_t* max_dst, Each each) {
-  const uint32_t span = 1u << g.S;
-  clear_bits(sm, g);
-  for (uint32_t k = threadIdx.x; k < span; k += kTreeThreads) sm.u.d.owner[k] = -1;
-  __syncthreads();
-  each([&](uint32_t off, uint32_t pos, float) { atomicMax(&sm.u.d.owner[off], (int)pos); });
-  __syncthreads();
+// for every entry of the partition, spread over the block's threads (the
+// same entries, in any order, on every call).  The sub-partitions are
+// handled one at a time: last batch position per offset through an LDS
+// owner table, then an LDS rebuild; the few levels between the
+// sub-partition roots and the partition root follow from the stored nodes.
+// Returns the block max of all entries' priority bits.
+template <int NT, typename Each>
+__device__ uint32_t dense_update(UpdSmem& sm, const TreePtrs& t, const Geom& g, uint32_t part,
+                                 Each each) {
+  DenseSmem& dn = sm.u.dn;
+  const int sb = g.S < kSubBits ? g.S : kSubBits;
+  const int e = g.S - sb;
+  const uint32_t sspan = 1u << sb, smask = sspan - 1u;
+  const uint32_t nwords = (sspan + 31) >> 5;
+  const uint32_t root = (1u << g.P) + part;
   uint32_t mb = 0;
-  each([&](uint32_t off, uint32_t pos, float p) {
-    mb = max(mb, __float_as_uint(p));
-    if (sm.u.d.owner[off] == (int)pos) {
-      sm.val[off] = p;
-      atomicOr(&sm.bits[off >> 5], 1u << (off & 31));
+  for (uint32_t q = 0; q < (1u << e); ++q) {
+    for (uint32_t k = threadIdx.x; k < sspan; k += NT) dn.owner[k] = -1;
+    for (uint32_t k = threadIdx.x; k < nwords; k += NT) dn.bits[k] = 0u;
+    if (threadIdx.x == 0) sm.flag = 0;
+    __syncthreads();
+    each([&](uint32_t off, uint32_t pos, float p) {
+      if (q == 0) mb = max(mb, __float_as_uint(p));
+      if ((off >> sb) == q) atomicMax(&dn.owner[off & smask], (int)pos);
+    });
+    __syncthreads();
+    each([&](uint32_t off, uint32_t pos, float p) {
+      const uint32_t o = off & smask;
+      if ((off >> sb) == q && dn.owner[o] == (int)pos) {
+        dn.val[o] = p;
+        atomicOr(&dn.bits[o >> 5], 1u << (o & 31));
+        sm.flag = 1;
+      }
+    });
+    __syncthreads();
+    if (sm.flag) dense_sub_rebuild<NT>(dn, t, (root << e) + q, g.n + (part << g.S) + (q << sb), sb);
+    __syncthreads();
+  }
+  if (e > 0 && threadIdx.x == 0) {
+    for (int j = e - 1; j >= 0; --j) {
+      for (uint32_t r = 0; r < (1u << j); ++r) {
+        const uint32_t x = (root << j) + r;
+        t.sum[x] = t.sum[2 * x] + t.sum[2 * x + 1];
+        t.mn[x] = min_f32(t.mn[2 * x], t.mn[2 * x + 1]);
+      }
     }
-  });
-  mb = block_max_bits(mb, sm);
-  if (threadIdx.x == 0) atomicMax(max_dst, mb);
-  __syncthreads();
-  repair_partition(sm, t, g, part);
+  }
+  return block_max_bits<NT>(mb, sm.sx);
 }
 
+// ------------------------------------------------------------ intake range
 
-// Repair after a contiguous run of new leaves, offsets [lo, hi) of the
-// partition, whose values are in sm.val (whole block).  At every level the
-// dirty nodes form a contiguous range and only its two end nodes can have an
-// unchanged child: the sibling left of the range's first node when that node
-// is a right child, and the sibling right of its last node when that node is
-// a left child.  Those (at most 2 per level) are loaded up front with the
-// caller's other loads; the range itself is rebuilt level by level in LDS.
-// Fills the boundary values into sm.sib_s / sib_m rows 0 (left) and 1 (right)
-// in prefetch_range_boundaries(), to be called before the values are known.
-__device__ __forceinline__ void prefetch_range_boundaries(PartSmem& sm, const TreePtrs& t,
+struct RangeSmem {
+  float val[kMaxSpan];                  // new leaf values by offset
+  float bs[2][kMaxSpan / 2];            // level values, two buffers, sums
+  float bm[2][kMaxSpan / 2];            // and mins
+  float bnd_s[2][kMaxSpanBits];         // boundary siblings per level: left, right
+  float bnd_m[2][kMaxSpanBits];
+};
+
+struct AddSmem {
+  union {
+    RangeSmem r;
+    UpdSmem d;
+  } u;
+  BlockScratch sx;
+};
+
+// The boundary siblings of a contiguous run of new leaves, offsets [lo, hi)
+// of the partition: at every level the dirty nodes form a contiguous range
+// and only its two end nodes can have an unchanged child -- the sibling left
+// of the range's first node when that node is a right child, and the sibling
+// right of its last node when that node is a left child.  Loaded by the
+// block's first wave, up front with the caller's other loads.
+__device__ __forceinline__ void prefetch_range_boundaries(RangeSmem& r, const TreePtrs& t,
                                                           const Geom& g, uint32_t part,
                                                           uint32_t lo, uint32_t hi) {
   const uint32_t a = g.n + (part << g.S) + lo, b = g.n + (part << g.S) + hi - 1;
@@ -440,34 +443,35 @@ __device__ __forceinline__ void prefetch_range_boundaries(PartSmem& sm, const Tr
     const bool need = left ? (x & 1u) : !(x & 1u);
     if (need) {
       const uint32_t sib = left ? x - 1 : x + 1;
-      sm.sib_s[left ? 0 : 1][q] = t.sum[sib];
-      sm.sib_m[left ? 0 : 1][q] = t.mn[sib];
+      r.bnd_s[left ? 0 : 1][q] = t.sum[sib];
+      r.bnd_m[left ? 0 : 1][q] = t.mn[sib];
     }
   }
 }
 
-__device__ void range_repair(PartSmem& sm, const TreePtrs& t, const Geom& g, uint32_t part,
+// Rebuild after a contiguous run [lo, hi) of new leaves (values in r.val),
+// level by level in LDS with a barrier between levels (whole block).
+__device__ void range_repair(RangeSmem& r, const TreePtrs& t, const Geom& g, uint32_t part,
                              uint32_t lo, uint32_t hi) {
   const uint32_t leaf0 = g.n + (part << g.S);
-  for (uint32_t off = lo + threadIdx.x; off < hi; off += kTreeThreads) {
-    t.sum[leaf0 + off] = sm.val[off];
-    t.mn[leaf0 + off] = sm.val[off];
+  for (uint32_t off = lo + threadIdx.x; off < hi; off += kTreeThreads)
+  {
+    t.sum[leaf0 + off] = r.val[off];
+    t.mn[leaf0 + off] = r.val[off];
   }
-  float* bs[2] = {sm.u.heap.s, sm.u.heap.s + kMaxSpan / 2};
-  float* bm[2] = {sm.u.heap.m, sm.u.heap.m + kMaxSpan / 2};
   uint32_t A = leaf0 + lo, Bn = leaf0 + hi - 1;  // children range (node indices)
-  const float* cs = sm.val + lo;                  // children values, index x - A
-  const float* cm = sm.val + lo;
+  const float* cs = r.val + lo;                   // children values, index x - A
+  const float* cm = r.val + lo;
   for (int k = 0; k < g.S; ++k) {
     const uint32_t pa = A >> 1, pb = Bn >> 1;
-    float* ns = bs[k & 1];
-    float* nm = bm[k & 1];
+    float* ns = r.bs[k & 1];
+    float* nm = r.bm[k & 1];
     for (uint32_t x = pa + threadIdx.x; x <= pb; x += kTreeThreads) {
-      const uint32_t l = 2 * x, r = 2 * x + 1;
-      const float ls = (l >= A) ? cs[l - A] : sm.sib_s[0][k];
-      const float lm = (l >= A) ? cm[l - A] : sm.sib_m[0][k];
-      const float rs = (r <= Bn) ? cs[r - A] : sm.sib_s[1][k];
-      const float rm = (r <= Bn) ? cm[r - A] : sm.sib_m[1][k];
+      const uint32_t l = 2 * x, rr = 2 * x + 1;
+      const float ls = (l >= A) ? cs[l - A] : r.bnd_s[0][k];
+      const float lm = (l >= A) ? cm[l - A] : r.bnd_m[0][k];
+      const float rs = (rr <= Bn) ? cs[rr - A] : r.bnd_s[1][k];
+      const float rm = (rr <= Bn) ? cm[rr - A] : r.bnd_m[1][k];
       const float s = ls + rs, m = min_f32(lm, rm);
       ns[x - pa] = s;
       nm[x - pa] = m;
@@ -487,18 +491,19 @@ __device__ void range_repair(PartSmem& sm, const TreePtrs& t, const Geom& g, uin
 __global__ void __launch_bounds__(256) init_kernel(TreePtrs t, Buckets bk, Geom g) {
   const uint64_t total = 2ull * g.n;
   const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
-  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride)
+  {
     t.sum[i] = 0.0f;
     t.mn[i] = __builtin_inff();
   }
   const uint32_t np = 1u << g.P;
-  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < np; i += stride) {
+  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < np; i += stride)
     bk.counts[i] = 0u;
-    bk.fill[i] = 0u;
-  }
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     t.ctrl->maxp_bits[0] = __float_as_uint(1.0f);
     t.ctrl->maxp_bits[1] = __float_as_uint(1.0f);
+    bk.ovf_n[0] = 0u;
+    bk.ovf_n[1] = 0u;
   }
 }
 
@@ -510,11 +515,12 @@ struct UpdateArgs {
   double alpha, eps;
   float p_nan;
   int src, dst;  // running-max slots: read / raise
+  int ovf;       // overflow counter of this call (bucketed path)
 };
 
 // Small batches: every partition's block scans the whole batch for its slots.
-__global__ void __launch_bounds__(256) update_scan_kernel(TreePtrs t, Geom g, UpdateArgs a) {
-  __shared__ PartSmem sm;
+__global__ void __launch_bounds__(kUpdThreads) update_scan_kernel(TreePtrs t, Geom g, UpdateArgs a) {
+  __shared__ UpdSmem sm;
   const uint32_t part = blockIdx.x;
   const uint32_t base = part << g.S;
   const float m0 = __uint_as_float(t.ctrl->maxp_bits[a.src]);
@@ -527,12 +533,12 @@ __global__ void __launch_bounds__(256) update_scan_kernel(TreePtrs t, Geom g, Up
   // Each thread loads its share of the batch in chunks of kChunk entries, all
   // loads of a chunk issued before any of them is looked at.
   constexpr int kChunk = 8;
-  for (uint32_t b0 = 0; b0 < a.B; b0 += kTreeThreads * kChunk) {
+  for (uint32_t b0 = 0; b0 < a.B; b0 += kUpdThreads * kChunk) {
     int64_t ix[kChunk];
     float tx[kChunk];
 #pragma unroll
     for (int c = 0; c < kChunk; ++c) {
-      const uint32_t b = b0 + c * kTreeThreads + threadIdx.x;
+      const uint32_t b = b0 + c * kUpdThreads + threadIdx.x;
       ix[c] = -1;
       tx[c] = 0.0f;
       if (b < a.B) {
@@ -544,7 +550,7 @@ __global__ void __launch_bounds__(256) update_scan_kernel(TreePtrs t, Geom g, Up
     for (int c = 0; c < kChunk; ++c) asm volatile("" ::"v"(tx[c]), "v"(ix[c]));
 #pragma unroll
     for (int c = 0; c < kChunk; ++c) {
-      const uint32_t b = b0 + c * kTreeThreads + threadIdx.x;
+      const uint32_t b = b0 + c * kUpdThreads + threadIdx.x;
       const int64_t i = ix[c];
       if (i >= 0 && i < (int64_t)a.size && ((uint64_t)i >> g.S) == part)
         collect(sm, t, g, part, (uint32_t)i - base, b, tx[c], m0, a.alpha, a.eps, a.p_nan);
@@ -552,104 +558,88 @@ __global__ void __launch_bounds__(256) update_scan_kernel(TreePtrs t, Geom g, Up
   }
   __syncthreads();
   const int m = sm.count;
-  if (threadIdx.x == 64) publish_max(sm, part, m0, max_dst);
+  if (threadIdx.x == 64) publish_max(sm.bmax, part, m0, max_dst);
   if (m == 0) return;
   if (m <= kSparseMax) {
-    if (threadIdx.x < 64) wave_update(sm, t, g, part, m);
+    if (threadIdx.x < 64) wave_update(sm.u.sp, t, g, part, m);
     return;
   }
-  // A crowded partition: the block reads its entries back from the LDS list,
-  // or -- past the list capacity -- straight from the batch again.
-  if (m <= kListCap) {
-    block_update(sm, t, g, part, max_dst, [&](auto f) {
-      for (int k = threadIdx.x; k < m; k += kTreeThreads) {
-        const Entry e = sm.u.d.ent[k];
-        f(e.off, e.pos, e.p);
-      }
-    });
-  } else {
-    block_update(sm, t, g, part, max_dst, [&](auto f) {
-      for (uint32_t b = threadIdx.x; b < a.B; b += kTreeThreads) {
-        const int64_t i = a.idx[b];
-        if (i >= 0 && i < (int64_t)a.size && ((uint64_t)i >> g.S) == part)
-          f((uint32_t)i - base, b, priority_of(a.td[b], m0, a.alpha, a.eps, a.p_nan));
-      }
-    });
-  }
+  // A crowded partition: its entries are read from the batch again.
+  dense_update<kUpdThreads>(sm, t, g, part, [&](auto f) {
+    for (uint32_t b = threadIdx.x; b < a.B; b += kUpdThreads) {
+      const int64_t i = a.idx[b];
+      if (i >= 0 && i < (int64_t)a.size && ((uint64_t)i >> g.S) == part)
+        f((uint32_t)i - base, b, priority_of(a.td[b], m0, a.alpha, a.eps, a.p_nan));
+    }
+  });
 }
 
-// Large batches, step 1: entries per partition.
-__global__ void __launch_bounds__(256) bucket_count_kernel(Buckets bk, Geom g, UpdateArgs a) {
+// Large batches, step 1: every valid entry goes to its partition's bucket
+// (kBucketCap entries per partition); past the cap, to an overflow list.
+__global__ void __launch_bounds__(256) bucket_kernel(Buckets bk, Geom g, UpdateArgs a) {
   const uint32_t b = blockIdx.x * blockDim.x + threadIdx.x;
   if (b >= a.B) return;
   const int64_t i = a.idx[b];
-  if (i >= 0 && i < (int64_t)a.size) atomicAdd(&bk.counts[(uint64_t)i >> g.S], 1u);
-}
-
-// Large batches, step 2: exclusive prefix of the counts (one block).
-__global__ void __launch_bounds__(256) bucket_scan_kernel(Buckets bk, Geom g) {
-  __shared__ PartSmem sm;
-  const uint32_t np = 1u << g.P;
-  uint32_t carry = 0;
-  for (uint32_t lo = 0; lo < np; lo += kTreeThreads) {
-    const uint32_t k = lo + threadIdx.x;
-    const int c = (k < np) ? (int)bk.counts[k] : 0;
-    int tot;
-    const int ex = block_excl_scan(c, sm, &tot);
-    if (k < np) bk.offs[k] = carry + (uint32_t)ex;
-    carry += (uint32_t)tot;
-  }
-  if (threadIdx.x == 0) bk.offs[np] = carry;
-}
-
-// Large batches, step 3: scatter the valid entries into their buckets.
-__global__ void __launch_bounds__(256) bucket_fill_kernel(Buckets bk, Geom g, UpdateArgs a) {
-  const uint32_t b = blockIdx.x * blockDim.x + threadIdx.x;
-  if (b >= a.B) return;
-  const int64_t i = a.idx[b];
+  const float x = a.td[b];
   if (i < 0 || i >= (int64_t)a.size) return;
   const uint32_t part = (uint32_t)((uint64_t)i >> g.S);
-  const uint32_t at = bk.offs[part] + atomicAdd(&bk.fill[part], 1u);
-  bk.slot[at] = (uint32_t)i;
-  bk.pos[at] = b;
-  bk.td[at] = a.td[b];
+  const uint32_t k = atomicAdd(&bk.counts[part], 1u);
+  if (k < kBucketCap) {
+    const uint32_t e = part * kBucketCap + k;
+    bk.slot[e] = (uint32_t)i;
+    bk.pos[e] = b;
+    bk.td[e] = x;
+  } else {
+    const uint32_t e = atomicAdd(&bk.ovf_n[a.ovf], 1u);
+    bk.oslot[e] = (uint32_t)i;
+    bk.opos[e] = b;
+    bk.otd[e] = x;
+  }
 }
 
-// Large batches, step 4: one block per partition reads its bucket.
-__global__ void __launch_bounds__(256) update_bucket_kernel(TreePtrs t, Buckets bk, Geom g,
+// Large batches, step 2: one block per partition reads its bucket.
+__global__ void __launch_bounds__(kUpdThreads) update_bucket_kernel(TreePtrs t, Buckets bk, Geom g,
                                                             UpdateArgs a) {
-  __shared__ PartSmem sm;
+  __shared__ UpdSmem sm;
   const uint32_t part = blockIdx.x;
   const uint32_t base = part << g.S;
   const float m0 = __uint_as_float(t.ctrl->maxp_bits[a.src]);
   uint32_t* max_dst = &t.ctrl->maxp_bits[a.dst];
-  const uint32_t lo = bk.offs[part], hi = bk.offs[part + 1];
-  const int m = (int)(hi - lo);
-  if (threadIdx.x == 0) {  // ready for the next call's counting pass
-    bk.counts[part] = 0u;
-    bk.fill[part] = 0u;
+  if (threadIdx.x == 0) {
+    sm.mtot = bk.counts[part];
+    bk.counts[part] = 0u;  // ready for the next call's bucketing
     sm.count = 0;
     sm.bmax = 0u;
-  }
-  if (m == 0) {
-    if (part == 0 && threadIdx.x == 0) atomicMax(max_dst, __float_as_uint(m0));
-    return;
+    if (part == 0) {
+      bk.ovf_n[a.ovf ^ 1] = 0u;  // the next call's overflow counter
+      atomicMax(max_dst, __float_as_uint(m0));
+    }
   }
   __syncthreads();
-  if (m <= kSparseMax) {
-    for (int k = threadIdx.x; k < m; k += kTreeThreads)
-      collect(sm, t, g, part, bk.slot[lo + k] - base, bk.pos[lo + k], bk.td[lo + k], m0,
-              a.alpha, a.eps, a.p_nan);
+  const uint32_t m = sm.mtot;
+  if (m == 0) return;
+  const uint32_t* bslot = bk.slot + part * kBucketCap;
+  const uint32_t* bpos = bk.pos + part * kBucketCap;
+  const float* btd = bk.td + part * kBucketCap;
+  if (m <= kBucketCap) {
+    for (uint32_t k = threadIdx.x; k < m; k += kUpdThreads)
+      collect(sm, t, g, part, bslot[k] - base, bpos[k], btd[k], m0, a.alpha, a.eps, a.p_nan);
     __syncthreads();
-    if (threadIdx.x == 64) publish_max(sm, part, m0, max_dst);
-    if (threadIdx.x < 64) wave_update(sm, t, g, part, m);
+    if (threadIdx.x == 64) publish_max(sm.bmax, part, m0, max_dst);
+    if (threadIdx.x < 64) wave_update(sm.u.sp, t, g, part, (int)m);
     return;
   }
-  if (part == 0 && threadIdx.x == 0) atomicMax(max_dst, __float_as_uint(m0));
-  block_update(sm, t, g, part, max_dst, [&](auto f) {
-    for (uint32_t e = lo + threadIdx.x; e < hi; e += kTreeThreads)
-      f(bk.slot[e] - base, bk.pos[e], priority_of(bk.td[e], m0, a.alpha, a.eps, a.p_nan));
+  const uint32_t novf = bk.ovf_n[a.ovf];
+  const uint32_t mb = dense_update<kUpdThreads>(sm, t, g, part, [&](auto f) {
+    for (uint32_t k = threadIdx.x; k < kBucketCap; k += kUpdThreads)
+      f(bslot[k] - base, bpos[k], priority_of(btd[k], m0, a.alpha, a.eps, a.p_nan));
+    for (uint32_t k = threadIdx.x; k < novf; k += kUpdThreads) {
+      const uint32_t i = bk.oslot[k];
+      if ((i >> g.S) == part)
+        f(i - base, bk.opos[k], priority_of(bk.otd[k], m0, a.alpha, a.eps, a.p_nan));
+    }
   });
+  if (threadIdx.x == 0) atomicMax(max_dst, mb);
 }
 
 struct AddArgs {
@@ -669,7 +659,7 @@ struct AddArgs {
 // "Experience Insertion"): new slots take the given priority or the running
 // max priority; rows are copied by the blocks past the tree blocks.
 __global__ void __launch_bounds__(256) add_kernel(TreePtrs t, Geom g, Storage st, AddArgs a) {
-  __shared__ PartSmem sm;
+  __shared__ AddSmem sm;
   if (blockIdx.x >= a.ntree) {
     // Row copy of the transitions into their ring slots.
     const uint32_t nb = gridDim.x - a.ntree;
@@ -730,24 +720,23 @@ __global__ void __launch_bounds__(256) add_kernel(TreePtrs t, Geom g, Storage st
     }
   }
   // One run (the usual case): its boundary siblings go out with the other loads.
-  if (runs == 1) prefetch_range_boundaries(sm, t, g, part, lo[0], hi[0]);
+  if (runs == 1) prefetch_range_boundaries(sm.u.r, t, g, part, lo[0], hi[0]);
   const float m0 = __uint_as_float(t.ctrl->maxp_bits[a.src]);
-  if (runs == 2) clear_bits(sm, g);
+  auto value_of = [&](uint32_t off) -> float {
+    const uint32_t slot = base + off;
+    const uint32_t j = (slot >= a.cursor) ? slot - a.cursor : slot + (g.n - a.cursor);
+    return a.prio ? a.prio[j] + 0.0f : m0;
+  };
   uint32_t mb = 0;
   for (int r = 0; r < runs; ++r) {
     for (uint32_t off = lo[r] + threadIdx.x; off < hi[r]; off += kTreeThreads) {
-      const uint32_t slot = base + off;
-      const uint32_t j = (slot >= a.cursor) ? slot - a.cursor : slot + (g.n - a.cursor);
-      float p = m0;
-      if (a.prio) {
-        p = a.prio[j] + 0.0f;
-        mb = max(mb, __float_as_uint(p));
-      }
-      sm.val[off] = p;
+      const float p = value_of(off);
+      mb = max(mb, __float_as_uint(p));
+      if (runs == 1) sm.u.r.val[off] = p;
     }
   }
   if (a.prio) {
-    mb = block_max_bits(mb, sm);
+    mb = block_max_bits<kTreeThreads>(mb, sm.sx);
     if (threadIdx.x == 0) {
       if (w == 0) mb = max(mb, __float_as_uint(m0));
       atomicMax(&t.ctrl->maxp_bits[a.dst], mb);
@@ -755,20 +744,26 @@ __global__ void __launch_bounds__(256) add_kernel(TreePtrs t, Geom g, Storage st
   }
   __syncthreads();
   if (runs == 1) {
-    range_repair(sm, t, g, part, lo[0], hi[0]);
+    range_repair(sm.u.r, t, g, part, lo[0], hi[0]);
     return;
   }
-  // Two runs in one partition (the ring wrapped inside it): general repair.
-  for (int r = 0; r < runs; ++r)
-    for (uint32_t off = lo[r] + threadIdx.x; off < hi[r]; off += kTreeThreads)
-      atomicOr(&sm.bits[off >> 5], 1u << (off & 31));
-  __syncthreads();
-  repair_partition(sm, t, g, part);
+  // Two runs in one partition (the ring wrapped inside it): general rebuild;
+  // slots are distinct, so the offset doubles as the batch position.
+  dense_update<kTreeThreads>(sm.u.d, t, g, part, [&](auto f) {
+    for (int r = 0; r < runs; ++r)
+      for (uint32_t off = lo[r] + threadIdx.x; off < hi[r]; off += kTreeThreads)
+        f(off, off, value_of(off));
+  });
 }
 
 // Nodes [1, 2^P) above the partitions, recomputed from depth P upwards.
+struct TopSmem {
+  float s[1 << kMaxTopBits];
+  float m[1 << kMaxTopBits];
+};
+
 __global__ void __launch_bounds__(256) top_kernel(TreePtrs t, Geom g) {
-  __shared__ PartSmem sm;
+  __shared__ TopSmem sm;
   const uint32_t np = 1u << g.P;
   if (g.P <= kMaxTopBits) {
     const uint32_t half = np >> 1;
@@ -776,18 +771,18 @@ __global__ void __launch_bounds__(256) top_kernel(TreePtrs t, Geom g) {
       const float2 cs = *reinterpret_cast<const float2*>(t.sum + 2 * h);
       const float2 cm = *reinterpret_cast<const float2*>(t.mn + 2 * h);
       const float s = cs.x + cs.y, m = min_f32(cm.x, cm.y);
-      sm.u.heap.s[h] = s;
-      sm.u.heap.m[h] = m;
+      sm.s[h] = s;
+      sm.m[h] = m;
       t.sum[h] = s;
       t.mn[h] = m;
     }
     for (uint32_t width = half >> 1; width >= 1; width >>= 1) {
       __syncthreads();
       for (uint32_t h = width + threadIdx.x; h < 2 * width; h += kTreeThreads) {
-        const float s = sm.u.heap.s[2 * h] + sm.u.heap.s[2 * h + 1];
-        const float m = min_f32(sm.u.heap.m[2 * h], sm.u.heap.m[2 * h + 1]);
-        sm.u.heap.s[h] = s;
-        sm.u.heap.m[h] = m;
+        const float s = sm.s[2 * h] + sm.s[2 * h + 1];
+        const float m = min_f32(sm.m[2 * h], sm.m[2 * h + 1]);
+        sm.s[h] = s;
+        sm.m[h] = m;
         t.sum[h] = s;
         t.mn[h] = m;
       }
@@ -797,10 +792,8 @@ __global__ void __launch_bounds__(256) top_kernel(TreePtrs t, Geom g) {
     for (int l = g.P - 1; l >= 0; --l) {
       const uint32_t lo = 1u << l;
       for (uint32_t h = lo + threadIdx.x; h < 2 * lo; h += kTreeThreads) {
-        const float2 cs = *reinterpret_cast<const float2*>(t.sum + 2 * h);
-        const float2 cm = *reinterpret_cast<const float2*>(t.mn + 2 * h);
-        t.sum[h] = cs.x + cs.y;
-        t.mn[h] = min_f32(cm.x, cm.y);
+        t.sum[h] = t.sum[2 * h] + t.sum[2 * h + 1];
+        t.mn[h] = min_f32(t.mn[2 * h], t.mn[2 * h + 1]);
       }
       __threadfence_block();
       __syncthreads();
@@ -828,9 +821,16 @@ hipError_t launch_top(const TreePtrs& t, const Geom& g, hipStream_t s) {
   return hipGetLastError();
 }
 
+bool update_uses_buckets(const Geom& g, int64_t B) {
+  // Every partition's block scans the batch: np * B loads in all.  Past 2^20
+  // of them, bucket the batch first.
+  const uint64_t np = 1ull << g.P;
+  return np * (uint64_t)B > (1ull << 20);
+}
+
 hipError_t launch_update(const TreePtrs& t, const Buckets& bk, const Geom& g, uint32_t size,
                          int64_t B, const int64_t* idx, const float* td, double alpha,
-                         double eps, int src, int dst, hipStream_t s) {
+                         double eps, int src, int dst, int ovf, hipStream_t s) {
   UpdateArgs a;
   a.idx = idx;
   a.td = td;
@@ -841,19 +841,16 @@ hipError_t launch_update(const TreePtrs& t, const Buckets& bk, const Geom& g, ui
   a.p_nan = (float)pow(eps, alpha);
   a.src = src;
   a.dst = dst;
+  a.ovf = ovf;
   const uint64_t np = 1ull << g.P;
-  // Every partition block scans the batch: np * B loads in all.  Past ~4M
-  // loads, or for batches the LDS list could not hold, bucket first.
-  if (np * (uint64_t)B <= (1ull << 22) && B <= 8192) {
-    hipLaunchKernelGGL(update_scan_kernel, dim3((unsigned)np), dim3(kTreeThreads), 0, s, t, g,
+  if (!update_uses_buckets(g, B)) {
+    hipLaunchKernelGGL(update_scan_kernel, dim3((unsigned)np), dim3(kUpdThreads), 0, s, t, g,
                        a);
     return hipGetLastError();
   }
   const unsigned eb = grid_for((uint64_t)B, kTreeThreads, 1u << 30);
-  hipLaunchKernelGGL(bucket_count_kernel, dim3(eb), dim3(kTreeThreads), 0, s, bk, g, a);
-  hipLaunchKernelGGL(bucket_scan_kernel, dim3(1), dim3(kTreeThreads), 0, s, bk, g);
-  hipLaunchKernelGGL(bucket_fill_kernel, dim3(eb), dim3(kTreeThreads), 0, s, bk, g, a);
-  hipLaunchKernelGGL(update_bucket_kernel, dim3((unsigned)np), dim3(kTreeThreads), 0, s, t, bk,
+  hipLaunchKernelGGL(bucket_kernel, dim3(eb), dim3(kTreeThreads), 0, s, bk, g, a);
+  hipLaunchKernelGGL(update_bucket_kernel, dim3((unsigned)np), dim3(kUpdThreads), 0, s, t, bk,
                      g, a);
   return hipGetLastError();
 }
