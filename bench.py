@@ -9,14 +9,25 @@ Default workload: the Ape-X replay shard, 2^21 leaves, B = 512, 400-item
 intake, indices only.  Prints one JSON line.
 
 The timed region is K steps between two HIP events on the launch stream
-(torch's current stream).  A second pass of K steps records an event
-around every operation to time each kernel live; the roofline figure uses
-the dominant one.  The CPU baseline is the plain single-threaded oracle
+(torch's current stream).  A second pass runs each operation on its own, K
+back-to-back launches between two events, to time each kernel live; the
+roofline figure uses the dominant one.  The CPU baseline is the plain single-threaded oracle
 running the same workload for a bounded number of steps on the host.
+
+The roofline's "traffic" is the HBM bytes one launch of the dominant
+operation moves as the hardware counts them (rocprofv3 FETCH_SIZE and
+WRITE_SIZE per dispatch, each scaled by what the same counter reads for a
+plain device copy of known size).  The counters cannot be read from inside
+this process, so they are taken in separate profiler runs and ingested into
+profiles/hbm_traffic.json together with a digest of the kernel sources; the
+figure is reported only while the sources still match that digest.
+    python3 bench.py --copy-calibration      # the copy the counters are scaled by
+    python3 bench.py --ingest-pmc DIR        # DIR holds the rocprofv3 csv runs
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -32,6 +43,114 @@ import workloads  # noqa: E402
 
 METRIC = "PER samples/s + priority updates/s at 2^21 leaves (B=512); % of HBM roofline"
 PEAK_HBM_GBS = 8000.0
+CSRC = os.path.join(ROOT, "sum_tree_sampling_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+CALIB_FLOATS = 64 << 20          # 256 MiB copied by --copy-calibration
+CALIB_REPS = 3
+# Kernels that make up each operation (the sample may be preceded by a top
+# rebuild, the update is one kernel or a bucket pass plus its update).
+OP_KERNELS = {
+    "sample": ("sample_kernel", "top_kernel"),
+    "update": ("update_scan_kernel", "bucket_kernel", "update_bucket_kernel"),
+    "add": ("add_kernel",),
+}
+
+
+def kernel_source_digest() -> str:
+    """sha256 over the HIP sources and headers the kernels are built from."""
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        if f.endswith((".hip", ".h")):
+            h.update(f.encode())
+            with open(os.path.join(CSRC, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()
+
+
+def _short_kernel(name: str) -> str:
+    import re
+    name = name.replace("per::(anonymous namespace)::", "").replace("void ", "")
+    return re.sub(r"[<(].*$", "", name).strip()
+
+
+def _counter_rows(path: str) -> dict:
+    """{short kernel name: [counter value per dispatch]} of a rocprofv3 csv."""
+    import csv
+    out: dict = {}
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            out.setdefault(_short_kernel(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+    return out
+
+
+def ingest_pmc(d: str) -> None:
+    """Write profiles/hbm_traffic.json from rocprofv3 --pmc csv runs under d:
+    d/calib_{FETCH_SIZE,WRITE_SIZE}/run_counter_collection.csv (the copy of
+    --copy-calibration) and d/<workload>_{FETCH_SIZE,WRITE_SIZE}/... (this
+    bench on that workload).  Per-dispatch values are medians (the few setup
+    dispatches of the fill do not move them)."""
+    counters = ("FETCH_SIZE", "WRITE_SIZE")
+    true_kib = CALIB_FLOATS * 4 / 1024.0
+    calib = {}
+    for c in counters:
+        rows = _counter_rows(os.path.join(d, "calib_%s" % c, "run_counter_collection.csv"))
+        copy = [k for k in rows if "copy" in k.lower()]
+        if not copy:
+            raise SystemExit("no copy kernel in the %s calibration run" % c)
+        reported = float(np.median(rows[copy[0]]))
+        calib[c] = {"kernel": copy[0], "reported_kib": reported, "true_kib": true_kib,
+                    "factor": true_kib / reported}
+    res = {"source_sha256": kernel_source_digest(), "calibration": calib, "workloads": {}}
+    for w in workloads.WORKLOADS:
+        paths = [os.path.join(d, "%s_%s" % (w, c), "run_counter_collection.csv") for c in counters]
+        if not all(os.path.exists(p) for p in paths):
+            continue
+        per_c = [_counter_rows(p) for p in paths]
+        ops = {}
+        for op, names in OP_KERNELS.items():
+            if op == "add" and not workloads.spec(w)["intake"]:
+                continue  # only the fill before the timed steps
+            kern, tot = {}, 0.0
+            for k in names:
+                if k not in per_c[0]:
+                    continue
+                f = float(np.median(per_c[0][k])) * calib["FETCH_SIZE"]["factor"] * 1024
+                wr = float(np.median(per_c[1][k])) * calib["WRITE_SIZE"]["factor"] * 1024
+                kern[k] = {"fetch_bytes": f, "write_bytes": wr, "dispatches": len(per_c[0][k])}
+                tot += f + wr
+            if kern:
+                ops[op] = {"bytes": tot, "kernels": kern}
+        res["workloads"][w] = ops
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(res, fh, indent=1, sort_keys=True)
+        fh.write("\n")
+    print(json.dumps(res, indent=1, sort_keys=True))
+
+
+def measured_traffic(workload: str, op: str):
+    """Counted HBM bytes per launch of op, or None (not profiled, or the
+    kernel sources changed since)."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != kernel_source_digest():
+        return None
+    e = t.get("workloads", {}).get(workload, {}).get(op)
+    return None if e is None else float(e["bytes"])
+
+
+def copy_calibration() -> None:
+    """A plain device-to-device copy of CALIB_FLOATS f32, CALIB_REPS times."""
+    import torch
+    x = torch.ones(CALIB_FLOATS, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(CALIB_REPS):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print("copied %d bytes x %d" % (CALIB_FLOATS * 4, CALIB_REPS), flush=True)
 
 
 def expected_dirty_internal(n: int, U: int) -> float:
@@ -95,7 +214,17 @@ def main():
     ap.add_argument("--workload", default="apex_shard_2m", choices=list(workloads.WORKLOADS))
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run the plain copy the HBM counters are scaled by")
+    ap.add_argument("--ingest-pmc", metavar="DIR",
+                    help="only write profiles/hbm_traffic.json from rocprofv3 runs in DIR")
     args = ap.parse_args()
+    if args.ingest_pmc:
+        ingest_pmc(args.ingest_pmc)
+        return
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the sum tree runs on a single device "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
@@ -148,19 +277,11 @@ def main():
                    dones=torch.empty(B, dtype=torch.uint8, device=dev))
     intake = spec["intake"]
 
-    def step(s, ev=None):
-        if ev is not None:
-            ev[0].record(stream)
+    def step(s):
         g.sample(u_d[s], beta=spec["beta"], weights=spec["weights"], out=out)
-        if ev is not None:
-            ev[1].record(stream)
         g.update(idx_d[s] if idx_d is not None else out["idx"], td_d[s])
-        if ev is not None:
-            ev[2].record(stream)
         if intake:
             g.add(intake)
-        if ev is not None:
-            ev[3].record(stream)
 
     for s in range(args.warmup):
         step(s)
@@ -179,20 +300,28 @@ def main():
     host_ms = (time.perf_counter() - t0) * 1e3
     ms_per_step = e0.elapsed_time(e1) / args.steps
 
-    # Pass 2: an event around every operation of K more steps.
+    # Pass 2: each operation on its own, K back-to-back launches between two
+    # events (an event pair around every launch would add its own dispatch
+    # gap to each one).  The sampled indices of this pass feed its updates.
     base = args.warmup + args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    for s in range(args.steps):
-        step(base + s, evs[s])
-    torch.cuda.synchronize()
-    op_ms = {"sample": [], "update": [], "add": []}
-    for ev in evs:
-        op_ms["sample"].append(ev[0].elapsed_time(ev[1]))
-        op_ms["update"].append(ev[1].elapsed_time(ev[2]))
-        if intake:
-            op_ms["add"].append(ev[2].elapsed_time(ev[3]))
-    op_avg = {k: float(np.mean(v)) for k, v in op_ms.items() if v}
-    op_med = {k: float(np.median(v)) for k, v in op_ms.items() if v}
+    idx_hist = torch.empty((args.steps, B), dtype=torch.int64, device=dev)
+    ops = {
+        "sample": lambda s: g.sample(u_d[base + s], beta=spec["beta"], weights=spec["weights"],
+                                     out=dict(out, idx=idx_hist[s])),
+        "update": lambda s: g.update(idx_d[base + s] if idx_d is not None else idx_hist[s],
+                                     td_d[base + s]),
+    }
+    if intake:
+        ops["add"] = lambda s: g.add(intake)
+    op_avg = {}
+    for name, fn in ops.items():
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for s in range(args.steps):
+            fn(s)
+        b.record(stream)
+        torch.cuda.synchronize()
+        op_avg[name] = a.elapsed_time(b) / args.steps
 
     byts = algorithmic_bytes(spec)
     dom = max(op_avg, key=op_avg.get)
@@ -218,12 +347,12 @@ def main():
         "samples_per_s": B / (op_avg["sample"] * 1e-3),
         "updates_per_s": B / (op_avg["update"] * 1e-3),
         "op_ms_avg": op_avg,
-        "op_ms_median": op_med,
         "host_ms_per_step": host_ms / args.steps,
         "step_algorithmic_bytes": step_bytes,
         "step_hbm_roofline_frac": step_bytes / (ms_per_step * 1e-3) / (PEAK_HBM_GBS * 1e9),
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": None,
+                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
+                     "traffic": measured_traffic(args.workload, dom),
                      "bytes_per_launch": byts[dom]},
         "cpu_baseline": None,
     }
