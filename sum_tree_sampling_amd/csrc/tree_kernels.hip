@@ -196,26 +196,30 @@ struct DenseSmem {
   uint32_t bits[kSub / 32];  // offsets that receive a new leaf
 };
 
+// LDS of an update block that owns PPB consecutive partitions: one sparse
+// area per partition (wave w repairs partition w of the block), sharing its
+// memory with the block-wide rebuild of a crowded partition.
+template <int PPB>
 struct UpdSmem {
   union {
-    SparseSmem sp;
+    SparseSmem sp[PPB];
     DenseSmem dn;
   } u;
   BlockScratch sx;
-  int count;      // entries collected
-  uint32_t bmax;  // max priority bits of the block's entries
-  uint32_t mtot;  // entries of the partition (bucketed path)
+  int count[PPB];      // entries collected per partition
+  uint32_t mtot[PPB];  // entries per partition (bucketed path)
+  uint32_t bmax;       // max priority bits of the block's entries
   int flag;
 };
 
-// Collect one entry of this block's partition (any thread): its priority
-// and, for the first 64 entries, the stored siblings along its leaf's whole
-// path to the partition root, loaded before the priority's pow so that both
-// latencies overlap.
-__device__ __forceinline__ void collect(UpdSmem& sm, const TreePtrs& t, const Geom& g,
-                                        uint32_t part, uint32_t off, uint32_t pos, float td,
-                                        float m0, double alpha, double eps, float p_nan) {
-  const int k = atomicAdd(&sm.count, 1);
+// Collect entry k of a partition (any thread): for the first 64 entries the
+// stored siblings along its leaf's whole path to the partition root go to
+// the partition's sparse area, loaded before the priority's pow so that both
+// latencies overlap.  Returns the priority.
+__device__ __forceinline__ float collect(SparseSmem& sp, int k, const TreePtrs& t,
+                                         const Geom& g, uint32_t part, uint32_t off,
+                                         uint32_t pos, float td, float m0, double alpha,
+                                         double eps, float p_nan) {
   float ps[kMaxSpanBits], pm[kMaxSpanBits];
   const uint32_t node = g.n + (part << g.S) + off;
   if (k < kSparseMax) {
@@ -229,27 +233,31 @@ __device__ __forceinline__ void collect(UpdSmem& sm, const TreePtrs& t, const Ge
     }
   }
   const float p = priority_of(td, m0, alpha, eps, p_nan);
-  atomicMax(&sm.bmax, __float_as_uint(p));
   if (k < kSparseMax) {
-    sm.u.sp.key[k] = ((uint64_t)off << 32) | pos;
-    sm.u.sp.pval[k] = p;
+    sp.key[k] = ((uint64_t)off << 32) | pos;
+    sp.pval[k] = p;
 #pragma unroll
     for (int q = 0; q < kMaxSpanBits; ++q) {
       if (q < g.S) {
-        sm.u.sp.sib_s[k][q] = ps[q];
-        sm.u.sp.sib_m[k][q] = pm[q];
+        sp.sib_s[k][q] = ps[q];
+        sp.sib_m[k][q] = pm[q];
       }
     }
   }
+  return p;
 }
 
-// Raise the running-max slot by the block's max priority (one thread; part 0
-// also carries the value at the start of the call over).
-__device__ __forceinline__ void publish_max(uint32_t bmax, uint32_t part, float m0,
+// Raise the running-max slot by max priority bits mb (one thread).  The block
+// holding partition 0 carries the value at the start of the call over
+// (carry); every other caller has something to add only when it exceeds
+// that value, which spares the one contended address nearly all atomics.
+__device__ __forceinline__ void publish_max(uint32_t mb, bool carry, float m0,
                                             uint32_t* max_dst) {
-  uint32_t mb = bmax;
-  if (part == 0) mb = max(mb, __float_as_uint(m0));
-  if (mb) atomicMax(max_dst, mb);
+  const uint32_t m0b = __float_as_uint(m0);
+  if (carry)
+    atomicMax(max_dst, max(mb, m0b));
+  else if (mb > m0b)
+    atomicMax(max_dst, mb);
 }
 
 // One wave updates a partition holding m <= 64 collected entries: sort them
@@ -365,9 +373,8 @@ __device__ void dense_sub_rebuild(DenseSmem& dn, const TreePtrs& t, uint32_t sub
 // sub-partition roots and the partition root follow from the stored nodes.
 // Returns the block max of all entries' priority bits.
 template <int NT, typename Each>
-__device__ uint32_t dense_update(UpdSmem& sm, const TreePtrs& t, const Geom& g, uint32_t part,
-                                 Each each) {
-  DenseSmem& dn = sm.u.dn;
+__device__ uint32_t dense_update(DenseSmem& dn, int& flag, BlockScratch& sx, const TreePtrs& t,
+                                 const Geom& g, uint32_t part, Each each) {
   const int sb = g.S < kSubBits ? g.S : kSubBits;
   const int e = g.S - sb;
   const uint32_t sspan = 1u << sb, smask = sspan - 1u;
@@ -377,7 +384,7 @@ __device__ uint32_t dense_update(UpdSmem& sm, const TreePtrs& t, const Geom& g, 
   for (uint32_t q = 0; q < (1u << e); ++q) {
     for (uint32_t k = threadIdx.x; k < sspan; k += NT) dn.owner[k] = -1;
     for (uint32_t k = threadIdx.x; k < nwords; k += NT) dn.bits[k] = 0u;
-    if (threadIdx.x == 0) sm.flag = 0;
+    if (threadIdx.x == 0) flag = 0;
     __syncthreads();
     each([&](uint32_t off, uint32_t pos, float p) {
       if (q == 0) mb = max(mb, __float_as_uint(p));
@@ -389,11 +396,11 @@ __device__ uint32_t dense_update(UpdSmem& sm, const TreePtrs& t, const Geom& g, 
       if ((off >> sb) == q && dn.owner[o] == (int)pos) {
         dn.val[o] = p;
         atomicOr(&dn.bits[o >> 5], 1u << (o & 31));
-        sm.flag = 1;
+        flag = 1;
       }
     });
     __syncthreads();
-    if (sm.flag) dense_sub_rebuild<NT>(dn, t, (root << e) + q, g.n + (part << g.S) + (q << sb), sb);
+    if (flag) dense_sub_rebuild<NT>(dn, t, (root << e) + q, g.n + (part << g.S) + (q << sb), sb);
     __syncthreads();
   }
   if (e > 0 && threadIdx.x == 0) {
@@ -405,7 +412,7 @@ __device__ uint32_t dense_update(UpdSmem& sm, const TreePtrs& t, const Geom& g, 
       }
     }
   }
-  return block_max_bits<NT>(mb, sm.sx);
+  return block_max_bits<NT>(mb, sx);
 }
 
 // ------------------------------------------------------------ intake range
@@ -421,9 +428,10 @@ struct RangeSmem {
 struct AddSmem {
   union {
     RangeSmem r;
-    UpdSmem d;
+    DenseSmem dn;
   } u;
   BlockScratch sx;
+  int flag;
 };
 
 // The boundary siblings of a contiguous run of new leaves, offsets [lo, hi)
@@ -518,17 +526,18 @@ struct UpdateArgs {
   int ovf;       // overflow counter of this call (bucketed path)
 };
 
-// Small batches: every partition's block scans the whole batch for its slots.
+// Small batches: each block owns PPB consecutive partitions and scans the
+// whole batch for their slots; wave w repairs partition w of the block when
+// it is sparse, crowded partitions are rebuilt by the whole block after.
+template <int PPB>
 __global__ void __launch_bounds__(kUpdThreads) update_scan_kernel(TreePtrs t, Geom g, UpdateArgs a) {
-  __shared__ UpdSmem sm;
-  const uint32_t part = blockIdx.x;
-  const uint32_t base = part << g.S;
+  __shared__ UpdSmem<PPB> sm;
+  const uint32_t part0 = blockIdx.x * PPB;
+  const int nparts = (int)min((uint32_t)PPB, (1u << g.P) - part0);
   const float m0 = __uint_as_float(t.ctrl->maxp_bits[a.src]);
   uint32_t* max_dst = &t.ctrl->maxp_bits[a.dst];
-  if (threadIdx.x == 0) {
-    sm.count = 0;
-    sm.bmax = 0u;
-  }
+  if (threadIdx.x < PPB) sm.count[threadIdx.x] = 0;
+  if (threadIdx.x == 0) sm.bmax = 0u;
   __syncthreads();
   // Each thread loads its share of the batch in chunks of kChunk entries, all
   // loads of a chunk issued before any of them is looked at.
@@ -552,26 +561,41 @@ __global__ void __launch_bounds__(kUpdThreads) update_scan_kernel(TreePtrs t, Ge
     for (int c = 0; c < kChunk; ++c) {
       const uint32_t b = b0 + c * kUpdThreads + threadIdx.x;
       const int64_t i = ix[c];
-      if (i >= 0 && i < (int64_t)a.size && ((uint64_t)i >> g.S) == part)
-        collect(sm, t, g, part, (uint32_t)i - base, b, tx[c], m0, a.alpha, a.eps, a.p_nan);
+      if (i < 0 || i >= (int64_t)a.size) continue;
+      const uint32_t q = (uint32_t)((uint64_t)i >> g.S) - part0;  // wraps below part0
+      if (q < (uint32_t)nparts) {
+        const uint32_t part = part0 + q;
+        const int k = atomicAdd(&sm.count[q], 1);
+        const float p = collect(sm.u.sp[q], k, t, g, part, (uint32_t)i - (part << g.S), b, tx[c],
+                                m0, a.alpha, a.eps, a.p_nan);
+        atomicMax(&sm.bmax, __float_as_uint(p));
+      }
     }
   }
   __syncthreads();
-  const int m = sm.count;
-  if (threadIdx.x == 64) publish_max(sm.bmax, part, m0, max_dst);
-  if (m == 0) return;
-  if (m <= kSparseMax) {
-    if (threadIdx.x < 64) wave_update(sm.u.sp, t, g, part, m);
-    return;
+  if (threadIdx.x == 64) publish_max(sm.bmax, blockIdx.x == 0, m0, max_dst);
+  const int w = threadIdx.x >> 6;
+  bool crowded = false;
+  for (int q = 0; q < nparts; ++q) crowded |= sm.count[q] > kSparseMax;
+  if (w < nparts) {
+    const int m = sm.count[w];
+    if (m > 0 && m <= kSparseMax) wave_update(sm.u.sp[w], t, g, part0 + w, m);
   }
-  // A crowded partition: its entries are read from the batch again.
-  dense_update<kUpdThreads>(sm, t, g, part, [&](auto f) {
-    for (uint32_t b = threadIdx.x; b < a.B; b += kUpdThreads) {
-      const int64_t i = a.idx[b];
-      if (i >= 0 && i < (int64_t)a.size && ((uint64_t)i >> g.S) == part)
-        f((uint32_t)i - base, b, priority_of(a.td[b], m0, a.alpha, a.eps, a.p_nan));
-    }
-  });
+  if (!crowded) return;
+  // The dense rebuild reuses the sparse areas: every wave is done with them.
+  __syncthreads();
+  for (int q = 0; q < nparts; ++q) {
+    if (sm.count[q] <= kSparseMax) continue;
+    const uint32_t part = part0 + q, base = part << g.S;
+    // Its entries are read from the batch again.
+    dense_update<kUpdThreads>(sm.u.dn, sm.flag, sm.sx, t, g, part, [&](auto f) {
+      for (uint32_t b = threadIdx.x; b < a.B; b += kUpdThreads) {
+        const int64_t i = a.idx[b];
+        if (i >= 0 && i < (int64_t)a.size && ((uint64_t)i >> g.S) == part)
+          f((uint32_t)i - base, b, priority_of(a.td[b], m0, a.alpha, a.eps, a.p_nan));
+      }
+    });
+  }
 }
 
 // Large batches, step 1: every valid entry goes to its partition's bucket
@@ -597,49 +621,72 @@ __global__ void __launch_bounds__(256) bucket_kernel(Buckets bk, Geom g, UpdateA
   }
 }
 
-// Large batches, step 2: one block per partition reads its bucket.
+// Large batches, step 2: each block owns PPB consecutive partitions; wave w
+// reads the bucket of partition w of the block and repairs it (lane k takes
+// entry k), crowded partitions (more entries than a bucket holds) are
+// rebuilt by the whole block after, from their bucket and the overflow list.
+template <int PPB>
 __global__ void __launch_bounds__(kUpdThreads) update_bucket_kernel(TreePtrs t, Buckets bk, Geom g,
                                                             UpdateArgs a) {
-  __shared__ UpdSmem sm;
-  const uint32_t part = blockIdx.x;
-  const uint32_t base = part << g.S;
+  __shared__ UpdSmem<PPB> sm;
+  const uint32_t part0 = blockIdx.x * PPB;
+  const int nparts = (int)min((uint32_t)PPB, (1u << g.P) - part0);
   const float m0 = __uint_as_float(t.ctrl->maxp_bits[a.src]);
   uint32_t* max_dst = &t.ctrl->maxp_bits[a.dst];
-  if (threadIdx.x == 0) {
-    sm.mtot = bk.counts[part];
-    bk.counts[part] = 0u;  // ready for the next call's bucketing
-    sm.count = 0;
-    sm.bmax = 0u;
-    if (part == 0) {
-      bk.ovf_n[a.ovf ^ 1] = 0u;  // the next call's overflow counter
-      atomicMax(max_dst, __float_as_uint(m0));
-    }
+  if (threadIdx.x < (unsigned)nparts) {
+    sm.mtot[threadIdx.x] = bk.counts[part0 + threadIdx.x];
+    bk.counts[part0 + threadIdx.x] = 0u;  // ready for the next call's bucketing
+  }
+  if (threadIdx.x == 0 && blockIdx.x == 0) {
+    bk.ovf_n[a.ovf ^ 1] = 0u;  // the next call's overflow counter
+    publish_max(0u, true, m0, max_dst);
   }
   __syncthreads();
-  const uint32_t m = sm.mtot;
-  if (m == 0) return;
-  const uint32_t* bslot = bk.slot + part * kBucketCap;
-  const uint32_t* bpos = bk.pos + part * kBucketCap;
-  const float* btd = bk.td + part * kBucketCap;
-  if (m <= kBucketCap) {
-    for (uint32_t k = threadIdx.x; k < m; k += kUpdThreads)
-      collect(sm, t, g, part, bslot[k] - base, bpos[k], btd[k], m0, a.alpha, a.eps, a.p_nan);
-    __syncthreads();
-    if (threadIdx.x == 64) publish_max(sm.bmax, part, m0, max_dst);
-    if (threadIdx.x < 64) wave_update(sm.u.sp, t, g, part, (int)m);
-    return;
-  }
-  const uint32_t novf = bk.ovf_n[a.ovf];
-  const uint32_t mb = dense_update<kUpdThreads>(sm, t, g, part, [&](auto f) {
-    for (uint32_t k = threadIdx.x; k < kBucketCap; k += kUpdThreads)
-      f(bslot[k] - base, bpos[k], priority_of(btd[k], m0, a.alpha, a.eps, a.p_nan));
-    for (uint32_t k = threadIdx.x; k < novf; k += kUpdThreads) {
-      const uint32_t i = bk.oslot[k];
-      if ((i >> g.S) == part)
-        f(i - base, bk.opos[k], priority_of(bk.otd[k], m0, a.alpha, a.eps, a.p_nan));
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  bool crowded = false;
+  for (int q = 0; q < nparts; ++q) crowded |= sm.mtot[q] > (uint32_t)kBucketCap;
+  if (w < nparts) {
+    const uint32_t part = part0 + w, m = sm.mtot[w];
+    if (m > 0 && m <= (uint32_t)kBucketCap) {
+      SparseSmem& sp = sm.u.sp[w];
+      uint32_t pb = 0u;
+      if ((uint32_t)lane < m) {
+        const uint32_t e = part * kBucketCap + lane;
+        const float p = collect(sp, lane, t, g, part, bk.slot[e] - (part << g.S), bk.pos[e],
+                                bk.td[e], m0, a.alpha, a.eps, a.p_nan);
+        pb = __float_as_uint(p);
+      }
+      pb = wave_max_u32(pb);
+      if (lane == 0) publish_max(pb, false, m0, max_dst);
+      // The wave reads what its own lanes wrote to its sparse area: LDS
+      // operations of one wave complete in order.
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      wave_update(sp, t, g, part, (int)m);
     }
-  });
-  if (threadIdx.x == 0) atomicMax(max_dst, mb);
+  }
+  if (!crowded) return;
+  // The dense rebuild reuses the sparse areas: every wave is done with them.
+  __syncthreads();
+  const uint32_t novf = bk.ovf_n[a.ovf];
+  for (int q = 0; q < nparts; ++q) {
+    if (sm.mtot[q] <= (uint32_t)kBucketCap) continue;
+    const uint32_t part = part0 + q, base = part << g.S;
+    const uint32_t* bslot = bk.slot + part * kBucketCap;
+    const uint32_t* bpos = bk.pos + part * kBucketCap;
+    const float* btd = bk.td + part * kBucketCap;
+    const uint32_t mb = dense_update<kUpdThreads>(sm.u.dn, sm.flag, sm.sx, t, g, part, [&](auto f) {
+      for (uint32_t k = threadIdx.x; k < kBucketCap; k += kUpdThreads)
+        f(bslot[k] - base, bpos[k], priority_of(btd[k], m0, a.alpha, a.eps, a.p_nan));
+      for (uint32_t k = threadIdx.x; k < novf; k += kUpdThreads) {
+        const uint32_t i = bk.oslot[k];
+        if ((i >> g.S) == part)
+          f(i - base, bk.opos[k], priority_of(bk.otd[k], m0, a.alpha, a.eps, a.p_nan));
+      }
+    });
+    if (threadIdx.x == 0) publish_max(mb, false, m0, max_dst);
+  }
 }
 
 struct AddArgs {
@@ -737,10 +784,7 @@ __global__ void __launch_bounds__(256) add_kernel(TreePtrs t, Geom g, Storage st
   }
   if (a.prio) {
     mb = block_max_bits<kTreeThreads>(mb, sm.sx);
-    if (threadIdx.x == 0) {
-      if (w == 0) mb = max(mb, __float_as_uint(m0));
-      atomicMax(&t.ctrl->maxp_bits[a.dst], mb);
-    }
+    if (threadIdx.x == 0) publish_max(mb, w == 0, m0, &t.ctrl->maxp_bits[a.dst]);
   }
   __syncthreads();
   if (runs == 1) {
@@ -749,7 +793,7 @@ __global__ void __launch_bounds__(256) add_kernel(TreePtrs t, Geom g, Storage st
   }
   // Two runs in one partition (the ring wrapped inside it): general rebuild;
   // slots are distinct, so the offset doubles as the batch position.
-  dense_update<kTreeThreads>(sm.u.d, t, g, part, [&](auto f) {
+  dense_update<kTreeThreads>(sm.u.dn, sm.flag, sm.sx, t, g, part, [&](auto f) {
     for (int r = 0; r < runs; ++r)
       for (uint32_t off = lo[r] + threadIdx.x; off < hi[r]; off += kTreeThreads)
         f(off, off, value_of(off));
@@ -844,14 +888,23 @@ hipError_t launch_update(const TreePtrs& t, const Buckets& bk, const Geom& g, ui
   a.ovf = ovf;
   const uint64_t np = 1ull << g.P;
   if (!update_uses_buckets(g, B)) {
-    hipLaunchKernelGGL(update_scan_kernel, dim3((unsigned)np), dim3(kUpdThreads), 0, s, t, g,
+    // One partition per block: the batch scan is spread over the most blocks.
+    hipLaunchKernelGGL(update_scan_kernel<1>, dim3((unsigned)np), dim3(kUpdThreads), 0, s, t, g,
                        a);
     return hipGetLastError();
   }
+  // Bucketed: four partitions per block, one wave each, while the batch
+  // spreads thin over the partitions (<= 16 entries each on average), so
+  // that every wave of a block repairs; denser batches take one partition
+  // per block, so that crowded partitions are rebuilt in parallel.
+  const bool thin = (uint64_t)B <= 16 * np;
+  const unsigned grid = thin ? (unsigned)((np + 3) / 4) : (unsigned)np;
   const unsigned eb = grid_for((uint64_t)B, kTreeThreads, 1u << 30);
   hipLaunchKernelGGL(bucket_kernel, dim3(eb), dim3(kTreeThreads), 0, s, bk, g, a);
-  hipLaunchKernelGGL(update_bucket_kernel, dim3((unsigned)np), dim3(kUpdThreads), 0, s, t, bk,
-                     g, a);
+  if (thin)
+    hipLaunchKernelGGL(update_bucket_kernel<4>, dim3(grid), dim3(kUpdThreads), 0, s, t, bk, g, a);
+  else
+    hipLaunchKernelGGL(update_bucket_kernel<1>, dim3(grid), dim3(kUpdThreads), 0, s, t, bk, g, a);
   return hipGetLastError();
 }
 
