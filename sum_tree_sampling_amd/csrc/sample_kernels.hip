@@ -23,7 +23,7 @@
 //
 // Weights ("GPU-Resident Prioritized Experience Replay", section "Sampling
 // Kernels"): w = (N*P(i))^-beta normalised by the weight of the min-tree root
-// priority, in f64.  Rows are copied by the whole wave, 16 bytes per lane per
+// priority; N and the total cancel, so w = (p_i / p_min)^-beta, in f64.  Rows are copied by the whole wave, 16 bytes per lane per
 // access, straight into the caller's buffers ("True Single-Graph
 // Implementation Plan", Task 3).
 
@@ -35,6 +35,12 @@ namespace per {
 namespace {
 
 constexpr int kSampleThreads = 256;
+// Partition roots a lane reduces in the top rebuild: 2^kMaxTopBits roots
+// over four waves of 64 lanes.
+constexpr int kLgMaxRootsPerLane = kMaxTopBits - 8;
+constexpr int kMaxRootsPerLane = 1 << kLgMaxRootsPerLane;
+
+__device__ __forceinline__ float min_f32(float a, float b) { return (b < a) ? b : a; }
 
 struct SampleArgs {
   float* sum;
@@ -129,34 +135,109 @@ __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleArgs a) {
   float T, pmin;
   if (a.top_mode == kTopRebuild) {
     // Nodes [1, 2^P) from the partition roots at depth P: sums in top[],
-    // mins in mtop[].
-    const uint32_t np = 1u << a.P;
+    // mins in mtop[].  Each wave reduces a contiguous segment of the roots
+    // (four segments when there are at least 256 roots, else one): a lane
+    // loads c consecutive roots and reduces them in registers, then the
+    // lanes' results meet through shuffles, every node formed on the way
+    // stored to LDS.  Only the joins of the four segment roots wait for a
+    // barrier.
+    const int P = a.P;
+    const uint32_t np = 1u << P;
     float* mtop = top + 2 * np;
-    // All of a thread's loads go out before the first one is stored to LDS.
-    constexpr int kPer = (1 << kMaxTopBits) / kSampleThreads;
-    float ls[kPer], lm[kPer];
+    const int wv = threadIdx.x >> 6;
+    const int lgw = (P >= 8) ? 2 : 0;           // log2 of the waves used
+    const int lgseg = P - lgw;                  // log2 of a wave's roots
+    const int lgc = lgseg > 6 ? lgseg - 6 : 0;  // log2 of roots per lane
+    const int lgl = lgseg - lgc;                // log2 of the lanes used
+    if (lgc >= 2) {
+      // Four or more roots per lane: the whole block loads the roots
+      // coalesced into the depth-P level of top[] first (a lane's own roots
+      // would be 4 or more cache lines apart across the wave).
+      constexpr int kPer = (1 << kMaxTopBits) / kSampleThreads;
+      float ls[kPer], lm[kPer];
 #pragma unroll
-    for (int c = 0; c < kPer; ++c) {
-      const uint32_t k = threadIdx.x + c * kSampleThreads;
-      if (k < np) {
-        ls[c] = a.sum[np + k];
-        lm[c] = a.mn[np + k];
+      for (int c = 0; c < kPer; ++c) {
+        const uint32_t k = threadIdx.x + c * kSampleThreads;
+        if (k < np) {
+          ls[c] = a.sum[np + k];
+          lm[c] = a.mn[np + k];
+        }
       }
-    }
 #pragma unroll
-    for (int c = 0; c < kPer; ++c) {
-      const uint32_t k = threadIdx.x + c * kSampleThreads;
-      if (k < np) {
-        top[np + k] = ls[c];
-        mtop[np + k] = lm[c];
+      for (int c = 0; c < kPer; ++c) {
+        const uint32_t k = threadIdx.x + c * kSampleThreads;
+        if (k < np) {
+          top[np + k] = ls[c];
+          mtop[np + k] = lm[c];
+        }
+      }
+      __syncthreads();
+    }
+    if (wv < (1 << lgw)) {
+      const uint32_t k0 = np + ((uint32_t)wv << lgseg) + ((uint32_t)lane << lgc);  // first root
+      const bool on = lane < (1 << lgl);
+      const uint32_t c = 1u << lgc;
+      float v[kMaxRootsPerLane], mv[kMaxRootsPerLane];
+#pragma unroll
+      for (int i = 0; i < kMaxRootsPerLane; ++i) {
+        v[i] = 0.0f;
+        mv[i] = 0.0f;
+        if (on && (uint32_t)i < c) {
+          v[i] = (lgc >= 2) ? top[k0 + i] : a.sum[k0 + i];
+          mv[i] = (lgc >= 2) ? mtop[k0 + i] : a.mn[k0 + i];
+        }
+      }
+      if (on && lgc < 2) {
+#pragma unroll
+        for (int i = 0; i < kMaxRootsPerLane; ++i) {
+          if ((uint32_t)i < c) {
+            top[k0 + i] = v[i];
+            mtop[k0 + i] = mv[i];
+          }
+        }
+      }
+#pragma unroll
+      for (int r = 1; r <= kLgMaxRootsPerLane; ++r) {
+        if (r <= lgc) {
+          const uint32_t x0 = k0 >> r;
+#pragma unroll
+          for (int i = 0; i < (kMaxRootsPerLane >> r); ++i) {
+            if ((uint32_t)i < (c >> r)) {
+              v[i] = v[2 * i] + v[2 * i + 1];
+              mv[i] = min_f32(mv[2 * i], mv[2 * i + 1]);
+              if (on) {
+                top[x0 + i] = v[i];
+                mtop[x0 + i] = mv[i];
+              }
+            }
+          }
+        }
+      }
+      float s0 = v[0], m0 = mv[0];
+      for (int q = 0; q < lgl; ++q) {
+        const float sr = __shfl_down(s0, 1 << q);
+        const float mr = __shfl_down(m0, 1 << q);
+        if (on && (lane & ((2 << q) - 1)) == 0) {
+          s0 = s0 + sr;
+          m0 = min_f32(m0, mr);
+          const uint32_t x = k0 >> (lgc + q + 1);
+          top[x] = s0;
+          mtop[x] = m0;
+        }
       }
     }
     __syncthreads();
-    for (uint32_t width = np >> 1; width >= 1; width >>= 1) {
-      for (uint32_t h = width + threadIdx.x; h < 2 * width; h += kSampleThreads) {
-        top[h] = top[2 * h] + top[2 * h + 1];
-        const float l = mtop[2 * h], r = mtop[2 * h + 1];
-        mtop[h] = (r < l) ? r : l;
+    if (lgw > 0) {
+      // The four segment roots are nodes 4..7.
+      if (threadIdx.x == 0) {
+        const float s2 = top[4] + top[5], s3 = top[6] + top[7];
+        const float m2 = min_f32(mtop[4], mtop[5]), m3 = min_f32(mtop[6], mtop[7]);
+        top[2] = s2;
+        top[3] = s3;
+        mtop[2] = m2;
+        mtop[3] = m3;
+        top[1] = s2 + s3;
+        mtop[1] = min_f32(m2, m3);
       }
       __syncthreads();
     }
@@ -242,22 +323,26 @@ __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleArgs a) {
   }
 
   const uint32_t slot = node - a.n;
-  if (active && j == 0) {
+  const bool lead = active && j == 0;
+  // The scalar fields of the sampled transition: loaded now, stored after
+  // the rows, so that their trip to memory overlaps the row copy.
+  uint32_t act = 0u;
+  float rew = 0.0f;
+  uint8_t done = 0;
+  if (lead && a.states_out) {
+    act = a.st.actions[slot];
+    rew = a.st.rewards[slot];
+    done = a.st.dones[slot];
+  }
+  if (lead) {
     a.idx_out[b] = (int64_t)slot;
     if (a.w_out) {
+      // (N P_i)^-beta / (N P_min)^-beta = (p_i / p_min)^-beta: one pow, f64.
+      // With p_min > 0 every stored priority, the sampled one included, is
+      // > 0; with p_min = 0 the normaliser is infinite and w = 0.
       float w = 0.0f;
-      if (pmin > 0.0f) {
-        const double N = (double)a.size;
-        const double P_i = (double)leaf / (double)T;
-        const double P_min = (double)pmin / (double)T;
-        w = (float)(pow(N * P_i, -a.beta) / pow(N * P_min, -a.beta));
-      }
+      if (pmin > 0.0f) w = (float)pow((double)leaf / (double)pmin, -a.beta);
       a.w_out[b] = w;
-    }
-    if (a.states_out) {
-      a.actions_out[b] = a.st.actions[slot];
-      a.rewards_out[b] = a.st.rewards[slot];
-      a.dones_out[b] = a.st.dones[slot];
     }
   }
 
@@ -309,6 +394,11 @@ __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleArgs a) {
         }
       }
     }
+  }
+  if (lead && a.states_out) {
+    a.actions_out[b] = act;
+    a.rewards_out[b] = rew;
+    a.dones_out[b] = done;
   }
 }
 
