@@ -327,40 +327,35 @@ __device__ void dense_sub_rebuild(DenseSmem& dn, const TreePtrs& t, uint32_t sub
       const bool ba = has_bit(dn, a), bb = has_bit(dn, a + 1);
       const float ls = ba ? dn.val[a] : os[r].x, lm = ba ? dn.val[a] : om[r].x;
       const float rs = bb ? dn.val[a + 1] : os[r].y, rm = bb ? dn.val[a + 1] : om[r].y;
-      if (ba) {
-        t.sum[leaf0 + a] = ls;
-        t.mn[leaf0 + a] = lm;
-      }
-      if (bb) {
-        t.sum[leaf0 + a + 1] = rs;
-        t.mn[leaf0 + a + 1] = rm;
-      }
-      const float s = ls + rs, m = min_f32(lm, rm);
-      dn.hs[h] = s;
-      dn.hm[h] = m;
+      dn.hs[h] = ls + rs;
+      dn.hm[h] = min_f32(lm, rm);
       dn.dirty[h] = ba | bb;
-      if (ba | bb) {
-        const uint32_t x = ((subroot - 1u) << (sb - 1)) + h;
-        t.sum[x] = s;
-        t.mn[x] = m;
-      }
     }
   }
-  // local heap index h in [1, span) <-> global node ((subroot - 1) << depth(h)) + h
-  for (uint32_t width = half >> 1, dl = sb - 2; width >= 1; width >>= 1, --dl) {
+  // The levels above in LDS, nothing stored to global memory in between: a
+  // barrier waits for every outstanding memory operation, stores included.
+  for (uint32_t width = half >> 1; width >= 1; width >>= 1) {
     __syncthreads();
     for (uint32_t h = width + threadIdx.x; h < 2 * width; h += NT) {
-      const float s = dn.hs[2 * h] + dn.hs[2 * h + 1];
-      const float m = min_f32(dn.hm[2 * h], dn.hm[2 * h + 1]);
-      const uint8_t dv = dn.dirty[2 * h] | dn.dirty[2 * h + 1];
-      dn.hs[h] = s;
-      dn.hm[h] = m;
-      dn.dirty[h] = dv;
-      if (dv) {
-        const uint32_t x = ((subroot - 1u) << dl) + h;
-        t.sum[x] = s;
-        t.mn[x] = m;
-      }
+      dn.hs[h] = dn.hs[2 * h] + dn.hs[2 * h + 1];
+      dn.hm[h] = min_f32(dn.hm[2 * h], dn.hm[2 * h + 1]);
+      dn.dirty[h] = dn.dirty[2 * h] | dn.dirty[2 * h + 1];
+    }
+  }
+  __syncthreads();
+  // New leaves, then every node with a new leaf below it; local heap index
+  // h in [1, span) is global node ((subroot - 1) << depth(h)) + h.
+  for (uint32_t a = threadIdx.x; a < span; a += NT) {
+    if (has_bit(dn, a)) {
+      t.sum[leaf0 + a] = dn.val[a];
+      t.mn[leaf0 + a] = dn.val[a];
+    }
+  }
+  for (uint32_t h = 1 + threadIdx.x; h < span; h += NT) {
+    if (dn.dirty[h]) {
+      const uint32_t x = ((subroot - 1u) << (31 - __clz(h))) + h;
+      t.sum[x] = dn.hs[h];
+      t.mn[x] = dn.hm[h];
     }
   }
 }
@@ -418,10 +413,10 @@ __device__ uint32_t dense_update(DenseSmem& dn, int& flag, BlockScratch& sx, con
 // ------------------------------------------------------------ intake range
 
 struct RangeSmem {
-  float val[kMaxSpan];                  // new leaf values by offset
-  float bs[2][kMaxSpan / 2];            // level values, two buffers, sums
-  float bm[2][kMaxSpan / 2];            // and mins
-  float bnd_s[2][kMaxSpanBits];         // boundary siblings per level: left, right
+  float val[kMaxSpan];                      // new leaf values by offset
+  float ns[kMaxSpan + 2 * kMaxSpanBits];    // dirty nodes of heights 1..S, packed
+  float nm[kMaxSpan + 2 * kMaxSpanBits];    // height after height: sums, mins
+  float bnd_s[2][kMaxSpanBits];             // boundary siblings per level: left, right
   float bnd_m[2][kMaxSpanBits];
 };
 
@@ -457,38 +452,140 @@ __device__ __forceinline__ void prefetch_range_boundaries(RangeSmem& r, const Tr
   }
 }
 
+// The boundary sibling of height q = lane & 31 of a run [lo, hi) of new
+// leaves, into the registers of the block's first wave: lanes 0..31 the
+// sibling left of the run's first node at height q (needed when that node
+// is a right child), lanes 32..63 the sibling right of its last node (needed
+// when that node is a left child); other lanes and unneeded siblings: 0.
+__device__ __forceinline__ void load_range_boundary(const TreePtrs& t, const Geom& g,
+                                                    uint32_t part, uint32_t lo, uint32_t hi,
+                                                    float& sib_s, float& sib_m) {
+  const uint32_t a = g.n + (part << g.S) + lo, b = g.n + (part << g.S) + hi - 1;
+  const int q = threadIdx.x & 31;
+  if (threadIdx.x < 64 && q < g.S) {
+    const bool left = threadIdx.x < 32;
+    const uint32_t x = (left ? a : b) >> q;
+    if (left ? (x & 1u) : !(x & 1u)) {
+      const uint32_t sib = left ? x - 1 : x + 1;
+      sib_s = t.sum[sib];
+      sib_m = t.mn[sib];
+    }
+  }
+}
+
+// Repair after a contiguous run [lo, hi) of new leaves that all take the
+// value v.  A node strictly between the run's first and last node of its
+// height k covers 2^k new leaves and nothing else: its sum is v doubled k
+// times, which is exactly what the pairwise adds of its subtree give, and
+// its min is v.  Those nodes and the leaves are stored by the whole block,
+// independently.  Only the first and last node of each height can have an
+// old leaf below; the block's first wave walks them up together (every lane
+// takes the same steps, lane 0 stores), the stored siblings coming from the
+// registers load_range_boundary filled.  No barrier anywhere.
+__device__ __forceinline__ void uniform_range(const TreePtrs& t, const Geom& g, uint32_t part,
+                                              uint32_t lo, uint32_t hi, float v, float sib_s,
+                                              float sib_m) {
+  const uint32_t leaf0 = g.n + (part << g.S);
+  // Every load is complete before the first store: a wait placed after
+  // stores (the compiler joins the paths of the waves below) would also
+  // wait for those stores.
+  asm volatile("" ::"v"(v), "v"(sib_s), "v"(sib_m));
+  if (threadIdx.x < 64) {
+    uint32_t A = leaf0 + lo, Bn = leaf0 + hi - 1;  // first and last node of the height
+    float sL = v, mL = v, sR = v, mR = v;         // their sums and mins
+    float full = v;                               // sum of a node over new leaves only
+    for (int k = 0; k < g.S; ++k) {
+      // Siblings left of A (stored when A is a right child) and right of Bn
+      // (stored when Bn is a left child).
+      const float bls = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sib_s), k));
+      const float blm = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sib_m), k));
+      const float brs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sib_s), 32 + k));
+      const float brm = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sib_m), 32 + k));
+      // Node A+1 (the right sibling of A when A is a left child) and node
+      // Bn-1 (the left sibling of Bn when Bn is a right child).
+      const float ns = (A + 1 < Bn) ? full : ((A + 1 == Bn) ? sR : brs);
+      const float nm = (A + 1 < Bn) ? v : ((A + 1 == Bn) ? mR : brm);
+      const float ps = (Bn - 1 > A) ? full : ((Bn - 1 == A) ? sL : bls);
+      const float pm = (Bn - 1 > A) ? v : ((Bn - 1 == A) ? mL : blm);
+      const float nls = (A & 1u) ? bls + sL : sL + ns;
+      const float nlm = (A & 1u) ? min_f32(blm, mL) : min_f32(mL, nm);
+      const float nrs = (Bn & 1u) ? ps + sR : sR + brs;
+      const float nrm = (Bn & 1u) ? min_f32(pm, mR) : min_f32(mR, brm);
+      A >>= 1;
+      Bn >>= 1;
+      if (threadIdx.x == 0) {
+        t.sum[A] = nls;
+        t.mn[A] = nlm;
+        if (Bn != A) {
+          t.sum[Bn] = nrs;
+          t.mn[Bn] = nrm;
+        }
+      }
+      sL = nls;
+      mL = nlm;
+      sR = nrs;
+      mR = nrm;
+      full = full + full;
+    }
+  }
+  float full = v;  // sum of a node of height k covering new leaves only
+  for (int k = 0; k <= g.S; ++k) {
+    const uint32_t A = (leaf0 + lo) >> k, Bn = (leaf0 + hi - 1) >> k;
+    const uint32_t first = (k == 0) ? A : A + 1;
+    for (uint32_t x = first + threadIdx.x; x < Bn + (k == 0 ? 1u : 0u); x += kTreeThreads) {
+      t.sum[x] = full;
+      t.mn[x] = v;
+    }
+    full = full + full;
+  }
+}
+
 // Rebuild after a contiguous run [lo, hi) of new leaves (values in r.val),
 // level by level in LDS with a barrier between levels (whole block).
 __device__ void range_repair(RangeSmem& r, const TreePtrs& t, const Geom& g, uint32_t part,
                              uint32_t lo, uint32_t hi) {
+  // Heights 1..S in LDS first: a barrier waits for every outstanding memory
+  // operation of the block, stores included, so nothing is stored to
+  // global memory until the last one.
   const uint32_t leaf0 = g.n + (part << g.S);
-  for (uint32_t off = lo + threadIdx.x; off < hi; off += kTreeThreads)
-  {
-    t.sum[leaf0 + off] = r.val[off];
-    t.mn[leaf0 + off] = r.val[off];
-  }
   uint32_t A = leaf0 + lo, Bn = leaf0 + hi - 1;  // children range (node indices)
   const float* cs = r.val + lo;                   // children values, index x - A
   const float* cm = r.val + lo;
+  uint32_t at = 0;                                // packed position of the height
   for (int k = 0; k < g.S; ++k) {
     const uint32_t pa = A >> 1, pb = Bn >> 1;
-    float* ns = r.bs[k & 1];
-    float* nm = r.bm[k & 1];
+    float* ns = r.ns + at;
+    float* nm = r.nm + at;
     for (uint32_t x = pa + threadIdx.x; x <= pb; x += kTreeThreads) {
       const uint32_t l = 2 * x, rr = 2 * x + 1;
       const float ls = (l >= A) ? cs[l - A] : r.bnd_s[0][k];
       const float lm = (l >= A) ? cm[l - A] : r.bnd_m[0][k];
       const float rs = (rr <= Bn) ? cs[rr - A] : r.bnd_s[1][k];
       const float rm = (rr <= Bn) ? cm[rr - A] : r.bnd_m[1][k];
-      const float s = ls + rs, m = min_f32(lm, rm);
-      ns[x - pa] = s;
-      nm[x - pa] = m;
-      t.sum[x] = s;
-      t.mn[x] = m;
+      ns[x - pa] = ls + rs;
+      nm[x - pa] = min_f32(lm, rm);
     }
     __syncthreads();
     cs = ns;
     cm = nm;
+    at += pb - pa + 1;
+    A = pa;
+    Bn = pb;
+  }
+  for (uint32_t off = lo + threadIdx.x; off < hi; off += kTreeThreads) {
+    t.sum[leaf0 + off] = r.val[off];
+    t.mn[leaf0 + off] = r.val[off];
+  }
+  A = leaf0 + lo;
+  Bn = leaf0 + hi - 1;
+  at = 0;
+  for (int k = 0; k < g.S; ++k) {
+    const uint32_t pa = A >> 1, pb = Bn >> 1;
+    for (uint32_t x = pa + threadIdx.x; x <= pb; x += kTreeThreads) {
+      t.sum[x] = r.ns[at + x - pa];
+      t.mn[x] = r.nm[at + x - pa];
+    }
+    at += pb - pa + 1;
     A = pa;
     Bn = pb;
   }
@@ -766,6 +863,14 @@ __global__ void __launch_bounds__(256) add_kernel(TreePtrs t, Geom g, Storage st
       ++runs;
     }
   }
+  if (runs == 1 && !a.prio) {
+    // One run at the running max (the usual intake): no LDS, no barrier.
+    float sib_s = 0.0f, sib_m = 0.0f;
+    load_range_boundary(t, g, part, lo[0], hi[0], sib_s, sib_m);
+    const float m0 = __uint_as_float(t.ctrl->maxp_bits[a.src]);
+    uniform_range(t, g, part, lo[0], hi[0], m0, sib_s, sib_m);
+    return;
+  }
   // One run (the usual case): its boundary siblings go out with the other loads.
   if (runs == 1) prefetch_range_boundaries(sm.u.r, t, g, part, lo[0], hi[0]);
   const float m0 = __uint_as_float(t.ctrl->maxp_bits[a.src]);
@@ -814,22 +919,22 @@ __global__ void __launch_bounds__(256) top_kernel(TreePtrs t, Geom g) {
     for (uint32_t h = half + threadIdx.x; h < np; h += kTreeThreads) {
       const float2 cs = *reinterpret_cast<const float2*>(t.sum + 2 * h);
       const float2 cm = *reinterpret_cast<const float2*>(t.mn + 2 * h);
-      const float s = cs.x + cs.y, m = min_f32(cm.x, cm.y);
-      sm.s[h] = s;
-      sm.m[h] = m;
-      t.sum[h] = s;
-      t.mn[h] = m;
+      sm.s[h] = cs.x + cs.y;
+      sm.m[h] = min_f32(cm.x, cm.y);
     }
+    // In LDS level by level, stored once after the last barrier (a barrier
+    // also waits for outstanding global stores).
     for (uint32_t width = half >> 1; width >= 1; width >>= 1) {
       __syncthreads();
       for (uint32_t h = width + threadIdx.x; h < 2 * width; h += kTreeThreads) {
-        const float s = sm.s[2 * h] + sm.s[2 * h + 1];
-        const float m = min_f32(sm.m[2 * h], sm.m[2 * h + 1]);
-        sm.s[h] = s;
-        sm.m[h] = m;
-        t.sum[h] = s;
-        t.mn[h] = m;
+        sm.s[h] = sm.s[2 * h] + sm.s[2 * h + 1];
+        sm.m[h] = min_f32(sm.m[2 * h], sm.m[2 * h + 1]);
       }
+    }
+    __syncthreads();
+    for (uint32_t h = 1 + threadIdx.x; h < np; h += kTreeThreads) {
+      t.sum[h] = sm.s[h];
+      t.mn[h] = sm.m[h];
     }
   } else {
     // More top nodes than LDS holds: level by level through global memory.

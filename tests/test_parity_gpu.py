@@ -189,6 +189,27 @@ def test_ring_intake_and_random_ops(n):
         compare_trees(o, g, "ring n=%d step %d update" % (n, step))
 
 
+def test_intake_at_extreme_running_max():
+    """Intake at the running max after that max was driven to 3e38: the
+    interior subtrees of each run overflow to +inf, which the pairwise adds
+    and the repeated doubling of the uniform-run repair must reach alike."""
+    say("intake at 3e38")
+    n = 1 << 13
+    rng = np.random.default_rng(7)
+    o = Oracle(n, 0)
+    g = _buf(n)
+    p0 = rng.random(n).astype(np.float32)
+    o.add(n, prio=p0)
+    g.add(n, prio=dev(p0))
+    big = np.full(3, 3e38, np.float32)
+    o.add(3, prio=big)
+    g.add(3, prio=dev(big))
+    for c in (1, 2, 500, 4093, 3000):
+        o.add(c)
+        g.add(c)
+        compare_trees(o, g, "intake %d at 3e38" % c)
+
+
 def test_partial_fill_and_empty():
     from sum_tree_sampling_amd import PerError
     n = 1 << 15
