@@ -35,10 +35,6 @@ namespace per {
 namespace {
 
 constexpr int kSampleThreads = 256;
-// Partition roots a lane reduces in the top rebuild: 2^kMaxTopBits roots
-// over four waves of 64 lanes.
-constexpr int kLgMaxRootsPerLane = kMaxTopBits - 8;
-constexpr int kMaxRootsPerLane = 1 << kLgMaxRootsPerLane;
 
 __device__ __forceinline__ float min_f32(float a, float b) { return (b < a) ? b : a; }
 
@@ -145,14 +141,16 @@ __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleArgs a) {
     const uint32_t np = 1u << P;
     float* mtop = top + 2 * np;
     const int wv = threadIdx.x >> 6;
-    const int lgw = (P >= 8) ? 2 : 0;           // log2 of the waves used
-    const int lgseg = P - lgw;                  // log2 of a wave's roots
-    const int lgc = lgseg > 6 ? lgseg - 6 : 0;  // log2 of roots per lane
+    const int lgw = (P >= 8) ? 2 : 0;  // log2 of the waves of the wave stage
+    // With more than 512 roots the levels down to depth Pw = 8 are reduced
+    // block-wide first (coalesced loads, conflict-free pair reads, a barrier
+    // per level), so that a lane of the wave stage starts from one node;
+    // otherwise the wave stage starts from the roots, at most two per lane.
+    const int Pw = (P - lgw > 7) ? lgw + 6 : P;
+    const int lgseg = Pw - lgw;                 // log2 of a wave's nodes at depth Pw
+    const int lgc = lgseg > 6 ? lgseg - 6 : 0;  // log2 of nodes per lane (<= 1)
     const int lgl = lgseg - lgc;                // log2 of the lanes used
-    if (lgc >= 2) {
-      // Four or more roots per lane: the whole block loads the roots
-      // coalesced into the depth-P level of top[] first (a lane's own roots
-      // would be 4 or more cache lines apart across the wave).
+    if (Pw < P) {
       constexpr int kPer = (1 << kMaxTopBits) / kSampleThreads;
       float ls[kPer], lm[kPer];
 #pragma unroll
@@ -171,46 +169,46 @@ __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleArgs a) {
           mtop[np + k] = lm[c];
         }
       }
+      for (uint32_t width = np >> 1; width >= (1u << Pw); width >>= 1) {
+        __syncthreads();
+        for (uint32_t h = width + threadIdx.x; h < 2 * width; h += kSampleThreads) {
+          const float2 cs = reinterpret_cast<const float2*>(top)[h];  // children 2h, 2h+1
+          const float2 cm = reinterpret_cast<const float2*>(mtop)[h];
+          top[h] = cs.x + cs.y;
+          mtop[h] = min_f32(cm.x, cm.y);
+        }
+      }
       __syncthreads();
     }
     if (wv < (1 << lgw)) {
-      const uint32_t k0 = np + ((uint32_t)wv << lgseg) + ((uint32_t)lane << lgc);  // first root
+      const uint32_t k0 = (1u << Pw) + ((uint32_t)wv << lgseg) + ((uint32_t)lane << lgc);
       const bool on = lane < (1 << lgl);
       const uint32_t c = 1u << lgc;
-      float v[kMaxRootsPerLane], mv[kMaxRootsPerLane];
+      float v[2], mv[2];
 #pragma unroll
-      for (int i = 0; i < kMaxRootsPerLane; ++i) {
+      for (int i = 0; i < 2; ++i) {
         v[i] = 0.0f;
         mv[i] = 0.0f;
         if (on && (uint32_t)i < c) {
-          v[i] = (lgc >= 2) ? top[k0 + i] : a.sum[k0 + i];
-          mv[i] = (lgc >= 2) ? mtop[k0 + i] : a.mn[k0 + i];
+          v[i] = (Pw < P) ? top[k0 + i] : a.sum[k0 + i];
+          mv[i] = (Pw < P) ? mtop[k0 + i] : a.mn[k0 + i];
         }
       }
-      if (on && lgc < 2) {
+      if (on && Pw == P) {
 #pragma unroll
-        for (int i = 0; i < kMaxRootsPerLane; ++i) {
+        for (int i = 0; i < 2; ++i) {
           if ((uint32_t)i < c) {
             top[k0 + i] = v[i];
             mtop[k0 + i] = mv[i];
           }
         }
       }
-#pragma unroll
-      for (int r = 1; r <= kLgMaxRootsPerLane; ++r) {
-        if (r <= lgc) {
-          const uint32_t x0 = k0 >> r;
-#pragma unroll
-          for (int i = 0; i < (kMaxRootsPerLane >> r); ++i) {
-            if ((uint32_t)i < (c >> r)) {
-              v[i] = v[2 * i] + v[2 * i + 1];
-              mv[i] = min_f32(mv[2 * i], mv[2 * i + 1]);
-              if (on) {
-                top[x0 + i] = v[i];
-                mtop[x0 + i] = mv[i];
-              }
-            }
-          }
+      if (lgc == 1) {
+        v[0] = v[0] + v[1];
+        mv[0] = min_f32(mv[0], mv[1]);
+        if (on) {
+          top[k0 >> 1] = v[0];
+          mtop[k0 >> 1] = mv[0];
         }
       }
       float s0 = v[0], m0 = mv[0];
