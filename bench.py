@@ -141,6 +141,43 @@ def measured_traffic(workload: str, op: str):
     return None if e is None else float(e["bytes"])
 
 
+def graph_replay(g, step, K: int, base: int, stream) -> dict:
+    """K whole steps captured as one HIP graph and replayed: the step time
+    without per-launch host work, a labelled extra figure next to the eager
+    headline.  The library's host state (running-max slot, overflow counter,
+    ring cursor) advances during the capture exactly as in eager steps; K is
+    even, so the running-max and overflow parities of a replay start where
+    the previous one left them, while the captured intakes rewrite the same
+    ring slots on every replay."""
+    import torch
+    try:
+        gr = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step(base)  # warm the capture stream
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(gr):
+            for s in range(K):
+                step(base + s)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            gr.replay()
+        torch.cuda.synchronize()
+        reps = 20
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(torch.cuda.current_stream())
+        for _ in range(reps):
+            gr.replay()
+        b.record(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        return {"steps_per_graph": K, "replays": reps,
+                "ms_per_step": a.elapsed_time(b) / (reps * K)}
+    except Exception as e:  # capture not available: report instead of failing the line
+        return {"error": "%s: %s" % (type(e).__name__, e)}
+
+
 def copy_calibration() -> None:
     """A plain device-to-device copy of CALIB_FLOATS f32, CALIB_REPS times."""
     import torch
@@ -214,6 +251,9 @@ def main():
     ap.add_argument("--workload", default="apex_shard_2m", choices=list(workloads.WORKLOADS))
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph-steps", type=int, default=64,
+                    help="whole steps captured as one HIP graph for the labelled replay "
+                         "figure (even; 0 skips it)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run the plain copy the HBM counters are scaled by")
     ap.add_argument("--ingest-pmc", metavar="DIR",
@@ -323,6 +363,34 @@ def main():
         torch.cuda.synchronize()
         op_avg[name] = a.elapsed_time(b) / args.steps
 
+    # Pass 3: whole steps again, an event pair around every operation, for the
+    # spread of each (every pair also spans the dispatch gap in front of its
+    # kernel, so these run above the back-to-back averages).
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for s in range(args.steps):
+        e = evs[s]
+        e[0].record(stream)
+        g.sample(u_d[base + s], beta=spec["beta"], weights=spec["weights"], out=out)
+        e[1].record(stream)
+        g.update(idx_d[base + s] if idx_d is not None else out["idx"], td_d[base + s])
+        e[2].record(stream)
+        if intake:
+            g.add(intake)
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    spread = {}
+    for k, name in enumerate(["sample", "update", "add"]):
+        if name == "add" and not intake:
+            continue
+        t = np.array([e[k].elapsed_time(e[k + 1]) for e in evs])
+        spread[name] = {q: float(np.percentile(t, v)) for q, v in (("p10", 10), ("p50", 50), ("p90", 90))}
+
+    graph = None
+    kg = min(args.graph_steps, args.steps)  # inputs exist for K steps past base
+    kg -= kg % 2
+    if kg > 0:
+        graph = graph_replay(g, step, kg, base, stream)
+
     byts = algorithmic_bytes(spec)
     dom = max(op_avg, key=op_avg.get)
     achieved = byts[dom] / (op_avg[dom] * 1e-3) / 1e9
@@ -347,6 +415,8 @@ def main():
         "samples_per_s": B / (op_avg["sample"] * 1e-3),
         "updates_per_s": B / (op_avg["update"] * 1e-3),
         "op_ms_avg": op_avg,
+        "op_ms_bracketed": spread,
+        "graph_replay": graph,
         "host_ms_per_step": host_ms / args.steps,
         "step_algorithmic_bytes": step_bytes,
         "step_hbm_roofline_frac": step_bytes / (ms_per_step * 1e-3) / (PEAK_HBM_GBS * 1e9),
