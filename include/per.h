@@ -45,6 +45,7 @@ extern "C" {
 
 #define PER_MAX_CAPACITY (1LL << 30)
 #define PER_MAX_BATCH (1LL << 24)
+#define PER_MAX_OUT_STRIDE (1LL << 20)
 
 typedef struct per_s per_t;
 
@@ -145,6 +146,26 @@ int per_sample(per_t* h, int64_t B, const float* d_u, double beta, int64_t* d_id
                float* d_w_out, float* d_states_out, float* d_next_states_out,
                uint32_t* d_actions_out, float* d_rewards_out, uint8_t* d_dones_out,
                hipStream_t stream);
+
+/*
+ * per_sample written straight into a trainer's input buffers ("True
+ * Single-Graph Implementation Plan", Task 2: rows gathered into a padded
+ * destination, scalars gathered as f32 / i32; Task 3: the sampler writes the
+ * trainer's buffers directly).  Same masses, descent, indices and weights
+ * as per_sample.  Differences, all in the row outputs:
+ *  out_stride: floats per output state row, in [state_dim,
+ *    PER_MAX_OUT_STRIDE] (else PER_EINVAL); d_states_out / d_next_states_out
+ *    are [B x out_stride] f32 (16-byte aligned): columns [0, state_dim) hold
+ *    the stored row, columns [state_dim, out_stride) are written as +0.0.
+ *  d_actions_out [B] i32: the stored 32 bits of the action.
+ *  d_dones_out [B] f32: the stored done byte's value (0.0 or 1.0 for 0 / 1).
+ * Row outputs all NULL (then out_stride is only range-checked) or all given
+ * when the handle has storage.  Errors as per_sample.
+ */
+int per_sample_padded(per_t* h, int64_t B, const float* d_u, double beta, int64_t* d_idx_out,
+                      float* d_w_out, float* d_states_out, float* d_next_states_out,
+                      int64_t out_stride, int32_t* d_actions_out, float* d_rewards_out,
+                      float* d_dones_out, hipStream_t stream);
 
 /*
  * The nodes above the update partitions (the top levels of both trees) are

@@ -49,6 +49,8 @@ def _bind(path: str):
     lib.pero_update.argtypes = [vp, i64, vp, vp]
     lib.pero_sample.restype = ctypes.c_int
     lib.pero_sample.argtypes = [vp, i64, vp, f64, vp, vp, vp, vp, vp, vp, vp]
+    lib.pero_sample_padded.restype = ctypes.c_int
+    lib.pero_sample_padded.argtypes = [vp, i64, vp, f64, vp, vp, vp, vp, i64, vp, vp, vp]
     for name in ("pero_total", "pero_min", "pero_max_priority"):
         getattr(lib, name).restype = f32
         getattr(lib, name).argtypes = [vp]
@@ -142,6 +144,33 @@ class Oracle:
         if weights:
             res["w"] = w
         if rows and D > 0:
+            res.update(states=outs[0], next_states=outs[1], actions=outs[2],
+                       rewards=outs[3], dones=outs[4])
+        return res
+
+    def sample_padded(self, u, out_stride, beta=0.4, weights=True, rows=True):
+        """pero_sample_padded: rows [B, out_stride] f32 zero past state_dim,
+        actions i32, rewards f32, dones f32."""
+        u = _c(u, np.float32)
+        B = u.size
+        idx = np.empty(B, np.int64)
+        w = np.empty(B, np.float32) if weights else None
+        outs = [None] * 5
+        if rows and self.state_dim > 0:
+            outs = [np.full((B, out_stride), np.nan, np.float32),
+                    np.full((B, out_stride), np.nan, np.float32),
+                    np.empty(B, np.int32), np.empty(B, np.float32), np.empty(B, np.float32)]
+        rc = self._lib.pero_sample_padded(self._h, B, _ptr(u), float(beta), _ptr(idx), _ptr(w),
+                                          _ptr(outs[0]), _ptr(outs[1]), int(out_stride),
+                                          *[_ptr(o) for o in outs[2:]])
+        if rc == -3:
+            raise RuntimeError("sample from an empty buffer")
+        if rc != 0:
+            raise ValueError("pero_sample_padded failed rc=%d" % rc)
+        res = {"idx": idx}
+        if weights:
+            res["w"] = w
+        if rows and self.state_dim > 0:
             res.update(states=outs[0], next_states=outs[1], actions=outs[2],
                        rewards=outs[3], dones=outs[4])
         return res

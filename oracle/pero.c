@@ -217,6 +217,33 @@ int pero_sample(const pero_t* t, int64_t B, const float* u, double beta, int64_t
     return 0;
 }
 
+/* The same sample written straight into a trainer's buffers ("True
+ * Single-Graph Implementation Plan", Tasks 2 and 3): indices and weights are
+ * those of pero_sample; each state row goes into a destination row of
+ * out_stride >= D floats whose columns D .. out_stride-1 are 0; actions are
+ * written as i32 (the stored 32 bits), rewards as f32 and dones as f32 (the
+ * stored byte's value).  Row outputs all NULL, or all given. */
+int pero_sample_padded(const pero_t* t, int64_t B, const float* u, double beta, int64_t* idx_out,
+                       float* w_out, float* states_out, float* next_states_out,
+                       int64_t out_stride, int32_t* actions_out, float* rewards_out,
+                       float* dones_out) {
+    const int64_t D = t->D;
+    if (out_stride < D) return -1;
+    int rc = pero_sample(t, B, u, beta, idx_out, w_out, NULL, NULL, NULL, NULL, NULL);
+    if (rc != 0 || D == 0 || !states_out) return rc;
+    for (int64_t b = 0; b < B; ++b) {
+        const int64_t slot = idx_out[b];
+        for (int64_t c = 0; c < out_stride; ++c) {
+            states_out[b * out_stride + c] = (c < D) ? t->states[slot * D + c] : 0.0f;
+            next_states_out[b * out_stride + c] = (c < D) ? t->next_states[slot * D + c] : 0.0f;
+        }
+        memcpy(&actions_out[b], &t->actions[slot], sizeof(int32_t));
+        rewards_out[b] = t->rewards[slot];
+        dones_out[b] = (float)t->dones[slot];
+    }
+    return 0;
+}
+
 float pero_total(const pero_t* t) { return t->sum[1]; }
 float pero_min(const pero_t* t) { return t->mn[1]; }
 float pero_max_priority(const pero_t* t) { return t->maxp; }

@@ -71,6 +71,14 @@ int pero_sample(const pero_t* t, int64_t B, const float* u, double beta, int64_t
                 float* w_out, float* states_out, float* next_states_out,
                 uint32_t* actions_out, float* rewards_out, uint8_t* dones_out);
 
+/* pero_sample written into padded trainer buffers: state rows of out_stride
+ * >= D floats, zero past column D; actions i32 (stored bits), rewards f32,
+ * dones f32.  -1 if out_stride < D. */
+int pero_sample_padded(const pero_t* t, int64_t B, const float* u, double beta, int64_t* idx_out,
+                       float* w_out, float* states_out, float* next_states_out,
+                       int64_t out_stride, int32_t* actions_out, float* rewards_out,
+                       float* dones_out);
+
 float pero_total(const pero_t* t);
 float pero_min(const pero_t* t);
 float pero_max_priority(const pero_t* t);

@@ -243,14 +243,21 @@ int per_update(per_t* h, int64_t B, const int64_t* d_idx, const float* d_td,
   return ok();
 }
 
-int per_sample(per_t* h, int64_t B, const float* d_u, double beta, int64_t* d_idx_out,
-               float* d_w_out, float* d_states_out, float* d_next_states_out,
-               uint32_t* d_actions_out, float* d_rewards_out, uint8_t* d_dones_out,
-               hipStream_t stream) {
+namespace {
+
+// Shared by per_sample and per_sample_padded: out_stride floats per output
+// state row (>= state_dim), dones as u8 or as f32.
+int sample_impl(per_t* h, int64_t B, const float* d_u, double beta, int64_t* d_idx_out,
+                float* d_w_out, float* d_states_out, float* d_next_states_out,
+                int64_t out_stride, uint32_t* d_actions_out, float* d_rewards_out,
+                void* d_dones_out, bool dones_f32, hipStream_t stream, const char* what) {
   if (!h) return fail(PER_EINVAL, "handle is NULL");
   if (B < 0 || B > h->max_batch)
     return fail(PER_EINVAL, "B %lld outside [0, max_batch=%lld]", (long long)B,
                 (long long)h->max_batch);
+  if (out_stride < h->st.D || out_stride > PER_MAX_OUT_STRIDE)
+    return fail(PER_EINVAL, "out_stride %lld outside [state_dim=%d, %lld]", (long long)out_stride,
+                (int)h->st.D, (long long)PER_MAX_OUT_STRIDE);
   if (B == 0) return ok();
   if (!d_u || !d_idx_out) return fail(PER_EINVAL, "u and idx_out are required");
   if (!(beta >= 0.0) || !(beta < 1e300)) return fail(PER_EINVAL, "beta must be finite, >= 0");
@@ -273,10 +280,31 @@ int per_sample(per_t* h, int64_t B, const float* d_u, double beta, int64_t* d_id
   hipError_t e = per::launch_sample(h->t, h->g, h->st, plan, (uint32_t)h->size, B, d_u, beta,
                                     d_idx_out, d_w_out, any_rows ? d_states_out : nullptr,
                                     d_next_states_out, d_actions_out, d_rewards_out,
-                                    d_dones_out, h->top_stale, stream);
-  if (e != hipSuccess) return hip_fail(e, "per_sample");
+                                    d_dones_out, (uint32_t)out_stride, dones_f32, h->top_stale,
+                                    stream);
+  if (e != hipSuccess) return hip_fail(e, what);
   h->top_stale = false;
   return ok();
+}
+
+}  // namespace
+
+int per_sample(per_t* h, int64_t B, const float* d_u, double beta, int64_t* d_idx_out,
+               float* d_w_out, float* d_states_out, float* d_next_states_out,
+               uint32_t* d_actions_out, float* d_rewards_out, uint8_t* d_dones_out,
+               hipStream_t stream) {
+  return sample_impl(h, B, d_u, beta, d_idx_out, d_w_out, d_states_out, d_next_states_out,
+                     h ? h->st.D : 0, d_actions_out, d_rewards_out, d_dones_out, false, stream,
+                     "per_sample");
+}
+
+int per_sample_padded(per_t* h, int64_t B, const float* d_u, double beta, int64_t* d_idx_out,
+                      float* d_w_out, float* d_states_out, float* d_next_states_out,
+                      int64_t out_stride, int32_t* d_actions_out, float* d_rewards_out,
+                      float* d_dones_out, hipStream_t stream) {
+  return sample_impl(h, B, d_u, beta, d_idx_out, d_w_out, d_states_out, d_next_states_out,
+                     out_stride, reinterpret_cast<uint32_t*>(d_actions_out), d_rewards_out,
+                     d_dones_out, true, stream, "per_sample_padded");
 }
 
 static int copy_scalar(per_t* h, const void* src, float* d_out, hipStream_t stream,

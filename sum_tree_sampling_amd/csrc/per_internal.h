@@ -109,7 +109,8 @@ hipError_t launch_sample(const TreePtrs& t, const Geom& g, const Storage& st,
                          const SamplePlan& plan, uint32_t size, int64_t B, const float* u,
                          double beta, int64_t* idx_out, float* w_out, float* states_out,
                          float* next_out, uint32_t* actions_out, float* rewards_out,
-                         uint8_t* dones_out, bool write_top, hipStream_t s);
+                         void* dones_out, uint32_t out_stride, bool dones_f32,
+                         bool write_top, hipStream_t s);
 
 SamplePlan make_sample_plan(const Geom& g, int64_t B);
 

@@ -28,6 +28,7 @@
 // Implementation Plan", Task 3).
 
 #include <cstdlib>
+#include <type_traits>
 
 #include "per_internal.h"
 
@@ -52,7 +53,9 @@ struct SampleArgs {
   float* next_out;
   uint32_t* actions_out;
   float* rewards_out;
-  uint8_t* dones_out;
+  void* dones_out;      // u8 [B], or f32 [B] when dones_f32
+  uint32_t out_stride;  // floats per output state row, >= D; columns D.. are 0
+  int dones_f32;
   Storage st;
   int P;          // partitions = 2^P; the top P levels are rebuilt in LDS
   int top_mode;   // kTopNone / kTopRebuild / kTopWhole
@@ -113,6 +116,61 @@ __device__ __forceinline__ void load_values(const float* p, float* x) {
 }
 
 constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v / 2); }
+
+// Wave-cooperative row copy of a wave's SPW samples (sample s's slot in lane
+// s*G), in batches of kBatch accesses per lane: every load of a batch is
+// issued before the first store, so each lane keeps kBatch reads in flight
+// (16 bytes each when VEC).  An output row has W >= D floats; its columns
+// D .. W-1 are stored as 0 ("True Single-Graph Implementation Plan", Task 2:
+// padded rows).  A padding column re-reads the row's first column (the same
+// line, so the load stays unconditional and in its batch); the zero is
+// selected at the store, after the batch's loads.
+// kBatch (1, 2, 4 or 8) is chosen from the wave's access count so that a
+// wave copying a few short rows issues no idle loads.
+template <bool VEC, int SPW, int G, int kBatch>
+__device__ __forceinline__ void copy_rows(const SampleArgs& a, uint32_t wave_b0, uint32_t slot,
+                                          int lane, uint32_t D, uint32_t W) {
+  constexpr uint32_t kW = VEC ? 4u : 1u;      // floats per access
+  const uint32_t per_src = D / kW;            // loads per row
+  const uint32_t per_row = W / kW;            // stores per row
+  const uint32_t total = SPW * 2u * per_row;
+  using T = typename std::conditional<VEC, float4, float>::type;
+  // The four row pointers as values: a per-lane choice between two fields of
+  // the argument block would otherwise become a per-lane load of a pointer
+  // (and a wait) in front of every row access.
+  const float* const src_s = a.st.states;
+  const float* const src_n = a.st.next_states;
+  float* const dst_s = a.states_out;
+  float* const dst_n = a.next_out;
+  for (uint32_t t0 = 0; t0 < total; t0 += 64 * kBatch) {
+    T buf[kBatch];
+    T* dst[kBatch];
+    bool ok[kBatch], pad[kBatch];
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) {
+      const uint32_t t = t0 + q * 64 + lane;
+      uint32_t s = t / (2u * per_row);
+      if (s >= SPW) s = SPW - 1;
+      const uint32_t slot_s = (uint32_t)__shfl((int)slot, (int)s * G);
+      const uint32_t bs = wave_b0 + s;
+      ok[q] = t < total && bs < a.B;
+      const uint32_t rem = t - s * 2u * per_row;
+      const bool nxt = rem >= per_row;
+      const uint32_t c = nxt ? rem - per_row : rem;
+      pad[q] = c >= per_src;
+      const float* src = (nxt ? src_n : src_s) + (uint64_t)slot_s * D;
+      dst[q] = reinterpret_cast<T*>((nxt ? dst_n : dst_s) + (uint64_t)bs * W) + c;
+      // Unconditional: s is clamped to a sample of the wave (a descent of an
+      // inactive lane still ends on a leaf) and past-the-end or padding
+      // accesses read column 0, so the address is always in the row store.
+      buf[q] = reinterpret_cast<const T*>(src)[(pad[q] || !ok[q]) ? 0u : c];
+    }
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) {
+      if (ok[q]) *dst[q] = pad[q] ? T{} : buf[q];
+    }
+  }
+}
 
 template <int G, int V>
 __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleArgs a) {
@@ -345,58 +403,32 @@ __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleArgs a) {
   }
 
   if (a.states_out) {
-    // Wave-cooperative row copy of the wave's SPW samples, in batches of
-    // kBatch accesses per lane: every load of a batch is issued before the
-    // first store, so each lane keeps kBatch 16-byte reads in flight.
-    constexpr int kBatch = 8;
-    const uint32_t D = (uint32_t)a.st.D;
-    const bool vec = (D & 3u) == 0u;
-    const uint32_t per_row = vec ? D / 4 : D;  // accesses per row
-    const uint32_t total = SPW * 2u * per_row;
-    const uint32_t wave_b0 = wave * SPW;
-    for (uint32_t t0 = 0; t0 < total; t0 += 64 * kBatch) {
-      float4 buf[kBatch];
-      float* dst[kBatch];
-      bool ok[kBatch];
-#pragma unroll
-      for (int q = 0; q < kBatch; ++q) {
-        const uint32_t t = t0 + q * 64 + lane;
-        uint32_t s = t / (2u * per_row);
-        if (s >= SPW) s = SPW - 1;
-        const uint32_t slot_s = (uint32_t)__shfl((int)slot, (int)s * G);
-        const uint32_t bs = wave_b0 + s;
-        ok[q] = t < total && bs < a.B;
-        const uint32_t rem = t - s * 2u * per_row;
-        const bool nxt = rem >= per_row;
-        const uint32_t c = nxt ? rem - per_row : rem;
-        const float* src = (nxt ? a.st.next_states : a.st.states) + (uint64_t)slot_s * D;
-        dst[q] = (nxt ? a.next_out : a.states_out) + (uint64_t)bs * D;
-        buf[q] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        if (ok[q]) {
-          if (vec) {
-            buf[q] = *reinterpret_cast<const float4*>(src + 4u * c);
-            dst[q] += 4u * c;
-          } else {
-            buf[q].x = src[c];
-            dst[q] += c;
-          }
-        }
-      }
-#pragma unroll
-      for (int q = 0; q < kBatch; ++q) {
-        if (ok[q]) {
-          if (vec)
-            *reinterpret_cast<float4*>(dst[q]) = buf[q];
-          else
-            *dst[q] = buf[q].x;
-        }
-      }
+    const uint32_t D = (uint32_t)a.st.D, W = a.out_stride;
+    const bool vec = ((D | W) & 3u) == 0u;
+    const uint32_t per_lane = (SPW * 2u * (vec ? W / 4 : W) + 63u) / 64u;  // accesses per lane
+    if (vec) {
+      if (per_lane <= 1)
+        copy_rows<true, SPW, G, 1>(a, wave * SPW, slot, lane, D, W);
+      else if (per_lane <= 2)
+        copy_rows<true, SPW, G, 2>(a, wave * SPW, slot, lane, D, W);
+      else if (per_lane <= 4)
+        copy_rows<true, SPW, G, 4>(a, wave * SPW, slot, lane, D, W);
+      else
+        copy_rows<true, SPW, G, 8>(a, wave * SPW, slot, lane, D, W);
+    } else {
+      if (per_lane <= 2)
+        copy_rows<false, SPW, G, 2>(a, wave * SPW, slot, lane, D, W);
+      else
+        copy_rows<false, SPW, G, 8>(a, wave * SPW, slot, lane, D, W);
     }
   }
   if (lead && a.states_out) {
-    a.actions_out[b] = act;
+    a.actions_out[b] = act;  // the stored bits, read as u32 or i32 by the caller
     a.rewards_out[b] = rew;
-    a.dones_out[b] = done;
+    if (a.dones_f32)
+      static_cast<float*>(a.dones_out)[b] = (float)done;
+    else
+      static_cast<uint8_t*>(a.dones_out)[b] = done;
   }
 }
 
@@ -453,7 +485,8 @@ hipError_t launch_sample(const TreePtrs& t, const Geom& g, const Storage& st,
                          const SamplePlan& plan, uint32_t size, int64_t B, const float* u,
                          double beta, int64_t* idx_out, float* w_out, float* states_out,
                          float* next_out, uint32_t* actions_out, float* rewards_out,
-                         uint8_t* dones_out, bool write_top, hipStream_t s) {
+                         void* dones_out, uint32_t out_stride, bool dones_f32,
+                         bool write_top, hipStream_t s) {
   SampleArgs a{};
   a.sum = t.sum;
   a.mn = t.mn;
@@ -469,6 +502,8 @@ hipError_t launch_sample(const TreePtrs& t, const Geom& g, const Storage& st,
   a.actions_out = actions_out;
   a.rewards_out = rewards_out;
   a.dones_out = dones_out;
+  a.out_stride = out_stride;
+  a.dones_f32 = dones_f32 ? 1 : 0;
   a.st = st;
   a.P = g.P;
   a.top_mode = plan.top_mode;

@@ -45,6 +45,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
         "per_add": (c_int, [vp, i64, vp, vp, vp, vp, vp, vp, vp]),
         "per_update": (c_int, [vp, i64, vp, vp, vp]),
         "per_sample": (c_int, [vp, i64, vp, f64, vp, vp, vp, vp, vp, vp, vp, vp]),
+        "per_sample_padded": (c_int, [vp, i64, vp, f64, vp, vp, vp, vp, i64, vp, vp, vp, vp]),
         "per_flush": (c_int, [vp, vp]),
         "per_total": (c_int, [vp, vp, vp]),
         "per_min": (c_int, [vp, vp, vp]),
@@ -131,6 +132,15 @@ def per_sample(h, B, u, beta, idx_out, w_out=None, states_out=None, next_states_
     _check(load().per_sample(h, int(B), _p(u), float(beta), _p(idx_out), _p(w_out),
                              _p(states_out), _p(next_states_out), _p(actions_out),
                              _p(rewards_out), _p(dones_out), _stream(stream)))
+
+
+def per_sample_padded(h, B, u, beta, idx_out, w_out=None, states_out=None, next_states_out=None,
+                      out_stride=0, actions_out=None, rewards_out=None, dones_out=None,
+                      stream=None) -> None:
+    _check(load().per_sample_padded(h, int(B), _p(u), float(beta), _p(idx_out), _p(w_out),
+                                    _p(states_out), _p(next_states_out), int(out_stride),
+                                    _p(actions_out), _p(rewards_out), _p(dones_out),
+                                    _stream(stream)))
 
 
 def per_flush(h, stream=None) -> None:
@@ -259,6 +269,27 @@ class PerBuffer:
         per_sample(self.h, B, u, beta, out["idx"], out.get("w"), out.get("states"),
                    out.get("next_states"), out.get("actions"), out.get("rewards"),
                    out.get("dones"), stream)
+        return out
+
+    def sample_padded(self, u, out_stride, beta=0.4, weights=True, out=None, stream=None):
+        """per_sample_padded: state rows [B, out_stride] zero past state_dim,
+        actions i32, rewards f32, dones f32 (the trainer's input layout)."""
+        B = u.numel()
+        if out is None:
+            out = {"idx": torch.empty(B, dtype=torch.int64, device=self.device)}
+            if weights:
+                out["w"] = torch.empty(B, dtype=torch.float32, device=self.device)
+            if self.state_dim > 0:
+                out.update(
+                    states=torch.empty((B, out_stride), dtype=torch.float32, device=self.device),
+                    next_states=torch.empty((B, out_stride), dtype=torch.float32,
+                                            device=self.device),
+                    actions=torch.empty(B, dtype=torch.int32, device=self.device),
+                    rewards=torch.empty(B, dtype=torch.float32, device=self.device),
+                    dones=torch.empty(B, dtype=torch.float32, device=self.device))
+        per_sample_padded(self.h, B, u, beta, out["idx"], out.get("w"), out.get("states"),
+                          out.get("next_states"), out_stride, out.get("actions"),
+                          out.get("rewards"), out.get("dones"), stream)
         return out
 
     def scalar(self, which: str, stream=None) -> torch.Tensor:

@@ -446,7 +446,47 @@ def pin_k_priority_decimal(lib):
     o.close()
 
 
+def pin_l_padded_gather(lib):
+    """P-l: the direct-to-trainer gather ("True Single-Graph Implementation
+    Plan", Tasks 2 and 3) writes each stored state row into the first D
+    columns of a destination row of out_stride floats and exactly +0.0 after
+    them, actions as the stored 32 bits read as i32, rewards as stored and
+    dones as the stored byte's value in f32; its indices are those of the
+    plain sample for the same masses.  out_stride < D is refused."""
+    n, D = 1024, 8
+    r = workloads.rows("tiny_1k", 0, n)
+    pr = workloads.initial_priorities("tiny_1k")
+    acts = r["actions"].copy()
+    acts[::97] = np.uint32(0xFFFFFFF0)  # high bit set: must come back as the same bits
+    dones = r["dones"].copy()
+    dones[::131] = 7  # a byte other than 0 / 1 keeps its value
+    o = Oracle(n, D, lib=lib)
+    o.add(n, r["states"], r["next_states"], acts, r["rewards"], dones, prio=pr)
+    u = np.random.default_rng(21).random(500, dtype=np.float32)
+    plain = o.sample(u, rows=False)
+    for stride in (8, 9, 12, 37):
+        res = o.sample_padded(u, stride)
+        i = res["idx"]
+        assert np.array_equal(i, plain["idx"])
+        assert np.array_equal(res["w"].view(np.uint32), plain["w"].view(np.uint32))
+        for key, src in (("states", r["states"]), ("next_states", r["next_states"])):
+            out = res[key]
+            assert out.shape == (500, stride)
+            assert np.array_equal(out[:, :D].view(np.uint32), src[i].view(np.uint32)), key
+            assert np.all(out[:, D:].view(np.uint32) == 0), key
+        assert np.array_equal(res["actions"].view(np.uint32), acts[i])
+        assert np.array_equal(res["rewards"].view(np.uint32), r["rewards"][i].view(np.uint32))
+        assert np.array_equal(res["dones"], dones[i].astype(np.float32))
+    try:
+        o.sample_padded(u, D - 1)
+    except ValueError:
+        pass
+    else:
+        raise AssertionError("out_stride < state_dim accepted")
+    o.close()
+
+
 ALL_PINS = [pin_golden_hand_tree, pin_a_invariant, pin_b_root_bound, pin_c_update_equivalence,
             pin_d_dyadic_exact, pin_e_uniform_closed_form, pin_f_brute_force_band,
             pin_g_chi_square, pin_h_is_weights, pin_i_gather, pin_j_intake,
-            pin_k_priority_decimal]
+            pin_k_priority_decimal, pin_l_padded_gather]

@@ -49,6 +49,13 @@ MUTANTS = [
     ("given_prio_not_raising_max", "if (p > t->maxp) t->maxp = p;\n        } else {",
      "} else {"),
     ("negative_zero_kept", "p = prio[j] + 0.0f;", "p = prio[j];"),
+    ("pad_not_zero", "(c < D) ? t->states[slot * D + c] : 0.0f;",
+     "(c < D) ? t->states[slot * D + c] : t->states[slot * D];"),
+    ("pad_stride_ignored", "next_states_out[b * out_stride + c] =",
+     "next_states_out[b * D + c] ="),
+    ("dones_as_bool", "dones_out[b] = (float)t->dones[slot];",
+     "dones_out[b] = t->dones[slot] ? 1.0f : 0.0f;"),
+    ("pad_accepts_short_stride", "if (out_stride < D) return -1;", "if (out_stride < 0) return -1;"),
 ]
 
 _RUNNER = r"""

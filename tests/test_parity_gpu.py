@@ -189,6 +189,45 @@ def test_ring_intake_and_random_ops(n):
         compare_trees(o, g, "ring n=%d step %d update" % (n, step))
 
 
+@pytest.mark.parametrize("n,D,strides", [(1 << 10, 8, (8, 9, 12, 37)), (1 << 10, 5, (5, 8, 13)),
+                                          (1 << 20, 64, (72,))])
+def test_padded_gather(n, D, strides):
+    """per_sample_padded against the oracle: indices and rows bit for bit, the
+    padding columns +0.0 (outputs start as NaN), actions as the stored bits,
+    dones as f32, weights within 1e-6."""
+    say("padded", n, D, strides)
+    rng = np.random.default_rng(D)
+    o = Oracle(n, D)
+    g = _buf(n, D, max_batch=2048)
+    st = rng.standard_normal((n, D)).astype(np.float32)
+    nx = rng.standard_normal((n, D)).astype(np.float32)
+    ac = rng.integers(0, 3, n).astype(np.uint32)
+    ac[::97] = np.uint32(0xFFFFFFF0)
+    rw = rng.standard_normal(n).astype(np.float32)
+    dn = (rng.random(n) < 0.1).astype(np.uint8)
+    dn[::131] = 7
+    p0 = rng.random(n).astype(np.float32)
+    o.add(n, st, nx, ac, rw, dn, prio=p0)
+    g.add(n, dev(st), dev(nx), dev(ac), dev(rw), dev(dn), prio=dev(p0))
+    for stride in strides:
+        for B in (1, 333, 2048):
+            u = rng.random(B, dtype=np.float32)
+            ro = o.sample_padded(u, stride, beta=0.4)
+            out = {"idx": dev(np.full(B, -1, np.int64)),
+                   "w": dev(np.full(B, np.nan, np.float32)),
+                   "states": dev(np.full((B, stride), np.nan, np.float32)),
+                   "next_states": dev(np.full((B, stride), np.nan, np.float32)),
+                   "actions": dev(np.full(B, -1, np.int32)),
+                   "rewards": dev(np.full(B, np.nan, np.float32)),
+                   "dones": dev(np.full(B, np.nan, np.float32))}
+            rg = g.sample_padded(dev(u), stride, beta=0.4, out=out)
+            what = "padded n=%d D=%d stride=%d B=%d" % (n, D, stride, B)
+            assert_bits_equal(host(rg["idx"]), ro["idx"], what + " idx")
+            compare_weights(host(rg["w"]), ro["w"], what + " w")
+            for key in ("states", "next_states", "actions", "rewards", "dones"):
+                assert_bits_equal(host(rg[key]), ro[key], what + " " + key)
+
+
 def test_intake_at_extreme_running_max():
     """Intake at the running max after that max was driven to 3e38: the
     interior subtrees of each run overflow to +inf, which the pairwise adds
