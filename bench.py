@@ -204,8 +204,13 @@ def algorithmic_bytes(spec: dict) -> dict:
     sample = B * (4 + 8 * L + 8)                     # mass in, L sibling pairs, index out
     if spec["weights"]:
         sample += B * 4
-    if D > 0:
+    W = spec.get("out_stride") or D
+    if D > 0 and W == D:
         sample += B * 2 * (2 * 4 * D + 9)            # rows + scalars, read and written
+    elif D > 0:
+        # padded trainer layout: rows read at D, written at W floats; action,
+        # reward and done read as 4 + 4 + 1 bytes, written as 4 + 4 + 4
+        sample += B * (2 * (4 * D + 4 * W) + 9 + 12)
     update = B * 12 + U * 8 + 16 * expected_dirty_internal(n, U)
     c = spec["intake"]
     intake = 0.0
@@ -251,6 +256,9 @@ def main():
     ap.add_argument("--workload", default="apex_shard_2m", choices=list(workloads.WORKLOADS))
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--padded", type=int, default=0, metavar="STRIDE",
+                    help="sample with per_sample_padded into rows of STRIDE floats "
+                         "(the trainer layout; workloads with rows only)")
     ap.add_argument("--graph-steps", type=int, default=64,
                     help="whole steps captured as one HIP graph for the labelled replay "
                          "figure (even; 0 skips it)")
@@ -275,6 +283,10 @@ def main():
 
     spec = workloads.spec(args.workload)
     n, B, D = spec["capacity"], spec["batch"], spec["state_dim"]
+    if args.padded:
+        if D == 0 or args.padded < D:
+            raise SystemExit("--padded needs a workload with rows and STRIDE >= state_dim")
+        spec = dict(spec, out_stride=args.padded)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
@@ -309,7 +321,14 @@ def main():
     out = {"idx": torch.empty(B, dtype=torch.int64, device=dev)}
     if spec["weights"]:
         out["w"] = torch.empty(B, dtype=torch.float32, device=dev)
-    if rows:
+    W = spec.get("out_stride")
+    if W:
+        out.update(states=torch.empty((B, W), dtype=torch.float32, device=dev),
+                   next_states=torch.empty((B, W), dtype=torch.float32, device=dev),
+                   actions=torch.empty(B, dtype=torch.int32, device=dev),
+                   rewards=torch.empty(B, dtype=torch.float32, device=dev),
+                   dones=torch.empty(B, dtype=torch.float32, device=dev))
+    elif rows:
         out.update(states=torch.empty((B, D), dtype=torch.float32, device=dev),
                    next_states=torch.empty((B, D), dtype=torch.float32, device=dev),
                    actions=torch.empty(B, dtype=torch.int32, device=dev),
@@ -317,8 +336,14 @@ def main():
                    dones=torch.empty(B, dtype=torch.uint8, device=dev))
     intake = spec["intake"]
 
+    def do_sample(u, o):
+        if W:
+            g.sample_padded(u, W, beta=spec["beta"], out=o)
+        else:
+            g.sample(u, beta=spec["beta"], weights=spec["weights"], out=o)
+
     def step(s):
-        g.sample(u_d[s], beta=spec["beta"], weights=spec["weights"], out=out)
+        do_sample(u_d[s], out)
         g.update(idx_d[s] if idx_d is not None else out["idx"], td_d[s])
         if intake:
             g.add(intake)
@@ -346,8 +371,7 @@ def main():
     base = args.warmup + args.steps
     idx_hist = torch.empty((args.steps, B), dtype=torch.int64, device=dev)
     ops = {
-        "sample": lambda s: g.sample(u_d[base + s], beta=spec["beta"], weights=spec["weights"],
-                                     out=dict(out, idx=idx_hist[s])),
+        "sample": lambda s: do_sample(u_d[base + s], dict(out, idx=idx_hist[s])),
         "update": lambda s: g.update(idx_d[base + s] if idx_d is not None else idx_hist[s],
                                      td_d[base + s]),
     }
@@ -370,7 +394,7 @@ def main():
     for s in range(args.steps):
         e = evs[s]
         e[0].record(stream)
-        g.sample(u_d[base + s], beta=spec["beta"], weights=spec["weights"], out=out)
+        do_sample(u_d[base + s], out)
         e[1].record(stream)
         g.update(idx_d[base + s] if idx_d is not None else out["idx"], td_d[base + s])
         e[2].record(stream)
@@ -411,7 +435,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "capacity": n, "batch": B, "state_dim": D,
                    "intake": intake, "unique_updates": spec.get("unique", B),
-                   "weights": spec["weights"], "parallelism": "single GPU"},
+                   "weights": spec["weights"], "parallelism": "single GPU",
+                   "out_stride": W or D},
         "samples_per_s": B / (op_avg["sample"] * 1e-3),
         "updates_per_s": B / (op_avg["update"] * 1e-3),
         "op_ms_avg": op_avg,
