@@ -148,6 +148,34 @@ int per_sample(per_t* h, int64_t B, const float* d_u, double beta, int64_t* d_id
                hipStream_t stream);
 
 /*
+ * per_sample with the masses drawn on the device ("GPU-Resident Prioritized
+ * Experience Replay", section "Sampling Kernels": the uniform values come
+ * from a generator on the GPU, not from the host).  The generator is
+ * Philox4x64-10 (Salmon, Moraes, Dror and Shaw, "Parallel Random Numbers:
+ * As Easy as 1, 2, 3", SC 2011); word j of the stream of a seed is word
+ * j % 4 of the block at counter (j / 4, 0, 0, 0) under key (seed, 0).
+ * Sample b uses u_b = (word(offset + b) >> 40) * 2^-24, i.e. a 24-bit
+ * uniform in [0, 1); everything else is per_sample with d_u = those u_b.
+ * The caller advances offset (by B per call for fresh masses).
+ */
+int per_sample_philox(per_t* h, int64_t B, uint64_t seed, uint64_t offset, double beta,
+                      int64_t* d_idx_out, float* d_w_out, float* d_states_out,
+                      float* d_next_states_out, uint32_t* d_actions_out, float* d_rewards_out,
+                      uint8_t* d_dones_out, hipStream_t stream);
+
+/*
+ * Uniform sample over the filled slots, for prioritisation switched off
+ * ("GPU-Resident Prioritized Experience Replay", section "Experience
+ * Insertion": the same ring sampled uniformly from generated indices into
+ * [0, size)).  Slot b = ((word(offset + b) >> 32) * size) >> 32 with the
+ * stream of per_sample_philox; no weights (all equal).  Row outputs and
+ * errors as per_sample.
+ */
+int per_sample_uniform(per_t* h, int64_t B, uint64_t seed, uint64_t offset, int64_t* d_idx_out,
+                       float* d_states_out, float* d_next_states_out, uint32_t* d_actions_out,
+                       float* d_rewards_out, uint8_t* d_dones_out, hipStream_t stream);
+
+/*
  * per_sample written straight into a trainer's input buffers ("True
  * Single-Graph Implementation Plan", Task 2: rows gathered into a padded
  * destination, scalars gathered as f32 / i32; Task 3: the sampler writes the

@@ -50,6 +50,14 @@ def _bind(path: str):
     lib.pero_sample.restype = ctypes.c_int
     lib.pero_sample.argtypes = [vp, i64, vp, f64, vp, vp, vp, vp, vp, vp, vp]
     lib.pero_sample_padded.restype = ctypes.c_int
+    lib.pero_stream_word.restype = ctypes.c_uint64
+    lib.pero_stream_word.argtypes = [ctypes.c_uint64, ctypes.c_uint64]
+    lib.pero_sample_philox.restype = ctypes.c_int
+    lib.pero_sample_philox.argtypes = [vp, i64, ctypes.c_uint64, ctypes.c_uint64, f64, vp, vp, vp,
+                                       vp, vp, vp, vp]
+    lib.pero_sample_uniform.restype = ctypes.c_int
+    lib.pero_sample_uniform.argtypes = [vp, i64, ctypes.c_uint64, ctypes.c_uint64, vp, vp, vp,
+                                        vp, vp, vp]
     lib.pero_sample_padded.argtypes = [vp, i64, vp, f64, vp, vp, vp, vp, i64, vp, vp, vp]
     for name in ("pero_total", "pero_min", "pero_max_priority"):
         getattr(lib, name).restype = f32
@@ -147,6 +155,53 @@ class Oracle:
             res.update(states=outs[0], next_states=outs[1], actions=outs[2],
                        rewards=outs[3], dones=outs[4])
         return res
+
+    def stream_word(self, seed, j):
+        """Word j of the Philox4x64-10 stream of a seed."""
+        return int(self._lib.pero_stream_word(int(seed) & (2**64 - 1), int(j) & (2**64 - 1)))
+
+    def _rows(self, B, rows):
+        D = self.state_dim
+        if rows and D > 0:
+            return [np.empty((B, D), np.float32), np.empty((B, D), np.float32),
+                    np.empty(B, np.uint32), np.empty(B, np.float32), np.empty(B, np.uint8)]
+        return [None] * 5
+
+    def _result(self, idx, w, outs, rows):
+        res = {"idx": idx}
+        if w is not None:
+            res["w"] = w
+        if rows and self.state_dim > 0:
+            res.update(states=outs[0], next_states=outs[1], actions=outs[2],
+                       rewards=outs[3], dones=outs[4])
+        return res
+
+    def sample_philox(self, B, seed, offset, beta=0.4, weights=True, rows=False):
+        """pero_sample_philox: masses from words offset .. offset+B-1 of the stream."""
+        idx = np.empty(B, np.int64)
+        w = np.empty(B, np.float32) if weights else None
+        outs = self._rows(B, rows)
+        rc = self._lib.pero_sample_philox(self._h, B, int(seed) & (2**64 - 1),
+                                          int(offset) & (2**64 - 1), float(beta), _ptr(idx),
+                                          _ptr(w), *[_ptr(o) for o in outs])
+        if rc == -3:
+            raise RuntimeError("sample from an empty buffer")
+        if rc != 0:
+            raise ValueError("pero_sample_philox failed rc=%d" % rc)
+        return self._result(idx, w, outs, rows)
+
+    def sample_uniform(self, B, seed, offset, rows=False):
+        """pero_sample_uniform: slots uniform over [0, size) from the stream."""
+        idx = np.empty(B, np.int64)
+        outs = self._rows(B, rows)
+        rc = self._lib.pero_sample_uniform(self._h, B, int(seed) & (2**64 - 1),
+                                           int(offset) & (2**64 - 1), _ptr(idx),
+                                           *[_ptr(o) for o in outs])
+        if rc == -3:
+            raise RuntimeError("sample from an empty buffer")
+        if rc != 0:
+            raise ValueError("pero_sample_uniform failed rc=%d" % rc)
+        return self._result(idx, None, outs, rows)
 
     def sample_padded(self, u, out_stride, beta=0.4, weights=True, rows=True):
         """pero_sample_padded: rows [B, out_stride] f32 zero past state_dim,

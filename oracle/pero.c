@@ -244,6 +244,92 @@ int pero_sample_padded(const pero_t* t, int64_t B, const float* u, double beta, 
     return 0;
 }
 
+/* Philox4x64-10 (Salmon, Moraes, Dror and Shaw, "Parallel Random Numbers:
+ * As Easy as 1, 2, 3", SC 2011): ten rounds over a 4 x 64-bit counter with
+ * a 2 x 64-bit key; a round multiplies counter words 0 and 2 by the two
+ * round constants into 128-bit products and mixes their halves with words
+ * 1 and 3 and the key; the key gains the two Weyl constants between rounds. */
+void pero_philox4x64(const uint64_t ctr_in[4], const uint64_t key_in[2], uint64_t out[4]) {
+    uint64_t c0 = ctr_in[0], c1 = ctr_in[1], c2 = ctr_in[2], c3 = ctr_in[3];
+    uint64_t k0 = key_in[0], k1 = key_in[1];
+    for (int r = 0; r < 10; ++r) {
+        if (r > 0) {
+            k0 += 0x9E3779B97F4A7C15ull;
+            k1 += 0xBB67AE8584CAA73Bull;
+        }
+        unsigned __int128 p0 = (unsigned __int128)0xD2E7470EE14C6C93ull * c0;
+        unsigned __int128 p1 = (unsigned __int128)0xCA5A826395121157ull * c2;
+        uint64_t n0 = (uint64_t)(p1 >> 64) ^ c1 ^ k0;
+        uint64_t n1 = (uint64_t)p1;
+        uint64_t n2 = (uint64_t)(p0 >> 64) ^ c3 ^ k1;
+        uint64_t n3 = (uint64_t)p0;
+        c0 = n0;
+        c1 = n1;
+        c2 = n2;
+        c3 = n3;
+    }
+    out[0] = c0;
+    out[1] = c1;
+    out[2] = c2;
+    out[3] = c3;
+}
+
+/* Word j of the stream of a seed: word j % 4 of the block at counter
+ * (j / 4, 0, 0, 0) under key (seed, 0). */
+uint64_t pero_stream_word(uint64_t seed, uint64_t j) {
+    const uint64_t ctr[4] = {j / 4, 0, 0, 0};
+    const uint64_t key[2] = {seed, 0};
+    uint64_t out[4];
+    pero_philox4x64(ctr, key, out);
+    return out[j % 4];
+}
+
+/* Proportional sample with the masses drawn on the device side of the
+ * method ("GPU-Resident Prioritized Experience Replay", section "Sampling
+ * Kernels": the uniform values come from a generator, not from the host):
+ * sample b uses u_b = (word(offset + b) >> 40) * 2^-24, then pero_sample. */
+int pero_sample_philox(const pero_t* t, int64_t B, uint64_t seed, uint64_t offset, double beta,
+                       int64_t* idx_out, float* w_out, float* states_out,
+                       float* next_states_out, uint32_t* actions_out, float* rewards_out,
+                       uint8_t* dones_out) {
+    if (B < 0) return -1;
+    if (B == 0) return 0;
+    float* u = (float*)malloc(sizeof(float) * (size_t)B);
+    if (!u) return -1;
+    for (int64_t b = 0; b < B; ++b)
+        u[b] = (float)(pero_stream_word(seed, offset + (uint64_t)b) >> 40) * 0x1p-24f;
+    int rc = pero_sample(t, B, u, beta, idx_out, w_out, states_out, next_states_out,
+                         actions_out, rewards_out, dones_out);
+    free(u);
+    return rc;
+}
+
+/* Uniform sample over the filled slots (the same section: without
+ * prioritisation the ring is sampled uniformly from generated indices into
+ * [0, size)): idx_b = ((word(offset + b) >> 32) * size) >> 32, rows as in
+ * pero_sample. */
+int pero_sample_uniform(const pero_t* t, int64_t B, uint64_t seed, uint64_t offset,
+                        int64_t* idx_out, float* states_out, float* next_states_out,
+                        uint32_t* actions_out, float* rewards_out, uint8_t* dones_out) {
+    if (B < 0) return -1;
+    if (B == 0) return 0;
+    if (t->size == 0) return -3;
+    const int64_t D = t->D;
+    for (int64_t b = 0; b < B; ++b) {
+        const uint64_t hi = pero_stream_word(seed, offset + (uint64_t)b) >> 32;
+        const int64_t slot = (int64_t)((hi * (uint64_t)t->size) >> 32);
+        idx_out[b] = slot;
+        if (D > 0 && states_out) {
+            memcpy(states_out + b * D, t->states + slot * D, sizeof(float) * D);
+            memcpy(next_states_out + b * D, t->next_states + slot * D, sizeof(float) * D);
+            actions_out[b] = t->actions[slot];
+            rewards_out[b] = t->rewards[slot];
+            dones_out[b] = t->dones[slot];
+        }
+    }
+    return 0;
+}
+
 float pero_total(const pero_t* t) { return t->sum[1]; }
 float pero_min(const pero_t* t) { return t->mn[1]; }
 float pero_max_priority(const pero_t* t) { return t->maxp; }

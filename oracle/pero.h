@@ -71,6 +71,23 @@ int pero_sample(const pero_t* t, int64_t B, const float* u, double beta, int64_t
                 float* w_out, float* states_out, float* next_states_out,
                 uint32_t* actions_out, float* rewards_out, uint8_t* dones_out);
 
+/* Philox4x64-10 block, and word j of a seed's stream (word j % 4 of the
+ * block at counter (j / 4, 0, 0, 0) under key (seed, 0)). */
+void pero_philox4x64(const uint64_t ctr_in[4], const uint64_t key_in[2], uint64_t out[4]);
+uint64_t pero_stream_word(uint64_t seed, uint64_t j);
+
+/* pero_sample with u_b = (word(offset + b) >> 40) * 2^-24. */
+int pero_sample_philox(const pero_t* t, int64_t B, uint64_t seed, uint64_t offset, double beta,
+                       int64_t* idx_out, float* w_out, float* states_out,
+                       float* next_states_out, uint32_t* actions_out, float* rewards_out,
+                       uint8_t* dones_out);
+
+/* Uniform sample: idx_b = ((word(offset + b) >> 32) * size) >> 32; rows as
+ * pero_sample.  -3 if size == 0. */
+int pero_sample_uniform(const pero_t* t, int64_t B, uint64_t seed, uint64_t offset,
+                        int64_t* idx_out, float* states_out, float* next_states_out,
+                        uint32_t* actions_out, float* rewards_out, uint8_t* dones_out);
+
 /* pero_sample written into padded trainer buffers: state rows of out_stride
  * >= D floats, zero past column D; actions i32 (stored bits), rewards f32,
  * dones f32.  -1 if out_stride < D. */

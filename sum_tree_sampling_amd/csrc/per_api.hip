@@ -245,12 +245,16 @@ int per_update(per_t* h, int64_t B, const int64_t* d_idx, const float* d_td,
 
 namespace {
 
-// Shared by per_sample and per_sample_padded: out_stride floats per output
-// state row (>= state_dim), dones as u8 or as f32.
-int sample_impl(per_t* h, int64_t B, const float* d_u, double beta, int64_t* d_idx_out,
-                float* d_w_out, float* d_states_out, float* d_next_states_out,
-                int64_t out_stride, uint32_t* d_actions_out, float* d_rewards_out,
-                void* d_dones_out, bool dones_f32, hipStream_t stream, const char* what) {
+enum SampleKind { kGivenMasses, kStreamMasses, kUniform };
+
+// Shared by the sample entry points: masses given (d_u), drawn from the
+// generator stream (seed, offset), or a uniform sample from the stream;
+// out_stride floats per output state row (>= state_dim), dones as u8 or f32.
+int sample_impl(per_t* h, int64_t B, SampleKind kind, const float* d_u, uint64_t seed,
+                uint64_t offset, double beta, int64_t* d_idx_out, float* d_w_out,
+                float* d_states_out, float* d_next_states_out, int64_t out_stride,
+                uint32_t* d_actions_out, float* d_rewards_out, void* d_dones_out, bool dones_f32,
+                hipStream_t stream, const char* what) {
   if (!h) return fail(PER_EINVAL, "handle is NULL");
   if (B < 0 || B > h->max_batch)
     return fail(PER_EINVAL, "B %lld outside [0, max_batch=%lld]", (long long)B,
@@ -259,7 +263,8 @@ int sample_impl(per_t* h, int64_t B, const float* d_u, double beta, int64_t* d_i
     return fail(PER_EINVAL, "out_stride %lld outside [state_dim=%d, %lld]", (long long)out_stride,
                 (int)h->st.D, (long long)PER_MAX_OUT_STRIDE);
   if (B == 0) return ok();
-  if (!d_u || !d_idx_out) return fail(PER_EINVAL, "u and idx_out are required");
+  if (!d_idx_out) return fail(PER_EINVAL, "idx_out is required");
+  if (kind == kGivenMasses && !d_u) return fail(PER_EINVAL, "u is required");
   if (!(beta >= 0.0) || !(beta < 1e300)) return fail(PER_EINVAL, "beta must be finite, >= 0");
   const bool any_rows = d_states_out || d_next_states_out || d_actions_out || d_rewards_out ||
                         d_dones_out;
@@ -271,13 +276,21 @@ int sample_impl(per_t* h, int64_t B, const float* d_u, double beta, int64_t* d_i
                     reinterpret_cast<uintptr_t>(d_next_states_out)) & 15u))
     return fail(PER_EINVAL, "state outputs must be 16-byte aligned");
   if (h->size == 0) return fail(PER_EEMPTY, "sample from an empty buffer");
+  if (kind == kUniform) {
+    hipError_t e = per::launch_uniform(h->st, (uint32_t)h->size, B, seed, offset, d_idx_out,
+                                       any_rows ? d_states_out : nullptr, d_next_states_out,
+                                       d_actions_out, d_rewards_out, d_dones_out,
+                                       (uint32_t)out_stride, dones_f32, stream);
+    return e == hipSuccess ? ok() : hip_fail(e, what);
+  }
   const per::SamplePlan plan = per::make_sample_plan(h->g, B);
   if (h->top_stale && plan.top_mode != per::kTopRebuild) {  // the sampler will not rebuild the top itself
     hipError_t e = per::launch_top(h->t, h->g, stream);
     if (e != hipSuccess) return hip_fail(e, "per_sample: top rebuild");
     h->top_stale = false;
   }
-  hipError_t e = per::launch_sample(h->t, h->g, h->st, plan, (uint32_t)h->size, B, d_u, beta,
+  hipError_t e = per::launch_sample(h->t, h->g, h->st, plan, (uint32_t)h->size, B,
+                                    kind == kGivenMasses ? d_u : nullptr, seed, offset, beta,
                                     d_idx_out, d_w_out, any_rows ? d_states_out : nullptr,
                                     d_next_states_out, d_actions_out, d_rewards_out,
                                     d_dones_out, (uint32_t)out_stride, dones_f32, h->top_stale,
@@ -293,18 +306,35 @@ int per_sample(per_t* h, int64_t B, const float* d_u, double beta, int64_t* d_id
                float* d_w_out, float* d_states_out, float* d_next_states_out,
                uint32_t* d_actions_out, float* d_rewards_out, uint8_t* d_dones_out,
                hipStream_t stream) {
-  return sample_impl(h, B, d_u, beta, d_idx_out, d_w_out, d_states_out, d_next_states_out,
-                     h ? h->st.D : 0, d_actions_out, d_rewards_out, d_dones_out, false, stream,
-                     "per_sample");
+  return sample_impl(h, B, kGivenMasses, d_u, 0, 0, beta, d_idx_out, d_w_out, d_states_out,
+                     d_next_states_out, h ? h->st.D : 0, d_actions_out, d_rewards_out,
+                     d_dones_out, false, stream, "per_sample");
+}
+
+int per_sample_philox(per_t* h, int64_t B, uint64_t seed, uint64_t offset, double beta,
+                      int64_t* d_idx_out, float* d_w_out, float* d_states_out,
+                      float* d_next_states_out, uint32_t* d_actions_out, float* d_rewards_out,
+                      uint8_t* d_dones_out, hipStream_t stream) {
+  return sample_impl(h, B, kStreamMasses, nullptr, seed, offset, beta, d_idx_out, d_w_out,
+                     d_states_out, d_next_states_out, h ? h->st.D : 0, d_actions_out,
+                     d_rewards_out, d_dones_out, false, stream, "per_sample_philox");
+}
+
+int per_sample_uniform(per_t* h, int64_t B, uint64_t seed, uint64_t offset, int64_t* d_idx_out,
+                       float* d_states_out, float* d_next_states_out, uint32_t* d_actions_out,
+                       float* d_rewards_out, uint8_t* d_dones_out, hipStream_t stream) {
+  return sample_impl(h, B, kUniform, nullptr, seed, offset, 0.0, d_idx_out, nullptr, d_states_out,
+                     d_next_states_out, h ? h->st.D : 0, d_actions_out, d_rewards_out,
+                     d_dones_out, false, stream, "per_sample_uniform");
 }
 
 int per_sample_padded(per_t* h, int64_t B, const float* d_u, double beta, int64_t* d_idx_out,
                       float* d_w_out, float* d_states_out, float* d_next_states_out,
                       int64_t out_stride, int32_t* d_actions_out, float* d_rewards_out,
                       float* d_dones_out, hipStream_t stream) {
-  return sample_impl(h, B, d_u, beta, d_idx_out, d_w_out, d_states_out, d_next_states_out,
-                     out_stride, reinterpret_cast<uint32_t*>(d_actions_out), d_rewards_out,
-                     d_dones_out, true, stream, "per_sample_padded");
+  return sample_impl(h, B, kGivenMasses, d_u, 0, 0, beta, d_idx_out, d_w_out, d_states_out,
+                     d_next_states_out, out_stride, reinterpret_cast<uint32_t*>(d_actions_out),
+                     d_rewards_out, d_dones_out, true, stream, "per_sample_padded");
 }
 
 static int copy_scalar(per_t* h, const void* src, float* d_out, hipStream_t stream,

@@ -107,11 +107,18 @@ hipError_t launch_add(const TreePtrs& t, const Geom& g, const Storage& st, uint3
 
 hipError_t launch_sample(const TreePtrs& t, const Geom& g, const Storage& st,
                          const SamplePlan& plan, uint32_t size, int64_t B, const float* u,
-                         double beta, int64_t* idx_out, float* w_out, float* states_out,
+                         uint64_t seed, uint64_t offset, double beta, int64_t* idx_out,
+                         float* w_out, float* states_out,
                          float* next_out, uint32_t* actions_out, float* rewards_out,
                          void* dones_out, uint32_t out_stride, bool dones_f32,
                          bool write_top, hipStream_t s);
 
 SamplePlan make_sample_plan(const Geom& g, int64_t B);
+
+// Uniform sample of B slots over [0, size) from the generator stream.
+hipError_t launch_uniform(const Storage& st, uint32_t size, int64_t B, uint64_t seed,
+                          uint64_t offset, int64_t* idx_out, float* states_out, float* next_out,
+                          uint32_t* actions_out, float* rewards_out, void* dones_out,
+                          uint32_t out_stride, bool dones_f32, hipStream_t s);
 
 }  // namespace per

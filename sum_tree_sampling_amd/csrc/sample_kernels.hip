@@ -45,7 +45,9 @@ struct SampleArgs {
   uint32_t n;
   uint32_t size;
   uint32_t B;
-  const float* u;
+  const float* u;       // masses, or NULL: from the generator stream
+  uint64_t seed;        // generator key (seed, 0)
+  uint64_t offset;      // stream word of sample 0
   double beta;
   int64_t* idx_out;
   float* w_out;
@@ -172,7 +174,99 @@ __device__ __forceinline__ void copy_rows(const SampleArgs& a, uint32_t wave_b0,
   }
 }
 
-template <int G, int V>
+// Philox4x64-10 (Salmon, Moraes, Dror and Shaw, "Parallel Random Numbers: As
+// Easy as 1, 2, 3", SC 2011): ten rounds over a 4 x 64-bit counter and a
+// 2 x 64-bit key; a round takes the 128-bit products of counter words 0 and
+// 2 with the two round multipliers and mixes their halves with words 1 and 3
+// and the key, which gains the two Weyl increments between rounds.  Word j of
+// a seed's stream is word j % 4 of the block at counter (j / 4, 0, 0, 0)
+// under key (seed, 0).
+__device__ __forceinline__ uint64_t stream_word(uint64_t seed, uint64_t j) {
+  uint64_t c0 = j >> 2, c1 = 0, c2 = 0, c3 = 0;
+  uint64_t k0 = seed, k1 = 0;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) {
+      k0 += 0x9E3779B97F4A7C15ull;
+      k1 += 0xBB67AE8584CAA73Bull;
+    }
+    const uint64_t m0 = 0xD2E7470EE14C6C93ull, m1 = 0xCA5A826395121157ull;
+    const uint64_t hi0 = __umul64hi(m0, c0), lo0 = m0 * c0;
+    const uint64_t hi1 = __umul64hi(m1, c2), lo1 = m1 * c2;
+    const uint64_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    c0 = n0;
+    c1 = lo1;
+    c2 = n2;
+    c3 = lo0;
+  }
+  const uint32_t w = (uint32_t)(j & 3u);
+  return w == 0 ? c0 : (w == 1 ? c1 : (w == 2 ? c2 : c3));
+}
+
+// The mass uniform of a stream word: its top 24 bits times 2^-24, in [0, 1).
+__device__ __forceinline__ float stream_uniform(uint64_t w) {
+  return (float)(uint32_t)(w >> 40) * 0x1p-24f;
+}
+
+// Outputs of one sample (lead: the lane of its group that writes them): the
+// index, the IS weight and, cooperatively over the wave, the row copy.
+template <int G, int SPW>
+__device__ __forceinline__ void emit(const SampleArgs& a, uint32_t wave, int lane, uint32_t b,
+                                     bool lead, uint32_t slot, float leaf, float pmin) {
+  // The scalar fields of the sampled transition: loaded now, stored after
+  // the rows, so that their trip to memory overlaps the row copy.
+  uint32_t act = 0u;
+  float rew = 0.0f;
+  uint8_t done = 0;
+  if (lead && a.states_out) {
+    act = a.st.actions[slot];
+    rew = a.st.rewards[slot];
+    done = a.st.dones[slot];
+  }
+  if (lead) {
+    a.idx_out[b] = (int64_t)slot;
+    if (a.w_out) {
+      // (N P_i)^-beta / (N P_min)^-beta = (p_i / p_min)^-beta: one pow, f64.
+      // With p_min > 0 every stored priority, the sampled one included, is
+      // > 0; with p_min = 0 the normaliser is infinite and w = 0.
+      float w = 0.0f;
+      if (pmin > 0.0f) w = (float)pow((double)leaf / (double)pmin, -a.beta);
+      a.w_out[b] = w;
+    }
+  }
+
+  if (a.states_out) {
+    const uint32_t D = (uint32_t)a.st.D, W = a.out_stride;
+    const bool vec = ((D | W) & 3u) == 0u;
+    const uint32_t per_lane = (SPW * 2u * (vec ? W / 4 : W) + 63u) / 64u;  // accesses per lane
+    if (vec) {
+      if (per_lane <= 1)
+        copy_rows<true, SPW, G, 1>(a, wave * SPW, slot, lane, D, W);
+      else if (per_lane <= 2)
+        copy_rows<true, SPW, G, 2>(a, wave * SPW, slot, lane, D, W);
+      else if (per_lane <= 4)
+        copy_rows<true, SPW, G, 4>(a, wave * SPW, slot, lane, D, W);
+      else
+        copy_rows<true, SPW, G, 8>(a, wave * SPW, slot, lane, D, W);
+    } else {
+      if (per_lane <= 2)
+        copy_rows<false, SPW, G, 2>(a, wave * SPW, slot, lane, D, W);
+      else
+        copy_rows<false, SPW, G, 8>(a, wave * SPW, slot, lane, D, W);
+    }
+  }
+  if (lead && a.states_out) {
+    a.actions_out[b] = act;  // the stored bits, read as u32 or i32 by the caller
+    a.rewards_out[b] = rew;
+    if (a.dones_f32)
+      static_cast<float*>(a.dones_out)[b] = (float)done;
+    else
+      static_cast<uint8_t*>(a.dones_out)[b] = done;
+  }
+}
+
+// STREAM: masses from the generator stream instead of a.u.
+template <int G, int V, bool STREAM>
 __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleArgs a) {
   extern __shared__ float top[];  // nodes [0, 2^(K+1)) of the sum tree
   constexpr int LOGG = ilog2(G);
@@ -316,7 +410,9 @@ __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleArgs a) {
     pmin = a.mn[1];
   }
 
-  float m = active ? a.u[b] * T : 0.0f;
+  float ub = 0.0f;
+  if (active) ub = STREAM ? stream_uniform(stream_word(a.seed, a.offset + b)) : a.u[b];
+  float m = ub * T;
   if (!(m < T)) m = __uint_as_float(__float_as_uint(T) - 1u);  // largest f32 below T
 
   uint32_t node = 1;
@@ -378,58 +474,22 @@ __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleArgs a) {
     leaf = lv;
   }
 
-  const uint32_t slot = node - a.n;
-  const bool lead = active && j == 0;
-  // The scalar fields of the sampled transition: loaded now, stored after
-  // the rows, so that their trip to memory overlaps the row copy.
-  uint32_t act = 0u;
-  float rew = 0.0f;
-  uint8_t done = 0;
-  if (lead && a.states_out) {
-    act = a.st.actions[slot];
-    rew = a.st.rewards[slot];
-    done = a.st.dones[slot];
-  }
-  if (lead) {
-    a.idx_out[b] = (int64_t)slot;
-    if (a.w_out) {
-      // (N P_i)^-beta / (N P_min)^-beta = (p_i / p_min)^-beta: one pow, f64.
-      // With p_min > 0 every stored priority, the sampled one included, is
-      // > 0; with p_min = 0 the normaliser is infinite and w = 0.
-      float w = 0.0f;
-      if (pmin > 0.0f) w = (float)pow((double)leaf / (double)pmin, -a.beta);
-      a.w_out[b] = w;
-    }
-  }
+  emit<G, SPW>(a, wave, lane, b, active && j == 0, node - a.n, leaf, pmin);
+}
 
-  if (a.states_out) {
-    const uint32_t D = (uint32_t)a.st.D, W = a.out_stride;
-    const bool vec = ((D | W) & 3u) == 0u;
-    const uint32_t per_lane = (SPW * 2u * (vec ? W / 4 : W) + 63u) / 64u;  // accesses per lane
-    if (vec) {
-      if (per_lane <= 1)
-        copy_rows<true, SPW, G, 1>(a, wave * SPW, slot, lane, D, W);
-      else if (per_lane <= 2)
-        copy_rows<true, SPW, G, 2>(a, wave * SPW, slot, lane, D, W);
-      else if (per_lane <= 4)
-        copy_rows<true, SPW, G, 4>(a, wave * SPW, slot, lane, D, W);
-      else
-        copy_rows<true, SPW, G, 8>(a, wave * SPW, slot, lane, D, W);
-    } else {
-      if (per_lane <= 2)
-        copy_rows<false, SPW, G, 2>(a, wave * SPW, slot, lane, D, W);
-      else
-        copy_rows<false, SPW, G, 8>(a, wave * SPW, slot, lane, D, W);
-    }
-  }
-  if (lead && a.states_out) {
-    a.actions_out[b] = act;  // the stored bits, read as u32 or i32 by the caller
-    a.rewards_out[b] = rew;
-    if (a.dones_f32)
-      static_cast<float*>(a.dones_out)[b] = (float)done;
-    else
-      static_cast<uint8_t*>(a.dones_out)[b] = done;
-  }
+// Uniform sample over the filled slots ("GPU-Resident Prioritized
+// Experience Replay", section "Experience Insertion": without
+// prioritisation the same ring is sampled uniformly from generated indices
+// into [0, size)): one lane per sample, slot = ((word >> 32) * size) >> 32,
+// then the rows.  Lanes past B still land on a filled slot, which the wave's
+// row copy relies on.
+__global__ void __launch_bounds__(kSampleThreads) uniform_kernel(SampleArgs a) {
+  const int lane = threadIdx.x & 63;
+  const uint32_t wave = blockIdx.x * (kSampleThreads / 64) + (threadIdx.x >> 6);
+  const uint32_t b = wave * 64 + (uint32_t)lane;
+  const uint64_t hi = stream_word(a.seed, a.offset + b) >> 32;
+  const uint32_t slot = (uint32_t)((hi * (uint64_t)a.size) >> 32);
+  emit<1, 64>(a, wave, lane, b, b < a.B, slot, 0.0f, 0.0f);
 }
 
 template <int G, int V>
@@ -440,7 +500,10 @@ hipError_t launch_variant(const SampleArgs& a, hipStream_t s) {
   size_t lds = 0;
   if (a.top_mode == kTopRebuild) lds = 2 * (sizeof(float) << (a.P + 1));
   if (a.top_mode == kTopWhole) lds = sizeof(float) << (a.top + 1);
-  hipLaunchKernelGGL((sample_kernel<G, V>), dim3(grid), dim3(kSampleThreads), lds, s, a);
+  if (a.u)
+    hipLaunchKernelGGL((sample_kernel<G, V, false>), dim3(grid), dim3(kSampleThreads), lds, s, a);
+  else
+    hipLaunchKernelGGL((sample_kernel<G, V, true>), dim3(grid), dim3(kSampleThreads), lds, s, a);
   return hipGetLastError();
 }
 
@@ -483,7 +546,8 @@ SamplePlan make_sample_plan(const Geom& g, int64_t B) {
 
 hipError_t launch_sample(const TreePtrs& t, const Geom& g, const Storage& st,
                          const SamplePlan& plan, uint32_t size, int64_t B, const float* u,
-                         double beta, int64_t* idx_out, float* w_out, float* states_out,
+                         uint64_t seed, uint64_t offset, double beta, int64_t* idx_out,
+                         float* w_out, float* states_out,
                          float* next_out, uint32_t* actions_out, float* rewards_out,
                          void* dones_out, uint32_t out_stride, bool dones_f32,
                          bool write_top, hipStream_t s) {
@@ -494,6 +558,8 @@ hipError_t launch_sample(const TreePtrs& t, const Geom& g, const Storage& st,
   a.size = size;
   a.B = (uint32_t)B;
   a.u = u;
+  a.seed = seed;
+  a.offset = offset;
   a.beta = beta;
   a.idx_out = idx_out;
   a.w_out = w_out;
@@ -519,6 +585,30 @@ hipError_t launch_sample(const TreePtrs& t, const Geom& g, const Storage& st,
     default:
       return launch_variant<64, 4>(a, s);
   }
+}
+
+hipError_t launch_uniform(const Storage& st, uint32_t size, int64_t B, uint64_t seed,
+                          uint64_t offset, int64_t* idx_out, float* states_out, float* next_out,
+                          uint32_t* actions_out, float* rewards_out, void* dones_out,
+                          uint32_t out_stride, bool dones_f32, hipStream_t s) {
+  SampleArgs a{};
+  a.size = size;
+  a.B = (uint32_t)B;
+  a.seed = seed;
+  a.offset = offset;
+  a.idx_out = idx_out;
+  a.states_out = states_out;
+  a.next_out = next_out;
+  a.actions_out = actions_out;
+  a.rewards_out = rewards_out;
+  a.dones_out = dones_out;
+  a.out_stride = out_stride;
+  a.dones_f32 = dones_f32 ? 1 : 0;
+  a.st = st;
+  const uint64_t waves = ((uint64_t)B + 63) / 64;
+  hipLaunchKernelGGL(uniform_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(kSampleThreads), 0,
+                     s, a);
+  return hipGetLastError();
 }
 
 }  // namespace per

@@ -26,6 +26,8 @@ class PerError(RuntimeError):
         self.code = code
 
 
+_U64 = (1 << 64) - 1
+
 def load(path: str | None = None) -> ctypes.CDLL:
     """Load libper.so (raises if it is missing: build it with build.build())."""
     global _lib
@@ -36,6 +38,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
         raise ImportError("libper.so not built at %s; run sum_tree_sampling_amd.build.build()" % p)
     lib = ctypes.CDLL(p)
     i64, i32, f64, vp, sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_double, ctypes.c_void_p, ctypes.c_size_t
+    u64 = ctypes.c_uint64
     c_int = ctypes.c_int
     sig = {
         "per_workspace_bytes": (c_int, [i64, i64, ctypes.POINTER(sz)]),
@@ -46,6 +49,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
         "per_update": (c_int, [vp, i64, vp, vp, vp]),
         "per_sample": (c_int, [vp, i64, vp, f64, vp, vp, vp, vp, vp, vp, vp, vp]),
         "per_sample_padded": (c_int, [vp, i64, vp, f64, vp, vp, vp, vp, i64, vp, vp, vp, vp]),
+        "per_sample_philox": (c_int, [vp, i64, u64, u64, f64, vp, vp, vp, vp, vp, vp, vp, vp]),
+        "per_sample_uniform": (c_int, [vp, i64, u64, u64, vp, vp, vp, vp, vp, vp, vp]),
         "per_flush": (c_int, [vp, vp]),
         "per_total": (c_int, [vp, vp, vp]),
         "per_min": (c_int, [vp, vp, vp]),
@@ -141,6 +146,23 @@ def per_sample_padded(h, B, u, beta, idx_out, w_out=None, states_out=None, next_
                                     _p(states_out), _p(next_states_out), int(out_stride),
                                     _p(actions_out), _p(rewards_out), _p(dones_out),
                                     _stream(stream)))
+
+
+def per_sample_philox(h, B, seed, offset, beta, idx_out, w_out=None, states_out=None,
+                      next_states_out=None, actions_out=None, rewards_out=None, dones_out=None,
+                      stream=None) -> None:
+    _check(load().per_sample_philox(h, int(B), int(seed) & _U64, int(offset) & _U64, float(beta),
+                                    _p(idx_out), _p(w_out), _p(states_out), _p(next_states_out),
+                                    _p(actions_out), _p(rewards_out), _p(dones_out),
+                                    _stream(stream)))
+
+
+def per_sample_uniform(h, B, seed, offset, idx_out, states_out=None, next_states_out=None,
+                       actions_out=None, rewards_out=None, dones_out=None, stream=None) -> None:
+    _check(load().per_sample_uniform(h, int(B), int(seed) & _U64, int(offset) & _U64,
+                                     _p(idx_out), _p(states_out), _p(next_states_out),
+                                     _p(actions_out), _p(rewards_out), _p(dones_out),
+                                     _stream(stream)))
 
 
 def per_flush(h, stream=None) -> None:
@@ -269,6 +291,37 @@ class PerBuffer:
         per_sample(self.h, B, u, beta, out["idx"], out.get("w"), out.get("states"),
                    out.get("next_states"), out.get("actions"), out.get("rewards"),
                    out.get("dones"), stream)
+        return out
+
+    def _outs(self, B, weights, rows):
+        out = {"idx": torch.empty(B, dtype=torch.int64, device=self.device)}
+        if weights:
+            out["w"] = torch.empty(B, dtype=torch.float32, device=self.device)
+        if rows:
+            D = self.state_dim
+            out.update(
+                states=torch.empty((B, D), dtype=torch.float32, device=self.device),
+                next_states=torch.empty((B, D), dtype=torch.float32, device=self.device),
+                actions=torch.empty(B, dtype=torch.int32, device=self.device),
+                rewards=torch.empty(B, dtype=torch.float32, device=self.device),
+                dones=torch.empty(B, dtype=torch.uint8, device=self.device))
+        return out
+
+    def sample_philox(self, B, seed, offset, beta=0.4, weights=True, rows=False, out=None,
+                      stream=None):
+        """per_sample_philox: masses from stream words offset .. offset+B-1."""
+        out = out or self._outs(B, weights, rows)
+        per_sample_philox(self.h, B, seed, offset, beta, out["idx"], out.get("w"),
+                          out.get("states"), out.get("next_states"), out.get("actions"),
+                          out.get("rewards"), out.get("dones"), stream)
+        return out
+
+    def sample_uniform(self, B, seed, offset, rows=False, out=None, stream=None):
+        """per_sample_uniform: B slots uniform over [0, size) from the stream."""
+        out = out or self._outs(B, False, rows)
+        per_sample_uniform(self.h, B, seed, offset, out["idx"], out.get("states"),
+                           out.get("next_states"), out.get("actions"), out.get("rewards"),
+                           out.get("dones"), stream)
         return out
 
     def sample_padded(self, u, out_stride, beta=0.4, weights=True, out=None, stream=None):

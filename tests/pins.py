@@ -486,7 +486,59 @@ def pin_l_padded_gather(lib):
     o.close()
 
 
+def _numpy_stream(seed, j0, count):
+    """Words j0 .. j0+count-1 of a seed's stream from numpy's own Philox4x64-10
+    (numpy increments its 256-bit counter before each block, so a counter one
+    below block j0 // 4 makes its first block that one)."""
+    M = 2**64 - 1
+    blk = j0 // 4
+    ctr = [M, M, M, M] if blk == 0 else [blk - 1, 0, 0, 0]
+    g = np.random.Philox(key=np.array([seed, 0], np.uint64), counter=np.array(ctr, np.uint64))
+    words = g.random_raw(count + j0 % 4 + 4)
+    return [int(x) for x in words[j0 % 4:j0 % 4 + count]]
+
+
+def pin_m_device_masses(lib):
+    """P-m: the device-side generator ("GPU-Resident Prioritized Experience
+    Replay", section "Sampling Kernels": masses and uniform indices come from
+    a generator on the GPU) is Philox4x64-10 (Salmon et al., SC 2011): its
+    words equal numpy's independent Philox4x64-10 implementation; the
+    sample with generated masses equals the plain sample given the same
+    masses; uniform indices are the multiply-shift of the word's high half
+    into [0, size) and pass a chi-square test."""
+    o = Oracle(1024, 8, lib=lib)
+    for seed, j0 in ((0, 0), (1, 5), (12345, 1 << 20), (2**64 - 1, 3), (77, (1 << 40) + 2)):
+        ref = _numpy_stream(seed, j0, 11)
+        got = [o.stream_word(seed, j0 + k) for k in range(11)]
+        assert got == ref, (seed, j0)
+    r = workloads.rows("tiny_1k", 0, 1024)
+    pr = workloads.initial_priorities("tiny_1k")
+    o.add(1024, r["states"], r["next_states"], r["actions"], r["rewards"], r["dones"], prio=pr)
+    seed, off, B = 99, 4097, 777
+    words = _numpy_stream(seed, off, B)
+    u = np.array([(x >> 40) * 2.0**-24 for x in words], np.float32)
+    assert np.all(u >= 0) and np.all(u < 1)
+    a = o.sample(u, beta=0.4, rows=True)
+    b = o.sample_philox(B, seed, off, beta=0.4, rows=True)
+    for key in ("idx", "w", "states", "next_states", "actions", "rewards", "dones"):
+        assert np.array_equal(a[key].view(np.uint8), b[key].view(np.uint8)), key
+    o.close()
+    # uniform indices over a size that is not a power of two
+    o = Oracle(1024, lib=lib)
+    o.add(1000)
+    B = 1 << 18
+    res = o.sample_uniform(B, 5, 0)["idx"]
+    ref = [((x >> 32) * 1000) >> 32 for x in _numpy_stream(5, 0, 64)]
+    assert res[:64].tolist() == ref
+    assert res.min() >= 0 and res.max() < 1000
+    counts = np.bincount(res, minlength=1000)
+    chi2 = float(((counts - B / 1000) ** 2 / (B / 1000)).sum())
+    import scipy.stats
+    assert scipy.stats.chi2.sf(chi2, 999) > 1e-3, chi2
+    o.close()
+
+
 ALL_PINS = [pin_golden_hand_tree, pin_a_invariant, pin_b_root_bound, pin_c_update_equivalence,
             pin_d_dyadic_exact, pin_e_uniform_closed_form, pin_f_brute_force_band,
             pin_g_chi_square, pin_h_is_weights, pin_i_gather, pin_j_intake,
-            pin_k_priority_decimal, pin_l_padded_gather]
+            pin_k_priority_decimal, pin_l_padded_gather, pin_m_device_masses]

@@ -56,6 +56,12 @@ MUTANTS = [
     ("dones_as_bool", "dones_out[b] = (float)t->dones[slot];",
      "dones_out[b] = t->dones[slot] ? 1.0f : 0.0f;"),
     ("pad_accepts_short_stride", "if (out_stride < D) return -1;", "if (out_stride < 0) return -1;"),
+    ("philox_round_constant", "0xD2E7470EE14C6C93ull", "0xD2E7470EE14C6C95ull"),
+    ("philox_no_key_bump", "            k1 += 0xBB67AE8584CAA73Bull;\n", ""),
+    ("philox_nine_rounds", "for (int r = 0; r < 10; ++r)", "for (int r = 0; r < 9; ++r)"),
+    ("stream_word_order", "return out[j % 4];", "return out[3 - j % 4];"),
+    ("mass_wrong_bits", ">> 40) * 0x1p-24f", ">> 41) * 0x1p-24f"),
+    ("uniform_modulo", "(int64_t)((hi * (uint64_t)t->size) >> 32)", "(int64_t)(hi % (uint64_t)t->size)"),
 ]
 
 _RUNNER = r"""

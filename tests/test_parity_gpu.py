@@ -228,6 +228,55 @@ def test_padded_gather(n, D, strides):
                 assert_bits_equal(host(rg[key]), ro[key], what + " " + key)
 
 
+@pytest.mark.parametrize("B", [1, 333, 20000])
+def test_device_masses(B):
+    """per_sample_philox against the oracle (masses from Philox4x64-10 words
+    offset .. offset+B-1 on both sides): indices and rows bit for bit,
+    weights within 1e-6; B = 20000 takes the one-lane-per-sample sampler."""
+    say("philox masses", B)
+    n, D = 1 << 12, 8
+    rng = np.random.default_rng(B)
+    o = Oracle(n, D)
+    g = _buf(n, D, max_batch=32768)
+    st = rng.standard_normal((n, D)).astype(np.float32)
+    nx = rng.standard_normal((n, D)).astype(np.float32)
+    ac = rng.integers(0, 3, n).astype(np.uint32)
+    rw = rng.standard_normal(n).astype(np.float32)
+    dn = (rng.random(n) < 0.1).astype(np.uint8)
+    p0 = (rng.random(n) ** 0.6).astype(np.float32)
+    o.add(n, st, nx, ac, rw, dn, prio=p0)
+    g.add(n, dev(st), dev(nx), dev(ac), dev(rw), dev(dn), prio=dev(p0))
+    for seed, off in ((0, 0), (7, 3), (2**63 + 5, 1 << 33), (2**64 - 1, 2**64 - 4 * B - 2)):
+        ro = o.sample_philox(B, seed, off, beta=0.4, rows=True)
+        rg = g.sample_philox(B, seed, off, beta=0.4, rows=True)
+        compare_sample(rg, ro, "philox B=%d seed=%d off=%d" % (B, seed, off), rows=True)
+
+
+@pytest.mark.parametrize("size,B", [(1, 5), (1000, 333), (4096, 70000), (3 << 11, 64)])
+def test_uniform_sample(size, B):
+    """per_sample_uniform against the oracle: slots ((word >> 32) * size) >> 32
+    and their rows, bit for bit, over partly filled rings."""
+    say("uniform", size, B)
+    n, D = 1 << 13, 5
+    rng = np.random.default_rng(size)
+    o = Oracle(n, D)
+    g = _buf(n, D, max_batch=1 << 17)
+    st = rng.standard_normal((size, D)).astype(np.float32)
+    nx = rng.standard_normal((size, D)).astype(np.float32)
+    ac = rng.integers(0, 3, size).astype(np.uint32)
+    rw = rng.standard_normal(size).astype(np.float32)
+    dn = (rng.random(size) < 0.1).astype(np.uint8)
+    o.add(size, st, nx, ac, rw, dn)
+    g.add(size, dev(st), dev(nx), dev(ac), dev(rw), dev(dn))
+    for seed, off in ((3, 0), (2**64 - 1, 12345)):
+        ro = o.sample_uniform(B, seed, off, rows=True)
+        rg = g.sample_uniform(B, seed, off, rows=True)
+        what = "uniform size=%d B=%d seed=%d" % (size, B, seed)
+        assert_bits_equal(host(rg["idx"]), ro["idx"], what + " idx")
+        for key in ("states", "next_states", "actions", "rewards", "dones"):
+            assert_bits_equal(host(rg[key]), ro[key], what + " " + key)
+
+
 def test_intake_at_extreme_running_max():
     """Intake at the running max after that max was driven to 3e38: the
     interior subtrees of each run overflow to +inf, which the pairwise adds
