@@ -202,7 +202,11 @@ def algorithmic_bytes(spec: dict) -> dict:
     L = int(math.log2(n))
     U = spec.get("unique", B)
     sample = B * (4 + 8 * L + 8)                     # mass in, L sibling pairs, index out
-    if spec["weights"]:
+    if spec.get("masses") == "philox":
+        sample -= B * 4                              # masses made on the device
+    if spec.get("uniform"):
+        sample = B * 8                               # index out; no tree walk, no weight
+    elif spec["weights"]:
         sample += B * 4
     W = spec.get("out_stride") or D
     if D > 0 and W == D:
@@ -211,7 +215,7 @@ def algorithmic_bytes(spec: dict) -> dict:
         # padded trainer layout: rows read at D, written at W floats; action,
         # reward and done read as 4 + 4 + 1 bytes, written as 4 + 4 + 4
         sample += B * (2 * (4 * D + 4 * W) + 9 + 12)
-    update = B * 12 + U * 8 + 16 * expected_dirty_internal(n, U)
+    update = 0.0 if spec.get("uniform") else B * 12 + U * 8 + 16 * expected_dirty_internal(n, U)
     c = spec["intake"]
     intake = 0.0
     if c:
@@ -259,6 +263,11 @@ def main():
     ap.add_argument("--padded", type=int, default=0, metavar="STRIDE",
                     help="sample with per_sample_padded into rows of STRIDE floats "
                          "(the trainer layout; workloads with rows only)")
+    ap.add_argument("--masses", choices=["array", "philox"], default="array",
+                    help="sample masses from a pre-uploaded array (default) or drawn on "
+                         "the device (per_sample_philox)")
+    ap.add_argument("--uniform", action="store_true",
+                    help="prioritisation off: per_sample_uniform, no priority update")
     ap.add_argument("--graph-steps", type=int, default=64,
                     help="whole steps captured as one HIP graph for the labelled replay "
                          "figure (even; 0 skips it)")
@@ -286,7 +295,10 @@ def main():
     if args.padded:
         if D == 0 or args.padded < D:
             raise SystemExit("--padded needs a workload with rows and STRIDE >= state_dim")
+        if args.uniform or args.masses != "array":
+            raise SystemExit("--padded goes with array masses and proportional sampling")
         spec = dict(spec, out_stride=args.padded)
+    spec = dict(spec, masses=args.masses, uniform=args.uniform)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
@@ -336,15 +348,27 @@ def main():
                    dones=torch.empty(B, dtype=torch.uint8, device=dev))
     intake = spec["intake"]
 
-    def do_sample(u, o):
-        if W:
-            g.sample_padded(u, W, beta=spec["beta"], out=o)
+    seed = 0x5EED
+    if args.uniform:
+        out.pop("w", None)
+
+    def do_sample(s, o):
+        if args.uniform:
+            g.sample_uniform(B, seed, s * B, out=o)
+        elif args.masses == "philox":
+            g.sample_philox(B, seed, s * B, beta=spec["beta"], out=o)
+        elif W:
+            g.sample_padded(u_d[s], W, beta=spec["beta"], out=o)
         else:
-            g.sample(u, beta=spec["beta"], weights=spec["weights"], out=o)
+            g.sample(u_d[s], beta=spec["beta"], weights=spec["weights"], out=o)
+
+    def do_update(s, idx):
+        if not args.uniform:
+            g.update(idx, td_d[s])
 
     def step(s):
-        do_sample(u_d[s], out)
-        g.update(idx_d[s] if idx_d is not None else out["idx"], td_d[s])
+        do_sample(s, out)
+        do_update(s, idx_d[s] if idx_d is not None else out["idx"])
         if intake:
             g.add(intake)
 
@@ -371,10 +395,11 @@ def main():
     base = args.warmup + args.steps
     idx_hist = torch.empty((args.steps, B), dtype=torch.int64, device=dev)
     ops = {
-        "sample": lambda s: do_sample(u_d[base + s], dict(out, idx=idx_hist[s])),
-        "update": lambda s: g.update(idx_d[base + s] if idx_d is not None else idx_hist[s],
-                                     td_d[base + s]),
+        "sample": lambda s: do_sample(base + s, dict(out, idx=idx_hist[s])),
     }
+    if not args.uniform:
+        ops["update"] = lambda s: g.update(idx_d[base + s] if idx_d is not None else idx_hist[s],
+                                           td_d[base + s])
     if intake:
         ops["add"] = lambda s: g.add(intake)
     op_avg = {}
@@ -394,9 +419,9 @@ def main():
     for s in range(args.steps):
         e = evs[s]
         e[0].record(stream)
-        do_sample(u_d[base + s], out)
+        do_sample(base + s, out)
         e[1].record(stream)
-        g.update(idx_d[base + s] if idx_d is not None else out["idx"], td_d[base + s])
+        do_update(base + s, idx_d[base + s] if idx_d is not None else out["idx"])
         e[2].record(stream)
         if intake:
             g.add(intake)
@@ -404,7 +429,7 @@ def main():
     torch.cuda.synchronize()
     spread = {}
     for k, name in enumerate(["sample", "update", "add"]):
-        if name == "add" and not intake:
+        if (name == "add" and not intake) or (name == "update" and args.uniform):
             continue
         t = np.array([e[k].elapsed_time(e[k + 1]) for e in evs])
         spread[name] = {q: float(np.percentile(t, v)) for q, v in (("p10", 10), ("p50", 50), ("p90", 90))}
@@ -436,9 +461,10 @@ def main():
         "config": {"workload": args.workload, "capacity": n, "batch": B, "state_dim": D,
                    "intake": intake, "unique_updates": spec.get("unique", B),
                    "weights": spec["weights"], "parallelism": "single GPU",
-                   "out_stride": W or D},
+                   "out_stride": W or D, "masses": args.masses,
+                   "sampling": "uniform" if args.uniform else "proportional"},
         "samples_per_s": B / (op_avg["sample"] * 1e-3),
-        "updates_per_s": B / (op_avg["update"] * 1e-3),
+        "updates_per_s": B / (op_avg["update"] * 1e-3) if "update" in op_avg else None,
         "op_ms_avg": op_avg,
         "op_ms_bracketed": spread,
         "graph_replay": graph,

@@ -480,16 +480,19 @@ __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleArgs a) {
 // Uniform sample over the filled slots ("GPU-Resident Prioritized
 // Experience Replay", section "Experience Insertion": without
 // prioritisation the same ring is sampled uniformly from generated indices
-// into [0, size)): one lane per sample, slot = ((word >> 32) * size) >> 32,
-// then the rows.  Lanes past B still land on a filled slot, which the wave's
-// row copy relies on.
+// into [0, size)): G lanes per sample (as the proportional sampler: 16 for
+// small batches, so that they spread over more of the chip, else 1), slot =
+// ((word >> 32) * size) >> 32, then the rows.  Lanes past B still land on a
+// filled slot, which the wave's row copy relies on.
+template <int G>
 __global__ void __launch_bounds__(kSampleThreads) uniform_kernel(SampleArgs a) {
+  constexpr int SPW = 64 / G;
   const int lane = threadIdx.x & 63;
   const uint32_t wave = blockIdx.x * (kSampleThreads / 64) + (threadIdx.x >> 6);
-  const uint32_t b = wave * 64 + (uint32_t)lane;
+  const uint32_t b = wave * SPW + (uint32_t)(lane / G);
   const uint64_t hi = stream_word(a.seed, a.offset + b) >> 32;
   const uint32_t slot = (uint32_t)((hi * (uint64_t)a.size) >> 32);
-  emit<1, 64>(a, wave, lane, b, b < a.B, slot, 0.0f, 0.0f);
+  emit<G, SPW>(a, wave, lane, b, b < a.B && (lane & (G - 1)) == 0, slot, 0.0f, 0.0f);
 }
 
 template <int G, int V>
@@ -605,9 +608,15 @@ hipError_t launch_uniform(const Storage& st, uint32_t size, int64_t B, uint64_t 
   a.out_stride = out_stride;
   a.dones_f32 = dones_f32 ? 1 : 0;
   a.st = st;
-  const uint64_t waves = ((uint64_t)B + 63) / 64;
-  hipLaunchKernelGGL(uniform_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(kSampleThreads), 0,
-                     s, a);
+  if (B <= 16384) {
+    const uint64_t waves = ((uint64_t)B + 3) / 4;
+    hipLaunchKernelGGL(uniform_kernel<16>, dim3((unsigned)((waves + 3) / 4)),
+                       dim3(kSampleThreads), 0, s, a);
+  } else {
+    const uint64_t waves = ((uint64_t)B + 63) / 64;
+    hipLaunchKernelGGL(uniform_kernel<1>, dim3((unsigned)((waves + 3) / 4)),
+                       dim3(kSampleThreads), 0, s, a);
+  }
   return hipGetLastError();
 }
 
