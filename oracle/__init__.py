@@ -67,6 +67,15 @@ def _bind(path: str):
         getattr(lib, name).argtypes = [vp]
     lib.pero_state_dim.restype = i32
     lib.pero_state_dim.argtypes = [vp]
+    lib.pero_rank_refresh.restype = ctypes.c_int
+    lib.pero_rank_refresh.argtypes = [vp]
+    lib.pero_sample_rank.restype = ctypes.c_int
+    lib.pero_sample_rank.argtypes = [vp, i64, vp, f64, vp, vp, vp, vp, vp, vp, vp]
+    lib.pero_rank_order.restype = ctypes.POINTER(i64)
+    lib.pero_rank_order.argtypes = [vp]
+    for name in ("pero_rank_sum_tree", "pero_rank_min_tree"):
+        getattr(lib, name).restype = ctypes.POINTER(f32)
+        getattr(lib, name).argtypes = [vp]
     for name in ("pero_sum_tree", "pero_min_tree"):
         getattr(lib, name).restype = ctypes.POINTER(f32)
         getattr(lib, name).argtypes = [vp]
@@ -258,3 +267,36 @@ class Oracle:
     def min_tree(self) -> np.ndarray:
         p = self._lib.pero_min_tree(self._h)
         return np.ctypeslib.as_array(p, shape=(2 * self.capacity,)).copy()
+
+    def rank_refresh(self):
+        """pero_rank_refresh: rank the filled slots, rebuild the rank-weight tree."""
+        if self._lib.pero_rank_refresh(self._h) != 0:
+            raise MemoryError("pero_rank_refresh failed")
+
+    def rank_order(self) -> np.ndarray:
+        """Slots by rank (descending priority, ties by slot), as of the refresh."""
+        p = self._lib.pero_rank_order(self._h)
+        return np.ctypeslib.as_array(p, shape=(self.capacity,))[:self.size].copy()
+
+    def rank_sum_tree(self) -> np.ndarray:
+        p = self._lib.pero_rank_sum_tree(self._h)
+        return np.ctypeslib.as_array(p, shape=(2 * self.capacity,)).copy()
+
+    def rank_min_tree(self) -> np.ndarray:
+        p = self._lib.pero_rank_min_tree(self._h)
+        return np.ctypeslib.as_array(p, shape=(2 * self.capacity,)).copy()
+
+    def sample_rank(self, u, beta=0.4, weights=True, rows=False):
+        """pero_sample_rank: rank-based sample as of the last refresh."""
+        u = _c(u, np.float32)
+        B = u.size
+        idx = np.empty(B, np.int64)
+        w = np.empty(B, np.float32) if weights else None
+        outs = self._rows(B, rows)
+        rc = self._lib.pero_sample_rank(self._h, B, _ptr(u), float(beta), _ptr(idx), _ptr(w),
+                                        *[_ptr(o) for o in outs])
+        if rc == -3:
+            raise RuntimeError("rank sample before a refresh, or from an empty buffer")
+        if rc != 0:
+            raise ValueError("pero_sample_rank failed rc=%d" % rc)
+        return self._result(idx, w, outs, rows)

@@ -24,6 +24,11 @@ struct pero {
     uint8_t* dones;     /* [n] */
     int64_t size, cursor;
     float maxp;         /* running max priority */
+    /* rank-based sampling, as of the last pero_rank_refresh */
+    int64_t rank_size;  /* filled slots when refreshed; 0 = never */
+    int64_t* order;     /* [n] slots by descending priority, ties by slot */
+    float* rsum;        /* [2n] tree over the rank weights, as sum */
+    float* rmn;         /* [2n] and its twin min tree */
 };
 
 /* Recompute every ancestor of tree node i, from its parent up to the root.
@@ -90,6 +95,9 @@ void pero_destroy(pero_t* t) {
     free(t->actions);
     free(t->rewards);
     free(t->dones);
+    free(t->order);
+    free(t->rsum);
+    free(t->rmn);
     free(t);
 }
 
@@ -161,11 +169,11 @@ int pero_update(pero_t* t, int64_t B, const int64_t* idx, const float* td) {
  * child's sum exceeds the remaining mass go left, otherwise subtract it and
  * go right.  Reading: the mass is carried in f32 and a zero right child
  * also sends the walk left. */
-static int64_t descend(const pero_t* t, float m) {
+static int64_t descend_tree(const float* sum, int64_t n, float m) {
     int64_t i = 1;
-    while (i < t->n) {
-        float l = t->sum[2 * i];
-        float r = t->sum[2 * i + 1];
+    while (i < n) {
+        float l = sum[2 * i];
+        float r = sum[2 * i + 1];
         if (l > m || r == 0.0f) {
             i = 2 * i;
         } else {
@@ -173,7 +181,18 @@ static int64_t descend(const pero_t* t, float m) {
             i = 2 * i + 1;
         }
     }
-    return i - t->n;
+    return i - n;
+}
+
+/* IS weight of a sampled priority p: (N*P(i))^-beta normalised by its
+ * largest value, which belongs to the minimum priority ("GPU-Resident
+ * Prioritized Experience Replay", section "Sampling Kernels"); 0 when the
+ * minimum priority is 0. */
+static float is_weight(double N, float p, float pmin, float total, double beta) {
+    if (!(pmin > 0.0f)) return 0.0f;
+    double P_i = (double)p / (double)total;
+    double P_min = (double)pmin / (double)total;
+    return (float)(pow(N * P_i, -beta) / pow(N * P_min, -beta));
 }
 
 /* "GPU-Resident Prioritized Experience Replay", section "Sampling Kernels":
@@ -194,18 +213,9 @@ int pero_sample(const pero_t* t, int64_t B, const float* u, double beta, int64_t
     for (int64_t b = 0; b < B; ++b) {
         float m = u[b] * total;
         if (!(m < total)) m = nextafterf(total, 0.0f);
-        int64_t slot = descend(t, m);
+        int64_t slot = descend_tree(t->sum, t->n, m);
         idx_out[b] = slot;
-        if (w_out) {
-            float p = t->sum[t->n + slot];
-            if (pmin > 0.0f) {
-                double P_i = (double)p / (double)total;
-                double P_min = (double)pmin / (double)total;
-                w_out[b] = (float)(pow(N * P_i, -beta) / pow(N * P_min, -beta));
-            } else {
-                w_out[b] = 0.0f;
-            }
-        }
+        if (w_out) w_out[b] = is_weight(N, t->sum[t->n + slot], pmin, total, beta);
         if (D > 0 && states_out) {
             memcpy(states_out + b * D, t->states + slot * D, sizeof(float) * D);
             memcpy(next_states_out + b * D, t->next_states + slot * D, sizeof(float) * D);
@@ -329,6 +339,95 @@ int pero_sample_uniform(const pero_t* t, int64_t B, uint64_t seed, uint64_t offs
     }
     return 0;
 }
+
+/* Rank-based prioritisation ("GPU-Resident Prioritized Experience Replay",
+ * section "Sampling Kernels", rank-based: sort the (priority, index) pairs
+ * descending, then sample with probabilities 1/rank^alpha through their
+ * cumulative sum, gather, IS weights).  The refresh ranks the filled slots:
+ * order[r] is the slot of rank r + 1, by descending priority, equal
+ * priorities by ascending slot; the rank weights w_r = f32((r+1)^-alpha) are
+ * the leaves of a second tree built like the priority trees (sums and mins
+ * of children), which holds their cumulative sums for the descent. */
+typedef struct {
+    float p;
+    int64_t slot;
+} rank_pair;
+
+static int by_priority_desc(const void* a, const void* b) {
+    const rank_pair* x = (const rank_pair*)a;
+    const rank_pair* y = (const rank_pair*)b;
+    if (x->p > y->p) return -1;
+    if (x->p < y->p) return 1;
+    return (x->slot < y->slot) ? -1 : (x->slot > y->slot);
+}
+
+int pero_rank_refresh(pero_t* t) {
+    const int64_t n = t->n;
+    if (!t->order) {
+        t->order = (int64_t*)calloc((size_t)n, sizeof(int64_t));
+        t->rsum = (float*)calloc((size_t)(2 * n), sizeof(float));
+        t->rmn = (float*)calloc((size_t)(2 * n), sizeof(float));
+        if (!t->order || !t->rsum || !t->rmn) return -1;
+    }
+    rank_pair* pairs = (rank_pair*)malloc(sizeof(rank_pair) * (size_t)(t->size ? t->size : 1));
+    if (!pairs) return -1;
+    for (int64_t s = 0; s < t->size; ++s) {
+        pairs[s].p = t->sum[n + s];
+        pairs[s].slot = s;
+    }
+    qsort(pairs, (size_t)t->size, sizeof(rank_pair), by_priority_desc);
+    for (int64_t r = 0; r < t->size; ++r) t->order[r] = pairs[r].slot;
+    free(pairs);
+    for (int64_t r = 0; r < n; ++r) {
+        const float w = (r < t->size) ? (float)pow((double)(r + 1), -t->alpha) : 0.0f;
+        t->rsum[n + r] = w;
+        t->rmn[n + r] = (r < t->size) ? w : INFINITY;
+    }
+    for (int64_t i = n - 1; i >= 1; --i) {
+        float l = t->rsum[2 * i], r = t->rsum[2 * i + 1];
+        t->rsum[i] = l + r;
+        float a = t->rmn[2 * i], b = t->rmn[2 * i + 1];
+        t->rmn[i] = (b < a) ? b : a;
+    }
+    t->rank_size = t->size;
+    return 0;
+}
+
+/* Rank-based sample as of the last refresh: the descent of pero_sample on
+ * the rank-weight tree gives a rank r; the sampled slot is order[r]; the IS
+ * weight is that of pero_sample with the rank weights as priorities and
+ * N = the filled size at the refresh.  -3 if never refreshed or empty. */
+int pero_sample_rank(const pero_t* t, int64_t B, const float* u, double beta, int64_t* idx_out,
+                     float* w_out, float* states_out, float* next_states_out,
+                     uint32_t* actions_out, float* rewards_out, uint8_t* dones_out) {
+    if (B < 0) return -1;
+    if (B == 0) return 0;
+    if (t->rank_size == 0) return -3;
+    const float total = t->rsum[1];
+    const float pmin = t->rmn[1];
+    const double N = (double)t->rank_size;
+    const int64_t D = t->D;
+    for (int64_t b = 0; b < B; ++b) {
+        float m = u[b] * total;
+        if (!(m < total)) m = nextafterf(total, 0.0f);
+        const int64_t r = descend_tree(t->rsum, t->n, m);
+        const int64_t slot = t->order[r];
+        idx_out[b] = slot;
+        if (w_out) w_out[b] = is_weight(N, t->rsum[t->n + r], pmin, total, beta);
+        if (D > 0 && states_out) {
+            memcpy(states_out + b * D, t->states + slot * D, sizeof(float) * D);
+            memcpy(next_states_out + b * D, t->next_states + slot * D, sizeof(float) * D);
+            actions_out[b] = t->actions[slot];
+            rewards_out[b] = t->rewards[slot];
+            dones_out[b] = t->dones[slot];
+        }
+    }
+    return 0;
+}
+
+const int64_t* pero_rank_order(const pero_t* t) { return t->order; }
+const float* pero_rank_sum_tree(const pero_t* t) { return t->rsum; }
+const float* pero_rank_min_tree(const pero_t* t) { return t->rmn; }
 
 float pero_total(const pero_t* t) { return t->sum[1]; }
 float pero_min(const pero_t* t) { return t->mn[1]; }

@@ -88,6 +88,19 @@ int pero_sample_uniform(const pero_t* t, int64_t B, uint64_t seed, uint64_t offs
                         int64_t* idx_out, float* states_out, float* next_states_out,
                         uint32_t* actions_out, float* rewards_out, uint8_t* dones_out);
 
+/* Rank-based sampling: pero_rank_refresh ranks the filled slots (order[r]
+ * = slot of rank r + 1, by descending priority, ties by ascending slot) and
+ * builds the tree over the rank weights f32((r+1)^-alpha); pero_sample_rank
+ * descends that tree and samples order[r].  The rank arrays are valid after
+ * a refresh (NULL before the first). */
+int pero_rank_refresh(pero_t* t);
+int pero_sample_rank(const pero_t* t, int64_t B, const float* u, double beta, int64_t* idx_out,
+                     float* w_out, float* states_out, float* next_states_out,
+                     uint32_t* actions_out, float* rewards_out, uint8_t* dones_out);
+const int64_t* pero_rank_order(const pero_t* t);
+const float* pero_rank_sum_tree(const pero_t* t);
+const float* pero_rank_min_tree(const pero_t* t);
+
 /* pero_sample written into padded trainer buffers: state rows of out_stride
  * >= D floats, zero past column D; actions i32 (stored bits), rewards f32,
  * dones f32.  -1 if out_stride < D. */

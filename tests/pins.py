@@ -538,7 +538,63 @@ def pin_m_device_masses(lib):
     o.close()
 
 
+def pin_n_rank_based(lib):
+    """P-n: rank-based prioritisation ("GPU-Resident Prioritized Experience
+    Replay", section "Sampling Kernels", rank-based): the order is the filled
+    slots by descending priority with ties by ascending slot (numpy lexsort);
+    the rank weights are f32((r+1)^-alpha) (numpy f64 power) under a tree
+    equal to the rebuild of its leaves; with alpha = 0 every rank is equally
+    likely and sample == order[floor(u * size)]; the IS weights equal
+    (rank / size)^(alpha * beta) up to f32 rounding; rank frequencies follow
+    r^-alpha (chi-square)."""
+    n = 1024
+    rng = np.random.default_rng(31)
+    p = rng.integers(0, 50, 900).astype(np.float32) / 8  # many ties and zeros
+    for alpha in (0.7, 0.0):
+        o = Oracle(n, alpha=alpha, lib=lib)
+        o.add(900, prio=p)
+        o.rank_refresh()
+        order = o.rank_order()
+        ref = np.lexsort((np.arange(900), -p.astype(np.float64)))
+        assert np.array_equal(order, ref)
+        rs, rm = o.rank_sum_tree(), o.rank_min_tree()
+        w = np.zeros(n, np.float32)
+        w[:900] = (np.arange(1, 901, dtype=np.float64) ** -alpha).astype(np.float32)
+        assert np.array_equal(rs[n:].view(np.uint32), w.view(np.uint32))
+        es, em = rebuild_with_empty(w, np.arange(n) < 900)
+        assert np.array_equal(rs[1:].view(np.uint32), es[1:].view(np.uint32))
+        assert np.array_equal(rm[1:].view(np.uint32), em[1:].view(np.uint32))
+        if alpha == 0.0:
+            o.close()
+            continue
+        u = rng.random(20000, dtype=np.float32)
+        res = o.sample_rank(u, beta=0.5)
+        rank = np.argsort(order)[res["idx"]] + 1  # 1-based rank of each sampled slot
+        expw = (rank / 900.0) ** (alpha * 0.5)
+        assert np.allclose(res["w"], expw, rtol=1e-6, atol=0)
+        M = 1 << 18
+        res = o.sample_rank(rng.random(M, dtype=np.float32), weights=False)
+        counts = np.bincount(np.argsort(order)[res["idx"]], minlength=900).astype(np.float64)
+        prob = np.arange(1, 901, dtype=np.float64) ** -alpha
+        expc = M * prob / prob.sum()
+        keep = expc >= 5
+        chi2 = float((((counts - expc) ** 2) / expc)[keep].sum())
+        import scipy.stats
+        assert scipy.stats.chi2.sf(chi2, int(keep.sum()) - 1) > 1e-3, chi2
+        o.close()
+    # alpha = 0 over a full power-of-two ring: uniform over ranks, exactly
+    o = Oracle(n, alpha=0.0, lib=lib)
+    o.add(n, prio=rng.random(n).astype(np.float32))
+    o.rank_refresh()
+    u = (rng.integers(0, 1 << 20, 5000) / float(1 << 20)).astype(np.float32)
+    res = o.sample_rank(u, beta=0.4)
+    assert np.array_equal(res["idx"], o.rank_order()[np.floor(u.astype(np.float64) * n).astype(np.int64)])
+    assert np.all(res["w"] == 1.0)
+    o.close()
+
+
 ALL_PINS = [pin_golden_hand_tree, pin_a_invariant, pin_b_root_bound, pin_c_update_equivalence,
             pin_d_dyadic_exact, pin_e_uniform_closed_form, pin_f_brute_force_band,
             pin_g_chi_square, pin_h_is_weights, pin_i_gather, pin_j_intake,
-            pin_k_priority_decimal, pin_l_padded_gather, pin_m_device_masses]
+            pin_k_priority_decimal, pin_l_padded_gather, pin_m_device_masses,
+            pin_n_rank_based]

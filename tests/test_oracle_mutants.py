@@ -17,8 +17,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 MUTANTS = [
     ("tie_goes_left", "if (l > m || r == 0.0f)", "if (l >= m || r == 0.0f)"),
     ("no_zero_guard", "if (l > m || r == 0.0f)", "if (l > m)"),
-    ("children_swapped", "float l = t->sum[2 * i];\n        float r = t->sum[2 * i + 1];",
-     "float l = t->sum[2 * i + 1];\n        float r = t->sum[2 * i];"),
+    ("children_swapped", "float l = sum[2 * i];\n        float r = sum[2 * i + 1];",
+     "float l = sum[2 * i + 1];\n        float r = sum[2 * i];"),
     ("mass_added", "m = m - l;", "m = m + l;"),
     ("mass_not_reduced", "m = m - l;", "m = m;"),
     ("sum_drops_right", "t->sum[i] = l + r;", "t->sum[i] = l;"),
@@ -61,6 +61,14 @@ MUTANTS = [
     ("philox_nine_rounds", "for (int r = 0; r < 10; ++r)", "for (int r = 0; r < 9; ++r)"),
     ("stream_word_order", "return out[j % 4];", "return out[3 - j % 4];"),
     ("mass_wrong_bits", ">> 40) * 0x1p-24f", ">> 41) * 0x1p-24f"),
+    ("rank_ties_by_slot_desc", "return (x->slot < y->slot) ? -1 : (x->slot > y->slot);",
+     "return (x->slot > y->slot) ? -1 : (x->slot < y->slot);"),
+    ("rank_ascending", "if (x->p > y->p) return -1;\n    if (x->p < y->p) return 1;",
+     "if (x->p > y->p) return 1;\n    if (x->p < y->p) return -1;"),
+    ("rank_weight_off_by_one", "pow((double)(r + 1), -t->alpha)", "pow((double)(r + 2), -t->alpha)"),
+    ("rank_weight_sign", "pow((double)(r + 1), -t->alpha)", "pow((double)(r + 1), t->alpha)"),
+    ("rank_descends_priorities", "descend_tree(t->rsum, t->n, m)", "descend_tree(t->sum, t->n, m)"),
+    ("rank_slot_not_through_order", "const int64_t slot = t->order[r];", "const int64_t slot = r;"),
     ("uniform_modulo", "(int64_t)((hi * (uint64_t)t->size) >> 32)", "(int64_t)(hi % (uint64_t)t->size)"),
 ]
 
