@@ -176,6 +176,44 @@ int per_sample_uniform(per_t* h, int64_t B, uint64_t seed, uint64_t offset, int6
                        float* d_rewards_out, uint8_t* d_dones_out, hipStream_t stream);
 
 /*
+ * Rank-based prioritisation ("GPU-Resident Prioritized Experience Replay",
+ * section "Sampling Kernels", rank-based: the (priority, index) pairs sorted
+ * descending, then sampling with probabilities 1/rank^alpha through their
+ * cumulative sum, gather and IS weights).
+ *
+ * per_rank_workspace_bytes: bytes of the extra device workspace a handle of
+ *   this capacity needs for it (the trees over the rank weights, 2 x 2 x
+ *   capacity f32; the sort's buffers, 4 x capacity u32; its tile counts).
+ * per_rank_attach: hands that workspace (caller-owned, 256-byte aligned,
+ *   kept until per_destroy) to the handle.  PER_ENOSPC if too small.
+ * per_rank_refresh: ranks the filled slots [0, size) by descending leaf
+ *   priority, equal priorities by ascending slot (stable radix sort), and,
+ *   when size changed since the last refresh, rebuilds the trees over the
+ *   rank weights w_r = f32(pow_f64(r + 1, -alpha)) for ranks r < size (sum 0
+ *   / min +inf beyond), with the pairwise rules of the priority trees.
+ *   Later per_update / per_add calls do not change the ranking until the
+ *   next refresh.  PER_EEMPTY if size == 0; PER_EINVAL without a workspace.
+ * per_sample_rank: per_sample over the rank-weight trees as of the last
+ *   refresh: the descent on mass f32(u_b * W), W = the sum of the rank
+ *   weights, gives a rank r, and the sample is the slot of rank r; the IS
+ *   weight is per_sample's with the rank weights as priorities and N = the
+ *   size at the refresh.  Arguments, row outputs and errors as per_sample;
+ *   PER_EEMPTY before the first refresh.
+ * per_rank_ptrs: read-only device views for inspection: the ranking
+ *   (d_order[r] = slot of rank r, r < size at the refresh) and the two
+ *   rank-weight trees (2 x capacity f32 each, node 0 unused).
+ */
+int per_rank_workspace_bytes(int64_t capacity, size_t* out);
+int per_rank_attach(per_t* h, void* d_ws, size_t ws_bytes);
+int per_rank_refresh(per_t* h, hipStream_t stream);
+int per_sample_rank(per_t* h, int64_t B, const float* d_u, double beta, int64_t* d_idx_out,
+                    float* d_w_out, float* d_states_out, float* d_next_states_out,
+                    uint32_t* d_actions_out, float* d_rewards_out, uint8_t* d_dones_out,
+                    hipStream_t stream);
+int per_rank_ptrs(const per_t* h, const uint32_t** d_order, const float** d_rank_sum,
+                  const float** d_rank_min);
+
+/*
  * per_sample written straight into a trainer's input buffers ("True
  * Single-Graph Implementation Plan", Task 2: rows gathered into a padded
  * destination, scalars gathered as f32 / i32; Task 3: the sampler writes the

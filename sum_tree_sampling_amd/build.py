@@ -9,7 +9,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libper.so")
-SOURCES = ["per_api.hip", "tree_kernels.hip", "sample_kernels.hip"]
+SOURCES = ["per_api.hip", "tree_kernels.hip", "sample_kernels.hip", "rank_kernels.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # IEEE f32 arithmetic as written: no contraction into FMA, no fast-math, no

@@ -25,6 +25,14 @@ struct per_s {
   int ovf;         // overflow counter for the next bucketed update
   bool top_stale;  // nodes above the partitions not yet rebuilt
   int device;
+  // rank-based prioritisation (after per_rank_attach)
+  bool rank_attached;
+  per::TreePtrs rt;      // trees over the rank weights (ctrl unused)
+  uint32_t* rkeys[2];    // radix-sort ping-pong buffers, n words each
+  uint32_t* rvals[2];    // rvals[0] holds the ranking after a refresh
+  uint32_t* rhist;       // 16 words per 4096-item tile
+  int64_t rank_size;     // filled slots at the last refresh (0: none)
+  int64_t rank_built;    // count the rank-weight trees were built for (-1: none)
 };
 
 namespace {
@@ -184,6 +192,9 @@ int per_create(per_t** out, int64_t capacity, int32_t state_dim, int64_t max_bat
   h->epoch = 0;
   h->ovf = 0;
   h->top_stale = false;
+  h->rank_attached = false;
+  h->rank_size = 0;
+  h->rank_built = -1;
   if (hipGetDevice(&h->device) != hipSuccess) h->device = -1;
   hipError_t e = per::launch_init(h->t, h->bk, h->g, stream);
   if (e != hipSuccess) {
@@ -245,7 +256,7 @@ int per_update(per_t* h, int64_t B, const int64_t* d_idx, const float* d_td,
 
 namespace {
 
-enum SampleKind { kGivenMasses, kStreamMasses, kUniform };
+enum SampleKind { kGivenMasses, kStreamMasses, kUniform, kRank };
 
 // Shared by the sample entry points: masses given (d_u), drawn from the
 // generator stream (seed, offset), or a uniform sample from the stream;
@@ -264,7 +275,7 @@ int sample_impl(per_t* h, int64_t B, SampleKind kind, const float* d_u, uint64_t
                 (int)h->st.D, (long long)PER_MAX_OUT_STRIDE);
   if (B == 0) return ok();
   if (!d_idx_out) return fail(PER_EINVAL, "idx_out is required");
-  if (kind == kGivenMasses && !d_u) return fail(PER_EINVAL, "u is required");
+  if ((kind == kGivenMasses || kind == kRank) && !d_u) return fail(PER_EINVAL, "u is required");
   if (!(beta >= 0.0) || !(beta < 1e300)) return fail(PER_EINVAL, "beta must be finite, >= 0");
   const bool any_rows = d_states_out || d_next_states_out || d_actions_out || d_rewards_out ||
                         d_dones_out;
@@ -276,6 +287,17 @@ int sample_impl(per_t* h, int64_t B, SampleKind kind, const float* d_u, uint64_t
                     reinterpret_cast<uintptr_t>(d_next_states_out)) & 15u))
     return fail(PER_EINVAL, "state outputs must be 16-byte aligned");
   if (h->size == 0) return fail(PER_EEMPTY, "sample from an empty buffer");
+  if (kind == kRank) {
+    if (h->rank_size == 0) return fail(PER_EEMPTY, "rank sample before per_rank_refresh");
+    const per::SamplePlan plan = per::make_sample_plan(h->g, B);
+    hipError_t e = per::launch_sample(h->rt, h->g, h->st, plan, (uint32_t)h->rank_size, B, d_u,
+                                      0, 0, beta, d_idx_out, d_w_out,
+                                      any_rows ? d_states_out : nullptr, d_next_states_out,
+                                      d_actions_out, d_rewards_out, d_dones_out,
+                                      (uint32_t)out_stride, dones_f32, false, stream,
+                                      h->rvals[0]);
+    return e == hipSuccess ? ok() : hip_fail(e, what);
+  }
   if (kind == kUniform) {
     hipError_t e = per::launch_uniform(h->st, (uint32_t)h->size, B, seed, offset, d_idx_out,
                                        any_rows ? d_states_out : nullptr, d_next_states_out,
@@ -379,6 +401,98 @@ int64_t per_size(const per_t* h) { return h ? h->size : -1; }
 int64_t per_cursor(const per_t* h) { return h ? h->cursor : -1; }
 int64_t per_capacity(const per_t* h) { return h ? (int64_t)h->g.n : -1; }
 int32_t per_state_dim(const per_t* h) { return h ? h->st.D : -1; }
+
+namespace {
+
+struct RankLayout {
+  size_t rsum, rmn, keys0, keys1, vals0, vals1, hist, total;
+};
+
+RankLayout rank_layout(int64_t n) {
+  RankLayout l;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align256(o + bytes);
+    return at;
+  };
+  l.rsum = take(sizeof(float) * 2 * (size_t)n);
+  l.rmn = take(sizeof(float) * 2 * (size_t)n);
+  l.keys0 = take(sizeof(uint32_t) * (size_t)n);
+  l.keys1 = take(sizeof(uint32_t) * (size_t)n);
+  l.vals0 = take(sizeof(uint32_t) * (size_t)n);
+  l.vals1 = take(sizeof(uint32_t) * (size_t)n);
+  l.hist = take(sizeof(uint32_t) * 16 * (size_t)per::rank_tiles(n));
+  l.total = o;
+  return l;
+}
+
+}  // namespace
+
+int per_rank_workspace_bytes(int64_t capacity, size_t* out) {
+  if (!out) return fail(PER_EINVAL, "out is NULL");
+  int rc = check_capacity(capacity);
+  if (rc) return rc;
+  *out = rank_layout(capacity).total;
+  return ok();
+}
+
+int per_rank_attach(per_t* h, void* d_ws, size_t ws_bytes) {
+  if (!h || !d_ws) return fail(PER_EINVAL, "NULL argument");
+  if (reinterpret_cast<uintptr_t>(d_ws) & 255u)
+    return fail(PER_EINVAL, "rank workspace is not 256-byte aligned");
+  const RankLayout l = rank_layout(h->g.n);
+  if (ws_bytes < l.total)
+    return fail(PER_ENOSPC, "rank workspace of %zu bytes, %zu needed", ws_bytes, l.total);
+  char* base = static_cast<char*>(d_ws);
+  h->rt.sum = reinterpret_cast<float*>(base + l.rsum);
+  h->rt.mn = reinterpret_cast<float*>(base + l.rmn);
+  h->rt.ctrl = nullptr;
+  h->rkeys[0] = reinterpret_cast<uint32_t*>(base + l.keys0);
+  h->rkeys[1] = reinterpret_cast<uint32_t*>(base + l.keys1);
+  h->rvals[0] = reinterpret_cast<uint32_t*>(base + l.vals0);
+  h->rvals[1] = reinterpret_cast<uint32_t*>(base + l.vals1);
+  h->rhist = reinterpret_cast<uint32_t*>(base + l.hist);
+  h->rank_attached = true;
+  h->rank_size = 0;
+  h->rank_built = -1;
+  return ok();
+}
+
+int per_rank_refresh(per_t* h, hipStream_t stream) {
+  if (!h) return fail(PER_EINVAL, "handle is NULL");
+  if (!h->rank_attached) return fail(PER_EINVAL, "no rank workspace: call per_rank_attach");
+  if (h->size == 0) return fail(PER_EEMPTY, "ranking an empty buffer");
+  hipError_t e = per::launch_rank_sort(h->t.sum + h->g.n, (uint32_t)h->size, h->rkeys, h->rvals,
+                                       h->rhist, stream);
+  if (e != hipSuccess) return hip_fail(e, "per_rank_refresh: sort");
+  if (h->rank_built != h->size) {
+    e = per::launch_rank_build(h->rt, h->g, (uint32_t)h->size, h->alpha, stream);
+    if (e != hipSuccess) return hip_fail(e, "per_rank_refresh: rank weights");
+    h->rank_built = h->size;
+  }
+  h->rank_size = h->size;
+  return ok();
+}
+
+int per_sample_rank(per_t* h, int64_t B, const float* d_u, double beta, int64_t* d_idx_out,
+                    float* d_w_out, float* d_states_out, float* d_next_states_out,
+                    uint32_t* d_actions_out, float* d_rewards_out, uint8_t* d_dones_out,
+                    hipStream_t stream) {
+  return sample_impl(h, B, kRank, d_u, 0, 0, beta, d_idx_out, d_w_out, d_states_out,
+                     d_next_states_out, h ? h->st.D : 0, d_actions_out, d_rewards_out,
+                     d_dones_out, false, stream, "per_sample_rank");
+}
+
+int per_rank_ptrs(const per_t* h, const uint32_t** d_order, const float** d_rank_sum,
+                  const float** d_rank_min) {
+  if (!h || !d_order || !d_rank_sum || !d_rank_min) return fail(PER_EINVAL, "NULL argument");
+  if (!h->rank_attached) return fail(PER_EINVAL, "no rank workspace: call per_rank_attach");
+  *d_order = h->rvals[0];
+  *d_rank_sum = h->rt.sum;
+  *d_rank_min = h->rt.mn;
+  return ok();
+}
 
 int per_tree_ptrs(const per_t* h, const float** d_sum, const float** d_min) {
   if (!h || !d_sum || !d_min) return fail(PER_EINVAL, "NULL argument");

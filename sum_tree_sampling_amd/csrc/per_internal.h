@@ -111,9 +111,19 @@ hipError_t launch_sample(const TreePtrs& t, const Geom& g, const Storage& st,
                          float* w_out, float* states_out,
                          float* next_out, uint32_t* actions_out, float* rewards_out,
                          void* dones_out, uint32_t out_stride, bool dones_f32,
-                         bool write_top, hipStream_t s);
+                         bool write_top, hipStream_t s, const uint32_t* order = nullptr);
 
 SamplePlan make_sample_plan(const Geom& g, int64_t B);
+
+// Rank-based prioritisation: a stable radix sort of the slots [0, count) by
+// descending leaf priority (keys / vals: two ping-pong buffers of n words,
+// the ranking ends in vals[0]; hist: 16 * rank_tiles(n) words), and the
+// build of the trees over the rank weights (count filled ranks).
+hipError_t launch_rank_sort(const float* leaves, uint32_t count, uint32_t* const keys[2],
+                            uint32_t* const vals[2], uint32_t* hist, hipStream_t s);
+hipError_t launch_rank_build(const TreePtrs& rt, const Geom& g, uint32_t count, double alpha,
+                             hipStream_t s);
+uint32_t rank_tiles(int64_t n);
 
 // Uniform sample of B slots over [0, size) from the generator stream.
 hipError_t launch_uniform(const Storage& st, uint32_t size, int64_t B, uint64_t seed,

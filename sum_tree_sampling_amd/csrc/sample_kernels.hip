@@ -45,6 +45,7 @@ struct SampleArgs {
   uint32_t n;
   uint32_t size;
   uint32_t B;
+  const uint32_t* order;  // rank-based: the slot of each leaf (rank), or NULL
   const float* u;       // masses, or NULL: from the generator stream
   uint64_t seed;        // generator key (seed, 0)
   uint64_t offset;      // stream word of sample 0
@@ -474,7 +475,9 @@ __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleArgs a) {
     leaf = lv;
   }
 
-  emit<G, SPW>(a, wave, lane, b, active && j == 0, node - a.n, leaf, pmin);
+  uint32_t slot = node - a.n;
+  if (a.order) slot = a.order[slot];  // rank-based: the descent gave a rank
+  emit<G, SPW>(a, wave, lane, b, active && j == 0, slot, leaf, pmin);
 }
 
 // Uniform sample over the filled slots ("GPU-Resident Prioritized
@@ -553,13 +556,14 @@ hipError_t launch_sample(const TreePtrs& t, const Geom& g, const Storage& st,
                          float* w_out, float* states_out,
                          float* next_out, uint32_t* actions_out, float* rewards_out,
                          void* dones_out, uint32_t out_stride, bool dones_f32,
-                         bool write_top, hipStream_t s) {
+                         bool write_top, hipStream_t s, const uint32_t* order) {
   SampleArgs a{};
   a.sum = t.sum;
   a.mn = t.mn;
   a.n = g.n;
   a.size = size;
   a.B = (uint32_t)B;
+  a.order = order;
   a.u = u;
   a.seed = seed;
   a.offset = offset;

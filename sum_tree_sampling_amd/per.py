@@ -51,6 +51,12 @@ def load(path: str | None = None) -> ctypes.CDLL:
         "per_sample_padded": (c_int, [vp, i64, vp, f64, vp, vp, vp, vp, i64, vp, vp, vp, vp]),
         "per_sample_philox": (c_int, [vp, i64, u64, u64, f64, vp, vp, vp, vp, vp, vp, vp, vp]),
         "per_sample_uniform": (c_int, [vp, i64, u64, u64, vp, vp, vp, vp, vp, vp, vp]),
+        "per_rank_workspace_bytes": (c_int, [i64, ctypes.POINTER(sz)]),
+        "per_rank_attach": (c_int, [vp, vp, sz]),
+        "per_rank_refresh": (c_int, [vp, vp]),
+        "per_sample_rank": (c_int, [vp, i64, vp, f64, vp, vp, vp, vp, vp, vp, vp, vp]),
+        "per_rank_ptrs": (c_int, [vp, ctypes.POINTER(vp), ctypes.POINTER(vp),
+                                  ctypes.POINTER(vp)]),
         "per_flush": (c_int, [vp, vp]),
         "per_total": (c_int, [vp, vp, vp]),
         "per_min": (c_int, [vp, vp, vp]),
@@ -163,6 +169,33 @@ def per_sample_uniform(h, B, seed, offset, idx_out, states_out=None, next_states
                                      _p(idx_out), _p(states_out), _p(next_states_out),
                                      _p(actions_out), _p(rewards_out), _p(dones_out),
                                      _stream(stream)))
+
+
+def per_rank_workspace_bytes(capacity) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load().per_rank_workspace_bytes(int(capacity), ctypes.byref(out)))
+    return out.value
+
+
+def per_rank_attach(h, ws, nbytes) -> None:
+    _check(load().per_rank_attach(h, _p(ws), int(nbytes)))
+
+
+def per_rank_refresh(h, stream=None) -> None:
+    _check(load().per_rank_refresh(h, _stream(stream)))
+
+
+def per_sample_rank(h, B, u, beta, idx_out, w_out=None, states_out=None, next_states_out=None,
+                    actions_out=None, rewards_out=None, dones_out=None, stream=None) -> None:
+    _check(load().per_sample_rank(h, int(B), _p(u), float(beta), _p(idx_out), _p(w_out),
+                                  _p(states_out), _p(next_states_out), _p(actions_out),
+                                  _p(rewards_out), _p(dones_out), _stream(stream)))
+
+
+def per_rank_ptrs(h):
+    o, s, m = ctypes.c_void_p(0), ctypes.c_void_p(0), ctypes.c_void_p(0)
+    _check(load().per_rank_ptrs(h, ctypes.byref(o), ctypes.byref(s), ctypes.byref(m)))
+    return o.value, s.value, m.value
 
 
 def per_flush(h, stream=None) -> None:
@@ -322,6 +355,41 @@ class PerBuffer:
         per_sample_uniform(self.h, B, seed, offset, out["idx"], out.get("states"),
                            out.get("next_states"), out.get("actions"), out.get("rewards"),
                            out.get("dones"), stream)
+        return out
+
+    def rank_attach(self):
+        """Allocate and attach the rank-based workspace (torch-owned)."""
+        nbytes = per_rank_workspace_bytes(self.capacity)
+        self.rank_ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=self.device)
+        off = (-self.rank_ws.data_ptr()) % 256
+        self._rank_ws = self.rank_ws[off:off + nbytes]
+        per_rank_attach(self.h, self._rank_ws, nbytes)
+
+    def rank_refresh(self, stream=None):
+        per_rank_refresh(self.h, stream)
+
+    def _rank_view(self, ptr, count, dtype):
+        base = self._rank_ws.data_ptr()
+        item = torch.empty((), dtype=dtype).element_size()
+        return self._rank_ws[ptr - base:ptr - base + count * item].view(dtype)
+
+    def rank_order(self) -> torch.Tensor:
+        """Device view of the ranking (slot of each rank, int32 bits of u32)."""
+        o, _, _ = per_rank_ptrs(self.h)
+        return self._rank_view(o, self.size, torch.int32)
+
+    def rank_trees(self):
+        """Device views of the two rank-weight trees (2n f32 each)."""
+        _, s, m = per_rank_ptrs(self.h)
+        return (self._rank_view(s, 2 * self.capacity, torch.float32),
+                self._rank_view(m, 2 * self.capacity, torch.float32))
+
+    def sample_rank(self, u, beta=0.4, weights=True, rows=False, out=None, stream=None):
+        """per_sample_rank: rank-based sample as of the last refresh."""
+        out = out or self._outs(u.numel(), weights, rows)
+        per_sample_rank(self.h, u.numel(), u, beta, out["idx"], out.get("w"), out.get("states"),
+                        out.get("next_states"), out.get("actions"), out.get("rewards"),
+                        out.get("dones"), stream)
         return out
 
     def sample_padded(self, u, out_stride, beta=0.4, weights=True, out=None, stream=None):

@@ -277,6 +277,59 @@ def test_uniform_sample(size, B):
             assert_bits_equal(host(rg[key]), ro[key], what + " " + key)
 
 
+@pytest.mark.parametrize("n,size,D,B", [(1 << 12, 1 << 12, 0, 300), (1 << 16, 50000, 5, 20000),
+                                        (1 << 21, 1 << 21, 0, 512)])
+def test_rank_based(n, size, D, B):
+    """Rank-based prioritisation against the oracle: the ranking (ties by
+    slot), both rank-weight trees bit for bit, and samples (indices and rows
+    bit for bit, weights within 1e-6); again after an update (ranking only)
+    and after more intake (rank-weight trees rebuilt)."""
+    say("rank", n, size, D, B)
+    rng = np.random.default_rng(size)
+    o = Oracle(n, D)
+    g = _buf(n, D, max_batch=max(B, 4096))
+    g.rank_attach()
+    first = size - min(size // 3, 1000)
+
+    def intake(c, p):
+        if D:
+            st = rng.standard_normal((c, D)).astype(np.float32)
+            ac = rng.integers(0, 3, c).astype(np.uint32)
+            rw = rng.standard_normal(c).astype(np.float32)
+            dn = (rng.random(c) < 0.1).astype(np.uint8)
+            o.add(c, st, st, ac, rw, dn, prio=p)
+            g.add(c, dev(st), dev(st), dev(ac), dev(rw), dev(dn), prio=None if p is None else dev(p))
+        else:
+            o.add(c, prio=p)
+            g.add(c, prio=None if p is None else dev(p))
+
+    intake(first, (rng.integers(0, 64, first) / 16).astype(np.float32))  # ties and zeros
+
+    def check(what):
+        o.rank_refresh()
+        g.rank_refresh()
+        torch.cuda.synchronize()
+        assert_bits_equal(host(g.rank_order()).view(np.uint32), o.rank_order().astype(np.uint32),
+                          what + " order")
+        rs, rm = g.rank_trees()
+        assert_bits_equal(host(rs)[1:], o.rank_sum_tree()[1:], what + " rank sum tree")
+        assert_bits_equal(host(rm)[1:], o.rank_min_tree()[1:], what + " rank min tree")
+        u = rng.random(B, dtype=np.float32)
+        ro = o.sample_rank(u, beta=0.4, rows=D > 0)
+        rg = g.sample_rank(dev(u), beta=0.4, rows=D > 0)
+        compare_sample(rg, ro, what + " sample", rows=D > 0)
+
+    check("rank n=%d first" % n)
+    idx = rng.integers(0, first, 2000).astype(np.int64)
+    td = rng.standard_normal(2000).astype(np.float32)
+    o.update(idx, td)
+    g.update(dev(idx), dev(td))
+    check("rank n=%d after update" % n)
+    if size > first:
+        intake(size - first, None)
+        check("rank n=%d after intake" % n)
+
+
 def test_intake_at_extreme_running_max():
     """Intake at the running max after that max was driven to 3e38: the
     interior subtrees of each run overflow to +inf, which the pairwise adds
