@@ -204,6 +204,10 @@ def algorithmic_bytes(spec: dict) -> dict:
     sample = B * (4 + 8 * L + 8)                     # mass in, L sibling pairs, index out
     if spec.get("masses") == "philox":
         sample -= B * 4                              # masses made on the device
+    if spec.get("rank"):
+        # ranking: priorities read, ranking written (4 + 4 bytes a slot); the
+        # rank-weight descent as the proportional one, plus the order lookup
+        sample += 8 * n + 4 * B
     if spec.get("uniform"):
         sample = B * 8                               # index out; no tree walk, no weight
     elif spec["weights"]:
@@ -268,6 +272,9 @@ def main():
                          "the device (per_sample_philox)")
     ap.add_argument("--uniform", action="store_true",
                     help="prioritisation off: per_sample_uniform, no priority update")
+    ap.add_argument("--rank", action="store_true",
+                    help="rank-based prioritisation: every step refreshes the ranking "
+                         "(per_rank_refresh) and samples with per_sample_rank")
     ap.add_argument("--graph-steps", type=int, default=64,
                     help="whole steps captured as one HIP graph for the labelled replay "
                          "figure (even; 0 skips it)")
@@ -295,10 +302,12 @@ def main():
     if args.padded:
         if D == 0 or args.padded < D:
             raise SystemExit("--padded needs a workload with rows and STRIDE >= state_dim")
-        if args.uniform or args.masses != "array":
+        if args.uniform or args.masses != "array" or args.rank:
             raise SystemExit("--padded goes with array masses and proportional sampling")
+    if args.rank and (args.uniform or args.masses != "array"):
+        raise SystemExit("--rank goes with array masses")
         spec = dict(spec, out_stride=args.padded)
-    spec = dict(spec, masses=args.masses, uniform=args.uniform)
+    spec = dict(spec, masses=args.masses, uniform=args.uniform, rank=args.rank)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
@@ -352,8 +361,14 @@ def main():
     if args.uniform:
         out.pop("w", None)
 
+    if args.rank:
+        g.rank_attach()
+
     def do_sample(s, o):
-        if args.uniform:
+        if args.rank:
+            g.rank_refresh()
+            g.sample_rank(u_d[s], beta=spec["beta"], out=o)
+        elif args.uniform:
             g.sample_uniform(B, seed, s * B, out=o)
         elif args.masses == "philox":
             g.sample_philox(B, seed, s * B, beta=spec["beta"], out=o)
@@ -462,7 +477,8 @@ def main():
                    "intake": intake, "unique_updates": spec.get("unique", B),
                    "weights": spec["weights"], "parallelism": "single GPU",
                    "out_stride": W or D, "masses": args.masses,
-                   "sampling": "uniform" if args.uniform else "proportional"},
+                   "sampling": ("uniform" if args.uniform else
+                                ("rank" if args.rank else "proportional"))},
         "samples_per_s": B / (op_avg["sample"] * 1e-3),
         "updates_per_s": B / (op_avg["update"] * 1e-3) if "update" in op_avg else None,
         "op_ms_avg": op_avg,

@@ -56,9 +56,11 @@ __device__ __forceinline__ void tile_counts(TileSmem& sm, const uint32_t* k, int
   const int t = threadIdx.x;
 #pragma unroll
   for (int d = 0; d < kDigits; ++d) sm.cnt[d * kRankThreads + t] = 0u;
+  // Own column only, so no two threads touch one counter; LDS adds without a
+  // returned value issue back to back instead of as 16 dependent round trips.
 #pragma unroll
   for (int i = 0; i < kItems; ++i)
-    if (i < nvalid) sm.cnt[((k[i] >> shift) & (kDigits - 1)) * kRankThreads + t] += 1u;
+    if (i < nvalid) atomicAdd(&sm.cnt[((k[i] >> shift) & (kDigits - 1)) * kRankThreads + t], 1u);
   __syncthreads();
   // Thread t scans the 16 entries [16t, 16t + 16) (digit t / 16), then the
   // 16 segments of a digit (16 consecutive lanes of one wave) meet by shuffle.
@@ -115,13 +117,22 @@ __global__ void __launch_bounds__(kRankThreads) rank_hist_kernel(const uint32_t*
 
 // Exclusive scan of the m = 16 * ntiles histogram entries in place (one
 // block; digit-major order, so entry (d, tile) becomes the global position
-// of the tile's first item of digit d).
+// of the tile's first item of digit d).  m is a multiple of 16: a thread
+// owns 16-entry chunks, read and written as four 16-byte accesses each, all
+// of a chunk's loads issued together.
 __global__ void __launch_bounds__(1024) rank_scan_kernel(uint32_t* hist, uint32_t m) {
   __shared__ uint32_t wsum[16];
-  const uint32_t per = (m + 1023) / 1024;
-  const uint32_t lo = threadIdx.x * per, hi = min(lo + per, m);
+  const uint32_t nchunks = m / 16;
+  const uint32_t per = (nchunks + 1023) / 1024;  // chunks per thread
+  const uint32_t c0 = threadIdx.x * per, c1 = min(c0 + per, nchunks);
   uint32_t s = 0;
-  for (uint32_t i = lo; i < hi; ++i) s += hist[i];
+  for (uint32_t c = c0; c < c1; ++c) {
+    uint4 q[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) q[j] = reinterpret_cast<const uint4*>(hist)[4 * c + j];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s += q[j].x + q[j].y + q[j].z + q[j].w;
+  }
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   uint32_t inc = s;
 #pragma unroll
@@ -131,38 +142,74 @@ __global__ void __launch_bounds__(1024) rank_scan_kernel(uint32_t* hist, uint32_
   }
   if (lane == 63) wsum[w] = inc;
   __syncthreads();
-  uint32_t base = 0;
-  for (int k = 0; k < w; ++k) base += wsum[k];
-  uint32_t run = base + inc - s;
-  for (uint32_t i = lo; i < hi; ++i) {
-    const uint32_t c = hist[i];
-    hist[i] = run;
-    run += c;
+  uint32_t run = inc - s;
+  for (int k = 0; k < w; ++k) run += wsum[k];
+  for (uint32_t c = c0; c < c1; ++c) {
+    uint4 q[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) q[j] = reinterpret_cast<const uint4*>(hist)[4 * c + j];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint4 o;
+      o.x = run;
+      run += q[j].x;
+      o.y = run;
+      run += q[j].y;
+      o.z = run;
+      run += q[j].z;
+      o.w = run;
+      run += q[j].w;
+      reinterpret_cast<uint4*>(hist)[4 * c + j] = o;
+    }
   }
 }
 
-// Stable scatter of one pass: every thread writes its items in order, each
-// to the next position of its digit.
+// Stable scatter of one pass.  The tile is first put in digit order in LDS
+// (every thread places its items, in order, after the tile's earlier items
+// of the same digit), then written out with consecutive threads on
+// consecutive items, so that each digit's run of the tile goes to
+// consecutive addresses.
+struct ScatterSmem {
+  TileSmem tc;
+  uint32_t key[kTile];
+  uint32_t val[kTile];
+  uint32_t dbase[kDigits];  // tile-local start of each digit
+  uint32_t gbase[kDigits];  // global start of this tile's run of each digit
+};
+
 __global__ void __launch_bounds__(kRankThreads) rank_scatter_kernel(
     const uint32_t* keys, const uint32_t* vals, uint32_t count, int shift,
     const uint32_t* hist, uint32_t* keys_out, uint32_t* vals_out) {
-  __shared__ TileSmem sm;
+  __shared__ ScatterSmem sm;
   uint32_t k[kItems], v[kItems];
   const int nvalid = load_tile(keys, count, k);
   load_tile(vals, count, v);
-  tile_counts(sm, k, nvalid, shift);
+  tile_counts(sm.tc, k, nvalid, shift);
   const int t = threadIdx.x;
-#pragma unroll
-  for (int d = 0; d < kDigits; ++d)
-    sm.cnt[d * kRankThreads + t] += hist[d * gridDim.x + blockIdx.x];
+  if (t < kDigits) {
+    uint32_t b = 0;
+    for (int d = 0; d < t; ++d) b += sm.tc.tot[d];
+    sm.dbase[t] = b;
+    sm.gbase[t] = hist[t * gridDim.x + blockIdx.x];
+  }
+  __syncthreads();
 #pragma unroll
   for (int i = 0; i < kItems; ++i) {
     if (i < nvalid) {
       const uint32_t d = (k[i] >> shift) & (kDigits - 1);
-      const uint32_t pos = sm.cnt[d * kRankThreads + t]++;
-      keys_out[pos] = k[i];
-      vals_out[pos] = v[i];
+      const uint32_t pos = sm.dbase[d] + sm.tc.cnt[d * kRankThreads + t]++;
+      sm.key[pos] = k[i];
+      sm.val[pos] = v[i];
     }
+  }
+  __syncthreads();
+  const uint32_t tile_n = min(kTile, count - blockIdx.x * kTile);
+  for (uint32_t i = t; i < tile_n; i += kRankThreads) {
+    const uint32_t kk = sm.key[i];
+    const uint32_t d = (kk >> shift) & (kDigits - 1);
+    const uint32_t pos = sm.gbase[d] + (i - sm.dbase[d]);
+    keys_out[pos] = kk;
+    vals_out[pos] = sm.val[i];
   }
 }
 
