@@ -141,15 +141,19 @@ def measured_traffic(workload: str, op: str):
     return None if e is None else float(e["bytes"])
 
 
-def graph_replay(g, step, K: int, base: int, stream) -> dict:
-    """K whole steps captured as one HIP graph and replayed: the step time
-    without per-launch host work, a labelled extra figure next to the eager
-    headline.  The library's host state (running-max slot, overflow counter,
-    ring cursor) advances during the capture exactly as in eager steps; K is
-    even, so the running-max and overflow parities of a replay start where
-    the previous one left them, while the captured intakes rewrite the same
-    ring slots on every replay."""
+def graph_replay(g, step, K: int, base: int, stream, use_graph_mode: bool = True) -> dict:
+    """K whole steps captured as one HIP graph in the library's graph mode
+    and replayed: the step time without per-launch host work, a labelled
+    extra figure next to the eager headline.  In graph mode the intakes take
+    the ring cursor and size from the device, so every replay writes the
+    next slots as eager steps would; K is even, so each slot parity
+    (running max, overflow list, ring state) is flipped an even number of
+    times and a replay starts on the slots the capture started on.  The
+    rank-based step re-ranks from the host's filled size, which graph mode
+    refuses: it is captured in eager mode, valid while the ring is full (its
+    captured intakes rewrite the same slots on every replay)."""
     import torch
+    entered = False
     try:
         gr = torch.cuda.CUDAGraph()
         side = torch.cuda.Stream()
@@ -158,6 +162,9 @@ def graph_replay(g, step, K: int, base: int, stream) -> dict:
             step(base)  # warm the capture stream
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
+        if use_graph_mode:
+            g.graph_mode(True)
+            entered = True
         with torch.cuda.graph(gr):
             for s in range(K):
                 step(base + s)
@@ -172,9 +179,18 @@ def graph_replay(g, step, K: int, base: int, stream) -> dict:
             gr.replay()
         b.record(torch.cuda.current_stream())
         torch.cuda.synchronize()
-        return {"steps_per_graph": K, "replays": reps,
+        if entered:
+            entered = False
+            g.graph_mode(False)
+        mode = "graph mode, device ring state" if use_graph_mode else "eager mode, full ring"
+        return {"steps_per_graph": K, "replays": reps, "mode": mode,
                 "ms_per_step": a.elapsed_time(b) / (reps * K)}
     except Exception as e:  # capture not available: report instead of failing the line
+        if entered:
+            try:
+                g.graph_mode(False)
+            except Exception:
+                pass
         return {"error": "%s: %s" % (type(e).__name__, e)}
 
 
@@ -453,7 +469,7 @@ def main():
     kg = min(args.graph_steps, args.steps)  # inputs exist for K steps past base
     kg -= kg % 2
     if kg > 0:
-        graph = graph_replay(g, step, kg, base, stream)
+        graph = graph_replay(g, step, kg, base, stream, use_graph_mode=not args.rank)
 
     byts = algorithmic_bytes(spec)
     dom = max(op_avg, key=op_avg.get)

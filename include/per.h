@@ -252,6 +252,44 @@ int per_total(per_t* h, float* d_out, hipStream_t stream);
 int per_min(per_t* h, float* d_out, hipStream_t stream);
 int per_max_priority(per_t* h, float* d_out, hipStream_t stream);
 
+/*
+ * Graph mode ("True Single-Graph Implementation Plan", its goal and
+ * architecture: one graph launch per training step, with counters kept on
+ * the GPU instead of written by the host; "H100 GPU Pipeline Optimization
+ * Design", section 2, CUDA Graph for experience collection: a captured loop
+ * reads the replay buffer's changing size through the device; "GPU-Resident
+ * Prioritized Experience Replay", section "Approach": no CPU involvement per
+ * training step).
+ *
+ * per_graph_mode(h, 1, s) makes the calls that follow capturable and
+ * replayable: per_add, per_update and per_sample_uniform read the ring's
+ * cursor and filled size from the device control block (every per_add
+ * writes the next state there, in either mode), and every sampling call
+ * rebuilds the nodes above the partitions instead of trusting the host's
+ * record of whether they are current.  Nothing is enqueued and nothing waits.
+ *
+ * Replay rule: the device keeps the running max, the bucketed update's
+ * overflow list and the ring state in two slots each, and a call reads one
+ * slot and writes the other, chosen on the host when it is issued.  A
+ * captured sequence therefore replays correctly only if it flips each of
+ * these slot parities an even number of times, so that each replay starts
+ * on the slots the capture started on.  One training step (per_add with
+ * running-max priorities, a sample, per_update) flips the running-max and
+ * ring parities once each: capture two steps.  Random-number offsets of
+ * per_sample_philox / per_sample_uniform are fixed at capture time.
+ * per_rank_refresh fails in graph mode; per_size / per_cursor report the
+ * host's count of the calls issued, which replays do not advance.
+ *
+ * per_graph_mode(h, 0, s) leaves graph mode: it waits for stream s, copies
+ * the ring state back from the device (so per_size / per_cursor count every
+ * replay) and marks the top levels stale.  It returns PER_EINVAL if the
+ * calls issued in graph mode broke the replay rule (the handle has left
+ * graph mode all the same), and PER_EHIP if the copy fails.  Entering twice
+ * or leaving when not in graph mode is PER_EINVAL.  Never call it while s is
+ * being captured.
+ */
+int per_graph_mode(per_t* h, int32_t on, hipStream_t stream);
+
 /* Host-side state: number of written slots, next slot to write, capacity,
  * floats per state row.  -1 for a NULL handle. */
 int64_t per_size(const per_t* h);

@@ -1,6 +1,6 @@
 // per_api.hip -- the C ABI declared in include/per.h: argument checks,
 // workspace layout, handle state and kernel launches.  Nothing here
-// allocates device memory or waits for the device.
+// allocates device memory, and only leaving graph mode waits for the device.
 
 #include <stdarg.h>
 #include <stdio.h>
@@ -23,7 +23,10 @@ struct per_s {
   int64_t size, cursor;
   int epoch;       // committed running-max slot
   int ovf;         // overflow counter for the next bucketed update
+  int ring;        // control-block slot holding the current ring state
   bool top_stale;  // nodes above the partitions not yet rebuilt
+  bool graph;      // graph mode: ring state read on the device, top always rebuilt
+  int entry_epoch, entry_ovf, entry_ring;  // parities when graph mode was entered
   int device;
   // rank-based prioritisation (after per_rank_attach)
   bool rank_attached;
@@ -59,6 +62,13 @@ int hip_fail(hipError_t e, const char* what) {
 }
 
 bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+// Ring state for a launch: the host's copy, or (graph mode) the device's.
+per::RingRef ring_ref(const per_s* h) { return per::RingRef{h->graph ? 1 : 0, h->ring}; }
+
+// Graph mode always rebuilds the nodes above the partitions: a replay cannot
+// know what ran before it.
+bool top_may_be_stale(const per_s* h) { return h->top_stale || (h->graph && h->g.P > 0); }
 
 int log2i(int64_t v) {
   int l = 0;
@@ -191,7 +201,9 @@ int per_create(per_t** out, int64_t capacity, int32_t state_dim, int64_t max_bat
   h->cursor = 0;
   h->epoch = 0;
   h->ovf = 0;
+  h->ring = 0;
   h->top_stale = false;
+  h->graph = false;
   h->rank_attached = false;
   h->rank_size = 0;
   h->rank_built = -1;
@@ -226,11 +238,12 @@ int per_add(per_t* h, int64_t count, const float* d_states, const float* d_next_
       return fail(PER_EINVAL, "state rows must be 16-byte aligned");
   }
   const int src = h->epoch, dst = d_prio ? (h->epoch ^ 1) : h->epoch;
-  hipError_t e = per::launch_add(h->t, h->g, h->st, (uint32_t)h->cursor, (uint32_t)count,
-                                 d_states, d_next_states, d_actions, d_rewards, d_dones,
-                                 d_prio, src, dst, stream);
+  hipError_t e = per::launch_add(h->t, h->g, h->st, ring_ref(h), (uint32_t)h->size,
+                                 (uint32_t)h->cursor, (uint32_t)count, d_states, d_next_states,
+                                 d_actions, d_rewards, d_dones, d_prio, src, dst, stream);
   if (e != hipSuccess) return hip_fail(e, "per_add");
   h->epoch = dst;
+  h->ring ^= 1;
   h->top_stale = h->g.P > 0;
   h->cursor = (h->cursor + count) % (int64_t)h->g.n;
   h->size = (h->size + count < (int64_t)h->g.n) ? h->size + count : (int64_t)h->g.n;
@@ -245,8 +258,9 @@ int per_update(per_t* h, int64_t B, const int64_t* d_idx, const float* d_td,
                 (long long)h->max_batch);
   if (B == 0) return ok();
   if (!d_idx || !d_td) return fail(PER_EINVAL, "idx and td are required");
-  hipError_t e = per::launch_update(h->t, h->bk, h->g, (uint32_t)h->size, B, d_idx, d_td,
-                                    h->alpha, h->eps, h->epoch, h->epoch ^ 1, h->ovf, stream);
+  hipError_t e = per::launch_update(h->t, h->bk, h->g, ring_ref(h), (uint32_t)h->size, B, d_idx,
+                                    d_td, h->alpha, h->eps, h->epoch, h->epoch ^ 1, h->ovf,
+                                    stream);
   if (e != hipSuccess) return hip_fail(e, "per_update");
   h->epoch ^= 1;
   if (per::update_uses_buckets(h->g, B)) h->ovf ^= 1;
@@ -299,14 +313,16 @@ int sample_impl(per_t* h, int64_t B, SampleKind kind, const float* d_u, uint64_t
     return e == hipSuccess ? ok() : hip_fail(e, what);
   }
   if (kind == kUniform) {
-    hipError_t e = per::launch_uniform(h->st, (uint32_t)h->size, B, seed, offset, d_idx_out,
-                                       any_rows ? d_states_out : nullptr, d_next_states_out,
+    hipError_t e = per::launch_uniform(h->st, h->t.ctrl, ring_ref(h), (uint32_t)h->size, B, seed,
+                                       offset, d_idx_out, any_rows ? d_states_out : nullptr,
+                                       d_next_states_out,
                                        d_actions_out, d_rewards_out, d_dones_out,
                                        (uint32_t)out_stride, dones_f32, stream);
     return e == hipSuccess ? ok() : hip_fail(e, what);
   }
   const per::SamplePlan plan = per::make_sample_plan(h->g, B);
-  if (h->top_stale && plan.top_mode != per::kTopRebuild) {  // the sampler will not rebuild the top itself
+  const bool stale = top_may_be_stale(h);
+  if (stale && plan.top_mode != per::kTopRebuild) {  // the sampler will not rebuild the top itself
     hipError_t e = per::launch_top(h->t, h->g, stream);
     if (e != hipSuccess) return hip_fail(e, "per_sample: top rebuild");
     h->top_stale = false;
@@ -315,8 +331,7 @@ int sample_impl(per_t* h, int64_t B, SampleKind kind, const float* d_u, uint64_t
                                     kind == kGivenMasses ? d_u : nullptr, seed, offset, beta,
                                     d_idx_out, d_w_out, any_rows ? d_states_out : nullptr,
                                     d_next_states_out, d_actions_out, d_rewards_out,
-                                    d_dones_out, (uint32_t)out_stride, dones_f32, h->top_stale,
-                                    stream);
+                                    d_dones_out, (uint32_t)out_stride, dones_f32, stale, stream);
   if (e != hipSuccess) return hip_fail(e, what);
   h->top_stale = false;
   return ok();
@@ -370,7 +385,7 @@ static int copy_scalar(per_t* h, const void* src, float* d_out, hipStream_t stre
 
 int per_flush(per_t* h, hipStream_t stream) {
   if (!h) return fail(PER_EINVAL, "handle is NULL");
-  if (h->top_stale) {
+  if (top_may_be_stale(h)) {
     hipError_t e = per::launch_top(h->t, h->g, stream);
     if (e != hipSuccess) return hip_fail(e, "per_flush");
     h->top_stale = false;
@@ -395,6 +410,34 @@ int per_min(per_t* h, float* d_out, hipStream_t stream) {
 int per_max_priority(per_t* h, float* d_out, hipStream_t stream) {
   if (!h || !d_out) return fail(PER_EINVAL, "NULL argument");
   return copy_scalar(h, &h->t.ctrl->maxp_bits[h->epoch], d_out, stream, "per_max_priority");
+}
+
+int per_graph_mode(per_t* h, int32_t on, hipStream_t stream) {
+  if (!h) return fail(PER_EINVAL, "handle is NULL");
+  if (on) {
+    if (h->graph) return fail(PER_EINVAL, "already in graph mode");
+    h->graph = true;
+    h->entry_epoch = h->epoch;
+    h->entry_ovf = h->ovf;
+    h->entry_ring = h->ring;
+    return ok();
+  }
+  if (!h->graph) return fail(PER_EINVAL, "not in graph mode");
+  // Replays have moved the ring on the device: take its state back.
+  per::Ctrl c;
+  hipError_t e = hipMemcpyAsync(&c, h->t.ctrl, sizeof c, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "per_graph_mode: ring state");
+  h->cursor = c.cursor[h->ring];
+  h->size = c.size[h->ring];
+  h->graph = false;
+  h->top_stale = h->g.P > 0;
+  if (h->epoch != h->entry_epoch || h->ovf != h->entry_ovf || h->ring != h->entry_ring)
+    return fail(PER_EINVAL,
+                "the calls made in graph mode flip a slot parity an odd number of times "
+                "(running max %d, overflow %d, ring %d): replaying them reads stale slots",
+                h->epoch ^ h->entry_epoch, h->ovf ^ h->entry_ovf, h->ring ^ h->entry_ring);
+  return ok();
 }
 
 int64_t per_size(const per_t* h) { return h ? h->size : -1; }
@@ -461,6 +504,7 @@ int per_rank_attach(per_t* h, void* d_ws, size_t ws_bytes) {
 
 int per_rank_refresh(per_t* h, hipStream_t stream) {
   if (!h) return fail(PER_EINVAL, "handle is NULL");
+  if (h->graph) return fail(PER_EINVAL, "per_rank_refresh needs the ring size: leave graph mode");
   if (!h->rank_attached) return fail(PER_EINVAL, "no rank workspace: call per_rank_attach");
   if (h->size == 0) return fail(PER_EEMPTY, "ranking an empty buffer");
   hipError_t e = per::launch_rank_sort(h->t.sum + h->g.n, (uint32_t)h->size, h->rkeys, h->rvals,

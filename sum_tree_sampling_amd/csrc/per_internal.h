@@ -23,10 +23,24 @@ constexpr int kTreeThreads = 256;
 // Device control block at the start of the workspace's control area.
 // The running max priority is kept in two slots (f32 bit patterns, raised
 // with atomicMax): a call that may raise it reads the committed slot and
-// raises the other, and the host then commits the other slot.
+// raises the other, and the host then commits the other slot.  The ring
+// state (cursor, size) is kept the same way: every intake reads slot r and
+// writes the next state to slot r ^ 1, and the host flips r.  In graph mode
+// the kernels take the ring state from these slots instead of from their
+// launch arguments, so that a captured sequence of calls replays with the
+// state of the replay, not of the capture.
 struct Ctrl {
   uint32_t maxp_bits[2];
+  uint32_t cursor[2];
+  uint32_t size[2];
   uint32_t pad[2];
+};
+
+// Where a kernel takes the ring state from: its arguments (dev == 0), or
+// slot `slot` of the control block (dev != 0, graph mode).
+struct RingRef {
+  int dev;
+  int slot;
 };
 
 // Geometry shared by host and kernels.
@@ -91,19 +105,23 @@ hipError_t launch_init(const TreePtrs& t, const Buckets& bk, const Geom& g, hipS
 // Batched update; B > 0.  src / dst: running-max slots to read / raise.
 // ovf: overflow counter of this call when the batch is bucketed (see
 // update_uses_buckets); alternate calls must alternate it.
-hipError_t launch_update(const TreePtrs& t, const Buckets& bk, const Geom& g, uint32_t size,
-                         int64_t B, const int64_t* idx, const float* td, double alpha,
-                         double eps, int src, int dst, int ovf, hipStream_t s);
+// The filled size bounds the accepted indices: size, or ctrl->size[ring.slot]
+// when ring.dev.
+hipError_t launch_update(const TreePtrs& t, const Buckets& bk, const Geom& g, RingRef ring,
+                         uint32_t size, int64_t B, const int64_t* idx, const float* td,
+                         double alpha, double eps, int src, int dst, int ovf, hipStream_t s);
 bool update_uses_buckets(const Geom& g, int64_t B);
 
 // Rebuild of the nodes above the partitions (one block).
 hipError_t launch_top(const TreePtrs& t, const Geom& g, hipStream_t s);
 
-// Ring intake of count > 0 items at cursor.
-hipError_t launch_add(const TreePtrs& t, const Geom& g, const Storage& st, uint32_t cursor,
-                      uint32_t count, const float* states, const float* next_states,
-                      const uint32_t* actions, const float* rewards, const uint8_t* dones,
-                      const float* prio, int src, int dst, hipStream_t s);
+// Ring intake of count > 0 items at cursor into a ring holding size items
+// (both read from ctrl slot ring.slot instead when ring.dev).  Either way the
+// ring state after the intake is written to ctrl slot ring.slot ^ 1.
+hipError_t launch_add(const TreePtrs& t, const Geom& g, const Storage& st, RingRef ring,
+                      uint32_t size, uint32_t cursor, uint32_t count, const float* states,
+                      const float* next_states, const uint32_t* actions, const float* rewards,
+                      const uint8_t* dones, const float* prio, int src, int dst, hipStream_t s);
 
 hipError_t launch_sample(const TreePtrs& t, const Geom& g, const Storage& st,
                          const SamplePlan& plan, uint32_t size, int64_t B, const float* u,
@@ -125,9 +143,10 @@ hipError_t launch_rank_build(const TreePtrs& rt, const Geom& g, uint32_t count, 
                              hipStream_t s);
 uint32_t rank_tiles(int64_t n);
 
-// Uniform sample of B slots over [0, size) from the generator stream.
-hipError_t launch_uniform(const Storage& st, uint32_t size, int64_t B, uint64_t seed,
-                          uint64_t offset, int64_t* idx_out, float* states_out, float* next_out,
+// Uniform sample of B slots over [0, size) from the generator stream (size
+// read from ctrl slot ring.slot when ring.dev).
+hipError_t launch_uniform(const Storage& st, const Ctrl* ctrl, RingRef ring, uint32_t size,
+                          int64_t B, uint64_t seed, uint64_t offset, int64_t* idx_out, float* states_out, float* next_out,
                           uint32_t* actions_out, float* rewards_out, void* dones_out,
                           uint32_t out_stride, bool dones_f32, hipStream_t s);
 

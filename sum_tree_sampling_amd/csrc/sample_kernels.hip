@@ -44,6 +44,7 @@ struct SampleArgs {
   float* mn;
   uint32_t n;
   uint32_t size;
+  const uint32_t* dev_size;  // uniform mode in graph mode: the filled size, read on the device
   uint32_t B;
   const uint32_t* order;  // rank-based: the slot of each leaf (rank), or NULL
   const float* u;       // masses, or NULL: from the generator stream
@@ -493,8 +494,9 @@ __global__ void __launch_bounds__(kSampleThreads) uniform_kernel(SampleArgs a) {
   const int lane = threadIdx.x & 63;
   const uint32_t wave = blockIdx.x * (kSampleThreads / 64) + (threadIdx.x >> 6);
   const uint32_t b = wave * SPW + (uint32_t)(lane / G);
+  const uint32_t size = a.dev_size ? *a.dev_size : a.size;
   const uint64_t hi = stream_word(a.seed, a.offset + b) >> 32;
-  const uint32_t slot = (uint32_t)((hi * (uint64_t)a.size) >> 32);
+  const uint32_t slot = (uint32_t)((hi * (uint64_t)size) >> 32);
   emit<G, SPW>(a, wave, lane, b, b < a.B && (lane & (G - 1)) == 0, slot, 0.0f, 0.0f);
 }
 
@@ -594,12 +596,14 @@ hipError_t launch_sample(const TreePtrs& t, const Geom& g, const Storage& st,
   }
 }
 
-hipError_t launch_uniform(const Storage& st, uint32_t size, int64_t B, uint64_t seed,
-                          uint64_t offset, int64_t* idx_out, float* states_out, float* next_out,
-                          uint32_t* actions_out, float* rewards_out, void* dones_out,
-                          uint32_t out_stride, bool dones_f32, hipStream_t s) {
+hipError_t launch_uniform(const Storage& st, const Ctrl* ctrl, RingRef ring, uint32_t size,
+                          int64_t B, uint64_t seed, uint64_t offset, int64_t* idx_out,
+                          float* states_out, float* next_out, uint32_t* actions_out,
+                          float* rewards_out, void* dones_out, uint32_t out_stride,
+                          bool dones_f32, hipStream_t s) {
   SampleArgs a{};
   a.size = size;
+  a.dev_size = ring.dev ? &ctrl->size[ring.slot] : nullptr;
   a.B = (uint32_t)B;
   a.seed = seed;
   a.offset = offset;

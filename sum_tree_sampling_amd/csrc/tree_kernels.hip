@@ -607,6 +607,10 @@ __global__ void __launch_bounds__(256) init_kernel(TreePtrs t, Buckets bk, Geom 
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     t.ctrl->maxp_bits[0] = __float_as_uint(1.0f);
     t.ctrl->maxp_bits[1] = __float_as_uint(1.0f);
+    for (int k = 0; k < 2; ++k) {
+      t.ctrl->cursor[k] = 0u;
+      t.ctrl->size[k] = 0u;
+    }
     bk.ovf_n[0] = 0u;
     bk.ovf_n[1] = 0u;
   }
@@ -616,12 +620,18 @@ struct UpdateArgs {
   const int64_t* idx;
   const float* td;
   uint32_t B;
-  uint32_t size;
+  uint32_t size;  // filled slots (host-tracked; see ring)
   double alpha, eps;
   float p_nan;
   int src, dst;  // running-max slots: read / raise
   int ovf;       // overflow counter of this call (bucketed path)
+  RingRef ring;  // graph mode: the size comes from ring_ctrl->size[ring.slot]
+  const Ctrl* ring_ctrl;
 };
+
+__device__ __forceinline__ uint32_t filled_size(const UpdateArgs& a) {
+  return a.ring.dev ? a.ring_ctrl->size[a.ring.slot] : a.size;
+}
 
 // Small batches: each block owns PPB consecutive partitions and scans the
 // whole batch for their slots; wave w repairs partition w of the block when
@@ -633,6 +643,7 @@ __global__ void __launch_bounds__(kUpdThreads) update_scan_kernel(TreePtrs t, Ge
   const int nparts = (int)min((uint32_t)PPB, (1u << g.P) - part0);
   const float m0 = __uint_as_float(t.ctrl->maxp_bits[a.src]);
   uint32_t* max_dst = &t.ctrl->maxp_bits[a.dst];
+  const uint32_t size = filled_size(a);
   if (threadIdx.x < PPB) sm.count[threadIdx.x] = 0;
   if (threadIdx.x == 0) sm.bmax = 0u;
   __syncthreads();
@@ -658,7 +669,7 @@ __global__ void __launch_bounds__(kUpdThreads) update_scan_kernel(TreePtrs t, Ge
     for (int c = 0; c < kChunk; ++c) {
       const uint32_t b = b0 + c * kUpdThreads + threadIdx.x;
       const int64_t i = ix[c];
-      if (i < 0 || i >= (int64_t)a.size) continue;
+      if (i < 0 || i >= (int64_t)size) continue;
       const uint32_t q = (uint32_t)((uint64_t)i >> g.S) - part0;  // wraps below part0
       if (q < (uint32_t)nparts) {
         const uint32_t part = part0 + q;
@@ -688,7 +699,7 @@ __global__ void __launch_bounds__(kUpdThreads) update_scan_kernel(TreePtrs t, Ge
     dense_update<kUpdThreads>(sm.u.dn, sm.flag, sm.sx, t, g, part, [&](auto f) {
       for (uint32_t b = threadIdx.x; b < a.B; b += kUpdThreads) {
         const int64_t i = a.idx[b];
-        if (i >= 0 && i < (int64_t)a.size && ((uint64_t)i >> g.S) == part)
+        if (i >= 0 && i < (int64_t)size && ((uint64_t)i >> g.S) == part)
           f((uint32_t)i - base, b, priority_of(a.td[b], m0, a.alpha, a.eps, a.p_nan));
       }
     });
@@ -702,7 +713,7 @@ __global__ void __launch_bounds__(256) bucket_kernel(Buckets bk, Geom g, UpdateA
   if (b >= a.B) return;
   const int64_t i = a.idx[b];
   const float x = a.td[b];
-  if (i < 0 || i >= (int64_t)a.size) return;
+  if (i < 0 || i >= (int64_t)filled_size(a)) return;
   const uint32_t part = (uint32_t)((uint64_t)i >> g.S);
   const uint32_t k = atomicAdd(&bk.counts[part], 1u);
   if (k < kBucketCap) {
@@ -786,12 +797,42 @@ __global__ void __launch_bounds__(kUpdThreads) update_bucket_kernel(TreePtrs t, 
   }
 }
 
+// Partitions touched by the ring range [cursor, cursor + count): one run,
+// or two when the range wraps past the end and the runs stay apart.
+struct TouchedRuns {
+  uint32_t first[2], len[2];
+};
+
+__host__ __device__ inline TouchedRuns touched_runs(uint32_t cursor, uint32_t count,
+                                                    const Geom& g) {
+  const uint64_t end = (uint64_t)cursor + count;
+  const uint32_t hi0 = (uint32_t)(end < g.n ? end : g.n);
+  uint32_t f0 = cursor >> g.S, l0 = (hi0 - 1) >> g.S;  // inclusive
+  uint32_t l1 = 0;
+  bool second = end > g.n;
+  if (second) {
+    l1 = (uint32_t)(end - g.n - 1) >> g.S;
+    if (l1 + 1 >= f0) {  // the two runs meet or overlap: one run over every partition
+      f0 = 0;
+      l0 = (1u << g.P) - 1;
+      second = false;
+    }
+  }
+  TouchedRuns r;
+  r.first[0] = f0;
+  r.len[0] = l0 - f0 + 1;
+  r.first[1] = 0;
+  r.len[1] = second ? l1 + 1 : 0;
+  return r;
+}
+
 struct AddArgs {
-  uint32_t cursor, count;
+  uint32_t cursor, count;  // cursor: host-tracked, unless ring.dev
+  uint32_t size;           // filled slots before the intake: host-tracked, unless ring.dev
+  RingRef ring;            // ring.dev: cursor and size come from ctrl slot ring.slot
   const float* prio;
-  uint32_t run_first[2], run_len[2];  // touched partitions: two disjoint runs
-  uint32_t ntree;                     // blocks doing tree work (the rest copy rows)
-  int src, dst;                       // running-max slots: read / raise
+  uint32_t ntree;  // blocks set aside for tree work (the rest copy rows)
+  int src, dst;    // running-max slots: read / raise
   const float* states;
   const float* next_states;
   const uint32_t* actions;
@@ -804,6 +845,21 @@ struct AddArgs {
 // max priority; rows are copied by the blocks past the tree blocks.
 __global__ void __launch_bounds__(256) add_kernel(TreePtrs t, Geom g, Storage st, AddArgs a) {
   __shared__ AddSmem sm;
+  uint32_t cursor = a.cursor, size = a.size;
+  if (a.ring.dev) {
+    cursor = t.ctrl->cursor[a.ring.slot];
+    size = t.ctrl->size[a.ring.slot];
+  }
+  // The ring state after this intake goes to the other slot, so that no
+  // block of this launch reads a value another block has changed.  The last
+  // block writes it: a row-copy block whenever rows are kept, which has no
+  // barrier to wait on the store.
+  if (blockIdx.x == gridDim.x - 1 && threadIdx.x == 0) {
+    const uint64_t next = (uint64_t)cursor + a.count;
+    const uint64_t filled = (uint64_t)size + a.count;
+    t.ctrl->cursor[a.ring.slot ^ 1] = (uint32_t)(next >= g.n ? next - g.n : next);
+    t.ctrl->size[a.ring.slot ^ 1] = (uint32_t)(filled < g.n ? filled : g.n);
+  }
   if (blockIdx.x >= a.ntree) {
     // Row copy of the transitions into their ring slots.
     const uint32_t nb = gridDim.x - a.ntree;
@@ -815,7 +871,7 @@ __global__ void __launch_bounds__(256) add_kernel(TreePtrs t, Geom g, Storage st
       const uint64_t total = (uint64_t)a.count * c4;
       for (uint64_t e = tid; e < total; e += stride) {
         const uint32_t j = (uint32_t)(e / c4), c = (uint32_t)(e % c4);
-        uint32_t slot = a.cursor + j;
+        uint32_t slot = cursor + j;
         if (slot >= g.n) slot -= g.n;
         const uint64_t so = (uint64_t)j * D + 4u * c, dof = (uint64_t)slot * D + 4u * c;
         *reinterpret_cast<float4*>(st.states + dof) =
@@ -827,14 +883,14 @@ __global__ void __launch_bounds__(256) add_kernel(TreePtrs t, Geom g, Storage st
       const uint64_t total = (uint64_t)a.count * D;
       for (uint64_t e = tid; e < total; e += stride) {
         const uint32_t j = (uint32_t)(e / D), c = (uint32_t)(e % D);
-        uint32_t slot = a.cursor + j;
+        uint32_t slot = cursor + j;
         if (slot >= g.n) slot -= g.n;
         st.states[(uint64_t)slot * D + c] = a.states[e];
         st.next_states[(uint64_t)slot * D + c] = a.next_states[e];
       }
     }
     for (uint32_t j = tid; j < a.count; j += stride) {
-      uint32_t slot = a.cursor + j;
+      uint32_t slot = cursor + j;
       if (slot >= g.n) slot -= g.n;
       st.actions[slot] = a.actions[j];
       st.rewards[slot] = a.rewards[j];
@@ -843,14 +899,15 @@ __global__ void __launch_bounds__(256) add_kernel(TreePtrs t, Geom g, Storage st
     return;
   }
   const uint32_t w = blockIdx.x;
-  const uint32_t part =
-      (w < a.run_len[0]) ? a.run_first[0] + w : a.run_first[1] + (w - a.run_len[0]);
+  const TouchedRuns tr = touched_runs(cursor, a.count, g);
+  if (w >= tr.len[0] + tr.len[1]) return;  // spare block of a worst-case grid
+  const uint32_t part = (w < tr.len[0]) ? tr.first[0] + w : tr.first[1] + (w - tr.len[0]);
   const uint32_t span = 1u << g.S;
   const uint32_t base = part << g.S;
   // The ring range [cursor, cursor + count) split at the wrap, clipped to
   // this partition: one or two runs of offsets.
-  const uint64_t end = (uint64_t)a.cursor + a.count;
-  const uint32_t r_lo[2] = {a.cursor, 0u};
+  const uint64_t end = (uint64_t)cursor + a.count;
+  const uint32_t r_lo[2] = {cursor, 0u};
   const uint32_t r_hi[2] = {(uint32_t)(end < g.n ? end : g.n),
                             (uint32_t)(end > g.n ? end - g.n : 0u)};
   uint32_t lo[2], hi[2];
@@ -876,7 +933,7 @@ __global__ void __launch_bounds__(256) add_kernel(TreePtrs t, Geom g, Storage st
   const float m0 = __uint_as_float(t.ctrl->maxp_bits[a.src]);
   auto value_of = [&](uint32_t off) -> float {
     const uint32_t slot = base + off;
-    const uint32_t j = (slot >= a.cursor) ? slot - a.cursor : slot + (g.n - a.cursor);
+    const uint32_t j = (slot >= cursor) ? slot - cursor : slot + (g.n - cursor);
     return a.prio ? a.prio[j] + 0.0f : m0;
   };
   uint32_t mb = 0;
@@ -977,10 +1034,12 @@ bool update_uses_buckets(const Geom& g, int64_t B) {
   return np * (uint64_t)B > (1ull << 20);
 }
 
-hipError_t launch_update(const TreePtrs& t, const Buckets& bk, const Geom& g, uint32_t size,
-                         int64_t B, const int64_t* idx, const float* td, double alpha,
-                         double eps, int src, int dst, int ovf, hipStream_t s) {
+hipError_t launch_update(const TreePtrs& t, const Buckets& bk, const Geom& g, RingRef ring,
+                         uint32_t size, int64_t B, const int64_t* idx, const float* td,
+                         double alpha, double eps, int src, int dst, int ovf, hipStream_t s) {
   UpdateArgs a;
+  a.ring = ring;
+  a.ring_ctrl = t.ctrl;
   a.idx = idx;
   a.td = td;
   a.B = (uint32_t)B;
@@ -1013,13 +1072,15 @@ hipError_t launch_update(const TreePtrs& t, const Buckets& bk, const Geom& g, ui
   return hipGetLastError();
 }
 
-hipError_t launch_add(const TreePtrs& t, const Geom& g, const Storage& st, uint32_t cursor,
-                      uint32_t count, const float* states, const float* next_states,
-                      const uint32_t* actions, const float* rewards, const uint8_t* dones,
-                      const float* prio, int src, int dst, hipStream_t s) {
+hipError_t launch_add(const TreePtrs& t, const Geom& g, const Storage& st, RingRef ring,
+                      uint32_t size, uint32_t cursor, uint32_t count, const float* states,
+                      const float* next_states, const uint32_t* actions, const float* rewards,
+                      const uint8_t* dones, const float* prio, int src, int dst, hipStream_t s) {
   AddArgs a;
   a.cursor = cursor;
   a.count = count;
+  a.size = size;
+  a.ring = ring;
   a.prio = prio;
   a.src = src;
   a.dst = dst;
@@ -1028,25 +1089,17 @@ hipError_t launch_add(const TreePtrs& t, const Geom& g, const Storage& st, uint3
   a.actions = actions;
   a.rewards = rewards;
   a.dones = dones;
-  // Touched partitions of [cursor, cursor+count) and, past the wrap, [0, end-n).
-  const uint64_t end = (uint64_t)cursor + count;
-  const uint32_t hi0 = (uint32_t)(end < g.n ? end : g.n);
-  uint32_t f0 = cursor >> g.S, l0 = (hi0 - 1) >> g.S;  // inclusive
-  uint32_t f1 = 0, l1 = 0;
-  bool second = end > g.n;
-  if (second) {
-    l1 = (uint32_t)(end - g.n - 1) >> g.S;
-    if (l1 + 1 >= f0) {  // the two runs meet or overlap: one run over every partition
-      f0 = 0;
-      l0 = (1u << g.P) - 1;
-      second = false;
-    }
+  const uint32_t np = 1u << g.P;
+  if (ring.dev) {
+    // The cursor is known only on the device: enough tree blocks for any
+    // placement of count slots (a cyclic range of c slots meets at most
+    // c / span + 2 partitions); the spare ones return at once.
+    const uint64_t worst = ((uint64_t)count >> g.S) + 2;
+    a.ntree = worst < np ? (uint32_t)worst : np;
+  } else {
+    const TouchedRuns tr = touched_runs(cursor, count, g);
+    a.ntree = tr.len[0] + tr.len[1];
   }
-  a.run_first[0] = f0;
-  a.run_len[0] = l0 - f0 + 1;
-  a.run_first[1] = second ? f1 : 0;
-  a.run_len[1] = second ? (l1 - f1 + 1) : 0;
-  a.ntree = a.run_len[0] + a.run_len[1];
   unsigned ncopy = 0;
   if (st.D > 0)
     ncopy = grid_for((uint64_t)count * (uint64_t)st.D / 4 + count, kTreeThreads * 4, 2048);

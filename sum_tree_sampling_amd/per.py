@@ -58,6 +58,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
         "per_rank_ptrs": (c_int, [vp, ctypes.POINTER(vp), ctypes.POINTER(vp),
                                   ctypes.POINTER(vp)]),
         "per_flush": (c_int, [vp, vp]),
+        "per_graph_mode": (c_int, [vp, i32, vp]),
         "per_total": (c_int, [vp, vp, vp]),
         "per_min": (c_int, [vp, vp, vp]),
         "per_max_priority": (c_int, [vp, vp, vp]),
@@ -202,6 +203,10 @@ def per_flush(h, stream=None) -> None:
     _check(load().per_flush(h, _stream(stream)))
 
 
+def per_graph_mode(h, on, stream=None) -> None:
+    _check(load().per_graph_mode(h, 1 if on else 0, _stream(stream)))
+
+
 def per_total(h, out, stream=None) -> None:
     _check(load().per_total(h, _p(out), _stream(stream)))
 
@@ -290,6 +295,11 @@ class PerBuffer:
     @property
     def cursor(self) -> int:
         return per_cursor(self.h)
+
+    def graph_mode(self, on: bool, stream=None) -> None:
+        """Enter / leave graph mode (per_graph_mode): calls issued in it may
+        be captured and replayed; leaving waits for the stream."""
+        per_graph_mode(self.h, on, stream)
 
     def sum_tree(self, stream=None) -> torch.Tensor:
         """Device view of the [2n] sum tree (index 0 unused), flushed first."""

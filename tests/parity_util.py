@@ -42,12 +42,16 @@ def assert_bits_equal(got: np.ndarray, exp: np.ndarray, what: str):
             what, bad.size, g.size, bad[:8].tolist(), g[bad[:8]].tolist(), e[bad[:8]].tolist()))
 
 
-def compare_trees(o: Oracle, g, what: str):
+def compare_trees(o: Oracle, g, what: str, ring: bool = True):
+    """Both trees and the running max bit for bit; the host's ring state too
+    unless ring is False (in graph mode it counts issued calls, not replays)."""
     n = o.capacity
     torch.cuda.synchronize()
     assert_bits_equal(host(g.sum_tree())[1:2 * n], o.sum_tree()[1:], what + " sum tree")
     assert_bits_equal(host(g.min_tree())[1:2 * n], o.min_tree()[1:], what + " min tree")
-    assert g.size == o.size and g.cursor == o.cursor, (what, g.size, o.size, g.cursor, o.cursor)
+    if ring:
+        assert g.size == o.size and g.cursor == o.cursor, (what, g.size, o.size, g.cursor,
+                                                           o.cursor)
     mp = host(g.scalar("max_priority"))[0]
     assert np.float32(mp).view(np.uint32) == np.float32(o.max_priority).view(np.uint32), \
         (what, mp, o.max_priority)

@@ -421,6 +421,140 @@ def test_top_deeper_than_lds():
         compare_trees(o, g, "2^25 step %d" % step)
 
 
+# ------------------------------------------------------------ graph mode
+
+def _rows_np(rng, c, D):
+    if D == 0:
+        return ()
+    return (rng.standard_normal((c, D)).astype(np.float32),
+            rng.standard_normal((c, D)).astype(np.float32),
+            rng.integers(0, 3, c).astype(np.uint32),
+            rng.standard_normal(c).astype(np.float32),
+            (rng.random(c) < 0.2).astype(np.uint8))
+
+
+@pytest.mark.parametrize("n,D,B,c,prio,uniform", [
+    (1 << 12, 8, 256, 300, False, False),   # one partition; the ring wraps every few replays
+    (1 << 16, 5, 1024, 3000, True, False),  # given priorities; scalar row copies
+    (1 << 20, 0, 8192, 5000, False, False),  # bucketed update: the overflow parity flips too
+    (1 << 13, 4, 500, 700, False, True),    # uniform sample over a ring still filling up
+])
+def test_graph_replay(n, D, B, c, prio, uniform):
+    """Two whole steps (intake, sample, update) issued in graph mode, first
+    eagerly, then captured once in a torch CUDA graph and replayed with fresh
+    inputs each time: after every replay both steps' samples and the trees
+    match the oracle taken through the same steps, while the ring moves (and
+    wraps) on the device only.  Leaving graph mode hands the device's ring
+    state back to the host, and eager calls then carry on from it."""
+    say("graph replay", n, D, B, c, prio, uniform)
+    rng = np.random.default_rng(n + c)
+    o = Oracle(n, D)
+    g = _buf(n, D, max_batch=max(B, 256))
+    k0 = n // 2 + 37
+    r0 = _rows_np(rng, k0, D)
+    p0 = (rng.random(k0) * 3).astype(np.float32)
+    o.add(k0, *r0, prio=p0)
+    g.add(k0, *[dev(x) for x in r0], prio=dev(p0))
+    beta = 0.5
+    seeds = [(11, 0), (12, 1 << 20)]  # per captured step: fixed at capture
+
+    def inputs():
+        return dict(rows=_rows_np(rng, c, D),
+                    prio=(rng.random(c) * 5).astype(np.float32) if prio else None,
+                    u=rng.random(B, dtype=np.float32),
+                    td=(rng.standard_normal(B) * 2).astype(np.float32))
+
+    first = [inputs(), inputs()]
+    stat = []
+    for k in range(2):
+        x = first[k]
+        stat.append(dict(rows=[dev(a) for a in x["rows"]],
+                         prio=dev(x["prio"]) if prio else None,
+                         u=dev(x["u"]), td=dev(x["td"]),
+                         out=g._outs(B, not uniform, D > 0)))
+
+    def refresh(xs):
+        for k in range(2):
+            s, x = stat[k], xs[k]
+            for t, a in zip(s["rows"], x["rows"]):
+                t.copy_(dev(a))
+            if prio:
+                s["prio"].copy_(dev(x["prio"]))
+            s["u"].copy_(dev(x["u"]))
+            s["td"].copy_(dev(x["td"]))
+
+    def issue(k):
+        s = stat[k]
+        g.add(c, *s["rows"], prio=s["prio"])
+        if uniform:
+            g.sample_uniform(B, seeds[k][0], seeds[k][1], rows=D > 0, out=s["out"])
+        else:
+            g.sample(s["u"], beta=beta, weights=True, rows=D > 0, out=s["out"])
+        g.update(s["out"]["idx"], s["td"])
+
+    def oracle_and_compare(xs, what):
+        for k in range(2):
+            x = xs[k]
+            o.add(c, *x["rows"], prio=x["prio"])
+            if uniform:
+                ro = o.sample_uniform(B, seeds[k][0], seeds[k][1], rows=D > 0)
+            else:
+                ro = o.sample(x["u"], beta=beta, weights=True, rows=D > 0)
+            o.update(ro["idx"], x["td"])
+            compare_sample(stat[k]["out"], ro, "%s step %d" % (what, k), rows=D > 0,
+                           weights=not uniform)
+        compare_trees(o, g, what, ring=False)
+
+    g.graph_mode(True)
+    refresh(first)
+    issue(0)
+    issue(1)
+    oracle_and_compare(first, "graph mode eager")
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        issue(0)
+        issue(1)
+    for r in range(4):
+        xs = [inputs(), inputs()]
+        refresh(xs)
+        graph.replay()
+        oracle_and_compare(xs, "replay %d" % r)
+    g.graph_mode(False)
+    assert g.size == o.size and g.cursor == o.cursor, (g.size, o.size, g.cursor, o.cursor)
+    xs = [inputs(), inputs()]
+    refresh(xs)
+    issue(0)
+    issue(1)
+    oracle_and_compare(xs, "eager after graph mode")
+    compare_trees(o, g, "eager after graph mode")
+    del graph
+    say("graph replay ok")
+
+
+def test_graph_mode_replay_rule():
+    """Leaving graph mode after calls that flip a slot parity an odd number
+    of times is reported (PER_EINVAL) yet still hands back the ring state;
+    entering twice or leaving twice is refused."""
+    from sum_tree_sampling_amd import PerError
+    n = 1 << 12
+    o = Oracle(n)
+    g = _buf(n)
+    g.graph_mode(True)
+    with pytest.raises(PerError) as e:
+        g.graph_mode(True)
+    assert e.value.code == -1
+    o.add(100)
+    g.add(100)  # one intake: the ring parity flips once
+    with pytest.raises(PerError) as e:
+        g.graph_mode(False)
+    assert e.value.code == -1 and "odd number" in str(e.value)
+    assert g.size == o.size == 100 and g.cursor == o.cursor == 100
+    with pytest.raises(PerError) as e:
+        g.graph_mode(False)
+    assert e.value.code == -1
+    compare_trees(o, g, "after the rule check")
+
+
 # ------------------------------------------------------------ full-size large buffer
 
 def test_large_16m_full_size():
