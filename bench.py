@@ -53,6 +53,7 @@ OP_KERNELS = {
     "sample": ("sample_kernel", "top_kernel"),
     "update": ("update_scan_kernel", "bucket_kernel", "update_bucket_kernel"),
     "add": ("add_kernel",),
+    "update_add": ("update_add_kernel",),
 }
 
 
@@ -108,7 +109,7 @@ def ingest_pmc(d: str) -> None:
         per_c = [_counter_rows(p) for p in paths]
         ops = {}
         for op, names in OP_KERNELS.items():
-            if op == "add" and not workloads.spec(w)["intake"]:
+            if op in ("add", "update_add") and not workloads.spec(w)["intake"]:
                 continue  # only the fill before the timed steps
             kern, tot = {}, 0.0
             for k in names:
@@ -240,6 +241,9 @@ def algorithmic_bytes(spec: dict) -> dict:
     intake = 0.0
     if c:
         intake = 8 * c + 16 * (c + 2 * L)            # leaves + contiguous dirty frontier
+    if spec.get("fused"):
+        # one launch does both: the bytes of each, nothing shared counted twice
+        return {"sample": float(sample), "update_add": float(update + intake)}
     return {"sample": float(sample), "update": float(update), "add": float(intake)}
 
 
@@ -291,6 +295,9 @@ def main():
     ap.add_argument("--rank", action="store_true",
                     help="rank-based prioritisation: every step refreshes the ranking "
                          "(per_rank_refresh) and samples with per_sample_rank")
+    ap.add_argument("--unfused", action="store_true",
+                    help="the step's update and intake as two calls (per_update, per_add) "
+                         "instead of the one per_update_add launch")
     ap.add_argument("--graph-steps", type=int, default=64,
                     help="whole steps captured as one HIP graph for the labelled replay "
                          "figure (even; 0 skips it)")
@@ -320,10 +327,13 @@ def main():
             raise SystemExit("--padded needs a workload with rows and STRIDE >= state_dim")
         if args.uniform or args.masses != "array" or args.rank:
             raise SystemExit("--padded goes with array masses and proportional sampling")
+        spec = dict(spec, out_stride=args.padded)
     if args.rank and (args.uniform or args.masses != "array"):
         raise SystemExit("--rank goes with array masses")
-        spec = dict(spec, out_stride=args.padded)
-    spec = dict(spec, masses=args.masses, uniform=args.uniform, rank=args.rank)
+    # The update and the intake of a step in one launch (per_update_add)
+    # unless asked for separately; without an update there is nothing to fuse.
+    fused = bool(spec["intake"]) and not args.uniform and not args.unfused
+    spec = dict(spec, masses=args.masses, uniform=args.uniform, rank=args.rank, fused=fused)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
@@ -399,9 +409,13 @@ def main():
 
     def step(s):
         do_sample(s, out)
-        do_update(s, idx_d[s] if idx_d is not None else out["idx"])
-        if intake:
-            g.add(intake)
+        idx = idx_d[s] if idx_d is not None else out["idx"]
+        if fused:
+            g.update_add(idx, td_d[s], intake)
+        else:
+            do_update(s, idx)
+            if intake:
+                g.add(intake)
 
     for s in range(args.warmup):
         step(s)
@@ -428,11 +442,16 @@ def main():
     ops = {
         "sample": lambda s: do_sample(base + s, dict(out, idx=idx_hist[s])),
     }
-    if not args.uniform:
-        ops["update"] = lambda s: g.update(idx_d[base + s] if idx_d is not None else idx_hist[s],
-                                           td_d[base + s])
-    if intake:
-        ops["add"] = lambda s: g.add(intake)
+    def hist_idx(s):
+        return idx_d[base + s] if idx_d is not None else idx_hist[s]
+
+    if fused:
+        ops["update_add"] = lambda s: g.update_add(hist_idx(s), td_d[base + s], intake)
+    else:
+        if not args.uniform:
+            ops["update"] = lambda s: g.update(hist_idx(s), td_d[base + s])
+        if intake:
+            ops["add"] = lambda s: g.add(intake)
     op_avg = {}
     for name, fn in ops.items():
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -452,14 +471,19 @@ def main():
         e[0].record(stream)
         do_sample(base + s, out)
         e[1].record(stream)
-        do_update(base + s, idx_d[base + s] if idx_d is not None else out["idx"])
+        idx = idx_d[base + s] if idx_d is not None else out["idx"]
+        if fused:
+            g.update_add(idx, td_d[base + s], intake)
+        else:
+            do_update(base + s, idx)
         e[2].record(stream)
-        if intake:
+        if intake and not fused:
             g.add(intake)
         e[3].record(stream)
     torch.cuda.synchronize()
     spread = {}
-    for k, name in enumerate(["sample", "update", "add"]):
+    names = ["sample", "update_add"] if fused else ["sample", "update", "add"]
+    for k, name in enumerate(names):
         if (name == "add" and not intake) or (name == "update" and args.uniform):
             continue
         t = np.array([e[k].elapsed_time(e[k + 1]) for e in evs])
@@ -493,10 +517,12 @@ def main():
                    "intake": intake, "unique_updates": spec.get("unique", B),
                    "weights": spec["weights"], "parallelism": "single GPU",
                    "out_stride": W or D, "masses": args.masses,
+                   "update_and_intake": "one launch" if fused else "separate calls",
                    "sampling": ("uniform" if args.uniform else
                                 ("rank" if args.rank else "proportional"))},
         "samples_per_s": B / (op_avg["sample"] * 1e-3),
-        "updates_per_s": B / (op_avg["update"] * 1e-3) if "update" in op_avg else None,
+        "updates_per_s": (B / (op_avg["update"] * 1e-3) if "update" in op_avg else
+                          (B / (op_avg["update_add"] * 1e-3) if fused else None)),
         "op_ms_avg": op_avg,
         "op_ms_bracketed": spread,
         "graph_replay": graph,

@@ -122,6 +122,26 @@ int per_update(per_t* h, int64_t B, const int64_t* d_idx, const float* d_td,
                hipStream_t stream);
 
 /*
+ * per_update(h, B, d_idx, d_td) followed by per_add(h, count, rows..., d_prio)
+ * in one kernel launch where possible ("Putting prioritized replay's segment
+ * tree on a GPU", section "The Tree Under Every Prioritized Replay": the
+ * replay rank takes a priority update for every learner batch plus intake
+ * batches from the actors; "True Single-Graph Implementation Plan", its
+ * goal: fewer launches per step).  The result -- trees, running max, ring
+ * state, stored rows -- is that of the two calls in that order: the intake
+ * overwrites slots the update just set, and NULL d_prio gives the new slots
+ * the running max after the update.  Arguments and errors as for the two
+ * calls, all checked before anything is enqueued.  B == 0 or count == 0
+ * reduces to the other call; a batch large enough for the bucketed update
+ * (more than 2^20 / 2^P entries, 2^P = capacity / 4096 partitions) is
+ * enqueued as the two calls.
+ */
+int per_update_add(per_t* h, int64_t B, const int64_t* d_idx, const float* d_td, int64_t count,
+                   const float* d_states, const float* d_next_states, const uint32_t* d_actions,
+                   const float* d_rewards, const uint8_t* d_dones, const float* d_prio,
+                   hipStream_t stream);
+
+/*
  * Batched proportional sample ("Putting prioritized replay's segment tree on a
  * GPU", section "Sampling Is a Descent"; importance weights and gather,
  * "GPU-Resident Prioritized Experience Replay", section "Sampling Kernels";

@@ -223,41 +223,63 @@ int per_destroy(per_t* h) {
   return ok();
 }
 
-int per_add(per_t* h, int64_t count, const float* d_states, const float* d_next_states,
-            const uint32_t* d_actions, const float* d_rewards, const uint8_t* d_dones,
-            const float* d_prio, hipStream_t stream) {
-  if (!h) return fail(PER_EINVAL, "handle is NULL");
+namespace {
+
+int check_add(const per_t* h, int64_t count, const float* d_states, const float* d_next_states,
+              const uint32_t* d_actions, const float* d_rewards, const uint8_t* d_dones) {
   if (count < 0 || count > (int64_t)h->g.n)
     return fail(PER_EINVAL, "count %lld outside [0, capacity]", (long long)count);
-  if (count == 0) return ok();
-  if (h->st.D > 0) {
+  if (count > 0 && h->st.D > 0) {
     if (!(d_states && d_next_states && d_actions && d_rewards && d_dones))
       return fail(PER_EINVAL, "the handle has storage: all five row arrays are required");
     if ((reinterpret_cast<uintptr_t>(d_states) | reinterpret_cast<uintptr_t>(d_next_states)) &
         15u)
       return fail(PER_EINVAL, "state rows must be 16-byte aligned");
   }
+  return PER_OK;
+}
+
+int check_update(const per_t* h, int64_t B, const int64_t* d_idx, const float* d_td) {
+  if (B < 0 || B > h->max_batch)
+    return fail(PER_EINVAL, "B %lld outside [0, max_batch=%lld]", (long long)B,
+                (long long)h->max_batch);
+  if (B > 0 && (!d_idx || !d_td)) return fail(PER_EINVAL, "idx and td are required");
+  return PER_OK;
+}
+
+// Host state after an intake of count items was enqueued.
+void advance_ring(per_t* h, int64_t count) {
+  h->ring ^= 1;
+  h->top_stale = h->g.P > 0;
+  h->cursor = (h->cursor + count) % (int64_t)h->g.n;
+  h->size = (h->size + count < (int64_t)h->g.n) ? h->size + count : (int64_t)h->g.n;
+}
+
+}  // namespace
+
+int per_add(per_t* h, int64_t count, const float* d_states, const float* d_next_states,
+            const uint32_t* d_actions, const float* d_rewards, const uint8_t* d_dones,
+            const float* d_prio, hipStream_t stream) {
+  if (!h) return fail(PER_EINVAL, "handle is NULL");
+  int rc = check_add(h, count, d_states, d_next_states, d_actions, d_rewards, d_dones);
+  if (rc) return rc;
+  if (count == 0) return ok();
   const int src = h->epoch, dst = d_prio ? (h->epoch ^ 1) : h->epoch;
   hipError_t e = per::launch_add(h->t, h->g, h->st, ring_ref(h), (uint32_t)h->size,
                                  (uint32_t)h->cursor, (uint32_t)count, d_states, d_next_states,
                                  d_actions, d_rewards, d_dones, d_prio, src, dst, stream);
   if (e != hipSuccess) return hip_fail(e, "per_add");
   h->epoch = dst;
-  h->ring ^= 1;
-  h->top_stale = h->g.P > 0;
-  h->cursor = (h->cursor + count) % (int64_t)h->g.n;
-  h->size = (h->size + count < (int64_t)h->g.n) ? h->size + count : (int64_t)h->g.n;
+  advance_ring(h, count);
   return ok();
 }
 
 int per_update(per_t* h, int64_t B, const int64_t* d_idx, const float* d_td,
                hipStream_t stream) {
   if (!h) return fail(PER_EINVAL, "handle is NULL");
-  if (B < 0 || B > h->max_batch)
-    return fail(PER_EINVAL, "B %lld outside [0, max_batch=%lld]", (long long)B,
-                (long long)h->max_batch);
+  int rc = check_update(h, B, d_idx, d_td);
+  if (rc) return rc;
   if (B == 0) return ok();
-  if (!d_idx || !d_td) return fail(PER_EINVAL, "idx and td are required");
   hipError_t e = per::launch_update(h->t, h->bk, h->g, ring_ref(h), (uint32_t)h->size, B, d_idx,
                                     d_td, h->alpha, h->eps, h->epoch, h->epoch ^ 1, h->ovf,
                                     stream);
@@ -265,6 +287,36 @@ int per_update(per_t* h, int64_t B, const int64_t* d_idx, const float* d_td,
   h->epoch ^= 1;
   if (per::update_uses_buckets(h->g, B)) h->ovf ^= 1;
   h->top_stale = h->g.P > 0;
+  return ok();
+}
+
+int per_update_add(per_t* h, int64_t B, const int64_t* d_idx, const float* d_td, int64_t count,
+                   const float* d_states, const float* d_next_states, const uint32_t* d_actions,
+                   const float* d_rewards, const uint8_t* d_dones, const float* d_prio,
+                   hipStream_t stream) {
+  if (!h) return fail(PER_EINVAL, "handle is NULL");
+  int rc = check_update(h, B, d_idx, d_td);
+  if (rc) return rc;
+  rc = check_add(h, count, d_states, d_next_states, d_actions, d_rewards, d_dones);
+  if (rc) return rc;
+  if (count == 0) return per_update(h, B, d_idx, d_td, stream);
+  if (B == 0 || per::update_uses_buckets(h->g, B)) {
+    // Nothing to fuse, or a batch large enough for the bucketed update: the
+    // two calls, one after the other (both checked above, so neither fails
+    // on its arguments).
+    rc = per_update(h, B, d_idx, d_td, stream);
+    if (rc) return rc;
+    return per_add(h, count, d_states, d_next_states, d_actions, d_rewards, d_dones, d_prio,
+                   stream);
+  }
+  const int src = h->epoch, dst = h->epoch ^ 1;
+  hipError_t e = per::launch_update_add(h->t, h->g, h->st, ring_ref(h), (uint32_t)h->size,
+                                        (uint32_t)h->cursor, B, d_idx, d_td, h->alpha, h->eps,
+                                        (uint32_t)count, d_states, d_next_states, d_actions,
+                                        d_rewards, d_dones, d_prio, src, dst, stream);
+  if (e != hipSuccess) return hip_fail(e, "per_update_add");
+  h->epoch = dst;
+  advance_ring(h, count);
   return ok();
 }
 

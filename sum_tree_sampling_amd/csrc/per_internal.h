@@ -123,6 +123,16 @@ hipError_t launch_add(const TreePtrs& t, const Geom& g, const Storage& st, RingR
                       const float* next_states, const uint32_t* actions, const float* rewards,
                       const uint8_t* dones, const float* prio, int src, int dst, hipStream_t s);
 
+// An update batch (B > 0, not bucketed: !update_uses_buckets(g, B)) and then
+// an intake of count > 0 items, in one launch; the running max is read from
+// slot src and raised in slot dst by both parts.
+hipError_t launch_update_add(const TreePtrs& t, const Geom& g, const Storage& st, RingRef ring,
+                             uint32_t size, uint32_t cursor, int64_t B, const int64_t* idx,
+                             const float* td, double alpha, double eps, uint32_t count,
+                             const float* states, const float* next_states,
+                             const uint32_t* actions, const float* rewards, const uint8_t* dones,
+                             const float* prio, int src, int dst, hipStream_t s);
+
 hipError_t launch_sample(const TreePtrs& t, const Geom& g, const Storage& st,
                          const SamplePlan& plan, uint32_t size, int64_t B, const float* u,
                          uint64_t seed, uint64_t offset, double beta, int64_t* idx_out,

@@ -36,6 +36,8 @@
 // (all priorities are >= 0, so the bit patterns order like the values); the
 // host flips the committed slot after enqueueing the call.
 
+#include <type_traits>
+
 #include "per_internal.h"
 
 namespace per {
@@ -209,6 +211,7 @@ struct UpdSmem {
   int count[PPB];      // entries collected per partition
   uint32_t mtot[PPB];  // entries per partition (bucketed path)
   uint32_t bmax;       // max priority bits of the block's entries
+  uint32_t ball;       // max priority bits of the whole batch (fused intake blocks)
   int flag;
 };
 
@@ -636,16 +639,26 @@ __device__ __forceinline__ uint32_t filled_size(const UpdateArgs& a) {
 // Small batches: each block owns PPB consecutive partitions and scans the
 // whole batch for their slots; wave w repairs partition w of the block when
 // it is sparse, crowded partitions are rebuilt by the whole block after.
-template <int PPB>
-__global__ void __launch_bounds__(kUpdThreads) update_scan_kernel(TreePtrs t, Geom g, UpdateArgs a) {
-  __shared__ UpdSmem<PPB> sm;
-  const uint32_t part0 = blockIdx.x * PPB;
+// m0: the running max at the start of the call.  FUSED (one partition per
+// block): entries at offsets skip(off) are left out of the repair, their
+// priorities still raising the running max, and with `all` set
+// (block-uniform) sm.ball receives, once the scan's barrier is passed, the
+// max priority bits over every entry of the batch inside [0, size), the
+// block's own and the others'.  Returns whether a partition was crowded
+// (then rebuilt by the whole block, which has passed a barrier since);
+// otherwise wave w returns right after its sparse repair.
+template <int PPB, bool FUSED, typename SM, typename Skip>
+__device__ __forceinline__ bool scan_update(SM& sm, const TreePtrs& t, const Geom& g,
+                                            const UpdateArgs& a, uint32_t part0, uint32_t size,
+                                            float m0, bool all, Skip skip) {
   const int nparts = (int)min((uint32_t)PPB, (1u << g.P) - part0);
-  const float m0 = __uint_as_float(t.ctrl->maxp_bits[a.src]);
   uint32_t* max_dst = &t.ctrl->maxp_bits[a.dst];
-  const uint32_t size = filled_size(a);
+  uint32_t mall = 0;  // max priority bits of every entry looked at (FUSED)
   if (threadIdx.x < PPB) sm.count[threadIdx.x] = 0;
-  if (threadIdx.x == 0) sm.bmax = 0u;
+  if (threadIdx.x == 0) {
+    sm.bmax = 0u;
+    sm.ball = 0u;
+  }
   __syncthreads();
   // Each thread loads its share of the batch in chunks of kChunk entries, all
   // loads of a chunk issued before any of them is looked at.
@@ -671,13 +684,29 @@ __global__ void __launch_bounds__(kUpdThreads) update_scan_kernel(TreePtrs t, Ge
       const int64_t i = ix[c];
       if (i < 0 || i >= (int64_t)size) continue;
       const uint32_t q = (uint32_t)((uint64_t)i >> g.S) - part0;  // wraps below part0
-      if (q < (uint32_t)nparts) {
-        const uint32_t part = part0 + q;
-        const int k = atomicAdd(&sm.count[q], 1);
-        const float p = collect(sm.u.sp[q], k, t, g, part, (uint32_t)i - (part << g.S), b, tx[c],
-                                m0, a.alpha, a.eps, a.p_nan);
-        atomicMax(&sm.bmax, __float_as_uint(p));
-      }
+      const bool own = q < (uint32_t)nparts;
+      if (!own && !(FUSED && all)) continue;
+      // One priority computation for every entry looked at: collect()
+      // issues no loads for an entry index >= kSparseMax, which entries of
+      // other partitions and left-out ones take.
+      const uint32_t qq = own ? q : 0u;
+      const uint32_t part = part0 + qq;
+      const uint32_t off = (uint32_t)i - (part << g.S);
+      bool keep = own;
+      if constexpr (FUSED) keep = keep && !skip(off);
+      const int k = keep ? atomicAdd(&sm.count[qq], 1) : kSparseMax;
+      const float p = collect(sm.u.sp[qq], k, t, g, part, off, b, tx[c], m0, a.alpha, a.eps,
+                              a.p_nan);
+      if (own) atomicMax(&sm.bmax, __float_as_uint(p));
+      if constexpr (FUSED) mall = max(mall, __float_as_uint(p));
+    }
+  }
+  if constexpr (FUSED) {
+    if (all) {
+      // One LDS atomic per wave after a shuffle reduction: an atomic from
+      // every lane to one address becomes a lane-by-lane loop.
+      const uint32_t wm = wave_max_u32(mall);
+      if ((threadIdx.x & 63) == 0) atomicMax(&sm.ball, wm);
     }
   }
   __syncthreads();
@@ -689,7 +718,7 @@ __global__ void __launch_bounds__(kUpdThreads) update_scan_kernel(TreePtrs t, Ge
     const int m = sm.count[w];
     if (m > 0 && m <= kSparseMax) wave_update(sm.u.sp[w], t, g, part0 + w, m);
   }
-  if (!crowded) return;
+  if (!crowded) return false;
   // The dense rebuild reuses the sparse areas: every wave is done with them.
   __syncthreads();
   for (int q = 0; q < nparts; ++q) {
@@ -699,11 +728,21 @@ __global__ void __launch_bounds__(kUpdThreads) update_scan_kernel(TreePtrs t, Ge
     dense_update<kUpdThreads>(sm.u.dn, sm.flag, sm.sx, t, g, part, [&](auto f) {
       for (uint32_t b = threadIdx.x; b < a.B; b += kUpdThreads) {
         const int64_t i = a.idx[b];
-        if (i >= 0 && i < (int64_t)size && ((uint64_t)i >> g.S) == part)
+        if (i >= 0 && i < (int64_t)size && ((uint64_t)i >> g.S) == part &&
+            !(FUSED && skip((uint32_t)i - base)))
           f((uint32_t)i - base, b, priority_of(a.td[b], m0, a.alpha, a.eps, a.p_nan));
       }
     });
   }
+  return true;
+}
+
+template <int PPB>
+__global__ void __launch_bounds__(kUpdThreads) update_scan_kernel(TreePtrs t, Geom g, UpdateArgs a) {
+  __shared__ UpdSmem<PPB> sm;
+  const float m0 = __uint_as_float(t.ctrl->maxp_bits[a.src]);
+  scan_update<PPB, false>(sm, t, g, a, blockIdx.x * PPB, filled_size(a), m0, false,
+                          [](uint32_t) { return false; });
 }
 
 // Large batches, step 1: every valid entry goes to its partition's bucket
@@ -840,126 +879,252 @@ struct AddArgs {
   const uint8_t* dones;
 };
 
-// Ring intake ("GPU-Resident Prioritized Experience Replay", section
-// "Experience Insertion"): new slots take the given priority or the running
-// max priority; rows are copied by the blocks past the tree blocks.
-__global__ void __launch_bounds__(256) add_kernel(TreePtrs t, Geom g, Storage st, AddArgs a) {
-  __shared__ AddSmem sm;
-  uint32_t cursor = a.cursor, size = a.size;
+// The ring state before an intake: the launch's, or the device's (graph mode).
+__device__ __forceinline__ void ring_state(const TreePtrs& t, const AddArgs& a, uint32_t& cursor,
+                                           uint32_t& size) {
+  cursor = a.cursor;
+  size = a.size;
   if (a.ring.dev) {
     cursor = t.ctrl->cursor[a.ring.slot];
     size = t.ctrl->size[a.ring.slot];
   }
-  // The ring state after this intake goes to the other slot, so that no
-  // block of this launch reads a value another block has changed.  The last
-  // block writes it: a row-copy block whenever rows are kept, which has no
-  // barrier to wait on the store.
+}
+
+// The ring state after the intake goes to the other slot, so that no block
+// of the launch reads a value another block has changed.  One thread of the
+// last block: a row-copy block whenever rows are kept, with no barrier to
+// wait on the store.
+__device__ __forceinline__ void commit_ring(const TreePtrs& t, const Geom& g, const AddArgs& a,
+                                            uint32_t cursor, uint32_t size) {
   if (blockIdx.x == gridDim.x - 1 && threadIdx.x == 0) {
     const uint64_t next = (uint64_t)cursor + a.count;
     const uint64_t filled = (uint64_t)size + a.count;
     t.ctrl->cursor[a.ring.slot ^ 1] = (uint32_t)(next >= g.n ? next - g.n : next);
     t.ctrl->size[a.ring.slot ^ 1] = (uint32_t)(filled < g.n ? filled : g.n);
   }
-  if (blockIdx.x >= a.ntree) {
-    // Row copy of the transitions into their ring slots.
-    const uint32_t nb = gridDim.x - a.ntree;
-    const uint32_t tid = (blockIdx.x - a.ntree) * kTreeThreads + threadIdx.x;
-    const uint32_t stride = nb * kTreeThreads;
-    const uint32_t D = (uint32_t)st.D;
-    if ((D & 3u) == 0u) {
-      const uint32_t c4 = D >> 2;
-      const uint64_t total = (uint64_t)a.count * c4;
-      for (uint64_t e = tid; e < total; e += stride) {
-        const uint32_t j = (uint32_t)(e / c4), c = (uint32_t)(e % c4);
-        uint32_t slot = cursor + j;
-        if (slot >= g.n) slot -= g.n;
-        const uint64_t so = (uint64_t)j * D + 4u * c, dof = (uint64_t)slot * D + 4u * c;
-        *reinterpret_cast<float4*>(st.states + dof) =
-            *reinterpret_cast<const float4*>(a.states + so);
-        *reinterpret_cast<float4*>(st.next_states + dof) =
-            *reinterpret_cast<const float4*>(a.next_states + so);
-      }
-    } else {
-      const uint64_t total = (uint64_t)a.count * D;
-      for (uint64_t e = tid; e < total; e += stride) {
-        const uint32_t j = (uint32_t)(e / D), c = (uint32_t)(e % D);
-        uint32_t slot = cursor + j;
-        if (slot >= g.n) slot -= g.n;
-        st.states[(uint64_t)slot * D + c] = a.states[e];
-        st.next_states[(uint64_t)slot * D + c] = a.next_states[e];
-      }
-    }
-    for (uint32_t j = tid; j < a.count; j += stride) {
+}
+
+// Row copy of the intake's transitions into their ring slots, by the blocks
+// [first, gridDim.x) of the launch.
+__device__ void copy_intake_rows(const Storage& st, const Geom& g, const AddArgs& a,
+                                 uint32_t cursor, uint32_t first) {
+  const uint32_t nb = gridDim.x - first;
+  const uint32_t tid = (blockIdx.x - first) * kTreeThreads + threadIdx.x;
+  const uint32_t stride = nb * kTreeThreads;
+  const uint32_t D = (uint32_t)st.D;
+  if ((D & 3u) == 0u) {
+    const uint32_t c4 = D >> 2;
+    const uint64_t total = (uint64_t)a.count * c4;
+    for (uint64_t e = tid; e < total; e += stride) {
+      const uint32_t j = (uint32_t)(e / c4), c = (uint32_t)(e % c4);
       uint32_t slot = cursor + j;
       if (slot >= g.n) slot -= g.n;
-      st.actions[slot] = a.actions[j];
-      st.rewards[slot] = a.rewards[j];
-      st.dones[slot] = a.dones[j];
+      const uint64_t so = (uint64_t)j * D + 4u * c, dof = (uint64_t)slot * D + 4u * c;
+      *reinterpret_cast<float4*>(st.states + dof) =
+          *reinterpret_cast<const float4*>(a.states + so);
+      *reinterpret_cast<float4*>(st.next_states + dof) =
+          *reinterpret_cast<const float4*>(a.next_states + so);
     }
+  } else {
+    const uint64_t total = (uint64_t)a.count * D;
+    for (uint64_t e = tid; e < total; e += stride) {
+      const uint32_t j = (uint32_t)(e / D), c = (uint32_t)(e % D);
+      uint32_t slot = cursor + j;
+      if (slot >= g.n) slot -= g.n;
+      st.states[(uint64_t)slot * D + c] = a.states[e];
+      st.next_states[(uint64_t)slot * D + c] = a.next_states[e];
+    }
+  }
+  for (uint32_t j = tid; j < a.count; j += stride) {
+    uint32_t slot = cursor + j;
+    if (slot >= g.n) slot -= g.n;
+    st.actions[slot] = a.actions[j];
+    st.rewards[slot] = a.rewards[j];
+    st.dones[slot] = a.dones[j];
+  }
+}
+
+// The ring range [cursor, cursor + count) split at the wrap -- [cursor,
+// min(end, n)) and, past the wrap, [0, end - n) -- and clipped to partition
+// `part`: runs of offsets [lo0, hi0) and, when both meet it, [0, hi1).
+struct IntakeRuns {
+  int runs;  // 0, 1 or 2
+  uint32_t lo0, hi0, hi1;
+
+  __device__ bool has(uint32_t off) const {
+    return (off >= lo0 && off < hi0) || (runs == 2 && off < hi1);
+  }
+};
+
+__device__ __forceinline__ IntakeRuns intake_runs(uint32_t cursor, uint32_t count, const Geom& g,
+                                                  uint32_t part) {
+  const uint32_t span = 1u << g.S;
+  const uint32_t base = part << g.S;
+  const uint64_t end = (uint64_t)cursor + count;
+  const uint32_t a_lo = max(cursor, base);
+  const uint32_t a_hi = min((uint32_t)(end < g.n ? end : g.n), base + span);
+  const uint32_t b_hi = min((uint32_t)(end > g.n ? end - g.n : 0u), base + span);
+  const bool has_a = a_lo < a_hi, has_b = base < b_hi;
+  IntakeRuns r;
+  r.runs = (int)has_a + (int)has_b;
+  r.lo0 = has_a ? a_lo - base : 0u;
+  r.hi0 = has_a ? a_hi - base : (has_b ? b_hi - base : 0u);
+  r.hi1 = has_b ? b_hi - base : 0u;
+  return r;
+}
+
+// The intake's slots in partition `part` -- the ring range [cursor, cursor +
+// count) clipped to it: one run, or two when the ring wraps inside it --
+// take the given priorities (prio[j] for the range's j-th slot) or v, and
+// the nodes above them are repaired up to the partition root.  Given
+// priorities raise the running max at max_dst: thread 0 publishes the
+// block's max, carrying v over when carry is set and otherwise only when it
+// exceeds v (v must then already be there).  RANGE: sm holds a RangeSmem
+// for the LDS repair of a single run of given priorities; without one such
+// a run is rebuilt like two.  Returns at once when the range misses the
+// partition.  Every argument is block-uniform.
+template <bool RANGE, typename SM>
+__device__ __forceinline__ void intake_partition(SM& sm, const TreePtrs& t, const Geom& g,
+                                                 uint32_t part, uint32_t cursor, uint32_t count,
+                                                 const float* prio, float v, bool carry,
+                                                 uint32_t* max_dst) {
+  const uint32_t base = part << g.S;
+  const IntakeRuns ir = intake_runs(cursor, count, g, part);
+  const int runs = ir.runs;
+  const uint32_t lo0 = ir.lo0, hi0 = ir.hi0, hi1 = ir.hi1;
+  if (runs == 0) return;
+  if (runs == 1 && !prio) {
+    // One run at the running max (the usual intake): no LDS, no barrier.
+    float sib_s = 0.0f, sib_m = 0.0f;
+    load_range_boundary(t, g, part, lo0, hi0, sib_s, sib_m);
+    uniform_range(t, g, part, lo0, hi0, v, sib_s, sib_m);
+    return;
+  }
+  // One run: its boundary siblings go out with the other loads.
+  if constexpr (RANGE) {
+    if (runs == 1) prefetch_range_boundaries(sm.u.r, t, g, part, lo0, hi0);
+  }
+  auto value_of = [&](uint32_t off) -> float {
+    const uint32_t slot = base + off;
+    const uint32_t j = (slot >= cursor) ? slot - cursor : slot + (g.n - cursor);
+    return prio ? prio[j] + 0.0f : v;
+  };
+  // f(off) for every new offset of the partition, spread over the block.
+  auto each_offset = [&](auto f) {
+    for (uint32_t off = lo0 + threadIdx.x; off < hi0; off += kTreeThreads) f(off);
+    if (runs == 2)
+      for (uint32_t off = threadIdx.x; off < hi1; off += kTreeThreads) f(off);
+  };
+  uint32_t mb = 0;
+  each_offset([&](uint32_t off) {
+    const float p = value_of(off);
+    mb = max(mb, __float_as_uint(p));
+    if constexpr (RANGE) {
+      if (runs == 1) sm.u.r.val[off] = p;
+    }
+  });
+  if (prio) {
+    mb = block_max_bits<kTreeThreads>(mb, sm.sx);
+    if (threadIdx.x == 0) publish_max(mb, carry, v, max_dst);
+  }
+  __syncthreads();
+  if constexpr (RANGE) {
+    if (runs == 1) {
+      range_repair(sm.u.r, t, g, part, lo0, hi0);
+      return;
+    }
+  }
+  // Two runs in one partition (the ring wrapped inside it): general rebuild;
+  // slots are distinct, so the offset doubles as the batch position.
+  dense_update<kTreeThreads>(sm.u.dn, sm.flag, sm.sx, t, g, part, [&](auto f) {
+    each_offset([&](uint32_t off) { f(off, off, value_of(off)); });
+  });
+}
+
+// Ring intake ("GPU-Resident Prioritized Experience Replay", section
+// "Experience Insertion"): new slots take the given priority or the running
+// max priority; rows are copied by the blocks past the tree blocks.
+__global__ void __launch_bounds__(256) add_kernel(TreePtrs t, Geom g, Storage st, AddArgs a) {
+  __shared__ AddSmem sm;
+  uint32_t cursor, size;
+  ring_state(t, a, cursor, size);
+  commit_ring(t, g, a, cursor, size);
+  if (blockIdx.x >= a.ntree) {
+    copy_intake_rows(st, g, a, cursor, a.ntree);
     return;
   }
   const uint32_t w = blockIdx.x;
   const TouchedRuns tr = touched_runs(cursor, a.count, g);
   if (w >= tr.len[0] + tr.len[1]) return;  // spare block of a worst-case grid
   const uint32_t part = (w < tr.len[0]) ? tr.first[0] + w : tr.first[1] + (w - tr.len[0]);
-  const uint32_t span = 1u << g.S;
-  const uint32_t base = part << g.S;
-  // The ring range [cursor, cursor + count) split at the wrap, clipped to
-  // this partition: one or two runs of offsets.
-  const uint64_t end = (uint64_t)cursor + a.count;
-  const uint32_t r_lo[2] = {cursor, 0u};
-  const uint32_t r_hi[2] = {(uint32_t)(end < g.n ? end : g.n),
-                            (uint32_t)(end > g.n ? end - g.n : 0u)};
-  uint32_t lo[2], hi[2];
-  int runs = 0;
-  for (int r = 0; r < 2; ++r) {
-    const uint32_t l = max(r_lo[r], base), h = min(r_hi[r], base + span);
-    if (l < h) {
-      lo[runs] = l - base;
-      hi[runs] = h - base;
-      ++runs;
-    }
-  }
-  if (runs == 1 && !a.prio) {
-    // One run at the running max (the usual intake): no LDS, no barrier.
-    float sib_s = 0.0f, sib_m = 0.0f;
-    load_range_boundary(t, g, part, lo[0], hi[0], sib_s, sib_m);
-    const float m0 = __uint_as_float(t.ctrl->maxp_bits[a.src]);
-    uniform_range(t, g, part, lo[0], hi[0], m0, sib_s, sib_m);
-    return;
-  }
-  // One run (the usual case): its boundary siblings go out with the other loads.
-  if (runs == 1) prefetch_range_boundaries(sm.u.r, t, g, part, lo[0], hi[0]);
   const float m0 = __uint_as_float(t.ctrl->maxp_bits[a.src]);
-  auto value_of = [&](uint32_t off) -> float {
-    const uint32_t slot = base + off;
-    const uint32_t j = (slot >= cursor) ? slot - cursor : slot + (g.n - cursor);
-    return a.prio ? a.prio[j] + 0.0f : m0;
-  };
-  uint32_t mb = 0;
-  for (int r = 0; r < runs; ++r) {
-    for (uint32_t off = lo[r] + threadIdx.x; off < hi[r]; off += kTreeThreads) {
-      const float p = value_of(off);
-      mb = max(mb, __float_as_uint(p));
-      if (runs == 1) sm.u.r.val[off] = p;
-    }
-  }
-  if (a.prio) {
-    mb = block_max_bits<kTreeThreads>(mb, sm.sx);
-    if (threadIdx.x == 0) publish_max(mb, w == 0, m0, &t.ctrl->maxp_bits[a.dst]);
-  }
-  __syncthreads();
-  if (runs == 1) {
-    range_repair(sm.u.r, t, g, part, lo[0], hi[0]);
+  intake_partition<true>(sm, t, g, part, cursor, a.count, a.prio, m0, w == 0,
+                         &t.ctrl->maxp_bits[a.dst]);
+}
+
+// LDS of the fused update + intake block when the intake brings its own
+// priorities: the update's areas and the intake's range repair share it.
+struct UpdAddSmem {
+  union {
+    SparseSmem sp[1];
+    DenseSmem dn;
+    RangeSmem r;
+  } u;
+  BlockScratch sx;
+  int count[1];
+  uint32_t mtot[1];
+  uint32_t bmax;
+  uint32_t ball;
+  int flag;
+};
+
+// An update batch followed by an intake in one launch, with the result of
+// the two calls in that order.  Block `part` of the first 2^P updates its
+// partition from the batch as the scan path does, then applies the intake's
+// slots in it, if the ring range meets it, on top of the repaired subtree.
+// At the running max (PRIO false) those slots take the max after the
+// update: the value at the start or a larger priority of the batch, which
+// such a block gathers from the whole batch while scanning it.  Both raise
+// the running max in the same slot (a.dst == b.dst).  Blocks past the first
+// 2^P copy the intake's rows.
+template <bool PRIO>
+__global__ void __launch_bounds__(kUpdThreads) update_add_kernel(TreePtrs t, Geom g, Storage st,
+                                                                 UpdateArgs a, AddArgs b) {
+  __shared__ std::conditional_t<PRIO, UpdAddSmem, UpdSmem<1>> sm;
+  uint32_t cursor, size;
+  ring_state(t, b, cursor, size);
+  commit_ring(t, g, b, cursor, size);
+  const uint32_t np = 1u << g.P;
+  if (blockIdx.x >= np) {
+    copy_intake_rows(st, g, b, cursor, np);
     return;
   }
-  // Two runs in one partition (the ring wrapped inside it): general rebuild;
-  // slots are distinct, so the offset doubles as the batch position.
-  dense_update<kTreeThreads>(sm.u.dn, sm.flag, sm.sx, t, g, part, [&](auto f) {
-    for (int r = 0; r < runs; ++r)
-      for (uint32_t off = lo[r] + threadIdx.x; off < hi[r]; off += kTreeThreads)
-        f(off, off, value_of(off));
-  });
+  const uint32_t part = blockIdx.x;
+  const IntakeRuns ir = intake_runs(cursor, b.count, g, part);
+  const float m0 = __uint_as_float(t.ctrl->maxp_bits[a.src]);
+  // Update entries at slots the intake takes are left out of the repair
+  // (the intake overwrites them; their priorities still count).
+  const bool crowded = scan_update<1, true>(sm, t, g, a, part, size, m0, !PRIO && ir.runs > 0,
+                                            [&](uint32_t off) { return ir.has(off); });
+  if (ir.runs == 0) return;
+  float v = m0;
+  if constexpr (!PRIO) v = __uint_as_float(max(__float_as_uint(m0), sm.ball));
+  if (!PRIO && ir.runs == 1 && !crowded) {
+    // No barrier: the update's new leaves are all outside the run, so its
+    // repaired nodes meet the intake's only on the run's two boundary
+    // paths, which wave 0 computes -- after its own sparse repair, in
+    // program order, its loads of the boundary siblings seeing that
+    // repair's stores.  The run's interior nodes are the intake's alone.
+    float sib_s = 0.0f, sib_m = 0.0f;
+    load_range_boundary(t, g, part, ir.lo0, ir.hi0, sib_s, sib_m);
+    uniform_range(t, g, part, ir.lo0, ir.hi0, v, sib_s, sib_m);
+    return;
+  }
+  // The update's repair is complete, and visible to the whole block, before
+  // the intake reads the nodes around its run.
+  __syncthreads();
+  intake_partition<PRIO>(sm, t, g, part, cursor, b.count, b.prio, v, false,
+                         &t.ctrl->maxp_bits[b.dst]);
 }
 
 // Nodes [1, 2^P) above the partitions, recomputed from depth P upwards.
@@ -1104,6 +1269,52 @@ hipError_t launch_add(const TreePtrs& t, const Geom& g, const Storage& st, RingR
   if (st.D > 0)
     ncopy = grid_for((uint64_t)count * (uint64_t)st.D / 4 + count, kTreeThreads * 4, 2048);
   hipLaunchKernelGGL(add_kernel, dim3(a.ntree + ncopy), dim3(kTreeThreads), 0, s, t, g, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_update_add(const TreePtrs& t, const Geom& g, const Storage& st, RingRef ring,
+                             uint32_t size, uint32_t cursor, int64_t B, const int64_t* idx,
+                             const float* td, double alpha, double eps, uint32_t count,
+                             const float* states, const float* next_states,
+                             const uint32_t* actions, const float* rewards, const uint8_t* dones,
+                             const float* prio, int src, int dst, hipStream_t s) {
+  UpdateArgs a;
+  a.ring = ring;
+  a.ring_ctrl = t.ctrl;
+  a.idx = idx;
+  a.td = td;
+  a.B = (uint32_t)B;
+  a.size = size;
+  a.alpha = alpha;
+  a.eps = eps;
+  a.p_nan = (float)pow(eps, alpha);
+  a.src = src;
+  a.dst = dst;
+  a.ovf = 0;
+  AddArgs b;
+  b.cursor = cursor;
+  b.count = count;
+  b.size = size;
+  b.ring = ring;
+  b.prio = prio;
+  b.src = src;
+  b.dst = dst;
+  b.states = states;
+  b.next_states = next_states;
+  b.actions = actions;
+  b.rewards = rewards;
+  b.dones = dones;
+  const uint32_t np = 1u << g.P;
+  b.ntree = np;
+  unsigned ncopy = 0;
+  if (st.D > 0)
+    ncopy = grid_for((uint64_t)count * (uint64_t)st.D / 4 + count, kTreeThreads * 4, 2048);
+  if (prio)
+    hipLaunchKernelGGL(update_add_kernel<true>, dim3(np + ncopy), dim3(kUpdThreads), 0, s, t, g,
+                       st, a, b);
+  else
+    hipLaunchKernelGGL(update_add_kernel<false>, dim3(np + ncopy), dim3(kUpdThreads), 0, s, t, g,
+                       st, a, b);
   return hipGetLastError();
 }
 

@@ -47,6 +47,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
         "per_destroy": (c_int, [vp]),
         "per_add": (c_int, [vp, i64, vp, vp, vp, vp, vp, vp, vp]),
         "per_update": (c_int, [vp, i64, vp, vp, vp]),
+        "per_update_add": (c_int, [vp, i64, vp, vp, i64, vp, vp, vp, vp, vp, vp, vp]),
         "per_sample": (c_int, [vp, i64, vp, f64, vp, vp, vp, vp, vp, vp, vp, vp]),
         "per_sample_padded": (c_int, [vp, i64, vp, f64, vp, vp, vp, vp, i64, vp, vp, vp, vp]),
         "per_sample_philox": (c_int, [vp, i64, u64, u64, f64, vp, vp, vp, vp, vp, vp, vp, vp]),
@@ -137,6 +138,13 @@ def per_add(h, count, states=None, next_states=None, actions=None, rewards=None,
 
 def per_update(h, B, idx, td, stream=None) -> None:
     _check(load().per_update(h, int(B), _p(idx), _p(td), _stream(stream)))
+
+
+def per_update_add(h, B, idx, td, count, states=None, next_states=None, actions=None,
+                   rewards=None, dones=None, prio=None, stream=None) -> None:
+    _check(load().per_update_add(h, int(B), _p(idx), _p(td), int(count), _p(states),
+                                 _p(next_states), _p(actions), _p(rewards), _p(dones), _p(prio),
+                                 _stream(stream)))
 
 
 def per_sample(h, B, u, beta, idx_out, w_out=None, states_out=None, next_states_out=None,
@@ -316,6 +324,12 @@ class PerBuffer:
 
     def update(self, idx, td, stream=None):
         per_update(self.h, idx.numel(), idx, td, stream)
+
+    def update_add(self, idx, td, count, states=None, next_states=None, actions=None,
+                   rewards=None, dones=None, prio=None, stream=None):
+        """per_update_add: update(idx, td), then add(count, ...), in one launch."""
+        per_update_add(self.h, idx.numel(), idx, td, count, states, next_states, actions,
+                       rewards, dones, prio, stream)
 
     def sample(self, u, beta=0.4, weights=True, rows=False, out=None, stream=None):
         B = u.numel()

@@ -118,6 +118,8 @@ def test_null_handle_is_rejected(lib):
     assert lib.per_sample_rank(None, 1, 0x1000, 0.4, 0x1000, None, None, None, None, None, None,
                                None) == -1
     assert lib.per_graph_mode(None, 1, None) == -1
+    assert lib.per_update_add(None, 1, 0x1000, 0x1000, 1, None, None, None, None, None, None,
+                              None) == -1
     assert lib.per_total(None, 0x1000, None) == -1
     assert lib.per_destroy(None) == -1
     assert lib.per_size(None) == -1 and lib.per_cursor(None) == -1

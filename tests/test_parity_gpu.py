@@ -433,20 +433,22 @@ def _rows_np(rng, c, D):
             (rng.random(c) < 0.2).astype(np.uint8))
 
 
-@pytest.mark.parametrize("n,D,B,c,prio,uniform", [
-    (1 << 12, 8, 256, 300, False, False),   # one partition; the ring wraps every few replays
-    (1 << 16, 5, 1024, 3000, True, False),  # given priorities; scalar row copies
-    (1 << 20, 0, 8192, 5000, False, False),  # bucketed update: the overflow parity flips too
-    (1 << 13, 4, 500, 700, False, True),    # uniform sample over a ring still filling up
+@pytest.mark.parametrize("n,D,B,c,prio,uniform,fused", [
+    (1 << 12, 8, 256, 300, False, False, False),   # one partition; the ring wraps every few replays
+    (1 << 16, 5, 1024, 3000, True, False, False),  # given priorities; scalar row copies
+    (1 << 20, 0, 8192, 5000, False, False, False),  # bucketed update: the overflow parity flips too
+    (1 << 13, 4, 500, 700, False, True, False),    # uniform sample over a ring still filling up
+    (1 << 21, 0, 512, 400, False, False, True),    # the Ape-X shard step: sample, update + intake
+    (1 << 16, 5, 1024, 3000, True, False, True),   # fused, given priorities
 ])
-def test_graph_replay(n, D, B, c, prio, uniform):
+def test_graph_replay(n, D, B, c, prio, uniform, fused):
     """Two whole steps (intake, sample, update) issued in graph mode, first
     eagerly, then captured once in a torch CUDA graph and replayed with fresh
     inputs each time: after every replay both steps' samples and the trees
     match the oracle taken through the same steps, while the ring moves (and
     wraps) on the device only.  Leaving graph mode hands the device's ring
     state back to the host, and eager calls then carry on from it."""
-    say("graph replay", n, D, B, c, prio, uniform)
+    say("graph replay", n, D, B, c, prio, uniform, fused)
     rng = np.random.default_rng(n + c)
     o = Oracle(n, D)
     g = _buf(n, D, max_batch=max(B, 256))
@@ -484,23 +486,31 @@ def test_graph_replay(n, D, B, c, prio, uniform):
             s["td"].copy_(dev(x["td"]))
 
     def issue(k):
+        # a step: intake, sample, update -- or, fused: sample, update + intake
         s = stat[k]
-        g.add(c, *s["rows"], prio=s["prio"])
+        if not fused:
+            g.add(c, *s["rows"], prio=s["prio"])
         if uniform:
             g.sample_uniform(B, seeds[k][0], seeds[k][1], rows=D > 0, out=s["out"])
         else:
             g.sample(s["u"], beta=beta, weights=True, rows=D > 0, out=s["out"])
-        g.update(s["out"]["idx"], s["td"])
+        if fused:
+            g.update_add(s["out"]["idx"], s["td"], c, *s["rows"], prio=s["prio"])
+        else:
+            g.update(s["out"]["idx"], s["td"])
 
     def oracle_and_compare(xs, what):
         for k in range(2):
             x = xs[k]
-            o.add(c, *x["rows"], prio=x["prio"])
+            if not fused:
+                o.add(c, *x["rows"], prio=x["prio"])
             if uniform:
                 ro = o.sample_uniform(B, seeds[k][0], seeds[k][1], rows=D > 0)
             else:
                 ro = o.sample(x["u"], beta=beta, weights=True, rows=D > 0)
             o.update(ro["idx"], x["td"])
+            if fused:
+                o.add(c, *x["rows"], prio=x["prio"])
             compare_sample(stat[k]["out"], ro, "%s step %d" % (what, k), rows=D > 0,
                            weights=not uniform)
         compare_trees(o, g, what, ring=False)
@@ -553,6 +563,57 @@ def test_graph_mode_replay_rule():
         g.graph_mode(False)
     assert e.value.code == -1
     compare_trees(o, g, "after the rule check")
+
+
+@pytest.mark.parametrize("n,D,B,c,prio,fill", [
+    (1 << 21, 0, 512, 400, False, 1 << 21),    # the Ape-X shard step
+    (1 << 12, 8, 64, 300, False, 3000),        # one partition; the ring wraps inside it
+    (1 << 16, 5, 1000, 3000, True, 40000),     # given priorities; scalar row copies
+    (1 << 16, 4, 2000, 5000, False, 1 << 16),  # crowded partitions; the intake spans several
+    (1 << 20, 0, 8192, 700, False, 1 << 20),   # bucketed batch: enqueued as the two calls
+])
+def test_update_add(n, D, B, c, prio, fill):
+    """per_update_add against the oracle's update followed by its intake,
+    bit for bit: batches with repeats, skipped indices, NaN / Inf TD errors
+    and slots the intake overwrites at once; the running max, the ring and
+    the stored rows (through a sample) after every call."""
+    say("update_add", n, D, B, c, prio, fill)
+    rng = np.random.default_rng(n + B + c)
+    o = Oracle(n, D)
+    g = _buf(n, D, max_batch=max(B, 256))
+    r0 = _rows_np(rng, fill, D)
+    p0 = (rng.random(fill) * 2).astype(np.float32)
+    o.add(fill, *r0, prio=p0)
+    g.add(fill, *[dev(x) for x in r0], prio=dev(p0))
+    for step in range(6):
+        size, cur = o.size, o.cursor
+        idx = rng.integers(0, size, B).astype(np.int64)
+        k = B // 8
+        idx[:k] = (cur + rng.integers(0, c, k)) % n          # slots the intake takes next
+        idx[k:2 * k] = idx[2 * k:3 * k]                       # repeats: the last one wins
+        idx[3 * k] = -1
+        idx[3 * k + 1] = n + 5
+        # next to the run the intake takes: its boundary siblings' leaves
+        near = np.array([cur - 1, cur - 2, cur + c, cur + c + 1, cur - 37, cur + c + 100])
+        idx[3 * k + 2:3 * k + 8] = near % n
+        rng.shuffle(idx)
+        td = (rng.standard_normal(B) * 2).astype(np.float32)
+        td[rng.integers(0, B, 3)] = np.nan
+        if step % 2:
+            td[rng.integers(0, B, 2)] = np.inf
+        if step == 4:
+            td[rng.integers(0, B)] = 60.0  # the batch raises the running max the intake takes
+        rows = _rows_np(rng, c, D)
+        pr = (rng.random(c) * 8).astype(np.float32) if prio else None
+        o.update(idx, td)
+        o.add(c, *rows, prio=pr)
+        g.update_add(dev(idx), dev(td), c, *[dev(x) for x in rows],
+                     prio=None if pr is None else dev(pr))
+        compare_trees(o, g, "update_add step %d" % step)
+        if D:
+            u = rng.random(200, dtype=np.float32)
+            compare_sample(g.sample(dev(u), rows=True), o.sample(u, rows=True),
+                           "update_add step %d sample" % step, rows=True)
 
 
 # ------------------------------------------------------------ full-size large buffer
