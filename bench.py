@@ -113,8 +113,8 @@ def ingest_pmc(d: str) -> None:
                 continue  # only the fill before the timed steps
             kern, tot = {}, 0.0
             for k in names:
-                if k not in per_c[0]:
-                    continue
+                if k not in per_c[0] or len(per_c[0][k]) < 5:
+                    continue  # not run, or only by the set-up (the fill's intake)
                 f = float(np.median(per_c[0][k])) * calib["FETCH_SIZE"]["factor"] * 1024
                 wr = float(np.median(per_c[1][k])) * calib["WRITE_SIZE"]["factor"] * 1024
                 kern[k] = {"fetch_bytes": f, "write_bytes": wr, "dispatches": len(per_c[0][k])}
@@ -193,6 +193,55 @@ def graph_replay(g, step, K: int, base: int, stream, use_graph_mode: bool = True
             except Exception:
                 pass
         return {"error": "%s: %s" % (type(e).__name__, e)}
+
+
+def latency_floor() -> dict:
+    """The floor under a step of short launches (libper_probe.so): an empty
+    kernel launched back to back, and one lane's chain of dependent loads
+    through a random cyclic permutation -- in a 1 MiB table, warm in L2 (4
+    MiB per XCD), and over 100000 lines (12.5 MiB) of a 64 MiB table, warm
+    in the MALL but not in L2.  A descent pays one such load per tree level
+    below the levels it keeps in LDS."""
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "sum_tree_sampling_amd", "libper_probe.so"))
+    lib.per_probe_empty.argtypes = [ctypes.c_int64, ctypes.c_void_p]
+    lib.per_probe_chain.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                    ctypes.c_void_p, ctypes.c_void_p]
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def timed(fn) -> float:
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b)
+
+    def check(rc):
+        if rc != 0:
+            raise RuntimeError("latency probe failed (%d)" % rc)
+
+    K = 2000
+    check(lib.per_probe_empty(K, sp))
+    empty_us = timed(lambda: check(lib.per_probe_empty(K, sp))) * 1e3 / K
+    res = {"empty_kernel_us": empty_us}
+    rng = np.random.default_rng(0x1A7)
+    out = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for name, nbytes, depth in (("l2", 1 << 20, 20000), ("mall", 64 << 20, 100000)):
+        length = nbytes // 4
+        order = rng.permutation(length).astype(np.uint32)
+        nxt = np.empty(length, np.uint32)
+        nxt[order] = np.roll(order, -1)  # one cycle through every slot
+        d = torch.from_numpy(nxt.view(np.int32)).cuda()
+        torch.cuda.synchronize()
+        run = lambda: check(lib.per_probe_chain(ctypes.c_void_p(d.data_ptr()), length, depth,
+                                                ctypes.c_void_p(out.data_ptr()), sp))
+        run()  # warm: the timed walk revisits the same lines
+        res["%s_dependent_load_ns" % name] = timed(run) * 1e6 / depth
+        del d
+    return res
 
 
 def copy_calibration() -> None:
@@ -298,6 +347,8 @@ def main():
     ap.add_argument("--unfused", action="store_true",
                     help="the step's update and intake as two calls (per_update, per_add) "
                          "instead of the one per_update_add launch")
+    ap.add_argument("--no-latency-floor", action="store_true",
+                    help="skip the empty-kernel and dependent-load probes (profiling runs)")
     ap.add_argument("--graph-steps", type=int, default=64,
                     help="whole steps captured as one HIP graph for the labelled replay "
                          "figure (even; 0 skips it)")
@@ -495,6 +546,12 @@ def main():
     if kg > 0:
         graph = graph_replay(g, step, kg, base, stream, use_graph_mode=not args.rank)
 
+    floor = None
+    if not args.no_latency_floor:
+        floor = latency_floor()
+        floor["kernels_per_step"] = len(op_avg)
+        floor["launch_floor_us_per_step"] = floor["empty_kernel_us"] * len(op_avg)
+
     byts = algorithmic_bytes(spec)
     dom = max(op_avg, key=op_avg.get)
     achieved = byts[dom] / (op_avg[dom] * 1e-3) / 1e9
@@ -526,6 +583,7 @@ def main():
         "op_ms_avg": op_avg,
         "op_ms_bracketed": spread,
         "graph_replay": graph,
+        "latency_floor": floor,
         "host_ms_per_step": host_ms / args.steps,
         "step_algorithmic_bytes": step_bytes,
         "step_hbm_roofline_frac": step_bytes / (ms_per_step * 1e-3) / (PEAK_HBM_GBS * 1e9),

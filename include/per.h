@@ -13,8 +13,9 @@
  *    was created on).  Every device buffer is owned by the caller; the
  *    library never allocates or frees device memory.
  *  - Work is enqueued on the caller's stream and is ordered by it; no entry
- *    point synchronises the host with the device.  Inputs must stay alive and
- *    unchanged, and outputs untouched, until the stream has passed the call.
+ *    point synchronises the host with the device, except per_graph_mode
+ *    when it leaves graph mode.  Inputs must stay alive and unchanged, and
+ *    outputs untouched, until the stream has passed the call.
  *  - Host-side checks happen before anything is enqueued: on an error return
  *    nothing was enqueued and the handle is unchanged.
  *  - A handle may be used from one host thread at a time, and calls on one

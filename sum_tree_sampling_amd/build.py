@@ -1,4 +1,5 @@
-"""Compile the HIP library (libper.so) for gfx950, in-tree, with hipcc."""
+"""Compile the HIP library (libper.so) and the latency probe
+(libper_probe.so) for gfx950, in-tree, with hipcc."""
 from __future__ import annotations
 
 import os
@@ -10,6 +11,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libper.so")
 SOURCES = ["per_api.hip", "tree_kernels.hip", "sample_kernels.hip", "rank_kernels.hip"]
+PROBE_SRC = os.path.join(HERE, "probe", "latency_probe.hip")
+PROBE_LIB = os.path.join(HERE, "libper_probe.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # IEEE f32 arithmetic as written: no contraction into FMA, no fast-math, no
@@ -35,16 +38,19 @@ def _compile(src: str, obj: str) -> None:
 
 
 def build() -> str:
-    """Compile every source and link libper.so next to this file."""
+    """Compile every source and link libper.so (and libper_probe.so) next to
+    this file."""
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
-    objs = [os.path.join(objdir, s.replace(".hip", ".o")) for s in SOURCES]
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        list(ex.map(lambda so: _compile(*so), zip(SOURCES, objs)))
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
-    subprocess.check_call(cmd)
-    os.replace(tmp, LIB)
+    srcs = [os.path.join(CSRC, s) for s in SOURCES] + [PROBE_SRC]
+    objs = [os.path.join(objdir, os.path.basename(s).replace(".hip", ".o")) for s in srcs]
+    with ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        list(ex.map(lambda so: _compile(*so), zip(srcs, objs)))
+    for lib, lib_objs in ((LIB, objs[:-1]), (PROBE_LIB, objs[-1:])):
+        tmp = lib + ".tmp"
+        cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *lib_objs]
+        subprocess.check_call(cmd)
+        os.replace(tmp, lib)
     return LIB
 
 

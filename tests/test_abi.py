@@ -123,3 +123,31 @@ def test_null_handle_is_rejected(lib):
     assert lib.per_total(None, 0x1000, None) == -1
     assert lib.per_destroy(None) == -1
     assert lib.per_size(None) == -1 and lib.per_cursor(None) == -1
+
+
+PROBE_HEADER = os.path.join(ROOT, "include", "per_probe.h")
+PROBE_LIB = os.path.join(ROOT, "sum_tree_sampling_amd", "libper_probe.so")
+
+
+def test_probe_library_exports_and_checks():
+    """libper_probe.so exports what include/per_probe.h declares and rejects
+    bad arguments on the host (no launch is made for them)."""
+    if not os.path.exists(PROBE_LIB):
+        from sum_tree_sampling_amd import build
+        build.build()
+    text = re.sub(r"/\*.*?\*/", "", open(PROBE_HEADER).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(per_probe_[a-z_]+)\s*\(", text)))
+    assert names == ["per_probe_chain", "per_probe_empty"]
+    out = subprocess.run(["nm", "-D", "--defined-only", PROBE_LIB], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (per_probe_\w+)$", out, flags=re.M))
+    assert set(names) <= exported
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.per_probe_empty.argtypes = [ctypes.c_int64, ctypes.c_void_p]
+    lib.per_probe_chain.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                    ctypes.c_void_p, ctypes.c_void_p]
+    assert lib.per_probe_empty(0, None) == -1
+    assert lib.per_probe_chain(None, 1024, 10, 0x1000, None) == -1
+    assert lib.per_probe_chain(0x1000, 1000, 10, 0x1000, None) == -1   # not a power of two
+    assert lib.per_probe_chain(0x1000, 1024, 0, 0x1000, None) == -1
+    assert lib.per_probe_chain(0x1000, 1 << 31, 10, 0x1000, None) == -1
