@@ -167,13 +167,10 @@ __device__ void sparse_chain(const TreePtrs& t, const Geom& g, uint32_t part, in
       }
     }
     if (active) {
-      if (right) {
-        vs = os + vs;
-        vm = min_f32(om, vm);
-      } else {
-        vs = vs + os;
-        vm = min_f32(vm, om);
-      }
+      // f32 addition is commutative, and so is the min of priorities (never
+      // NaN or -0): the side of the child does not matter.
+      vs = vs + os;
+      vm = min_f32(vm, om);
       t.sum[child >> 1] = vs;
       t.mn[child >> 1] = vm;
     }
@@ -476,15 +473,28 @@ __device__ __forceinline__ void load_range_boundary(const TreePtrs& t, const Geo
   }
 }
 
+__device__ __forceinline__ float read_lane(float x, int k) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), k));
+}
+
 // Repair after a contiguous run [lo, hi) of new leaves that all take the
 // value v.  A node strictly between the run's first and last node of its
 // height k covers 2^k new leaves and nothing else: its sum is v doubled k
 // times, which is exactly what the pairwise adds of its subtree give, and
 // its min is v.  Those nodes and the leaves are stored by the whole block,
-// independently.  Only the first and last node of each height can have an
-// old leaf below; the block's first wave walks them up together (every lane
-// takes the same steps, lane 0 stores), the stored siblings coming from the
-// registers load_range_boundary filled.  No barrier anywhere.
+// independently.  Only the first and last node of each height (the run's two
+// boundary paths) can have an old leaf below, and the block's first wave
+// computes them.  Lane q first works out, for height q, the other child of
+// each path's node: a stored boundary sibling (from the registers
+// load_range_boundary filled: lane q the left one, lane 32 + q the right
+// one), an interior node, or -- where the paths meet -- the other path.
+// The wave then climbs the heights with one add and one min per path and
+// height (f32 addition is commutative, and so is the min of priorities,
+// which are never NaN or -0, so the order of the two children does not
+// matter), lane q keeping the two nodes of height q + 1; the lanes store
+// them together at the end.  A single instruction stream climbing S levels
+// costs several cycles per instruction, so the climb does nothing else.
+// No barrier anywhere.
 __device__ __forceinline__ void uniform_range(const TreePtrs& t, const Geom& g, uint32_t part,
                                               uint32_t lo, uint32_t hi, float v, float sib_s,
                                               float sib_m) {
@@ -494,41 +504,51 @@ __device__ __forceinline__ void uniform_range(const TreePtrs& t, const Geom& g, 
   // wait for those stores.
   asm volatile("" ::"v"(v), "v"(sib_s), "v"(sib_m));
   if (threadIdx.x < 64) {
-    uint32_t A = leaf0 + lo, Bn = leaf0 + hi - 1;  // first and last node of the height
-    float sL = v, mL = v, sR = v, mR = v;         // their sums and mins
-    float full = v;                               // sum of a node over new leaves only
-    for (int k = 0; k < g.S; ++k) {
-      // Siblings left of A (stored when A is a right child) and right of Bn
-      // (stored when Bn is a left child).
-      const float bls = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sib_s), k));
-      const float blm = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sib_m), k));
-      const float brs = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sib_s), 32 + k));
-      const float brm = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sib_m), 32 + k));
-      // Node A+1 (the right sibling of A when A is a left child) and node
-      // Bn-1 (the left sibling of Bn when Bn is a right child).
-      const float ns = (A + 1 < Bn) ? full : ((A + 1 == Bn) ? sR : brs);
-      const float nm = (A + 1 < Bn) ? v : ((A + 1 == Bn) ? mR : brm);
-      const float ps = (Bn - 1 > A) ? full : ((Bn - 1 == A) ? sL : bls);
-      const float pm = (Bn - 1 > A) ? v : ((Bn - 1 == A) ? mL : blm);
-      const float nls = (A & 1u) ? bls + sL : sL + ns;
-      const float nlm = (A & 1u) ? min_f32(blm, mL) : min_f32(mL, nm);
-      const float nrs = (Bn & 1u) ? ps + sR : sR + brs;
-      const float nrm = (Bn & 1u) ? min_f32(pm, mR) : min_f32(mR, brm);
-      A >>= 1;
-      Bn >>= 1;
-      if (threadIdx.x == 0) {
-        t.sum[A] = nls;
-        t.mn[A] = nlm;
-        if (Bn != A) {
-          t.sum[Bn] = nrs;
-          t.mn[Bn] = nrm;
+    const int lane = threadIdx.x;
+    const int q = lane & 31;
+    const float brs = __shfl(sib_s, 32 + q);  // right boundary siblings of height q
+    const float brm = __shfl(sib_m, 32 + q);
+    const uint32_t A = (leaf0 + lo) >> q, Bn = (leaf0 + hi - 1) >> q;  // the paths' nodes
+    const float full = v * __int_as_float((127 + q) << 23);           // v doubled q times
+    const bool merge = !(A & 1u) && A + 1u == Bn;  // the two paths share a parent
+    // The other child of each path's node at height q.
+    const float cls = (A & 1u) ? sib_s : ((A + 1u < Bn) ? full : brs);
+    const float clm = (A & 1u) ? sib_m : ((A + 1u < Bn) ? v : brm);
+    const float crs = (Bn & 1u) ? ((Bn - 1u > A) ? full : sib_s) : brs;
+    const float crm = (Bn & 1u) ? ((Bn - 1u > A) ? v : sib_m) : brm;
+    const uint64_t merges = __ballot(merge);
+    float sL = v, mL = v, sR = v, mR = v;      // the paths' nodes at the current height
+    float oLs = 0.0f, oLm = 0.0f, oRs = 0.0f, oRm = 0.0f;  // lane q: their parents
+#pragma unroll
+    for (int k = 0; k < kMaxSpanBits; ++k) {
+      if (k < g.S) {  // uniform
+        if ((merges >> k) & 1ull) {
+          sL = sL + sR;
+          mL = min_f32(mL, mR);
+          sR = sL;
+          mR = mL;
+        } else {
+          sL = sL + read_lane(cls, k);
+          mL = min_f32(mL, read_lane(clm, k));
+          sR = sR + read_lane(crs, k);
+          mR = min_f32(mR, read_lane(crm, k));
+        }
+        if (lane == k) {
+          oLs = sL;
+          oLm = mL;
+          oRs = sR;
+          oRm = mR;
         }
       }
-      sL = nls;
-      mL = nlm;
-      sR = nrs;
-      mR = nrm;
-      full = full + full;
+    }
+    if (lane < g.S) {
+      const uint32_t pa = A >> 1, pb = Bn >> 1;
+      t.sum[pa] = oLs;
+      t.mn[pa] = oLm;
+      if (pb != pa) {
+        t.sum[pb] = oRs;
+        t.mn[pb] = oRm;
+      }
     }
   }
   float full = v;  // sum of a node of height k covering new leaves only
