@@ -128,7 +128,7 @@ __device__ uint32_t block_max_bits(uint32_t v, BlockScratch& sx) {
 // chain ends exactly at the left child, whose value it holds, frozen.
 // Otherwise the other child is unchanged and its stored value is the
 // sibling's.  Must be called by all 64 lanes of the wave.
-__device__ void sparse_chain(const TreePtrs& t, const Geom& g, uint32_t part, int m, bool valid,
+__device__ __forceinline__ void sparse_chain(const TreePtrs& t, const Geom& g, uint32_t part, int m, bool valid,
                              uint32_t off, float p, const float* ps, const float* pm) {
   const int lane = threadIdx.x & 63;
   const uint32_t leaf = (part << g.S) + off;
@@ -265,7 +265,7 @@ __device__ __forceinline__ void publish_max(uint32_t mb, bool carry, float m0,
 // counted from LDS (m is small) -- so that the last batch position of each
 // offset is the last of its run, and repair the chains of those winners with
 // the prefetched siblings.
-__device__ void wave_update(SparseSmem& sp, const TreePtrs& t, const Geom& g, uint32_t part,
+__device__ __forceinline__ void wave_update(SparseSmem& sp, const TreePtrs& t, const Geom& g, uint32_t part,
                             int m) {
   const int lane = threadIdx.x & 63;
   const bool in = lane < m;
@@ -477,6 +477,40 @@ __device__ __forceinline__ float read_lane(float x, int k) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), k));
 }
 
+// The climb of uniform_range: the two boundary paths over `levels` heights
+// from the new leaves' value v, one add and one min per path and height with
+// the other children (cls, clm, crs, crm) of lane k at height k, or the
+// other path where merges has bit k.  Lane k keeps the nodes of height k + 1.
+// FIXED: levels is kMaxSpanBits, so the unrolled climb tests no level.
+template <bool FIXED>
+__device__ __forceinline__ void climb_paths(int levels, int lane, uint64_t merges, float v,
+                                            float cls, float clm, float crs, float crm,
+                                            float& oLs, float& oLm, float& oRs, float& oRm) {
+  float sL = v, mL = v, sR = v, mR = v;  // the paths' nodes at the current height
+#pragma unroll
+  for (int k = 0; k < kMaxSpanBits; ++k) {
+    if (FIXED || k < levels) {  // uniform
+      if ((merges >> k) & 1ull) {
+        sL = sL + sR;
+        mL = min_f32(mL, mR);
+        sR = sL;
+        mR = mL;
+      } else {
+        sL = sL + read_lane(cls, k);
+        mL = min_f32(mL, read_lane(clm, k));
+        sR = sR + read_lane(crs, k);
+        mR = min_f32(mR, read_lane(crm, k));
+      }
+      if (lane == k) {
+        oLs = sL;
+        oLm = mL;
+        oRs = sR;
+        oRm = mR;
+      }
+    }
+  }
+}
+
 // Repair after a contiguous run [lo, hi) of new leaves that all take the
 // value v.  A node strictly between the run's first and last node of its
 // height k covers 2^k new leaves and nothing else: its sum is v doubled k
@@ -493,8 +527,9 @@ __device__ __forceinline__ float read_lane(float x, int k) {
 // which are never NaN or -0, so the order of the two children does not
 // matter), lane q keeping the two nodes of height q + 1; the lanes store
 // them together at the end.  A single instruction stream climbing S levels
-// costs several cycles per instruction, so the climb does nothing else.
-// No barrier anywhere.
+// costs several cycles per instruction, so the climb does nothing else, and
+// the other waves store the leaves and the interior nodes meanwhile.  No
+// barrier anywhere.
 __device__ __forceinline__ void uniform_range(const TreePtrs& t, const Geom& g, uint32_t part,
                                               uint32_t lo, uint32_t hi, float v, float sib_s,
                                               float sib_m) {
@@ -517,30 +552,11 @@ __device__ __forceinline__ void uniform_range(const TreePtrs& t, const Geom& g, 
     const float crs = (Bn & 1u) ? ((Bn - 1u > A) ? full : sib_s) : brs;
     const float crm = (Bn & 1u) ? ((Bn - 1u > A) ? v : sib_m) : brm;
     const uint64_t merges = __ballot(merge);
-    float sL = v, mL = v, sR = v, mR = v;      // the paths' nodes at the current height
-    float oLs = 0.0f, oLm = 0.0f, oRs = 0.0f, oRm = 0.0f;  // lane q: their parents
-#pragma unroll
-    for (int k = 0; k < kMaxSpanBits; ++k) {
-      if (k < g.S) {  // uniform
-        if ((merges >> k) & 1ull) {
-          sL = sL + sR;
-          mL = min_f32(mL, mR);
-          sR = sL;
-          mR = mL;
-        } else {
-          sL = sL + read_lane(cls, k);
-          mL = min_f32(mL, read_lane(clm, k));
-          sR = sR + read_lane(crs, k);
-          mR = min_f32(mR, read_lane(crm, k));
-        }
-        if (lane == k) {
-          oLs = sL;
-          oLm = mL;
-          oRs = sR;
-          oRm = mR;
-        }
-      }
-    }
+    float oLs = 0.0f, oLm = 0.0f, oRs = 0.0f, oRm = 0.0f;  // lane q: the parents of height q
+    if (g.S == kMaxSpanBits)  // the usual partition: no per-level test in the climb
+      climb_paths<true>(kMaxSpanBits, lane, merges, v, cls, clm, crs, crm, oLs, oLm, oRs, oRm);
+    else
+      climb_paths<false>(g.S, lane, merges, v, cls, clm, crs, crm, oLs, oLm, oRs, oRm);
     if (lane < g.S) {
       const uint32_t pa = A >> 1, pb = Bn >> 1;
       t.sum[pa] = oLs;
@@ -551,15 +567,20 @@ __device__ __forceinline__ void uniform_range(const TreePtrs& t, const Geom& g, 
       }
     }
   }
-  float full = v;  // sum of a node of height k covering new leaves only
-  for (int k = 0; k <= g.S; ++k) {
-    const uint32_t A = (leaf0 + lo) >> k, Bn = (leaf0 + hi - 1) >> k;
-    const uint32_t first = (k == 0) ? A : A + 1;
-    for (uint32_t x = first + threadIdx.x; x < Bn + (k == 0 ? 1u : 0u); x += kTreeThreads) {
-      t.sum[x] = full;
-      t.mn[x] = v;
+  // The leaves and the interior nodes, by the other waves, while the first
+  // wave climbs.
+  if (threadIdx.x >= 64) {
+    float full = v;  // sum of a node of height k covering new leaves only
+    for (int k = 0; k <= g.S; ++k) {
+      const uint32_t A = (leaf0 + lo) >> k, Bn = (leaf0 + hi - 1) >> k;
+      const uint32_t first = (k == 0) ? A : A + 1;
+      for (uint32_t x = first + threadIdx.x - 64; x < Bn + (k == 0 ? 1u : 0u);
+           x += kTreeThreads - 64) {
+        t.sum[x] = full;
+        t.mn[x] = v;
+      }
+      full = full + full;
     }
-    full = full + full;
   }
 }
 
@@ -926,7 +947,7 @@ __device__ __forceinline__ void commit_ring(const TreePtrs& t, const Geom& g, co
 
 // Row copy of the intake's transitions into their ring slots, by the blocks
 // [first, gridDim.x) of the launch.
-__device__ void copy_intake_rows(const Storage& st, const Geom& g, const AddArgs& a,
+__device__ __forceinline__ void copy_intake_rows(const Storage& st, const Geom& g, const AddArgs& a,
                                  uint32_t cursor, uint32_t first) {
   const uint32_t nb = gridDim.x - first;
   const uint32_t tid = (blockIdx.x - first) * kTreeThreads + threadIdx.x;
