@@ -37,7 +37,14 @@ namespace {
 
 constexpr int kSampleThreads = 256;
 
-__device__ __forceinline__ float min_f32(float a, float b) { return (b < a) ? b : a; }
+// The min of two tree values.  Every value stored in or compared by these
+// trees is a priority or a sum of priorities: +0, a positive finite value or
+// +inf, never NaN or -0 (a given -0 priority is stored as +0).  For those the
+// f32 bit patterns order like the values, so the min is one integer min of
+// the bits, with the same result as (b < a) ? b : a.
+__device__ __forceinline__ float min_f32(float a, float b) {
+  return __uint_as_float(min(__float_as_uint(a), __float_as_uint(b)));
+}
 
 struct SampleArgs {
   float* sum;

@@ -47,7 +47,14 @@ constexpr int kSubBits = 10;  // crowded partitions are rebuilt in 2^10-leaf pie
 constexpr int kUpdThreads = 256;  // threads of an update block
 constexpr int kSub = 1 << kSubBits;
 
-__device__ __forceinline__ float min_f32(float a, float b) { return (b < a) ? b : a; }
+// The min of two tree values.  Every value stored in or compared by these
+// trees is a priority or a sum of priorities: +0, a positive finite value or
+// +inf, never NaN or -0 (a given -0 priority is stored as +0).  For those the
+// f32 bit patterns order like the values, so the min is one integer min of
+// the bits, with the same result as (b < a) ? b : a.
+__device__ __forceinline__ float min_f32(float a, float b) {
+  return __uint_as_float(min(__float_as_uint(a), __float_as_uint(b)));
+}
 
 // Priority of one TD error: f32 of (|td| + eps)^alpha in f64
 // ("GPU-Resident Prioritized Experience Replay", section "Priority update";
@@ -473,40 +480,37 @@ __device__ __forceinline__ void load_range_boundary(const TreePtrs& t, const Geo
   }
 }
 
-__device__ __forceinline__ float read_lane(float x, int k) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), k));
-}
-
 // The climb of uniform_range: the two boundary paths over `levels` heights
 // from the new leaves' value v, one add and one min per path and height with
-// the other children (cls, clm, crs, crm) of lane k at height k, or the
-// other path where merges has bit k.  Lane k keeps the nodes of height k + 1.
+// the other children other[k] (left path's sum and min, right path's sum and
+// min) at height k, or the other path where merges has bit k.  Lane k keeps
+// the nodes of height k + 1.
 // FIXED: levels is kMaxSpanBits, so the unrolled climb tests no level.
 template <bool FIXED>
 __device__ __forceinline__ void climb_paths(int levels, int lane, uint64_t merges, float v,
-                                            float cls, float clm, float crs, float crm,
-                                            float& oLs, float& oLm, float& oRs, float& oRm) {
+                                            const float4* other, float& oLs, float& oLm,
+                                            float& oRs, float& oRm) {
   float sL = v, mL = v, sR = v, mR = v;  // the paths' nodes at the current height
 #pragma unroll
   for (int k = 0; k < kMaxSpanBits; ++k) {
     if (FIXED || k < levels) {  // uniform
-      if ((merges >> k) & 1ull) {
-        sL = sL + sR;
-        mL = min_f32(mL, mR);
-        sR = sL;
-        mR = mL;
-      } else {
-        sL = sL + read_lane(cls, k);
-        mL = min_f32(mL, read_lane(clm, k));
-        sR = sR + read_lane(crs, k);
-        mR = min_f32(mR, read_lane(crm, k));
-      }
-      if (lane == k) {
-        oLs = sL;
-        oLm = mL;
-        oRs = sR;
-        oRm = mR;
-      }
+      // Where the paths meet, each takes the other as its other child (the
+      // two sums and the two mins are then equal).
+      const bool meet = (merges >> k) & 1ull;
+      const float4 c = other[k];  // the same LDS word for every lane
+      const float aLs = meet ? sR : c.x;
+      const float aLm = meet ? mR : c.y;
+      const float aRs = meet ? sL : c.z;
+      const float aRm = meet ? mL : c.w;
+      sL = sL + aLs;
+      mL = min_f32(mL, aLm);
+      sR = sR + aRs;
+      mR = min_f32(mR, aRm);
+      const bool mine = lane == k;
+      oLs = mine ? sL : oLs;
+      oLm = mine ? mL : oLm;
+      oRs = mine ? sR : oRs;
+      oRm = mine ? mR : oRm;
     }
   }
 }
@@ -552,11 +556,17 @@ __device__ __forceinline__ void uniform_range(const TreePtrs& t, const Geom& g, 
     const float crs = (Bn & 1u) ? ((Bn - 1u > A) ? full : sib_s) : brs;
     const float crm = (Bn & 1u) ? ((Bn - 1u > A) ? v : sib_m) : brm;
     const uint64_t merges = __ballot(merge);
+    // Handed to the climb through LDS: a lane reading the word of height k
+    // is an ordinary load the compiler may schedule early, where reading it
+    // from lane k's registers is an operation it must not hoist.
+    __shared__ float4 other[kMaxSpanBits];
+    if (lane < g.S) other[lane] = make_float4(cls, clm, crs, crm);
+    __builtin_amdgcn_wave_barrier();
     float oLs = 0.0f, oLm = 0.0f, oRs = 0.0f, oRm = 0.0f;  // lane q: the parents of height q
     if (g.S == kMaxSpanBits)  // the usual partition: no per-level test in the climb
-      climb_paths<true>(kMaxSpanBits, lane, merges, v, cls, clm, crs, crm, oLs, oLm, oRs, oRm);
+      climb_paths<true>(kMaxSpanBits, lane, merges, v, other, oLs, oLm, oRs, oRm);
     else
-      climb_paths<false>(g.S, lane, merges, v, cls, clm, crs, crm, oLs, oLm, oRs, oRm);
+      climb_paths<false>(g.S, lane, merges, v, other, oLs, oLm, oRs, oRm);
     if (lane < g.S) {
       const uint32_t pa = A >> 1, pb = Bn >> 1;
       t.sum[pa] = oLs;
