@@ -30,6 +30,7 @@
 #include <cstdlib>
 #include <type_traits>
 
+#include "lanes.h"
 #include "per_internal.h"
 
 namespace per {
@@ -75,50 +76,6 @@ struct SampleArgs {
   int nrounds;
   int rounds[kMaxRounds];
 };
-
-// Lane exchanges within a wave that avoid the LDS crossbar a general
-// shuffle goes through (a round trip of the memory pipeline): DPP moves
-// inside 16-lane rows, a swizzle inside 32-lane halves, a lane read.
-// xor_lanes(x, s): the value of lane i ^ 2^s.
-__device__ __forceinline__ float xor_lanes(float x, int s) {
-  const int v = __float_as_int(x);
-  switch (s) {  // s is a constant wherever this is unrolled
-    case 0:  // quad_perm [1,0,3,2]
-      return __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, true));
-    case 1:  // quad_perm [2,3,0,1]
-      return __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, true));
-    case 2: {  // row_half_mirror (lane i ^ 7), then quad_perm [3,2,1,0] (i ^ 3)
-      const int h = __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, true);
-      return __int_as_float(__builtin_amdgcn_update_dpp(0, h, 0x1B, 0xF, 0xF, true));
-    }
-    case 3:  // row_ror:8
-      return __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x128, 0xF, 0xF, true));
-    case 4:  // swizzle, bit mode: xor 16
-      return __int_as_float(__builtin_amdgcn_ds_swizzle(v, 0x401F));
-    default:
-      return __shfl_xor(x, 1 << s);
-  }
-}
-
-// down_lanes(x, q): the value of lane i + 2^q, for the lanes i that are
-// multiples of 2^(q+1) (the only ones that use it).
-__device__ __forceinline__ float down_lanes(float x, int q) {
-  const int v = __float_as_int(x);
-  switch (q) {  // q is a constant wherever this is unrolled
-    case 0:  // row_shl:1
-      return __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x101, 0xF, 0xF, true));
-    case 1:  // row_shl:2
-      return __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x102, 0xF, 0xF, true));
-    case 2:  // row_shl:4
-      return __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x104, 0xF, 0xF, true));
-    case 3:  // row_shl:8
-      return __int_as_float(__builtin_amdgcn_update_dpp(0, v, 0x108, 0xF, 0xF, true));
-    case 4:  // swizzle, bit mode: xor 16
-      return __int_as_float(__builtin_amdgcn_ds_swizzle(v, 0x401F));
-    default:  // lane 32, for lane 0
-      return __int_as_float(__builtin_amdgcn_readlane(v, 32));
-  }
-}
 
 // Pairwise (heap-order) sum of LEN register values: the value of their
 // common ancestor node.

@@ -38,6 +38,7 @@
 
 #include <type_traits>
 
+#include "lanes.h"
 #include "per_internal.h"
 
 namespace per {
@@ -97,12 +98,6 @@ __device__ int block_excl_scan(int v, BlockScratch& sx, int* total) {
   return off + x - v;
 }
 
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
-  return v;
-}
-
 // Block max of f32 bit patterns of non-negative values (0 if none); NT
 // threads per block.
 template <int NT = kTreeThreads>
@@ -144,7 +139,7 @@ __device__ __forceinline__ void sparse_chain(const TreePtrs& t, const Geom& g, u
     t.sum[node] = p;
     t.mn[node] = p;
   }
-  const uint32_t next_leaf = __shfl_down(leaf, 1);
+  const uint32_t next_leaf = next_lane(leaf);
   int d = g.P - 1;
   if (lane < m - 1) d = g.L - 1 - (31 - __clz(leaf ^ next_leaf));
 
