@@ -279,6 +279,11 @@ __device__ __forceinline__ void emit(const SampleArgs& a, uint32_t wave, int lan
 template <int G, int V, bool STREAM>
 __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleArgs a) {
   extern __shared__ float top[];  // nodes [0, 2^(K+1)) of the sum tree
+  // The arguments the first steps need, fetched in one batch: left to
+  // itself, the compiler loads each after the branch that first needs it,
+  // one dependent trip each.
+  asm volatile("" ::"s"(a.top_mode), "s"(a.P), "s"(a.sum), "s"(a.mn), "s"(a.u), "s"(a.B),
+               "s"(a.top), "s"(a.nrounds), "s"(a.write_top));
   constexpr int LOGG = ilog2(G);
   constexpr int LOGV = ilog2(V);
   constexpr int SPW = 64 / G;  // samples per wave

@@ -786,6 +786,9 @@ __device__ __forceinline__ bool scan_update(SM& sm, const TreePtrs& t, const Geo
 template <int PPB>
 __global__ void __launch_bounds__(kUpdThreads) update_scan_kernel(TreePtrs t, Geom g, UpdateArgs a) {
   __shared__ UpdSmem<PPB> sm;
+  // The arguments the first steps need, fetched in one batch.
+  asm volatile("" ::"s"(t.ctrl), "s"(a.idx), "s"(a.td), "s"(a.B), "s"(a.src), "s"(a.size),
+               "s"(a.ring.dev), "s"(g.n), "s"(g.S));
   const float m0 = __uint_as_float(t.ctrl->maxp_bits[a.src]);
   scan_update<PPB, false>(sm, t, g, a, blockIdx.x * PPB, filled_size(a), m0, false,
                           [](uint32_t) { return false; });
@@ -917,6 +920,7 @@ struct AddArgs {
   RingRef ring;            // ring.dev: cursor and size come from ctrl slot ring.slot
   const float* prio;
   uint32_t ntree;  // blocks set aside for tree work (the rest copy rows)
+  uint32_t last;   // the launch's last block, which commits the ring state
   int src, dst;    // running-max slots: read / raise
   const float* states;
   const float* next_states;
@@ -942,7 +946,7 @@ __device__ __forceinline__ void ring_state(const TreePtrs& t, const AddArgs& a, 
 // wait on the store.
 __device__ __forceinline__ void commit_ring(const TreePtrs& t, const Geom& g, const AddArgs& a,
                                             uint32_t cursor, uint32_t size) {
-  if (blockIdx.x == gridDim.x - 1 && threadIdx.x == 0) {
+  if (blockIdx.x == a.last && threadIdx.x == 0) {
     const uint64_t next = (uint64_t)cursor + a.count;
     const uint64_t filled = (uint64_t)size + a.count;
     t.ctrl->cursor[a.ring.slot ^ 1] = (uint32_t)(next >= g.n ? next - g.n : next);
@@ -951,10 +955,10 @@ __device__ __forceinline__ void commit_ring(const TreePtrs& t, const Geom& g, co
 }
 
 // Row copy of the intake's transitions into their ring slots, by the blocks
-// [first, gridDim.x) of the launch.
+// [first, a.last] of the launch.
 __device__ __forceinline__ void copy_intake_rows(const Storage& st, const Geom& g, const AddArgs& a,
                                  uint32_t cursor, uint32_t first) {
-  const uint32_t nb = gridDim.x - first;
+  const uint32_t nb = a.last + 1u - first;
   const uint32_t tid = (blockIdx.x - first) * kTreeThreads + threadIdx.x;
   const uint32_t stride = nb * kTreeThreads;
   const uint32_t D = (uint32_t)st.D;
@@ -1137,6 +1141,11 @@ template <bool PRIO>
 __global__ void __launch_bounds__(kUpdThreads) update_add_kernel(TreePtrs t, Geom g, Storage st,
                                                                  UpdateArgs a, AddArgs b) {
   __shared__ std::conditional_t<PRIO, UpdAddSmem, UpdSmem<1>> sm;
+  // The arguments the first steps need, fetched in one batch: left to
+  // itself, the compiler loads each after the branch that first needs it,
+  // one dependent trip each.
+  asm volatile("" ::"s"(t.ctrl), "s"(a.idx), "s"(a.td), "s"(a.B), "s"(a.src), "s"(b.cursor),
+               "s"(b.count), "s"(b.size), "s"(b.ring.dev), "s"(b.last), "s"(g.n), "s"(g.S));
   uint32_t cursor, size;
   ring_state(t, b, cursor, size);
   commit_ring(t, g, b, cursor, size);
@@ -1314,6 +1323,7 @@ hipError_t launch_add(const TreePtrs& t, const Geom& g, const Storage& st, RingR
   unsigned ncopy = 0;
   if (st.D > 0)
     ncopy = grid_for((uint64_t)count * (uint64_t)st.D / 4 + count, kTreeThreads * 4, 2048);
+  a.last = a.ntree + ncopy - 1u;
   hipLaunchKernelGGL(add_kernel, dim3(a.ntree + ncopy), dim3(kTreeThreads), 0, s, t, g, st, a);
   return hipGetLastError();
 }
@@ -1355,6 +1365,7 @@ hipError_t launch_update_add(const TreePtrs& t, const Geom& g, const Storage& st
   unsigned ncopy = 0;
   if (st.D > 0)
     ncopy = grid_for((uint64_t)count * (uint64_t)st.D / 4 + count, kTreeThreads * 4, 2048);
+  b.last = np + ncopy - 1u;
   if (prio)
     hipLaunchKernelGGL(update_add_kernel<true>, dim3(np + ncopy), dim3(kUpdThreads), 0, s, t, g,
                        st, a, b);
