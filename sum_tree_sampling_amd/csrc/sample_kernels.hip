@@ -506,6 +506,9 @@ __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleArgs a) {
 // filled slot, which the wave's row copy relies on.
 template <int G>
 __global__ void __launch_bounds__(kSampleThreads) uniform_kernel(SampleArgs a) {
+  // The arguments the first steps need, fetched in one batch.
+  asm volatile("" ::"s"(a.seed), "s"(a.offset), "s"(a.size), "s"(a.dev_size), "s"(a.B),
+               "s"(a.idx_out), "s"(a.st.D));
   constexpr int SPW = 64 / G;
   const int lane = threadIdx.x & 63;
   const uint32_t wave = blockIdx.x * (kSampleThreads / 64) + (threadIdx.x >> 6);

@@ -797,10 +797,14 @@ __global__ void __launch_bounds__(kUpdThreads) update_scan_kernel(TreePtrs t, Ge
 // Large batches, step 1: every valid entry goes to its partition's bucket
 // (kBucketCap entries per partition); past the cap, to an overflow list.
 __global__ void __launch_bounds__(256) bucket_kernel(Buckets bk, Geom g, UpdateArgs a) {
-  const uint32_t b = blockIdx.x * blockDim.x + threadIdx.x;
+  // The arguments the first steps need, fetched in one batch.
+  asm volatile("" ::"s"(a.idx), "s"(a.td), "s"(a.B), "s"(a.size), "s"(a.ring.dev),
+               "s"(bk.counts), "s"(g.S));
+  const uint32_t b = blockIdx.x * kTreeThreads + threadIdx.x;  // launched with kTreeThreads
   if (b >= a.B) return;
   const int64_t i = a.idx[b];
   const float x = a.td[b];
+  asm volatile("" ::"v"(i), "v"(x));  // both loads out before either is looked at
   if (i < 0 || i >= (int64_t)filled_size(a)) return;
   const uint32_t part = (uint32_t)((uint64_t)i >> g.S);
   const uint32_t k = atomicAdd(&bk.counts[part], 1u);
@@ -825,6 +829,9 @@ template <int PPB>
 __global__ void __launch_bounds__(kUpdThreads) update_bucket_kernel(TreePtrs t, Buckets bk, Geom g,
                                                             UpdateArgs a) {
   __shared__ UpdSmem<PPB> sm;
+  // The arguments the first steps need, fetched in one batch.
+  asm volatile("" ::"s"(t.ctrl), "s"(a.src), "s"(a.dst), "s"(a.ovf), "s"(bk.counts),
+               "s"(bk.slot), "s"(bk.pos), "s"(bk.td), "s"(g.P), "s"(g.S), "s"(g.n));
   const uint32_t part0 = blockIdx.x * PPB;
   const int nparts = (int)min((uint32_t)PPB, (1u << g.P) - part0);
   const float m0 = __uint_as_float(t.ctrl->maxp_bits[a.src]);
@@ -1096,6 +1103,9 @@ __device__ __forceinline__ void intake_partition(SM& sm, const TreePtrs& t, cons
 // max priority; rows are copied by the blocks past the tree blocks.
 __global__ void __launch_bounds__(256) add_kernel(TreePtrs t, Geom g, Storage st, AddArgs a) {
   __shared__ AddSmem sm;
+  // The arguments the first steps need, fetched in one batch.
+  asm volatile("" ::"s"(t.ctrl), "s"(a.cursor), "s"(a.count), "s"(a.size), "s"(a.ring.dev),
+               "s"(a.last), "s"(a.ntree), "s"(a.src), "s"(a.prio), "s"(g.n), "s"(g.S));
   uint32_t cursor, size;
   ring_state(t, a, cursor, size);
   commit_ring(t, g, a, cursor, size);
