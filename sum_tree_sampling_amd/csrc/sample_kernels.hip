@@ -294,6 +294,10 @@ __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleArgs a) {
   const uint32_t wave = blockIdx.x * (kSampleThreads / 64) + (threadIdx.x >> 6);
   const uint32_t b = wave * SPW + (uint32_t)(lane / G);
   const bool active = b < a.B;
+  // The sample's mass is fetched first, so that its trip overlaps the
+  // top rebuild's loads instead of following them.
+  float ub = 0.0f;
+  if (!STREAM && active) ub = a.u[b];
 
   float T, pmin;
   if (a.top_mode == kTopRebuild) {
@@ -428,8 +432,7 @@ __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleArgs a) {
     pmin = a.mn[1];
   }
 
-  float ub = 0.0f;
-  if (active) ub = STREAM ? stream_uniform(stream_word(a.seed, a.offset + b)) : a.u[b];
+  if (STREAM && active) ub = stream_uniform(stream_word(a.seed, a.offset + b));
   float m = ub * T;
   if (!(m < T)) m = __uint_as_float(__float_as_uint(T) - 1u);  // largest f32 below T
 
