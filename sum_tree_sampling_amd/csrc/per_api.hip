@@ -517,7 +517,7 @@ RankLayout rank_layout(int64_t n) {
   l.keys1 = take(sizeof(uint32_t) * (size_t)n);
   l.vals0 = take(sizeof(uint32_t) * (size_t)n);
   l.vals1 = take(sizeof(uint32_t) * (size_t)n);
-  l.hist = take(sizeof(uint32_t) * 16 * (size_t)per::rank_tiles(n));
+  l.hist = take(sizeof(uint32_t) * per::rank_hist_words(n));
   l.total = o;
   return l;
 }

@@ -145,13 +145,13 @@ SamplePlan make_sample_plan(const Geom& g, int64_t B);
 
 // Rank-based prioritisation: a stable radix sort of the slots [0, count) by
 // descending leaf priority (keys / vals: two ping-pong buffers of n words,
-// the ranking ends in vals[0]; hist: 16 * rank_tiles(n) words), and the
+// the ranking ends in vals[0]; hist: rank_hist_words(n) words), and the
 // build of the trees over the rank weights (count filled ranks).
 hipError_t launch_rank_sort(const float* leaves, uint32_t count, uint32_t* const keys[2],
                             uint32_t* const vals[2], uint32_t* hist, hipStream_t s);
 hipError_t launch_rank_build(const TreePtrs& rt, const Geom& g, uint32_t count, double alpha,
                              hipStream_t s);
-uint32_t rank_tiles(int64_t n);
+size_t rank_hist_words(int64_t n);
 
 // Uniform sample of B slots over [0, size) from the generator stream (size
 // read from ctrl slot ring.slot when ring.dev).

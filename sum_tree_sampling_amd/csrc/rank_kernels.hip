@@ -8,11 +8,16 @@
 //  * the ranking is a stable least-significant-digit radix sort of the slots
 //    [0, count) on the key ~bits(priority) (for priorities >= 0 the f32 bit
 //    patterns order like the values, so ascending keys are descending
-//    priorities; stability keeps equal priorities in slot order): eight
-//    passes of 4-bit digits over tiles of 4096 items -- a histogram of each
-//    tile, one scan of all tile histograms, and a scatter in which every
-//    thread writes its 16 consecutive items in order, so that each digit's
-//    items keep their order;
+//    priorities; stability keeps equal priorities in slot order): four
+//    passes of 8-bit digits over tiles of 4096 items.  A tile is read
+//    striped (wave w, step i, lane l holds item 1024 w + 64 i + l), so a
+//    wave's steps visit its items in order; in each step the lanes holding
+//    one digit find each other by eight ballots, which ranks every item
+//    among the earlier items of its digit without a per-thread counter
+//    table.  A pass is the tile histograms, a scan of each digit's row of
+//    tile counts, and a scatter that stages the tile in digit order in LDS
+//    and writes each digit's run to consecutive addresses.  The first pass
+//    reads the priorities themselves.
 //  * the cumulative sum is a tree over the rank weights f32((r+1)^-alpha)
 //    built with the priority trees' rules (sum and min of the two children),
 //    so the proportional descent over it gives the rank of a mass exactly.
@@ -24,180 +29,188 @@
 namespace per {
 namespace {
 
-constexpr int kRankThreads = 256;
-constexpr int kItems = 16;                                // consecutive items per thread
-constexpr uint32_t kTile = kRankThreads * kItems;         // 4096
-constexpr int kDigitBits = 4;
-constexpr int kDigits = 1 << kDigitBits;
+constexpr int kRankThreads = 256;                   // four waves
+constexpr int kItems = 16;                          // steps per wave
+constexpr uint32_t kTile = kRankThreads * kItems;   // 4096
+constexpr uint32_t kWaveItems = kTile / 4;          // 1024
+constexpr int kDigitBits = 8;
+constexpr int kDigits = 1 << kDigitBits;            // 256 = kRankThreads
+constexpr int kPasses = 32 / kDigitBits;
 
 __device__ __forceinline__ float rank_min(float a, float b) { return (b < a) ? b : a; }
 
-// Keys and values of the first pass, straight from the priority leaves.
-__global__ void __launch_bounds__(256) rank_seed_kernel(const float* leaves, uint32_t count,
-                                                        uint32_t* keys, uint32_t* vals) {
-  const uint32_t i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < count) {
-    keys[i] = ~__float_as_uint(leaves[i]);
-    vals[i] = i;
-  }
+// Item `i` of this lane in its tile's striped order, as an index into [0, count).
+__device__ __forceinline__ uint32_t striped_item(int i) {
+  return blockIdx.x * kTile + (threadIdx.x >> 6) * kWaveItems + (uint32_t)i * 64u +
+         (threadIdx.x & 63u);
 }
 
-// Per-thread digit counts of one tile in LDS, digit-major (cnt[d][t]); on
-// return cnt holds, for every digit, the exclusive prefix over the threads
-// (the tile-local position of each thread's first item of that digit), and
-// tot[d] the tile's count of digit d.
-struct TileSmem {
-  uint32_t cnt[kDigits * kRankThreads];
-  uint32_t tot[kDigits];
-};
-
-__device__ __forceinline__ void tile_counts(TileSmem& sm, const uint32_t* k, int nvalid,
-                                            int shift) {
-  const int t = threadIdx.x;
-#pragma unroll
-  for (int d = 0; d < kDigits; ++d) sm.cnt[d * kRankThreads + t] = 0u;
-  // Own column only, so no two threads touch one counter; LDS adds without a
-  // returned value issue back to back instead of as 16 dependent round trips.
-#pragma unroll
-  for (int i = 0; i < kItems; ++i)
-    if (i < nvalid) atomicAdd(&sm.cnt[((k[i] >> shift) & (kDigits - 1)) * kRankThreads + t], 1u);
-  __syncthreads();
-  // Thread t scans the 16 entries [16t, 16t + 16) (digit t / 16), then the
-  // 16 segments of a digit (16 consecutive lanes of one wave) meet by shuffle.
-  uint32_t* seg = sm.cnt + t * kItems;
-  uint32_t run = 0;
+// The tile's keys (and values) of this lane; FIRST: from the priorities, the
+// value being the slot.  ok[i]: the item exists.
+template <bool FIRST, bool VALS>
+__device__ __forceinline__ void load_striped(const uint32_t* keys, const uint32_t* vals,
+                                             const float* leaves, uint32_t count,
+                                             uint32_t k[kItems], uint32_t v[kItems],
+                                             bool ok[kItems]) {
 #pragma unroll
   for (int i = 0; i < kItems; ++i) {
-    const uint32_t c = seg[i];
-    seg[i] = run;
-    run += c;
+    const uint32_t x = striped_item(i);
+    ok[i] = x < count;
+    const uint32_t xs = ok[i] ? x : 0u;
+    if constexpr (FIRST) {
+      k[i] = ~__float_as_uint(leaves[xs]);
+      if constexpr (VALS) v[i] = x;
+    } else {
+      k[i] = keys[xs];
+      if constexpr (VALS) v[i] = vals[xs];
+    }
   }
-  uint32_t inc = run;
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) {
-    const uint32_t y = __shfl_up(inc, o, 16);
-    if ((t & 15) >= o) inc += y;
-  }
-  const uint32_t excl = inc - run;
-#pragma unroll
-  for (int i = 0; i < kItems; ++i) seg[i] += excl;
-  if ((t & 15) == 15) sm.tot[t >> 4] = inc;
-  __syncthreads();
 }
 
-__device__ __forceinline__ int load_tile(const uint32_t* src, uint32_t count, uint32_t* k) {
-  const uint32_t first = blockIdx.x * kTile + threadIdx.x * kItems;
-  const int nvalid = (first >= count) ? 0 : (int)min((uint32_t)kItems, count - first);
-  if (nvalid == kItems) {
+// The lanes of the wave whose item exists and has digit d (this lane's own
+// digit): one ballot per digit bit.  Every lane of the wave takes part.
+__device__ __forceinline__ uint64_t digit_peers(uint32_t d, bool ok) {
+  uint64_t m = __ballot(ok);
 #pragma unroll
-    for (int i = 0; i < kItems; i += 4) {
-      const uint4 q = *reinterpret_cast<const uint4*>(src + first + i);
-      k[i] = q.x;
-      k[i + 1] = q.y;
-      k[i + 2] = q.z;
-      k[i + 3] = q.w;
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < kItems; ++i) k[i] = (i < nvalid) ? src[first + i] : 0u;
+  for (int b = 0; b < kDigitBits; ++b) {
+    const bool bit = (d >> b) & 1u;
+    const uint64_t bal = __ballot(bit);
+    m &= bit ? bal : ~bal;
   }
-  return nvalid;
+  return m;
+}
+
+// Per-wave digit counts of a tile in wc[w][d], each wave counting its own
+// items in its own row (so no barrier and no atomics); in step i the lowest
+// lane of each digit adds the digit's lanes.  my[i] (RANKS): the item's
+// position among the wave's items of its digit.
+template <bool RANKS>
+__device__ __forceinline__ void wave_digit_counts(uint32_t (*wc)[kDigits], const uint32_t k[kItems],
+                                                  const bool ok[kItems], int shift,
+                                                  uint32_t my[kItems]) {
+  const int w = threadIdx.x >> 6;
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint64_t below = (1ull << lane) - 1ull;
+#pragma unroll
+  for (int d = 0; d < kDigits / 64; ++d) wc[w][lane + 64 * d] = 0u;
+#pragma unroll
+  for (int i = 0; i < kItems; ++i) {
+    const uint32_t d = (k[i] >> shift) & (kDigits - 1);
+    const uint64_t m = digit_peers(d, ok[i]);
+    const uint32_t before = (uint32_t)__popcll(m & below);
+    const uint32_t base = wc[w][d];  // every lane reads before the leaders write
+    if constexpr (RANKS) my[i] = base + before;
+    if (ok[i] && before == 0u) wc[w][d] = base + (uint32_t)__popcll(m);
+  }
+}
+
+// Exclusive prefix over the block's 256 threads of a and b at once.
+__device__ __forceinline__ void block_excl2(uint32_t a, uint32_t b, uint32_t* wsum, uint32_t& ea,
+                                            uint32_t& eb) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  uint32_t ia = a, ib = b;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t ya = __shfl_up(ia, o), yb = __shfl_up(ib, o);
+    if (lane >= o) {
+      ia += ya;
+      ib += yb;
+    }
+  }
+  if (lane == 63) {
+    wsum[w] = ia;
+    wsum[4 + w] = ib;
+  }
+  __syncthreads();
+  ea = ia - a;
+  eb = ib - b;
+  for (int q = 0; q < w; ++q) {
+    ea += wsum[q];
+    eb += wsum[4 + q];
+  }
 }
 
 // Tile histograms of one pass: hist[d * ntiles + tile].
+template <bool FIRST>
 __global__ void __launch_bounds__(kRankThreads) rank_hist_kernel(const uint32_t* keys,
+                                                                 const float* leaves,
                                                                  uint32_t count, int shift,
-                                                                 uint32_t* hist) {
-  __shared__ TileSmem sm;
-  uint32_t k[kItems];
-  const int nvalid = load_tile(keys, count, k);
-  tile_counts(sm, k, nvalid, shift);
-  if (threadIdx.x < kDigits) hist[threadIdx.x * gridDim.x + blockIdx.x] = sm.tot[threadIdx.x];
-}
-
-// Exclusive scan of the m = 16 * ntiles histogram entries in place (one
-// block; digit-major order, so entry (d, tile) becomes the global position
-// of the tile's first item of digit d).  m is a multiple of 16: a thread
-// owns 16-entry chunks, read and written as four 16-byte accesses each, all
-// of a chunk's loads issued together.
-__global__ void __launch_bounds__(1024) rank_scan_kernel(uint32_t* hist, uint32_t m) {
-  __shared__ uint32_t wsum[16];
-  const uint32_t nchunks = m / 16;
-  const uint32_t per = (nchunks + 1023) / 1024;  // chunks per thread
-  const uint32_t c0 = threadIdx.x * per, c1 = min(c0 + per, nchunks);
-  uint32_t s = 0;
-  for (uint32_t c = c0; c < c1; ++c) {
-    uint4 q[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) q[j] = reinterpret_cast<const uint4*>(hist)[4 * c + j];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) s += q[j].x + q[j].y + q[j].z + q[j].w;
-  }
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  uint32_t inc = s;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(inc, o);
-    if (lane >= o) inc += y;
-  }
-  if (lane == 63) wsum[w] = inc;
+                                                                 uint32_t ntiles, uint32_t* hist) {
+  __shared__ uint32_t wc[4][kDigits];
+  uint32_t k[kItems], my[kItems];
+  bool ok[kItems];
+  load_striped<FIRST, false>(keys, nullptr, leaves, count, k, nullptr, ok);
+  wave_digit_counts<false>(wc, k, ok, shift, my);
   __syncthreads();
-  uint32_t run = inc - s;
-  for (int k = 0; k < w; ++k) run += wsum[k];
-  for (uint32_t c = c0; c < c1; ++c) {
-    uint4 q[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) q[j] = reinterpret_cast<const uint4*>(hist)[4 * c + j];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint4 o;
-      o.x = run;
-      run += q[j].x;
-      o.y = run;
-      run += q[j].y;
-      o.z = run;
-      run += q[j].z;
-      o.w = run;
-      run += q[j].w;
-      reinterpret_cast<uint4*>(hist)[4 * c + j] = o;
-    }
-  }
+  const int t = threadIdx.x;
+  hist[(size_t)t * ntiles + blockIdx.x] = wc[0][t] + wc[1][t] + wc[2][t] + wc[3][t];
 }
 
-// Stable scatter of one pass.  The tile is first put in digit order in LDS
-// (every thread places its items, in order, after the tile's earlier items
-// of the same digit), then written out with consecutive threads on
-// consecutive items, so that each digit's run of the tile goes to
-// consecutive addresses.
+// Exclusive scan of each digit's row of tile counts in place (one block per
+// digit); tot[d] = the digit's count over all tiles.
+__global__ void __launch_bounds__(kRankThreads) rank_rowscan_kernel(uint32_t* hist,
+                                                                    uint32_t ntiles,
+                                                                    uint32_t* tot) {
+  __shared__ uint32_t wsum[8];
+  uint32_t* row = hist + (size_t)blockIdx.x * ntiles;
+  const uint32_t per = (ntiles + kRankThreads - 1) / kRankThreads;
+  const uint32_t c0 = min(threadIdx.x * per, ntiles), c1 = min(c0 + per, ntiles);
+  uint32_t s = 0;
+  for (uint32_t c = c0; c < c1; ++c) s += row[c];
+  uint32_t run, unused;
+  block_excl2(s, 0u, wsum, run, unused);
+  for (uint32_t c = c0; c < c1; ++c) {
+    const uint32_t x = row[c];
+    row[c] = run;
+    run += x;
+  }
+  if (threadIdx.x == kRankThreads - 1) tot[blockIdx.x] = run;
+}
+
+// Stable scatter of one pass.  Each wave ranks its items per digit; the
+// tile's digit starts and the waves' starts within each digit follow from
+// the counts; the tile is staged in digit order in LDS, then written out
+// with consecutive threads on consecutive staged items, so that each digit's
+// run goes to consecutive addresses from the digit's global start for this
+// tile (its row scan plus the counts of all smaller digits).
 struct ScatterSmem {
-  TileSmem tc;
   uint32_t key[kTile];
   uint32_t val[kTile];
-  uint32_t dbase[kDigits];  // tile-local start of each digit
-  uint32_t gbase[kDigits];  // global start of this tile's run of each digit
+  uint32_t wc[4][kDigits];  // per-wave counts, then per-wave starts in the tile
+  uint32_t dstart[kDigits];  // tile-local start of each digit
+  uint32_t gbase[kDigits];   // global start of this tile's run of each digit
+  uint32_t wsum[8];
 };
 
+template <bool FIRST>
 __global__ void __launch_bounds__(kRankThreads) rank_scatter_kernel(
-    const uint32_t* keys, const uint32_t* vals, uint32_t count, int shift,
-    const uint32_t* hist, uint32_t* keys_out, uint32_t* vals_out) {
+    const uint32_t* keys, const uint32_t* vals, const float* leaves, uint32_t count, int shift,
+    uint32_t ntiles, const uint32_t* hist, const uint32_t* tot, uint32_t* keys_out,
+    uint32_t* vals_out) {
   __shared__ ScatterSmem sm;
-  uint32_t k[kItems], v[kItems];
-  const int nvalid = load_tile(keys, count, k);
-  load_tile(vals, count, v);
-  tile_counts(sm.tc, k, nvalid, shift);
+  uint32_t k[kItems], v[kItems], my[kItems];
+  bool ok[kItems];
+  load_striped<FIRST, true>(keys, vals, leaves, count, k, v, ok);
   const int t = threadIdx.x;
-  if (t < kDigits) {
-    uint32_t b = 0;
-    for (int d = 0; d < t; ++d) b += sm.tc.tot[d];
-    sm.dbase[t] = b;
-    sm.gbase[t] = hist[t * gridDim.x + blockIdx.x];
-  }
+  const uint32_t row = hist[(size_t)t * ntiles + blockIdx.x];  // thread t: digit t
+  const uint32_t dtot = tot[t];
+  wave_digit_counts<true>(sm.wc, k, ok, shift, my);
   __syncthreads();
+  const uint32_t c0 = sm.wc[0][t], c1 = sm.wc[1][t], c2 = sm.wc[2][t], c3 = sm.wc[3][t];
+  uint32_t start, dbefore;
+  block_excl2(c0 + c1 + c2 + c3, dtot, sm.wsum, start, dbefore);
+  sm.dstart[t] = start;
+  sm.gbase[t] = dbefore + row;
+  sm.wc[0][t] = start;
+  sm.wc[1][t] = start + c0;
+  sm.wc[2][t] = start + c0 + c1;
+  sm.wc[3][t] = start + c0 + c1 + c2;
+  __syncthreads();
+  const int w = t >> 6;
 #pragma unroll
   for (int i = 0; i < kItems; ++i) {
-    if (i < nvalid) {
-      const uint32_t d = (k[i] >> shift) & (kDigits - 1);
-      const uint32_t pos = sm.dbase[d] + sm.tc.cnt[d * kRankThreads + t]++;
+    if (ok[i]) {
+      const uint32_t pos = sm.wc[w][(k[i] >> shift) & (kDigits - 1)] + my[i];
       sm.key[pos] = k[i];
       sm.val[pos] = v[i];
     }
@@ -207,7 +220,7 @@ __global__ void __launch_bounds__(kRankThreads) rank_scatter_kernel(
   for (uint32_t i = t; i < tile_n; i += kRankThreads) {
     const uint32_t kk = sm.key[i];
     const uint32_t d = (kk >> shift) & (kDigits - 1);
-    const uint32_t pos = sm.gbase[d] + (i - sm.dbase[d]);
+    const uint32_t pos = sm.gbase[d] + (i - sm.dstart[d]);
     keys_out[pos] = kk;
     vals_out[pos] = sm.val[i];
   }
@@ -256,17 +269,28 @@ __global__ void __launch_bounds__(kRankThreads) rank_build_kernel(TreePtrs t, Ge
 hipError_t launch_rank_sort(const float* leaves, uint32_t count, uint32_t* const keys[2],
                             uint32_t* const vals[2], uint32_t* hist, hipStream_t s) {
   if (count == 0) return hipSuccess;
-  const unsigned ntiles = (count + kTile - 1) / kTile;
-  hipLaunchKernelGGL(rank_seed_kernel, dim3((count + 255) / 256), dim3(256), 0, s, leaves, count,
-                     keys[0], vals[0]);
-  for (int p = 0; p < 32 / kDigitBits; ++p) {
+  const uint32_t ntiles = (count + kTile - 1) / kTile;
+  uint32_t* tot = hist + (size_t)kDigits * ntiles;
+  for (int p = 0; p < kPasses; ++p) {
     const int shift = kDigitBits * p;
-    hipLaunchKernelGGL(rank_hist_kernel, dim3(ntiles), dim3(kRankThreads), 0, s, keys[p & 1],
-                       count, shift, hist);
-    hipLaunchKernelGGL(rank_scan_kernel, dim3(1), dim3(1024), 0, s, hist,
-                       (uint32_t)kDigits * ntiles);
-    hipLaunchKernelGGL(rank_scatter_kernel, dim3(ntiles), dim3(kRankThreads), 0, s, keys[p & 1],
-                       vals[p & 1], count, shift, hist, keys[(p + 1) & 1], vals[(p + 1) & 1]);
+    const uint32_t* kin = keys[p & 1];
+    const uint32_t* vin = vals[p & 1];
+    uint32_t* kout = keys[(p + 1) & 1];
+    uint32_t* vout = vals[(p + 1) & 1];
+    if (p == 0)
+      hipLaunchKernelGGL(rank_hist_kernel<true>, dim3(ntiles), dim3(kRankThreads), 0, s, nullptr,
+                         leaves, count, shift, ntiles, hist);
+    else
+      hipLaunchKernelGGL(rank_hist_kernel<false>, dim3(ntiles), dim3(kRankThreads), 0, s, kin,
+                         nullptr, count, shift, ntiles, hist);
+    hipLaunchKernelGGL(rank_rowscan_kernel, dim3(kDigits), dim3(kRankThreads), 0, s, hist, ntiles,
+                       tot);
+    if (p == 0)
+      hipLaunchKernelGGL(rank_scatter_kernel<true>, dim3(ntiles), dim3(kRankThreads), 0, s,
+                         nullptr, nullptr, leaves, count, shift, ntiles, hist, tot, kout, vout);
+    else
+      hipLaunchKernelGGL(rank_scatter_kernel<false>, dim3(ntiles), dim3(kRankThreads), 0, s, kin,
+                         vin, nullptr, count, shift, ntiles, hist, tot, kout, vout);
   }
   return hipGetLastError();
 }
@@ -281,6 +305,8 @@ hipError_t launch_rank_build(const TreePtrs& rt, const Geom& g, uint32_t count, 
   return launch_top(rt, g, s);
 }
 
-uint32_t rank_tiles(int64_t n) { return (uint32_t)((n + kTile - 1) / kTile); }
+size_t rank_hist_words(int64_t n) {
+  return (size_t)kDigits * ((size_t)((n + kTile - 1) / kTile) + 1);
+}
 
 }  // namespace per
