@@ -82,9 +82,8 @@ __device__ __forceinline__ uint64_t digit_peers(uint32_t d, bool ok) {
 
 // Per-wave digit counts of a tile in wc[w][d], each wave counting its own
 // items in its own row (so no barrier and no atomics); in step i the lowest
-// lane of each digit adds the digit's lanes.  my[i] (RANKS): the item's
-// position among the wave's items of its digit.
-template <bool RANKS>
+// lane of each digit adds the digit's lanes.  my[i]: the item's position
+// among the wave's items of its digit.
 __device__ __forceinline__ void wave_digit_counts(uint32_t (*wc)[kDigits], const uint32_t k[kItems],
                                                   const bool ok[kItems], int shift,
                                                   uint32_t my[kItems]) {
@@ -99,7 +98,7 @@ __device__ __forceinline__ void wave_digit_counts(uint32_t (*wc)[kDigits], const
     const uint64_t m = digit_peers(d, ok[i]);
     const uint32_t before = (uint32_t)__popcll(m & below);
     const uint32_t base = wc[w][d];  // every lane reads before the leaders write
-    if constexpr (RANKS) my[i] = base + before;
+    my[i] = base + before;
     if (ok[i] && before == 0u) wc[w][d] = base + (uint32_t)__popcll(m);
   }
 }
@@ -130,17 +129,32 @@ __device__ __forceinline__ void block_excl2(uint32_t a, uint32_t b, uint32_t* ws
   }
 }
 
-// Tile histograms of one pass: hist[d * ntiles + tile].
-template <bool FIRST>
+// Tile histograms of one pass: hist[d * ntiles + tile].  MATCH: count by
+// ballots (the last pass, on the exponent's high bits, where most keys share
+// a few digits and LDS adds to one address would serialise), else by LDS
+// adds.
+template <bool FIRST, bool MATCH>
 __global__ void __launch_bounds__(kRankThreads) rank_hist_kernel(const uint32_t* keys,
                                                                  const float* leaves,
                                                                  uint32_t count, int shift,
                                                                  uint32_t ntiles, uint32_t* hist) {
   __shared__ uint32_t wc[4][kDigits];
-  uint32_t k[kItems], my[kItems];
+  uint32_t k[kItems];
   bool ok[kItems];
   load_striped<FIRST, false>(keys, nullptr, leaves, count, k, nullptr, ok);
-  wave_digit_counts<false>(wc, k, ok, shift, my);
+  if constexpr (MATCH) {
+    uint32_t my[kItems];
+    wave_digit_counts(wc, k, ok, shift, my);
+  } else {
+    // Order does not matter for the counts: LDS adds without a returned
+    // value, issued back to back, each wave into its own row.
+    const int w = threadIdx.x >> 6;
+#pragma unroll
+    for (int d = 0; d < kDigits / 64; ++d) wc[w][(threadIdx.x & 63) + 64 * d] = 0u;
+#pragma unroll
+    for (int i = 0; i < kItems; ++i)
+      if (ok[i]) atomicAdd(&wc[w][(k[i] >> shift) & (kDigits - 1)], 1u);
+  }
   __syncthreads();
   const int t = threadIdx.x;
   hist[(size_t)t * ntiles + blockIdx.x] = wc[0][t] + wc[1][t] + wc[2][t] + wc[3][t];
@@ -152,17 +166,35 @@ __global__ void __launch_bounds__(kRankThreads) rank_rowscan_kernel(uint32_t* hi
                                                                     uint32_t ntiles,
                                                                     uint32_t* tot) {
   __shared__ uint32_t wsum[8];
+  constexpr uint32_t kHeld = 16;  // entries a thread keeps in registers (up to 2^24 slots)
   uint32_t* row = hist + (size_t)blockIdx.x * ntiles;
   const uint32_t per = (ntiles + kRankThreads - 1) / kRankThreads;
   const uint32_t c0 = min(threadIdx.x * per, ntiles), c1 = min(c0 + per, ntiles);
-  uint32_t s = 0;
-  for (uint32_t c = c0; c < c1; ++c) s += row[c];
-  uint32_t run, unused;
-  block_excl2(s, 0u, wsum, run, unused);
-  for (uint32_t c = c0; c < c1; ++c) {
-    const uint32_t x = row[c];
-    row[c] = run;
-    run += x;
+  uint32_t s = 0, run, unused;
+  if (per <= kHeld) {
+    // All of a thread's loads issued together, the entries kept for the
+    // writes.
+    uint32_t x[kHeld];
+#pragma unroll
+    for (uint32_t j = 0; j < kHeld; ++j) x[j] = (c0 + j < c1) ? row[c0 + j] : 0u;
+#pragma unroll
+    for (uint32_t j = 0; j < kHeld; ++j) s += x[j];
+    block_excl2(s, 0u, wsum, run, unused);
+#pragma unroll
+    for (uint32_t j = 0; j < kHeld; ++j) {
+      if (c0 + j < c1) {
+        row[c0 + j] = run;
+        run += x[j];
+      }
+    }
+  } else {
+    for (uint32_t c = c0; c < c1; ++c) s += row[c];
+    block_excl2(s, 0u, wsum, run, unused);
+    for (uint32_t c = c0; c < c1; ++c) {
+      const uint32_t x = row[c];
+      row[c] = run;
+      run += x;
+    }
   }
   if (threadIdx.x == kRankThreads - 1) tot[blockIdx.x] = run;
 }
@@ -194,7 +226,7 @@ __global__ void __launch_bounds__(kRankThreads) rank_scatter_kernel(
   const int t = threadIdx.x;
   const uint32_t row = hist[(size_t)t * ntiles + blockIdx.x];  // thread t: digit t
   const uint32_t dtot = tot[t];
-  wave_digit_counts<true>(sm.wc, k, ok, shift, my);
+  wave_digit_counts(sm.wc, k, ok, shift, my);
   __syncthreads();
   const uint32_t c0 = sm.wc[0][t], c1 = sm.wc[1][t], c2 = sm.wc[2][t], c3 = sm.wc[3][t];
   uint32_t start, dbefore;
@@ -278,11 +310,14 @@ hipError_t launch_rank_sort(const float* leaves, uint32_t count, uint32_t* const
     uint32_t* kout = keys[(p + 1) & 1];
     uint32_t* vout = vals[(p + 1) & 1];
     if (p == 0)
-      hipLaunchKernelGGL(rank_hist_kernel<true>, dim3(ntiles), dim3(kRankThreads), 0, s, nullptr,
-                         leaves, count, shift, ntiles, hist);
+      hipLaunchKernelGGL((rank_hist_kernel<true, false>), dim3(ntiles), dim3(kRankThreads), 0, s,
+                         nullptr, leaves, count, shift, ntiles, hist);
+    else if (p < kPasses - 1)
+      hipLaunchKernelGGL((rank_hist_kernel<false, false>), dim3(ntiles), dim3(kRankThreads), 0, s,
+                         kin, nullptr, count, shift, ntiles, hist);
     else
-      hipLaunchKernelGGL(rank_hist_kernel<false>, dim3(ntiles), dim3(kRankThreads), 0, s, kin,
-                         nullptr, count, shift, ntiles, hist);
+      hipLaunchKernelGGL((rank_hist_kernel<false, true>), dim3(ntiles), dim3(kRankThreads), 0, s,
+                         kin, nullptr, count, shift, ntiles, hist);
     hipLaunchKernelGGL(rank_rowscan_kernel, dim3(kDigits), dim3(kRankThreads), 0, s, hist, ntiles,
                        tot);
     if (p == 0)
