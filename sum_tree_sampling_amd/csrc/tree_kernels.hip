@@ -724,27 +724,48 @@ __device__ __forceinline__ bool scan_update(SM& sm, const TreePtrs& t, const Geo
     }
 #pragma unroll
     for (int c = 0; c < kChunk; ++c) asm volatile("" ::"v"(tx[c]), "v"(ix[c]));
+    // The entries this lane looks at (bit c: slot c of the chunk).
+    uint32_t pending = 0u;
 #pragma unroll
     for (int c = 0; c < kChunk; ++c) {
-      const uint32_t b = b0 + c * kUpdThreads + threadIdx.x;
       const int64_t i = ix[c];
       if (i < 0 || i >= (int64_t)size) continue;
       const uint32_t q = (uint32_t)((uint64_t)i >> g.S) - part0;  // wraps below part0
-      const bool own = q < (uint32_t)nparts;
-      if (!own && !(FUSED && all)) continue;
-      // One priority computation for every entry looked at: collect()
-      // issues no loads for an entry index >= kSparseMax, which entries of
-      // other partitions and left-out ones take.
-      const uint32_t qq = own ? q : 0u;
-      const uint32_t part = part0 + qq;
-      const uint32_t off = (uint32_t)i - (part << g.S);
-      bool keep = own;
-      if constexpr (FUSED) keep = keep && !skip(off);
-      const int k = keep ? atomicAdd(&sm.count[qq], 1) : kSparseMax;
-      const float p = collect(sm.u.sp[qq], k, t, g, part, off, b, tx[c], m0, a.alpha, a.eps,
-                              a.p_nan);
-      if (own) atomicMax(&sm.bmax, __float_as_uint(p));
-      if constexpr (FUSED) mall = max(mall, __float_as_uint(p));
+      if (q < (uint32_t)nparts || (FUSED && all)) pending |= 1u << c;
+    }
+    // One entry per lane per round: entries of one wave in different slots
+    // are collected together, their sibling loads and pows overlapping,
+    // instead of one slot after the other.
+    while (__ballot(pending != 0u) != 0ull) {
+      if (pending != 0u) {
+        const int c = __builtin_ctz(pending);
+        pending &= pending - 1u;
+        int64_t i = ix[0];
+        float td = tx[0];
+#pragma unroll
+        for (int cc = 1; cc < kChunk; ++cc) {
+          if (c == cc) {
+            i = ix[cc];
+            td = tx[cc];
+          }
+        }
+        const uint32_t b = b0 + (uint32_t)c * kUpdThreads + threadIdx.x;
+        const uint32_t q = (uint32_t)((uint64_t)i >> g.S) - part0;
+        const bool own = q < (uint32_t)nparts;
+        // One priority computation for every entry looked at: collect()
+        // issues no loads for an entry index >= kSparseMax, which entries of
+        // other partitions and left-out ones take.
+        const uint32_t qq = own ? q : 0u;
+        const uint32_t part = part0 + qq;
+        const uint32_t off = (uint32_t)i - (part << g.S);
+        bool keep = own;
+        if constexpr (FUSED) keep = keep && !skip(off);
+        const int k = keep ? atomicAdd(&sm.count[qq], 1) : kSparseMax;
+        const float p = collect(sm.u.sp[qq], k, t, g, part, off, b, td, m0, a.alpha, a.eps,
+                                a.p_nan);
+        if (own) atomicMax(&sm.bmax, __float_as_uint(p));
+        if constexpr (FUSED) mall = max(mall, __float_as_uint(p));
+      }
     }
   }
   if constexpr (FUSED) {
