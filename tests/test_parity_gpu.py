@@ -616,6 +616,46 @@ def test_update_add(n, D, B, c, prio, fill):
                            "update_add step %d sample" % step, rows=True)
 
 
+@pytest.mark.parametrize("alpha,eps,kind", [
+    (0.6, 1e-6, "near ties"),      # several entries within a few ulps of the largest |td|
+    (0.6, 1e-6, "no finite td"),   # only NaN and infinite TD errors
+    (0.6, 0.0, "all zero"),        # eps 0, every |td| 0: every entry at the bound
+    (1e-5, 1e-6, "small alpha"),
+    (3.0, 0.5, "large alpha"),
+])
+def test_update_add_batch_max(alpha, eps, kind):
+    """The priority a fused intake at the running max takes is the max of
+    the whole batch's priorities, bit for bit with the oracle's update then
+    intake: near ties at the largest |td|, batches without a finite TD
+    error, zero errors with eps 0, and small and large alpha."""
+    say("update_add batch max", alpha, eps, kind)
+    n, B, c = 1 << 16, 1500, 300
+    rng = np.random.default_rng(int(alpha * 1e6) + len(kind))
+    o = Oracle(n, 0, alpha=alpha, eps=eps)
+    g = _buf(n, 0, max_batch=2048, alpha=alpha, eps=eps)
+    p0 = (rng.random(n) * 0.01).astype(np.float32)
+    o.add(n, prio=p0)
+    g.add(n, prio=dev(p0))
+    for step in range(4):
+        idx = rng.integers(0, n, B).astype(np.int64)
+        td = (rng.standard_normal(B) * 2).astype(np.float32)
+        if kind == "near ties":
+            top = np.float32(7.5 + step)
+            k = rng.choice(B, 12, replace=False)
+            # the largest |td| twice, then values 1 to 10 ulps below it, either sign
+            below = (top.view(np.uint32) - np.arange(1, 11, dtype=np.uint32)).view(np.float32)
+            td[k] = np.concatenate([[top, -top], below * np.where(np.arange(10) % 2, 1, -1)])
+        elif kind == "no finite td":
+            td[:] = np.nan
+            td[rng.integers(0, B, 5)] = np.inf if step % 2 else np.nan
+        elif kind == "all zero":
+            td[:] = 0.0
+        o.update(idx, td)
+        o.add(c)
+        g.update_add(dev(idx), dev(td), c)
+        compare_trees(o, g, "batch max %s step %d" % (kind, step))
+
+
 # ------------------------------------------------------------ full-size large buffer
 
 def test_large_16m_full_size():
