@@ -186,7 +186,6 @@ struct SparseSmem {
   float sib_m[kSparseMax][kMaxSpanBits];  // first 64 entries' leaf paths
   uint64_t key[kSparseMax];               // (offset << 32 | batch position)
   float pval[kSparseMax];                 // priorities
-  uint8_t order[kSparseMax];              // entry at each sorted position
 };
 
 struct DenseSmem {
@@ -272,16 +271,19 @@ __device__ __forceinline__ void wave_update(SparseSmem& sp, const TreePtrs& t, c
   const int lane = threadIdx.x & 63;
   const bool in = lane < m;
   const uint64_t mine = in ? sp.key[lane] : ~0ull;
+  // The ranks (a permutation of [0, m), lanes past m keeping their own
+  // index) are inverted by one lane permute, which gives each sorted
+  // position its entry.
   int rank = 0;
 #pragma unroll 4
   for (int j = 0; j < m; ++j) rank += (sp.key[j] < mine) ? 1 : 0;
-  if (in) sp.order[rank] = (uint8_t)lane;
-  __builtin_amdgcn_wave_barrier();
-  const int src = in ? sp.order[lane] : 0;
+  if (!in) rank = lane;
+  const int sorted = __builtin_amdgcn_ds_permute(rank << 2, lane);  // every lane takes part
+  const int src = in ? sorted : 0;
   const uint64_t key = sp.key[src];
   const uint32_t off = (uint32_t)(key >> 32);
   const float p = sp.pval[src];
-  const uint32_t next_off = __shfl_down(off, 1);
+  const uint32_t next_off = next_lane(off);  // lane m - 1 does not look at it
   const bool win = in && (lane == m - 1 || next_off != off);
   float ps[kMaxSpanBits], pm[kMaxSpanBits];
 #pragma unroll
