@@ -138,10 +138,12 @@ constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v / 2); }
 // line, so the load stays unconditional and in its batch); the zero is
 // selected at the store, after the batch's loads.
 // kBatch (1, 2, 4 or 8) is chosen from the wave's access count so that a
-// wave copying a few short rows issues no idle loads.
-template <bool VEC, int SPW, int G, int kBatch>
+// wave copying a few short rows issues no idle loads.  mid() runs once,
+// between the first batch's loads and its stores, so that its work overlaps
+// their trip.
+template <bool VEC, int SPW, int G, int kBatch, typename Mid>
 __device__ __forceinline__ void copy_rows(const SampleArgs& a, uint32_t wave_b0, uint32_t slot,
-                                          int lane, uint32_t D, uint32_t W) {
+                                          int lane, uint32_t D, uint32_t W, Mid mid) {
   constexpr uint32_t kW = VEC ? 4u : 1u;      // floats per access
   const uint32_t per_src = D / kW;            // loads per row
   const uint32_t per_row = W / kW;            // stores per row
@@ -177,11 +179,13 @@ __device__ __forceinline__ void copy_rows(const SampleArgs& a, uint32_t wave_b0,
       // accesses read column 0, so the address is always in the row store.
       buf[q] = reinterpret_cast<const T*>(src)[(pad[q] || !ok[q]) ? 0u : c];
     }
+    if (t0 == 0) mid();
 #pragma unroll
     for (int q = 0; q < kBatch; ++q) {
       if (ok[q]) *dst[q] = pad[q] ? T{} : buf[q];
     }
   }
+  if (total == 0) mid();
 }
 
 // Philox4x64-10 (Salmon, Moraes, Dror and Shaw, "Parallel Random Numbers: As
@@ -233,9 +237,10 @@ __device__ __forceinline__ void emit(const SampleArgs& a, uint32_t wave, int lan
     rew = a.st.rewards[slot];
     done = a.st.dones[slot];
   }
-  if (lead) {
-    a.idx_out[b] = (int64_t)slot;
-    if (a.w_out) {
+  if (lead) a.idx_out[b] = (int64_t)slot;
+  // The weight, computed while the rows' loads are in flight.
+  auto weight = [&]() {
+    if (lead && a.w_out) {
       // (N P_i)^-beta / (N P_min)^-beta = (p_i / p_min)^-beta: one pow, f64.
       // With p_min > 0 every stored priority, the sampled one included, is
       // > 0; with p_min = 0 the normaliser is infinite and w = 0.
@@ -243,26 +248,27 @@ __device__ __forceinline__ void emit(const SampleArgs& a, uint32_t wave, int lan
       if (pmin > 0.0f) w = (float)pow((double)leaf / (double)pmin, -a.beta);
       a.w_out[b] = w;
     }
-  }
+  };
 
+  if (!a.states_out) weight();
   if (a.states_out) {
     const uint32_t D = (uint32_t)a.st.D, W = a.out_stride;
     const bool vec = ((D | W) & 3u) == 0u;
     const uint32_t per_lane = (SPW * 2u * (vec ? W / 4 : W) + 63u) / 64u;  // accesses per lane
     if (vec) {
       if (per_lane <= 1)
-        copy_rows<true, SPW, G, 1>(a, wave * SPW, slot, lane, D, W);
+        copy_rows<true, SPW, G, 1>(a, wave * SPW, slot, lane, D, W, weight);
       else if (per_lane <= 2)
-        copy_rows<true, SPW, G, 2>(a, wave * SPW, slot, lane, D, W);
+        copy_rows<true, SPW, G, 2>(a, wave * SPW, slot, lane, D, W, weight);
       else if (per_lane <= 4)
-        copy_rows<true, SPW, G, 4>(a, wave * SPW, slot, lane, D, W);
+        copy_rows<true, SPW, G, 4>(a, wave * SPW, slot, lane, D, W, weight);
       else
-        copy_rows<true, SPW, G, 8>(a, wave * SPW, slot, lane, D, W);
+        copy_rows<true, SPW, G, 8>(a, wave * SPW, slot, lane, D, W, weight);
     } else {
       if (per_lane <= 2)
-        copy_rows<false, SPW, G, 2>(a, wave * SPW, slot, lane, D, W);
+        copy_rows<false, SPW, G, 2>(a, wave * SPW, slot, lane, D, W, weight);
       else
-        copy_rows<false, SPW, G, 8>(a, wave * SPW, slot, lane, D, W);
+        copy_rows<false, SPW, G, 8>(a, wave * SPW, slot, lane, D, W, weight);
     }
   }
   if (lead && a.states_out) {
