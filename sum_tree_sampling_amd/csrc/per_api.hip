@@ -355,7 +355,8 @@ int sample_impl(per_t* h, int64_t B, SampleKind kind, const float* d_u, uint64_t
   if (h->size == 0) return fail(PER_EEMPTY, "sample from an empty buffer");
   if (kind == kRank) {
     if (h->rank_size == 0) return fail(PER_EEMPTY, "rank sample before per_rank_refresh");
-    const per::SamplePlan plan = per::make_sample_plan(h->g, B);
+    const per::SamplePlan plan =
+        per::make_sample_plan(h->g, B, any_rows ? (uint32_t)h->st.D : 0u);
     hipError_t e = per::launch_sample(h->rt, h->g, h->st, plan, (uint32_t)h->rank_size, B, d_u,
                                       0, 0, beta, d_idx_out, d_w_out,
                                       any_rows ? d_states_out : nullptr, d_next_states_out,
@@ -372,7 +373,8 @@ int sample_impl(per_t* h, int64_t B, SampleKind kind, const float* d_u, uint64_t
                                        (uint32_t)out_stride, dones_f32, stream);
     return e == hipSuccess ? ok() : hip_fail(e, what);
   }
-  const per::SamplePlan plan = per::make_sample_plan(h->g, B);
+  const per::SamplePlan plan =
+      per::make_sample_plan(h->g, B, any_rows ? (uint32_t)h->st.D : 0u);
   const bool stale = top_may_be_stale(h);
   if (stale && plan.top_mode != per::kTopRebuild) {  // the sampler will not rebuild the top itself
     hipError_t e = per::launch_top(h->t, h->g, stream);

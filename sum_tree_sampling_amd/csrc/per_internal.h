@@ -141,7 +141,7 @@ hipError_t launch_sample(const TreePtrs& t, const Geom& g, const Storage& st,
                          void* dones_out, uint32_t out_stride, bool dones_f32,
                          bool write_top, hipStream_t s, const uint32_t* order = nullptr);
 
-SamplePlan make_sample_plan(const Geom& g, int64_t B);
+SamplePlan make_sample_plan(const Geom& g, int64_t B, uint32_t row_floats);
 
 // Rank-based prioritisation: a stable radix sort of the slots [0, count) by
 // descending leaf priority (keys / vals: two ping-pong buffers of n words,
