@@ -156,6 +156,13 @@ __device__ __forceinline__ void copy_rows(const SampleArgs& a, uint32_t wave_b0,
   const float* const src_n = a.st.next_states;
   float* const dst_s = a.states_out;
   float* const dst_n = a.next_out;
+  // With at most four samples per wave their slots are read once, from the
+  // lanes that hold them; otherwise each access fetches its sample's slot.
+  uint32_t few[SPW <= 4 ? SPW : 1];
+  if constexpr (SPW <= 4) {
+#pragma unroll
+    for (int k = 0; k < SPW; ++k) few[k] = (uint32_t)__builtin_amdgcn_readlane((int)slot, k * G);
+  }
   for (uint32_t t0 = 0; t0 < total; t0 += 64 * kBatch) {
     T buf[kBatch];
     T* dst[kBatch];
@@ -165,7 +172,15 @@ __device__ __forceinline__ void copy_rows(const SampleArgs& a, uint32_t wave_b0,
       const uint32_t t = t0 + q * 64 + lane;
       uint32_t s = t / (2u * per_row);
       if (s >= SPW) s = SPW - 1;
-      const uint32_t slot_s = (uint32_t)__shfl((int)slot, (int)s * G);
+      uint32_t slot_s;
+      if constexpr (SPW <= 4) {
+        slot_s = few[0];
+#pragma unroll
+        for (int k = 1; k < SPW; ++k)
+          if (s == (uint32_t)k) slot_s = few[k];
+      } else {
+        slot_s = (uint32_t)__shfl((int)slot, (int)s * G);
+      }
       const uint32_t bs = wave_b0 + s;
       ok[q] = t < total && bs < a.B;
       const uint32_t rem = t - s * 2u * per_row;
