@@ -381,9 +381,17 @@ __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleArgs a) {
       for (int i = 0; i < 2; ++i) {
         v[i] = 0.0f;
         mv[i] = 0.0f;
+        // Each source read in its own branch (Pw < P is uniform): merged,
+        // the two become one generic load behind a wait for all memory.
         if (on && (uint32_t)i < c) {
-          v[i] = (Pw < P) ? top[k0 + i] : a.sum[k0 + i];
-          mv[i] = (Pw < P) ? mtop[k0 + i] : a.mn[k0 + i];
+          if (Pw < P) {
+            v[i] = top[k0 + i];
+            mv[i] = mtop[k0 + i];
+            asm volatile("" ::"v"(v[i]), "v"(mv[i]));
+          } else {
+            v[i] = a.sum[k0 + i];
+            mv[i] = a.mn[k0 + i];
+          }
         }
       }
       if (on && Pw == P) {
@@ -442,6 +450,9 @@ __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleArgs a) {
     }
     T = top[1];
     pmin = mtop[1];
+    // Taken here, from LDS: left to itself the compiler merges the two
+    // branches' reads into one generic load behind a wait for all memory.
+    asm volatile("" ::"v"(T), "v"(pmin));
   } else {
     if (a.top_mode == kTopWhole) {
       const uint32_t cnt = 1u << (a.top + 1);  // whole tree, >= 4 floats
