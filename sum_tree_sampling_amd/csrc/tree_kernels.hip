@@ -116,6 +116,15 @@ __device__ uint32_t block_max_bits(uint32_t v, BlockScratch& sx) {
 
 // ------------------------------------------------------------ sparse chains
 
+// Leaves per partition as a power of two.  FULL: the usual 2^kMaxSpanBits,
+// known when compiling, so that the per-level loops of the sparse update
+// carry no test of the level against it (the tests also held the scalar
+// registers of the update kernels past their budget); else the geometry's.
+template <bool FULL>
+__device__ __forceinline__ int span_bits(const Geom& g) {
+  return FULL ? kMaxSpanBits : g.S;
+}
+
 // Sparse repair by one wave.  Lanes [0, m) hold the new leaves of the
 // partition sorted by offset (offset off, value p); `valid` marks one lane
 // per distinct offset (the others are ignored) and ps / pm hold the stored
@@ -130,10 +139,12 @@ __device__ uint32_t block_max_bits(uint32_t v, BlockScratch& sx) {
 // chain ends exactly at the left child, whose value it holds, frozen.
 // Otherwise the other child is unchanged and its stored value is the
 // sibling's.  Must be called by all 64 lanes of the wave.
+template <bool FULL>
 __device__ __forceinline__ void sparse_chain(const TreePtrs& t, const Geom& g, uint32_t part, int m, bool valid,
                              uint32_t off, float p, const float* ps, const float* pm) {
+  const int S = span_bits<FULL>(g);
   const int lane = threadIdx.x & 63;
-  const uint32_t leaf = (part << g.S) + off;
+  const uint32_t leaf = (part << S) + off;
   const uint32_t node = g.n + leaf;
   if (valid) {
     t.sum[node] = p;
@@ -147,7 +158,7 @@ __device__ __forceinline__ void sparse_chain(const TreePtrs& t, const Geom& g, u
   const uint64_t lanes_below = (1ull << lane) - 1ull;
 #pragma unroll
   for (int k = 0; k < kMaxSpanBits; ++k) {
-    if (k >= g.S) continue;     // uniform across the wave
+    if (k >= S) continue;       // uniform across the wave (none when FULL)
     const int l = g.L - 1 - k;  // depth of the node computed at this step
     const bool active = valid && d < l;
     const uint32_t child = node >> k;
@@ -217,16 +228,18 @@ struct UpdSmem {
 // stored siblings along its leaf's whole path to the partition root go to
 // the partition's sparse area, loaded before the priority's pow so that both
 // latencies overlap.  Returns the priority.
+template <bool FULL>
 __device__ __forceinline__ float collect(SparseSmem& sp, int k, const TreePtrs& t,
                                          const Geom& g, uint32_t part, uint32_t off,
                                          uint32_t pos, float td, float m0, double alpha,
                                          double eps, float p_nan) {
+  const int S = span_bits<FULL>(g);
   float ps[kMaxSpanBits], pm[kMaxSpanBits];
-  const uint32_t node = g.n + (part << g.S) + off;
+  const uint32_t node = g.n + (part << S) + off;
   if (k < kSparseMax) {
 #pragma unroll
     for (int q = 0; q < kMaxSpanBits; ++q) {
-      if (q < g.S) {
+      if (q < S) {
         const uint32_t sib = (node >> q) ^ 1u;
         ps[q] = t.sum[sib];
         pm[q] = t.mn[sib];
@@ -239,7 +252,7 @@ __device__ __forceinline__ float collect(SparseSmem& sp, int k, const TreePtrs& 
     sp.pval[k] = p;
 #pragma unroll
     for (int q = 0; q < kMaxSpanBits; ++q) {
-      if (q < g.S) {
+      if (q < S) {
         sp.sib_s[k][q] = ps[q];
         sp.sib_m[k][q] = pm[q];
       }
@@ -266,6 +279,7 @@ __device__ __forceinline__ void publish_max(uint32_t mb, bool carry, float m0,
 // counted from LDS (m is small) -- so that the last batch position of each
 // offset is the last of its run, and repair the chains of those winners with
 // the prefetched siblings.
+template <bool FULL>
 __device__ __forceinline__ void wave_update(SparseSmem& sp, const TreePtrs& t, const Geom& g, uint32_t part,
                             int m) {
   const int lane = threadIdx.x & 63;
@@ -291,7 +305,7 @@ __device__ __forceinline__ void wave_update(SparseSmem& sp, const TreePtrs& t, c
     ps[k] = sp.sib_s[src][k];
     pm[k] = sp.sib_m[src][k];
   }
-  sparse_chain(t, g, part, m, win, in ? off : 0u, p, ps, pm);
+  sparse_chain<FULL>(t, g, part, m, win, in ? off : 0u, p, ps, pm);
 }
 
 // ------------------------------------------------------------ crowded partitions
@@ -695,7 +709,7 @@ __device__ __forceinline__ uint32_t filled_size(const UpdateArgs& a) {
 // block's own and the others'.  Returns whether a partition was crowded
 // (then rebuilt by the whole block, which has passed a barrier since);
 // otherwise wave w returns right after its sparse repair.
-template <int PPB, bool FUSED, typename SM, typename Skip>
+template <int PPB, bool FUSED, bool FULL, typename SM, typename Skip>
 __device__ __forceinline__ bool scan_update(SM& sm, const TreePtrs& t, const Geom& g,
                                             const UpdateArgs& a, uint32_t part0, uint32_t size,
                                             float m0, bool all, Skip skip) {
@@ -732,7 +746,7 @@ __device__ __forceinline__ bool scan_update(SM& sm, const TreePtrs& t, const Geo
     for (int c = 0; c < kChunk; ++c) {
       const int64_t i = ix[c];
       if (i < 0 || i >= (int64_t)size) continue;
-      const uint32_t q = (uint32_t)((uint64_t)i >> g.S) - part0;  // wraps below part0
+      const uint32_t q = (uint32_t)((uint64_t)i >> span_bits<FULL>(g)) - part0;  // wraps below part0
       if (q < (uint32_t)nparts || (FUSED && all)) pending |= 1u << c;
     }
     // One entry per lane per round: entries of one wave in different slots
@@ -752,18 +766,18 @@ __device__ __forceinline__ bool scan_update(SM& sm, const TreePtrs& t, const Geo
           }
         }
         const uint32_t b = b0 + (uint32_t)c * kUpdThreads + threadIdx.x;
-        const uint32_t q = (uint32_t)((uint64_t)i >> g.S) - part0;
+        const uint32_t q = (uint32_t)((uint64_t)i >> span_bits<FULL>(g)) - part0;
         const bool own = q < (uint32_t)nparts;
         // One priority computation for every entry looked at: collect()
         // issues no loads for an entry index >= kSparseMax, which entries of
         // other partitions and left-out ones take.
         const uint32_t qq = own ? q : 0u;
         const uint32_t part = part0 + qq;
-        const uint32_t off = (uint32_t)i - (part << g.S);
+        const uint32_t off = (uint32_t)i - (part << span_bits<FULL>(g));
         bool keep = own;
         if constexpr (FUSED) keep = keep && !skip(off);
         const int k = keep ? atomicAdd(&sm.count[qq], 1) : kSparseMax;
-        const float p = collect(sm.u.sp[qq], k, t, g, part, off, b, td, m0, a.alpha, a.eps,
+        const float p = collect<FULL>(sm.u.sp[qq], k, t, g, part, off, b, td, m0, a.alpha, a.eps,
                                 a.p_nan);
         if (own) atomicMax(&sm.bmax, __float_as_uint(p));
         if constexpr (FUSED) mall = max(mall, __float_as_uint(p));
@@ -785,7 +799,7 @@ __device__ __forceinline__ bool scan_update(SM& sm, const TreePtrs& t, const Geo
   for (int q = 0; q < nparts; ++q) crowded |= sm.count[q] > kSparseMax;
   if (w < nparts) {
     const int m = sm.count[w];
-    if (m > 0 && m <= kSparseMax) wave_update(sm.u.sp[w], t, g, part0 + w, m);
+    if (m > 0 && m <= kSparseMax) wave_update<FULL>(sm.u.sp[w], t, g, part0 + w, m);
   }
   if (!crowded) return false;
   // The dense rebuild reuses the sparse areas: every wave is done with them.
@@ -806,15 +820,15 @@ __device__ __forceinline__ bool scan_update(SM& sm, const TreePtrs& t, const Geo
   return true;
 }
 
-template <int PPB>
+template <int PPB, bool FULL>
 __global__ void __launch_bounds__(kUpdThreads) update_scan_kernel(TreePtrs t, Geom g, UpdateArgs a) {
   __shared__ UpdSmem<PPB> sm;
   // The arguments the first steps need, fetched in one batch.
   asm volatile("" ::"s"(t.ctrl), "s"(a.idx), "s"(a.td), "s"(a.B), "s"(a.src), "s"(a.size),
                "s"(a.ring.dev), "s"(g.n), "s"(g.S));
   const float m0 = __uint_as_float(t.ctrl->maxp_bits[a.src]);
-  scan_update<PPB, false>(sm, t, g, a, blockIdx.x * PPB, filled_size(a), m0, false,
-                          [](uint32_t) { return false; });
+  scan_update<PPB, false, FULL>(sm, t, g, a, blockIdx.x * PPB, filled_size(a), m0, false,
+                                [](uint32_t) { return false; });
 }
 
 // Large batches, step 1: every valid entry goes to its partition's bucket
@@ -848,7 +862,7 @@ __global__ void __launch_bounds__(256) bucket_kernel(Buckets bk, Geom g, UpdateA
 // reads the bucket of partition w of the block and repairs it (lane k takes
 // entry k), crowded partitions (more entries than a bucket holds) are
 // rebuilt by the whole block after, from their bucket and the overflow list.
-template <int PPB>
+template <int PPB, bool FULL>
 __global__ void __launch_bounds__(kUpdThreads) update_bucket_kernel(TreePtrs t, Buckets bk, Geom g,
                                                             UpdateArgs a) {
   __shared__ UpdSmem<PPB> sm;
@@ -878,8 +892,9 @@ __global__ void __launch_bounds__(kUpdThreads) update_bucket_kernel(TreePtrs t, 
       uint32_t pb = 0u;
       if ((uint32_t)lane < m) {
         const uint32_t e = part * kBucketCap + lane;
-        const float p = collect(sp, lane, t, g, part, bk.slot[e] - (part << g.S), bk.pos[e],
-                                bk.td[e], m0, a.alpha, a.eps, a.p_nan);
+        const float p = collect<FULL>(sp, lane, t, g, part,
+                                      bk.slot[e] - (part << span_bits<FULL>(g)), bk.pos[e],
+                                      bk.td[e], m0, a.alpha, a.eps, a.p_nan);
         pb = __float_as_uint(p);
       }
       pb = wave_max_u32(pb);
@@ -889,7 +904,7 @@ __global__ void __launch_bounds__(kUpdThreads) update_bucket_kernel(TreePtrs t, 
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      wave_update(sp, t, g, part, (int)m);
+      wave_update<FULL>(sp, t, g, part, (int)m);
     }
   }
   if (!crowded) return;
@@ -1170,7 +1185,7 @@ struct UpdAddSmem {
 // such a block gathers from the whole batch while scanning it.  Both raise
 // the running max in the same slot (a.dst == b.dst).  Blocks past the first
 // 2^P copy the intake's rows.
-template <bool PRIO>
+template <bool PRIO, bool FULL>
 __global__ void __launch_bounds__(kUpdThreads) update_add_kernel(TreePtrs t, Geom g, Storage st,
                                                                  UpdateArgs a, AddArgs b) {
   __shared__ std::conditional_t<PRIO, UpdAddSmem, UpdSmem<1>> sm;
@@ -1192,7 +1207,7 @@ __global__ void __launch_bounds__(kUpdThreads) update_add_kernel(TreePtrs t, Geo
   const float m0 = __uint_as_float(t.ctrl->maxp_bits[a.src]);
   // Update entries at slots the intake takes are left out of the repair
   // (the intake overwrites them; their priorities still count).
-  const bool crowded = scan_update<1, true>(sm, t, g, a, part, size, m0, !PRIO && ir.runs > 0,
+  const bool crowded = scan_update<1, true, FULL>(sm, t, g, a, part, size, m0, !PRIO && ir.runs > 0,
                                             [&](uint32_t off) { return ir.has(off); });
   if (ir.runs == 0) return;
   float v = m0;
@@ -1306,8 +1321,12 @@ hipError_t launch_update(const TreePtrs& t, const Buckets& bk, const Geom& g, Ri
   const uint64_t np = 1ull << g.P;
   if (!update_uses_buckets(g, B)) {
     // One partition per block: the batch scan is spread over the most blocks.
-    hipLaunchKernelGGL(update_scan_kernel<1>, dim3((unsigned)np), dim3(kUpdThreads), 0, s, t, g,
-                       a);
+    if (g.S == kMaxSpanBits)
+      hipLaunchKernelGGL((update_scan_kernel<1, true>), dim3((unsigned)np), dim3(kUpdThreads), 0,
+                         s, t, g, a);
+    else
+      hipLaunchKernelGGL((update_scan_kernel<1, false>), dim3((unsigned)np), dim3(kUpdThreads), 0,
+                         s, t, g, a);
     return hipGetLastError();
   }
   // Bucketed: four partitions per block, one wave each, while the batch
@@ -1318,10 +1337,19 @@ hipError_t launch_update(const TreePtrs& t, const Buckets& bk, const Geom& g, Ri
   const unsigned grid = thin ? (unsigned)((np + 3) / 4) : (unsigned)np;
   const unsigned eb = grid_for((uint64_t)B, kTreeThreads, 1u << 30);
   hipLaunchKernelGGL(bucket_kernel, dim3(eb), dim3(kTreeThreads), 0, s, bk, g, a);
-  if (thin)
-    hipLaunchKernelGGL(update_bucket_kernel<4>, dim3(grid), dim3(kUpdThreads), 0, s, t, bk, g, a);
+  const bool full = g.S == kMaxSpanBits;
+  if (thin && full)
+    hipLaunchKernelGGL((update_bucket_kernel<4, true>), dim3(grid), dim3(kUpdThreads), 0, s, t, bk,
+                       g, a);
+  else if (thin)
+    hipLaunchKernelGGL((update_bucket_kernel<4, false>), dim3(grid), dim3(kUpdThreads), 0, s, t,
+                       bk, g, a);
+  else if (full)
+    hipLaunchKernelGGL((update_bucket_kernel<1, true>), dim3(grid), dim3(kUpdThreads), 0, s, t, bk,
+                       g, a);
   else
-    hipLaunchKernelGGL(update_bucket_kernel<1>, dim3(grid), dim3(kUpdThreads), 0, s, t, bk, g, a);
+    hipLaunchKernelGGL((update_bucket_kernel<1, false>), dim3(grid), dim3(kUpdThreads), 0, s, t,
+                       bk, g, a);
   return hipGetLastError();
 }
 
@@ -1399,12 +1427,19 @@ hipError_t launch_update_add(const TreePtrs& t, const Geom& g, const Storage& st
   if (st.D > 0)
     ncopy = grid_for((uint64_t)count * (uint64_t)st.D / 4 + count, kTreeThreads * 4, 2048);
   b.last = np + ncopy - 1u;
-  if (prio)
-    hipLaunchKernelGGL(update_add_kernel<true>, dim3(np + ncopy), dim3(kUpdThreads), 0, s, t, g,
-                       st, a, b);
+  const bool full = g.S == kMaxSpanBits;
+  if (prio && full)
+    hipLaunchKernelGGL((update_add_kernel<true, true>), dim3(np + ncopy), dim3(kUpdThreads), 0, s,
+                       t, g, st, a, b);
+  else if (prio)
+    hipLaunchKernelGGL((update_add_kernel<true, false>), dim3(np + ncopy), dim3(kUpdThreads), 0, s,
+                       t, g, st, a, b);
+  else if (full)
+    hipLaunchKernelGGL((update_add_kernel<false, true>), dim3(np + ncopy), dim3(kUpdThreads), 0, s,
+                       t, g, st, a, b);
   else
-    hipLaunchKernelGGL(update_add_kernel<false>, dim3(np + ncopy), dim3(kUpdThreads), 0, s, t, g,
-                       st, a, b);
+    hipLaunchKernelGGL((update_add_kernel<false, false>), dim3(np + ncopy), dim3(kUpdThreads), 0,
+                       s, t, g, st, a, b);
   return hipGetLastError();
 }
 
