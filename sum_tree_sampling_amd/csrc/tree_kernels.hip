@@ -475,12 +475,14 @@ __device__ __forceinline__ void prefetch_range_boundaries(RangeSmem& r, const Tr
 // sibling left of the run's first node at height q (needed when that node
 // is a right child), lanes 32..63 the sibling right of its last node (needed
 // when that node is a left child); other lanes and unneeded siblings: 0.
+template <bool FULL>
 __device__ __forceinline__ void load_range_boundary(const TreePtrs& t, const Geom& g,
                                                     uint32_t part, uint32_t lo, uint32_t hi,
                                                     float& sib_s, float& sib_m) {
-  const uint32_t a = g.n + (part << g.S) + lo, b = g.n + (part << g.S) + hi - 1;
+  const int S = span_bits<FULL>(g);
+  const uint32_t a = g.n + (part << S) + lo, b = g.n + (part << S) + hi - 1;
   const int q = threadIdx.x & 31;
-  if (threadIdx.x < 64 && q < g.S) {
+  if (threadIdx.x < 64 && q < S) {
     const bool left = threadIdx.x < 32;
     const uint32_t x = (left ? a : b) >> q;
     if (left ? (x & 1u) : !(x & 1u)) {
@@ -545,10 +547,12 @@ __device__ __forceinline__ void climb_paths(int levels, int lane, uint64_t merge
 // costs several cycles per instruction, so the climb does nothing else, and
 // the other waves store the leaves and the interior nodes meanwhile.  No
 // barrier anywhere.
+template <bool FULL>
 __device__ __forceinline__ void uniform_range(const TreePtrs& t, const Geom& g, uint32_t part,
                                               uint32_t lo, uint32_t hi, float v, float sib_s,
                                               float sib_m) {
-  const uint32_t leaf0 = g.n + (part << g.S);
+  const int S = span_bits<FULL>(g);
+  const uint32_t leaf0 = g.n + (part << S);
   // Every load is complete before the first store: a wait placed after
   // stores (the compiler joins the paths of the waves below) would also
   // wait for those stores.
@@ -571,14 +575,11 @@ __device__ __forceinline__ void uniform_range(const TreePtrs& t, const Geom& g, 
     // is an ordinary load the compiler may schedule early, where reading it
     // from lane k's registers is an operation it must not hoist.
     __shared__ float4 other[kMaxSpanBits];
-    if (lane < g.S) other[lane] = make_float4(cls, clm, crs, crm);
+    if (lane < S) other[lane] = make_float4(cls, clm, crs, crm);
     __builtin_amdgcn_wave_barrier();
     float oLs = 0.0f, oLm = 0.0f, oRs = 0.0f, oRm = 0.0f;  // lane q: the parents of height q
-    if (g.S == kMaxSpanBits)  // the usual partition: no per-level test in the climb
-      climb_paths<true>(kMaxSpanBits, lane, merges, v, other, oLs, oLm, oRs, oRm);
-    else
-      climb_paths<false>(g.S, lane, merges, v, other, oLs, oLm, oRs, oRm);
-    if (lane < g.S) {
+    climb_paths<FULL>(S, lane, merges, v, other, oLs, oLm, oRs, oRm);
+    if (lane < S) {
       const uint32_t pa = A >> 1, pb = Bn >> 1;
       t.sum[pa] = oLs;
       t.mn[pa] = oLm;
@@ -592,7 +593,7 @@ __device__ __forceinline__ void uniform_range(const TreePtrs& t, const Geom& g, 
   // wave climbs.
   if (threadIdx.x >= 64) {
     float full = v;  // sum of a node of height k covering new leaves only
-    for (int k = 0; k <= g.S; ++k) {
+    for (int k = 0; k <= S; ++k) {
       const uint32_t A = (leaf0 + lo) >> k, Bn = (leaf0 + hi - 1) >> k;
       const uint32_t first = (k == 0) ? A : A + 1;
       for (uint32_t x = first + threadIdx.x - 64; x < Bn + (k == 0 ? 1u : 0u);
@@ -1051,10 +1052,11 @@ struct IntakeRuns {
   }
 };
 
+template <bool FULL>
 __device__ __forceinline__ IntakeRuns intake_runs(uint32_t cursor, uint32_t count, const Geom& g,
                                                   uint32_t part) {
-  const uint32_t span = 1u << g.S;
-  const uint32_t base = part << g.S;
+  const uint32_t span = 1u << span_bits<FULL>(g);
+  const uint32_t base = part << span_bits<FULL>(g);
   const uint64_t end = (uint64_t)cursor + count;
   const uint32_t a_lo = max(cursor, base);
   const uint32_t a_hi = min((uint32_t)(end < g.n ? end : g.n), base + span);
@@ -1078,21 +1080,21 @@ __device__ __forceinline__ IntakeRuns intake_runs(uint32_t cursor, uint32_t coun
 // for the LDS repair of a single run of given priorities; without one such
 // a run is rebuilt like two.  Returns at once when the range misses the
 // partition.  Every argument is block-uniform.
-template <bool RANGE, typename SM>
+template <bool RANGE, bool FULL, typename SM>
 __device__ __forceinline__ void intake_partition(SM& sm, const TreePtrs& t, const Geom& g,
                                                  uint32_t part, uint32_t cursor, uint32_t count,
                                                  const float* prio, float v, bool carry,
                                                  uint32_t* max_dst) {
   const uint32_t base = part << g.S;
-  const IntakeRuns ir = intake_runs(cursor, count, g, part);
+  const IntakeRuns ir = intake_runs<FULL>(cursor, count, g, part);
   const int runs = ir.runs;
   const uint32_t lo0 = ir.lo0, hi0 = ir.hi0, hi1 = ir.hi1;
   if (runs == 0) return;
   if (runs == 1 && !prio) {
     // One run at the running max (the usual intake): no LDS, no barrier.
     float sib_s = 0.0f, sib_m = 0.0f;
-    load_range_boundary(t, g, part, lo0, hi0, sib_s, sib_m);
-    uniform_range(t, g, part, lo0, hi0, v, sib_s, sib_m);
+    load_range_boundary<FULL>(t, g, part, lo0, hi0, sib_s, sib_m);
+    uniform_range<FULL>(t, g, part, lo0, hi0, v, sib_s, sib_m);
     return;
   }
   // One run: its boundary siblings go out with the other loads.
@@ -1139,6 +1141,7 @@ __device__ __forceinline__ void intake_partition(SM& sm, const TreePtrs& t, cons
 // Ring intake ("GPU-Resident Prioritized Experience Replay", section
 // "Experience Insertion"): new slots take the given priority or the running
 // max priority; rows are copied by the blocks past the tree blocks.
+template <bool FULL>
 __global__ void __launch_bounds__(256) add_kernel(TreePtrs t, Geom g, Storage st, AddArgs a) {
   __shared__ AddSmem sm;
   // The arguments the first steps need, fetched in one batch.
@@ -1156,8 +1159,8 @@ __global__ void __launch_bounds__(256) add_kernel(TreePtrs t, Geom g, Storage st
   if (w >= tr.len[0] + tr.len[1]) return;  // spare block of a worst-case grid
   const uint32_t part = (w < tr.len[0]) ? tr.first[0] + w : tr.first[1] + (w - tr.len[0]);
   const float m0 = __uint_as_float(t.ctrl->maxp_bits[a.src]);
-  intake_partition<true>(sm, t, g, part, cursor, a.count, a.prio, m0, w == 0,
-                         &t.ctrl->maxp_bits[a.dst]);
+  intake_partition<true, FULL>(sm, t, g, part, cursor, a.count, a.prio, m0, w == 0,
+                               &t.ctrl->maxp_bits[a.dst]);
 }
 
 // LDS of the fused update + intake block when the intake brings its own
@@ -1203,7 +1206,7 @@ __global__ void __launch_bounds__(kUpdThreads) update_add_kernel(TreePtrs t, Geo
     return;
   }
   const uint32_t part = blockIdx.x;
-  const IntakeRuns ir = intake_runs(cursor, b.count, g, part);
+  const IntakeRuns ir = intake_runs<FULL>(cursor, b.count, g, part);
   const float m0 = __uint_as_float(t.ctrl->maxp_bits[a.src]);
   // Update entries at slots the intake takes are left out of the repair
   // (the intake overwrites them; their priorities still count).
@@ -1219,14 +1222,14 @@ __global__ void __launch_bounds__(kUpdThreads) update_add_kernel(TreePtrs t, Geo
     // program order, its loads of the boundary siblings seeing that
     // repair's stores.  The run's interior nodes are the intake's alone.
     float sib_s = 0.0f, sib_m = 0.0f;
-    load_range_boundary(t, g, part, ir.lo0, ir.hi0, sib_s, sib_m);
-    uniform_range(t, g, part, ir.lo0, ir.hi0, v, sib_s, sib_m);
+    load_range_boundary<FULL>(t, g, part, ir.lo0, ir.hi0, sib_s, sib_m);
+    uniform_range<FULL>(t, g, part, ir.lo0, ir.hi0, v, sib_s, sib_m);
     return;
   }
   // The update's repair is complete, and visible to the whole block, before
   // the intake reads the nodes around its run.
   __syncthreads();
-  intake_partition<PRIO>(sm, t, g, part, cursor, b.count, b.prio, v, false,
+  intake_partition<PRIO, FULL>(sm, t, g, part, cursor, b.count, b.prio, v, false,
                          &t.ctrl->maxp_bits[b.dst]);
 }
 
@@ -1385,7 +1388,12 @@ hipError_t launch_add(const TreePtrs& t, const Geom& g, const Storage& st, RingR
   if (st.D > 0)
     ncopy = grid_for((uint64_t)count * (uint64_t)st.D / 4 + count, kTreeThreads * 4, 2048);
   a.last = a.ntree + ncopy - 1u;
-  hipLaunchKernelGGL(add_kernel, dim3(a.ntree + ncopy), dim3(kTreeThreads), 0, s, t, g, st, a);
+  if (g.S == kMaxSpanBits)
+    hipLaunchKernelGGL(add_kernel<true>, dim3(a.ntree + ncopy), dim3(kTreeThreads), 0, s, t, g, st,
+                       a);
+  else
+    hipLaunchKernelGGL(add_kernel<false>, dim3(a.ntree + ncopy), dim3(kTreeThreads), 0, s, t, g,
+                       st, a);
   return hipGetLastError();
 }
 
