@@ -296,8 +296,11 @@ __device__ __forceinline__ void emit(const SampleArgs& a, uint32_t wave, int lan
   }
 }
 
-// STREAM: masses from the generator stream instead of a.u.
-template <int G, int V, bool STREAM>
+// STREAM: masses from the generator stream instead of a.u.  FN > 0: the
+// levels below the top are exactly FN rounds of FR levels (the usual
+// 4096-leaf partitions), known when compiling, so that the rounds are
+// unrolled and test no lane count; else a.nrounds rounds of a.rounds[r].
+template <int G, int V, bool STREAM, int FR, int FN>
 __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleArgs a) {
   extern __shared__ float top[];  // nodes [0, 2^(K+1)) of the sum tree
   // The arguments the first steps need, fetched in one batch: left to
@@ -478,8 +481,7 @@ __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleArgs a) {
   float leaf = 0.0f;
   if (a.nrounds == 0) leaf = top[node];
 
-  for (int r = 0; r < a.nrounds; ++r) {
-    const int R = a.rounds[r];
+  auto round = [&](const int R) {
     const int lg = R - LOGV;  // log2 of the lanes used this round (<= LOGG)
     const uint32_t base = node << R;
     const bool used = j < (1 << lg);
@@ -515,9 +517,16 @@ __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleArgs a) {
     float lv;
     const int e = lane_descent<V>(x, m, lv);
     uint32_t pos = (uint32_t)j * V + (uint32_t)e;
-    if constexpr (G > 1) {
+    if constexpr (G == 64) {
+      // One sample per wave: the lane that holds the path is wave-uniform.
       const uint64_t mask = __ballot(on);
-      const uint64_t gm = (G == 64) ? mask : ((mask >> gbase) & ((1ull << G) - 1ull));
+      const int src = mask ? (__ffsll((unsigned long long)mask) - 1) : 0;
+      m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m), src));
+      pos = (uint32_t)__builtin_amdgcn_readlane((int)pos, src);
+      lv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lv), src));
+    } else if constexpr (G > 1) {
+      const uint64_t mask = __ballot(on);
+      const uint64_t gm = (mask >> gbase) & ((1ull << G) - 1ull);
       const int src = gbase + (gm ? (__ffsll((unsigned long long)gm) - 1) : 0);
       m = __shfl(m, src);
       pos = (uint32_t)__shfl((int)pos, src);
@@ -525,6 +534,12 @@ __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleArgs a) {
     }
     node = base + pos;
     leaf = lv;
+  };
+  if constexpr (FN > 0) {
+#pragma unroll
+    for (int r = 0; r < FN; ++r) round(FR);
+  } else {
+    for (int r = 0; r < a.nrounds; ++r) round(a.rounds[r]);
   }
 
   uint32_t slot = node - a.n;
@@ -554,7 +569,9 @@ __global__ void __launch_bounds__(kSampleThreads) uniform_kernel(SampleArgs a) {
   emit<G, SPW>(a, wave, lane, b, b < a.B && (lane & (G - 1)) == 0, slot, 0.0f, 0.0f);
 }
 
-template <int G, int V>
+// FR, FN: the round shape of the usual partition for this G and V, taken
+// when the plan has exactly that shape.
+template <int G, int V, int FR, int FN>
 hipError_t launch_variant(const SampleArgs& a, hipStream_t s) {
   constexpr int SPW = 64 / G;
   const uint64_t waves = (a.B + SPW - 1) / SPW;
@@ -562,10 +579,20 @@ hipError_t launch_variant(const SampleArgs& a, hipStream_t s) {
   size_t lds = 0;
   if (a.top_mode == kTopRebuild) lds = 2 * (sizeof(float) << (a.P + 1));
   if (a.top_mode == kTopWhole) lds = sizeof(float) << (a.top + 1);
-  if (a.u)
-    hipLaunchKernelGGL((sample_kernel<G, V, false>), dim3(grid), dim3(kSampleThreads), lds, s, a);
+  bool fixed = a.nrounds == FN;
+  for (int r = 0; r < a.nrounds; ++r) fixed = fixed && a.rounds[r] == FR;
+  if (a.u && fixed)
+    hipLaunchKernelGGL((sample_kernel<G, V, false, FR, FN>), dim3(grid), dim3(kSampleThreads), lds,
+                       s, a);
+  else if (a.u)
+    hipLaunchKernelGGL((sample_kernel<G, V, false, 0, 0>), dim3(grid), dim3(kSampleThreads), lds,
+                       s, a);
+  else if (fixed)
+    hipLaunchKernelGGL((sample_kernel<G, V, true, FR, FN>), dim3(grid), dim3(kSampleThreads), lds,
+                       s, a);
   else
-    hipLaunchKernelGGL((sample_kernel<G, V, true>), dim3(grid), dim3(kSampleThreads), lds, s, a);
+    hipLaunchKernelGGL((sample_kernel<G, V, true, 0, 0>), dim3(grid), dim3(kSampleThreads), lds,
+                       s, a);
   return hipGetLastError();
 }
 
@@ -648,11 +675,11 @@ hipError_t launch_sample(const TreePtrs& t, const Geom& g, const Storage& st,
   for (int r = 0; r < kMaxRounds; ++r) a.rounds[r] = plan.rounds[r];
   switch (plan.mode) {
     case 2:
-      return launch_variant<16, 4>(a, s);
+      return launch_variant<16, 4, 6, 2>(a, s);
     case 3:
-      return launch_variant<1, 16>(a, s);
+      return launch_variant<1, 16, 4, 3>(a, s);
     default:
-      return launch_variant<64, 4>(a, s);
+      return launch_variant<64, 4, 6, 2>(a, s);
   }
 }
 
