@@ -300,7 +300,9 @@ __device__ __forceinline__ void emit(const SampleArgs& a, uint32_t wave, int lan
 // levels below the top are exactly FN rounds of FR levels (the usual
 // 4096-leaf partitions), known when compiling, so that the rounds are
 // unrolled and test no lane count; else a.nrounds rounds of a.rounds[r].
-template <int G, int V, bool STREAM, int FR, int FN>
+// TP > 0: the top is rebuilt from 2^TP partition roots (a.P == TP), so
+// that the rebuild's and the walk's loops are fixed too.
+template <int G, int V, bool STREAM, int FR, int FN, int TP>
 __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleArgs a) {
   extern __shared__ float top[];  // nodes [0, 2^(K+1)) of the sum tree
   // The arguments the first steps need, fetched in one batch: left to
@@ -332,7 +334,7 @@ __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleArgs a) {
     // lanes' results meet through shuffles, every node formed on the way
     // stored to LDS.  Only the joins of the four segment roots wait for a
     // barrier.
-    const int P = a.P;
+    const int P = TP > 0 ? TP : a.P;
     const uint32_t np = 1u << P;
     float* mtop = top + 2 * np;
     const int wv = threadIdx.x >> 6;
@@ -472,7 +474,9 @@ __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleArgs a) {
   if (!(m < T)) m = __uint_as_float(__float_as_uint(T) - 1u);  // largest f32 below T
 
   uint32_t node = 1;
-  for (int l = 0; l < a.top; ++l) {
+  const int levels_in_lds = TP > 0 ? TP : a.top;
+#pragma unroll
+  for (int l = 0; l < levels_in_lds; ++l) {
     const float2 c = reinterpret_cast<const float2*>(top)[node];  // children 2node, 2node+1
     const bool right = !(c.x > m || c.y == 0.0f);
     if (right) m = m - c.x;
@@ -569,6 +573,33 @@ __global__ void __launch_bounds__(kSampleThreads) uniform_kernel(SampleArgs a) {
   emit<G, SPW>(a, wave, lane, b, b < a.B && (lane & (G - 1)) == 0, slot, 0.0f, 0.0f);
 }
 
+template <int G, int V, bool STREAM, int FR, int FN, int TP>
+hipError_t launch_one(const SampleArgs& a, unsigned grid, size_t lds, hipStream_t s) {
+  hipLaunchKernelGGL((sample_kernel<G, V, STREAM, FR, FN, TP>), dim3(grid), dim3(kSampleThreads),
+                     lds, s, a);
+  return hipGetLastError();
+}
+
+// The usual round shape (FR, FN) with the top depth of trees of 2^20 to
+// 2^24 leaves fixed when compiling; other depths at run time.
+template <int G, int V, bool STREAM, int FR, int FN>
+hipError_t launch_fixed(const SampleArgs& a, unsigned grid, size_t lds, hipStream_t s) {
+  switch (a.top_mode == kTopRebuild ? a.P : 0) {
+    case 8:
+      return launch_one<G, V, STREAM, FR, FN, 8>(a, grid, lds, s);
+    case 9:
+      return launch_one<G, V, STREAM, FR, FN, 9>(a, grid, lds, s);
+    case 10:
+      return launch_one<G, V, STREAM, FR, FN, 10>(a, grid, lds, s);
+    case 11:
+      return launch_one<G, V, STREAM, FR, FN, 11>(a, grid, lds, s);
+    case 12:
+      return launch_one<G, V, STREAM, FR, FN, 12>(a, grid, lds, s);
+    default:
+      return launch_one<G, V, STREAM, FR, FN, 0>(a, grid, lds, s);
+  }
+}
+
 // FR, FN: the round shape of the usual partition for this G and V, taken
 // when the plan has exactly that shape.
 template <int G, int V, int FR, int FN>
@@ -581,19 +612,10 @@ hipError_t launch_variant(const SampleArgs& a, hipStream_t s) {
   if (a.top_mode == kTopWhole) lds = sizeof(float) << (a.top + 1);
   bool fixed = a.nrounds == FN;
   for (int r = 0; r < a.nrounds; ++r) fixed = fixed && a.rounds[r] == FR;
-  if (a.u && fixed)
-    hipLaunchKernelGGL((sample_kernel<G, V, false, FR, FN>), dim3(grid), dim3(kSampleThreads), lds,
-                       s, a);
-  else if (a.u)
-    hipLaunchKernelGGL((sample_kernel<G, V, false, 0, 0>), dim3(grid), dim3(kSampleThreads), lds,
-                       s, a);
-  else if (fixed)
-    hipLaunchKernelGGL((sample_kernel<G, V, true, FR, FN>), dim3(grid), dim3(kSampleThreads), lds,
-                       s, a);
-  else
-    hipLaunchKernelGGL((sample_kernel<G, V, true, 0, 0>), dim3(grid), dim3(kSampleThreads), lds,
-                       s, a);
-  return hipGetLastError();
+  if (a.u && fixed) return launch_fixed<G, V, false, FR, FN>(a, grid, lds, s);
+  if (a.u) return launch_one<G, V, false, 0, 0, 0>(a, grid, lds, s);
+  if (fixed) return launch_fixed<G, V, true, FR, FN>(a, grid, lds, s);
+  return launch_one<G, V, true, 0, 0, 0>(a, grid, lds, s);
 }
 
 // Split `levels` into rounds of lo..hi levels, larger rounds first.
