@@ -710,7 +710,7 @@ __device__ __forceinline__ uint32_t filled_size(const UpdateArgs& a) {
 // block's own and the others'.  Returns whether a partition was crowded
 // (then rebuilt by the whole block, which has passed a barrier since);
 // otherwise wave w returns right after its sparse repair.
-template <int PPB, bool FUSED, bool FULL, typename SM, typename Skip>
+template <int PPB, bool FUSED, bool FULL, int kChunk, typename SM, typename Skip>
 __device__ __forceinline__ bool scan_update(SM& sm, const TreePtrs& t, const Geom& g,
                                             const UpdateArgs& a, uint32_t part0, uint32_t size,
                                             float m0, bool all, Skip skip) {
@@ -724,8 +724,8 @@ __device__ __forceinline__ bool scan_update(SM& sm, const TreePtrs& t, const Geo
   }
   __syncthreads();
   // Each thread loads its share of the batch in chunks of kChunk entries, all
-  // loads of a chunk issued before any of them is looked at.
-  constexpr int kChunk = 8;
+  // loads of a chunk issued before any of them is looked at (kChunk is sized
+  // to the batch when launching: no idle slots for small batches).
   for (uint32_t b0 = 0; b0 < a.B; b0 += kUpdThreads * kChunk) {
     int64_t ix[kChunk];
     float tx[kChunk];
@@ -821,15 +821,15 @@ __device__ __forceinline__ bool scan_update(SM& sm, const TreePtrs& t, const Geo
   return true;
 }
 
-template <int PPB, bool FULL>
+template <int PPB, bool FULL, int CH>
 __global__ void __launch_bounds__(kUpdThreads) update_scan_kernel(TreePtrs t, Geom g, UpdateArgs a) {
   __shared__ UpdSmem<PPB> sm;
   // The arguments the first steps need, fetched in one batch.
   asm volatile("" ::"s"(t.ctrl), "s"(a.idx), "s"(a.td), "s"(a.B), "s"(a.src), "s"(a.size),
                "s"(a.ring.dev), "s"(g.n), "s"(g.S));
   const float m0 = __uint_as_float(t.ctrl->maxp_bits[a.src]);
-  scan_update<PPB, false, FULL>(sm, t, g, a, blockIdx.x * PPB, filled_size(a), m0, false,
-                                [](uint32_t) { return false; });
+  scan_update<PPB, false, FULL, CH>(sm, t, g, a, blockIdx.x * PPB, filled_size(a), m0, false,
+                                    [](uint32_t) { return false; });
 }
 
 // Large batches, step 1: every valid entry goes to its partition's bucket
@@ -1188,7 +1188,7 @@ struct UpdAddSmem {
 // such a block gathers from the whole batch while scanning it.  Both raise
 // the running max in the same slot (a.dst == b.dst).  Blocks past the first
 // 2^P copy the intake's rows.
-template <bool PRIO, bool FULL>
+template <bool PRIO, bool FULL, int CH>
 __global__ void __launch_bounds__(kUpdThreads) update_add_kernel(TreePtrs t, Geom g, Storage st,
                                                                  UpdateArgs a, AddArgs b) {
   __shared__ std::conditional_t<PRIO, UpdAddSmem, UpdSmem<1>> sm;
@@ -1210,7 +1210,7 @@ __global__ void __launch_bounds__(kUpdThreads) update_add_kernel(TreePtrs t, Geo
   const float m0 = __uint_as_float(t.ctrl->maxp_bits[a.src]);
   // Update entries at slots the intake takes are left out of the repair
   // (the intake overwrites them; their priorities still count).
-  const bool crowded = scan_update<1, true, FULL>(sm, t, g, a, part, size, m0, !PRIO && ir.runs > 0,
+  const bool crowded = scan_update<1, true, FULL, CH>(sm, t, g, a, part, size, m0, !PRIO && ir.runs > 0,
                                             [&](uint32_t off) { return ir.has(off); });
   if (ir.runs == 0) return;
   float v = m0;
@@ -1278,6 +1278,12 @@ __global__ void __launch_bounds__(256) top_kernel(TreePtrs t, Geom g) {
   }
 }
 
+// Batch entries per thread and chunk of the update scan: the batch over the
+// block's threads, rounded up to 2, 4 or 8 (larger batches take more chunks).
+inline int scan_chunk(int64_t B) {
+  return B <= 2 * kUpdThreads ? 2 : (B <= 4 * kUpdThreads ? 4 : 8);
+}
+
 inline unsigned grid_for(uint64_t work, unsigned per_block, unsigned cap) {
   uint64_t b = (work + per_block - 1) / per_block;
   if (b < 1) b = 1;
@@ -1324,12 +1330,19 @@ hipError_t launch_update(const TreePtrs& t, const Buckets& bk, const Geom& g, Ri
   const uint64_t np = 1ull << g.P;
   if (!update_uses_buckets(g, B)) {
     // One partition per block: the batch scan is spread over the most blocks.
-    if (g.S == kMaxSpanBits)
-      hipLaunchKernelGGL((update_scan_kernel<1, true>), dim3((unsigned)np), dim3(kUpdThreads), 0,
-                         s, t, g, a);
+    const int ch = scan_chunk(B);
+    if (g.S == kMaxSpanBits && ch == 2)
+      hipLaunchKernelGGL((update_scan_kernel<1, true, 2>), dim3((unsigned)np), dim3(kUpdThreads),
+                         0, s, t, g, a);
+    else if (g.S == kMaxSpanBits && ch == 4)
+      hipLaunchKernelGGL((update_scan_kernel<1, true, 4>), dim3((unsigned)np), dim3(kUpdThreads),
+                         0, s, t, g, a);
+    else if (g.S == kMaxSpanBits)
+      hipLaunchKernelGGL((update_scan_kernel<1, true, 8>), dim3((unsigned)np), dim3(kUpdThreads),
+                         0, s, t, g, a);
     else
-      hipLaunchKernelGGL((update_scan_kernel<1, false>), dim3((unsigned)np), dim3(kUpdThreads), 0,
-                         s, t, g, a);
+      hipLaunchKernelGGL((update_scan_kernel<1, false, 8>), dim3((unsigned)np), dim3(kUpdThreads),
+                         0, s, t, g, a);
     return hipGetLastError();
   }
   // Bucketed: four partitions per block, one wave each, while the batch
@@ -1436,18 +1449,24 @@ hipError_t launch_update_add(const TreePtrs& t, const Geom& g, const Storage& st
     ncopy = grid_for((uint64_t)count * (uint64_t)st.D / 4 + count, kTreeThreads * 4, 2048);
   b.last = np + ncopy - 1u;
   const bool full = g.S == kMaxSpanBits;
-  if (prio && full)
-    hipLaunchKernelGGL((update_add_kernel<true, true>), dim3(np + ncopy), dim3(kUpdThreads), 0, s,
-                       t, g, st, a, b);
+  const int ch = scan_chunk(B);
+  const dim3 grid(np + ncopy), block(kUpdThreads);
+  if (!full && prio)
+    hipLaunchKernelGGL((update_add_kernel<true, false, 8>), grid, block, 0, s, t, g, st, a, b);
+  else if (!full)
+    hipLaunchKernelGGL((update_add_kernel<false, false, 8>), grid, block, 0, s, t, g, st, a, b);
+  else if (prio && ch == 2)
+    hipLaunchKernelGGL((update_add_kernel<true, true, 2>), grid, block, 0, s, t, g, st, a, b);
+  else if (prio && ch == 4)
+    hipLaunchKernelGGL((update_add_kernel<true, true, 4>), grid, block, 0, s, t, g, st, a, b);
   else if (prio)
-    hipLaunchKernelGGL((update_add_kernel<true, false>), dim3(np + ncopy), dim3(kUpdThreads), 0, s,
-                       t, g, st, a, b);
-  else if (full)
-    hipLaunchKernelGGL((update_add_kernel<false, true>), dim3(np + ncopy), dim3(kUpdThreads), 0, s,
-                       t, g, st, a, b);
+    hipLaunchKernelGGL((update_add_kernel<true, true, 8>), grid, block, 0, s, t, g, st, a, b);
+  else if (ch == 2)
+    hipLaunchKernelGGL((update_add_kernel<false, true, 2>), grid, block, 0, s, t, g, st, a, b);
+  else if (ch == 4)
+    hipLaunchKernelGGL((update_add_kernel<false, true, 4>), grid, block, 0, s, t, g, st, a, b);
   else
-    hipLaunchKernelGGL((update_add_kernel<false, false>), dim3(np + ncopy), dim3(kUpdThreads), 0,
-                       s, t, g, st, a, b);
+    hipLaunchKernelGGL((update_add_kernel<false, true, 8>), grid, block, 0, s, t, g, st, a, b);
   return hipGetLastError();
 }
 
