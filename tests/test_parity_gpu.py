@@ -82,6 +82,36 @@ def test_sampler_modes_agree(mode, monkeypatch):
         compare_trees(o, g, "mode %s batch %d tree" % (mode, rep))
 
 
+@pytest.mark.parametrize("L", [22, 23, 24])
+def test_sampler_top_depths(L):
+    """Trees of 2^22 to 2^24 leaves (10 to 12 levels above the 4096-leaf
+    partitions, each a variant of its own) in every descent mode, before and
+    after an update: indices bit for bit, weights within 1e-6."""
+    n = 1 << L
+    say("top depth", L)
+    rng = np.random.default_rng(L)
+    o = Oracle(n)
+    g = _buf(n, max_batch=4096)
+    p0 = (rng.random(n) ** 0.6).astype(np.float32)
+    o.add(n, prio=p0)
+    g.add(n, prio=dev(p0))
+    for step in range(2):
+        for mode in ("1", "2", "3"):
+            os.environ["PER_SAMPLE_MODE"] = mode
+            try:
+                u = rng.random(700, dtype=np.float32)
+                u[:2] = [0.0, np.nextafter(np.float32(1), np.float32(0))]
+                compare_sample(g.sample(dev(u), beta=0.4), o.sample(u, beta=0.4),
+                               "L=%d step %d mode %s" % (L, step, mode))
+            finally:
+                del os.environ["PER_SAMPLE_MODE"]
+        idx = rng.integers(0, n, 3000).astype(np.int64)
+        td = (rng.standard_normal(3000) * 2).astype(np.float32)
+        o.update(idx, td)
+        g.update(dev(idx), dev(td))
+        compare_trees(o, g, "L=%d step %d update" % (L, step))
+
+
 def test_zero_priorities_never_sampled():
     name = "collision_stress_2m"
     n = 1 << 21
