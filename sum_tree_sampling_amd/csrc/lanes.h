@@ -68,4 +68,12 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
              (uint32_t)__builtin_amdgcn_readlane((int)v, 32));
 }
 
+// The bitwise or over the wave, the same in every lane.
+__device__ __forceinline__ uint32_t wave_or_u32(uint32_t v) {
+#pragma unroll
+  for (int s = 0; s < 5; ++s) v |= (uint32_t)__float_as_uint(xor_lanes(__uint_as_float(v), s));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 0) |
+         (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+}
+
 }  // namespace per

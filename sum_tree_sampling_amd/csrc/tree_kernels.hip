@@ -156,6 +156,9 @@ __device__ __forceinline__ void sparse_chain(const TreePtrs& t, const Geom& g, u
 
   float vs = p, vm = p;
   const uint64_t lanes_below = (1ull << lane) - 1ull;
+  // Bit k: some chain ends at step k (d == L - 1 - k); the last lane's
+  // chain ends at the partition root, past every step.
+  const uint32_t ends = wave_or_u32(valid ? 1u << (g.L - 1 - d) : 0u);
 #pragma unroll
   for (int k = 0; k < kMaxSpanBits; ++k) {
     if (k >= S) continue;       // uniform across the wave (none when FULL)
@@ -166,8 +169,8 @@ __device__ __forceinline__ void sparse_chain(const TreePtrs& t, const Geom& g, u
     float os = ps[k], om = pm[k];
     // Chains ending here (d == l) deliver their value to the right; most
     // levels have none, so the lookup runs only when one does (uniform test).
-    const uint64_t eq = __ballot(valid && d == l);
-    if (eq != 0ull) {
+    if ((ends >> k) & 1u) {
+      const uint64_t eq = __ballot(valid && d == l);
       const uint64_t le = __ballot(valid && d <= l);
       const uint64_t below = le & lanes_below;
       const int src = below ? 63 - __clzll(below) : lane;
