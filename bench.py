@@ -411,11 +411,15 @@ def main():
     inp = workloads.StepInputs(args.workload)
     u_all = np.stack([inp.u() for _ in range(total)])
     td_all = np.stack([inp.td() for _ in range(total)])
-    u_d = torch.from_numpy(u_all).to(dev)
-    td_d = torch.from_numpy(td_all).to(dev)
+    # One view per step, made before timing: indexing a tensor inside the
+    # loop costs microseconds of host time per call, which the short steps
+    # would otherwise wait on.
+    u_d = list(torch.from_numpy(u_all).to(dev).unbind(0))
+    td_d = list(torch.from_numpy(td_all).to(dev).unbind(0))
     idx_d = None
     if "unique" in spec:
-        idx_d = torch.from_numpy(np.stack([inp.update_idx() for _ in range(total)])).to(dev)
+        idx_d = list(torch.from_numpy(np.stack([inp.update_idx() for _ in range(total)]))
+                     .to(dev).unbind(0))
     rows = D > 0
     out = {"idx": torch.empty(B, dtype=torch.int64, device=dev)}
     if spec["weights"]:
