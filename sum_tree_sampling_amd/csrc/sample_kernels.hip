@@ -632,15 +632,16 @@ void split_rounds(int levels, int hi, SamplePlan& p) {
 // Modes: 1 = one wave per sample (G=64, V=4, rounds of up to 8 levels);
 // 2 = 16 lanes per sample (G=16, V=4, up to 6 levels);
 // 3 = one lane per sample (G=1, V=16, rounds of exactly 4 levels).
-// Batches of a few hundred to a few thousand samples that gather rows of 32
-// floats or more take one wave per sample: the row copies then spread over
-// four times as many waves (measured on the DQN step, 2^20 slots of 64
-// floats, B = 1024: 0.65 us less per step); without rows, or with very few
-// samples, the extra blocks and top rebuilds cost more than they give.
+// Batches of a few hundred samples take one wave per sample, up to a few
+// thousand when they gather rows of 32 floats or more: the row copies then
+// spread over four times as many waves (measured on the DQN step, 2^20
+// slots of 64 floats, B = 1024: 0.65 us less per step; without rows, 2^21
+// slots and B = 512: 0.1 us less).  With very few samples, or thousands
+// without rows, the extra blocks and top rebuilds cost more than they give.
 SamplePlan make_sample_plan(const Geom& g, int64_t B, uint32_t row_floats) {
   SamplePlan p{};
   p.mode = (B <= 16384) ? 2 : 3;
-  if (row_floats >= 32 && B >= 256 && B <= 2048) p.mode = 1;
+  if (B >= 256 && B <= (row_floats >= 32 ? 2048 : 1024)) p.mode = 1;
   const char* env = getenv("PER_SAMPLE_MODE");
   if (env && atoi(env) >= 1 && atoi(env) <= 3) p.mode = atoi(env);
   if (g.P > 0 && g.P <= kMaxTopBits) {
