@@ -256,11 +256,12 @@ int per_sample_padded(per_t* h, int64_t B, const float* d_u, double beta, int64_
 
 /*
  * The nodes above the update partitions (the top levels of both trees) are
- * rebuilt lazily: per_add and per_update leave them to the next per_sample,
- * which needs them anyway and writes them back.  per_flush enqueues that
- * rebuild now if it is pending (one small kernel; a no-op otherwise), so that
- * the arrays of per_tree_ptrs hold every node.  per_total and per_min call
- * it themselves.
+ * rebuilt lazily: per_add and per_update leave them stale, and per_sample
+ * rebuilds them in on-chip memory for its own descent without storing them
+ * (on trees too deep for that it stores them first).  per_flush enqueues
+ * the rebuild of the stored top now if it is pending (one small kernel; a
+ * no-op otherwise), so that the arrays of per_tree_ptrs hold every node.
+ * per_total and per_min call it themselves.
  */
 int per_flush(per_t* h, hipStream_t stream);
 

@@ -361,7 +361,7 @@ int sample_impl(per_t* h, int64_t B, SampleKind kind, const float* d_u, uint64_t
                                       0, 0, beta, d_idx_out, d_w_out,
                                       any_rows ? d_states_out : nullptr, d_next_states_out,
                                       d_actions_out, d_rewards_out, d_dones_out,
-                                      (uint32_t)out_stride, dones_f32, false, stream,
+                                      (uint32_t)out_stride, dones_f32, stream,
                                       h->rvals[0]);
     return e == hipSuccess ? ok() : hip_fail(e, what);
   }
@@ -385,9 +385,10 @@ int sample_impl(per_t* h, int64_t B, SampleKind kind, const float* d_u, uint64_t
                                     kind == kGivenMasses ? d_u : nullptr, seed, offset, beta,
                                     d_idx_out, d_w_out, any_rows ? d_states_out : nullptr,
                                     d_next_states_out, d_actions_out, d_rewards_out,
-                                    d_dones_out, (uint32_t)out_stride, dones_f32, stale, stream);
+                                    d_dones_out, (uint32_t)out_stride, dones_f32, stream);
   if (e != hipSuccess) return hip_fail(e, what);
-  h->top_stale = false;
+  // A rebuilding sampler keeps its top in LDS: the stored top stays pending
+  // until per_flush (or a sampler that reads it from memory) rebuilds it.
   return ok();
 }
 

@@ -139,7 +139,7 @@ hipError_t launch_sample(const TreePtrs& t, const Geom& g, const Storage& st,
                          float* w_out, float* states_out,
                          float* next_out, uint32_t* actions_out, float* rewards_out,
                          void* dones_out, uint32_t out_stride, bool dones_f32,
-                         bool write_top, hipStream_t s, const uint32_t* order = nullptr);
+                         hipStream_t s, const uint32_t* order = nullptr);
 
 SamplePlan make_sample_plan(const Geom& g, int64_t B, uint32_t row_floats);
 

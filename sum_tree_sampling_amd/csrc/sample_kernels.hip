@@ -71,7 +71,6 @@ struct SampleArgs {
   Storage st;
   int P;          // partitions = 2^P; the top P levels are rebuilt in LDS
   int top_mode;   // kTopNone / kTopRebuild / kTopWhole
-  int write_top;  // block 0 stores the rebuilt top nodes
   int top;        // levels walked in LDS
   int nrounds;
   int rounds[kMaxRounds];
@@ -309,7 +308,7 @@ __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleArgs a) {
   // itself, the compiler loads each after the branch that first needs it,
   // one dependent trip each.
   asm volatile("" ::"s"(a.top_mode), "s"(a.P), "s"(a.sum), "s"(a.mn), "s"(a.u), "s"(a.B),
-               "s"(a.top), "s"(a.nrounds), "s"(a.write_top));
+               "s"(a.top), "s"(a.nrounds));
   constexpr int LOGG = ilog2(G);
   constexpr int LOGV = ilog2(V);
   constexpr int SPW = 64 / G;  // samples per wave
@@ -446,12 +445,6 @@ __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleArgs a) {
         mtop[1] = min_f32(m2, m3);
       }
       __syncthreads();
-    }
-    if (a.write_top && blockIdx.x == 0) {
-      for (uint32_t h = 1 + threadIdx.x; h < np; h += kSampleThreads) {
-        a.sum[h] = top[h];
-        a.mn[h] = mtop[h];
-      }
     }
     T = top[1];
     pmin = mtop[1];
@@ -668,7 +661,7 @@ hipError_t launch_sample(const TreePtrs& t, const Geom& g, const Storage& st,
                          float* w_out, float* states_out,
                          float* next_out, uint32_t* actions_out, float* rewards_out,
                          void* dones_out, uint32_t out_stride, bool dones_f32,
-                         bool write_top, hipStream_t s, const uint32_t* order) {
+                         hipStream_t s, const uint32_t* order) {
   SampleArgs a{};
   a.sum = t.sum;
   a.mn = t.mn;
@@ -692,7 +685,6 @@ hipError_t launch_sample(const TreePtrs& t, const Geom& g, const Storage& st,
   a.st = st;
   a.P = g.P;
   a.top_mode = plan.top_mode;
-  a.write_top = write_top ? 1 : 0;
   a.top = plan.top_levels;
   a.nrounds = plan.nrounds;
   for (int r = 0; r < kMaxRounds; ++r) a.rounds[r] = plan.rounds[r];
