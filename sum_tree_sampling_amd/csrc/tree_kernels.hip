@@ -707,19 +707,16 @@ __device__ __forceinline__ uint32_t filled_size(const UpdateArgs& a) {
 // it is sparse, crowded partitions are rebuilt by the whole block after.
 // m0: the running max at the start of the call.  FUSED (one partition per
 // block): entries at offsets skip(off) are left out of the repair, their
-// priorities still raising the running max, and with `all` set
-// (block-uniform) sm.ball receives, once the scan's barrier is passed, the
-// max priority bits over every entry of the batch inside [0, size), the
-// block's own and the others'.  Returns whether a partition was crowded
-// (then rebuilt by the whole block, which has passed a barrier since);
-// otherwise wave w returns right after its sparse repair.
+// priorities still raising the running max; sm.ball is cleared for the
+// caller's batch max.  Returns whether a partition was crowded (then
+// rebuilt by the whole block, which has passed a barrier since); otherwise
+// wave w returns right after its sparse repair.
 template <int PPB, bool FUSED, bool FULL, int kChunk, typename SM, typename Skip>
 __device__ __forceinline__ bool scan_update(SM& sm, const TreePtrs& t, const Geom& g,
                                             const UpdateArgs& a, uint32_t part0, uint32_t size,
-                                            float m0, bool all, Skip skip) {
+                                            float m0, Skip skip) {
   const int nparts = (int)min((uint32_t)PPB, (1u << g.P) - part0);
   uint32_t* max_dst = &t.ctrl->maxp_bits[a.dst];
-  uint32_t mall = 0;  // max priority bits of every entry looked at (FUSED)
   if (threadIdx.x < PPB) sm.count[threadIdx.x] = 0;
   if (threadIdx.x == 0) {
     sm.bmax = 0u;
@@ -751,7 +748,7 @@ __device__ __forceinline__ bool scan_update(SM& sm, const TreePtrs& t, const Geo
       const int64_t i = ix[c];
       if (i < 0 || i >= (int64_t)size) continue;
       const uint32_t q = (uint32_t)((uint64_t)i >> span_bits<FULL>(g)) - part0;  // wraps below part0
-      if (q < (uint32_t)nparts || (FUSED && all)) pending |= 1u << c;
+      if (q < (uint32_t)nparts) pending |= 1u << c;
     }
     // One entry per lane per round: entries of one wave in different slots
     // are collected together, their sibling loads and pows overlapping,
@@ -771,29 +768,17 @@ __device__ __forceinline__ bool scan_update(SM& sm, const TreePtrs& t, const Geo
         }
         const uint32_t b = b0 + (uint32_t)c * kUpdThreads + threadIdx.x;
         const uint32_t q = (uint32_t)((uint64_t)i >> span_bits<FULL>(g)) - part0;
-        const bool own = q < (uint32_t)nparts;
-        // One priority computation for every entry looked at: collect()
-        // issues no loads for an entry index >= kSparseMax, which entries of
-        // other partitions and left-out ones take.
-        const uint32_t qq = own ? q : 0u;
-        const uint32_t part = part0 + qq;
+        // The entry is the block's: collect() issues no loads for an entry
+        // index >= kSparseMax, which left-out entries take.
+        const uint32_t part = part0 + q;
         const uint32_t off = (uint32_t)i - (part << span_bits<FULL>(g));
-        bool keep = own;
-        if constexpr (FUSED) keep = keep && !skip(off);
-        const int k = keep ? atomicAdd(&sm.count[qq], 1) : kSparseMax;
-        const float p = collect<FULL>(sm.u.sp[qq], k, t, g, part, off, b, td, m0, a.alpha, a.eps,
-                                a.p_nan);
-        if (own) atomicMax(&sm.bmax, __float_as_uint(p));
-        if constexpr (FUSED) mall = max(mall, __float_as_uint(p));
+        bool keep = true;
+        if constexpr (FUSED) keep = !skip(off);
+        const int k = keep ? atomicAdd(&sm.count[q], 1) : kSparseMax;
+        const float p = collect<FULL>(sm.u.sp[q], k, t, g, part, off, b, td, m0, a.alpha, a.eps,
+                                      a.p_nan);
+        atomicMax(&sm.bmax, __float_as_uint(p));
       }
-    }
-  }
-  if constexpr (FUSED) {
-    if (all) {
-      // One LDS atomic per wave after a shuffle reduction: an atomic from
-      // every lane to one address becomes a lane-by-lane loop.
-      const uint32_t wm = wave_max_u32(mall);
-      if ((threadIdx.x & 63) == 0) atomicMax(&sm.ball, wm);
     }
   }
   __syncthreads();
@@ -831,7 +816,7 @@ __global__ void __launch_bounds__(kUpdThreads) update_scan_kernel(TreePtrs t, Ge
   asm volatile("" ::"s"(t.ctrl), "s"(a.idx), "s"(a.td), "s"(a.B), "s"(a.src), "s"(a.size),
                "s"(a.ring.dev), "s"(g.n), "s"(g.S));
   const float m0 = __uint_as_float(t.ctrl->maxp_bits[a.src]);
-  scan_update<PPB, false, FULL, CH>(sm, t, g, a, blockIdx.x * PPB, filled_size(a), m0, false,
+  scan_update<PPB, false, FULL, CH>(sm, t, g, a, blockIdx.x * PPB, filled_size(a), m0,
                                     [](uint32_t) { return false; });
 }
 
@@ -1182,6 +1167,69 @@ struct UpdAddSmem {
   int flag;
 };
 
+// The max priority bits over the batch entries b = first, first + stride,
+// ... with an index in [0, size): what priority_of gives each (NaN and
+// infinite TD errors included).  Called by whole waves (stride a multiple of
+// 64).  p = f32(pow(|td| + eps, alpha)) rises with |td|, and an entry whose y
+// = |td| + eps lies below y* (1 - 2^-24), y* the largest finite one of its
+// wave and chunk, has an exact p at least a factor (1 - 2^-24)^alpha <= 1 -
+// 2^-41 (alpha >= 2^-16) below that of y*: far more than the few-ulp error
+// of the f64 pow, so it cannot exceed the max after rounding.  So only the
+// entries at or above that bound are raised to alpha.
+__device__ __forceinline__ uint32_t batch_max_bits(const UpdateArgs& a, uint32_t size, float m0,
+                                                   uint32_t first, uint32_t stride) {
+  constexpr int kC = 4;
+  const bool few = a.alpha >= 0x1p-16;
+  uint32_t mall = 0u;
+  for (uint32_t b0 = 0; b0 < a.B; b0 += stride * kC) {  // the same trips in every wave
+    int64_t ix[kC];
+    float tx[kC];
+#pragma unroll
+    for (int c = 0; c < kC; ++c) {
+      const uint32_t b = b0 + c * stride + first;
+      ix[c] = -1;
+      tx[c] = 0.0f;
+      if (b < a.B) {
+        ix[c] = a.idx[b];
+        tx[c] = a.td[b];
+      }
+    }
+    uint32_t pend = 0u, xb = 0u;
+#pragma unroll
+    for (int c = 0; c < kC; ++c) {
+      if (ix[c] < 0 || ix[c] >= (int64_t)size) continue;
+      const float x = fabsf(tx[c]);
+      if (__builtin_isnan(x)) {
+        mall = max(mall, __float_as_uint(a.p_nan));
+      } else if (__builtin_isinf(x)) {
+        mall = max(mall, __float_as_uint(m0));
+      } else {
+        xb = max(xb, __float_as_uint(x));
+        pend |= 1u << c;
+      }
+    }
+    if (few) {
+      const double ys = (double)__uint_as_float(wave_max_u32(xb)) + a.eps;
+      const double bound = ys - ys * 0x1p-24;
+#pragma unroll
+      for (int c = 0; c < kC; ++c)
+        if (((pend >> c) & 1u) && (double)fabsf(tx[c]) + a.eps < bound) pend &= ~(1u << c);
+    }
+    while (__ballot(pend != 0u) != 0ull) {  // one entry per lane per round
+      if (pend != 0u) {
+        const int c = __builtin_ctz(pend);
+        pend &= pend - 1u;
+        float td = tx[0];
+#pragma unroll
+        for (int cc = 1; cc < kC; ++cc)
+          if (c == cc) td = tx[cc];
+        mall = max(mall, __float_as_uint(priority_of(td, m0, a.alpha, a.eps, a.p_nan)));
+      }
+    }
+  }
+  return mall;
+}
+
 // An update batch followed by an intake in one launch, with the result of
 // the two calls in that order.  Block `part` of the first 2^P updates its
 // partition from the batch as the scan path does, then applies the intake's
@@ -1213,27 +1261,42 @@ __global__ void __launch_bounds__(kUpdThreads) update_add_kernel(TreePtrs t, Geo
   const float m0 = __uint_as_float(t.ctrl->maxp_bits[a.src]);
   // Update entries at slots the intake takes are left out of the repair
   // (the intake overwrites them; their priorities still count).
-  const bool crowded = scan_update<1, true, FULL, CH>(sm, t, g, a, part, size, m0, !PRIO && ir.runs > 0,
-                                            [&](uint32_t off) { return ir.has(off); });
+  const bool crowded = scan_update<1, true, FULL, CH>(sm, t, g, a, part, size, m0,
+                                                    [&](uint32_t off) { return ir.has(off); });
   if (ir.runs == 0) return;
-  float v = m0;
-  if constexpr (!PRIO) v = __uint_as_float(max(__float_as_uint(m0), sm.ball));
-  if (!PRIO && ir.runs == 1 && !crowded) {
-    // No barrier: the update's new leaves are all outside the run, so its
-    // repaired nodes meet the intake's only on the run's two boundary
-    // paths, which wave 0 computes -- after its own sparse repair, in
-    // program order, its loads of the boundary siblings seeing that
-    // repair's stores.  The run's interior nodes are the intake's alone.
+  if constexpr (PRIO) {
+    // The update's repair is complete, and visible to the whole block,
+    // before the intake reads the nodes around its run.
+    __syncthreads();
+    intake_partition<PRIO, FULL>(sm, t, g, part, cursor, b.count, b.prio, m0, false,
+                                 &t.ctrl->maxp_bits[b.dst]);
+  } else {
+    // At the running max the intake takes the max priority over the whole
+    // batch (the value at the start or a larger one of the batch): waves 1-3
+    // compute it while wave 0 finishes the partition's sparse repair and, for
+    // the usual single run, loads the run's boundary siblings, which in
+    // program order see that repair's stores.  The update's new leaves are
+    // all outside the run, so its repaired nodes meet the intake's only on
+    // the run's two boundary paths, which wave 0 climbs; the run's interior
+    // nodes are the intake's alone.
+    const bool one = ir.runs == 1 && !crowded;
     float sib_s = 0.0f, sib_m = 0.0f;
-    load_range_boundary<FULL>(t, g, part, ir.lo0, ir.hi0, sib_s, sib_m);
-    uniform_range<FULL>(t, g, part, ir.lo0, ir.hi0, v, sib_s, sib_m);
-    return;
+    if (threadIdx.x >= 64) {
+      const uint32_t wm = wave_max_u32(batch_max_bits(a, size, m0, threadIdx.x - 64,
+                                                      kUpdThreads - 64));
+      if ((threadIdx.x & 63) == 0) atomicMax(&sm.ball, wm);
+    } else if (one) {
+      load_range_boundary<FULL>(t, g, part, ir.lo0, ir.hi0, sib_s, sib_m);
+    }
+    __syncthreads();
+    const float v = __uint_as_float(max(__float_as_uint(m0), sm.ball));
+    if (one) {
+      uniform_range<FULL>(t, g, part, ir.lo0, ir.hi0, v, sib_s, sib_m);
+      return;
+    }
+    intake_partition<PRIO, FULL>(sm, t, g, part, cursor, b.count, b.prio, v, false,
+                                 &t.ctrl->maxp_bits[b.dst]);
   }
-  // The update's repair is complete, and visible to the whole block, before
-  // the intake reads the nodes around its run.
-  __syncthreads();
-  intake_partition<PRIO, FULL>(sm, t, g, part, cursor, b.count, b.prio, v, false,
-                         &t.ctrl->maxp_bits[b.dst]);
 }
 
 // Nodes [1, 2^P) above the partitions, recomputed from depth P upwards.
