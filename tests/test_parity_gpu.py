@@ -601,6 +601,8 @@ def test_graph_mode_replay_rule():
     (1 << 16, 5, 1000, 3000, True, 40000),     # given priorities; scalar row copies
     (1 << 16, 4, 2000, 5000, False, 1 << 16),  # crowded partitions; the intake spans several
     (1 << 20, 0, 8192, 700, False, 1 << 20),   # bucketed batch: enqueued as the two calls
+    (1 << 16, 0, 513, 300, False, 1 << 16),    # just past two batch entries per thread
+    (1 << 16, 3, 1025, 200, False, 50000),     # just past four
 ])
 def test_update_add(n, D, B, c, prio, fill):
     """per_update_add against the oracle's update followed by its intake,
