@@ -9,10 +9,17 @@ Default workload: the Ape-X replay shard, 2^21 leaves, B = 512, 400-item
 intake, indices only.  Prints one JSON line.
 
 The timed region is K steps between two HIP events on the launch stream
-(torch's current stream).  A second pass runs each operation on its own, K
-back-to-back launches between two events, to time each kernel live; the
-roofline figure uses the dominant one.  The CPU baseline is the plain single-threaded oracle
-running the same workload for a bounded number of steps on the host.
+(torch's current stream); every call of every step is marshalled for the C
+ABI before the first event, so the loop does nothing on the host but call
+the library.  A second pass times each operation's kernels live, step by
+step: per_time_next makes the library launch the operation through
+hipExtLaunchKernel with a start and a stop event, which bracket its kernels
+on the device (what a kernel trace measures, without the dispatch gap in
+front of each launch).  The roofline figure uses the dominant operation by
+that time.  A third pass records an event pair around each operation for
+comparison.  The other workloads follow as sub-results ("configs").  The CPU
+baseline is the plain single-threaded oracle running the same workload on
+the host, each call timed in C (bench_oracle.cpp).
 
 The roofline's "traffic" is the HBM bytes one launch of the dominant
 operation moves as the hardware counts them (rocprofv3 FETCH_SIZE and
@@ -143,59 +150,6 @@ def measured_traffic(workload: str, op: str):
     return None if e is None else float(e["bytes"])
 
 
-def graph_replay(g, step, K: int, base: int, stream, use_graph_mode: bool = True) -> dict:
-    """K whole steps captured as one HIP graph in the library's graph mode
-    and replayed: the step time without per-launch host work, a labelled
-    extra figure next to the eager headline.  In graph mode the intakes take
-    the ring cursor and size from the device, so every replay writes the
-    next slots as eager steps would; K is even, so each slot parity
-    (running max, overflow list, ring state) is flipped an even number of
-    times and a replay starts on the slots the capture started on.  The
-    rank-based step re-ranks from the host's filled size, which graph mode
-    refuses: it is captured in eager mode, valid while the ring is full (its
-    captured intakes rewrite the same slots on every replay)."""
-    import torch
-    entered = False
-    try:
-        gr = torch.cuda.CUDAGraph()
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            step(base)  # warm the capture stream
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        if use_graph_mode:
-            g.graph_mode(True)
-            entered = True
-        with torch.cuda.graph(gr):
-            for s in range(K):
-                step(base + s)
-        torch.cuda.synchronize()
-        for _ in range(3):
-            gr.replay()
-        torch.cuda.synchronize()
-        reps = 20
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(torch.cuda.current_stream())
-        for _ in range(reps):
-            gr.replay()
-        b.record(torch.cuda.current_stream())
-        torch.cuda.synchronize()
-        if entered:
-            entered = False
-            g.graph_mode(False)
-        mode = "graph mode, device ring state" if use_graph_mode else "eager mode, full ring"
-        return {"steps_per_graph": K, "replays": reps, "mode": mode,
-                "ms_per_step": a.elapsed_time(b) / (reps * K)}
-    except Exception as e:  # capture not available: report instead of failing the line
-        if entered:
-            try:
-                g.graph_mode(False)
-            except Exception:
-                pass
-        return {"error": "%s: %s" % (type(e).__name__, e)}
-
-
 def latency_floor() -> dict:
     """The floor under a step of short launches (libper_probe.so): an empty
     kernel launched back to back, and one lane's chain of dependent loads
@@ -297,33 +251,396 @@ def algorithmic_bytes(spec: dict) -> dict:
     return {"sample": float(sample), "update": float(update), "add": float(intake)}
 
 
-def cpu_baseline(spec: dict, seconds: float) -> dict:
-    """The oracle, single-threaded, on a bounded number of steps of the workload."""
+
+
+# ------------------------------------------------------------ CPU baseline
+
+ORACLE_TIMER_SRC = os.path.join(ROOT, "bench_oracle.cpp")
+ORACLE_TIMER_LIB = os.path.join(ROOT, "bench_oracle.so")
+
+
+def build_oracle_timer(force: bool = True) -> str:
+    """Compile bench_oracle.cpp and a copy of the oracle (pero.c, with the
+    oracle's own flags) into bench_oracle.so next to this file."""
+    if not force and os.path.exists(ORACLE_TIMER_LIB):
+        return ORACLE_TIMER_LIB
+    import subprocess
     import oracle
-    n, B = spec["capacity"], spec["batch"]
-    o = oracle.Oracle(n, 0)
+    objdir = os.path.join(ROOT, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    obj = os.path.join(objdir, "pero_timer.o")
+    cflags = [f for f in oracle.CFLAGS if f != "-shared"]
+    subprocess.check_call(["gcc", *cflags, "-c", os.path.join(ROOT, "oracle", "pero.c"), "-o", obj])
+    tmp = ORACLE_TIMER_LIB + ".tmp"
+    subprocess.check_call(["g++", "-O2", "-std=c++17", "-fPIC", "-shared", "-I", ROOT, "-o", tmp,
+                           ORACLE_TIMER_SRC, obj, "-lm"])
+    os.replace(tmp, ORACLE_TIMER_LIB)
+    return ORACLE_TIMER_LIB
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(spec: dict, seconds: float) -> dict:
+    """The oracle as it stands, one thread, on the workload's own steps: each
+    call timed in C with std::chrono::steady_clock (bench_oracle.cpp) until
+    `seconds` of CPU time are spent.  Workloads with rows gather them too."""
+    import ctypes
+    lib = ctypes.CDLL(build_oracle_timer(force=False))
+    vp, i64, i32, f64 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_double
+    lib.oracle_time_steps.restype = ctypes.c_int
+    lib.oracle_time_steps.argtypes = [i64, i32, f64, f64, vp, vp, vp, vp, vp, vp, i64, i64, vp, vp,
+                                      vp, i64, f64, i32, i32, i64, f64, vp]
+    n, B, D = spec["capacity"], spec["batch"], spec["state_dim"]
+    if D > 0:
+        raise ValueError("the CPU baseline runs the index-only workloads")
     pr = workloads.initial_priorities(spec["name"])
-    o.add(n, prio=pr)
     inp = workloads.StepInputs(spec["name"])
-    steps, t_total = 0, 0.0
-    while t_total < seconds and steps < 1_000_000:
-        u, td = inp.u(), inp.td()
-        t0 = time.perf_counter()
-        res = o.sample(u, weights=spec["weights"])
-        idx = inp.update_idx() if "unique" in spec else res["idx"]
-        o.update(idx, td)
-        if spec["intake"]:
-            o.add(spec["intake"])
-        t_total += time.perf_counter() - t0
-        steps += 1
-    per_step = t_total / steps
+    nsteps = 256  # inputs cycle after this many steps
+    u = np.ascontiguousarray(np.stack([inp.u() for _ in range(nsteps)]))
+    td = np.ascontiguousarray(np.stack([inp.td() for _ in range(nsteps)]))
+    idx = None
+    if "unique" in spec:
+        idx = np.ascontiguousarray(np.stack([inp.update_idx() for _ in range(nsteps)]))
+    out = (ctypes.c_double * 4)()
+    ptr = lambda a: None if a is None else a.ctypes.data
+    rc = lib.oracle_time_steps(n, 0, workloads.ALPHA, workloads.EPS, ptr(pr), None, None, None,
+                               None, None, B, nsteps, ptr(u), ptr(td), ptr(idx), spec["intake"],
+                               spec["beta"], 1 if spec["weights"] else 0, 0, 1_000_000, seconds,
+                               out)
+    if rc != 0:
+        raise RuntimeError("oracle timing failed")
+    ts, tu, ta, steps = out[0], out[1], out[2], int(out[3])
+    per_step = (ts + tu + ta) / steps
     return {"value": B / per_step, "unit": "samples/s", "cores": 1, "kind": "oracle",
-            "sample": "%d steps of %s (sample %d + update %d%s) on the single-threaded C "
-                      "oracle, %.1f s of CPU time; host has %d usable cores" % (
+            "sample": "%d steps of %s (sample %d + update %d%s) on the single-threaded C oracle, "
+                      "each call timed with std::chrono::steady_clock, %.1f s of CPU time; "
+                      "CPU %s, %d usable cores on the host" % (
                           steps, spec["name"], B, B,
                           (" + intake %d" % spec["intake"]) if spec["intake"] else "",
-                          t_total, len(os.sched_getaffinity(0))),
-            "ms_per_step": per_step * 1e3}
+                          ts + tu + ta, cpu_model(), len(os.sched_getaffinity(0))),
+            "ms_per_step": per_step * 1e3,
+            "op_ms": {"sample": ts / steps * 1e3, "update": tu / steps * 1e3,
+                      **({"add": ta / steps * 1e3} if spec["intake"] else {})},
+            "cpu_model": cpu_model()}
+
+
+# ------------------------------------------------------------ GPU runs
+
+class Run:
+    """One workload on the GPU: the buffer filled, every step's inputs
+    resident in HBM, and each step's calls marshalled for the C ABI ahead of
+    time, so that the timed loops do nothing on the host but call into the
+    library.  Rows are drawn on the device (torch's generator, seeded; the
+    workload's distributions): their values never change a step's work,
+    which only copies them."""
+
+    def __init__(self, name: str, steps_total: int, mode: dict, dev):
+        import torch
+        from sum_tree_sampling_amd import PerBuffer, per
+        self.torch = torch
+        self.lib = per.load()
+        spec = workloads.spec(name)
+        self.name = name
+        n, B, D = spec["capacity"], spec["batch"], spec["state_dim"]
+        self.n, self.B, self.D = n, B, D
+        W = mode.get("padded") or 0
+        if W:
+            spec = dict(spec, out_stride=W)
+        self.uniform, self.rank = mode.get("uniform", False), mode.get("rank", False)
+        self.masses = mode.get("masses", "array")
+        self.fused = bool(spec["intake"]) and not self.uniform and not mode.get("unfused", False)
+        self.spec = dict(spec, masses=self.masses, uniform=self.uniform, rank=self.rank,
+                         fused=self.fused)
+        self.W = W
+        self.dev = dev
+        self.g = g = PerBuffer(n, D, max_batch=B, device=dev)
+        pr = workloads.initial_priorities(name)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(spec["seed"])
+        chunk = 1 << 20
+        for lo in range(0, n, chunk):
+            c = min(chunk, n - lo)
+            p = None if pr is None else torch.from_numpy(pr[lo:lo + c]).to(dev)
+            if D > 0:
+                g.add(c, torch.randn((c, D), generator=gen, device=dev),
+                      torch.randn((c, D), generator=gen, device=dev),
+                      torch.randint(0, 3, (c,), generator=gen, device=dev, dtype=torch.int32),
+                      torch.randn(c, generator=gen, device=dev),
+                      (torch.rand(c, generator=gen, device=dev) < 0.01).to(torch.uint8), prio=p)
+            else:
+                g.add(c, prio=p)
+        torch.cuda.synchronize()
+        if self.rank:
+            g.rank_attach()
+        inp = workloads.StepInputs(name)
+        self.u = torch.from_numpy(np.stack([inp.u() for _ in range(steps_total)])).to(dev)
+        self.td = torch.from_numpy(np.stack([inp.td() for _ in range(steps_total)])).to(dev)
+        self.idx = None
+        if "unique" in spec:
+            self.idx = torch.from_numpy(np.stack([inp.update_idx() for _ in range(steps_total)])
+                                        ).to(dev)
+        self.steps_total = steps_total
+        out = {"idx": torch.empty(B, dtype=torch.int64, device=dev)}
+        if spec["weights"] and not self.uniform:
+            out["w"] = torch.empty(B, dtype=torch.float32, device=dev)
+        if D > 0:
+            Wo = W or D
+            out.update(states=torch.empty((B, Wo), dtype=torch.float32, device=dev),
+                       next_states=torch.empty((B, Wo), dtype=torch.float32, device=dev),
+                       actions=torch.empty(B, dtype=torch.int32, device=dev),
+                       rewards=torch.empty(B, dtype=torch.float32, device=dev),
+                       dones=torch.empty(B, dtype=torch.float32 if W else torch.uint8,
+                                         device=dev))
+        self.out = out
+        self.ops = (["sample", "update_add"] if self.fused else
+                    ["sample"] + ([] if self.uniform else ["update"]) +
+                    (["add"] if spec["intake"] else []))
+        self.torch.cuda.synchronize()
+
+    def calls(self, s: int, sp: int):
+        """[(op, [(c function, args), ...]), ...] of step s on stream sp."""
+        lib, h, B, spec = self.lib, self.g.h, self.B, self.spec
+        o = {k: v.data_ptr() for k, v in self.out.items()}
+        rows = [o.get("states"), o.get("next_states")]
+        scal = [o.get("actions"), o.get("rewards"), o.get("dones")]
+        u = self.u[s].data_ptr()
+        td = self.td[s].data_ptr()
+        beta, seed = spec["beta"], 0x5EED
+        if self.rank:
+            smp = [(lib.per_rank_refresh, (h, sp)),
+                   (lib.per_sample_rank, (h, B, u, beta, o["idx"], o.get("w"), *rows, *scal, sp))]
+        elif self.uniform:
+            smp = [(lib.per_sample_uniform, (h, B, seed, s * B, o["idx"], *rows, *scal, sp))]
+        elif self.masses == "philox":
+            smp = [(lib.per_sample_philox, (h, B, seed, s * B, beta, o["idx"], o.get("w"), *rows,
+                                            *scal, sp))]
+        elif self.W:
+            smp = [(lib.per_sample_padded, (h, B, u, beta, o["idx"], o.get("w"), *rows, self.W,
+                                            *scal, sp))]
+        else:
+            smp = [(lib.per_sample, (h, B, u, beta, o["idx"], o.get("w"), *rows, *scal, sp))]
+        res = [("sample", smp)]
+        ui = self.idx[s].data_ptr() if self.idx is not None else o["idx"]
+        c = spec["intake"]
+        if self.fused:
+            res.append(("update_add", [(lib.per_update_add, (h, B, ui, td, c, None, None, None,
+                                                             None, None, None, sp))]))
+        else:
+            if not self.uniform:
+                res.append(("update", [(lib.per_update, (h, B, ui, td, sp))]))
+            if c:
+                res.append(("add", [(lib.per_add, (h, c, None, None, None, None, None, None,
+                                                   sp))]))
+        return res
+
+    def check(self, rc: int):
+        if rc != 0:
+            from sum_tree_sampling_amd import per
+            raise RuntimeError("per call failed: %s" % per.per_last_error())
+
+    def run_steps(self, first: int, count: int, sp: int):
+        rc = 0
+        for s in range(first, first + count):
+            for _, cl in self.calls(s, sp):
+                for f, a in cl:
+                    rc |= f(*a)
+        self.check(rc)
+
+    def timed_steps(self, first: int, count: int, stream) -> float:
+        """ms per step over `count` whole steps between two events; the
+        calls are marshalled before the first event."""
+        torch = self.torch
+        sp = stream.cuda_stream
+        plan = [[(f, a) for _, cl in self.calls(s, sp) for f, a in cl]
+                for s in range(first, first + count)]
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        rc = 0
+        e0.record(stream)
+        for st in plan:
+            for f, a in st:
+                rc |= f(*a)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        self.check(rc)
+        return e0.elapsed_time(e1) / count
+
+    def kernel_times(self, first: int, count: int, stream) -> dict:
+        """Per op, the span of its kernels on the device in each of `count`
+        whole steps (per_time_next: the first kernel's start to the last
+        kernel's end, through hipExtLaunchKernel's events), in ms."""
+        torch = self.torch
+        lib = self.lib
+        sp = stream.cuda_stream
+        nops = len(self.ops)
+        evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range(nops)] for _ in range(count)]
+        for row in evs:  # torch creates an event when it is first recorded
+            for a, b in row:
+                a.record(stream)
+                b.record(stream)
+        torch.cuda.synchronize()
+        plan = []
+        for k, s in enumerate(range(first, first + count)):
+            st = []
+            for j, (op, cl) in enumerate(self.calls(s, sp)):
+                a, b = evs[k][j]
+                for i, (f, args) in enumerate(cl):
+                    start = a.cuda_event if i == 0 else None
+                    stop = b.cuda_event if i == len(cl) - 1 else None
+                    st.append((lib.per_time_next, (start, stop)))
+                    st.append((f, args))
+            plan.append(st)
+        rc = 0
+        for st in plan:
+            for f, a in st:
+                rc |= f(*a)
+        torch.cuda.synchronize()
+        self.check(rc)
+        return {op: np.array([evs[k][j][0].elapsed_time(evs[k][j][1]) for k in range(count)])
+                for j, op in enumerate(self.ops)}
+
+    def bracketed_times(self, first: int, count: int, stream) -> dict:
+        """Per op, an event pair recorded around its calls in each of
+        `count` whole steps (each pair also spans the dispatch gap in front
+        of the op's first kernel), in ms."""
+        torch = self.torch
+        sp = stream.cuda_stream
+        nops = len(self.ops)
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nops + 1)]
+               for _ in range(count)]
+        plan = [self.calls(s, sp) for s in range(first, first + count)]
+        rc = 0
+        for k, st in enumerate(plan):
+            evs[k][0].record(stream)
+            for j, (_, cl) in enumerate(st):
+                for f, a in cl:
+                    rc |= f(*a)
+                evs[k][j + 1].record(stream)
+        torch.cuda.synchronize()
+        self.check(rc)
+        return {op: np.array([evs[k][j].elapsed_time(evs[k][j + 1]) for k in range(count)])
+                for j, op in enumerate(self.ops)}
+
+    def graph_replay(self, first: int, K: int) -> dict:
+        """K whole steps captured as one HIP graph in the library's graph mode
+        and replayed: the step time without per-launch host work, a labelled
+        extra figure next to the eager headline.  In graph mode the intakes
+        take the ring cursor and size from the device, so every replay writes
+        the next slots as eager steps would; K is even, so each slot parity
+        (running max, overflow list, ring state) is flipped an even number of
+        times and a replay starts on the slots the capture started on.  The
+        rank-based step re-ranks from the host's filled size, which graph mode
+        refuses: it is captured in eager mode, valid while the ring is full
+        (its captured intakes rewrite the same slots on every replay)."""
+        torch = self.torch
+        g = self.g
+        use_graph_mode = not self.rank
+        entered = False
+        try:
+            gr = torch.cuda.CUDAGraph()
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                self.run_steps(first, 1, side.cuda_stream)  # warm the capture stream
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            if use_graph_mode:
+                g.graph_mode(True)
+                entered = True
+            with torch.cuda.graph(gr):
+                self.run_steps(first, K, torch.cuda.current_stream().cuda_stream)
+            torch.cuda.synchronize()
+            for _ in range(3):
+                gr.replay()
+            torch.cuda.synchronize()
+            reps = 20
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(torch.cuda.current_stream())
+            for _ in range(reps):
+                gr.replay()
+            b.record(torch.cuda.current_stream())
+            torch.cuda.synchronize()
+            if entered:
+                entered = False
+                g.graph_mode(False)
+            mode = "graph mode, device ring state" if use_graph_mode else "eager mode, full ring"
+            return {"steps_per_graph": K, "replays": reps, "mode": mode,
+                    "ms_per_step": a.elapsed_time(b) / (reps * K)}
+        except Exception as e:  # capture not available: report instead of failing the line
+            if entered:
+                try:
+                    g.graph_mode(False)
+                except Exception:
+                    pass
+            return {"error": "%s: %s" % (type(e).__name__, e)}
+
+    def close(self):
+        self.g.close()
+        self.g = None
+        self.u = self.td = self.idx = self.out = None
+
+
+def progress(*a) -> None:
+    print("bench:", *a, file=sys.stderr, flush=True)
+
+
+def pct(t: np.ndarray) -> dict:
+    return {q: float(np.percentile(t, v)) for q, v in (("p10", 10), ("p50", 50), ("p90", 90))}
+
+
+def measure(run: Run, K: int, W: int, Kop: int, stream, graph_steps: int = 0) -> dict:
+    """The headline pass and the per-op passes of one workload."""
+    run.run_steps(0, W, stream.cuda_stream)
+    run.torch.cuda.synchronize()
+    ms_per_step = run.timed_steps(W, K, stream)
+    base = W + K
+    kt = run.kernel_times(base, Kop, stream)
+    br = run.bracketed_times(base, min(K, Kop), stream)
+    op_avg = {op: float(t.mean()) for op, t in kt.items()}
+    byts = algorithmic_bytes(run.spec)
+    dom = max(op_avg, key=op_avg.get)
+    achieved = byts[dom] / (op_avg[dom] * 1e-3) / 1e9
+    step_bytes = sum(byts.values())
+    B = run.B
+    upd = "update_add" if run.fused else ("update" if "update" in op_avg else None)
+    res = {
+        "ms_per_step": ms_per_step,
+        "samples_per_s": B / (op_avg["sample"] * 1e-3),
+        "updates_per_s": None if upd is None else B / (op_avg[upd] * 1e-3),
+        "op_ms_avg": op_avg,
+        "op_ms_kernel": {op: pct(t) for op, t in kt.items()},
+        "op_ms_bracketed": {op: pct(t) for op, t in br.items()},
+        "op_steps": Kop,
+        "step_algorithmic_bytes": step_bytes,
+        "step_hbm_roofline_frac": step_bytes / (ms_per_step * 1e-3) / (PEAK_HBM_GBS * 1e9),
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
+                     "traffic": measured_traffic(run.name, dom),
+                     "bytes_per_launch": byts[dom]},
+    }
+    if graph_steps > 0:
+        res["graph_replay"] = run.graph_replay(base, graph_steps)
+    return res
+
+
+def config_of(run: Run, args_masses: str = "array") -> dict:
+    spec = run.spec
+    return {"workload": run.name, "capacity": run.n, "batch": run.B, "state_dim": run.D,
+            "intake": spec["intake"], "unique_updates": spec.get("unique", run.B),
+            "weights": spec["weights"], "parallelism": "single GPU",
+            "out_stride": run.W or run.D, "masses": run.masses,
+            "update_and_intake": "one launch" if run.fused else "separate calls",
+            "sampling": "uniform" if run.uniform else ("rank" if run.rank else "proportional")}
 
 
 def main():
@@ -332,8 +649,12 @@ def main():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="apex_shard_2m", choices=list(workloads.WORKLOADS))
+    ap.add_argument("--op-steps", type=int, default=200,
+                    help="steps of the per-operation kernel-timing pass (at least --steps)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="measure only --workload, not the other workloads as well")
     ap.add_argument("--padded", type=int, default=0, metavar="STRIDE",
                     help="sample with per_sample_padded into rows of STRIDE floats "
                          "(the trainer layout; workloads with rows only)")
@@ -370,236 +691,79 @@ def main():
         sys.exit(2)
 
     import torch
-    from sum_tree_sampling_amd import PerBuffer
 
     spec = workloads.spec(args.workload)
-    n, B, D = spec["capacity"], spec["batch"], spec["state_dim"]
+    D = spec["state_dim"]
     if args.padded:
         if D == 0 or args.padded < D:
             raise SystemExit("--padded needs a workload with rows and STRIDE >= state_dim")
         if args.uniform or args.masses != "array" or args.rank:
             raise SystemExit("--padded goes with array masses and proportional sampling")
-        spec = dict(spec, out_stride=args.padded)
     if args.rank and (args.uniform or args.masses != "array"):
         raise SystemExit("--rank goes with array masses")
-    # The update and the intake of a step in one launch (per_update_add)
-    # unless asked for separately; without an update there is nothing to fuse.
-    fused = bool(spec["intake"]) and not args.uniform and not args.unfused
-    spec = dict(spec, masses=args.masses, uniform=args.uniform, rank=args.rank, fused=fused)
+    mode = dict(padded=args.padded, masses=args.masses, uniform=args.uniform, rank=args.rank,
+                unfused=args.unfused)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
 
-    g = PerBuffer(n, D, max_batch=B, device=dev)
-    pr = workloads.initial_priorities(args.workload)
-    chunk = 1 << 20
-    for lo in range(0, n, chunk):
-        c = min(chunk, n - lo)
-        p = None if pr is None else torch.from_numpy(pr[lo:lo + c]).to(dev)
-        if D > 0:
-            r = workloads.rows(args.workload, lo, c)
-            g.add(c, torch.from_numpy(r["states"]).to(dev),
-                  torch.from_numpy(r["next_states"]).to(dev),
-                  torch.from_numpy(r["actions"].view(np.int32)).to(dev),
-                  torch.from_numpy(r["rewards"]).to(dev), torch.from_numpy(r["dones"]).to(dev),
-                  prio=p)
-        else:
-            g.add(c, prio=p)
-    torch.cuda.synchronize()
-
-    total = args.warmup + 2 * args.steps
-    inp = workloads.StepInputs(args.workload)
-    u_all = np.stack([inp.u() for _ in range(total)])
-    td_all = np.stack([inp.td() for _ in range(total)])
-    # One view per step, made before timing: indexing a tensor inside the
-    # loop costs microseconds of host time per call, which the short steps
-    # would otherwise wait on.
-    u_d = list(torch.from_numpy(u_all).to(dev).unbind(0))
-    td_d = list(torch.from_numpy(td_all).to(dev).unbind(0))
-    idx_d = None
-    if "unique" in spec:
-        idx_d = list(torch.from_numpy(np.stack([inp.update_idx() for _ in range(total)]))
-                     .to(dev).unbind(0))
-    rows = D > 0
-    out = {"idx": torch.empty(B, dtype=torch.int64, device=dev)}
-    if spec["weights"]:
-        out["w"] = torch.empty(B, dtype=torch.float32, device=dev)
-    W = spec.get("out_stride")
-    if W:
-        out.update(states=torch.empty((B, W), dtype=torch.float32, device=dev),
-                   next_states=torch.empty((B, W), dtype=torch.float32, device=dev),
-                   actions=torch.empty(B, dtype=torch.int32, device=dev),
-                   rewards=torch.empty(B, dtype=torch.float32, device=dev),
-                   dones=torch.empty(B, dtype=torch.float32, device=dev))
-    elif rows:
-        out.update(states=torch.empty((B, D), dtype=torch.float32, device=dev),
-                   next_states=torch.empty((B, D), dtype=torch.float32, device=dev),
-                   actions=torch.empty(B, dtype=torch.int32, device=dev),
-                   rewards=torch.empty(B, dtype=torch.float32, device=dev),
-                   dones=torch.empty(B, dtype=torch.uint8, device=dev))
-    intake = spec["intake"]
-
-    seed = 0x5EED
-    if args.uniform:
-        out.pop("w", None)
-
-    if args.rank:
-        g.rank_attach()
-
-    def do_sample(s, o):
-        if args.rank:
-            g.rank_refresh()
-            g.sample_rank(u_d[s], beta=spec["beta"], out=o)
-        elif args.uniform:
-            g.sample_uniform(B, seed, s * B, out=o)
-        elif args.masses == "philox":
-            g.sample_philox(B, seed, s * B, beta=spec["beta"], out=o)
-        elif W:
-            g.sample_padded(u_d[s], W, beta=spec["beta"], out=o)
-        else:
-            g.sample(u_d[s], beta=spec["beta"], weights=spec["weights"], out=o)
-
-    def do_update(s, idx):
-        if not args.uniform:
-            g.update(idx, td_d[s])
-
-    def step(s):
-        do_sample(s, out)
-        idx = idx_d[s] if idx_d is not None else out["idx"]
-        if fused:
-            g.update_add(idx, td_d[s], intake)
-        else:
-            do_update(s, idx)
-            if intake:
-                g.add(intake)
-
-    for s in range(args.warmup):
-        step(s)
-    torch.cuda.synchronize()
-
-    # Pass 1: the headline, K whole steps between two events.
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    base = args.warmup
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for s in range(args.steps):
-        step(base + s)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    host_ms = (time.perf_counter() - t0) * 1e3
-    ms_per_step = e0.elapsed_time(e1) / args.steps
-
-    # Pass 2: each operation on its own, K back-to-back launches between two
-    # events (an event pair around every launch would add its own dispatch
-    # gap to each one).  The sampled indices of this pass feed its updates.
-    base = args.warmup + args.steps
-    idx_hist = torch.empty((args.steps, B), dtype=torch.int64, device=dev)
-    ops = {
-        "sample": lambda s: do_sample(base + s, dict(out, idx=idx_hist[s])),
-    }
-    def hist_idx(s):
-        return idx_d[base + s] if idx_d is not None else idx_hist[s]
-
-    if fused:
-        ops["update_add"] = lambda s: g.update_add(hist_idx(s), td_d[base + s], intake)
-    else:
-        if not args.uniform:
-            ops["update"] = lambda s: g.update(hist_idx(s), td_d[base + s])
-        if intake:
-            ops["add"] = lambda s: g.add(intake)
-    op_avg = {}
-    for name, fn in ops.items():
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for s in range(args.steps):
-            fn(s)
-        b.record(stream)
-        torch.cuda.synchronize()
-        op_avg[name] = a.elapsed_time(b) / args.steps
-
-    # Pass 3: whole steps again, an event pair around every operation, for the
-    # spread of each (every pair also spans the dispatch gap in front of its
-    # kernel, so these run above the back-to-back averages).
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    for s in range(args.steps):
-        e = evs[s]
-        e[0].record(stream)
-        do_sample(base + s, out)
-        e[1].record(stream)
-        idx = idx_d[base + s] if idx_d is not None else out["idx"]
-        if fused:
-            g.update_add(idx, td_d[base + s], intake)
-        else:
-            do_update(base + s, idx)
-        e[2].record(stream)
-        if intake and not fused:
-            g.add(intake)
-        e[3].record(stream)
-    torch.cuda.synchronize()
-    spread = {}
-    names = ["sample", "update_add"] if fused else ["sample", "update", "add"]
-    for k, name in enumerate(names):
-        if (name == "add" and not intake) or (name == "update" and args.uniform):
-            continue
-        t = np.array([e[k].elapsed_time(e[k + 1]) for e in evs])
-        spread[name] = {q: float(np.percentile(t, v)) for q, v in (("p10", 10), ("p50", 50), ("p90", 90))}
-
-    graph = None
-    kg = min(args.graph_steps, args.steps)  # inputs exist for K steps past base
+    K, W = args.steps, args.warmup
+    Kop = max(K, args.op_steps)
+    kg = min(args.graph_steps, Kop)
     kg -= kg % 2
-    if kg > 0:
-        graph = graph_replay(g, step, kg, base, stream, use_graph_mode=not args.rank)
-
+    progress("filling", args.workload)
+    run = Run(args.workload, W + K + Kop, mode, dev)
+    progress("timing", args.workload)
+    m = measure(run, K, W, Kop, stream, graph_steps=kg)
     floor = None
     if not args.no_latency_floor:
         floor = latency_floor()
-        floor["kernels_per_step"] = len(op_avg)
-        floor["launch_floor_us_per_step"] = floor["empty_kernel_us"] * len(op_avg)
-
-    byts = algorithmic_bytes(spec)
-    dom = max(op_avg, key=op_avg.get)
-    achieved = byts[dom] / (op_avg[dom] * 1e-3) / 1e9
-    step_bytes = sum(byts.values())
-
+        floor["kernels_per_step"] = len(run.ops)
+        floor["launch_floor_us_per_step"] = floor["empty_kernel_us"] * len(run.ops)
     res = {
         "metric": METRIC,
-        "value": B / (ms_per_step * 1e-3),
+        "value": run.B / (m["ms_per_step"] * 1e-3),
         "unit": "samples/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": m["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": args.workload, "capacity": n, "batch": B, "state_dim": D,
-                   "intake": intake, "unique_updates": spec.get("unique", B),
-                   "weights": spec["weights"], "parallelism": "single GPU",
-                   "out_stride": W or D, "masses": args.masses,
-                   "update_and_intake": "one launch" if fused else "separate calls",
-                   "sampling": ("uniform" if args.uniform else
-                                ("rank" if args.rank else "proportional"))},
-        "samples_per_s": B / (op_avg["sample"] * 1e-3),
-        "updates_per_s": (B / (op_avg["update"] * 1e-3) if "update" in op_avg else
-                          (B / (op_avg["update_add"] * 1e-3) if fused else None)),
-        "op_ms_avg": op_avg,
-        "op_ms_bracketed": spread,
-        "graph_replay": graph,
+        "config": config_of(run),
+        **{k: v for k, v in m.items() if k != "ms_per_step"},
         "latency_floor": floor,
-        "host_ms_per_step": host_ms / args.steps,
-        "step_algorithmic_bytes": step_bytes,
-        "step_hbm_roofline_frac": step_bytes / (ms_per_step * 1e-3) / (PEAK_HBM_GBS * 1e9),
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
-                     "traffic": measured_traffic(args.workload, dom),
-                     "bytes_per_launch": byts[dom]},
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(spec, args.cpu_seconds)
+    spec_run = run.spec
+    run.close()
+    del run
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline and spec_run["state_dim"] == 0:
+        progress("cpu baseline")
+        res["cpu_baseline"] = cpu_baseline(spec_run, args.cpu_seconds)
+    if not args.no_configs:
+        # The other workloads, each with the same number of timed steps (at
+        # most 200) and the default sampling mode: parity-test shapes, shown
+        # as sub-results next to the headline.
+        subs = {}
+        Ks, Ws = min(K, 200), min(W, 20)
+        Kops = max(Ks, min(Kop, 200))
+        for name in workloads.WORKLOADS:
+            if name == args.workload:
+                continue
+            progress("filling", name)
+            r = Run(name, Ws + Ks + Kops, {}, dev)
+            progress("timing", name)
+            sm = measure(r, Ks, Ws, Kops, stream)
+            subs[name] = {"config": config_of(r), "steps": Ks, "warmup": Ws, **sm}
+            r.close()
+            del r
+            torch.cuda.empty_cache()
+        res["configs"] = subs
     print(json.dumps(res), flush=True)
 
 

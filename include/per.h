@@ -255,13 +255,41 @@ int per_sample_padded(per_t* h, int64_t B, const float* d_u, double beta, int64_
                       float* d_dones_out, hipStream_t stream);
 
 /*
- * The nodes above the update partitions (the top levels of both trees) are
- * rebuilt lazily: per_add and per_update leave them stale, and per_sample
- * rebuilds them in on-chip memory for its own descent without storing them
- * (on trees too deep for that it stores them first).  per_flush enqueues
- * the rebuild of the stored top now if it is pending (one small kernel; a
- * no-op otherwise), so that the arrays of per_tree_ptrs hold every node.
- * per_total and per_min call it themselves.
+ * Lanes that carry one sample through the descent: 64 (one wave per
+ * sample), 16 (four samples per wave) or 1 (one lane per sample); 0, the
+ * default, lets the library choose by batch size and row width.  Every
+ * layout computes the same indices, weights and rows ("Putting prioritized
+ * replay's segment tree on a GPU", section "Sampling Is a Descent": each
+ * descent is independent of the others); the choice only changes how the
+ * batch spreads over the chip.  Applies to the handle's later sampling
+ * calls.  PER_EINVAL for any other value.
+ */
+int per_set_sample_lanes(per_t* h, int32_t lanes);
+
+/*
+ * Device-side timing of one call ("Putting prioritized replay's segment
+ * tree on a GPU", section "Measuring the Trade Honestly": each operation
+ * timed on its own).  The next entry point called on this host thread that
+ * enqueues kernels records `start` (if not NULL) as its first kernel begins
+ * and `stop` (if not NULL) as its last kernel ends, through
+ * hipExtLaunchKernel; hipEventElapsedTime(start, stop) then gives the span
+ * of the call's kernels on the device without the dispatch gap before the
+ * first one.  The request is dropped when that call returns, whatever it
+ * returns.  The events must be created by the caller; do not request timing
+ * for a call issued into a stream under graph capture.  Returns PER_OK.
+ */
+int per_time_next(hipEvent_t start, hipEvent_t stop);
+
+/*
+ * The nodes above the update partitions (the top levels of both trees,
+ * "Putting prioritized replay's segment tree on a GPU", section "The Tree
+ * Under Every Prioritized Replay": every internal node is the sum -- or
+ * min -- of its two children) are rebuilt lazily: per_add and per_update
+ * leave them stale, and per_sample rebuilds them in on-chip memory for its
+ * own descent without storing them (on trees too deep for that it stores
+ * them first).  per_flush enqueues the rebuild of the stored top now if it
+ * is pending (one small kernel; a no-op otherwise), so that the arrays of
+ * per_tree_ptrs hold every node.  per_total and per_min call it themselves.
  */
 int per_flush(per_t* h, hipStream_t stream);
 
@@ -269,6 +297,13 @@ int per_flush(per_t* h, hipStream_t stream);
  * Enqueue a 4-byte device copy of the sum-tree root (total priority), the
  * min-tree root (min priority over written slots; +inf when empty) or the
  * running max priority into d_out.  The caller synchronises to read it.
+ * The two roots are node 1 of the flat trees ("Putting prioritized replay's
+ * segment tree on a GPU", section "The Tree Under Every Prioritized Replay":
+ * the root holds the total that masses are drawn from, and the twin min
+ * tree gives the smallest priority for the importance-weight
+ * normalisation); the running max priority is what new transitions enter
+ * with ("GPU-Resident Prioritized Experience Replay", section "Experience
+ * Insertion").  per_total and per_min flush the top levels first.
  */
 int per_total(per_t* h, float* d_out, hipStream_t stream);
 int per_min(per_t* h, float* d_out, hipStream_t stream);

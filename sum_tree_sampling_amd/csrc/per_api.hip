@@ -26,6 +26,7 @@ struct per_s {
   int ring;        // control-block slot holding the current ring state
   bool top_stale;  // nodes above the partitions not yet rebuilt
   bool graph;      // graph mode: ring state read on the device, top always rebuilt
+  int sample_mode;  // descent layout forced by per_set_sample_lanes (0: by batch)
   int entry_epoch, entry_ovf, entry_ring;  // parities when graph mode was entered
   int device;
   // rank-based prioritisation (after per_rank_attach)
@@ -41,7 +42,10 @@ struct per_s {
 namespace {
 
 thread_local std::string g_last_error;
+thread_local per::KernelTiming g_timing;
 
+// Every entry point returns through fail() or ok(), which also drop a
+// pending timing request: per_time_next applies to one call only.
 int fail(int code, const char* fmt, ...) {
   char buf[512];
   va_list ap;
@@ -49,11 +53,13 @@ int fail(int code, const char* fmt, ...) {
   vsnprintf(buf, sizeof buf, fmt, ap);
   va_end(ap);
   g_last_error = buf;
+  g_timing = per::KernelTiming{};
   return code;
 }
 
 int ok() {
   g_last_error.clear();
+  g_timing = per::KernelTiming{};
   return PER_OK;
 }
 
@@ -103,6 +109,8 @@ per::Geom make_geom(int64_t capacity) {
 }  // namespace
 
 namespace per {
+
+KernelTiming& kernel_timing() { return g_timing; }
 
 Layout workspace_layout(int64_t n, int64_t max_batch) {
   const Geom g = make_geom(n);
@@ -204,6 +212,7 @@ int per_create(per_t** out, int64_t capacity, int32_t state_dim, int64_t max_bat
   h->ring = 0;
   h->top_stale = false;
   h->graph = false;
+  h->sample_mode = 0;
   h->rank_attached = false;
   h->rank_size = 0;
   h->rank_built = -1;
@@ -356,7 +365,7 @@ int sample_impl(per_t* h, int64_t B, SampleKind kind, const float* d_u, uint64_t
   if (kind == kRank) {
     if (h->rank_size == 0) return fail(PER_EEMPTY, "rank sample before per_rank_refresh");
     const per::SamplePlan plan =
-        per::make_sample_plan(h->g, B, any_rows ? (uint32_t)h->st.D : 0u);
+        per::make_sample_plan(h->g, B, any_rows ? (uint32_t)h->st.D : 0u, h->sample_mode);
     hipError_t e = per::launch_sample(h->rt, h->g, h->st, plan, (uint32_t)h->rank_size, B, d_u,
                                       0, 0, beta, d_idx_out, d_w_out,
                                       any_rows ? d_states_out : nullptr, d_next_states_out,
@@ -374,7 +383,7 @@ int sample_impl(per_t* h, int64_t B, SampleKind kind, const float* d_u, uint64_t
     return e == hipSuccess ? ok() : hip_fail(e, what);
   }
   const per::SamplePlan plan =
-      per::make_sample_plan(h->g, B, any_rows ? (uint32_t)h->st.D : 0u);
+      per::make_sample_plan(h->g, B, any_rows ? (uint32_t)h->st.D : 0u, h->sample_mode);
   const bool stale = top_may_be_stale(h);
   if (stale && plan.top_mode != per::kTopRebuild) {  // the sampler will not rebuild the top itself
     hipError_t e = per::launch_top(h->t, h->g, stream);
@@ -493,6 +502,27 @@ int per_graph_mode(per_t* h, int32_t on, hipStream_t stream) {
                 "(running max %d, overflow %d, ring %d): replaying them reads stale slots",
                 h->epoch ^ h->entry_epoch, h->ovf ^ h->entry_ovf, h->ring ^ h->entry_ring);
   return ok();
+}
+
+int per_set_sample_lanes(per_t* h, int32_t lanes) {
+  if (!h) return fail(PER_EINVAL, "handle is NULL");
+  int mode;
+  switch (lanes) {
+    case 0: mode = 0; break;
+    case 64: mode = 1; break;
+    case 16: mode = 2; break;
+    case 1: mode = 3; break;
+    default: return fail(PER_EINVAL, "lanes per sample must be 0, 1, 16 or 64 (got %d)", lanes);
+  }
+  h->sample_mode = mode;
+  return ok();
+}
+
+int per_time_next(hipEvent_t start, hipEvent_t stop) {
+  g_last_error.clear();
+  g_timing.start = start;
+  g_timing.stop = stop;
+  return PER_OK;
 }
 
 int64_t per_size(const per_t* h) { return h ? h->size : -1; }

@@ -2,10 +2,36 @@
 // installed; the public ABI is include/per.h).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace per {
+
+// Kernel-timing request of the calling host thread (per_time_next): while
+// set, launches go through hipExtLaunchKernel, the first one recording
+// `start` as it begins and each one recording `stop` as it ends, so that the
+// two events bracket the call's kernels on the device.
+struct KernelTiming {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+KernelTiming& kernel_timing();
+
+// Every kernel of the library is launched through here.
+template <typename... KArgs, typename... Args>
+hipError_t launch_kernel(void (*kern)(KArgs...), dim3 grid, dim3 block, size_t lds, hipStream_t s,
+                         Args... args) {
+  KernelTiming& t = kernel_timing();
+  if (t.start || t.stop) {
+    hipExtLaunchKernelGGL(kern, grid, block, (uint32_t)lds, s, t.start, t.stop, 0u,
+                          static_cast<KArgs>(args)...);
+    t.start = nullptr;  // only the call's first kernel opens the interval
+  } else {
+    kern<<<grid, block, lds, s>>>(static_cast<KArgs>(args)...);
+  }
+  return hipGetLastError();
+}
 
 // Leaves per partition = 2^kMaxSpanBits.  The batched update and the intake
 // work one workgroup per partition (an aligned subtree); the few levels above
@@ -141,7 +167,9 @@ hipError_t launch_sample(const TreePtrs& t, const Geom& g, const Storage& st,
                          void* dones_out, uint32_t out_stride, bool dones_f32,
                          hipStream_t s, const uint32_t* order = nullptr);
 
-SamplePlan make_sample_plan(const Geom& g, int64_t B, uint32_t row_floats);
+// forced_mode: 0 chooses the layout by batch and row width; 1, 2, 3 force
+// one wave, 16 lanes or one lane per sample.
+SamplePlan make_sample_plan(const Geom& g, int64_t B, uint32_t row_floats, int forced_mode);
 
 // Rank-based prioritisation: a stable radix sort of the slots [0, count) by
 // descending leaf priority (keys / vals: two ping-pong buffers of n words,

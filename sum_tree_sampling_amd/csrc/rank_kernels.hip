@@ -309,33 +309,36 @@ hipError_t launch_rank_sort(const float* leaves, uint32_t count, uint32_t* const
     const uint32_t* vin = vals[p & 1];
     uint32_t* kout = keys[(p + 1) & 1];
     uint32_t* vout = vals[(p + 1) & 1];
+    hipError_t e;
     if (p == 0)
-      hipLaunchKernelGGL((rank_hist_kernel<true, false>), dim3(ntiles), dim3(kRankThreads), 0, s,
-                         nullptr, leaves, count, shift, ntiles, hist);
+      e = launch_kernel(rank_hist_kernel<true, false>, dim3(ntiles), dim3(kRankThreads), 0, s,
+                        nullptr, leaves, count, shift, ntiles, hist);
     else if (p < kPasses - 1)
-      hipLaunchKernelGGL((rank_hist_kernel<false, false>), dim3(ntiles), dim3(kRankThreads), 0, s,
-                         kin, nullptr, count, shift, ntiles, hist);
+      e = launch_kernel(rank_hist_kernel<false, false>, dim3(ntiles), dim3(kRankThreads), 0, s,
+                        kin, nullptr, count, shift, ntiles, hist);
     else
-      hipLaunchKernelGGL((rank_hist_kernel<false, true>), dim3(ntiles), dim3(kRankThreads), 0, s,
-                         kin, nullptr, count, shift, ntiles, hist);
-    hipLaunchKernelGGL(rank_rowscan_kernel, dim3(kDigits), dim3(kRankThreads), 0, s, hist, ntiles,
-                       tot);
+      e = launch_kernel(rank_hist_kernel<false, true>, dim3(ntiles), dim3(kRankThreads), 0, s,
+                        kin, nullptr, count, shift, ntiles, hist);
+    if (e != hipSuccess) return e;
+    e = launch_kernel(rank_rowscan_kernel, dim3(kDigits), dim3(kRankThreads), 0, s, hist, ntiles,
+                      tot);
+    if (e != hipSuccess) return e;
     if (p == 0)
-      hipLaunchKernelGGL(rank_scatter_kernel<true>, dim3(ntiles), dim3(kRankThreads), 0, s,
-                         nullptr, nullptr, leaves, count, shift, ntiles, hist, tot, kout, vout);
+      e = launch_kernel(rank_scatter_kernel<true>, dim3(ntiles), dim3(kRankThreads), 0, s,
+                        nullptr, nullptr, leaves, count, shift, ntiles, hist, tot, kout, vout);
     else
-      hipLaunchKernelGGL(rank_scatter_kernel<false>, dim3(ntiles), dim3(kRankThreads), 0, s, kin,
-                         vin, nullptr, count, shift, ntiles, hist, tot, kout, vout);
+      e = launch_kernel(rank_scatter_kernel<false>, dim3(ntiles), dim3(kRankThreads), 0, s, kin,
+                        vin, nullptr, count, shift, ntiles, hist, tot, kout, vout);
+    if (e != hipSuccess) return e;
   }
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 hipError_t launch_rank_build(const TreePtrs& rt, const Geom& g, uint32_t count, double alpha,
                              hipStream_t s) {
   const size_t lds = sizeof(float) * 4 * (size_t(1) << g.S);
-  hipLaunchKernelGGL(rank_build_kernel, dim3(1u << g.P), dim3(kRankThreads), lds, s, rt, g, count,
-                     alpha);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch_kernel(rank_build_kernel, dim3(1u << g.P), dim3(kRankThreads), lds, s, rt,
+                               g, count, alpha);
   if (e != hipSuccess || g.P == 0) return e;
   return launch_top(rt, g, s);
 }

@@ -11,9 +11,10 @@
 // G = 1: one lane per sample; G = 64: one wave per sample) carries one
 // sample.  The top of the tree is walked in LDS: each block first rebuilds the
 // 2^P - 1 nodes above the update partitions from the 2^P partition roots (one
-// coalesced load), which also gives it the total and the min priority; block
-// 0 writes those nodes back when the writers left them stale.  (Trees of at
-// most 2^10 leaves are staged whole.)  The remaining levels are covered in
+// coalesced load), which also gives it the total and the min priority.  The
+// rebuilt nodes stay in LDS: the stored ones are refreshed only by
+// top_kernel (per_flush, or before a sampler that reads them from memory).
+// (Trees of at most 2^10 leaves are staged whole.)  The remaining levels are covered in
 // rounds: a round of R levels below node c loads the 2^R contiguous
 // descendants of c at depth +R (G lanes x V values, 16-byte vector loads),
 // rebuilds the R-1 intermediate levels by pairwise adds -- bit-identical to
@@ -27,7 +28,6 @@
 // access, straight into the caller's buffers ("True Single-Graph
 // Implementation Plan", Task 3).
 
-#include <cstdlib>
 #include <type_traits>
 
 #include "lanes.h"
@@ -568,9 +568,8 @@ __global__ void __launch_bounds__(kSampleThreads) uniform_kernel(SampleArgs a) {
 
 template <int G, int V, bool STREAM, int FR, int FN, int TP>
 hipError_t launch_one(const SampleArgs& a, unsigned grid, size_t lds, hipStream_t s) {
-  hipLaunchKernelGGL((sample_kernel<G, V, STREAM, FR, FN, TP>), dim3(grid), dim3(kSampleThreads),
-                     lds, s, a);
-  return hipGetLastError();
+  return launch_kernel(sample_kernel<G, V, STREAM, FR, FN, TP>, dim3(grid), dim3(kSampleThreads),
+                       lds, s, a);
 }
 
 // The usual round shape (FR, FN) with the top depth of trees of 2^20 to
@@ -631,12 +630,11 @@ void split_rounds(int levels, int hi, SamplePlan& p) {
 // slots of 64 floats, B = 1024: 0.65 us less per step; without rows, 2^21
 // slots and B = 512: 0.1 us less).  With very few samples, or thousands
 // without rows, the extra blocks and top rebuilds cost more than they give.
-SamplePlan make_sample_plan(const Geom& g, int64_t B, uint32_t row_floats) {
+SamplePlan make_sample_plan(const Geom& g, int64_t B, uint32_t row_floats, int forced_mode) {
   SamplePlan p{};
   p.mode = (B <= 16384) ? 2 : 3;
   if (B >= 256 && B <= (row_floats >= 32 ? 2048 : 1024)) p.mode = 1;
-  const char* env = getenv("PER_SAMPLE_MODE");
-  if (env && atoi(env) >= 1 && atoi(env) <= 3) p.mode = atoi(env);
+  if (forced_mode >= 1 && forced_mode <= 3) p.mode = forced_mode;
   if (g.P > 0 && g.P <= kMaxTopBits) {
     p.top_mode = kTopRebuild;
     p.top_levels = g.P;
@@ -720,14 +718,12 @@ hipError_t launch_uniform(const Storage& st, const Ctrl* ctrl, RingRef ring, uin
   a.st = st;
   if (B <= 16384) {
     const uint64_t waves = ((uint64_t)B + 3) / 4;
-    hipLaunchKernelGGL(uniform_kernel<16>, dim3((unsigned)((waves + 3) / 4)),
-                       dim3(kSampleThreads), 0, s, a);
-  } else {
-    const uint64_t waves = ((uint64_t)B + 63) / 64;
-    hipLaunchKernelGGL(uniform_kernel<1>, dim3((unsigned)((waves + 3) / 4)),
-                       dim3(kSampleThreads), 0, s, a);
+    return launch_kernel(uniform_kernel<16>, dim3((unsigned)((waves + 3) / 4)),
+                         dim3(kSampleThreads), 0, s, a);
   }
-  return hipGetLastError();
+  const uint64_t waves = ((uint64_t)B + 63) / 64;
+  return launch_kernel(uniform_kernel<1>, dim3((unsigned)((waves + 3) / 4)), dim3(kSampleThreads),
+                       0, s, a);
 }
 
 }  // namespace per

@@ -23,9 +23,9 @@
 //     run is rebuilt from its range and the two boundary paths.
 //  3. The 2^P - 1 nodes above the partitions are not touched by the writers.
 //     They are a pure function of the partition roots, and the sampler
-//     rebuilds them in LDS anyway to walk the top of the tree; its first
-//     block writes them back.  top_kernel rebuilds them for readers of the
-//     stored tree (total, min, inspection).
+//     rebuilds them in LDS anyway to walk the top of the tree, without
+//     storing them.  top_kernel rebuilds the stored ones for readers of the
+//     stored tree (total, min, inspection, a sampler without an LDS top).
 // Every node is recomputed from its two children, never updated by adding a
 // delta, and no level is read before the level below it is complete (the
 // dependency rule of section "The Race Condition Worth Writing Down").
@@ -1361,13 +1361,11 @@ inline unsigned grid_for(uint64_t work, unsigned per_block, unsigned cap) {
 
 hipError_t launch_init(const TreePtrs& t, const Buckets& bk, const Geom& g, hipStream_t s) {
   const unsigned grid = grid_for(2ull * g.n, kTreeThreads * 8, 4096);
-  hipLaunchKernelGGL(init_kernel, dim3(grid), dim3(kTreeThreads), 0, s, t, bk, g);
-  return hipGetLastError();
+  return launch_kernel(init_kernel, dim3(grid), dim3(kTreeThreads), 0, s, t, bk, g);
 }
 
 hipError_t launch_top(const TreePtrs& t, const Geom& g, hipStream_t s) {
-  hipLaunchKernelGGL(top_kernel, dim3(1), dim3(kTreeThreads), 0, s, t, g);
-  return hipGetLastError();
+  return launch_kernel(top_kernel, dim3(1), dim3(kTreeThreads), 0, s, t, g);
 }
 
 bool update_uses_buckets(const Geom& g, int64_t B) {
@@ -1397,19 +1395,14 @@ hipError_t launch_update(const TreePtrs& t, const Buckets& bk, const Geom& g, Ri
   if (!update_uses_buckets(g, B)) {
     // One partition per block: the batch scan is spread over the most blocks.
     const int ch = scan_chunk(B);
+    const dim3 grid((unsigned)np), block(kUpdThreads);
     if (g.S == kMaxSpanBits && ch == 2)
-      hipLaunchKernelGGL((update_scan_kernel<1, true, 2>), dim3((unsigned)np), dim3(kUpdThreads),
-                         0, s, t, g, a);
-    else if (g.S == kMaxSpanBits && ch == 4)
-      hipLaunchKernelGGL((update_scan_kernel<1, true, 4>), dim3((unsigned)np), dim3(kUpdThreads),
-                         0, s, t, g, a);
-    else if (g.S == kMaxSpanBits)
-      hipLaunchKernelGGL((update_scan_kernel<1, true, 8>), dim3((unsigned)np), dim3(kUpdThreads),
-                         0, s, t, g, a);
-    else
-      hipLaunchKernelGGL((update_scan_kernel<1, false, 8>), dim3((unsigned)np), dim3(kUpdThreads),
-                         0, s, t, g, a);
-    return hipGetLastError();
+      return launch_kernel(update_scan_kernel<1, true, 2>, grid, block, 0, s, t, g, a);
+    if (g.S == kMaxSpanBits && ch == 4)
+      return launch_kernel(update_scan_kernel<1, true, 4>, grid, block, 0, s, t, g, a);
+    if (g.S == kMaxSpanBits)
+      return launch_kernel(update_scan_kernel<1, true, 8>, grid, block, 0, s, t, g, a);
+    return launch_kernel(update_scan_kernel<1, false, 8>, grid, block, 0, s, t, g, a);
   }
   // Bucketed: four partitions per block, one wave each, while the batch
   // spreads thin over the partitions (<= 16 entries each on average), so
@@ -1418,21 +1411,20 @@ hipError_t launch_update(const TreePtrs& t, const Buckets& bk, const Geom& g, Ri
   const bool thin = (uint64_t)B <= 16 * np;
   const unsigned grid = thin ? (unsigned)((np + 3) / 4) : (unsigned)np;
   const unsigned eb = grid_for((uint64_t)B, kTreeThreads, 1u << 30);
-  hipLaunchKernelGGL(bucket_kernel, dim3(eb), dim3(kTreeThreads), 0, s, bk, g, a);
+  hipError_t e = launch_kernel(bucket_kernel, dim3(eb), dim3(kTreeThreads), 0, s, bk, g, a);
+  if (e != hipSuccess) return e;
   const bool full = g.S == kMaxSpanBits;
   if (thin && full)
-    hipLaunchKernelGGL((update_bucket_kernel<4, true>), dim3(grid), dim3(kUpdThreads), 0, s, t, bk,
+    return launch_kernel(update_bucket_kernel<4, true>, dim3(grid), dim3(kUpdThreads), 0, s, t,
+                         bk, g, a);
+  if (thin)
+    return launch_kernel(update_bucket_kernel<4, false>, dim3(grid), dim3(kUpdThreads), 0, s, t,
+                         bk, g, a);
+  if (full)
+    return launch_kernel(update_bucket_kernel<1, true>, dim3(grid), dim3(kUpdThreads), 0, s, t,
+                         bk, g, a);
+  return launch_kernel(update_bucket_kernel<1, false>, dim3(grid), dim3(kUpdThreads), 0, s, t, bk,
                        g, a);
-  else if (thin)
-    hipLaunchKernelGGL((update_bucket_kernel<4, false>), dim3(grid), dim3(kUpdThreads), 0, s, t,
-                       bk, g, a);
-  else if (full)
-    hipLaunchKernelGGL((update_bucket_kernel<1, true>), dim3(grid), dim3(kUpdThreads), 0, s, t, bk,
-                       g, a);
-  else
-    hipLaunchKernelGGL((update_bucket_kernel<1, false>), dim3(grid), dim3(kUpdThreads), 0, s, t,
-                       bk, g, a);
-  return hipGetLastError();
 }
 
 hipError_t launch_add(const TreePtrs& t, const Geom& g, const Storage& st, RingRef ring,
@@ -1468,12 +1460,10 @@ hipError_t launch_add(const TreePtrs& t, const Geom& g, const Storage& st, RingR
     ncopy = grid_for((uint64_t)count * (uint64_t)st.D / 4 + count, kTreeThreads * 4, 2048);
   a.last = a.ntree + ncopy - 1u;
   if (g.S == kMaxSpanBits)
-    hipLaunchKernelGGL(add_kernel<true>, dim3(a.ntree + ncopy), dim3(kTreeThreads), 0, s, t, g, st,
-                       a);
-  else
-    hipLaunchKernelGGL(add_kernel<false>, dim3(a.ntree + ncopy), dim3(kTreeThreads), 0, s, t, g,
+    return launch_kernel(add_kernel<true>, dim3(a.ntree + ncopy), dim3(kTreeThreads), 0, s, t, g,
+                         st, a);
+  return launch_kernel(add_kernel<false>, dim3(a.ntree + ncopy), dim3(kTreeThreads), 0, s, t, g,
                        st, a);
-  return hipGetLastError();
 }
 
 hipError_t launch_update_add(const TreePtrs& t, const Geom& g, const Storage& st, RingRef ring,
@@ -1518,22 +1508,20 @@ hipError_t launch_update_add(const TreePtrs& t, const Geom& g, const Storage& st
   const int ch = scan_chunk(B);
   const dim3 grid(np + ncopy), block(kUpdThreads);
   if (!full && prio)
-    hipLaunchKernelGGL((update_add_kernel<true, false, 8>), grid, block, 0, s, t, g, st, a, b);
-  else if (!full)
-    hipLaunchKernelGGL((update_add_kernel<false, false, 8>), grid, block, 0, s, t, g, st, a, b);
-  else if (prio && ch == 2)
-    hipLaunchKernelGGL((update_add_kernel<true, true, 2>), grid, block, 0, s, t, g, st, a, b);
-  else if (prio && ch == 4)
-    hipLaunchKernelGGL((update_add_kernel<true, true, 4>), grid, block, 0, s, t, g, st, a, b);
-  else if (prio)
-    hipLaunchKernelGGL((update_add_kernel<true, true, 8>), grid, block, 0, s, t, g, st, a, b);
-  else if (ch == 2)
-    hipLaunchKernelGGL((update_add_kernel<false, true, 2>), grid, block, 0, s, t, g, st, a, b);
-  else if (ch == 4)
-    hipLaunchKernelGGL((update_add_kernel<false, true, 4>), grid, block, 0, s, t, g, st, a, b);
-  else
-    hipLaunchKernelGGL((update_add_kernel<false, true, 8>), grid, block, 0, s, t, g, st, a, b);
-  return hipGetLastError();
+    return launch_kernel(update_add_kernel<true, false, 8>, grid, block, 0, s, t, g, st, a, b);
+  if (!full)
+    return launch_kernel(update_add_kernel<false, false, 8>, grid, block, 0, s, t, g, st, a, b);
+  if (prio && ch == 2)
+    return launch_kernel(update_add_kernel<true, true, 2>, grid, block, 0, s, t, g, st, a, b);
+  if (prio && ch == 4)
+    return launch_kernel(update_add_kernel<true, true, 4>, grid, block, 0, s, t, g, st, a, b);
+  if (prio)
+    return launch_kernel(update_add_kernel<true, true, 8>, grid, block, 0, s, t, g, st, a, b);
+  if (ch == 2)
+    return launch_kernel(update_add_kernel<false, true, 2>, grid, block, 0, s, t, g, st, a, b);
+  if (ch == 4)
+    return launch_kernel(update_add_kernel<false, true, 4>, grid, block, 0, s, t, g, st, a, b);
+  return launch_kernel(update_add_kernel<false, true, 8>, grid, block, 0, s, t, g, st, a, b);
 }
 
 }  // namespace per

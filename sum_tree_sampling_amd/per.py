@@ -47,6 +47,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
         "per_destroy": (c_int, [vp]),
         "per_add": (c_int, [vp, i64, vp, vp, vp, vp, vp, vp, vp]),
         "per_update": (c_int, [vp, i64, vp, vp, vp]),
+        "per_set_sample_lanes": (c_int, [vp, i32]),
+        "per_time_next": (c_int, [vp, vp]),
         "per_update_add": (c_int, [vp, i64, vp, vp, i64, vp, vp, vp, vp, vp, vp, vp]),
         "per_sample": (c_int, [vp, i64, vp, f64, vp, vp, vp, vp, vp, vp, vp, vp]),
         "per_sample_padded": (c_int, [vp, i64, vp, f64, vp, vp, vp, vp, i64, vp, vp, vp, vp]),
@@ -138,6 +140,24 @@ def per_add(h, count, states=None, next_states=None, actions=None, rewards=None,
 
 def per_update(h, B, idx, td, stream=None) -> None:
     _check(load().per_update(h, int(B), _p(idx), _p(td), _stream(stream)))
+
+
+def per_set_sample_lanes(h, lanes) -> None:
+    _check(load().per_set_sample_lanes(h, int(lanes)))
+
+
+def per_time_next(start=None, stop=None) -> None:
+    """Time the next call's kernels: start / stop are torch.cuda.Event
+    (created with enable_timing=True) or raw hipEvent_t handles."""
+    _check(load().per_time_next(_event(start), _event(stop)))
+
+
+def _event(e):
+    if e is None:
+        return None
+    if isinstance(e, int):
+        return e
+    return e.cuda_event if hasattr(e, "cuda_event") else int(e)
 
 
 def per_update_add(h, B, idx, td, count, states=None, next_states=None, actions=None,
@@ -324,6 +344,10 @@ class PerBuffer:
 
     def update(self, idx, td, stream=None):
         per_update(self.h, idx.numel(), idx, td, stream)
+
+    def set_sample_lanes(self, lanes: int) -> None:
+        """per_set_sample_lanes: 64, 16 or 1 lanes per sample; 0 = automatic."""
+        per_set_sample_lanes(self.h, lanes)
 
     def update_add(self, idx, td, count, states=None, next_states=None, actions=None,
                    rewards=None, dones=None, prio=None, stream=None):

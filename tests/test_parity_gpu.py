@@ -1,8 +1,6 @@
 """GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
 same seeded inputs.  Trees, indices, rows and the running max are compared
 bit for bit; IS weights within 1e-6 relative."""
-import os
-
 import numpy as np
 import pytest
 import torch
@@ -22,7 +20,7 @@ def _buf(n, D=0, max_batch=4096, **kw):
 
 # ------------------------------------------------------------ the five workloads
 
-STEPS = {"tiny_1k": 30, "apex_shard_2m": 5, "dqn_1m": 3, "collision_stress_2m": 3}
+STEPS = {"tiny_1k": 30, "apex_shard_2m": 6, "dqn_1m": 3, "collision_stress_2m": 3}
 
 
 @pytest.mark.parametrize("name", list(STEPS))
@@ -41,11 +39,18 @@ def test_workload_parity(name):
         ro = o.sample(u, beta=s["beta"], weights=True, rows=rows)
         rg = g.sample(dev(u), beta=s["beta"], weights=True, rows=rows)
         compare_sample(rg, ro, "%s step %d sample" % (name, step), rows=rows)
-        # the sampler rebuilt the top levels in LDS and wrote them back
+        # sampling leaves the trees as they were (read through per_flush,
+        # which stores any top levels the writers left pending)
         compare_trees(o, g, "%s step %d after sample" % (name, step))
         idx = inp.update_idx() if "unique" in s else ro["idx"]
         td = inp.td()
         o.update(idx, td)
+        if s["intake"] and step % 2:
+            # the update and the intake in one launch, as the benchmark runs them
+            o.add(s["intake"])
+            g.update_add(dev(idx), dev(td), s["intake"])
+            compare_trees(o, g, "%s step %d update + intake" % (name, step))
+            continue
         g.update(dev(idx), dev(td))
         compare_trees(o, g, "%s step %d update" % (name, step))
         if s["intake"]:
@@ -55,15 +60,19 @@ def test_workload_parity(name):
     say("workload", name, "ok")
 
 
+# Lanes per sample of each descent layout (per_set_sample_lanes).
+LANES = {"1": 64, "2": 16, "3": 1}
+
+
 @pytest.mark.parametrize("mode", ["1", "2", "3"])
-def test_sampler_modes_agree(mode, monkeypatch):
+def test_sampler_modes_agree(mode):
     """Each descent variant (one wave, 16 lanes, one lane per sample) returns
     the oracle's indices, weights and rows."""
-    monkeypatch.setenv("PER_SAMPLE_MODE", mode)
     n, D = 1 << 20, 64
     say("sampler mode", mode)
     o = Oracle(n, D)
     g = _buf(n, D, max_batch=20000)
+    g.set_sample_lanes(LANES[mode])
     fill("dqn_1m", o, g)
     # non-uniform priorities so that every level matters
     inp = workloads.StepInputs("dqn_1m", batch=3000)
@@ -97,14 +106,12 @@ def test_sampler_top_depths(L):
     g.add(n, prio=dev(p0))
     for step in range(2):
         for mode in ("1", "2", "3"):
-            os.environ["PER_SAMPLE_MODE"] = mode
-            try:
-                u = rng.random(700, dtype=np.float32)
-                u[:2] = [0.0, np.nextafter(np.float32(1), np.float32(0))]
-                compare_sample(g.sample(dev(u), beta=0.4), o.sample(u, beta=0.4),
-                               "L=%d step %d mode %s" % (L, step, mode))
-            finally:
-                del os.environ["PER_SAMPLE_MODE"]
+            g.set_sample_lanes(LANES[mode])
+            u = rng.random(700, dtype=np.float32)
+            u[:2] = [0.0, np.nextafter(np.float32(1), np.float32(0))]
+            compare_sample(g.sample(dev(u), beta=0.4), o.sample(u, beta=0.4),
+                           "L=%d step %d mode %s" % (L, step, mode))
+        g.set_sample_lanes(0)
         idx = rng.integers(0, n, 3000).astype(np.int64)
         td = (rng.standard_normal(3000) * 2).astype(np.float32)
         o.update(idx, td)
@@ -121,18 +128,15 @@ def test_zero_priorities_never_sampled():
     pr = fill(name, o, g)
     rng = np.random.default_rng(3)
     for mode in ("1", "2", "3"):
-        os.environ["PER_SAMPLE_MODE"] = mode
-        try:
-            u = rng.random(4096, dtype=np.float32)
-            u[:64] = np.float32(1) - np.float32(2.0 ** -24) * np.arange(1, 65, dtype=np.float32)
-            ro = o.sample(u, weights=False)
-            rg = g.sample(dev(u), weights=True)
-            compare_sample(rg, ro, "zeros mode " + mode, weights=False)
-            got = host(rg["idx"])
-            assert np.all(pr[got] > 0)
-            assert np.all(host(rg["w"]) == 0.0)  # min priority is 0
-        finally:
-            del os.environ["PER_SAMPLE_MODE"]
+        g.set_sample_lanes(LANES[mode])
+        u = rng.random(4096, dtype=np.float32)
+        u[:64] = np.float32(1) - np.float32(2.0 ** -24) * np.arange(1, 65, dtype=np.float32)
+        ro = o.sample(u, weights=False)
+        rg = g.sample(dev(u), weights=True)
+        compare_sample(rg, ro, "zeros mode " + mode, weights=False)
+        got = host(rg["idx"])
+        assert np.all(pr[got] > 0)
+        assert np.all(host(rg["w"]) == 0.0)  # min priority is 0
 
 
 # ------------------------------------------------------------ update paths
@@ -437,11 +441,9 @@ def test_top_deeper_than_lds():
     for step in range(2):
         u = rng.random(2048, dtype=np.float32)
         for mode in ("1", "2", "3"):
-            os.environ["PER_SAMPLE_MODE"] = mode
-            try:
-                compare_sample(g.sample(dev(u)), o.sample(u), "2^25 mode " + mode)
-            finally:
-                del os.environ["PER_SAMPLE_MODE"]
+            g.set_sample_lanes(LANES[mode])
+            compare_sample(g.sample(dev(u)), o.sample(u), "2^25 mode " + mode)
+        g.set_sample_lanes(0)
         idx = rng.integers(0, n, 2048).astype(np.int64)
         td = rng.standard_normal(2048).astype(np.float32)
         o.update(idx, td)
@@ -692,43 +694,74 @@ def test_update_add_batch_max(alpha, eps, kind):
 
 def test_large_16m_full_size():
     """2^24 leaves, 2 x [2^24 x 128] f32 rows, B = 65536 with the sampler's
-    default plan: the whole trees and all indices against the oracle; rows of
-    sampled slots against the generator for four row chunks and against a
-    PyTorch index_select of the device storage for all of them."""
+    default plan, two steps.  The oracle (trees only) runs both steps first,
+    so that the sampled slots are known before the rows exist; the fill then
+    generates every row chunk once, checks the device storage of each chunk
+    against it (all five fields) and keeps the generator's rows at the
+    oracle's sampled slots.  The device's steps are then checked against
+    those: both trees after every operation, all indices and weights, and
+    all five gathered fields of every sampled row."""
     name = "large_16m"
     s = workloads.spec(name)
     n, B, D = s["capacity"], s["batch"], s["state_dim"]
-    say("large: filling", n, D)
-    o = Oracle(n)  # trees only: rows are checked against the generator
-    g = _buf(n, D, max_batch=B)
-    fill(name, o, g)
-    compare_trees(o, g, "large after fill")
-    keep = [0, 7, 100, 255]
-    kept = {k: workloads.row_chunk(name, k) for k in keep}
-    for k, r in kept.items():
-        lo = k * workloads.ROW_CHUNK
-        assert_bits_equal(host(g.storage["states"][lo:lo + workloads.ROW_CHUNK]), r["states"],
-                          "storage chunk %d" % k)
+    keys = ("states", "next_states", "actions", "rewards", "dones")
+    say("large: oracle steps", n, B)
+    o = Oracle(n)
+    pr = workloads.initial_priorities(name)
+    o.add(n, prio=pr)
+    snap = [(o.sum_tree().copy(), o.min_tree().copy(), o.max_priority)]
     inp = workloads.StepInputs(name)
+    steps = []
     for step in range(2):
-        say("large step", step)
         u = inp.u()
         ro = o.sample(u, beta=s["beta"])
+        td = inp.td()
+        o.update(ro["idx"], td)
+        snap.append((o.sum_tree().copy(), o.min_tree().copy(), o.max_priority))
+        steps.append((u, td, ro))
+    o.close()
+
+    say("large: filling", n, D)
+    g = _buf(n, D, max_batch=B)
+    expect = [{k: None for k in keys} for _ in steps]
+    chunk = 1 << 20
+    for lo in range(0, n, chunk):
+        say("  fill rows [%d, %d)" % (lo, lo + chunk))
+        r = workloads.rows(name, lo, chunk)
+        g.add(chunk, dev(r["states"]), dev(r["next_states"]), dev(r["actions"]),
+              dev(r["rewards"]), dev(r["dones"]), prio=dev(pr[lo:lo + chunk]))
+        torch.cuda.synchronize()
+        for k in keys:
+            got = host(g.storage[k][lo:lo + chunk])
+            if k == "actions":
+                got = got.view(np.uint32)
+            assert_bits_equal(got, r[k], "storage %s rows [%d, %d)" % (k, lo, lo + chunk))
+        for st, (_, _, ro) in enumerate(steps):
+            idx = ro["idx"]
+            sel = np.nonzero((idx >= lo) & (idx < lo + chunk))[0]
+            for k in keys:
+                if expect[st][k] is None:
+                    expect[st][k] = np.zeros((B,) + r[k].shape[1:], r[k].dtype)
+                expect[st][k][sel] = r[k][idx[sel] - lo]
+        del r
+
+    def check_trees(sn, what):
+        sm, mm, mp = sn
+        torch.cuda.synchronize()
+        assert_bits_equal(host(g.sum_tree())[1:2 * n], sm[1:], what + " sum tree")
+        assert_bits_equal(host(g.min_tree())[1:2 * n], mm[1:], what + " min tree")
+        got = host(g.scalar("max_priority"))[0]
+        assert np.float32(got).view(np.uint32) == np.float32(mp).view(np.uint32), (what, got, mp)
+
+    check_trees(snap[0], "large after fill")
+    for step, (u, td, ro) in enumerate(steps):
+        say("large step", step)
         rg = g.sample(dev(u), beta=s["beta"], rows=True)
         compare_sample(rg, ro, "large step %d" % step)
-        idx_t = rg["idx"]
-        for key in ("states", "next_states", "actions", "rewards", "dones"):
-            ref = torch.index_select(g.storage[key], 0, idx_t)
-            assert torch.equal(rg[key], ref), key
-        idx = ro["idx"]
-        ch = idx // workloads.ROW_CHUNK
-        for k, r in kept.items():
-            sel = np.nonzero(ch == k)[0]
-            off = idx[sel] - k * workloads.ROW_CHUNK
-            assert_bits_equal(host(rg["states"])[sel], r["states"][off], "rows chunk %d" % k)
-            assert_bits_equal(host(rg["next_states"])[sel], r["next_states"][off],
-                              "next rows chunk %d" % k)
-        td = inp.td()
-        o.update(idx, td)
-        g.update(dev(idx), dev(td))
-        compare_trees(o, g, "large step %d update" % step)
+        for k in keys:
+            got = host(rg[k])
+            if k == "actions":
+                got = got.view(np.uint32)
+            assert_bits_equal(got, expect[step][k], "large step %d gathered %s" % (step, k))
+        g.update(rg["idx"], dev(td))
+        check_trees(snap[step + 1], "large step %d update" % step)
