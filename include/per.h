@@ -123,6 +123,25 @@ int per_update(per_t* h, int64_t B, const int64_t* d_idx, const float* d_td,
                hipStream_t stream);
 
 /*
+ * per_update for callers that cannot allocate device memory at the call:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  Same arguments, result and errors as per_update.  A batch
+ * that takes the bucketed update (more than 2^20 / 2^P entries, 2^P =
+ * capacity / 4096 partitions) keeps its buckets, overflow list and counters
+ * in a static device array of the library (4 MiB, one per device, held until
+ * the process ends) instead of in the handle's workspace; the call clears
+ * its counters first with a small kernel.  Limits of that array: capacity
+ * <= 2^24 and B <= 2^16 for a bucketed batch, else PER_EINVAL; smaller
+ * batches need no scratch and take any size per_update takes.  The call
+ * allocates nothing and launches no allocating routine.  Every handle on a
+ * device shares the one array: per_update_static calls that may overlap on
+ * one device (on different streams or from different host threads) race on
+ * it and must be ordered by the caller.
+ */
+int per_update_static(per_t* h, int64_t B, const int64_t* d_idx, const float* d_td,
+                      hipStream_t stream);
+
+/*
  * per_update(h, B, d_idx, d_td) followed by per_add(h, count, rows..., d_prio)
  * in one kernel launch where possible ("Putting prioritized replay's segment
  * tree on a GPU", section "The Tree Under Every Prioritized Replay": the

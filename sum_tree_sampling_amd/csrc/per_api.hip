@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <cstdlib>
+#include <mutex>
 #include <new>
 #include <string>
 
@@ -106,11 +107,67 @@ per::Geom make_geom(int64_t capacity) {
   return g;
 }
 
+// ---------------------------------------------------- static update scratch
+//
+// per_update_static takes the bucketed update's scratch (bucket counts,
+// overflow counters, buckets, overflow list) from this array instead of the
+// handle's workspace.  Each device that loads the library holds its own copy
+// until the process ends; host code reaches it only through the address
+// hipGetSymbolAddress gives on that device (the array's name on the host is
+// a stand-in, not a device address).  Sized for 2^12 partitions of 4096
+// leaves (capacity <= 2^24) and batches of up to 2^16 entries.
+constexpr int64_t kStaticMaxParts = int64_t(1) << 12;
+constexpr int64_t kStaticMaxBatch = int64_t(1) << 16;
+constexpr size_t kStaticScratchBytes = size_t(4) << 20;
+constexpr int kMaxDevices = 64;
+
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // the array's address on each device (NULL: not resolved)
+
+// Resolves the array's address on `device`, which must be the current
+// device.  Once per device; later calls return at once.
+int resolve_static_scratch(int device) {
+  if (device < 0 || device >= kMaxDevices) return PER_OK;  // per_update_static refuses it
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[device]) return PER_OK;
+  void* p = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return hip_fail(e, "static update scratch: hipGetSymbolAddress");
+  g_scratch_ptr[device] = p;
+  return PER_OK;
+}
+
 }  // namespace
 
 namespace per {
 
 KernelTiming& kernel_timing() { return g_timing; }
+
+// The bucketed update's scratch for np partitions and max_batch entries,
+// laid out from `base` (256-byte aligned) with the workspace's rules; the
+// layout's end is returned in *end.
+Buckets bucket_layout(char* base, size_t np, int64_t max_batch, size_t* end) {
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align256(o + bytes);
+    return base + at;
+  };
+  const size_t nb = np * kBucketCap;
+  Buckets b;
+  b.counts = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * np));
+  b.ovf_n = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * 2));
+  b.slot = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * nb));
+  b.pos = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * nb));
+  b.td = reinterpret_cast<float*>(take(sizeof(float) * nb));
+  b.oslot = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * (size_t)max_batch));
+  b.opos = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * (size_t)max_batch));
+  b.otd = reinterpret_cast<float*>(take(sizeof(float) * (size_t)max_batch));
+  if (end) *end = o;
+  return b;
+}
 
 Layout workspace_layout(int64_t n, int64_t max_batch) {
   const Geom g = make_geom(n);
@@ -217,6 +274,11 @@ int per_create(per_t** out, int64_t capacity, int32_t state_dim, int64_t max_bat
   h->rank_size = 0;
   h->rank_built = -1;
   if (hipGetDevice(&h->device) != hipSuccess) h->device = -1;
+  rc = resolve_static_scratch(h->device);
+  if (rc) {
+    delete h;
+    return rc;
+  }
   hipError_t e = per::launch_init(h->t, h->bk, h->g, stream);
   if (e != hipSuccess) {
     delete h;
@@ -295,6 +357,39 @@ int per_update(per_t* h, int64_t B, const int64_t* d_idx, const float* d_td,
   if (e != hipSuccess) return hip_fail(e, "per_update");
   h->epoch ^= 1;
   if (per::update_uses_buckets(h->g, B)) h->ovf ^= 1;
+  h->top_stale = h->g.P > 0;
+  return ok();
+}
+
+int per_update_static(per_t* h, int64_t B, const int64_t* d_idx, const float* d_td,
+                      hipStream_t stream) {
+  if (!h) return fail(PER_EINVAL, "handle is NULL");
+  int rc = check_update(h, B, d_idx, d_td);
+  if (rc) return rc;
+  if (B == 0) return ok();
+  const int64_t np = int64_t(1) << h->g.P;
+  const bool bucketed = per::update_uses_buckets(h->g, B);
+  if (bucketed && (np > kStaticMaxParts || B > kStaticMaxBatch))
+    return fail(PER_EINVAL,
+                "per_update_static: a bucketed batch needs capacity <= 2^24 and B <= 2^16 "
+                "(capacity %lld, B %lld)", (long long)h->g.n, (long long)B);
+  if (h->device < 0 || h->device >= kMaxDevices || !g_scratch_ptr[h->device])
+    return fail(PER_EHIP, "per_update_static: no static scratch on device %d", h->device);
+  size_t end = 0;
+  const per::Buckets sb =
+      per::bucket_layout(static_cast<char*>(g_scratch_ptr[h->device]), (size_t)np,
+                         kStaticMaxBatch, &end);
+  if (end > kStaticScratchBytes)
+    return fail(PER_EINVAL, "per_update_static: scratch layout exceeds the array");
+  hipError_t e = hipSuccess;
+  // The array keeps the previous call's counters (of any handle on this
+  // device): clear them, then always use overflow counter 0.
+  if (bucketed) e = per::launch_bucket_clear(sb, h->g, stream);
+  if (e == hipSuccess)
+    e = per::launch_update(h->t, sb, h->g, ring_ref(h), (uint32_t)h->size, B, d_idx, d_td,
+                           h->alpha, h->eps, h->epoch, h->epoch ^ 1, 0, stream);
+  if (e != hipSuccess) return hip_fail(e, "per_update_static");
+  h->epoch ^= 1;
   h->top_stale = h->g.P > 0;
   return ok();
 }

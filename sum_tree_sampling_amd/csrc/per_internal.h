@@ -111,6 +111,9 @@ struct Layout {
   size_t sum, mn, ctrl, counts, ovf_n, slot, pos, td, oslot, opos, otd, total;
 };
 Layout workspace_layout(int64_t n, int64_t max_batch);
+// The bucketed update's scratch for np partitions and max_batch entries laid
+// out from base (256-byte aligned); *end receives the bytes it spans.
+Buckets bucket_layout(char* base, size_t np, int64_t max_batch, size_t* end);
 
 // Descent plan of the sampler.  The top of the tree reaches LDS either by a
 // rebuild from the partition roots (kTopRebuild, 0 < P <= kMaxTopBits), by
@@ -137,6 +140,9 @@ hipError_t launch_update(const TreePtrs& t, const Buckets& bk, const Geom& g, Ri
                          uint32_t size, int64_t B, const int64_t* idx, const float* td,
                          double alpha, double eps, int src, int dst, int ovf, hipStream_t s);
 bool update_uses_buckets(const Geom& g, int64_t B);
+// Zero the bucket counts of the 2^P partitions and both overflow counters
+// (a fill kernel, so that a captured sequence clears them on every replay).
+hipError_t launch_bucket_clear(const Buckets& bk, const Geom& g, hipStream_t s);
 
 // Rebuild of the nodes above the partitions (one block).
 hipError_t launch_top(const TreePtrs& t, const Geom& g, hipStream_t s);

@@ -685,6 +685,12 @@ __global__ void __launch_bounds__(256) init_kernel(TreePtrs t, Buckets bk, Geom 
   }
 }
 
+__global__ void __launch_bounds__(256) bucket_clear_kernel(Buckets bk, uint32_t np) {
+  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < np; i += gridDim.x * blockDim.x)
+    bk.counts[i] = 0u;
+  if (blockIdx.x == 0 && threadIdx.x < 2) bk.ovf_n[threadIdx.x] = 0u;
+}
+
 struct UpdateArgs {
   const int64_t* idx;
   const float* td;
@@ -1366,6 +1372,12 @@ hipError_t launch_init(const TreePtrs& t, const Buckets& bk, const Geom& g, hipS
 
 hipError_t launch_top(const TreePtrs& t, const Geom& g, hipStream_t s) {
   return launch_kernel(top_kernel, dim3(1), dim3(kTreeThreads), 0, s, t, g);
+}
+
+hipError_t launch_bucket_clear(const Buckets& bk, const Geom& g, hipStream_t s) {
+  const uint32_t np = 1u << g.P;
+  return launch_kernel(bucket_clear_kernel, dim3(grid_for(np, kTreeThreads, 64)),
+                       dim3(kTreeThreads), 0, s, bk, np);
 }
 
 bool update_uses_buckets(const Geom& g, int64_t B) {

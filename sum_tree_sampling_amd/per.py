@@ -47,6 +47,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
         "per_destroy": (c_int, [vp]),
         "per_add": (c_int, [vp, i64, vp, vp, vp, vp, vp, vp, vp]),
         "per_update": (c_int, [vp, i64, vp, vp, vp]),
+        "per_update_static": (c_int, [vp, i64, vp, vp, vp]),
         "per_set_sample_lanes": (c_int, [vp, i32]),
         "per_time_next": (c_int, [vp, vp]),
         "per_update_add": (c_int, [vp, i64, vp, vp, i64, vp, vp, vp, vp, vp, vp, vp]),
@@ -140,6 +141,10 @@ def per_add(h, count, states=None, next_states=None, actions=None, rewards=None,
 
 def per_update(h, B, idx, td, stream=None) -> None:
     _check(load().per_update(h, int(B), _p(idx), _p(td), _stream(stream)))
+
+
+def per_update_static(h, B, idx, td, stream=None) -> None:
+    _check(load().per_update_static(h, int(B), _p(idx), _p(td), _stream(stream)))
 
 
 def per_set_sample_lanes(h, lanes) -> None:
@@ -344,6 +349,11 @@ class PerBuffer:
 
     def update(self, idx, td, stream=None):
         per_update(self.h, idx.numel(), idx, td, stream)
+
+    def update_static(self, idx, td, stream=None):
+        """per_update_static: per_update with its scratch in the library's
+        static device array (allocates nothing)."""
+        per_update_static(self.h, idx.numel(), idx, td, stream)
 
     def set_sample_lanes(self, lanes: int) -> None:
         """per_set_sample_lanes: 64, 16 or 1 lanes per sample; 0 = automatic."""

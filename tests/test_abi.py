@@ -121,6 +121,7 @@ def test_null_handle_is_rejected(lib):
     assert lib.per_update_add(None, 1, 0x1000, 0x1000, 1, None, None, None, None, None, None,
                               None) == -1
     assert lib.per_total(None, 0x1000, None) == -1
+    assert lib.per_update_static(None, 1, 0x1000, 0x1000, None) == -1
     assert lib.per_set_sample_lanes(None, 0) == -1
     assert lib.per_time_next(None, None) == 0
     assert lib.per_destroy(None) == -1
