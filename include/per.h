@@ -169,9 +169,10 @@ int per_update_add(per_t* h, int64_t B, const int64_t* d_idx, const float* d_td,
  * Plan", Task 3).
  *  B in [0, max_batch]; PER_EEMPTY if size == 0 (checked on the host).
  *  d_u [B] f32 uniforms in [0, 1) (unchecked).  Sample b uses the mass
- *    m = f32(u_b * total), clamped below total, and walks from the root: if
- *    the left child's sum exceeds m, or the right child's sum is 0, go left;
- *    otherwise m = f32(m - left) and go right.
+ *    m = f32(u_b * total), clamped below total, and picks one child per
+ *    level from the root: the right one when the left child's sum is at
+ *    most m and the right child's sum is not 0 (then m = f32(m - left sum)),
+ *    else the left one.
  *  d_idx_out [B] i64: sampled slots (required).
  *  d_w_out [B] f32 or NULL: w_b = f32((N*P_b)^-beta / (N*P_min)^-beta) in
  *    f64, N = size, P_b = p_b / total, P_min = min-tree root / total; 0 when

@@ -164,24 +164,26 @@ int pero_update(pero_t* t, int64_t B, const int64_t* idx, const float* td) {
     return 0;
 }
 
-/* One descent for mass m in [0, total).  "Putting prioritized replay's
- * segment tree on a GPU", section "Sampling Is a Descent": if the left
- * child's sum exceeds the remaining mass go left, otherwise subtract it and
- * go right.  Reading: the mass is carried in f32 and a zero right child
- * also sends the walk left. */
+/* The leaf offset that mass m in [0, total) selects ("Putting prioritized
+ * replay's segment tree on a GPU", section "Sampling Is a Descent").  The
+ * offset is built one bit per level, most significant first: at depth d the
+ * walk stands on node 2^d + off and compares the remaining mass with its two
+ * children.  The bit is 1 -- the right child -- when the left child's sum
+ * does not exceed the mass, and then that sum is taken off the mass.
+ * Readings: the mass is an f32 and every subtraction is rounded to f32, and
+ * a right child whose sum is 0 is never taken. */
 static int64_t descend_tree(const float* sum, int64_t n, float m) {
-    int64_t i = 1;
-    while (i < n) {
-        float l = sum[2 * i];
-        float r = sum[2 * i + 1];
-        if (l > m || r == 0.0f) {
-            i = 2 * i;
-        } else {
-            m = m - l;
-            i = 2 * i + 1;
-        }
+    int levels = 0;
+    while (((int64_t)1 << levels) < n) ++levels;
+    int64_t off = 0;
+    for (int d = 0; d < levels; ++d) {
+        const int64_t node = ((int64_t)1 << d) + off;
+        const float left = sum[2 * node], right = sum[2 * node + 1];
+        const int bit = !(left > m) && right != 0.0f;
+        if (bit) m -= left;
+        off = 2 * off + bit;
     }
-    return i - n;
+    return off;
 }
 
 /* IS weight of a sampled priority p: (N*P(i))^-beta normalised by its

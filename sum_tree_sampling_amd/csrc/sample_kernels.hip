@@ -3,9 +3,10 @@
 // fused in one kernel.
 //
 // Descent rule ("Putting prioritized replay's segment tree on a GPU",
-// section "Sampling Is a Descent"): at each node, if the left child's sum
-// exceeds the remaining mass m (or the right child's sum is 0) go left,
-// otherwise m = f32(m - left) and go right.
+// section "Sampling Is a Descent"): each level decides one bit of the leaf
+// offset.  The right child is taken when the left child's sum is at most the
+// remaining mass and the right child's sum is not 0; the left sum is then
+// taken off the mass (an f32 subtraction).
 //
 // Layout of the work: a group of G lanes (G = 16: four samples per wave;
 // G = 1: one lane per sample; G = 64: one wave per sample) carries one

@@ -15,12 +15,14 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 # (name, original text, mutated text)
 MUTANTS = [
-    ("tie_goes_left", "if (l > m || r == 0.0f)", "if (l >= m || r == 0.0f)"),
-    ("no_zero_guard", "if (l > m || r == 0.0f)", "if (l > m)"),
-    ("children_swapped", "float l = sum[2 * i];\n        float r = sum[2 * i + 1];",
-     "float l = sum[2 * i + 1];\n        float r = sum[2 * i];"),
-    ("mass_added", "m = m - l;", "m = m + l;"),
-    ("mass_not_reduced", "m = m - l;", "m = m;"),
+    ("tie_goes_left", "const int bit = !(left > m) && right != 0.0f;",
+     "const int bit = !(left >= m) && right != 0.0f;"),
+    ("no_zero_guard", "const int bit = !(left > m) && right != 0.0f;",
+     "const int bit = !(left > m);"),
+    ("children_swapped", "const float left = sum[2 * node], right = sum[2 * node + 1];",
+     "const float left = sum[2 * node + 1], right = sum[2 * node];"),
+    ("mass_added", "if (bit) m -= left;", "if (bit) m += left;"),
+    ("mass_not_reduced", "if (bit) m -= left;", "if (bit) m -= 0.0f;"),
     ("sum_drops_right", "t->sum[i] = l + r;", "t->sum[i] = l;"),
     ("sum_wrong_index", "float l = t->sum[2 * i], r = t->sum[2 * i + 1];",
      "float l = t->sum[2 * i], r = t->sum[2 * i];"),
