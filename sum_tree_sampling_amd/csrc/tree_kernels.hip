@@ -45,6 +45,14 @@ namespace per {
 namespace {
 
 constexpr int kSubBits = 10;  // crowded partitions are rebuilt in 2^10-leaf pieces
+// Whether the scan path (small batches) also takes its low siblings from
+// the leaf's line (line_siblings).  It does not: there a partition holds one
+// or two entries and the step is bound by latency, which the line's extra
+// loads and adds lengthen (measured: Ape-X update + intake 6.1 -> 6.6 us,
+// DQN update 6.4 -> 7.4 us), while the bucketed path, bound by the count of
+// lines its many entries touch, gains (2^24 leaves, 65536 entries: 32.9 ->
+// 27.3 us).
+constexpr bool kScanLine = false;
 constexpr int kUpdThreads = 256;  // threads of an update block
 constexpr int kSub = 1 << kSubBits;
 
@@ -227,11 +235,52 @@ struct UpdSmem {
   int flag;
 };
 
+// The parent of two tree values: their f32 sum, or their min.
+template <bool MIN>
+__device__ __forceinline__ float join(float a, float b) {
+  return MIN ? min_f32(a, b) : a + b;
+}
+
+template <bool MIN>
+__device__ __forceinline__ float join4(float4 v) {
+  return join<MIN>(join<MIN>(v.x, v.y), join<MIN>(v.z, v.w));
+}
+
+// Heights of a leaf's path whose siblings lie in the leaf's aligned 32-leaf
+// line (128 bytes): the sibling at height h < 5 is the subtree over the 2^h
+// leaves of block (node >> h) ^ 1, next to the leaf's own block.
+constexpr int kLineHeights = 5;
+
+// The stored siblings at heights 0..4 of the path from leaf node `node`
+// (n a multiple of 32), from the leaves of its line: the leaves of each
+// sibling block, reduced pairwise in heap order (a stored node is exactly
+// the f32 sum, or the min, of its two children, so this is its stored value
+// bit for bit).  Nine loads that all fall in one line, instead of one line
+// per height.
+template <bool MIN>
+__device__ __forceinline__ void line_siblings(const float* tree, uint32_t node, float* sib) {
+  const float s0 = tree[node ^ 1u];
+  const float2 s1 = *reinterpret_cast<const float2*>(tree + (((node >> 1) ^ 1u) << 1));
+  const float4 s2 = *reinterpret_cast<const float4*>(tree + (((node >> 2) ^ 1u) << 2));
+  const float4* p3 = reinterpret_cast<const float4*>(tree + (((node >> 3) ^ 1u) << 3));
+  const float4* p4 = reinterpret_cast<const float4*>(tree + (((node >> 4) ^ 1u) << 4));
+  const float4 s3a = p3[0], s3b = p3[1];
+  const float4 s4a = p4[0], s4b = p4[1], s4c = p4[2], s4d = p4[3];
+  sib[0] = s0;
+  sib[1] = join<MIN>(s1.x, s1.y);
+  sib[2] = join4<MIN>(s2);
+  sib[3] = join<MIN>(join4<MIN>(s3a), join4<MIN>(s3b));
+  sib[4] = join<MIN>(join<MIN>(join4<MIN>(s4a), join4<MIN>(s4b)),
+                     join<MIN>(join4<MIN>(s4c), join4<MIN>(s4d)));
+}
+
 // Collect entry k of a partition (any thread): for the first 64 entries the
 // stored siblings along its leaf's whole path to the partition root go to
 // the partition's sparse area, loaded before the priority's pow so that both
-// latencies overlap.  Returns the priority.
-template <bool FULL>
+// latencies overlap.  LINE (with FULL): the siblings of heights 0..4 come
+// from the leaf's line (line_siblings), the others one load each.  Returns
+// the priority.
+template <bool FULL, bool LINE>
 __device__ __forceinline__ float collect(SparseSmem& sp, int k, const TreePtrs& t,
                                          const Geom& g, uint32_t part, uint32_t off,
                                          uint32_t pos, float td, float m0, double alpha,
@@ -240,8 +289,12 @@ __device__ __forceinline__ float collect(SparseSmem& sp, int k, const TreePtrs& 
   float ps[kMaxSpanBits], pm[kMaxSpanBits];
   const uint32_t node = g.n + (part << S) + off;
   if (k < kSparseMax) {
+    if constexpr (FULL && LINE) {
+      line_siblings<false>(t.sum, node, ps);
+      line_siblings<true>(t.mn, node, pm);
+    }
 #pragma unroll
-    for (int q = 0; q < kMaxSpanBits; ++q) {
+    for (int q = (FULL && LINE) ? kLineHeights : 0; q < kMaxSpanBits; ++q) {
       if (q < S) {
         const uint32_t sib = (node >> q) ^ 1u;
         ps[q] = t.sum[sib];
@@ -717,7 +770,7 @@ __device__ __forceinline__ uint32_t filled_size(const UpdateArgs& a) {
 // caller's batch max.  Returns whether a partition was crowded (then
 // rebuilt by the whole block, which has passed a barrier since); otherwise
 // wave w returns right after its sparse repair.
-template <int PPB, bool FUSED, bool FULL, int kChunk, typename SM, typename Skip>
+template <int PPB, bool FUSED, bool FULL, int kChunk, bool LINE, typename SM, typename Skip>
 __device__ __forceinline__ bool scan_update(SM& sm, const TreePtrs& t, const Geom& g,
                                             const UpdateArgs& a, uint32_t part0, uint32_t size,
                                             float m0, Skip skip) {
@@ -781,8 +834,8 @@ __device__ __forceinline__ bool scan_update(SM& sm, const TreePtrs& t, const Geo
         bool keep = true;
         if constexpr (FUSED) keep = !skip(off);
         const int k = keep ? atomicAdd(&sm.count[q], 1) : kSparseMax;
-        const float p = collect<FULL>(sm.u.sp[q], k, t, g, part, off, b, td, m0, a.alpha, a.eps,
-                                      a.p_nan);
+        const float p = collect<FULL, LINE>(sm.u.sp[q], k, t, g, part, off, b, td, m0, a.alpha,
+                                            a.eps, a.p_nan);
         atomicMax(&sm.bmax, __float_as_uint(p));
       }
     }
@@ -815,15 +868,15 @@ __device__ __forceinline__ bool scan_update(SM& sm, const TreePtrs& t, const Geo
   return true;
 }
 
-template <int PPB, bool FULL, int CH>
+template <int PPB, bool FULL, int CH, bool LINE>
 __global__ void __launch_bounds__(kUpdThreads) update_scan_kernel(TreePtrs t, Geom g, UpdateArgs a) {
   __shared__ UpdSmem<PPB> sm;
   // The arguments the first steps need, fetched in one batch.
   asm volatile("" ::"s"(t.ctrl), "s"(a.idx), "s"(a.td), "s"(a.B), "s"(a.src), "s"(a.size),
                "s"(a.ring.dev), "s"(g.n), "s"(g.S));
   const float m0 = __uint_as_float(t.ctrl->maxp_bits[a.src]);
-  scan_update<PPB, false, FULL, CH>(sm, t, g, a, blockIdx.x * PPB, filled_size(a), m0,
-                                    [](uint32_t) { return false; });
+  scan_update<PPB, false, FULL, CH, LINE>(sm, t, g, a, blockIdx.x * PPB, filled_size(a), m0,
+                                          [](uint32_t) { return false; });
 }
 
 // Large batches, step 1: every valid entry goes to its partition's bucket
@@ -887,9 +940,9 @@ __global__ void __launch_bounds__(kUpdThreads) update_bucket_kernel(TreePtrs t, 
       uint32_t pb = 0u;
       if ((uint32_t)lane < m) {
         const uint32_t e = part * kBucketCap + lane;
-        const float p = collect<FULL>(sp, lane, t, g, part,
-                                      bk.slot[e] - (part << span_bits<FULL>(g)), bk.pos[e],
-                                      bk.td[e], m0, a.alpha, a.eps, a.p_nan);
+        const float p = collect<FULL, true>(sp, lane, t, g, part,
+                                            bk.slot[e] - (part << span_bits<FULL>(g)),
+                                            bk.pos[e], bk.td[e], m0, a.alpha, a.eps, a.p_nan);
         pb = __float_as_uint(p);
       }
       pb = wave_max_u32(pb);
@@ -1267,8 +1320,8 @@ __global__ void __launch_bounds__(kUpdThreads) update_add_kernel(TreePtrs t, Geo
   const float m0 = __uint_as_float(t.ctrl->maxp_bits[a.src]);
   // Update entries at slots the intake takes are left out of the repair
   // (the intake overwrites them; their priorities still count).
-  const bool crowded = scan_update<1, true, FULL, CH>(sm, t, g, a, part, size, m0,
-                                                    [&](uint32_t off) { return ir.has(off); });
+  const bool crowded = scan_update<1, true, FULL, CH, kScanLine>(
+      sm, t, g, a, part, size, m0, [&](uint32_t off) { return ir.has(off); });
   if (ir.runs == 0) return;
   if constexpr (PRIO) {
     // The update's repair is complete, and visible to the whole block,
@@ -1409,12 +1462,12 @@ hipError_t launch_update(const TreePtrs& t, const Buckets& bk, const Geom& g, Ri
     const int ch = scan_chunk(B);
     const dim3 grid((unsigned)np), block(kUpdThreads);
     if (g.S == kMaxSpanBits && ch == 2)
-      return launch_kernel(update_scan_kernel<1, true, 2>, grid, block, 0, s, t, g, a);
+      return launch_kernel(update_scan_kernel<1, true, 2, kScanLine>, grid, block, 0, s, t, g, a);
     if (g.S == kMaxSpanBits && ch == 4)
-      return launch_kernel(update_scan_kernel<1, true, 4>, grid, block, 0, s, t, g, a);
+      return launch_kernel(update_scan_kernel<1, true, 4, kScanLine>, grid, block, 0, s, t, g, a);
     if (g.S == kMaxSpanBits)
-      return launch_kernel(update_scan_kernel<1, true, 8>, grid, block, 0, s, t, g, a);
-    return launch_kernel(update_scan_kernel<1, false, 8>, grid, block, 0, s, t, g, a);
+      return launch_kernel(update_scan_kernel<1, true, 8, kScanLine>, grid, block, 0, s, t, g, a);
+    return launch_kernel(update_scan_kernel<1, false, 8, false>, grid, block, 0, s, t, g, a);
   }
   // Bucketed: four partitions per block, one wave each, while the batch
   // spreads thin over the partitions (<= 16 entries each on average), so
