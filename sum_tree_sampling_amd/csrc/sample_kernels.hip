@@ -325,8 +325,76 @@ __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleArgs a) {
   float ub = 0.0f;
   if (!STREAM && active) ub = a.u[b];
 
+  // One sample per wave and a top of 2^8 .. 2^10 roots: each wave keeps the
+  // whole top in registers instead of sharing an LDS copy with its block.
+  constexpr bool kWaveTop = G == 64 && TP >= 8 && TP <= 10;
   float T, pmin;
-  if (a.top_mode == kTopRebuild) {
+  uint32_t node = 1;
+  if constexpr (kWaveTop) {
+    // Lane l holds roots [C l, C l + C), sums and mins.  The nodes above
+    // them follow by pairwise adds: within the lane (lane_descent forms
+    // them as it goes), then across lanes, where after step k lane l holds
+    // the node over the 2^k aligned lanes around it (f32 addition is
+    // commutative, so both lanes of a pair get the node's value).  The walk
+    // through the cross-lane levels reads the two children of the current
+    // node from the first lane of each half (the path is wave-uniform, so
+    // these are lane reads), and the last log2(C) levels run inside the
+    // chosen lane.  Bit for bit the stored nodes, as every other top
+    // rebuild; no LDS and no barrier.
+    constexpr int C = (1 << TP) / 64;
+    const uint32_t np = 1u << TP;
+    float r[C], mr[C];
+#pragma unroll
+    for (int i = 0; i < C; i += 4) {
+      const float4 q = *reinterpret_cast<const float4*>(a.sum + np + (uint32_t)lane * C + i);
+      const float4 w = *reinterpret_cast<const float4*>(a.mn + np + (uint32_t)lane * C + i);
+      r[i] = q.x;
+      r[i + 1] = q.y;
+      r[i + 2] = q.z;
+      r[i + 3] = q.w;
+      mr[i] = w.x;
+      mr[i + 1] = w.y;
+      mr[i + 2] = w.z;
+      mr[i + 3] = w.w;
+    }
+    float x[6];
+    x[0] = pair_sum<C>(r);
+    float mm = mr[0];
+#pragma unroll
+    for (int i = 1; i < C; ++i) mm = min_f32(mm, mr[i]);
+#pragma unroll
+    for (int k = 1; k < 6; ++k) x[k] = x[k - 1] + xor_lanes(x[k - 1], k - 1);
+#pragma unroll
+    for (int k = 0; k < 5; ++k) mm = min_f32(mm, xor_lanes(mm, k));
+    const float left0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x[5]), 0));
+    const float right0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x[5]), 32));
+    T = left0 + right0;
+    pmin = min_f32(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(mm), 0)),
+                   __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mm), 32)));
+    if (STREAM && active) ub = stream_uniform(stream_word(a.seed, a.offset + b));
+    // The wave's one mass, made visibly uniform so that the walk's decisions
+    // and lane numbers stay scalar.
+    ub = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(ub)));
+    float m = ub * T;
+    if (!(m < T)) m = __uint_as_float(__float_as_uint(T) - 1u);  // largest f32 below T
+    int base = 0;  // first lane under the current node
+#pragma unroll
+    for (int k = 5; k >= 0; --k) {  // each child covers 2^k lanes
+      const float cl = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x[k]), base));
+      const float cr =
+          __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x[k]), base + (1 << k)));
+      const bool right = !(cl > m || cr == 0.0f);
+      if (right) {
+        m = m - cl;
+        base += 1 << k;
+      }
+    }
+    float lm = m, lv;
+    const int e = lane_descent<C>(r, lm, lv);
+    m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lm), base));
+    node = np + (uint32_t)(base * C + __builtin_amdgcn_readlane(e, base));
+    ub = m;  // carried to the rounds below
+  } else if (a.top_mode == kTopRebuild) {
     // Nodes [1, 2^P) from the partition roots at depth P: sums in top[],
     // mins in mtop[].  Each wave reduces a contiguous segment of the roots
     // (four segments when there are at least 256 roots, else one): a lane
@@ -463,21 +531,24 @@ __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleArgs a) {
     pmin = a.mn[1];
   }
 
-  if (STREAM && active) ub = stream_uniform(stream_word(a.seed, a.offset + b));
-  float m = ub * T;
-  if (!(m < T)) m = __uint_as_float(__float_as_uint(T) - 1u);  // largest f32 below T
-
-  uint32_t node = 1;
-  const int levels_in_lds = TP > 0 ? TP : a.top;
+  float m;
+  if constexpr (kWaveTop) {
+    m = ub;  // the mass left after the wave's walk through the top
+  } else {
+    if (STREAM && active) ub = stream_uniform(stream_word(a.seed, a.offset + b));
+    m = ub * T;
+    if (!(m < T)) m = __uint_as_float(__float_as_uint(T) - 1u);  // largest f32 below T
+    const int levels_in_lds = TP > 0 ? TP : a.top;
 #pragma unroll
-  for (int l = 0; l < levels_in_lds; ++l) {
-    const float2 c = reinterpret_cast<const float2*>(top)[node];  // children 2node, 2node+1
-    const bool right = !(c.x > m || c.y == 0.0f);
-    if (right) m = m - c.x;
-    node = 2 * node + (right ? 1u : 0u);
+    for (int l = 0; l < levels_in_lds; ++l) {
+      const float2 c = reinterpret_cast<const float2*>(top)[node];  // children 2node, 2node+1
+      const bool right = !(c.x > m || c.y == 0.0f);
+      if (right) m = m - c.x;
+      node = 2 * node + (right ? 1u : 0u);
+    }
   }
   float leaf = 0.0f;
-  if (a.nrounds == 0) leaf = top[node];
+  if (!kWaveTop && a.nrounds == 0) leaf = top[node];
 
   auto round = [&](const int R) {
     const int lg = R - LOGV;  // log2 of the lanes used this round (<= LOGG)
@@ -602,6 +673,8 @@ hipError_t launch_variant(const SampleArgs& a, hipStream_t s) {
   const unsigned grid = (unsigned)((waves + 3) / 4);
   size_t lds = 0;
   if (a.top_mode == kTopRebuild) lds = 2 * (sizeof(float) << (a.P + 1));
+  // One sample per wave over 2^8 .. 2^10 roots: the top lives in registers.
+  if (G == 64 && a.top_mode == kTopRebuild && a.P >= 8 && a.P <= 10) lds = 0;
   if (a.top_mode == kTopWhole) lds = sizeof(float) << (a.top + 1);
   bool fixed = a.nrounds == FN;
   for (int r = 0; r < a.nrounds; ++r) fixed = fixed && a.rounds[r] == FR;

@@ -453,6 +453,66 @@ def test_top_deeper_than_lds():
         compare_trees(o, g, "2^25 step %d" % step)
 
 
+# ------------------------------------------------------------ large trees
+
+@pytest.mark.parametrize("L", [23, 24])
+def test_large_tree_writers(L):
+    """Trees of 2^23 and 2^24 leaves (2^11 and 2^12 partitions): after every
+    kind of writer launch -- intake with and without priorities, a wrapping
+    intake, the scanned and the bucketed update, the fused update + intake --
+    both trees match the oracle bit for bit, and the samplers match in every
+    layout."""
+    n = 1 << L
+    say("stored top", L)
+    rng = np.random.default_rng(100 + L)
+    o = Oracle(n)
+    g = _buf(n, max_batch=65536)
+    k0 = n - 3000
+    p0 = (rng.random(k0) ** 0.6).astype(np.float32)
+    o.add(k0, prio=p0)
+    g.add(k0, prio=dev(p0))
+
+    def check(what):
+        torch.cuda.synchronize()
+        assert_bits_equal(host(g.sum_tree())[1:2 * n], o.sum_tree()[1:], what + " sum tree")
+        assert_bits_equal(host(g.min_tree())[1:2 * n], o.min_tree()[1:], what + " min tree")
+
+    def sample_all(what):
+        for mode in ("1", "2", "3"):
+            g.set_sample_lanes(LANES[mode])
+            u = rng.random(3000, dtype=np.float32)
+            u[:2] = [0.0, np.nextafter(np.float32(1), np.float32(0))]
+            compare_sample(g.sample(dev(u), beta=0.4), o.sample(u, beta=0.4),
+                           "%s mode %s" % (what, mode))
+        g.set_sample_lanes(0)
+
+    check("fill")
+    sample_all("fill")
+    o.add(2000)
+    g.add(2000)                                   # at the running max
+    check("intake at the running max")
+    pr = (rng.random(5000) * 3).astype(np.float32)
+    o.add(5000, prio=pr)
+    g.add(5000, prio=dev(pr))                     # wraps past the end, given priorities
+    check("wrapping intake")
+    for B in (200, 8192, 65536):                  # scanned, then bucketed
+        idx = rng.integers(0, n, B).astype(np.int64)
+        idx[: B // 8] = idx[B // 8: B // 4]
+        td = (rng.standard_normal(B) * 2).astype(np.float32)
+        o.update(idx, td)
+        g.update(dev(idx), dev(td))
+        check("update B=%d" % B)
+    idx = rng.integers(0, n, 300).astype(np.int64)
+    td = rng.standard_normal(300).astype(np.float32)
+    o.update(idx, td)
+    o.add(700)
+    g.update_add(dev(idx), dev(td), 700)
+    check("update + intake")
+    sample_all("after the writers")
+    assert np.float32(host(g.scalar("total"))[0]) == np.float32(o.sum_tree()[1])
+    assert np.float32(host(g.scalar("min"))[0]) == np.float32(o.min_tree()[1])
+
+
 # ------------------------------------------------------------ graph mode
 
 def _rows_np(rng, c, D):
@@ -472,6 +532,8 @@ def _rows_np(rng, c, D):
     (1 << 13, 4, 500, 700, False, True, False),    # uniform sample over a ring still filling up
     (1 << 21, 0, 512, 400, False, False, True),    # the Ape-X shard step: sample, update + intake
     (1 << 16, 5, 1024, 3000, True, False, True),   # fused, given priorities
+    (1 << 23, 0, 700, 400, False, False, True),    # 2^11 partitions, fused
+    (1 << 24, 0, 65536, 5000, True, False, False),  # 2^12 partitions, bucketed, given priorities
 ])
 def test_graph_replay(n, D, B, c, prio, uniform, fused):
     """Two whole steps (intake, sample, update) issued in graph mode, first
