@@ -136,9 +136,12 @@ def ingest_pmc(d: str) -> None:
     print(json.dumps(res, indent=1, sort_keys=True))
 
 
-def measured_traffic(workload: str, op: str):
-    """Counted HBM bytes per launch of op, or None (not profiled, or the
-    kernel sources changed since)."""
+def measured_traffic(workload: str, op: str, default_mode: bool = True):
+    """Counted HBM bytes per launch of op, or None (not profiled, the kernel
+    sources changed since, or a sampling mode other than the default one the
+    counters were taken in: other modes launch other kernels)."""
+    if not default_mode:
+        return None
     try:
         with open(TRAFFIC_FILE) as fh:
             t = json.load(fh)
@@ -212,7 +215,10 @@ def copy_calibration() -> None:
 
 
 def expected_dirty_internal(n: int, U: int) -> float:
-    """Expected distinct internal ancestors of U uniform distinct leaves."""
+    """Expected distinct internal ancestors of U leaves drawn uniformly with
+    replacement (a batch of sampled slots, duplicates included).  For U
+    distinct leaves the count is higher by under 0.2% at the workloads'
+    sizes (1.1% at 2^10 leaves)."""
     L = int(math.log2(n))
     return sum((2.0 ** l) * (1.0 - (1.0 - 2.0 ** -l) ** U) for l in range(L))
 
@@ -359,6 +365,9 @@ class Run:
         self.uniform, self.rank = mode.get("uniform", False), mode.get("rank", False)
         self.masses = mode.get("masses", "array")
         self.fused = bool(spec["intake"]) and not self.uniform and not mode.get("unfused", False)
+        # the mode the HBM counters of the traffic file are taken in
+        self.default_mode = (not W and not self.uniform and not self.rank
+                             and self.masses == "array" and not mode.get("unfused", False))
         self.spec = dict(spec, masses=self.masses, uniform=self.uniform, rank=self.rank,
                          fused=self.fused)
         self.W = W
@@ -625,7 +634,7 @@ def measure(run: Run, K: int, W: int, Kop: int, stream, graph_steps: int = 0) ->
         "step_hbm_roofline_frac": step_bytes / (ms_per_step * 1e-3) / (PEAK_HBM_GBS * 1e9),
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
-                     "traffic": measured_traffic(run.name, dom),
+                     "traffic": measured_traffic(run.name, dom, run.default_mode),
                      "bytes_per_launch": byts[dom]},
     }
     if graph_steps > 0:

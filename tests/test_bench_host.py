@@ -1,0 +1,59 @@
+"""Host-side logic of bench.py: the algorithmic byte counts the roofline
+divides by, and when a counted-traffic figure may be reported."""
+import json
+
+import numpy as np
+import pytest
+
+import bench
+import workloads
+
+
+def test_expected_dirty_internal_matches_simulation():
+    # expected number of distinct internal ancestors of U leaves drawn
+    # uniformly with replacement, against a count over random draws on a
+    # 2^10-leaf tree
+    rng = np.random.default_rng(7)
+    n, U, trials = 1 << 10, 64, 400
+    L = 10
+    counts = []
+    for _ in range(trials):
+        leaves = rng.integers(0, n, U)
+        nodes = set()
+        for leaf in leaves:
+            v = int(leaf) + n  # heap numbering: root 1, leaves n..2n-1
+            while v > 1:
+                v //= 2
+                nodes.add(v)
+        counts.append(len(nodes))
+    assert bench.expected_dirty_internal(n, U) == pytest.approx(np.mean(counts), rel=0.01)
+    # every leaf dirties the root; one leaf dirties exactly L internal nodes
+    assert bench.expected_dirty_internal(n, 1) == pytest.approx(L)
+    # many draws dirty every internal node
+    assert bench.expected_dirty_internal(n, 1 << 16) == pytest.approx(n - 1)
+
+
+def test_apex_step_bytes():
+    spec = dict(workloads.spec("apex_shard_2m"), masses="array", fused=True)
+    b = bench.algorithmic_bytes(spec)
+    assert set(b) == {"sample", "update_add"}
+    # 512 descents over 21 levels: mass in, 21 sibling pairs, index out (no
+    # weights in this workload)
+    assert not spec["weights"]
+    assert b["sample"] == 512 * (4 + 8 * 21 + 8)
+    assert sum(b.values()) == pytest.approx(0.212e6, rel=0.01)
+    sep = bench.algorithmic_bytes(dict(spec, fused=False))
+    assert sep["update"] + sep["add"] == pytest.approx(b["update_add"])
+
+
+def test_traffic_only_for_the_profiled_mode():
+    with open(bench.TRAFFIC_FILE) as fh:
+        t = json.load(fh)
+    e = t["workloads"]["apex_shard_2m"]["update_add"]["bytes"]
+    assert bench.measured_traffic("apex_shard_2m", "update_add", False) is None
+    got = bench.measured_traffic("apex_shard_2m", "update_add", True)
+    if t.get("source_sha256") == bench.kernel_source_digest():
+        assert got == pytest.approx(float(e))
+    else:
+        assert got is None
+    assert bench.measured_traffic("no_such_workload", "sample", True) is None
