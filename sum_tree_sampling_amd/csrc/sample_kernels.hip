@@ -140,7 +140,10 @@ constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v / 2); }
 // kBatch (1, 2, 4 or 8) is chosen from the wave's access count so that a
 // wave copying a few short rows issues no idle loads.  mid() runs once,
 // between the first batch's loads and its stores, so that its work overlaps
-// their trip.
+// their trip.  With one lane per sample (G = 1) a wave copies 64 samples'
+// rows alone, batch after batch: there the loads of batch k + 1 are issued
+// before the stores of batch k, so that 2 kBatch reads stay in flight and a
+// batch's stores wait only for its own loads.
 template <bool VEC, int SPW, int G, int kBatch, typename Mid>
 __device__ __forceinline__ void copy_rows(const SampleArgs& a, uint32_t wave_b0, uint32_t slot,
                                           int lane, uint32_t D, uint32_t W, Mid mid) {
@@ -163,10 +166,10 @@ __device__ __forceinline__ void copy_rows(const SampleArgs& a, uint32_t wave_b0,
 #pragma unroll
     for (int k = 0; k < SPW; ++k) few[k] = (uint32_t)__builtin_amdgcn_readlane((int)slot, k * G);
   }
-  for (uint32_t t0 = 0; t0 < total; t0 += 64 * kBatch) {
-    T buf[kBatch];
-    T* dst[kBatch];
-    bool ok[kBatch], pad[kBatch];
+  // The loads of the batch at access t0: buf receives the values, dst the
+  // output addresses, ok whether the access exists, pad whether it is a
+  // padding column.
+  auto issue = [&](uint32_t t0, T* buf, T** dst, bool* ok, bool* pad) {
 #pragma unroll
     for (int q = 0; q < kBatch; ++q) {
       const uint32_t t = t0 + q * 64 + lane;
@@ -194,10 +197,46 @@ __device__ __forceinline__ void copy_rows(const SampleArgs& a, uint32_t wave_b0,
       // accesses read column 0, so the address is always in the row store.
       buf[q] = reinterpret_cast<const T*>(src)[(pad[q] || !ok[q]) ? 0u : c];
     }
-    if (t0 == 0) mid();
+  };
+  auto store = [&](const T* buf, T* const* dst, const bool* ok, const bool* pad) {
 #pragma unroll
     for (int q = 0; q < kBatch; ++q) {
       if (ok[q]) *dst[q] = pad[q] ? T{} : buf[q];
+    }
+  };
+  if constexpr (G == 1) {
+    T buf[kBatch];
+    T* dst[kBatch];
+    bool ok[kBatch], pad[kBatch];
+    if (total > 0) {
+      issue(0, buf, dst, ok, pad);
+      mid();
+    }
+    for (uint32_t t0 = 0; t0 < total; t0 += 64 * kBatch) {
+      T nbuf[kBatch];
+      T* ndst[kBatch];
+      bool nok[kBatch], npad[kBatch];
+      const bool more = t0 + 64 * kBatch < total;  // uniform
+      if (more) issue(t0 + 64 * kBatch, nbuf, ndst, nok, npad);
+      store(buf, dst, ok, pad);
+      if (more) {
+#pragma unroll
+        for (int q = 0; q < kBatch; ++q) {
+          buf[q] = nbuf[q];
+          dst[q] = ndst[q];
+          ok[q] = nok[q];
+          pad[q] = npad[q];
+        }
+      }
+    }
+  } else {
+    for (uint32_t t0 = 0; t0 < total; t0 += 64 * kBatch) {
+      T buf[kBatch];
+      T* dst[kBatch];
+      bool ok[kBatch], pad[kBatch];
+      issue(t0, buf, dst, ok, pad);
+      if (t0 == 0) mid();
+      store(buf, dst, ok, pad);
     }
   }
   if (total == 0) mid();

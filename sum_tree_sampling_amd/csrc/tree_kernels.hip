@@ -929,8 +929,19 @@ __global__ void __launch_bounds__(kUpdThreads) update_bucket_kernel(TreePtrs t, 
     bk.ovf_n[a.ovf ^ 1] = 0u;  // the next call's overflow counter
     publish_max(0u, true, m0, max_dst);
   }
-  __syncthreads();
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // Every lane loads its entry of the wave's bucket before the count is
+  // known, so that the entries arrive together with the counts instead of
+  // one trip after them (the lanes past the count drop theirs).
+  uint32_t es = 0u, ep = 0u;
+  float et = 0.0f;
+  if (w < nparts) {
+    const uint32_t e = (part0 + w) * kBucketCap + lane;
+    es = bk.slot[e];
+    ep = bk.pos[e];
+    et = bk.td[e];
+  }
+  __syncthreads();
   bool crowded = false;
   for (int q = 0; q < nparts; ++q) crowded |= sm.mtot[q] > (uint32_t)kBucketCap;
   if (w < nparts) {
@@ -939,10 +950,9 @@ __global__ void __launch_bounds__(kUpdThreads) update_bucket_kernel(TreePtrs t, 
       SparseSmem& sp = sm.u.sp[w];
       uint32_t pb = 0u;
       if ((uint32_t)lane < m) {
-        const uint32_t e = part * kBucketCap + lane;
         const float p = collect<FULL, true>(sp, lane, t, g, part,
-                                            bk.slot[e] - (part << span_bits<FULL>(g)),
-                                            bk.pos[e], bk.td[e], m0, a.alpha, a.eps, a.p_nan);
+                                            es - (part << span_bits<FULL>(g)), ep, et, m0,
+                                            a.alpha, a.eps, a.p_nan);
         pb = __float_as_uint(p);
       }
       pb = wave_max_u32(pb);
