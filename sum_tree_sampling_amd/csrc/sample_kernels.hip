@@ -435,54 +435,94 @@ __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleArgs a) {
     ub = m;  // carried to the rounds below
   } else if (a.top_mode == kTopRebuild) {
     // Nodes [1, 2^P) from the partition roots at depth P: sums in top[],
-    // mins in mtop[].  Each wave reduces a contiguous segment of the roots
-    // (four segments when there are at least 256 roots, else one): a lane
-    // loads c consecutive roots and reduces them in registers, then the
-    // lanes' results meet through shuffles, every node formed on the way
-    // stored to LDS.  Only the joins of the four segment roots wait for a
-    // barrier.
+    // mins in mtop[].  With more than 512 roots the levels down to depth 8
+    // are reduced block-wide first, two levels per pass: a thread takes four
+    // consecutive nodes (one 16-byte access), stores them and forms their two
+    // parents and their grandparent in registers, so that a barrier separates
+    // every second level only; the first pass reads the roots from global
+    // memory.  Thread t ends holding node 2^8 + t.  Then each wave reduces a
+    // contiguous segment of depth 8 (or, with at most 512 roots, of the roots
+    // themselves, at most two per lane) in registers and lane shuffles,
+    // every node formed on the way stored to LDS.  Only the joins of the four
+    // segment roots wait for a barrier.
     const int P = TP > 0 ? TP : a.P;
     const uint32_t np = 1u << P;
     float* mtop = top + 2 * np;
     const int wv = threadIdx.x >> 6;
     const int lgw = (P >= 8) ? 2 : 0;  // log2 of the waves of the wave stage
-    // With more than 512 roots the levels down to depth Pw = 8 are reduced
-    // block-wide first (coalesced loads, conflict-free pair reads, a barrier
-    // per level), so that a lane of the wave stage starts from one node;
-    // otherwise the wave stage starts from the roots, at most two per lane.
     const int Pw = (P - lgw > 7) ? lgw + 6 : P;
     const int lgseg = Pw - lgw;                 // log2 of a wave's nodes at depth Pw
     const int lgc = lgseg > 6 ? lgseg - 6 : 0;  // log2 of nodes per lane (<= 1)
     const int lgl = lgseg - lgc;                // log2 of the lanes used
+    // Four nodes of depth d at index q (a multiple of 4): stored when they
+    // come from global memory, and their parents and grandparent formed and
+    // stored; returns the grandparent.
+    auto quad = [&](int d, uint32_t q, float4 cs, float4 cm, bool fresh, float& gm) {
+      if (fresh) {
+        *reinterpret_cast<float4*>(top + (1u << d) + q) = cs;
+        *reinterpret_cast<float4*>(mtop + (1u << d) + q) = cm;
+      }
+      const float2 ps = make_float2(cs.x + cs.y, cs.z + cs.w);
+      const float2 pm = make_float2(min_f32(cm.x, cm.y), min_f32(cm.z, cm.w));
+      *reinterpret_cast<float2*>(top + (1u << (d - 1)) + (q >> 1)) = ps;
+      *reinterpret_cast<float2*>(mtop + (1u << (d - 1)) + (q >> 1)) = pm;
+      const float gs = ps.x + ps.y;
+      gm = min_f32(pm.x, pm.y);
+      top[(1u << (d - 2)) + (q >> 2)] = gs;
+      mtop[(1u << (d - 2)) + (q >> 2)] = gm;
+      return gs;
+    };
+    float hs = 0.0f, hm = 0.0f;  // node 2^Pw + threadIdx.x, when Pw < P
     if (Pw < P) {
-      constexpr int kPer = (1 << kMaxTopBits) / kSampleThreads;
-      float ls[kPer], lm[kPer];
+      constexpr int kG = (1 << kMaxTopBits) / 4 / kSampleThreads;  // root quads per thread
+      const uint32_t nq = np >> 2;
+      float4 rs[kG], rm[kG];
 #pragma unroll
-      for (int c = 0; c < kPer; ++c) {
-        const uint32_t k = threadIdx.x + c * kSampleThreads;
-        if (k < np) {
-          ls[c] = a.sum[np + k];
-          lm[c] = a.mn[np + k];
+      for (int c = 0; c < kG; ++c) {
+        const uint32_t g = threadIdx.x + c * kSampleThreads;
+        if (g < nq) {
+          rs[c] = *reinterpret_cast<const float4*>(a.sum + np + 4 * g);
+          rm[c] = *reinterpret_cast<const float4*>(a.mn + np + 4 * g);
         }
       }
 #pragma unroll
-      for (int c = 0; c < kPer; ++c) {
-        const uint32_t k = threadIdx.x + c * kSampleThreads;
-        if (k < np) {
-          top[np + k] = ls[c];
-          mtop[np + k] = lm[c];
+      for (int c = 0; c < kG; ++c) {
+        const uint32_t g = threadIdx.x + c * kSampleThreads;
+        if (g < nq) {
+          float m2;
+          const float s2 = quad(P, 4 * g, rs[c], rm[c], true, m2);
+          if (c == 0) {  // with 2^10 roots this is node 2^8 + threadIdx.x
+            hs = s2;
+            hm = m2;
+          }
         }
       }
-      for (uint32_t width = np >> 1; width >= (1u << Pw); width >>= 1) {
+      // Down to depth 8 in LDS; each pass that reaches it leaves thread t
+      // with node 2^8 + t.
+      for (int d = P - 2; d > Pw;) {
         __syncthreads();
-        for (uint32_t h = width + threadIdx.x; h < 2 * width; h += kSampleThreads) {
-          const float2 cs = reinterpret_cast<const float2*>(top)[h];  // children 2h, 2h+1
-          const float2 cm = reinterpret_cast<const float2*>(mtop)[h];
-          top[h] = cs.x + cs.y;
-          mtop[h] = min_f32(cm.x, cm.y);
+        if (d - Pw >= 2) {
+          for (uint32_t g = threadIdx.x; g < (1u << (d - 2)); g += kSampleThreads) {
+            const float4 cs = reinterpret_cast<const float4*>(top + (1u << d))[g];
+            const float4 cm = reinterpret_cast<const float4*>(mtop + (1u << d))[g];
+            float m2;
+            const float s2 = quad(d, 4 * g, cs, cm, false, m2);
+            hs = s2;
+            hm = m2;
+          }
+          d -= 2;
+        } else {
+          for (uint32_t g = threadIdx.x; g < (1u << (d - 1)); g += kSampleThreads) {
+            const float2 cs = reinterpret_cast<const float2*>(top + (1u << d))[g];
+            const float2 cm = reinterpret_cast<const float2*>(mtop + (1u << d))[g];
+            hs = cs.x + cs.y;
+            hm = min_f32(cm.x, cm.y);
+            top[(1u << (d - 1)) + g] = hs;
+            mtop[(1u << (d - 1)) + g] = hm;
+          }
+          d -= 1;
         }
       }
-      __syncthreads();
     }
     if (wv < (1 << lgw)) {
       const uint32_t k0 = (1u << Pw) + ((uint32_t)wv << lgseg) + ((uint32_t)lane << lgc);
@@ -493,13 +533,10 @@ __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleArgs a) {
       for (int i = 0; i < 2; ++i) {
         v[i] = 0.0f;
         mv[i] = 0.0f;
-        // Each source read in its own branch (Pw < P is uniform): merged,
-        // the two become one generic load behind a wait for all memory.
         if (on && (uint32_t)i < c) {
-          if (Pw < P) {
-            v[i] = top[k0 + i];
-            mv[i] = mtop[k0 + i];
-            asm volatile("" ::"v"(v[i]), "v"(mv[i]));
+          if (Pw < P) {  // lgc == 0: the node this thread formed above
+            v[i] = hs;
+            mv[i] = hm;
           } else {
             v[i] = a.sum[k0 + i];
             mv[i] = a.mn[k0 + i];
