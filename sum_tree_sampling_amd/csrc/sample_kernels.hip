@@ -143,8 +143,10 @@ constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v / 2); }
 // their trip.  With one lane per sample (G = 1) a wave copies 64 samples'
 // rows alone, batch after batch: there the loads of batch k + 1 are issued
 // before the stores of batch k, so that 2 kBatch reads stay in flight and a
-// batch's stores wait only for its own loads.
-template <bool VEC, int SPW, int G, int kBatch, typename Mid>
+// batch's stores wait only for its own loads.  NT: the rows are read with
+// the non-temporal hint, so that a large gather streams past the caches
+// instead of evicting the tree nodes the descents and updates reuse.
+template <bool VEC, bool NT, int SPW, int G, int kBatch, typename Mid>
 __device__ __forceinline__ void copy_rows(const SampleArgs& a, uint32_t wave_b0, uint32_t slot,
                                           int lane, uint32_t D, uint32_t W, Mid mid) {
   constexpr uint32_t kW = VEC ? 4u : 1u;      // floats per access
@@ -195,7 +197,16 @@ __device__ __forceinline__ void copy_rows(const SampleArgs& a, uint32_t wave_b0,
       // Unconditional: s is clamped to a sample of the wave (a descent of an
       // inactive lane still ends on a leaf) and past-the-end or padding
       // accesses read column 0, so the address is always in the row store.
-      buf[q] = reinterpret_cast<const T*>(src)[(pad[q] || !ok[q]) ? 0u : c];
+      const uint32_t col = (pad[q] || !ok[q]) ? 0u : c;
+      if constexpr (NT && VEC) {
+        typedef float f32x4 __attribute__((ext_vector_type(4)));
+        const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src) + col);
+        buf[q] = make_float4(x.x, x.y, x.z, x.w);
+      } else if constexpr (NT) {
+        buf[q] = __builtin_nontemporal_load(src + col);
+      } else {
+        buf[q] = reinterpret_cast<const T*>(src)[col];
+      }
     }
   };
   auto store = [&](const T* buf, T* const* dst, const bool* ok, const bool* pad) {
@@ -277,8 +288,9 @@ __device__ __forceinline__ float stream_uniform(uint64_t w) {
 }
 
 // Outputs of one sample (lead: the lane of its group that writes them): the
-// index, the IS weight and, cooperatively over the wave, the row copy.
-template <int G, int SPW>
+// index, the IS weight and, cooperatively over the wave, the row copy (NT:
+// rows read with the non-temporal hint).
+template <int G, int SPW, bool NT>
 __device__ __forceinline__ void emit(const SampleArgs& a, uint32_t wave, int lane, uint32_t b,
                                      bool lead, uint32_t slot, float leaf, float pmin) {
   // The scalar fields of the sampled transition: loaded now, stored after
@@ -311,18 +323,18 @@ __device__ __forceinline__ void emit(const SampleArgs& a, uint32_t wave, int lan
     const uint32_t per_lane = (SPW * 2u * (vec ? W / 4 : W) + 63u) / 64u;  // accesses per lane
     if (vec) {
       if (per_lane <= 1)
-        copy_rows<true, SPW, G, 1>(a, wave * SPW, slot, lane, D, W, weight);
+        copy_rows<true, NT, SPW, G, 1>(a, wave * SPW, slot, lane, D, W, weight);
       else if (per_lane <= 2)
-        copy_rows<true, SPW, G, 2>(a, wave * SPW, slot, lane, D, W, weight);
+        copy_rows<true, NT, SPW, G, 2>(a, wave * SPW, slot, lane, D, W, weight);
       else if (per_lane <= 4)
-        copy_rows<true, SPW, G, 4>(a, wave * SPW, slot, lane, D, W, weight);
+        copy_rows<true, NT, SPW, G, 4>(a, wave * SPW, slot, lane, D, W, weight);
       else
-        copy_rows<true, SPW, G, 8>(a, wave * SPW, slot, lane, D, W, weight);
+        copy_rows<true, NT, SPW, G, 8>(a, wave * SPW, slot, lane, D, W, weight);
     } else {
       if (per_lane <= 2)
-        copy_rows<false, SPW, G, 2>(a, wave * SPW, slot, lane, D, W, weight);
+        copy_rows<false, NT, SPW, G, 2>(a, wave * SPW, slot, lane, D, W, weight);
       else
-        copy_rows<false, SPW, G, 8>(a, wave * SPW, slot, lane, D, W, weight);
+        copy_rows<false, NT, SPW, G, 8>(a, wave * SPW, slot, lane, D, W, weight);
     }
   }
   if (lead && a.states_out) {
@@ -689,7 +701,7 @@ __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleArgs a) {
 
   uint32_t slot = node - a.n;
   if (a.order) slot = a.order[slot];  // rank-based: the descent gave a rank
-  emit<G, SPW>(a, wave, lane, b, active && j == 0, slot, leaf, pmin);
+  emit<G, SPW, true>(a, wave, lane, b, active && j == 0, slot, leaf, pmin);
 }
 
 // Uniform sample over the filled slots ("GPU-Resident Prioritized
@@ -711,7 +723,7 @@ __global__ void __launch_bounds__(kSampleThreads) uniform_kernel(SampleArgs a) {
   const uint32_t size = a.dev_size ? *a.dev_size : a.size;
   const uint64_t hi = stream_word(a.seed, a.offset + b) >> 32;
   const uint32_t slot = (uint32_t)((hi * (uint64_t)size) >> 32);
-  emit<G, SPW>(a, wave, lane, b, b < a.B && (lane & (G - 1)) == 0, slot, 0.0f, 0.0f);
+  emit<G, SPW, false>(a, wave, lane, b, b < a.B && (lane & (G - 1)) == 0, slot, 0.0f, 0.0f);
 }
 
 template <int G, int V, bool STREAM, int FR, int FN, int TP>
