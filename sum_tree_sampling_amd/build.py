@@ -3,6 +3,7 @@
 from __future__ import annotations
 
 import os
+import re
 import subprocess
 import sys
 from concurrent.futures import ThreadPoolExecutor
@@ -25,14 +26,42 @@ FLAGS = [
 ]
 
 
+# The compiler's per-kernel resource report, read to refuse kernels that use
+# scratch memory: a kernel on the path keeps its values in registers and LDS
+# (a helper left out of line, or an array indexed through a pointer, would
+# silently move them to per-lane scratch in device memory).
+RESOURCE_FLAG = "-Rpass-analysis=kernel-resource-usage"
+
+
+def scratch_users(report: str) -> list:
+    """Kernels of a resource report with a nonzero ScratchSize."""
+    out, name = [], None
+    for ln in report.splitlines():
+        m = re.search(r"Function Name: (\S+)", ln)
+        if m:
+            name = m.group(1)
+            continue
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", ln)
+        if m and name and int(m.group(1)) > 0:
+            out.append((name, int(m.group(1))))
+    return out
+
+
 def _compile(src: str, obj: str) -> None:
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, RESOURCE_FLAG, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError("hipcc failed on %s" % src)
+    users = scratch_users(r.stderr)
+    if users:
+        raise RuntimeError("kernels of %s use scratch memory: %s" % (
+            os.path.basename(src), ", ".join("%s (%d B/lane)" % u for u in users)))
     # the host pass does not know the packed-fp32 feature; that note is expected
-    noise = [ln for ln in r.stderr.splitlines() if "packed-fp32-ops" not in ln and ln.strip()]
+    # and the resource report (remarks with their source excerpts) is read above
+    noise = [ln for ln in r.stderr.splitlines()
+             if "packed-fp32-ops" not in ln and "remark:" not in ln
+             and not re.match(r"^\s*\d*\s*\|", ln) and ln.strip()]
     if noise:
         sys.stderr.write("\n".join(noise) + "\n")
 

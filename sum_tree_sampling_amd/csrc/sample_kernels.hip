@@ -142,8 +142,12 @@ constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v / 2); }
 // between the first batch's loads and its stores, so that its work overlaps
 // their trip.  With one lane per sample (G = 1) a wave copies 64 samples'
 // rows alone, batch after batch: there the loads of batch k + 1 are issued
-// before the stores of batch k, so that 2 kBatch reads stay in flight and a
-// batch's stores wait only for its own loads.  NT: the rows are read with
+// before the stores of batch k, and those stores wait for every load in
+// flight, so they go out one trip after their own loads.  Loads and stores
+// share the wave's one memory counter: waiting only for batch k's loads
+// would also wait for batch k - 1's stores, issued just before them, and is
+// slower (2^24 leaves, 65536 rows of 128 floats: 36.2 against 34.1 us).
+// Elsewhere the wave's few batches go one after the other.  NT: the rows are read with
 // the non-temporal hint, so that a large gather streams past the caches
 // instead of evicting the tree nodes the descents and updates reuse.
 template <bool VEC, bool NT, int SPW, int G, int kBatch, typename Mid>
@@ -241,13 +245,53 @@ __device__ __forceinline__ void copy_rows(const SampleArgs& a, uint32_t wave_b0,
       }
     }
   } else {
+    // Written out in the loop: captured by a lambda, the slots in few[]
+    // would live in scratch memory.
     for (uint32_t t0 = 0; t0 < total; t0 += 64 * kBatch) {
       T buf[kBatch];
       T* dst[kBatch];
       bool ok[kBatch], pad[kBatch];
-      issue(t0, buf, dst, ok, pad);
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q) {
+        const uint32_t t = t0 + q * 64 + lane;
+        uint32_t s = t / (2u * per_row);
+        if (s >= SPW) s = SPW - 1;
+        uint32_t slot_s;
+        if constexpr (SPW <= 4) {
+          slot_s = few[0];
+#pragma unroll
+          for (int k = 1; k < SPW; ++k)
+            if (s == (uint32_t)k) slot_s = few[k];
+        } else {
+          slot_s = (uint32_t)__shfl((int)slot, (int)s * G);
+        }
+        const uint32_t bs = wave_b0 + s;
+        ok[q] = t < total && bs < a.B;
+        const uint32_t rem = t - s * 2u * per_row;
+        const bool nxt = rem >= per_row;
+        const uint32_t c = nxt ? rem - per_row : rem;
+        pad[q] = c >= per_src;
+        const float* src = (nxt ? src_n : src_s) + (uint64_t)slot_s * D;
+        dst[q] = reinterpret_cast<T*>((nxt ? dst_n : dst_s) + (uint64_t)bs * W) + c;
+        // Unconditional: s is clamped to a sample of the wave and
+        // past-the-end or padding accesses read column 0.
+        const uint32_t col = (pad[q] || !ok[q]) ? 0u : c;
+        if constexpr (NT && VEC) {
+          typedef float f32x4 __attribute__((ext_vector_type(4)));
+          const f32x4 x =
+              __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src) + col);
+          buf[q] = make_float4(x.x, x.y, x.z, x.w);
+        } else if constexpr (NT) {
+          buf[q] = __builtin_nontemporal_load(src + col);
+        } else {
+          buf[q] = reinterpret_cast<const T*>(src)[col];
+        }
+      }
       if (t0 == 0) mid();
-      store(buf, dst, ok, pad);
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q) {
+        if (ok[q]) *dst[q] = pad[q] ? T{} : buf[q];
+      }
     }
   }
   if (total == 0) mid();

@@ -57,3 +57,19 @@ def test_traffic_only_for_the_profiled_mode():
     else:
         assert got is None
     assert bench.measured_traffic("no_such_workload", "sample", True) is None
+
+
+def test_build_refuses_scratch():
+    # the build reads the compiler's per-kernel resource report and refuses
+    # kernels that keep values in scratch memory
+    from sum_tree_sampling_amd import build
+    report = "\n".join([
+        "x.hip:10:1: remark: Function Name: _Z1av [-Rpass-analysis=kernel-resource-usage]",
+        "x.hip:10:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]",
+        "   10 | __global__ void a() {",
+        "      | ^",
+        "x.hip:20:1: remark: Function Name: _Z1bv [-Rpass-analysis=kernel-resource-usage]",
+        "x.hip:20:1: remark:     ScratchSize [bytes/lane]: 32 [-Rpass-analysis=kernel-resource-usage]",
+    ])
+    assert build.scratch_users(report) == [("_Z1bv", 32)]
+    assert build.scratch_users("") == []
