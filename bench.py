@@ -26,8 +26,8 @@ operation moves as the hardware counts them (rocprofv3 FETCH_SIZE and
 WRITE_SIZE per dispatch, each scaled by what the same counter reads for a
 plain device copy of known size).  The counters cannot be read from inside
 this process, so they are taken in separate profiler runs and ingested into
-profiles/hbm_traffic.json together with a digest of the kernel sources; the
-figure is reported only while the sources still match that digest.
+profiles/hbm_traffic.json together with a digest of the built library; the
+figure is reported only while libper.so still matches that digest.
     python3 bench.py --copy-calibration      # the copy the counters are scaled by
     python3 bench.py --ingest-pmc DIR        # DIR holds the rocprofv3 csv runs
 """
@@ -50,7 +50,7 @@ import workloads  # noqa: E402
 
 METRIC = "PER samples/s + priority updates/s at 2^21 leaves (B=512); % of HBM roofline"
 PEAK_HBM_GBS = 8000.0
-CSRC = os.path.join(ROOT, "sum_tree_sampling_amd", "csrc")
+LIBRARY = os.path.join(ROOT, "sum_tree_sampling_amd", "libper.so")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 CALIB_FLOATS = 64 << 20          # 256 MiB copied by --copy-calibration
 CALIB_REPS = 3
@@ -64,15 +64,12 @@ OP_KERNELS = {
 }
 
 
-def kernel_source_digest() -> str:
-    """sha256 over the HIP sources and headers the counted kernels are built
-    from (the rank sort's file is left out: none of them comes from it)."""
+def library_digest() -> str:
+    """sha256 of the built library whose kernels the counters were taken on
+    (the build is deterministic: the same sources give the same file)."""
     h = hashlib.sha256()
-    for f in sorted(os.listdir(CSRC)):
-        if f.endswith((".hip", ".h")) and f != "rank_kernels.hip":
-            h.update(f.encode())
-            with open(os.path.join(CSRC, f), "rb") as fh:
-                h.update(fh.read())
+    with open(LIBRARY, "rb") as fh:
+        h.update(fh.read())
     return h.hexdigest()
 
 
@@ -109,7 +106,7 @@ def ingest_pmc(d: str) -> None:
         reported = float(np.median(rows[copy[0]]))
         calib[c] = {"kernel": copy[0], "reported_kib": reported, "true_kib": true_kib,
                     "factor": true_kib / reported}
-    res = {"source_sha256": kernel_source_digest(), "calibration": calib, "workloads": {}}
+    res = {"library_sha256": library_digest(), "calibration": calib, "workloads": {}}
     for w in workloads.WORKLOADS:
         paths = [os.path.join(d, "%s_%s" % (w, c), "run_counter_collection.csv") for c in counters]
         if not all(os.path.exists(p) for p in paths):
@@ -137,9 +134,10 @@ def ingest_pmc(d: str) -> None:
 
 
 def measured_traffic(workload: str, op: str, default_mode: bool = True):
-    """Counted HBM bytes per launch of op, or None (not profiled, the kernel
-    sources changed since, or a sampling mode other than the default one the
-    counters were taken in: other modes launch other kernels)."""
+    """Counted HBM bytes per launch of op, or None (not profiled, the library
+    rebuilt from changed sources since, or a sampling mode other than the
+    default one the counters were taken in: other modes launch other
+    kernels)."""
     if not default_mode:
         return None
     try:
@@ -147,7 +145,10 @@ def measured_traffic(workload: str, op: str, default_mode: bool = True):
             t = json.load(fh)
     except (OSError, ValueError):
         return None
-    if t.get("source_sha256") != kernel_source_digest():
+    try:
+        if t.get("library_sha256") != library_digest():
+            return None
+    except OSError:
         return None
     e = t.get("workloads", {}).get(workload, {}).get(op)
     return None if e is None else float(e["bytes"])

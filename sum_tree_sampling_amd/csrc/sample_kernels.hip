@@ -10,13 +10,15 @@
 //
 // Layout of the work: a group of G lanes (G = 16: four samples per wave;
 // G = 1: one lane per sample; G = 64: one wave per sample) carries one
-// sample.  The top of the tree is walked in LDS: each block first rebuilds the
-// 2^P - 1 nodes above the update partitions from the 2^P partition roots (one
-// coalesced load), which also gives it the total and the min priority.  The
-// rebuilt nodes stay in LDS: the stored ones are refreshed only by
-// top_kernel (per_flush, or before a sampler that reads them from memory).
-// (Trees of at most 2^10 leaves are staged whole.)  The remaining levels are covered in
-// rounds: a round of R levels below node c loads the 2^R contiguous
+// sample.  The top of the tree is walked on chip: each block first rebuilds
+// the 2^P - 1 nodes above the update partitions from the 2^P partition roots
+// (coalesced loads), which also gives it the total and the min priority --
+// in LDS, or, with one sample per wave over 2^8 .. 2^10 roots, in each
+// wave's registers.  The rebuilt nodes stay on chip: the stored ones are
+// refreshed only by top_kernel (per_flush, or before a sampler that reads
+// them from memory).  (Trees of at most 2^10 leaves are staged whole.)  The
+// remaining levels are covered in rounds: a round of R levels below node c
+// loads the 2^R contiguous
 // descendants of c at depth +R (G lanes x V values, 16-byte vector loads),
 // rebuilds the R-1 intermediate levels by pairwise adds -- bit-identical to
 // the stored nodes, since every stored node is exactly the f32 sum of its
@@ -25,9 +27,10 @@
 //
 // Weights ("GPU-Resident Prioritized Experience Replay", section "Sampling
 // Kernels"): w = (N*P(i))^-beta normalised by the weight of the min-tree root
-// priority; N and the total cancel, so w = (p_i / p_min)^-beta, in f64.  Rows are copied by the whole wave, 16 bytes per lane per
-// access, straight into the caller's buffers ("True Single-Graph
-// Implementation Plan", Task 3).
+// priority; N and the total cancel, so w = (p_i / p_min)^-beta, in f64.
+// Rows are copied by the whole wave, 16 bytes per lane per access, straight
+// into the caller's buffers ("True Single-Graph Implementation Plan", Task
+// 3).
 
 #include <type_traits>
 

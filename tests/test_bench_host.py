@@ -52,7 +52,7 @@ def test_traffic_only_for_the_profiled_mode():
     e = t["workloads"]["apex_shard_2m"]["update_add"]["bytes"]
     assert bench.measured_traffic("apex_shard_2m", "update_add", False) is None
     got = bench.measured_traffic("apex_shard_2m", "update_add", True)
-    if t.get("source_sha256") == bench.kernel_source_digest():
+    if t.get("library_sha256") == bench.library_digest():
         assert got == pytest.approx(float(e))
     else:
         assert got is None
