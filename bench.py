@@ -608,6 +608,15 @@ def pct(t: np.ndarray) -> dict:
     return {q: float(np.percentile(t, v)) for q, v in (("p10", 10), ("p50", 50), ("p90", 90))}
 
 
+def central_mean(t: np.ndarray) -> float:
+    """Mean of the values between the 10th and 90th percentile: a few steps
+    whose timing events are held up read several times the kernel's span,
+    and the plain mean then lies above the kernel durations a profiler's
+    trace reports for the same kernels."""
+    lo, hi = np.percentile(t, [10, 90])
+    return float(t[(t >= lo) & (t <= hi)].mean())
+
+
 def measure(run: Run, K: int, W: int, Kop: int, stream, graph_steps: int = 0) -> dict:
     """The headline pass and the per-op passes of one workload."""
     run.run_steps(0, W, stream.cuda_stream)
@@ -616,7 +625,7 @@ def measure(run: Run, K: int, W: int, Kop: int, stream, graph_steps: int = 0) ->
     base = W + K
     kt = run.kernel_times(base, Kop, stream)
     br = run.bracketed_times(base, min(K, Kop), stream)
-    op_avg = {op: float(t.mean()) for op, t in kt.items()}
+    op_avg = {op: central_mean(t) for op, t in kt.items()}
     byts = algorithmic_bytes(run.spec)
     dom = max(op_avg, key=op_avg.get)
     achieved = byts[dom] / (op_avg[dom] * 1e-3) / 1e9
@@ -628,6 +637,7 @@ def measure(run: Run, K: int, W: int, Kop: int, stream, graph_steps: int = 0) ->
         "samples_per_s": B / (op_avg["sample"] * 1e-3),
         "updates_per_s": None if upd is None else B / (op_avg[upd] * 1e-3),
         "op_ms_avg": op_avg,
+        "op_ms_mean": {op: float(t.mean()) for op, t in kt.items()},
         "op_ms_kernel": {op: pct(t) for op, t in kt.items()},
         "op_ms_bracketed": {op: pct(t) for op, t in br.items()},
         "op_steps": Kop,

@@ -73,3 +73,11 @@ def test_build_refuses_scratch():
     ])
     assert build.scratch_users(report) == [("_Z1bv", 32)]
     assert build.scratch_users("") == []
+
+
+def test_central_mean():
+    # the mean of the values between the 10th and 90th percentile: outliers
+    # at either end do not move it
+    t = np.concatenate([np.full(90, 4.0), np.full(10, 40.0)])
+    assert bench.central_mean(t) == pytest.approx(4.0)
+    assert bench.central_mean(np.arange(1, 101, dtype=float)) == pytest.approx(50.5, abs=0.6)
