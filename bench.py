@@ -609,11 +609,11 @@ def pct(t: np.ndarray) -> dict:
 
 
 def central_mean(t: np.ndarray) -> float:
-    """Mean of the values between the 10th and 90th percentile: a few steps
-    whose timing events are held up read several times the kernel's span,
-    and the plain mean then lies above the kernel durations a profiler's
-    trace reports for the same kernels."""
-    lo, hi = np.percentile(t, [10, 90])
+    """Mean of the values between the 25th and 75th percentile: steps whose
+    timing events are held up (more than a tenth of them in some runs) read
+    twice the kernel's span or more, and the plain mean then lies above the
+    kernel durations a profiler's trace reports for the same kernels."""
+    lo, hi = np.percentile(t, [25, 75])
     return float(t[(t >= lo) & (t <= hi)].mean())
 
 

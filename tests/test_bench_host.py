@@ -76,8 +76,8 @@ def test_build_refuses_scratch():
 
 
 def test_central_mean():
-    # the mean of the values between the 10th and 90th percentile: outliers
+    # the mean of the values between the 25th and 75th percentile: outliers
     # at either end do not move it
-    t = np.concatenate([np.full(90, 4.0), np.full(10, 40.0)])
+    t = np.concatenate([np.full(80, 4.0), np.full(20, 40.0)])
     assert bench.central_mean(t) == pytest.approx(4.0)
     assert bench.central_mean(np.arange(1, 101, dtype=float)) == pytest.approx(50.5, abs=0.6)
