@@ -426,6 +426,67 @@ def test_scalars_and_errors():
     assert float(host(g.scalar("max_priority"))[0]) == 1.0
 
 
+def test_time_next():
+    """per_time_next: the next call's kernels (one or two launches) run between
+    the caller's events and give the same trees and outputs as an untimed
+    call; the request is dropped after that call."""
+    from sum_tree_sampling_amd import per
+    n, D = 1 << 20, 8  # 256 partitions: an update of 8192 entries is bucketed
+    say("time_next", n)
+    rng = np.random.default_rng(11)
+    bufs = [_buf(n, D, max_batch=1 << 15) for _ in range(2)]
+    p0 = (rng.random(n) ** 0.6).astype(np.float32)
+    rows = [rng.standard_normal((n, D)).astype(np.float32) for _ in range(2)]
+    ac = rng.integers(0, 3, n).astype(np.uint32)
+    rw = rng.standard_normal(n).astype(np.float32)
+    dn = (rng.random(n) < 0.1).astype(np.uint8)
+    for g in bufs:
+        g.add(n, dev(rows[0]), dev(rows[1]), dev(ac), dev(rw), dev(dn), prio=dev(p0))
+    u = dev(rng.random(777, dtype=np.float32))
+    small = (dev(rng.integers(0, n, 300).astype(np.int64)),
+             dev(rng.standard_normal(300).astype(np.float32)))
+    large = (dev(rng.integers(0, n, 8192).astype(np.int64)),   # bucketed: two launches
+             dev(rng.standard_normal(8192).astype(np.float32)))
+    ops = [("sample", lambda g: g.sample(u, beta=0.4, rows=True)),
+           ("update", lambda g: g.update(*small)),
+           ("bucketed update", lambda g: g.update(*large)),
+           ("add", lambda g: g.add(100, dev(rows[0][:100]), dev(rows[1][:100]), dev(ac[:100]),
+                                   dev(rw[:100]), dev(dn[:100])))]
+    for what, op in ops:
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()  # torch creates an event when it is first recorded
+        b.record()
+        torch.cuda.synchronize()
+        per.per_time_next(a, b)
+        timed = op(bufs[0])
+        plain = op(bufs[1])
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b)
+        assert 0.0 < ms < 100.0, "%s: span %.4f ms" % (what, ms)
+        if isinstance(timed, dict):
+            for k in timed:
+                assert_bits_equal(host(timed[k]), host(plain[k]), what + " " + k)
+        for t0, t1, tree in ((bufs[0].sum_tree(), bufs[1].sum_tree(), "sum"),
+                             (bufs[0].min_tree(), bufs[1].min_tree(), "min")):
+            assert_bits_equal(host(t0), host(t1), "%s %s tree" % (what, tree))
+    # a request is dropped with the call that follows it, whatever it returns
+    a = torch.cuda.Event(enable_timing=True)
+    a.record()
+    torch.cuda.synchronize()
+    per.per_time_next(a, None)
+    with pytest.raises(per.PerError):  # B past max_batch
+        bufs[0].update(dev(np.zeros((1 << 15) + 1, np.int64)),
+                       dev(np.zeros((1 << 15) + 1, np.float32)))
+    c = torch.cuda.Event(enable_timing=True)
+    c.record()
+    bufs[0].update(*small)  # untimed: must not record the event again
+    torch.cuda.synchronize()
+    assert a.elapsed_time(c) >= 0.0  # a still holds its first record, before c
+    for g in bufs:
+        g.close()
+
+
 def test_top_deeper_than_lds():
     """2^25 leaves: 2^13 partitions, so the levels above them are rebuilt by
     the one-block top kernel through global memory before sampling."""
