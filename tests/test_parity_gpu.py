@@ -773,6 +773,62 @@ def test_update_add(n, D, B, c, prio, fill):
                            "update_add step %d sample" % step, rows=True)
 
 
+@pytest.mark.parametrize("lo,c", [
+    (1, 4094),     # all but the partition's first and last leaf
+    (2047, 2),     # across the middle
+    (100, 1),      # one leaf
+    (4095, 1),     # the last leaf: left siblings only
+    (0, 37),       # from the first leaf: right siblings only
+    (1234, 777),
+    (3000, 1096),  # up to the last leaf
+])
+def test_update_add_boundary_siblings(lo, c):
+    """A fused update and intake at the running max whose batch repairs the
+    nodes the intake's climb takes as its run's boundary siblings: entries
+    under every such sibling, at every height and on both sides, some under
+    the same sibling or at the same leaf, plus entries inside the run
+    (overwritten by the intake) and in other partitions; trees bit for bit
+    with the oracle's update then intake."""
+    say("update_add boundary siblings", lo, c)
+    n, span, part = 1 << 16, 1 << 12, 5
+    rng = np.random.default_rng(lo * 7919 + c)
+    o = Oracle(n, 0)
+    g = _buf(n, 0, max_batch=512)
+    p0 = (rng.random(n) * 2).astype(np.float32)
+    o.add(n, prio=p0)
+    g.add(n, prio=dev(p0))
+    for step in range(3):
+        # move the ring's cursor to the run's first slot
+        shift = (part * span + lo - o.cursor) % n
+        if shift:
+            pr = (rng.random(shift) * 2).astype(np.float32)
+            o.add(shift, prio=pr)
+            g.add(shift, prio=dev(pr))
+        assert o.cursor == part * span + lo
+        a, b = lo, lo + c - 1  # the run's first and last offset in the partition
+        picks = []
+        for h in range(12):
+            if (a >> h) & 1:  # left sibling of height h
+                s0 = ((a >> h) - 1) << h
+                picks += list(rng.integers(s0, s0 + (1 << h), 1 + (h % 3 == 1)))
+            if not (b >> h) & 1:  # right sibling of height h
+                s0 = ((b >> h) + 1) << h
+                picks += list(rng.integers(s0, s0 + (1 << h), 1 + (h % 3 == 2)))
+        picks += list(rng.integers(a, b + 1, 3))           # inside the run
+        picks = [part * span + x for x in picks]
+        picks += picks[:4]                                  # repeats: the last one wins
+        picks += list(rng.integers(0, n, 40))               # other partitions
+        idx = np.array(picks, dtype=np.int64)
+        rng.shuffle(idx)
+        td = (rng.standard_normal(len(idx)) * 2).astype(np.float32)
+        if step == 1:
+            td[rng.integers(0, len(idx), 2)] = np.nan
+        o.update(idx, td)
+        o.add(c)
+        g.update_add(dev(idx), dev(td), c)
+        compare_trees(o, g, "boundary siblings lo %d c %d step %d" % (lo, c, step))
+
+
 @pytest.mark.parametrize("alpha,eps,kind", [
     (0.6, 1e-6, "near ties"),      # several entries within a few ulps of the largest |td|
     (0.6, 1e-6, "no finite td"),   # only NaN and infinite TD errors
