@@ -203,6 +203,88 @@ def latency_floor() -> dict:
     return res
 
 
+STAMPS_LIB = os.path.join(ROOT, "sum_tree_sampling_amd", "libper_stamps.so")
+STAMP_SLOTS = 16  # phases per block (include/per_stamps.h)
+
+
+def step_phases(raw: np.ndarray) -> dict:
+    """Phase times, in µs from the first block's start, of one launch of the
+    fused update + intake kernel, from its stamps (libper_stamps.so; slots as
+    in include/per_stamps.h).  raw: [blocks, 16] 100 MHz clock values, 0
+    where nothing was stored; values below the launch's first start are a
+    launch before's and are dropped.  Blocks that stored slot 3 meet the ring
+    range (the intake's); the others end at their repair.  Repair phases are
+    taken over the blocks that sorted entries."""
+    t = raw.astype(np.float64)
+    t0 = t[:, 0][t[:, 0] > 0].min()
+    t = np.where(t >= t0, (t - t0) / 100.0, np.nan)
+    intake = ~np.isnan(t[:, 3])
+    end = np.fmax(t[:, 2], t[:, 5])
+    o = ~intake
+    rep = o & ~np.isnan(t[:, 14])
+    res = {
+        "span": float(np.nanmax(end)),
+        "others_end_p50": float(np.nanmedian(end[o])),
+        "others_end_max": float(np.nanmax(end[o])),
+        "scan_wave0_p50": float(np.nanmedian(t[o, 1])),
+        "scan_all_waves_p50": float(np.nanmedian(np.nanmax(t[o][:, [1, 10, 11, 12]], axis=1))),
+        "repair_start_p50": float(np.nanmedian(t[o, 8])),
+        "repair_p50": float(np.nanmedian(t[rep, 2] - t[rep, 8])),
+        "repair_sort_p50": float(np.nanmedian(t[rep, 13] - t[rep, 8])),
+        "repair_lds_p50": float(np.nanmedian(t[rep, 14] - t[rep, 13])),
+        "repair_chain_p50": float(np.nanmedian(t[rep, 2] - t[rep, 14])),
+    }
+    if intake.any():
+        b = np.flatnonzero(intake)[np.nanargmax(end[intake])]
+        for k, name in ((1, "scan"), (2, "repair_end"), (3, "boundary_loads"), (4, "barrier"),
+                        (5, "climb_end"), (6, "batch_max")):
+            res["intake_" + name] = float(t[b, k])
+        res["intake_after_others"] = float(end[b] - np.nanmax(end[o]))
+    return res
+
+
+def phase_stamps(workload: str, groups: int) -> dict:
+    """The fused update + intake kernel's phases (step_phases) over `groups`
+    launches, each the last of three whole steps after the stamps were
+    cleared, with the phase-stamped build in place of libper.so: p10, p50 and
+    p90 of each figure over the launches."""
+    import ctypes
+
+    import torch
+    from sum_tree_sampling_amd import per
+    if not os.path.exists(STAMPS_LIB):
+        raise SystemExit("libper_stamps.so not built: run sum_tree_sampling_amd.build.build()")
+    per._lib = per.load(STAMPS_LIB)
+    lib = per._lib
+    lib.per_stamps_clear.argtypes = [ctypes.c_void_p]
+    lib.per_stamps_clear.restype = ctypes.c_int
+    lib.per_stamps_read.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_void_p]
+    lib.per_stamps_read.restype = ctypes.c_int
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    warm, per_group = 50, 3
+    run = Run(workload, warm + per_group * groups, {}, dev)
+    if "update_add" not in run.ops:
+        raise SystemExit("--phase-stamps needs a workload whose step fuses update and intake")
+    sp = torch.cuda.current_stream().cuda_stream
+    run.run_steps(0, warm, sp)
+    torch.cuda.synchronize()
+    nb = min(max(run.n >> 12, 1), 4096)  # the kernel's tree blocks (partitions)
+    buf = np.zeros(4096 * STAMP_SLOTS, np.uint64)
+    rows = []
+    for gi in range(groups):
+        if lib.per_stamps_clear(sp) != 0:
+            raise RuntimeError("per_stamps_clear failed")
+        run.run_steps(warm + per_group * gi, per_group, sp)
+        if lib.per_stamps_read(ctypes.c_void_p(buf.ctypes.data), buf.size, sp) != 0:
+            raise RuntimeError("per_stamps_read failed")
+        rows.append(step_phases(buf.reshape(4096, STAMP_SLOTS)[:nb]))
+    run.close()
+    keys = sorted({k for r in rows for k in r})
+    return {k: [round(float(np.percentile([r[k] for r in rows if k in r], q)), 3)
+                for q in (10, 50, 90)] for k in keys}
+
+
 def copy_calibration() -> None:
     """A plain device-to-device copy of CALIB_FLOATS f32, CALIB_REPS times."""
     import torch
@@ -698,12 +780,20 @@ def main():
                     help="only run the plain copy the HBM counters are scaled by")
     ap.add_argument("--ingest-pmc", metavar="DIR",
                     help="only write profiles/hbm_traffic.json from rocprofv3 runs in DIR")
+    ap.add_argument("--phase-stamps", type=int, default=0, metavar="LAUNCHES",
+                    help="only print the fused update + intake kernel's per-block phase times "
+                         "over LAUNCHES launches (libper_stamps.so)")
     args = ap.parse_args()
     if args.ingest_pmc:
         ingest_pmc(args.ingest_pmc)
         return
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.phase_stamps:
+        print(json.dumps({"workload": args.workload, "launches": args.phase_stamps,
+                          "unit": "us (p10, p50, p90)",
+                          "phases": phase_stamps(args.workload, args.phase_stamps)}), flush=True)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the sum tree runs on a single device "

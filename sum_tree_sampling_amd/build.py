@@ -1,5 +1,6 @@
-"""Compile the HIP library (libper.so) and the latency probe
-(libper_probe.so) for gfx950, in-tree, with hipcc."""
+"""Compile the HIP library (libper.so), the latency probe (libper_probe.so)
+and the library's phase-stamped measurement build (libper_stamps.so) for
+gfx950, in-tree, with hipcc."""
 from __future__ import annotations
 
 import os
@@ -14,6 +15,8 @@ LIB = os.path.join(HERE, "libper.so")
 SOURCES = ["per_api.hip", "tree_kernels.hip", "sample_kernels.hip", "rank_kernels.hip"]
 PROBE_SRC = os.path.join(HERE, "probe", "latency_probe.hip")
 PROBE_LIB = os.path.join(HERE, "libper_probe.so")
+STAMPS_LIB = os.path.join(HERE, "libper_stamps.so")
+STAMPED = "tree_kernels.hip"  # the source whose kernels carry the phase stamps
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # IEEE f32 arithmetic as written: no contraction into FMA, no fast-math, no
@@ -47,8 +50,8 @@ def scratch_users(report: str) -> list:
     return out
 
 
-def _compile(src: str, obj: str) -> None:
-    cmd = [HIPCC, *FLAGS, RESOURCE_FLAG, "-c", src, "-o", obj]
+def _compile(src: str, obj: str, defines: tuple = ()) -> None:
+    cmd = [HIPCC, *FLAGS, *["-D" + d for d in defines], RESOURCE_FLAG, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
@@ -67,15 +70,22 @@ def _compile(src: str, obj: str) -> None:
 
 
 def build() -> str:
-    """Compile every source and link libper.so (and libper_probe.so) next to
+    """Compile every source and link libper.so, libper_probe.so and
+    libper_stamps.so (libper.so with PER_PHASE_STAMPS in STAMPED) next to
     this file."""
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
     srcs = [os.path.join(CSRC, s) for s in SOURCES] + [PROBE_SRC]
     objs = [os.path.join(objdir, os.path.basename(s).replace(".hip", ".o")) for s in srcs]
-    with ThreadPoolExecutor(max_workers=len(srcs)) as ex:
-        list(ex.map(lambda so: _compile(*so), zip(srcs, objs)))
-    for lib, lib_objs in ((LIB, objs[:-1]), (PROBE_LIB, objs[-1:])):
+    stamped_obj = os.path.join(objdir, STAMPED.replace(".hip", "_stamps.o"))
+    jobs = [(s, o, ()) for s, o in zip(srcs, objs)]
+    jobs.append((os.path.join(CSRC, STAMPED), stamped_obj, ("PER_PHASE_STAMPS",)))
+    with ThreadPoolExecutor(max_workers=len(jobs)) as ex:
+        list(ex.map(lambda job: _compile(*job), jobs))
+    lib_objs = objs[:-1]
+    stamps_objs = [stamped_obj if os.path.basename(o) == STAMPED.replace(".hip", ".o") else o
+                   for o in lib_objs]
+    for lib, lib_objs in ((LIB, lib_objs), (PROBE_LIB, objs[-1:]), (STAMPS_LIB, stamps_objs)):
         tmp = lib + ".tmp"
         cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *lib_objs]
         subprocess.check_call(cmd)

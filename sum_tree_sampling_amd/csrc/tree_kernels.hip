@@ -41,6 +41,42 @@
 #include "lanes.h"
 #include "per_internal.h"
 
+// Phase stamps of the update kernels, in the measurement build only
+// (libper_stamps.so, PER_PHASE_STAMPS defined): lane 0 of wave w of block b
+// stores the 100 MHz real-time clock at the end of phase k into
+// per_phase_stamps[b * kStampPhases + k] (phases: include/per_stamps.h).
+// Each stamp waits for its own scalar read of the clock.  In the product
+// build the stamps are empty statements.
+#ifdef PER_PHASE_STAMPS
+constexpr int kStampBlocks = 4096, kStampPhases = 16;
+__device__ unsigned long long per_phase_stamps[kStampBlocks * kStampPhases];
+#define PER_STAMP(w, k)                                                        \
+  do {                                                                         \
+    if (threadIdx.x == 64u * (w) && blockIdx.x < (unsigned)kStampBlocks)       \
+      per_phase_stamps[blockIdx.x * kStampPhases + (k)] = __builtin_amdgcn_s_memrealtime(); \
+  } while (0)
+
+extern "C" int per_stamps_clear(hipStream_t stream) {
+  void* p = nullptr;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(per_phase_stamps)) != hipSuccess) return -4;
+  return hipMemsetAsync(p, 0, sizeof(per_phase_stamps), stream) == hipSuccess ? 0 : -4;
+}
+
+extern "C" int per_stamps_read(unsigned long long* out, long long count, hipStream_t stream) {
+  if (!out || count < 0 || count > (long long)(kStampBlocks * kStampPhases)) return -1;
+  void* p = nullptr;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(per_phase_stamps)) != hipSuccess) return -4;
+  if (hipMemcpyAsync(out, p, (size_t)count * sizeof(unsigned long long), hipMemcpyDeviceToHost,
+                     stream) != hipSuccess)
+    return -4;
+  return hipStreamSynchronize(stream) == hipSuccess ? 0 : -4;
+}
+#else
+#define PER_STAMP(w, k) \
+  do {                  \
+  } while (0)
+#endif
+
 namespace per {
 namespace {
 
@@ -353,6 +389,7 @@ __device__ __forceinline__ void wave_update(SparseSmem& sp, const TreePtrs& t, c
   const uint64_t key = sp.key[src];
   const uint32_t off = (uint32_t)(key >> 32);
   const float p = sp.pval[src];
+  PER_STAMP(0, 13);
   const uint32_t next_off = next_lane(off);  // lane m - 1 does not look at it
   const bool win = in && (lane == m - 1 || next_off != off);
   float ps[kMaxSpanBits], pm[kMaxSpanBits];
@@ -361,6 +398,7 @@ __device__ __forceinline__ void wave_update(SparseSmem& sp, const TreePtrs& t, c
     ps[k] = sp.sib_s[src][k];
     pm[k] = sp.sib_m[src][k];
   }
+  PER_STAMP(0, 14);
   sparse_chain<FULL>(t, g, part, m, win, in ? off : 0u, p, ps, pm);
 }
 
@@ -644,6 +682,7 @@ __device__ __forceinline__ void uniform_range(const TreePtrs& t, const Geom& g, 
         t.mn[pb] = oRm;
       }
     }
+    PER_STAMP(0, 5);
   }
   // The leaves and the interior nodes, by the other waves, while the first
   // wave climbs.
@@ -840,7 +879,12 @@ __device__ __forceinline__ bool scan_update(SM& sm, const TreePtrs& t, const Geo
       }
     }
   }
+  PER_STAMP(0, 1);
+  PER_STAMP(1, 10);
+  PER_STAMP(2, 11);
+  PER_STAMP(3, 12);
   __syncthreads();
+  PER_STAMP(0, 8);
   if (threadIdx.x == 64) publish_max(sm.bmax, blockIdx.x == 0, m0, max_dst);
   const int w = threadIdx.x >> 6;
   bool crowded = false;
@@ -849,6 +893,7 @@ __device__ __forceinline__ bool scan_update(SM& sm, const TreePtrs& t, const Geo
     const int m = sm.count[w];
     if (m > 0 && m <= kSparseMax) wave_update<FULL>(sm.u.sp[w], t, g, part0 + w, m);
   }
+  PER_STAMP(0, 2);
   if (!crowded) return false;
   // The dense rebuild reuses the sparse areas: every wave is done with them.
   __syncthreads();
@@ -1317,6 +1362,8 @@ __global__ void __launch_bounds__(kUpdThreads) update_add_kernel(TreePtrs t, Geo
   // one dependent trip each.
   asm volatile("" ::"s"(t.ctrl), "s"(a.idx), "s"(a.td), "s"(a.B), "s"(a.src), "s"(b.cursor),
                "s"(b.count), "s"(b.size), "s"(b.ring.dev), "s"(b.last), "s"(g.n), "s"(g.S));
+  PER_STAMP(0, 0);
+  PER_STAMP(1, 7);
   uint32_t cursor, size;
   ring_state(t, b, cursor, size);
   commit_ring(t, g, b, cursor, size);
@@ -1354,10 +1401,13 @@ __global__ void __launch_bounds__(kUpdThreads) update_add_kernel(TreePtrs t, Geo
       const uint32_t wm = wave_max_u32(batch_max_bits(a, size, m0, threadIdx.x - 64,
                                                       kUpdThreads - 64));
       if ((threadIdx.x & 63) == 0) atomicMax(&sm.ball, wm);
+      PER_STAMP(1, 6);
     } else if (one) {
       load_range_boundary<FULL>(t, g, part, ir.lo0, ir.hi0, sib_s, sib_m);
     }
+    PER_STAMP(0, 3);
     __syncthreads();
+    PER_STAMP(0, 4);
     const float v = __uint_as_float(max(__float_as_uint(m0), sm.ball));
     if (one) {
       uniform_range<FULL>(t, g, part, ir.lo0, ir.hi0, v, sib_s, sib_m);

@@ -154,3 +154,32 @@ def test_probe_library_exports_and_checks():
     assert lib.per_probe_chain(0x1000, 1000, 10, 0x1000, None) == -1   # not a power of two
     assert lib.per_probe_chain(0x1000, 1024, 0, 0x1000, None) == -1
     assert lib.per_probe_chain(0x1000, 1 << 31, 10, 0x1000, None) == -1
+
+
+STAMPS_HEADER = os.path.join(ROOT, "include", "per_stamps.h")
+STAMPS_LIB = os.path.join(ROOT, "sum_tree_sampling_amd", "libper_stamps.so")
+
+
+def test_stamps_library_exports_and_checks(lib):
+    """libper_stamps.so exports what include/per.h and include/per_stamps.h
+    declare and rejects bad arguments on the host; libper.so carries no
+    stamps."""
+    text = re.sub(r"/\*.*?\*/", "", open(STAMPS_HEADER).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(per_stamps_[a-z_]+)\s*\(", text)))
+    assert names == ["per_stamps_clear", "per_stamps_read"]
+
+    def exported(path):
+        out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True,
+                             check=True).stdout
+        return set(re.findall(r"\bT (per_\w+)$", out, flags=re.M))
+
+    stamped = exported(STAMPS_LIB)
+    for name in declared_functions() + names:
+        assert name in stamped, name
+    assert not [n for n in exported(LIB) if n.startswith("per_stamps_")]
+    sl = ctypes.CDLL(STAMPS_LIB)
+    sl.per_stamps_read.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_void_p]
+    buf = (ctypes.c_ulonglong * 4)()
+    assert sl.per_stamps_read(None, 4, None) == -1
+    assert sl.per_stamps_read(buf, -1, None) == -1
+    assert sl.per_stamps_read(buf, 4096 * 16 + 1, None) == -1

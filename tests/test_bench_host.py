@@ -81,3 +81,33 @@ def test_central_mean():
     t = np.concatenate([np.full(80, 4.0), np.full(20, 40.0)])
     assert bench.central_mean(t) == pytest.approx(4.0)
     assert bench.central_mean(np.arange(1, 101, dtype=float)) == pytest.approx(50.5, abs=0.6)
+
+
+def test_step_phases():
+    # four blocks (100 MHz ticks): three without intake, one meeting the ring
+    # range; a stale slot from an earlier launch (below the first start) is
+    # dropped, so block 1 does not count as an intake block
+    raw = np.zeros((4, 16), np.uint64)
+    t0 = 10_000
+    for b in range(4):
+        raw[b, 0] = t0 + 10 * b
+        raw[b, 1] = t0 + 100
+        raw[b, [10, 11, 12]] = t0 + 150
+        raw[b, 8] = t0 + 200
+        raw[b, 13] = t0 + 220
+        raw[b, 14] = t0 + 230
+        raw[b, 2] = t0 + 300 + 10 * b
+    raw[1, 3] = t0 - 5  # stale
+    raw[3, [6, 3, 4, 5]] = [t0 + 350, t0 + 400, t0 + 420, t0 + 500]
+    r = bench.step_phases(raw)
+    assert r["span"] == pytest.approx(5.0)
+    assert r["others_end_max"] == pytest.approx(3.2)
+    assert r["others_end_p50"] == pytest.approx(3.1)
+    assert r["scan_all_waves_p50"] == pytest.approx(1.5)
+    assert r["repair_p50"] == pytest.approx(1.1)
+    assert r["repair_sort_p50"] == pytest.approx(0.2)
+    assert r["repair_lds_p50"] == pytest.approx(0.1)
+    assert r["repair_chain_p50"] == pytest.approx(0.8)
+    assert r["intake_climb_end"] == pytest.approx(5.0)
+    assert r["intake_batch_max"] == pytest.approx(3.5)
+    assert r["intake_after_others"] == pytest.approx(1.8)
