@@ -243,8 +243,34 @@ def step_phases(raw: np.ndarray) -> dict:
     return res
 
 
+def sampler_spread(raw: np.ndarray) -> dict:
+    """Start and end of the proportional sampler's blocks, in µs from the
+    launch's first wave start, from its stamps (libper_stamps.so): raw is
+    [blocks, 8] 100 MHz clock values, waves' starts in columns 0-3 and ends in
+    4-7, 0 where nothing was stored.  A block starts with its first wave and
+    ends with its last; blocks are dealt to the XCDs in turn (block mod 8)."""
+    t = raw.astype(np.float64)
+    used = t[:, 0] > 0
+    t = t[used]
+    st, en = t[:, 0:4].min(axis=1), t[:, 4:8].max(axis=1)
+    t0 = st.min()
+    st, en = (st - t0) / 100.0, (en - t0) / 100.0
+    x = np.flatnonzero(used) % 8
+    dur = en - st
+    return {
+        "span": float(en.max()),
+        "last_block_start": float(st.max()),
+        "block_time_p50": float(np.median(dur)),
+        "block_time_max": float(dur.max()),
+        "last_end_after_median_end": float(en.max() - np.median(en)),
+        **{"xcd%d_start_p50" % k: float(np.median(st[x == k])) for k in range(8) if (x == k).any()},
+        **{"xcd%d_last_end" % k: float(en[x == k].max()) for k in range(8) if (x == k).any()},
+    }
+
+
 def phase_stamps(workload: str, groups: int) -> dict:
-    """The fused update + intake kernel's phases (step_phases) over `groups`
+    """The fused update + intake kernel's phases (step_phases, when the step
+    fuses them) and the sampler's block spread (sampler_spread) over `groups`
     launches, each the last of three whole steps after the stamps were
     cleared, with the phase-stamped build in place of libper.so: p10, p50 and
     p90 of each figure over the launches."""
@@ -260,29 +286,43 @@ def phase_stamps(workload: str, groups: int) -> dict:
     lib.per_stamps_clear.restype = ctypes.c_int
     lib.per_stamps_read.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_void_p]
     lib.per_stamps_read.restype = ctypes.c_int
+    lib.per_sample_stamps_clear.argtypes = [ctypes.c_void_p]
+    lib.per_sample_stamps_clear.restype = ctypes.c_int
+    lib.per_sample_stamps_read.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_void_p]
+    lib.per_sample_stamps_read.restype = ctypes.c_int
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     warm, per_group = 50, 3
     run = Run(workload, warm + per_group * groups, {}, dev)
-    if "update_add" not in run.ops:
-        raise SystemExit("--phase-stamps needs a workload whose step fuses update and intake")
+    fused = "update_add" in run.ops
     sp = torch.cuda.current_stream().cuda_stream
     run.run_steps(0, warm, sp)
     torch.cuda.synchronize()
-    nb = min(max(run.n >> 12, 1), 4096)  # the kernel's tree blocks (partitions)
+    nb = min(max(run.n >> 12, 1), 4096)  # the update kernel's tree blocks (partitions)
     buf = np.zeros(4096 * STAMP_SLOTS, np.uint64)
-    rows = []
+    sbuf = np.zeros(4096 * 8, np.uint64)
+    rows, srows = [], []
     for gi in range(groups):
-        if lib.per_stamps_clear(sp) != 0:
-            raise RuntimeError("per_stamps_clear failed")
+        if lib.per_stamps_clear(sp) != 0 or lib.per_sample_stamps_clear(sp) != 0:
+            raise RuntimeError("clearing the stamps failed")
         run.run_steps(warm + per_group * gi, per_group, sp)
-        if lib.per_stamps_read(ctypes.c_void_p(buf.ctypes.data), buf.size, sp) != 0:
-            raise RuntimeError("per_stamps_read failed")
-        rows.append(step_phases(buf.reshape(4096, STAMP_SLOTS)[:nb]))
+        if (lib.per_stamps_read(ctypes.c_void_p(buf.ctypes.data), buf.size, sp) != 0 or
+                lib.per_sample_stamps_read(ctypes.c_void_p(sbuf.ctypes.data), sbuf.size, sp) != 0):
+            raise RuntimeError("reading the stamps failed")
+        if fused:
+            rows.append(step_phases(buf.reshape(4096, STAMP_SLOTS)[:nb]))
+        srows.append(sampler_spread(sbuf.reshape(4096, 8)))
     run.close()
-    keys = sorted({k for r in rows for k in r})
-    return {k: [round(float(np.percentile([r[k] for r in rows if k in r], q)), 3)
-                for q in (10, 50, 90)] for k in keys}
+
+    def summary(rs):
+        keys = sorted({k for r in rs for k in r}, key=lambda k: (k.startswith("xcd"), k))
+        return {k: [round(float(np.percentile([r[k] for r in rs if k in r], q)), 3)
+                    for q in (10, 50, 90)] for k in keys}
+
+    out = {"sampler": summary(srows)}
+    if fused:
+        out["update_add"] = summary(rows)
+    return out
 
 
 def copy_calibration() -> None:
@@ -781,8 +821,9 @@ def main():
     ap.add_argument("--ingest-pmc", metavar="DIR",
                     help="only write profiles/hbm_traffic.json from rocprofv3 runs in DIR")
     ap.add_argument("--phase-stamps", type=int, default=0, metavar="LAUNCHES",
-                    help="only print the fused update + intake kernel's per-block phase times "
-                         "over LAUNCHES launches (libper_stamps.so)")
+                    help="only print the per-block phase times of the fused update + intake "
+                         "kernel and the sampler's block spread over LAUNCHES launches "
+                         "(libper_stamps.so)")
     args = ap.parse_args()
     if args.ingest_pmc:
         ingest_pmc(args.ingest_pmc)

@@ -1,7 +1,8 @@
 /*
- * per_stamps.h -- phase stamps of the update kernels (libper_stamps.so,
- * gfx950): a measurement build of libper.so, the same sources compiled with
- * PER_PHASE_STAMPS, that exports every call of per.h plus the two below.
+ * per_stamps.h -- phase stamps of the update kernels and the sampler
+ * (libper_stamps.so, gfx950): a measurement build of libper.so, the same
+ * sources compiled with PER_PHASE_STAMPS, that exports every call of per.h
+ * plus the four below.
  * Not part of the replay buffer.
  *
  * A batch of a few hundred updates on a 2^21-leaf tree moves a fraction of
@@ -28,9 +29,15 @@
  *  14   0    the repair's sibling reads from LDS
  *
  * Slots 0-7 are stored by the fused update + intake kernel only; 1, 2, 8 and
- * 10-14 also by the other update kernels that share those phases.  Each stamp
- * waits for its own scalar read of the clock, so a phase ending in a stamp
- * reads long by that wait.
+ * 10-14 also by the other update kernels that share those phases.
+ *
+ * The proportional sampler (section "Sampling Is a Descent" of the same page)
+ * keeps a second array of 4096 x 8 u64: lane 0 of wave w (of 4) of block b
+ * stores the clock when the wave starts into slot [b * 8 + w] and when it is
+ * done (descent, weights and rows) into slot [b * 8 + 4 + w].
+ *
+ * Each stamp waits for its own scalar read of the clock, so a phase ending in
+ * a stamp reads long by that wait.
  *
  * Work goes to the caller's stream.  Return 0, -1 for a bad argument
  * (checked on the host) or -4 for a HIP error.
@@ -50,6 +57,10 @@ int per_stamps_clear(hipStream_t stream);
 /* Copy the first `count` slots (0 <= count <= 4096 * 16) to host memory at
  * `out`, then wait for the stream. */
 int per_stamps_read(unsigned long long* out, long long count, hipStream_t stream);
+
+/* The same for the sampler's array (0 <= count <= 4096 * 8). */
+int per_sample_stamps_clear(hipStream_t stream);
+int per_sample_stamps_read(unsigned long long* out, long long count, hipStream_t stream);
 
 #ifdef __cplusplus
 }

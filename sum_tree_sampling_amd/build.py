@@ -16,7 +16,7 @@ SOURCES = ["per_api.hip", "tree_kernels.hip", "sample_kernels.hip", "rank_kernel
 PROBE_SRC = os.path.join(HERE, "probe", "latency_probe.hip")
 PROBE_LIB = os.path.join(HERE, "libper_probe.so")
 STAMPS_LIB = os.path.join(HERE, "libper_stamps.so")
-STAMPED = "tree_kernels.hip"  # the source whose kernels carry the phase stamps
+STAMPED = ("tree_kernels.hip", "sample_kernels.hip")  # sources whose kernels carry stamps
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # IEEE f32 arithmetic as written: no contraction into FMA, no fast-math, no
@@ -71,20 +71,21 @@ def _compile(src: str, obj: str, defines: tuple = ()) -> None:
 
 def build() -> str:
     """Compile every source and link libper.so, libper_probe.so and
-    libper_stamps.so (libper.so with PER_PHASE_STAMPS in STAMPED) next to
-    this file."""
+    libper_stamps.so (libper.so with PER_PHASE_STAMPS in the STAMPED sources)
+    next to this file."""
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
     srcs = [os.path.join(CSRC, s) for s in SOURCES] + [PROBE_SRC]
     objs = [os.path.join(objdir, os.path.basename(s).replace(".hip", ".o")) for s in srcs]
-    stamped_obj = os.path.join(objdir, STAMPED.replace(".hip", "_stamps.o"))
+    stamped = {f.replace(".hip", ".o"): os.path.join(objdir, f.replace(".hip", "_stamps.o"))
+               for f in STAMPED}
     jobs = [(s, o, ()) for s, o in zip(srcs, objs)]
-    jobs.append((os.path.join(CSRC, STAMPED), stamped_obj, ("PER_PHASE_STAMPS",)))
+    jobs += [(os.path.join(CSRC, f), stamped[f.replace(".hip", ".o")], ("PER_PHASE_STAMPS",))
+             for f in STAMPED]
     with ThreadPoolExecutor(max_workers=len(jobs)) as ex:
         list(ex.map(lambda job: _compile(*job), jobs))
     lib_objs = objs[:-1]
-    stamps_objs = [stamped_obj if os.path.basename(o) == STAMPED.replace(".hip", ".o") else o
-                   for o in lib_objs]
+    stamps_objs = [stamped.get(os.path.basename(o), o) for o in lib_objs]
     for lib, lib_objs in ((LIB, lib_objs), (PROBE_LIB, objs[-1:]), (STAMPS_LIB, stamps_objs)):
         tmp = lib + ".tmp"
         cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *lib_objs]

@@ -37,6 +37,44 @@
 #include "lanes.h"
 #include "per_internal.h"
 
+// Start and end stamps of the proportional sampler's waves, in the
+// measurement build only (libper_stamps.so, PER_PHASE_STAMPS defined): lane 0
+// of wave w (of 4) of block b stores the 100 MHz real-time clock when the
+// wave starts into per_sample_stamps[b * 8 + w] and when it is done into
+// per_sample_stamps[b * 8 + 4 + w] (include/per_stamps.h).  In the product
+// build the stamps are empty statements.
+#ifdef PER_PHASE_STAMPS
+constexpr int kSampleStampBlocks = 4096;
+__device__ unsigned long long per_sample_stamps[kSampleStampBlocks * 8];
+#define PER_SAMPLE_STAMP(k)                                                               \
+  do {                                                                                    \
+    if ((threadIdx.x & 63u) == 0 && blockIdx.x < (unsigned)kSampleStampBlocks)           \
+      per_sample_stamps[blockIdx.x * 8 + (k) * 4 + (threadIdx.x >> 6)] =                  \
+          __builtin_amdgcn_s_memrealtime();                                               \
+  } while (0)
+
+extern "C" int per_sample_stamps_clear(hipStream_t stream) {
+  void* p = nullptr;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(per_sample_stamps)) != hipSuccess) return -4;
+  return hipMemsetAsync(p, 0, sizeof(per_sample_stamps), stream) == hipSuccess ? 0 : -4;
+}
+
+extern "C" int per_sample_stamps_read(unsigned long long* out, long long count,
+                                      hipStream_t stream) {
+  if (!out || count < 0 || count > (long long)(kSampleStampBlocks * 8)) return -1;
+  void* p = nullptr;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(per_sample_stamps)) != hipSuccess) return -4;
+  if (hipMemcpyAsync(out, p, (size_t)count * sizeof(unsigned long long), hipMemcpyDeviceToHost,
+                     stream) != hipSuccess)
+    return -4;
+  return hipStreamSynchronize(stream) == hipSuccess ? 0 : -4;
+}
+#else
+#define PER_SAMPLE_STAMP(k) \
+  do {                      \
+  } while (0)
+#endif
+
 namespace per {
 namespace {
 
@@ -408,6 +446,7 @@ __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleArgs a) {
   // one dependent trip each.
   asm volatile("" ::"s"(a.top_mode), "s"(a.P), "s"(a.sum), "s"(a.mn), "s"(a.u), "s"(a.B),
                "s"(a.top), "s"(a.nrounds));
+  PER_SAMPLE_STAMP(0);
   constexpr int LOGG = ilog2(G);
   constexpr int LOGV = ilog2(V);
   constexpr int SPW = 64 / G;  // samples per wave
@@ -749,6 +788,7 @@ __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleArgs a) {
   uint32_t slot = node - a.n;
   if (a.order) slot = a.order[slot];  // rank-based: the descent gave a rank
   emit<G, SPW, true>(a, wave, lane, b, active && j == 0, slot, leaf, pmin);
+  PER_SAMPLE_STAMP(1);
 }
 
 // Uniform sample over the filled slots ("GPU-Resident Prioritized

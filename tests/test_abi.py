@@ -165,8 +165,9 @@ def test_stamps_library_exports_and_checks(lib):
     declare and rejects bad arguments on the host; libper.so carries no
     stamps."""
     text = re.sub(r"/\*.*?\*/", "", open(STAMPS_HEADER).read(), flags=re.S)
-    names = sorted(set(re.findall(r"\b(per_stamps_[a-z_]+)\s*\(", text)))
-    assert names == ["per_stamps_clear", "per_stamps_read"]
+    names = sorted(set(re.findall(r"\b(per_(?:sample_)?stamps_[a-z_]+)\s*\(", text)))
+    assert names == ["per_sample_stamps_clear", "per_sample_stamps_read", "per_stamps_clear",
+                     "per_stamps_read"]
 
     def exported(path):
         out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True,
@@ -176,10 +177,13 @@ def test_stamps_library_exports_and_checks(lib):
     stamped = exported(STAMPS_LIB)
     for name in declared_functions() + names:
         assert name in stamped, name
-    assert not [n for n in exported(LIB) if n.startswith("per_stamps_")]
+    assert not [n for n in exported(LIB) if "stamps" in n]
     sl = ctypes.CDLL(STAMPS_LIB)
     sl.per_stamps_read.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_void_p]
     buf = (ctypes.c_ulonglong * 4)()
     assert sl.per_stamps_read(None, 4, None) == -1
     assert sl.per_stamps_read(buf, -1, None) == -1
     assert sl.per_stamps_read(buf, 4096 * 16 + 1, None) == -1
+    sl.per_sample_stamps_read.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_void_p]
+    assert sl.per_sample_stamps_read(None, 4, None) == -1
+    assert sl.per_sample_stamps_read(buf, 4096 * 8 + 1, None) == -1

@@ -111,3 +111,22 @@ def test_step_phases():
     assert r["intake_climb_end"] == pytest.approx(5.0)
     assert r["intake_batch_max"] == pytest.approx(3.5)
     assert r["intake_after_others"] == pytest.approx(1.8)
+
+
+def test_sampler_spread():
+    # 16 blocks of 4 waves; block b's waves start at 10b, 10b+1, ... ticks and
+    # end 2000 ticks later, except block 13 (XCD 5), which ends 500 later
+    raw = np.zeros((4096, 8), np.uint64)
+    t0 = 50_000
+    for b in range(16):
+        raw[b, 0:4] = t0 + 10 * b + np.arange(4)
+        raw[b, 4:8] = t0 + 10 * b + 2000 + np.arange(4)
+    raw[13, 7] += 500
+    r = bench.sampler_spread(raw)
+    assert r["last_block_start"] == pytest.approx(1.5)
+    assert r["block_time_p50"] == pytest.approx(20.03)
+    assert r["block_time_max"] == pytest.approx(25.03)
+    assert r["span"] == pytest.approx(1.3 + 25.03)
+    assert r["xcd5_start_p50"] == pytest.approx(0.9)  # blocks 5 and 13
+    assert r["xcd5_last_end"] == pytest.approx(1.3 + 25.03)
+    assert r["xcd0_last_end"] == pytest.approx(0.8 + 20.03)
