@@ -51,7 +51,8 @@
 extern "C" {
 #endif
 
-/* Enqueue the zeroing of every slot. */
+/* Enqueue the zeroing of every slot (a memset: not for a stream being
+ * captured into a graph). */
 int per_stamps_clear(hipStream_t stream);
 
 /* Copy the first `count` slots (0 <= count <= 4096 * 16) to host memory at
