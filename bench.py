@@ -251,6 +251,8 @@ def sampler_spread(raw: np.ndarray) -> dict:
     ends with its last; blocks are dealt to the XCDs in turn (block mod 8)."""
     t = raw.astype(np.float64)
     used = t[:, 0] > 0
+    if not used.any():  # no proportional-sampler launch in the step
+        return {}
     t = t[used]
     st, en = t[:, 0:4].min(axis=1), t[:, 4:8].max(axis=1)
     t0 = st.min()
@@ -272,16 +274,23 @@ def phase_stamps(workload: str, groups: int) -> dict:
     """The fused update + intake kernel's phases (step_phases, when the step
     fuses them) and the sampler's block spread (sampler_spread) over `groups`
     launches, each the last of three whole steps after the stamps were
-    cleared, with the phase-stamped build in place of libper.so: p10, p50 and
-    p90 of each figure over the launches."""
-    import ctypes
-
-    import torch
+    cleared, with the phase-stamped build in place of libper.so (restored
+    after): p10, p50 and p90 of each figure over the launches."""
     from sum_tree_sampling_amd import per
     if not os.path.exists(STAMPS_LIB):
         raise SystemExit("libper_stamps.so not built: run sum_tree_sampling_amd.build.build()")
+    prev = per._lib
     per._lib = per.load(STAMPS_LIB)
-    lib = per._lib
+    try:
+        return _phase_stamps_run(per._lib, workload, groups)
+    finally:
+        per._lib = prev
+
+
+def _phase_stamps_run(lib, workload: str, groups: int) -> dict:
+    import ctypes
+
+    import torch
     lib.per_stamps_clear.argtypes = [ctypes.c_void_p]
     lib.per_stamps_clear.restype = ctypes.c_int
     lib.per_stamps_read.argtypes = [ctypes.c_void_p, ctypes.c_longlong, ctypes.c_void_p]
@@ -319,7 +328,7 @@ def phase_stamps(workload: str, groups: int) -> dict:
         return {k: [round(float(np.percentile([r[k] for r in rs if k in r], q)), 3)
                     for q in (10, 50, 90)] for k in keys}
 
-    out = {"sampler": summary(srows)}
+    out = {"sampler": summary([r for r in srows if r])}
     if fused:
         out["update_add"] = summary(rows)
     return out

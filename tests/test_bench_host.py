@@ -130,3 +130,8 @@ def test_sampler_spread():
     assert r["xcd5_start_p50"] == pytest.approx(0.9)  # blocks 5 and 13
     assert r["xcd5_last_end"] == pytest.approx(1.3 + 25.03)
     assert r["xcd0_last_end"] == pytest.approx(0.8 + 20.03)
+
+
+def test_sampler_spread_without_stamps():
+    # a step without a proportional-sampler launch leaves no stamps
+    assert bench.sampler_spread(np.zeros((4096, 8), np.uint64)) == {}
