@@ -25,6 +25,7 @@
 //    kernel of the priority trees finishes the nodes above.
 
 #include "per_internal.h"
+#include "pow_f32.h"
 
 namespace per {
 namespace {
@@ -274,7 +275,7 @@ __global__ void __launch_bounds__(kRankThreads) rank_build_kernel(TreePtrs t, Ge
   const uint32_t root = (1u << g.P) + blockIdx.x;
   for (uint32_t o = threadIdx.x; o < span; o += kRankThreads) {
     const uint32_t r = r0 + o;
-    const float w = (r < count) ? (float)pow((double)(r + 1), -alpha) : 0.0f;
+    const float w = (r < count) ? pow_f32((double)(r + 1), -alpha) : 0.0f;
     hs[span + o] = w;
     hm[span + o] = (r < count) ? w : __builtin_inff();
   }

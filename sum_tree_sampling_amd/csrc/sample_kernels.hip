@@ -36,6 +36,7 @@
 
 #include "lanes.h"
 #include "per_internal.h"
+#include "pow_f32.h"
 
 // Start and end stamps of the proportional sampler's waves, in the
 // measurement build only (libper_stamps.so, PER_PHASE_STAMPS defined): lane 0
@@ -392,11 +393,12 @@ __device__ __forceinline__ void emit(const SampleArgs& a, uint32_t wave, int lan
   // The weight, computed while the rows' loads are in flight.
   auto weight = [&]() {
     if (lead && a.w_out) {
-      // (N P_i)^-beta / (N P_min)^-beta = (p_i / p_min)^-beta: one pow, f64.
+      // (N P_i)^-beta / (N P_min)^-beta = (p_i / p_min)^-beta: one pow, f64
+      // (pow_f32: the f64 pow's f32 value by a shorter route).
       // With p_min > 0 every stored priority, the sampled one included, is
       // > 0; with p_min = 0 the normaliser is infinite and w = 0.
       float w = 0.0f;
-      if (pmin > 0.0f) w = (float)pow((double)leaf / (double)pmin, -a.beta);
+      if (pmin > 0.0f) w = pow_f32((double)leaf / (double)pmin, -a.beta);
       a.w_out[b] = w;
     }
   };

@@ -40,6 +40,7 @@
 
 #include "lanes.h"
 #include "per_internal.h"
+#include "pow_f32.h"
 
 // Phase stamps of the update kernels, in the measurement build only
 // (libper_stamps.so, PER_PHASE_STAMPS defined): lane 0 of wave w of block b
@@ -105,12 +106,14 @@ __device__ __forceinline__ float min_f32(float a, float b) {
 // ("GPU-Resident Prioritized Experience Replay", section "Priority update";
 // NaN / Inf clamp of section "Error Handling & Fallback": NaN takes the value
 // of td = 0, computed on the host as p_nan, and +/-Inf the max at batch start).
+// pow_f32 gives the f64 pow's f32 value by the shorter exp2(alpha log2 y)
+// wherever that rounds the same way.
 __device__ __forceinline__ float priority_of(float td, float max_at_start, double alpha,
                                              double eps, float p_nan) {
   const float x = fabsf(td);
   if (__builtin_isnan(x)) return p_nan;
   if (__builtin_isinf(x)) return max_at_start;
-  return (float)pow((double)x + eps, alpha);
+  return pow_f32((double)x + eps, alpha);
 }
 
 // ------------------------------------------------------------ block helpers

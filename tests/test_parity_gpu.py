@@ -829,6 +829,40 @@ def test_update_add_boundary_siblings(lo, c):
         compare_trees(o, g, "boundary siblings lo %d c %d step %d" % (lo, c, step))
 
 
+@pytest.mark.parametrize("alpha,eps", [
+    (0.6, 1e-6),
+    (1e-5, 1e-6),
+    (3.0, 0.5),     # large results: 1e30^3 leaves the f32 range
+    (1.0, 0.0),     # |td| = 0 with eps 0: y = 0
+    (0.25, 1e-30),
+])
+def test_priority_wide_range(alpha, eps):
+    """Priorities of TD errors spanning the f32 range -- log-uniform
+    magnitudes from 1e-30 to 1e30 of either sign, zeros, the smallest normal
+    and subnormal f32, the largest f32, NaN and infinities -- each slot
+    updated once, by a bucketed batch and by a scanned one, bit for bit with
+    the oracle's f32 of the f64 pow: whichever route the device's power takes,
+    its f32 is the same."""
+    say("priority wide range", alpha, eps)
+    n = 1 << 18
+    rng = np.random.default_rng(int(alpha * 1000) + int(-np.log10(eps)) if eps else 7)
+    o = Oracle(n, 0, alpha=alpha, eps=eps)
+    g = _buf(n, 0, max_batch=n, alpha=alpha, eps=eps)
+    p0 = (rng.random(n) * 2).astype(np.float32)
+    o.add(n, prio=p0)
+    g.add(n, prio=dev(p0))
+    mag = 10.0 ** rng.uniform(-30, 30, n)
+    td = (mag * np.where(rng.random(n) < 0.5, -1.0, 1.0)).astype(np.float32)
+    special = np.array([0.0, -0.0, 1.17549435e-38, 1e-45, 3.4028235e38, -3.4028235e38,
+                        np.nan, np.inf, -np.inf, 1.0, -1.0, 0.5], dtype=np.float32)
+    td[rng.choice(n, special.size * 8, replace=False)] = np.tile(special, 8)
+    idx = rng.permutation(n).astype(np.int64)
+    for lo, hi in ((0, n - 2048), (n - 2048, n)):  # the bucketed path, then the scan path
+        o.update(idx[lo:hi], td[lo:hi])
+        g.update(dev(idx[lo:hi]), dev(td[lo:hi]))
+        compare_trees(o, g, "priority wide range alpha %g eps %g, entries %d..%d" % (alpha, eps, lo, hi))
+
+
 @pytest.mark.parametrize("alpha,eps,kind", [
     (0.6, 1e-6, "near ties"),      # several entries within a few ulps of the largest |td|
     (0.6, 1e-6, "no finite td"),   # only NaN and infinite TD errors
