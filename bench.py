@@ -207,14 +207,17 @@ STAMPS_LIB = os.path.join(ROOT, "sum_tree_sampling_amd", "libper_stamps.so")
 STAMP_SLOTS = 16  # phases per block (include/per_stamps.h)
 
 
-def step_phases(raw: np.ndarray) -> dict:
+def step_phases(raw: np.ndarray, entries: np.ndarray | None = None) -> dict:
     """Phase times, in µs from the first block's start, of one launch of the
     fused update + intake kernel, from its stamps (libper_stamps.so; slots as
     in include/per_stamps.h).  raw: [blocks, 16] 100 MHz clock values, 0
     where nothing was stored; values below the launch's first start are a
     launch before's and are dropped.  Blocks that stored slot 3 meet the ring
     range (the intake's); the others end at their repair.  Repair phases are
-    taken over the blocks that sorted entries."""
+    taken over the blocks that sorted entries.  entries (optional): the
+    update's entries per block (partition), for the median end of the blocks
+    without intake by entries held (0 to 4, then 5 or more) and the entries of
+    the last of them to end."""
     t = raw.astype(np.float64)
     t0 = t[:, 0][t[:, 0] > 0].min()
     t = np.where(t >= t0, (t - t0) / 100.0, np.nan)
@@ -240,6 +243,14 @@ def step_phases(raw: np.ndarray) -> dict:
                         (5, "climb_end"), (6, "batch_max")):
             res["intake_" + name] = float(t[b, k])
         res["intake_after_others"] = float(end[b] - np.nanmax(end[o]))
+    if entries is not None:
+        m = np.minimum(entries, 5)
+        for k in range(6):
+            sel = o & (m == k)
+            if sel.any():
+                res["end_with_%d%s_entries" % (k, "+" if k == 5 else "")] = float(np.nanmedian(end[sel]))
+        oi = np.flatnonzero(o)
+        res["last_block_entries"] = float(entries[oi[np.nanargmax(end[oi])]])
     return res
 
 
@@ -319,7 +330,14 @@ def _phase_stamps_run(lib, workload: str, groups: int) -> dict:
                 lib.per_sample_stamps_read(ctypes.c_void_p(sbuf.ctypes.data), sbuf.size, sp) != 0):
             raise RuntimeError("reading the stamps failed")
         if fused:
-            rows.append(step_phases(buf.reshape(4096, STAMP_SLOTS)[:nb]))
+            # the update's entries per partition in the launch read: the last
+            # step's batch (the step's own samples unless the workload brings
+            # its own update indices)
+            last = warm + per_group * gi + per_group - 1
+            ui = (run.idx[last] if run.idx is not None else run.out["idx"]).cpu().numpy()
+            ui = ui[(ui >= 0) & (ui < run.n)]
+            ent = np.bincount(ui >> 12, minlength=nb)[:nb] if run.n >= 4096 else None
+            rows.append(step_phases(buf.reshape(4096, STAMP_SLOTS)[:nb], ent))
         srows.append(sampler_spread(sbuf.reshape(4096, 8)))
     run.close()
 

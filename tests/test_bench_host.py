@@ -111,6 +111,14 @@ def test_step_phases():
     assert r["intake_climb_end"] == pytest.approx(5.0)
     assert r["intake_batch_max"] == pytest.approx(3.5)
     assert r["intake_after_others"] == pytest.approx(1.8)
+    # with the update's entries per partition: block ends by entries held
+    # (block 3 meets the ring range and is left out), and the last block's
+    r = bench.step_phases(raw, np.array([0, 7, 1, 2]))
+    assert r["end_with_0_entries"] == pytest.approx(3.0)
+    assert r["end_with_1_entries"] == pytest.approx(3.2)
+    assert r["end_with_5+_entries"] == pytest.approx(3.1)
+    assert "end_with_2_entries" not in r
+    assert r["last_block_entries"] == 1
 
 
 def test_sampler_spread():
