@@ -1284,6 +1284,20 @@ struct UpdAddSmem {
   int flag;
 };
 
+// Whether f32(pow(y, alpha)) <= m0 for every y <= ys, decided by f32
+// logarithms (2^-16 <= alpha <= 16): true when alpha log2(ys) lies below
+// log2(m0) by more than 2^-12 (1 + |alpha log2 ys| + |log2 m0|).  Rounding ys
+// and alpha to f32, the product and each logarithm (taken as within 2^-20 +
+// 2^-21 |result|) move the two sides by under 2^-15 (1 + |alpha log2 ys| +
+// |log2 m0|) together, so then ys^alpha < m0 (1 - 2^-13), and the f64 pow,
+// within a few of its ulps, rounds to at most m0.  Zero, infinite and NaN
+// operands make a side infinite or NaN and the answer false.
+__device__ __forceinline__ bool stays_below(double ys, float m0, double alpha) {
+  if (alpha > 16.0) return false;
+  const float za = (float)alpha * log2f((float)ys), lm = log2f(m0);
+  return za < lm - 0x1p-12f * (1.0f + fabsf(za) + fabsf(lm));
+}
+
 // The max priority bits over the batch entries b = first, first + stride,
 // ... with an index in [0, size): what priority_of gives each (NaN and
 // infinite TD errors included).  Called by whole waves (stride a multiple of
@@ -1292,7 +1306,9 @@ struct UpdAddSmem {
 // wave and chunk, has an exact p at least a factor (1 - 2^-24)^alpha <= 1 -
 // 2^-41 (alpha >= 2^-16) below that of y*: far more than the few-ulp error
 // of the f64 pow, so it cannot exceed the max after rounding.  So only the
-// entries at or above that bound are raised to alpha.
+// entries at or above that bound are raised to alpha, and none when even y*
+// cannot lift the priority above m0 (stays_below): the caller takes the max
+// with m0, so a result below m0 is as good as the exact one there.
 __device__ __forceinline__ uint32_t batch_max_bits(const UpdateArgs& a, uint32_t size, float m0,
                                                    uint32_t first, uint32_t stride) {
   constexpr int kC = 4;
@@ -1331,6 +1347,7 @@ __device__ __forceinline__ uint32_t batch_max_bits(const UpdateArgs& a, uint32_t
 #pragma unroll
       for (int c = 0; c < kC; ++c)
         if (((pend >> c) & 1u) && (double)fabsf(tx[c]) + a.eps < bound) pend &= ~(1u << c);
+      if (stays_below(ys, m0, a.alpha)) pend = 0u;
     }
     while (__ballot(pend != 0u) != 0ull) {  // one entry per lane per round
       if (pend != 0u) {

@@ -903,6 +903,39 @@ def test_update_add_batch_max(alpha, eps, kind):
         compare_trees(o, g, "batch max %s step %d" % (kind, step))
 
 
+@pytest.mark.parametrize("alpha", [0.6, 1.0, 0.05, 7.0, 20.0])
+def test_update_add_batch_max_near_running_max(alpha):
+    """A fused intake at the running max when the batch's largest priority
+    lies just below, at or just above the running max m0 (relative gaps from
+    2^-8 down to 2^-20, both sides of the margin within which the kernel
+    raises the largest |td| to alpha instead of deciding from logarithms that
+    it cannot exceed m0; alpha 20 lies beyond the logarithm test's range): the
+    trees, the running max and the intake's priority bit for bit with the
+    oracle's update then intake."""
+    say("update_add batch max near m0", alpha)
+    n, B, c, eps = 1 << 14, 600, 100, 1e-6
+    rng = np.random.default_rng(int(alpha * 1000) + 7)
+    o = Oracle(n, 0, alpha=alpha, eps=eps)
+    g = _buf(n, 0, max_batch=1024, alpha=alpha, eps=eps)
+    p0 = (rng.random(n) * 0.01).astype(np.float32)
+    o.add(n, prio=p0)
+    g.add(n, prio=dev(p0))
+    gaps = [-2.0**-8, -2.0**-11, -2.0**-12, -2.0**-13, -2.0**-14, -2.0**-20, 0.0, 2.0**-20, -2.0**-12]
+    for step in range(len(gaps) + 1):
+        idx = rng.integers(0, n, B).astype(np.int64)
+        td = (rng.random(B) * 0.5).astype(np.float32)
+        if step == 0:
+            td[0] = 3.0  # the running max rises to 3^alpha
+        else:
+            m = float(o.max_priority)
+            y = (m * (1.0 + gaps[step - 1])) ** (1.0 / alpha) - eps
+            td[rng.integers(0, B)] = np.float32(y) * (1 if step % 2 else -1)
+        o.update(idx, td)
+        o.add(c)
+        g.update_add(dev(idx), dev(td), c)
+        compare_trees(o, g, "batch max near m0, alpha %g step %d" % (alpha, step))
+
+
 # ------------------------------------------------------------ full-size large buffer
 
 def test_large_16m_full_size():
