@@ -441,13 +441,18 @@ __device__ __forceinline__ void emit(const SampleArgs& a, uint32_t wave, int lan
 // TP > 0: the top is rebuilt from 2^TP partition roots (a.P == TP), so
 // that the rebuild's and the walk's loops are fixed too.
 template <int G, int V, bool STREAM, int FR, int FN, int TP>
-__global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleArgs a) {
+__global__ void __launch_bounds__(kSampleThreads) sample_kernel(const float* u, float* sum, float* mn,
+                                                                uint32_t B, SampleArgs a) {
+  // The masses, the trees and the batch size arrive in scalar registers with
+  // the wave (the leading arguments, preloaded; the same as a's), so the
+  // first loads issue at once.
   extern __shared__ float top[];  // nodes [0, 2^(K+1)) of the sum tree
-  // The arguments the first steps need, fetched in one batch: left to
+  // The other arguments the first steps need, fetched in one batch: left to
   // itself, the compiler loads each after the branch that first needs it,
-  // one dependent trip each.
-  asm volatile("" ::"s"(a.top_mode), "s"(a.P), "s"(a.sum), "s"(a.mn), "s"(a.u), "s"(a.B),
-               "s"(a.top), "s"(a.nrounds));
+  // one dependent trip each.  With the top's depth fixed when compiling they
+  // are fetched once the first loads are in flight (below).
+  if constexpr (TP == 0)
+    asm volatile("" ::"s"(a.top_mode), "s"(a.P), "s"(a.top), "s"(a.nrounds));
   PER_SAMPLE_STAMP(0);
   constexpr int LOGG = ilog2(G);
   constexpr int LOGV = ilog2(V);
@@ -458,11 +463,11 @@ __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleArgs a) {
   const int gbase = lane & ~(G - 1);
   const uint32_t wave = blockIdx.x * (kSampleThreads / 64) + (threadIdx.x >> 6);
   const uint32_t b = wave * SPW + (uint32_t)(lane / G);
-  const bool active = b < a.B;
+  const bool active = b < B;
   // The sample's mass is fetched first, so that its trip overlaps the
   // top rebuild's loads instead of following them.
   float ub = 0.0f;
-  if (!STREAM && active) ub = a.u[b];
+  if (!STREAM && active) ub = u[b];
 
   // One sample per wave and a top of 2^8 .. 2^10 roots: each wave keeps the
   // whole top in registers instead of sharing an LDS copy with its block.
@@ -485,8 +490,8 @@ __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleArgs a) {
     float r[C], mr[C];
 #pragma unroll
     for (int i = 0; i < C; i += 4) {
-      const float4 q = *reinterpret_cast<const float4*>(a.sum + np + (uint32_t)lane * C + i);
-      const float4 w = *reinterpret_cast<const float4*>(a.mn + np + (uint32_t)lane * C + i);
+      const float4 q = *reinterpret_cast<const float4*>(sum + np + (uint32_t)lane * C + i);
+      const float4 w = *reinterpret_cast<const float4*>(mn + np + (uint32_t)lane * C + i);
       r[i] = q.x;
       r[i + 1] = q.y;
       r[i + 2] = q.z;
@@ -496,6 +501,7 @@ __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleArgs a) {
       mr[i + 2] = w.z;
       mr[i + 3] = w.w;
     }
+    asm volatile("" ::"s"(a.top), "s"(a.nrounds));
     float x[6];
     x[0] = pair_sum<C>(r);
     float mm = mr[0];
@@ -533,7 +539,7 @@ __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleArgs a) {
     m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lm), base));
     node = np + (uint32_t)(base * C + __builtin_amdgcn_readlane(e, base));
     ub = m;  // carried to the rounds below
-  } else if (a.top_mode == kTopRebuild) {
+  } else if (TP > 0 || a.top_mode == kTopRebuild) {
     // Nodes [1, 2^P) from the partition roots at depth P: sums in top[],
     // mins in mtop[].  With more than 512 roots the levels down to depth 8
     // are reduced block-wide first, two levels per pass: a thread takes four
@@ -581,10 +587,11 @@ __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleArgs a) {
       for (int c = 0; c < kG; ++c) {
         const uint32_t g = threadIdx.x + c * kSampleThreads;
         if (g < nq) {
-          rs[c] = *reinterpret_cast<const float4*>(a.sum + np + 4 * g);
-          rm[c] = *reinterpret_cast<const float4*>(a.mn + np + 4 * g);
+          rs[c] = *reinterpret_cast<const float4*>(sum + np + 4 * g);
+          rm[c] = *reinterpret_cast<const float4*>(mn + np + 4 * g);
         }
       }
+      if constexpr (TP > 0) asm volatile("" ::"s"(a.top), "s"(a.nrounds));
 #pragma unroll
       for (int c = 0; c < kG; ++c) {
         const uint32_t g = threadIdx.x + c * kSampleThreads;
@@ -638,8 +645,8 @@ __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleArgs a) {
             v[i] = hs;
             mv[i] = hm;
           } else {
-            v[i] = a.sum[k0 + i];
-            mv[i] = a.mn[k0 + i];
+            v[i] = sum[k0 + i];
+            mv[i] = mn[k0 + i];
           }
         }
       }
@@ -700,11 +707,11 @@ __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleArgs a) {
     if (a.top_mode == kTopWhole) {
       const uint32_t cnt = 1u << (a.top + 1);  // whole tree, >= 4 floats
       for (uint32_t i = threadIdx.x * 4; i < cnt; i += kSampleThreads * 4)
-        *reinterpret_cast<float4*>(top + i) = *reinterpret_cast<const float4*>(a.sum + i);
+        *reinterpret_cast<float4*>(top + i) = *reinterpret_cast<const float4*>(sum + i);
       __syncthreads();
     }
-    T = a.sum[1];
-    pmin = a.mn[1];
+    T = sum[1];
+    pmin = mn[1];
   }
 
   float m;
@@ -732,7 +739,7 @@ __global__ void __launch_bounds__(kSampleThreads) sample_kernel(SampleArgs a) {
     const bool used = j < (1 << lg);
     float x[V];
     if (used) {
-      load_values<V>(a.sum + base + (uint32_t)j * V, x);
+      load_values<V>(sum + base + (uint32_t)j * V, x);
     } else {
 #pragma unroll
       for (int i = 0; i < V; ++i) x[i] = 0.0f;
@@ -818,7 +825,7 @@ __global__ void __launch_bounds__(kSampleThreads) uniform_kernel(SampleArgs a) {
 template <int G, int V, bool STREAM, int FR, int FN, int TP>
 hipError_t launch_one(const SampleArgs& a, unsigned grid, size_t lds, hipStream_t s) {
   return launch_kernel(sample_kernel<G, V, STREAM, FR, FN, TP>, dim3(grid), dim3(kSampleThreads),
-                       lds, s, a);
+                       lds, s, a.u, a.sum, a.mn, a.B, a);
 }
 
 // The usual round shape (FR, FN) with the top depth of trees of 2^20 to

@@ -803,6 +803,24 @@ __device__ __forceinline__ uint32_t filled_size(const UpdateArgs& a) {
   return a.ring.dev ? a.ring_ctrl->size[a.ring.slot] : a.size;
 }
 
+// Entries b0 + c kUpdThreads + threadIdx.x (c < kChunk) of a batch of B:
+// their slots (-1 past the end) and TD errors, all loads issued before any
+// is used.
+template <int kChunk>
+__device__ __forceinline__ void load_chunk(const int64_t* idx, const float* td, uint32_t B,
+                                           uint32_t b0, int64_t* ix, float* tx) {
+#pragma unroll
+  for (int c = 0; c < kChunk; ++c) {
+    const uint32_t b = b0 + c * kUpdThreads + threadIdx.x;
+    ix[c] = -1;
+    tx[c] = 0.0f;
+    if (b < B) {
+      ix[c] = idx[b];
+      tx[c] = td[b];
+    }
+  }
+}
+
 // Small batches: each block owns PPB consecutive partitions and scans the
 // whole batch for their slots; wave w repairs partition w of the block when
 // it is sparse, crowded partitions are rebuilt by the whole block after.
@@ -811,11 +829,13 @@ __device__ __forceinline__ uint32_t filled_size(const UpdateArgs& a) {
 // priorities still raising the running max; sm.ball is cleared for the
 // caller's batch max.  Returns whether a partition was crowded (then
 // rebuilt by the whole block, which has passed a barrier since); otherwise
-// wave w returns right after its sparse repair.
+// wave w returns right after its sparse repair.  ix0, tx0: the batch's
+// first chunk (load_chunk at b0 = 0), loaded by the caller at kernel start.
 template <int PPB, bool FUSED, bool FULL, int kChunk, bool LINE, typename SM, typename Skip>
 __device__ __forceinline__ bool scan_update(SM& sm, const TreePtrs& t, const Geom& g,
                                             const UpdateArgs& a, uint32_t part0, uint32_t size,
-                                            float m0, Skip skip) {
+                                            float m0, const int64_t* ix0, const float* tx0,
+                                            Skip skip) {
   const int nparts = (int)min((uint32_t)PPB, (1u << g.P) - part0);
   uint32_t* max_dst = &t.ctrl->maxp_bits[a.dst];
   if (threadIdx.x < PPB) sm.count[threadIdx.x] = 0;
@@ -830,15 +850,14 @@ __device__ __forceinline__ bool scan_update(SM& sm, const TreePtrs& t, const Geo
   for (uint32_t b0 = 0; b0 < a.B; b0 += kUpdThreads * kChunk) {
     int64_t ix[kChunk];
     float tx[kChunk];
+    if (b0 == 0) {
 #pragma unroll
-    for (int c = 0; c < kChunk; ++c) {
-      const uint32_t b = b0 + c * kUpdThreads + threadIdx.x;
-      ix[c] = -1;
-      tx[c] = 0.0f;
-      if (b < a.B) {
-        ix[c] = a.idx[b];
-        tx[c] = a.td[b];
+      for (int c = 0; c < kChunk; ++c) {
+        ix[c] = ix0[c];
+        tx[c] = tx0[c];
       }
+    } else {
+      load_chunk<kChunk>(a.idx, a.td, a.B, b0, ix, tx);
     }
 #pragma unroll
     for (int c = 0; c < kChunk; ++c) asm volatile("" ::"v"(tx[c]), "v"(ix[c]));
@@ -917,14 +936,25 @@ __device__ __forceinline__ bool scan_update(SM& sm, const TreePtrs& t, const Geo
 }
 
 template <int PPB, bool FULL, int CH, bool LINE>
-__global__ void __launch_bounds__(kUpdThreads) update_scan_kernel(TreePtrs t, Geom g, UpdateArgs a) {
+__global__ void __launch_bounds__(kUpdThreads) update_scan_kernel(const int64_t* bidx, const float* btd,
+                                                                  uint32_t bB, Ctrl* ctrl, TreePtrs t,
+                                                                  Geom g, UpdateArgs a) {
   __shared__ UpdSmem<PPB> sm;
-  // The arguments the first steps need, fetched in one batch.
-  asm volatile("" ::"s"(t.ctrl), "s"(a.idx), "s"(a.td), "s"(a.B), "s"(a.src), "s"(a.size),
-               "s"(a.ring.dev), "s"(g.n), "s"(g.S));
+  // The batch and the control block arrive in scalar registers with the
+  // wave (the leading arguments, preloaded; the same as a's and t's), so
+  // the batch's first chunk is loaded before anything else.
+  int64_t ix0[CH];
+  float tx0[CH];
+  load_chunk<CH>(bidx, btd, bB, 0, ix0, tx0);
+  a.idx = bidx;
+  a.td = btd;
+  a.B = bB;
+  t.ctrl = ctrl;
+  // The other arguments the first steps need, fetched in one batch.
+  asm volatile("" ::"s"(a.src), "s"(a.size), "s"(a.ring.dev), "s"(g.n), "s"(g.S));
   const float m0 = __uint_as_float(t.ctrl->maxp_bits[a.src]);
-  scan_update<PPB, false, FULL, CH, LINE>(sm, t, g, a, blockIdx.x * PPB, filled_size(a), m0,
-                                          [](uint32_t) { return false; });
+  scan_update<PPB, false, FULL, CH, LINE>(sm, t, g, a, blockIdx.x * PPB, filled_size(a), m0, ix0,
+                                          tx0, [](uint32_t) { return false; });
 }
 
 // Large batches, step 1: every valid entry goes to its partition's bucket
@@ -1374,14 +1404,26 @@ __device__ __forceinline__ uint32_t batch_max_bits(const UpdateArgs& a, uint32_t
 // the running max in the same slot (a.dst == b.dst).  Blocks past the first
 // 2^P copy the intake's rows.
 template <bool PRIO, bool FULL, int CH>
-__global__ void __launch_bounds__(kUpdThreads) update_add_kernel(TreePtrs t, Geom g, Storage st,
-                                                                 UpdateArgs a, AddArgs b) {
+__global__ void __launch_bounds__(kUpdThreads) update_add_kernel(const int64_t* bidx, const float* btd,
+                                                                 uint32_t bB, Ctrl* ctrl, TreePtrs t,
+                                                                 Geom g, Storage st, UpdateArgs a,
+                                                                 AddArgs b) {
   __shared__ std::conditional_t<PRIO, UpdAddSmem, UpdSmem<1>> sm;
-  // The arguments the first steps need, fetched in one batch: left to
+  // The batch and the control block arrive in scalar registers with the
+  // wave (the leading arguments, preloaded; the same as a's and t's), so
+  // the batch's first chunk is loaded before anything else.
+  int64_t ix0[CH];
+  float tx0[CH];
+  load_chunk<CH>(bidx, btd, bB, 0, ix0, tx0);
+  a.idx = bidx;
+  a.td = btd;
+  a.B = bB;
+  t.ctrl = ctrl;
+  // The other arguments the first steps need, fetched in one batch: left to
   // itself, the compiler loads each after the branch that first needs it,
   // one dependent trip each.
-  asm volatile("" ::"s"(t.ctrl), "s"(a.idx), "s"(a.td), "s"(a.B), "s"(a.src), "s"(b.cursor),
-               "s"(b.count), "s"(b.size), "s"(b.ring.dev), "s"(b.last), "s"(g.n), "s"(g.S));
+  asm volatile("" ::"s"(a.src), "s"(b.cursor), "s"(b.count), "s"(b.size), "s"(b.ring.dev),
+               "s"(b.last), "s"(g.n), "s"(g.S));
   PER_STAMP(0, 0);
   PER_STAMP(1, 7);
   uint32_t cursor, size;
@@ -1398,7 +1440,7 @@ __global__ void __launch_bounds__(kUpdThreads) update_add_kernel(TreePtrs t, Geo
   // Update entries at slots the intake takes are left out of the repair
   // (the intake overwrites them; their priorities still count).
   const bool crowded = scan_update<1, true, FULL, CH, kScanLine>(
-      sm, t, g, a, part, size, m0, [&](uint32_t off) { return ir.has(off); });
+      sm, t, g, a, part, size, m0, ix0, tx0, [&](uint32_t off) { return ir.has(off); });
   if (ir.runs == 0) return;
   if constexpr (PRIO) {
     // The update's repair is complete, and visible to the whole block,
@@ -1542,12 +1584,12 @@ hipError_t launch_update(const TreePtrs& t, const Buckets& bk, const Geom& g, Ri
     const int ch = scan_chunk(B);
     const dim3 grid((unsigned)np), block(kUpdThreads);
     if (g.S == kMaxSpanBits && ch == 2)
-      return launch_kernel(update_scan_kernel<1, true, 2, kScanLine>, grid, block, 0, s, t, g, a);
+      return launch_kernel(update_scan_kernel<1, true, 2, kScanLine>, grid, block, 0, s, a.idx, a.td, a.B, t.ctrl, t, g, a);
     if (g.S == kMaxSpanBits && ch == 4)
-      return launch_kernel(update_scan_kernel<1, true, 4, kScanLine>, grid, block, 0, s, t, g, a);
+      return launch_kernel(update_scan_kernel<1, true, 4, kScanLine>, grid, block, 0, s, a.idx, a.td, a.B, t.ctrl, t, g, a);
     if (g.S == kMaxSpanBits)
-      return launch_kernel(update_scan_kernel<1, true, 8, kScanLine>, grid, block, 0, s, t, g, a);
-    return launch_kernel(update_scan_kernel<1, false, 8, false>, grid, block, 0, s, t, g, a);
+      return launch_kernel(update_scan_kernel<1, true, 8, kScanLine>, grid, block, 0, s, a.idx, a.td, a.B, t.ctrl, t, g, a);
+    return launch_kernel(update_scan_kernel<1, false, 8, false>, grid, block, 0, s, a.idx, a.td, a.B, t.ctrl, t, g, a);
   }
   // Bucketed: four partitions per block, one wave each, while the batch
   // spreads thin over the partitions (<= 16 entries each on average), so
@@ -1653,20 +1695,20 @@ hipError_t launch_update_add(const TreePtrs& t, const Geom& g, const Storage& st
   const int ch = scan_chunk(B);
   const dim3 grid(np + ncopy), block(kUpdThreads);
   if (!full && prio)
-    return launch_kernel(update_add_kernel<true, false, 8>, grid, block, 0, s, t, g, st, a, b);
+    return launch_kernel(update_add_kernel<true, false, 8>, grid, block, 0, s, a.idx, a.td, a.B, t.ctrl, t, g, st, a, b);
   if (!full)
-    return launch_kernel(update_add_kernel<false, false, 8>, grid, block, 0, s, t, g, st, a, b);
+    return launch_kernel(update_add_kernel<false, false, 8>, grid, block, 0, s, a.idx, a.td, a.B, t.ctrl, t, g, st, a, b);
   if (prio && ch == 2)
-    return launch_kernel(update_add_kernel<true, true, 2>, grid, block, 0, s, t, g, st, a, b);
+    return launch_kernel(update_add_kernel<true, true, 2>, grid, block, 0, s, a.idx, a.td, a.B, t.ctrl, t, g, st, a, b);
   if (prio && ch == 4)
-    return launch_kernel(update_add_kernel<true, true, 4>, grid, block, 0, s, t, g, st, a, b);
+    return launch_kernel(update_add_kernel<true, true, 4>, grid, block, 0, s, a.idx, a.td, a.B, t.ctrl, t, g, st, a, b);
   if (prio)
-    return launch_kernel(update_add_kernel<true, true, 8>, grid, block, 0, s, t, g, st, a, b);
+    return launch_kernel(update_add_kernel<true, true, 8>, grid, block, 0, s, a.idx, a.td, a.B, t.ctrl, t, g, st, a, b);
   if (ch == 2)
-    return launch_kernel(update_add_kernel<false, true, 2>, grid, block, 0, s, t, g, st, a, b);
+    return launch_kernel(update_add_kernel<false, true, 2>, grid, block, 0, s, a.idx, a.td, a.B, t.ctrl, t, g, st, a, b);
   if (ch == 4)
-    return launch_kernel(update_add_kernel<false, true, 4>, grid, block, 0, s, t, g, st, a, b);
-  return launch_kernel(update_add_kernel<false, true, 8>, grid, block, 0, s, t, g, st, a, b);
+    return launch_kernel(update_add_kernel<false, true, 4>, grid, block, 0, s, a.idx, a.td, a.B, t.ctrl, t, g, st, a, b);
+  return launch_kernel(update_add_kernel<false, true, 8>, grid, block, 0, s, a.idx, a.td, a.B, t.ctrl, t, g, st, a, b);
 }
 
 }  // namespace per
