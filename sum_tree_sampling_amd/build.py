@@ -25,7 +25,7 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-ffp-contract=off", "-fno-fast-math", "-fno-gpu-flush-denormals-to-zero",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    "-mllvm", "-amdgpu-kernarg-preload-count=4",
+    "-mllvm", "-amdgpu-kernarg-preload-count=5",
     "-Wall", "-Wno-unused-function",
 ]
 

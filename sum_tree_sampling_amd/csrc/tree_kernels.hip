@@ -959,18 +959,22 @@ __global__ void __launch_bounds__(kUpdThreads) update_scan_kernel(const int64_t*
 
 // Large batches, step 1: every valid entry goes to its partition's bucket
 // (kBucketCap entries per partition); past the cap, to an overflow list.
-__global__ void __launch_bounds__(256) bucket_kernel(Buckets bk, Geom g, UpdateArgs a) {
-  // The arguments the first steps need, fetched in one batch.
-  asm volatile("" ::"s"(a.idx), "s"(a.td), "s"(a.B), "s"(a.size), "s"(a.ring.dev),
-               "s"(bk.counts), "s"(g.S));
+__global__ void __launch_bounds__(256) bucket_kernel(const int64_t* idx, const float* td, uint32_t B,
+                                                     uint32_t* counts, Buckets bk, Geom g,
+                                                     UpdateArgs a) {
+  // The batch and the counts arrive in scalar registers with the wave (the
+  // leading arguments, preloaded; the same as a's and bk's), so the entry's
+  // loads issue at once.
   const uint32_t b = blockIdx.x * kTreeThreads + threadIdx.x;  // launched with kTreeThreads
-  if (b >= a.B) return;
-  const int64_t i = a.idx[b];
-  const float x = a.td[b];
+  if (b >= B) return;
+  const int64_t i = idx[b];
+  const float x = td[b];
+  // The other arguments the next steps need, fetched in one batch.
+  asm volatile("" ::"s"(a.size), "s"(a.ring.dev), "s"(g.S));
   asm volatile("" ::"v"(i), "v"(x));  // both loads out before either is looked at
   if (i < 0 || i >= (int64_t)filled_size(a)) return;
   const uint32_t part = (uint32_t)((uint64_t)i >> g.S);
-  const uint32_t k = atomicAdd(&bk.counts[part], 1u);
+  const uint32_t k = atomicAdd(&counts[part], 1u);
   if (k < kBucketCap) {
     const uint32_t e = part * kBucketCap + k;
     bk.slot[e] = (uint32_t)i;
@@ -989,25 +993,20 @@ __global__ void __launch_bounds__(256) bucket_kernel(Buckets bk, Geom g, UpdateA
 // entry k), crowded partitions (more entries than a bucket holds) are
 // rebuilt by the whole block after, from their bucket and the overflow list.
 template <int PPB, bool FULL>
-__global__ void __launch_bounds__(kUpdThreads) update_bucket_kernel(TreePtrs t, Buckets bk, Geom g,
-                                                            UpdateArgs a) {
+__global__ void __launch_bounds__(kUpdThreads) update_bucket_kernel(uint32_t* counts, const uint32_t* slot,
+                                                                    const uint32_t* pos,
+                                                                    const float* etd, uint32_t np,
+                                                                    TreePtrs t, Buckets bk, Geom g,
+                                                                    UpdateArgs a) {
   __shared__ UpdSmem<PPB> sm;
-  // The arguments the first steps need, fetched in one batch.
-  asm volatile("" ::"s"(t.ctrl), "s"(a.src), "s"(a.dst), "s"(a.ovf), "s"(bk.counts),
-               "s"(bk.slot), "s"(bk.pos), "s"(bk.td), "s"(g.P), "s"(g.S), "s"(g.n));
+  // The buckets and the partition count arrive in scalar registers with the
+  // wave (the leading arguments, preloaded; the same as bk's and 2^g.P), so
+  // the counts and entries are loaded before anything else.
   const uint32_t part0 = blockIdx.x * PPB;
-  const int nparts = (int)min((uint32_t)PPB, (1u << g.P) - part0);
-  const float m0 = __uint_as_float(t.ctrl->maxp_bits[a.src]);
-  uint32_t* max_dst = &t.ctrl->maxp_bits[a.dst];
-  if (threadIdx.x < (unsigned)nparts) {
-    sm.mtot[threadIdx.x] = bk.counts[part0 + threadIdx.x];
-    bk.counts[part0 + threadIdx.x] = 0u;  // ready for the next call's bucketing
-  }
-  if (threadIdx.x == 0 && blockIdx.x == 0) {
-    bk.ovf_n[a.ovf ^ 1] = 0u;  // the next call's overflow counter
-    publish_max(0u, true, m0, max_dst);
-  }
+  const int nparts = (int)min((uint32_t)PPB, np - part0);
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  uint32_t cnt = 0u;
+  if (threadIdx.x < (unsigned)nparts) cnt = counts[part0 + threadIdx.x];
   // Every lane loads its entry of the wave's bucket before the count is
   // known, so that the entries arrive together with the counts instead of
   // one trip after them (the lanes past the count drop theirs).
@@ -1015,9 +1014,21 @@ __global__ void __launch_bounds__(kUpdThreads) update_bucket_kernel(TreePtrs t, 
   float et = 0.0f;
   if (w < nparts) {
     const uint32_t e = (part0 + w) * kBucketCap + lane;
-    es = bk.slot[e];
-    ep = bk.pos[e];
-    et = bk.td[e];
+    es = slot[e];
+    ep = pos[e];
+    et = etd[e];
+  }
+  // The other arguments the next steps need, fetched in one batch.
+  asm volatile("" ::"s"(t.ctrl), "s"(a.src), "s"(a.dst), "s"(a.ovf), "s"(g.S), "s"(g.n));
+  const float m0 = __uint_as_float(t.ctrl->maxp_bits[a.src]);
+  uint32_t* max_dst = &t.ctrl->maxp_bits[a.dst];
+  if (threadIdx.x < (unsigned)nparts) {
+    sm.mtot[threadIdx.x] = cnt;
+    counts[part0 + threadIdx.x] = 0u;  // ready for the next call's bucketing
+  }
+  if (threadIdx.x == 0 && blockIdx.x == 0) {
+    bk.ovf_n[a.ovf ^ 1] = 0u;  // the next call's overflow counter
+    publish_max(0u, true, m0, max_dst);
   }
   __syncthreads();
   bool crowded = false;
@@ -1598,20 +1609,21 @@ hipError_t launch_update(const TreePtrs& t, const Buckets& bk, const Geom& g, Ri
   const bool thin = (uint64_t)B <= 16 * np;
   const unsigned grid = thin ? (unsigned)((np + 3) / 4) : (unsigned)np;
   const unsigned eb = grid_for((uint64_t)B, kTreeThreads, 1u << 30);
-  hipError_t e = launch_kernel(bucket_kernel, dim3(eb), dim3(kTreeThreads), 0, s, bk, g, a);
+  hipError_t e = launch_kernel(bucket_kernel, dim3(eb), dim3(kTreeThreads), 0, s, a.idx, a.td, a.B,
+                               bk.counts, bk, g, a);
   if (e != hipSuccess) return e;
   const bool full = g.S == kMaxSpanBits;
   if (thin && full)
-    return launch_kernel(update_bucket_kernel<4, true>, dim3(grid), dim3(kUpdThreads), 0, s, t,
-                         bk, g, a);
+    return launch_kernel(update_bucket_kernel<4, true>, dim3(grid), dim3(kUpdThreads), 0, s,
+                         bk.counts, bk.slot, bk.pos, bk.td, np, t, bk, g, a);
   if (thin)
-    return launch_kernel(update_bucket_kernel<4, false>, dim3(grid), dim3(kUpdThreads), 0, s, t,
-                         bk, g, a);
+    return launch_kernel(update_bucket_kernel<4, false>, dim3(grid), dim3(kUpdThreads), 0, s,
+                         bk.counts, bk.slot, bk.pos, bk.td, np, t, bk, g, a);
   if (full)
-    return launch_kernel(update_bucket_kernel<1, true>, dim3(grid), dim3(kUpdThreads), 0, s, t,
-                         bk, g, a);
-  return launch_kernel(update_bucket_kernel<1, false>, dim3(grid), dim3(kUpdThreads), 0, s, t, bk,
-                       g, a);
+    return launch_kernel(update_bucket_kernel<1, true>, dim3(grid), dim3(kUpdThreads), 0, s,
+                         bk.counts, bk.slot, bk.pos, bk.td, np, t, bk, g, a);
+  return launch_kernel(update_bucket_kernel<1, false>, dim3(grid), dim3(kUpdThreads), 0, s,
+                         bk.counts, bk.slot, bk.pos, bk.td, np, t, bk, g, a);
 }
 
 hipError_t launch_add(const TreePtrs& t, const Geom& g, const Storage& st, RingRef ring,
