@@ -376,6 +376,31 @@ __device__ __forceinline__ float stream_uniform(uint64_t w) {
 // Outputs of one sample (lead: the lane of its group that writes them): the
 // index, the IS weight and, cooperatively over the wave, the row copy (NT:
 // rows read with the non-temporal hint).
+// The IS weight (p / pmin)^-beta of a sampled priority p >= pmin > 0.  With
+// both normal and 0 <= beta <= 1: p = 2^e1 m1, pmin = 2^e0 m0 (m in [1, 2)),
+// so log2(p / pmin) = L = (e1 - e0) + log2 m1 - log2 m0, the integer part
+// exact and each f32 logarithm of a significand within 2^-24 of the true
+// value; z = -beta L in f64, n the integer nearest z and w = 2^n 2^(z - n)
+// with the fraction's power in f32.  The exponent is then off by at most
+// beta 2^-23 + 2^-26 (the fraction rounded to f32) and the f32 power by one
+// unit in its last place, so w lies within 2.1e-7 relative of the exact
+// value, and of the f64 formula's value rounded to f32 within 2.7e-7.
+// Otherwise, or where w would leave the f32 normal range, the f64 power
+// (pow_f32).
+__device__ __forceinline__ float is_weight(float p, float pmin, double beta) {
+  const uint32_t pb = __float_as_uint(p), qb = __float_as_uint(pmin);
+  const uint32_t pe = pb >> 23, qe = qb >> 23;  // sign and exponent: positive normal in [1, 254]
+  if (pe - 1u < 254u && qe - 1u < 254u && beta >= 0.0 && beta <= 1.0) {
+    const float m1 = __uint_as_float((pb & 0x007FFFFFu) | 0x3F800000u);
+    const float m0 = __uint_as_float((qb & 0x007FFFFFu) | 0x3F800000u);
+    const double L = (double)((int)pe - (int)qe) + ((double)log2f(m1) - (double)log2f(m0));
+    const double z = -beta * L;
+    const double n = rint(z);
+    if (n >= -125.0 && n <= 127.0) return ldexpf(exp2f((float)(z - n)), (int)n);
+  }
+  return pow_f32((double)p / (double)pmin, -beta);
+}
+
 template <int G, int SPW, bool NT>
 __device__ __forceinline__ void emit(const SampleArgs& a, uint32_t wave, int lane, uint32_t b,
                                      bool lead, uint32_t slot, float leaf, float pmin) {
@@ -393,12 +418,11 @@ __device__ __forceinline__ void emit(const SampleArgs& a, uint32_t wave, int lan
   // The weight, computed while the rows' loads are in flight.
   auto weight = [&]() {
     if (lead && a.w_out) {
-      // (N P_i)^-beta / (N P_min)^-beta = (p_i / p_min)^-beta: one pow, f64
-      // (pow_f32: the f64 pow's f32 value by a shorter route).
-      // With p_min > 0 every stored priority, the sampled one included, is
-      // > 0; with p_min = 0 the normaliser is infinite and w = 0.
+      // (N P_i)^-beta / (N P_min)^-beta = (p_i / p_min)^-beta: one power
+      // (is_weight).  With p_min > 0 every stored priority, the sampled one
+      // included, is > 0; with p_min = 0 the normaliser is infinite and w = 0.
       float w = 0.0f;
-      if (pmin > 0.0f) w = pow_f32((double)leaf / (double)pmin, -a.beta);
+      if (pmin > 0.0f) w = is_weight(leaf, pmin, a.beta);
       a.w_out[b] = w;
     }
   };

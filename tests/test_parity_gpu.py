@@ -936,6 +936,39 @@ def test_update_add_batch_max_near_running_max(alpha):
         compare_trees(o, g, "batch max near m0, alpha %g step %d" % (alpha, step))
 
 
+@pytest.mark.parametrize("beta", [0.0, 0.4, 0.7, 1.0, 1.5])
+@pytest.mark.parametrize("spread", ["wide, tiny min", "wide", "narrow"])
+def test_is_weights_wide_range(beta, spread):
+    """IS weights against the oracle's f64 form (N P_i)^-beta / (N P_min)^-beta
+    in each sampler layout (B = 512, 4096, 20480 on 2^16 leaves), with the
+    sampled priorities spread over 2^-20 .. 2^20 (or 1/2 .. 2) and the
+    minimum priority 2^-60 or the spread's own: within 1e-6 relative always,
+    and within 3e-7 for beta <= 1, the bound of the sampler's f32 route
+    there (the f64 power elsewhere)."""
+    say("IS weights", beta, spread)
+    n = 1 << 16
+    rng = np.random.default_rng(int(beta * 10) + 100 * len(spread))
+    lo, hi = (-1.0, 1.0) if spread == "narrow" else (-20.0, 20.0)
+    p = np.exp2(rng.uniform(lo, hi, n)).astype(np.float32)
+    if spread == "wide, tiny min":
+        p[rng.integers(0, n)] = np.float32(2.0**-60)
+    o = Oracle(n, 0)
+    g = _buf(n, 0, max_batch=1 << 15)
+    o.add(n, prio=p)
+    g.add(n, prio=dev(p))
+    for B in (512, 4096, 20480):
+        u = rng.random(B, dtype=np.float32)
+        ro = o.sample(u, beta=beta)
+        rg = g.sample(dev(u), beta=beta)
+        what = "IS weights beta %g %s B %d" % (beta, spread, B)
+        compare_sample(rg, ro, what)
+        if beta <= 1.0:
+            got = host(rg["w"]).astype(np.float64)
+            exp = np.asarray(ro["w"], np.float64)
+            rel = np.abs(got - exp) / np.abs(exp)
+            assert rel.max() <= 3e-7, (what, float(rel.max()))
+
+
 # ------------------------------------------------------------ full-size large buffer
 
 def test_large_16m_full_size():
