@@ -821,6 +821,13 @@ __device__ __forceinline__ void load_chunk(const int64_t* idx, const float* td, 
   }
 }
 
+// Word `slot` (0 or 1) of a two-slot field of the control block, from a
+// copy loaded whole at kernel start (one scalar trip through the preloaded
+// pointer, issued before the slot is known).
+__device__ __forceinline__ uint32_t ctrl_word(const uint32_t (&w)[2], int slot) {
+  return slot ? w[1] : w[0];
+}
+
 // Small batches: each block owns PPB consecutive partitions and scans the
 // whole batch for their slots; wave w repairs partition w of the block when
 // it is sparse, crowded partitions are rebuilt by the whole block after.
@@ -946,15 +953,18 @@ __global__ void __launch_bounds__(kUpdThreads) update_scan_kernel(const int64_t*
   int64_t ix0[CH];
   float tx0[CH];
   load_chunk<CH>(bidx, btd, bB, 0, ix0, tx0);
+  const Ctrl c = *ctrl;
   a.idx = bidx;
   a.td = btd;
   a.B = bB;
   t.ctrl = ctrl;
   // The other arguments the first steps need, fetched in one batch.
-  asm volatile("" ::"s"(a.src), "s"(a.size), "s"(a.ring.dev), "s"(g.n), "s"(g.S));
-  const float m0 = __uint_as_float(t.ctrl->maxp_bits[a.src]);
-  scan_update<PPB, false, FULL, CH, LINE>(sm, t, g, a, blockIdx.x * PPB, filled_size(a), m0, ix0,
-                                          tx0, [](uint32_t) { return false; });
+  asm volatile("" ::"s"(a.src), "s"(a.size), "s"(a.ring.dev), "s"(a.ring.slot), "s"(g.n),
+               "s"(g.S));
+  const float m0 = __uint_as_float(ctrl_word(c.maxp_bits, a.src));
+  const uint32_t size = a.ring.dev ? ctrl_word(c.size, a.ring.slot) : a.size;
+  scan_update<PPB, false, FULL, CH, LINE>(sm, t, g, a, blockIdx.x * PPB, size, m0, ix0, tx0,
+                                          [](uint32_t) { return false; });
 }
 
 // Large batches, step 1: every valid entry goes to its partition's bucket
@@ -1426,6 +1436,7 @@ __global__ void __launch_bounds__(kUpdThreads) update_add_kernel(const int64_t* 
   int64_t ix0[CH];
   float tx0[CH];
   load_chunk<CH>(bidx, btd, bB, 0, ix0, tx0);
+  const Ctrl c = *ctrl;
   a.idx = bidx;
   a.td = btd;
   a.B = bB;
@@ -1434,11 +1445,13 @@ __global__ void __launch_bounds__(kUpdThreads) update_add_kernel(const int64_t* 
   // itself, the compiler loads each after the branch that first needs it,
   // one dependent trip each.
   asm volatile("" ::"s"(a.src), "s"(b.cursor), "s"(b.count), "s"(b.size), "s"(b.ring.dev),
-               "s"(b.last), "s"(g.n), "s"(g.S));
+               "s"(b.ring.slot), "s"(b.last), "s"(g.n), "s"(g.S));
   PER_STAMP(0, 0);
   PER_STAMP(1, 7);
-  uint32_t cursor, size;
-  ring_state(t, b, cursor, size);
+  // The ring state before the intake: the launch's, or the device's (graph
+  // mode), from the control block's copy.
+  const uint32_t cursor = b.ring.dev ? ctrl_word(c.cursor, b.ring.slot) : b.cursor;
+  const uint32_t size = b.ring.dev ? ctrl_word(c.size, b.ring.slot) : b.size;
   commit_ring(t, g, b, cursor, size);
   const uint32_t np = 1u << g.P;
   if (blockIdx.x >= np) {
@@ -1447,7 +1460,7 @@ __global__ void __launch_bounds__(kUpdThreads) update_add_kernel(const int64_t* 
   }
   const uint32_t part = blockIdx.x;
   const IntakeRuns ir = intake_runs<FULL>(cursor, b.count, g, part);
-  const float m0 = __uint_as_float(t.ctrl->maxp_bits[a.src]);
+  const float m0 = __uint_as_float(ctrl_word(c.maxp_bits, a.src));
   // Update entries at slots the intake takes are left out of the repair
   // (the intake overwrites them; their priorities still count).
   const bool crowded = scan_update<1, true, FULL, CH, kScanLine>(
