@@ -126,7 +126,7 @@ int per_update(per_t* h, int64_t B, const int64_t* d_idx, const float* d_td,
  * per_update for callers that cannot allocate device memory at the call:
  * code under HIP graph capture, tight serving loops, harnesses that forbid
  * allocation.  Same arguments, result and errors as per_update.  A batch
- * that takes the bucketed update (more than 2^20 / 2^P entries, 2^P =
+ * that takes the bucketed update (more than 2^21 / 2^P entries, 2^P =
  * capacity / 4096 partitions) keeps its buckets, overflow list and counters
  * in a static device array of the library (4 MiB, one per device, held until
  * the process ends) instead of in the handle's workspace; the call clears
@@ -153,7 +153,7 @@ int per_update_static(per_t* h, int64_t B, const int64_t* d_idx, const float* d_
  * the running max after the update.  Arguments and errors as for the two
  * calls, all checked before anything is enqueued.  B == 0 or count == 0
  * reduces to the other call; a batch large enough for the bucketed update
- * (more than 2^20 / 2^P entries, 2^P = capacity / 4096 partitions) is
+ * (more than 2^21 / 2^P entries, 2^P = capacity / 4096 partitions) is
  * enqueued as the two calls.
  */
 int per_update_add(per_t* h, int64_t B, const int64_t* d_idx, const float* d_td, int64_t count,

@@ -1580,10 +1580,11 @@ hipError_t launch_bucket_clear(const Buckets& bk, const Geom& g, hipStream_t s) 
 }
 
 bool update_uses_buckets(const Geom& g, int64_t B) {
-  // Every partition's block scans the batch: np * B loads in all.  Past 2^20
-  // of them, bucket the batch first.
+  // Every partition's block scans the batch: np * B loads in all.  Past 2^21
+  // of them, bucket the batch first (measured: 4096 entries on 512
+  // partitions update in 8.6 us by the scan, 10.2 us bucketed).
   const uint64_t np = 1ull << g.P;
-  return np * (uint64_t)B > (1ull << 20);
+  return np * (uint64_t)B > (1ull << 21);
 }
 
 hipError_t launch_update(const TreePtrs& t, const Buckets& bk, const Geom& g, RingRef ring,

@@ -431,7 +431,7 @@ def test_time_next():
     the caller's events and give the same trees and outputs as an untimed
     call; the request is dropped after that call."""
     from sum_tree_sampling_amd import per
-    n, D = 1 << 20, 8  # 256 partitions: an update of 8192 entries is bucketed
+    n, D = 1 << 20, 8  # 256 partitions: an update of 16384 entries is bucketed
     say("time_next", n)
     rng = np.random.default_rng(11)
     bufs = [_buf(n, D, max_batch=1 << 15) for _ in range(2)]
@@ -445,8 +445,8 @@ def test_time_next():
     u = dev(rng.random(777, dtype=np.float32))
     small = (dev(rng.integers(0, n, 300).astype(np.int64)),
              dev(rng.standard_normal(300).astype(np.float32)))
-    large = (dev(rng.integers(0, n, 8192).astype(np.int64)),   # bucketed: two launches
-             dev(rng.standard_normal(8192).astype(np.float32)))
+    large = (dev(rng.integers(0, n, 16384).astype(np.int64)),   # bucketed: two launches
+             dev(rng.standard_normal(16384).astype(np.float32)))
     ops = [("sample", lambda g: g.sample(u, beta=0.4, rows=True)),
            ("update", lambda g: g.update(*small)),
            ("bucketed update", lambda g: g.update(*large)),
@@ -589,7 +589,7 @@ def _rows_np(rng, c, D):
 @pytest.mark.parametrize("n,D,B,c,prio,uniform,fused", [
     (1 << 12, 8, 256, 300, False, False, False),   # one partition; the ring wraps every few replays
     (1 << 16, 5, 1024, 3000, True, False, False),  # given priorities; scalar row copies
-    (1 << 20, 0, 8192, 5000, False, False, False),  # bucketed update: the overflow parity flips too
+    (1 << 20, 0, 16384, 5000, False, False, False),  # bucketed update: the overflow parity flips too
     (1 << 13, 4, 500, 700, False, True, False),    # uniform sample over a ring still filling up
     (1 << 21, 0, 512, 400, False, False, True),    # the Ape-X shard step: sample, update + intake
     (1 << 16, 5, 1024, 3000, True, False, True),   # fused, given priorities
@@ -725,7 +725,7 @@ def test_graph_mode_replay_rule():
     (1 << 12, 8, 64, 300, False, 3000),        # one partition; the ring wraps inside it
     (1 << 16, 5, 1000, 3000, True, 40000),     # given priorities; scalar row copies
     (1 << 16, 4, 2000, 5000, False, 1 << 16),  # crowded partitions; the intake spans several
-    (1 << 20, 0, 8192, 700, False, 1 << 20),   # bucketed batch: enqueued as the two calls
+    (1 << 20, 0, 16384, 700, False, 1 << 20),  # bucketed batch: enqueued as the two calls
     (1 << 16, 0, 513, 300, False, 1 << 16),    # just past two batch entries per thread
     (1 << 16, 3, 1025, 200, False, 50000),     # just past four
 ])

@@ -33,8 +33,8 @@ def _same(a, b, what):
 
 
 @pytest.mark.parametrize("L,batches,crowd", [
-    (22, (4096, 1500), False),    # 1024 partitions: thin bucketed batches
-    (20, (8192, 5000), False),    # 256 partitions, > 16 entries each: one partition per block
+    (22, (4096, 2500), False),    # 1024 partitions: thin bucketed batches
+    (20, (16384, 9000), False),   # 256 partitions, > 16 entries each: one partition per block
     (22, (6000, 2600), True),     # most entries in three partitions: overflow list
     (24, (65536, 30000), False),  # the largest capacity and batch the array holds
     (21, (300, 200), False),      # small batches: no scratch at all
