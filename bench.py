@@ -160,13 +160,17 @@ def latency_floor() -> dict:
     through a random cyclic permutation -- in a 1 MiB table, warm in L2 (4
     MiB per XCD), and over 100000 lines (12.5 MiB) of a 64 MiB table, warm
     in the MALL but not in L2.  A descent pays one such load per tree level
-    below the levels it keeps in LDS."""
+    below the levels it keeps in LDS.  Also the cost of a launch whose empty
+    kernel takes an argument block of 16, 256 or 512 bytes, eager and
+    replayed from a graph (the path's kernels take 200-330 bytes)."""
     import ctypes
     import torch
     lib = ctypes.CDLL(os.path.join(ROOT, "sum_tree_sampling_amd", "libper_probe.so"))
     lib.per_probe_empty.argtypes = [ctypes.c_int64, ctypes.c_void_p]
     lib.per_probe_chain.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                                     ctypes.c_void_p, ctypes.c_void_p]
+    lib.per_probe_launch_cost.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                          ctypes.POINTER(ctypes.c_double)]
     stream = torch.cuda.current_stream()
     sp = ctypes.c_void_p(stream.cuda_stream)
 
@@ -186,6 +190,13 @@ def latency_floor() -> dict:
     check(lib.per_probe_empty(K, sp))
     empty_us = timed(lambda: check(lib.per_probe_empty(K, sp))) * 1e3 / K
     res = {"empty_kernel_us": empty_us}
+    # what an argument block adds: eager launches wait for the host to write
+    # each block to device memory, a graph's replays do not
+    for nbytes in (16, 256, 512):
+        for graph in (0, 1):
+            us = ctypes.c_double(0.0)
+            check(lib.per_probe_launch_cost(3000, nbytes, graph, ctypes.byref(us)))
+            res["launch_%dB_args_%s_us" % (nbytes, "graph" if graph else "eager")] = us.value
     rng = np.random.default_rng(0x1A7)
     out = torch.zeros(1, dtype=torch.int32, device="cuda")
     for name, nbytes, depth in (("l2", 1 << 20, 20000), ("mall", 64 << 20, 100000)):

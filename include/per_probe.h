@@ -6,11 +6,13 @@
  * chains of dependent loads, one per tree level ("Putting prioritized
  * replay's segment tree on a GPU", section "Sampling Is a Descent": a
  * descent reads one node pair per level, each read depending on the last).
- * These two calls measure those two costs on their own.
+ * The first two calls measure those two costs on their own; the third
+ * measures what an argument block adds to a launch.
  *
  * Device pointers are prefixed d_ and owned by the caller; work goes to the
- * caller's stream; nothing is allocated and nothing waits.  Return 0, or -1
- * for a bad argument (checked on the host), or -4 for a HIP launch error.
+ * caller's stream; nothing is allocated and nothing waits (except in
+ * per_probe_launch_cost, which says so).  Return 0, or -1 for a bad argument
+ * (checked on the host), or -4 for a HIP error.
  */
 #ifndef PER_PROBE_H
 #define PER_PROBE_H
@@ -35,6 +37,15 @@ int per_probe_empty(int64_t launches, hipStream_t stream);
  * before and land on a line the others rarely share. */
 int per_probe_chain(const uint32_t* d_next, int64_t length, int64_t depth, uint32_t* d_out,
                     hipStream_t stream);
+
+/* The cost of one launch of an empty kernel (one 64-lane block) that takes
+ * an argument block of arg_bytes (16, 256 or 512) bytes, in us, into
+ * *us_per_launch: `launches` (in [100, 100000], a multiple of 100) launches
+ * back to back on a stream of the call's own, timed with events after a
+ * warm-up; with graph != 0 the same launches are captured 100 at a time into
+ * a HIP graph and replayed, so that no host work stands between them.
+ * Creates and destroys its stream, events and graph; waits for the work. */
+int per_probe_launch_cost(int64_t launches, int arg_bytes, int graph, double* us_per_launch);
 
 #ifdef __cplusplus
 }

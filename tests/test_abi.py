@@ -140,7 +140,7 @@ def test_probe_library_exports_and_checks():
         build.build()
     text = re.sub(r"/\*.*?\*/", "", open(PROBE_HEADER).read(), flags=re.S)
     names = sorted(set(re.findall(r"\b(per_probe_[a-z_]+)\s*\(", text)))
-    assert names == ["per_probe_chain", "per_probe_empty"]
+    assert names == ["per_probe_chain", "per_probe_empty", "per_probe_launch_cost"]
     out = subprocess.run(["nm", "-D", "--defined-only", PROBE_LIB], capture_output=True,
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT (per_probe_\w+)$", out, flags=re.M))
@@ -154,6 +154,13 @@ def test_probe_library_exports_and_checks():
     assert lib.per_probe_chain(0x1000, 1000, 10, 0x1000, None) == -1   # not a power of two
     assert lib.per_probe_chain(0x1000, 1024, 0, 0x1000, None) == -1
     assert lib.per_probe_chain(0x1000, 1 << 31, 10, 0x1000, None) == -1
+    lib.per_probe_launch_cost.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                          ctypes.POINTER(ctypes.c_double)]
+    us = ctypes.c_double(0.0)
+    assert lib.per_probe_launch_cost(3000, 256, 0, None) == -1
+    assert lib.per_probe_launch_cost(50, 256, 0, ctypes.byref(us)) == -1     # under 100
+    assert lib.per_probe_launch_cost(3050, 256, 1, ctypes.byref(us)) == -1   # not whole graphs
+    assert lib.per_probe_launch_cost(3000, 100, 0, ctypes.byref(us)) == -1   # no such block
 
 
 STAMPS_HEADER = os.path.join(ROOT, "include", "per_stamps.h")
