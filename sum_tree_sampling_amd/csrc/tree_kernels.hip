@@ -257,10 +257,23 @@ struct DenseSmem {
   uint32_t bits[kSub / 32];  // offsets that receive a new leaf
 };
 
+// A wave's batch entries listed for the scan's collect when some lane holds
+// more than one of them (scan_update), one list per wave; kept only by the
+// blocks of the variants that use them (WL).
+struct WaveList {
+  int64_t idx[64];
+  float td[64];
+  uint32_t pos[64];
+};
+struct WaveLists {
+  WaveList w[kUpdThreads / 64];
+};
+struct NoWaveLists {};
+
 // LDS of an update block that owns PPB consecutive partitions: one sparse
 // area per partition (wave w repairs partition w of the block), sharing its
 // memory with the block-wide rebuild of a crowded partition.
-template <int PPB>
+template <int PPB, bool WL = false>
 struct UpdSmem {
   union {
     SparseSmem sp[PPB];
@@ -272,6 +285,7 @@ struct UpdSmem {
   uint32_t bmax;       // max priority bits of the block's entries
   uint32_t ball;       // max priority bits of the whole batch (fused intake blocks)
   int flag;
+  std::conditional_t<WL, WaveLists, NoWaveLists> wl;  // last: the others' offsets stay put
 };
 
 // The parent of two tree values: their f32 sum, or their min.
@@ -877,6 +891,65 @@ __device__ __forceinline__ bool scan_update(SM& sm, const TreePtrs& t, const Geo
       const uint32_t q = (uint32_t)((uint64_t)i >> span_bits<FULL>(g)) - part0;  // wraps below part0
       if (q < (uint32_t)nparts) pending |= 1u << c;
     }
+    // A lane holding several entries would collect them one round (one
+    // sibling trip and power) after another.  Then the wave lists its
+    // entries in LDS first -- entry e counted lane by lane in slot order --
+    // and lane e mod 64 takes entry e, 64 entries per round.  Compiled for
+    // the larger batches (four or more entries per thread and chunk), where
+    // a busy partition's entries often share a lane: the code costs the
+    // smaller ones more than it saves.
+    if constexpr (kChunk >= 4 && FULL) {
+     const uint32_t cnt = (uint32_t)__builtin_popcount(pending);
+     if (__ballot(cnt > 1u) != 0ull) {
+      WaveList& wl = sm.wl.w[threadIdx.x >> 6];
+      const int lane = threadIdx.x & 63;
+      const uint64_t below = (1ull << lane) - 1ull;
+      uint32_t pre = 0u, total = 0u;  // entries of the lower lanes; of the wave
+#pragma unroll
+      for (int bit = 0; (1 << bit) <= kChunk; ++bit) {
+        const uint64_t bm = __ballot((cnt >> bit) & 1u);
+        pre += (uint32_t)__popcll(bm & below) << bit;
+        total += (uint32_t)__popcll(bm) << bit;
+      }
+      for (uint32_t r0 = 0; r0 < total; r0 += 64u) {
+        uint32_t e = pre;
+#pragma unroll
+        for (int c = 0; c < kChunk; ++c) {
+          if ((pending >> c) & 1u) {
+            if (e - r0 < 64u) {
+              wl.idx[e - r0] = ix[c];
+              wl.td[e - r0] = tx[c];
+              wl.pos[e - r0] = b0 + (uint32_t)c * kUpdThreads + threadIdx.x;
+            }
+            ++e;
+          }
+        }
+        // The wave reads what its own lanes wrote: LDS operations of one
+        // wave complete in order.
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (r0 + (uint32_t)lane < total) {
+          // the entry is the block's (as in the rounds below)
+          const int64_t i = wl.idx[lane];
+          const uint32_t q = (uint32_t)((uint64_t)i >> span_bits<FULL>(g)) - part0;
+          const uint32_t part = part0 + q;
+          const uint32_t off = (uint32_t)i - (part << span_bits<FULL>(g));
+          bool keep = true;
+          if constexpr (FUSED) keep = !skip(off);
+          const int k = keep ? atomicAdd(&sm.count[q], 1) : kSparseMax;
+          const float p = collect<FULL, LINE>(sm.u.sp[q], k, t, g, part, off, wl.pos[lane],
+                                              wl.td[lane], m0, a.alpha, a.eps, a.p_nan);
+          atomicMax(&sm.bmax, __float_as_uint(p));
+        }
+        // and overwrites the list only after every lane has read its entry
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      }
+      pending = 0u;
+     }
+    }
     // One entry per lane per round: entries of one wave in different slots
     // are collected together, their sibling loads and pows overlapping,
     // instead of one slot after the other.
@@ -946,7 +1019,7 @@ template <int PPB, bool FULL, int CH, bool LINE>
 __global__ void __launch_bounds__(kUpdThreads) update_scan_kernel(const int64_t* bidx, const float* btd,
                                                                   uint32_t bB, Ctrl* ctrl, TreePtrs t,
                                                                   Geom g, UpdateArgs a) {
-  __shared__ UpdSmem<PPB> sm;
+  __shared__ UpdSmem<PPB, (CH >= 4 && FULL)> sm;
   // The batch and the control block arrive in scalar registers with the
   // wave (the leading arguments, preloaded; the same as a's and t's), so
   // the batch's first chunk is loaded before anything else.
@@ -1321,6 +1394,7 @@ __global__ void __launch_bounds__(256) add_kernel(TreePtrs t, Geom g, Storage st
 
 // LDS of the fused update + intake block when the intake brings its own
 // priorities: the update's areas and the intake's range repair share it.
+template <bool WL = false>
 struct UpdAddSmem {
   union {
     SparseSmem sp[1];
@@ -1333,6 +1407,7 @@ struct UpdAddSmem {
   uint32_t bmax;
   uint32_t ball;
   int flag;
+  std::conditional_t<WL, WaveLists, NoWaveLists> wl;  // last: the others' offsets stay put
 };
 
 // Whether f32(pow(y, alpha)) <= m0 for every y <= ys, decided by f32
@@ -1429,7 +1504,7 @@ __global__ void __launch_bounds__(kUpdThreads) update_add_kernel(const int64_t* 
                                                                  uint32_t bB, Ctrl* ctrl, TreePtrs t,
                                                                  Geom g, Storage st, UpdateArgs a,
                                                                  AddArgs b) {
-  __shared__ std::conditional_t<PRIO, UpdAddSmem, UpdSmem<1>> sm;
+  __shared__ std::conditional_t<PRIO, UpdAddSmem<(CH >= 4 && FULL)>, UpdSmem<1, (CH >= 4 && FULL)>> sm;
   // The batch and the control block arrive in scalar registers with the
   // wave (the leading arguments, preloaded; the same as a's and t's), so
   // the batch's first chunk is loaded before anything else.
