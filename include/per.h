@@ -128,7 +128,7 @@ int per_update(per_t* h, int64_t B, const int64_t* d_idx, const float* d_td,
  * allocation.  Same arguments, result and errors as per_update.  A batch
  * that takes the bucketed update (more than 2^21 / 2^P entries, 2^P =
  * capacity / 4096 partitions) keeps its buckets, overflow list and counters
- * in a static device array of the library (4 MiB, one per device, held until
+ * in a static device array of the library (5 MiB, one per device, held until
  * the process ends) instead of in the handle's workspace; the call clears
  * its counters first with a small kernel.  Limits of that array: capacity
  * <= 2^24 and B <= 2^16 for a bucketed batch, else PER_EINVAL; smaller

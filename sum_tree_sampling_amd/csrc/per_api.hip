@@ -118,7 +118,7 @@ per::Geom make_geom(int64_t capacity) {
 // leaves (capacity <= 2^24) and batches of up to 2^16 entries.
 constexpr int64_t kStaticMaxParts = int64_t(1) << 12;
 constexpr int64_t kStaticMaxBatch = int64_t(1) << 16;
-constexpr size_t kStaticScratchBytes = size_t(4) << 20;
+constexpr size_t kStaticScratchBytes = size_t(5) << 20;
 constexpr int kMaxDevices = 64;
 
 static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
@@ -157,7 +157,7 @@ Buckets bucket_layout(char* base, size_t np, int64_t max_batch, size_t* end) {
   };
   const size_t nb = np * kBucketCap;
   Buckets b;
-  b.counts = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * np));
+  b.counts = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * np * kCountStride));
   b.ovf_n = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * 2));
   b.slot = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * nb));
   b.pos = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * nb));
@@ -183,7 +183,7 @@ Layout workspace_layout(int64_t n, int64_t max_batch) {
   l.sum = take(sizeof(float) * 2 * (size_t)n);
   l.mn = take(sizeof(float) * 2 * (size_t)n);
   l.ctrl = take(sizeof(Ctrl));
-  l.counts = take(sizeof(uint32_t) * np);
+  l.counts = take(sizeof(uint32_t) * np * kCountStride);
   l.ovf_n = take(sizeof(uint32_t) * 2);
   l.slot = take(sizeof(uint32_t) * nb);
   l.pos = take(sizeof(uint32_t) * nb);

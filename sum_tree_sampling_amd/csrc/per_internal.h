@@ -86,8 +86,13 @@ struct TreePtrs {
 // Scratch of the bucketed (large-batch) update: a bucket of kBucketCap
 // entries per partition and an overflow list for the rest.
 constexpr int kBucketCap = kSparseMax;
+// Words between two partitions' bucket counts: one count per 128-byte line,
+// so that the bucketing pass's atomic adds to different partitions do not
+// queue behind each other on a shared line (2^24 leaves, 65536 entries:
+// update 25.2 -> 24.0 us against packed counts).
+constexpr uint32_t kCountStride = 32;
 struct Buckets {
-  uint32_t* counts;   // [2^P] entries per partition (reset by the update)
+  uint32_t* counts;   // [2^P * kCountStride] entries of partition p at [p * kCountStride] (reset by the update)
   uint32_t* ovf_n;    // [2] overflow counters, used by alternate calls
   uint32_t* slot;     // [2^P * kBucketCap] leaf slot of each bucketed entry
   uint32_t* pos;      // its batch position

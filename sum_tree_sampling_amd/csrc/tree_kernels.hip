@@ -781,7 +781,7 @@ __global__ void __launch_bounds__(256) init_kernel(TreePtrs t, Buckets bk, Geom 
   }
   const uint32_t np = 1u << g.P;
   for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < np; i += stride)
-    bk.counts[i] = 0u;
+    bk.counts[i * kCountStride] = 0u;
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     t.ctrl->maxp_bits[0] = __float_as_uint(1.0f);
     t.ctrl->maxp_bits[1] = __float_as_uint(1.0f);
@@ -796,7 +796,7 @@ __global__ void __launch_bounds__(256) init_kernel(TreePtrs t, Buckets bk, Geom 
 
 __global__ void __launch_bounds__(256) bucket_clear_kernel(Buckets bk, uint32_t np) {
   for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < np; i += gridDim.x * blockDim.x)
-    bk.counts[i] = 0u;
+    bk.counts[i * kCountStride] = 0u;
   if (blockIdx.x == 0 && threadIdx.x < 2) bk.ovf_n[threadIdx.x] = 0u;
 }
 
@@ -1057,7 +1057,7 @@ __global__ void __launch_bounds__(256) bucket_kernel(const int64_t* idx, const f
   asm volatile("" ::"v"(i), "v"(x));  // both loads out before either is looked at
   if (i < 0 || i >= (int64_t)filled_size(a)) return;
   const uint32_t part = (uint32_t)((uint64_t)i >> g.S);
-  const uint32_t k = atomicAdd(&counts[part], 1u);
+  const uint32_t k = atomicAdd(&counts[part * kCountStride], 1u);
   if (k < kBucketCap) {
     const uint32_t e = part * kBucketCap + k;
     bk.slot[e] = (uint32_t)i;
@@ -1089,7 +1089,7 @@ __global__ void __launch_bounds__(kUpdThreads) update_bucket_kernel(uint32_t* co
   const int nparts = (int)min((uint32_t)PPB, np - part0);
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   uint32_t cnt = 0u;
-  if (threadIdx.x < (unsigned)nparts) cnt = counts[part0 + threadIdx.x];
+  if (threadIdx.x < (unsigned)nparts) cnt = counts[(part0 + threadIdx.x) * kCountStride];
   // Every lane loads its entry of the wave's bucket before the count is
   // known, so that the entries arrive together with the counts instead of
   // one trip after them (the lanes past the count drop theirs).
@@ -1107,7 +1107,7 @@ __global__ void __launch_bounds__(kUpdThreads) update_bucket_kernel(uint32_t* co
   uint32_t* max_dst = &t.ctrl->maxp_bits[a.dst];
   if (threadIdx.x < (unsigned)nparts) {
     sm.mtot[threadIdx.x] = cnt;
-    counts[part0 + threadIdx.x] = 0u;  // ready for the next call's bucketing
+    counts[(part0 + threadIdx.x) * kCountStride] = 0u;  // ready for the next call's bucketing
   }
   if (threadIdx.x == 0 && blockIdx.x == 0) {
     bk.ovf_n[a.ovf ^ 1] = 0u;  // the next call's overflow counter
