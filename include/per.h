@@ -174,9 +174,12 @@ int per_update_add(per_t* h, int64_t B, const int64_t* d_idx, const float* d_td,
  *    most m and the right child's sum is not 0 (then m = f32(m - left sum)),
  *    else the left one.
  *  d_idx_out [B] i64: sampled slots (required).
- *  d_w_out [B] f32 or NULL: w_b = f32((N*P_b)^-beta / (N*P_min)^-beta) in
- *    f64, N = size, P_b = p_b / total, P_min = min-tree root / total; 0 when
- *    the min priority is 0.
+ *  d_w_out [B] f32 or NULL: w_b = (N*P_b)^-beta / (N*P_min)^-beta, N = size,
+ *    P_b = p_b / total, P_min = min-tree root / total, i.e. (p_b / p_min)^-beta;
+ *    0 when the min priority is 0.  For 0 <= beta <= 1 and normal priorities
+ *    it is taken from the exact exponent difference, f32 logarithms of the
+ *    significands and an f32 power of two, within 3e-7 relative of the f64
+ *    value rounded to f32; otherwise the f32 of the f64 power.
  *  Row outputs (all NULL, or all given when the handle has storage):
  *    d_states_out / d_next_states_out [B x state_dim] f32 (16-byte aligned),
  *    d_actions_out [B] u32, d_rewards_out [B] f32, d_dones_out [B] u8: byte
