@@ -185,8 +185,13 @@ __device__ __forceinline__ int span_bits(const Geom& g) {
 // valid lane j < i with d_j <= depth(X) has d_j == depth(X); that lane's
 // chain ends exactly at the left child, whose value it holds, frozen.
 // Otherwise the other child is unchanged and its stored value is the
-// sibling's.  Must be called by all 64 lanes of the wave.
-template <bool FULL>
+// sibling's.  Must be called by all 64 lanes of the wave.  PAIR: the lanes
+// hold the leaves of two consecutive partitions, part and part + 1 (off up
+// to 2^(S+1)); a lane whose right neighbour lies in the other partition
+// takes d = P - 1 like the last lane, so each chain stops at its own
+// partition's root, and the first partition's last chain, with d below
+// every depth the loop visits, ends no chain of the second.
+template <bool FULL, bool PAIR = false>
 __device__ __forceinline__ void sparse_chain(const TreePtrs& t, const Geom& g, uint32_t part, int m, bool valid,
                              uint32_t off, float p, const float* ps, const float* pm) {
   const int S = span_bits<FULL>(g);
@@ -200,6 +205,7 @@ __device__ __forceinline__ void sparse_chain(const TreePtrs& t, const Geom& g, u
   const uint32_t next_leaf = next_lane(leaf);
   int d = g.P - 1;
   if (lane < m - 1) d = g.L - 1 - (31 - __clz(leaf ^ next_leaf));
+  if constexpr (PAIR) d = max(d, (int)g.P - 1);
 
   float vs = p, vm = p;
   const uint64_t lanes_below = (1ull << lane) - 1ull;
@@ -388,7 +394,7 @@ __device__ __forceinline__ void publish_max(uint32_t mb, bool carry, float m0,
 // counted from LDS (m is small) -- so that the last batch position of each
 // offset is the last of its run, and repair the chains of those winners with
 // the prefetched siblings.
-template <bool FULL>
+template <bool FULL, bool PAIR = false>
 __device__ __forceinline__ void wave_update(SparseSmem& sp, const TreePtrs& t, const Geom& g, uint32_t part,
                             int m) {
   const int lane = threadIdx.x & 63;
@@ -416,7 +422,7 @@ __device__ __forceinline__ void wave_update(SparseSmem& sp, const TreePtrs& t, c
     pm[k] = sp.sib_m[src][k];
   }
   PER_STAMP(0, 14);
-  sparse_chain<FULL>(t, g, part, m, win, in ? off : 0u, p, ps, pm);
+  sparse_chain<FULL, PAIR>(t, g, part, m, win, in ? off : 0u, p, ps, pm);
 }
 
 // ------------------------------------------------------------ crowded partitions
@@ -1160,6 +1166,123 @@ __global__ void __launch_bounds__(kUpdThreads) update_bucket_kernel(uint32_t* co
   }
 }
 
+// The sparse repair of m <= 64 bucket entries by one wave (lane k holding
+// entry k: slot es, batch position ep, TD error et) in partition part, or
+// in part and part + 1 (PAIR, the first's entries first).
+template <bool PAIR>
+__device__ __forceinline__ void bucket_repair(SparseSmem& sp, const TreePtrs& t, const Geom& g,
+                                              const UpdateArgs& a, uint32_t part, uint32_t m,
+                                              uint32_t es, uint32_t ep, float et, float m0,
+                                              uint32_t* max_dst) {
+  const int lane = threadIdx.x & 63;
+  uint32_t pb = 0u;
+  if ((uint32_t)lane < m) {
+    const float p = collect<true, true>(sp, lane, t, g, part, es - (part << kMaxSpanBits), ep, et,
+                                        m0, a.alpha, a.eps, a.p_nan);
+    pb = __float_as_uint(p);
+  }
+  pb = wave_max_u32(pb);
+  if (lane == 0) publish_max(pb, false, m0, max_dst);
+  // The wave reads what its own lanes wrote to its sparse area: LDS
+  // operations of one wave complete in order.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  wave_update<true, PAIR>(sp, t, g, part, (int)m);
+}
+
+// Large batches, step 2, for thin batches over many full partitions: as
+// update_bucket_kernel, with eight partitions per block and the pair 2w,
+// 2w + 1 to wave w.  When the two buckets fit one wave together, lane k
+// takes entry k of the first and the second's entries follow it (moved
+// down the lanes by a shuffle), and one sort and one chain repair both
+// partitions.  A wave's chain costs the same instructions whether it
+// carries 16 entries or 32, and with every wave of the grid resident the
+// chains are bound by instruction issue, so this halves their cost.  Two
+// buckets that do not fit one wave are repaired one after the other;
+// crowded partitions are rebuilt by the whole block after.
+__global__ void __launch_bounds__(kUpdThreads) update_bucket_pair_kernel(uint32_t* counts,
+                                                                         const uint32_t* slot,
+                                                                         const uint32_t* pos,
+                                                                         const float* etd, uint32_t np,
+                                                                         TreePtrs t, Buckets bk, Geom g,
+                                                                         UpdateArgs a) {
+  constexpr int PPB = 8;
+  __shared__ UpdSmem<PPB> sm;
+  // As in update_bucket_kernel: the counts and both buckets' entries are
+  // loaded first, through the preloaded leading arguments.
+  const uint32_t part0 = blockIdx.x * PPB;
+  const int nparts = (int)min((uint32_t)PPB, np - part0);
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  uint32_t cnt = 0u;
+  if (threadIdx.x < (unsigned)nparts) cnt = counts[(part0 + threadIdx.x) * kCountStride];
+  uint32_t es[2] = {0u, 0u}, ep[2] = {0u, 0u};
+  float et[2] = {0.0f, 0.0f};
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    if (2 * w + h < nparts) {
+      const uint32_t e = (part0 + 2 * w + h) * kBucketCap + lane;
+      es[h] = slot[e];
+      ep[h] = pos[e];
+      et[h] = etd[e];
+    }
+  }
+  asm volatile("" ::"s"(t.ctrl), "s"(a.src), "s"(a.dst), "s"(a.ovf), "s"(g.n));
+  const float m0 = __uint_as_float(t.ctrl->maxp_bits[a.src]);
+  uint32_t* max_dst = &t.ctrl->maxp_bits[a.dst];
+  if (threadIdx.x < (unsigned)nparts) {
+    sm.mtot[threadIdx.x] = cnt;
+    counts[(part0 + threadIdx.x) * kCountStride] = 0u;  // ready for the next call's bucketing
+  }
+  if (threadIdx.x == 0 && blockIdx.x == 0) {
+    bk.ovf_n[a.ovf ^ 1] = 0u;  // the next call's overflow counter
+    publish_max(0u, true, m0, max_dst);
+  }
+  __syncthreads();
+  bool crowded = false;
+  for (int q = 0; q < nparts; ++q) crowded |= sm.mtot[q] > (uint32_t)kBucketCap;
+  const uint32_t pa = part0 + 2 * w;  // the wave's first partition
+  const uint32_t ma = 2 * w < nparts ? sm.mtot[2 * w] : 0u;
+  const uint32_t mb = 2 * w + 1 < nparts ? sm.mtot[2 * w + 1] : 0u;
+  const bool sa = ma > 0u && ma <= (uint32_t)kBucketCap;
+  const bool sb = mb > 0u && mb <= (uint32_t)kBucketCap;
+  if (sa && sb && ma + mb <= (uint32_t)kSparseMax) {  // uniform across the wave
+    const int src = lane >= (int)ma ? lane - (int)ma : 0;
+    const uint32_t s1 = (uint32_t)__shfl((int)es[1], src);
+    const uint32_t p1 = (uint32_t)__shfl((int)ep[1], src);
+    const float t1 = __shfl(et[1], src);
+    const bool first = (uint32_t)lane < ma;
+    bucket_repair<true>(sm.u.sp[2 * w], t, g, a, pa, ma + mb, first ? es[0] : s1,
+                        first ? ep[0] : p1, first ? et[0] : t1, m0, max_dst);
+  } else {
+    if (sa) bucket_repair<false>(sm.u.sp[2 * w], t, g, a, pa, ma, es[0], ep[0], et[0], m0, max_dst);
+    if (sb)
+      bucket_repair<false>(sm.u.sp[2 * w + 1], t, g, a, pa + 1u, mb, es[1], ep[1], et[1], m0,
+                           max_dst);
+  }
+  if (!crowded) return;
+  // The dense rebuild reuses the sparse areas: every wave is done with them.
+  __syncthreads();
+  const uint32_t novf = bk.ovf_n[a.ovf];
+  for (int q = 0; q < nparts; ++q) {
+    if (sm.mtot[q] <= (uint32_t)kBucketCap) continue;
+    const uint32_t part = part0 + q, base = part << g.S;
+    const uint32_t* bslot = bk.slot + part * kBucketCap;
+    const uint32_t* bpos = bk.pos + part * kBucketCap;
+    const float* btd = bk.td + part * kBucketCap;
+    const uint32_t mbits = dense_update<kUpdThreads>(sm.u.dn, sm.flag, sm.sx, t, g, part, [&](auto f) {
+      for (uint32_t k = threadIdx.x; k < kBucketCap; k += kUpdThreads)
+        f(bslot[k] - base, bpos[k], priority_of(btd[k], m0, a.alpha, a.eps, a.p_nan));
+      for (uint32_t k = threadIdx.x; k < novf; k += kUpdThreads) {
+        const uint32_t i = bk.oslot[k];
+        if ((i >> g.S) == part)
+          f(i - base, bk.opos[k], priority_of(bk.otd[k], m0, a.alpha, a.eps, a.p_nan));
+      }
+    });
+    if (threadIdx.x == 0) publish_max(mbits, false, m0, max_dst);
+  }
+}
+
 // Partitions touched by the ring range [cursor, cursor + count): one run,
 // or two when the range wraps past the end and the runs stay apart.
 struct TouchedRuns {
@@ -1633,6 +1756,10 @@ inline int scan_chunk(int64_t B) {
   return B <= 2 * kUpdThreads ? 2 : (B <= 4 * kUpdThreads ? 4 : (B <= 8 * kUpdThreads ? 8 : 16));
 }
 
+// The fewest blocks the bucketed repair with two partitions per wave is
+// launched with: one per CU of the MI355X.
+constexpr uint32_t kPairMinBlocks = 256;
+
 inline unsigned grid_for(uint64_t work, unsigned per_block, unsigned cap) {
   uint64_t b = (work + per_block - 1) / per_block;
   if (b < 1) b = 1;
@@ -1707,6 +1834,11 @@ hipError_t launch_update(const TreePtrs& t, const Buckets& bk, const Geom& g, Ri
                                bk.counts, bk, g, a);
   if (e != hipSuccess) return e;
   const bool full = g.S == kMaxSpanBits;
+  // Two partitions per wave while eight per block still give at least one
+  // block per CU.
+  if (thin && full && np >= 8u * kPairMinBlocks)
+    return launch_kernel(update_bucket_pair_kernel, dim3((unsigned)(np / 8)), dim3(kUpdThreads), 0, s,
+                         bk.counts, bk.slot, bk.pos, bk.td, np, t, bk, g, a);
   if (thin && full)
     return launch_kernel(update_bucket_kernel<4, true>, dim3(grid), dim3(kUpdThreads), 0, s,
                          bk.counts, bk.slot, bk.pos, bk.td, np, t, bk, g, a);

@@ -574,6 +574,59 @@ def test_large_tree_writers(L):
     assert np.float32(host(g.scalar("min"))[0]) == np.float32(o.min_tree()[1])
 
 
+def test_bucketed_partition_pairs():
+    """A 2^23-leaf tree (2^11 partitions of 4096 leaves) updated by batches of
+    ~12000 entries, which the bucketed repair takes two partitions per wave:
+    pairs whose buckets fit one wave together (with repeated slots and the
+    two leaves on either side of the partition boundary), pairs that do not
+    (repaired one after the other), a crowded partition beside a sparse one,
+    a pair with one empty partition, and the first and last partitions.  Both
+    trees and the running max match the oracle bit for bit after each of
+    three calls in a row (counts and overflow list cleared between them)."""
+    L, S = 23, 12
+    n, span = 1 << L, 1 << S
+    np_ = n >> S
+    rng = np.random.default_rng(2323)
+    o = Oracle(n)
+    g = _buf(n, max_batch=16384)
+    p0 = (rng.random(n) ** 0.6).astype(np.float32)
+    o.add(n, prio=p0)
+    g.add(n, prio=dev(p0))
+
+    def leaves(part, k):
+        off = rng.integers(0, span, k)
+        off[k // 2: k // 2 + k // 4] = off[: k // 4]  # repeated slots
+        return part * span + off
+
+    for call in range(3):
+        special = {
+            10: 40, 11: 30,        # 70 together: one after the other
+            20: 30, 21: 30,        # 64 together with the boundary leaves: one wave
+            30: 100, 31: 10,       # crowded (overflow list) beside sparse
+            40: 0, 41: 20,         # one empty partition
+            0: 25, 1: 25,          # the first pair
+            np_ - 2: 12, np_ - 1: 33,  # the last pair
+        }
+        base = rng.integers(0, n, 12000)
+        base = base[~np.isin(base >> S, list(special))]
+        r = base.size // 8
+        base[:r] = base[r: 2 * r]  # repeated slots
+        parts = [base]
+        for part, k in special.items():
+            if k:
+                parts.append(leaves(part, k))
+        # the two leaves on either side of a boundary, inside a one-wave pair
+        parts.append(np.array([21 * span - 1, 21 * span, 21 * span - 1, 21 * span]))
+        parts.append(np.array([0, n - 1, 0]))
+        idx = np.concatenate(parts).astype(np.int64)
+        rng.shuffle(idx)
+        td = (rng.standard_normal(idx.size) * (1 + call)).astype(np.float32)
+        say("bucketed pairs call", call, "B", idx.size)
+        o.update(idx, td)
+        g.update(dev(idx), dev(td))
+        compare_trees(o, g, "bucketed pairs call %d" % call)
+
+
 # ------------------------------------------------------------ graph mode
 
 def _rows_np(rng, c, D):
