@@ -58,7 +58,8 @@ CALIB_REPS = 3
 # rebuild, the update is one kernel or a bucket pass plus its update).
 OP_KERNELS = {
     "sample": ("sample_kernel", "top_kernel"),
-    "update": ("update_scan_kernel", "bucket_kernel", "update_bucket_kernel"),
+    "update": ("update_scan_kernel", "bucket_kernel", "update_bucket_kernel",
+               "update_bucket_pair_kernel"),
     "add": ("add_kernel",),
     "update_add": ("update_add_kernel",),
 }
